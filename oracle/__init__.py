@@ -1,0 +1,9 @@
+"""CPU oracle of the sparse-KV decode step -- test infrastructure only.
+
+Only tests/, the entry point's smoke() check and bench.py's cpu_baseline leg
+may import this package.  The GPU library neither imports it nor shares any
+code with it.
+"""
+
+from .step import *  # noqa: F401,F403
+from .step import PINS  # noqa: F401

@@ -1,0 +1,474 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself:
+hand-worked fixtures (tests/golden), the pages' closed forms, brute force on
+tiny inputs, exact rational arithmetic, a library attention routine, and
+special cases with known answers.
+
+Pages (by title):
+  [P1] "8 agents x 250K context on two 3090s: sparse KV decode with a rank-64
+       key sketch and a host-RAM tier"
+  [P3] "You can offload most of Qwen3.8-Flash-Next's KV cache to RAM with
+       little decode slowdown"
+  [P4] "3.14M Context on 3x 3090: The Power of an Architecture That Puts KV
+       Cache in Host RAM"
+"""
+
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+MiB = 1 << 20
+KiB = 1 << 10
+
+
+def _lines(name):
+    with open(os.path.join(GOLD, name)) as f:
+        for ln in f:
+            ln = ln.strip()
+            if ln and not ln.startswith("#"):
+                yield ln
+
+
+# --------------------------------------------------------------------------
+# formats and scores
+# --------------------------------------------------------------------------
+
+def test_int4_nibbles_fixture():
+    for ln in _lines("int4_nibbles.txt"):
+        parts = ln.split()
+        if parts[0] == "score":
+            code_bytes = np.array([int(x, 16) for x in parts[1].split(",")], dtype=np.uint8)
+            qv = np.array([int(x) for x in parts[2].split(",")], dtype=np.int8)
+            scale = np.array([np.float16(float(parts[3]))])
+            codes = code_bytes.reshape(1, 1, -1)
+            keys = oracle.sketch_keys(qv.reshape(1, -1), codes, scale.reshape(1, 1), [1], 0, 0, 0)
+            dot = int(np.dot(oracle.unpack_int4(code_bytes).astype(np.int64), qv.astype(np.int64)))
+            assert dot == int(parts[4])
+            assert keys[0, 0] == float(parts[5])
+            continue
+        byte = np.array([int(parts[0], 16)], dtype=np.uint8)
+        got = oracle.unpack_int4(byte).tolist()
+        assert got == [int(parts[1]), int(parts[2])], (parts, got)
+
+
+def test_sketch_keys_exact_rational():
+    """key = dot * scale with no rounding: compared with exact rationals and a
+    per-bit brute-force decode of the nibbles."""
+    rng = np.random.default_rng(7)
+    B, T, nb = 2, 50, 16
+    codes = rng.integers(0, 256, size=(B, T, nb), dtype=np.uint8)
+    scale = rng.uniform(0.001, 3.0, size=(B, T)).astype(np.float16)
+    qs = rng.integers(-127, 128, size=(B, 2 * nb), dtype=np.int8)
+    keys = oracle.sketch_keys(qs, codes, scale, [T, T - 7], 3, 0, 5)
+    for b in range(B):
+        Tb = [T, T - 7][b]
+        for t in range(T):
+            if not (3 <= t < Tb - 5):
+                assert np.isnan(keys[b, t])
+                continue
+            dot = 0
+            for j in range(nb):
+                byte = int(codes[b, t, j])
+                for half in range(2):
+                    nib = (byte >> (4 * half)) & 0xF
+                    val = nib - 16 if nib & 0x8 else nib
+                    dot += val * int(qs[b, 2 * j + half])
+            exact = Fraction(dot) * Fraction(float(scale[b, t]))
+            assert Fraction(keys[b, t]) == exact
+
+
+def test_pooled_keys_exact_rational():
+    """Pooled scores equal the exact rational dot product (in-domain bf16 data)."""
+    g = torch.Generator().manual_seed(3)
+    qi = synth.flush_bf16_domain(torch.randn(1, 128, generator=g) * 3)
+    kp = synth.flush_bf16_domain(torch.randn(1, 20, 128, generator=g) * 5)
+    qi_b = qi.view(torch.int16).numpy().view(np.uint16)
+    kp_b = kp.view(torch.int16).numpy().view(np.uint16)
+    keys = oracle.pooled_keys(qi_b, kp_b, [4 * 17 + 2])
+    qf = qi.float().numpy()
+    kf = kp.float().numpy()
+    for blk in range(20):
+        if blk >= 17:
+            assert np.isnan(keys[0, blk])
+            continue
+        exact = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(qf[0], kf[0, blk]))
+        assert Fraction(keys[0, blk]) == exact
+
+
+# --------------------------------------------------------------------------
+# query sketch
+# --------------------------------------------------------------------------
+
+def _parse_sketch_case(ln):
+    kv = dict(p.split("=", 1) for p in ln.split()[1:])
+    G, D = int(kv["group"]), int(kv["D"])
+    cols = [int(c) for c in kv["cols"].split(",")]
+    qrows = [[float(x) for x in r.split(",")] for r in kv["q"].split(";")]
+    basis = np.zeros((1, D, len(cols)), dtype=np.float32)
+    for r, c in enumerate(cols):
+        basis[0, c, r] = 1.0
+    q = np.array(qrows, dtype=np.float16).reshape(1, G, D)
+    return q, basis, G, [int(x) for x in kv["expect"].split(",")]
+
+
+def test_query_sketch_fixture():
+    for ln in _lines("query_sketch.txt"):
+        q, basis, G, expect = _parse_sketch_case(ln)
+        qs, qscale = oracle.query_sketch(q, basis, G)
+        assert qs[0].tolist() == expect, ln
+        if all(e == 0 for e in expect):
+            assert qscale[0] == 0
+        else:
+            assert qscale[0] > 0
+
+
+def test_query_sketch_scale_invariance():
+    """Doubling the query doubles every fp32 intermediate exactly, so the int8
+    codes are unchanged and the scale doubles."""
+    c = synth.make_token_case(2, 64, n_kv=4, n_q=24, D=256, S=4, k=8, L=4, seed=11)
+    q = c.q.numpy()
+    qs1, sc1 = oracle.query_sketch(q, c.basis.numpy(), 6)
+    qs2, sc2 = oracle.query_sketch((q.astype(np.float32) * 2).astype(np.float16), c.basis.numpy(), 6)
+    assert np.array_equal(qs1, qs2)
+    assert np.array_equal(sc2, sc1 * 2)
+
+
+def test_query_sketch_projection_bound():
+    """The int8 code times its scale is within half a step of the fp64 projection
+    of the summed query (plus fp32 rounding)."""
+    c = synth.make_token_case(3, 64, n_kv=4, n_q=24, D=256, S=4, k=8, L=4, seed=12)
+    q = c.q.numpy().astype(np.float64)
+    bas = c.basis.numpy().astype(np.float64)
+    qs, sc = oracle.query_sketch(c.q.numpy(), c.basis.numpy(), 6)
+    for b in range(3):
+        qbar = q[b].reshape(4, 6, 256).sum(axis=1)
+        s = np.einsum("hd,hdr->hr", qbar, bas).reshape(-1)
+        err = np.abs(qs[b].astype(np.float64) * sc[b] - s)
+        assert np.max(err) <= 0.5 * sc[b] + 1e-4 * np.max(np.abs(s))
+        assert np.max(np.abs(qs[b])) == 127
+
+
+# --------------------------------------------------------------------------
+# selection
+# --------------------------------------------------------------------------
+
+def _brute_topk(keys, cand, k):
+    """Rank by counting: a candidate is kept iff fewer than k candidates beat
+    it (larger key, or equal key at a lower position)."""
+    keep = []
+    for c in cand:
+        beats = sum(1 for d in cand if keys[d] > keys[c] or (keys[d] == keys[c] and d < c))
+        if beats < k:
+            keep.append(c)
+    return keep
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_select_tokens_bruteforce(seed):
+    rng = np.random.default_rng(seed)
+    S, k, L = 3, 7, 5
+    for T in (0, 1, 14, 15, 16, 40, 64):
+        keys = rng.integers(-4, 5, size=T).astype(np.float64)   # many exact ties
+        got = oracle.select_tokens(keys, T, S, k, L)
+        if T <= S + k + L:
+            assert got.tolist() == list(range(T))
+            continue
+        mid = _brute_topk(keys, list(range(S, T - L)), k)
+        want = sorted(set(range(S)) | set(mid) | set(range(T - L, T)))
+        assert got.tolist() == want
+        assert len(got) == S + k + L
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_select_blocks_bruteforce(seed):
+    rng = np.random.default_rng(100 + seed)
+    kb = 5
+    for T in (0, 3, 20, 23, 24, 25, 26, 27, 61):
+        nb = T // 4
+        keys = rng.integers(-3, 4, size=max(nb, 1)).astype(np.float64)
+        got = oracle.select_blocks(keys, T, kb)
+        if nb <= kb:
+            assert got.tolist() == list(range(T))
+            continue
+        blocks = _brute_topk(keys, list(range(nb)), kb)
+        want = sorted({4 * b + i for b in blocks for i in range(4)} | set(range(4 * nb, T)))
+        assert got.tolist() == want
+
+
+def test_select_all_equal_keys():
+    """All keys equal: the tie rule keeps the first k candidates."""
+    T, S, k, L = 1000, 10, 50, 20
+    got = oracle.select_tokens(np.zeros(T), T, S, k, L)
+    assert got.tolist() == list(range(S + k)) + list(range(T - L, T))
+    gotb = oracle.select_blocks(np.ones(T // 4), T, 30)
+    assert gotb.tolist() == list(range(120))
+
+
+def test_dense_threshold_block_mode():
+    """[P4] "Why": selection starts once the context exceeds 4*block_topk+3 =
+    2051; above it exactly 2048 tokens of complete blocks are read."""
+    kb = 512
+    assert 4 * kb + 3 == 2051
+    for T in (1, 2048, 2050, 2051):
+        assert oracle.select_blocks(np.zeros(T // 4), T, kb).size == T
+    got = oracle.select_blocks(np.arange(2052 // 4, dtype=np.float64), 2052, kb)
+    assert got.size == 2048 and 0 not in got.tolist()   # exactly one block (the lowest-key one) dropped
+    for T in (2052, 2053, 3000, 3_000_001, 1_048_576):
+        nb = T // 4
+        got = oracle.select_blocks(np.zeros(nb), T, kb)
+        assert got.size == 2048 + T % 4      # budget does not grow with context
+
+
+def test_dense_threshold_token_mode():
+    """[P1] "The mechanism": top 2048 + 64 sinks + last 1024 (config shapes);
+    dense exactly while T <= S + k + L."""
+    for (S, k, L) in ((64, 2048, 1024), (16, 256, 128)):
+        thr = S + k + L
+        assert oracle.select_tokens(np.zeros(thr), thr, S, k, L).size == thr
+        for T in (thr + 1, thr + 2, 250_000):
+            assert oracle.select_tokens(np.zeros(T), T, S, k, L).size == thr
+    assert 64 + 2048 + 1024 == 3136 and 16 + 256 + 128 == 400
+
+
+def test_budget_fractions():
+    """[P1]: 2048 of 250K is ~0.8%; with sinks and tail ~1% of tokens are read."""
+    assert round(100 * 2048 / 250_000, 1) == 0.8
+    assert 1.0 <= 100 * 3136 / 250_000 < 1.5
+
+
+def test_needles_recovered_token_mode():
+    c = synth.make_token_case(1, 4096, n_kv=2, n_q=8, D=128, S=16, k=256, L=128,
+                              kv_format="f16", seed=1001)
+    c2 = synth.make_token_case(2, 40_000, n_kv=4, n_q=24, D=256, S=64, k=2048, L=1024,
+                               kv_format="i8", seed=1002)
+    for case in (c, c2):
+        qs, _ = oracle.query_sketch(case.q.numpy(), case.basis.numpy(), case.group)
+        keys = oracle.sketch_keys(qs, case.codes.numpy(), case.sk_scale.numpy(), case.lens,
+                                  case.S, case.k, case.L)
+        for b in range(case.B):
+            sel = oracle.select_tokens(keys[b], case.lens[b], case.S, case.k, case.L)
+            assert len(case.needles[b]) == 8
+            assert np.isin(case.needles[b].numpy(), sel).all()
+
+
+def test_needles_recovered_block_mode():
+    c = synth.make_block_case(1, 65_536, n_kv=2, n_q=16, D=256, k=512, seed=1003)
+    keys = oracle.pooled_keys(c.qi.view(torch.int16).numpy(), c.kp.view(torch.int16).numpy(), c.lens)
+    sel = oracle.select_blocks(keys[0], c.lens[0], c.k)
+    for blk in c.needles[0].tolist():
+        assert all(t in set(sel.tolist()) for t in range(4 * blk, 4 * blk + 4))
+
+
+# --------------------------------------------------------------------------
+# attention
+# --------------------------------------------------------------------------
+
+def _small_token_case(kv_format="i8", T=300, seed=5):
+    return synth.make_token_case(2, T, [T, T - 37], n_kv=2, n_q=6, D=64, S=4, k=1000, L=8,
+                                 kv_format=kv_format, n_needles=0, seed=seed)
+
+
+@pytest.mark.parametrize("fmt", ["i8", "f16"])
+def test_attention_matches_torch_sdpa(fmt):
+    """Dense decode attention equals torch's fp64 scaled_dot_product_attention."""
+    c = _small_token_case(fmt)
+    ks = None if c.k_scale is None else c.k_scale.numpy()
+    vs = None if c.v_scale is None else c.v_scale.numpy()
+    sm = 64 ** -0.5
+    for b in range(c.B):
+        T = c.lens[b]
+        got = oracle.dense_attention(c.q[b].numpy(), c.k_cache[b].numpy(), c.v_cache[b].numpy(),
+                                     None if ks is None else ks[b], None if vs is None else vs[b],
+                                     T, sm, c.group, fmt)
+        kd = c.k_cache[b, :T].double()
+        vd = c.v_cache[b, :T].double()
+        if fmt == "i8":
+            kd = kd * c.k_scale[b, :T].double().unsqueeze(-1)
+            vd = vd * c.v_scale[b, :T].double().unsqueeze(-1)
+        kk = kd.permute(1, 0, 2).repeat_interleave(c.group, dim=0)   # [H_q][T][D]
+        vv = vd.permute(1, 0, 2).repeat_interleave(c.group, dim=0)
+        qq = c.q[b].double().unsqueeze(1)                             # [H_q][1][D]
+        ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, scale=sm)[:, 0]
+        np.testing.assert_allclose(got, ref.numpy(), rtol=0, atol=1e-12)
+
+
+def test_attention_special_cases():
+    c = _small_token_case("i8")
+    k, v = c.k_cache[0].numpy(), c.v_cache[0].numpy()
+    ks, vs = c.k_scale[0].numpy(), c.v_scale[0].numpy()
+    # one selected row -> the output is that row of V, exactly
+    out = oracle.sparse_attention(c.q[0].numpy(), k, v, ks, vs, [123], 0.125, c.group, "i8")
+    vrow = v[123].astype(np.float64) * vs[123].astype(np.float64)[:, None]
+    for j in range(c.n_q):
+        assert np.array_equal(out[j], vrow[j // c.group])
+    # zero query -> uniform weights -> mean of the selected V rows
+    idx = np.array([3, 50, 51, 200])
+    out = oracle.sparse_attention(np.zeros_like(c.q[0].numpy()), k, v, ks, vs, idx, 0.125, c.group, "i8")
+    vd = v[idx].astype(np.float64) * vs[idx].astype(np.float64)[..., None]
+    for j in range(c.n_q):
+        np.testing.assert_allclose(out[j], vd[:, j // c.group].mean(axis=0), rtol=0, atol=1e-15)
+    # nothing selected -> zeros
+    out = oracle.sparse_attention(c.q[0].numpy(), k, v, ks, vs, [], 0.125, c.group, "i8")
+    assert not out.any()
+
+
+@pytest.mark.parametrize("fmt", ["i8", "f16"])
+def test_dense_equals_sparse_bitwise(fmt):
+    """North-star check 1: with a budget no smaller than the context, the
+    selected-row attention equals dense attention bit for bit."""
+    c = _small_token_case(fmt, T=500)
+    qs, qsc = oracle.query_sketch(c.q.numpy(), c.basis.numpy(), c.group)
+    keys = oracle.sketch_keys(qs, c.codes.numpy(), c.sk_scale.numpy(), c.lens, c.S, c.k, c.L)
+    ks = None if c.k_scale is None else c.k_scale.numpy()
+    vs = None if c.v_scale is None else c.v_scale.numpy()
+    for b in range(c.B):
+        T = c.lens[b]
+        assert c.k >= T - c.S - c.L
+        idx = oracle.select_tokens(keys[b], T, c.S, c.k, c.L)
+        sp = oracle.sparse_attention(c.q[b].numpy(), c.k_cache[b].numpy(), c.v_cache[b].numpy(),
+                                     None if ks is None else ks[b], None if vs is None else vs[b],
+                                     idx, 0.125, c.group, fmt)
+        de = oracle.dense_attention(c.q[b].numpy(), c.k_cache[b].numpy(), c.v_cache[b].numpy(),
+                                    None if ks is None else ks[b], None if vs is None else vs[b],
+                                    T, 0.125, c.group, fmt)
+        assert np.array_equal(sp, de)
+    # the same in block mode (budget 600 blocks >= T/4)
+    cb = synth.make_block_case(1, 2000, n_kv=2, n_q=4, D=64, k=600, n_needles=0, seed=9)
+    keys = oracle.pooled_keys(cb.qi.view(torch.int16).numpy(), cb.kp.view(torch.int16).numpy(), cb.lens)
+    idx = oracle.select_blocks(keys[0], 2000, 600)
+    kb = cb.k_cache[0].view(torch.int16).numpy()
+    vb = cb.v_cache[0].view(torch.int16).numpy()
+    qb = cb.q[0].view(torch.int16).numpy()
+    sp = oracle.sparse_attention(qb, kb, vb, None, None, idx, 0.1, 2, "bf16")
+    de = oracle.dense_attention(qb, kb, vb, None, None, 2000, 0.1, 2, "bf16")
+    assert np.array_equal(sp, de)
+
+
+# --------------------------------------------------------------------------
+# byte closed forms
+# --------------------------------------------------------------------------
+
+def test_byte_closed_forms():
+    # [P3], [P4] "Why": 2048 selected x 2 KV heads x 256 x (K and V) x 2 B = 4 MiB/layer, 48 MiB/token
+    assert oracle.kv_gather_bytes(2048, 2, 256, 2) == 4 * MiB
+    assert 12 * oracle.kv_gather_bytes(2048, 2, 256, 2) == 48 * MiB
+    # [P3]: 2,048 B per token per QSA layer; 512 MiB per layer at 262,144 tokens; 6 GiB for 12
+    assert oracle.kv_gather_bytes(1, 2, 256, 2) == 2048
+    assert 262_144 * 2048 == 512 * MiB and 12 * 512 * MiB == 6 * 1024 * MiB
+    # [P4] "What Needs to Stay in VRAM": pooled keys 128 x 2 B per block -> 64 MiB/layer at 1 Mi tokens
+    assert oracle.block_scan_bytes(1_048_576 // 4, 128) == 64 * MiB
+    # [P3]: pooled key 64 B per token + 2 B slot = 66 B per token per layer
+    assert oracle.block_scan_bytes(1, 128) // 4 == 64 and 64 + 2 == 66
+    # [P4] intro / "What Needs to Stay in VRAM": 27.75 KiB/token = 27.00 in RAM + 0.75 in VRAM (12 layers)
+    assert 12 * (2048 + 256 + 64) == 27.75 * KiB
+    assert 12 * (2048 + 256) == 27.00 * KiB and 12 * 64 == 0.75 * KiB
+    # [P1] "The mechanism": int4 sketch ~2.1 KB per token over 16 layers
+    per_layer = oracle.token_scan_bytes(1, 4, 64)
+    assert per_layer == 130 and 16 * per_layer == 2080
+    assert 0.52e9 <= 250_000 * 16 * per_layer <= 0.53e9            # "0.53 int4 sketch" GB/agent
+    # [P1]: 272 B per token-head at int4; 4.4 GB per 250K agent (16 layers x 4 KV heads)
+    assert oracle.host_record_bytes(256) == 272
+    assert round(250_000 * 16 * 4 * 272 / 1e9, 1) == 4.4
+    # the per-step K/V budget does not depend on context length ([P4] "Why")
+    for T in (2052, 100_000, 3_000_000):
+        n = oracle.select_blocks(np.zeros(T // 4), T - T % 4, 512).size
+        assert oracle.kv_gather_bytes(n, 2, 256, 2) == 4 * MiB
+
+
+# --------------------------------------------------------------------------
+# host tier
+# --------------------------------------------------------------------------
+
+def test_host_dequant_fixture():
+    lines = list(_lines("host_dequant.txt"))
+    scales = [float(x) for x in lines[0].split()[1].split(",")]
+    sprime = float(lines[1].split()[1])
+    D = 128
+    codes = np.zeros(D, dtype=np.int8)
+    expect = np.zeros(D, dtype=np.int8)
+    for ln in lines[2:]:
+        i, cc, e = (int(x) for x in ln.split())
+        codes[i], expect[i] = cc, e
+    row = np.concatenate([synth.pack_int4(torch.from_numpy(codes)).numpy(),
+                          np.array(scales, dtype=np.float16).view(np.uint8)])
+    r8, sp = oracle.host_row_dequant(row, D)
+    assert float(sp) == sprime
+    assert r8.tolist() == expect.tolist()
+
+
+def test_host_dequant_invariants():
+    rng = np.random.default_rng(4)
+    D = 256
+    for _ in range(200):
+        codes = rng.integers(-8, 8, size=D).astype(np.int8)
+        gs = rng.uniform(0, 2, size=D // 64).astype(np.float16)
+        row = np.concatenate([synth.pack_int4(torch.from_numpy(codes)).numpy(), gs.view(np.uint8)])
+        r8, sp = oracle.host_row_dequant(row, D)
+        assert np.all(np.abs(r8.astype(int)) <= 127)
+        for g in range(D // 64):
+            c = codes[64 * g:64 * g + 64].astype(int)
+            r = r8[64 * g:64 * g + 64].astype(int)
+            order = np.argsort(c, kind="stable")
+            assert np.all(np.diff(r[order]) >= 0)          # monotone in the code
+            assert np.all(np.sign(r) * np.sign(c) >= 0)     # sign preserved
+
+
+def test_clock_fixture():
+    lines = list(_lines("clock_trace.txt"))
+    n = int(lines[0].split()[1])
+    tier = oracle.ClockTier(n, 100, window=1)
+    for ln in lines[1:]:
+        if ln.startswith("final"):
+            assert tier.pos.tolist() == [int(x) for x in ln.split()[1:]]
+            continue
+        s, picks, slots, hits, misses = (p.strip() for p in ln.split("|"))
+        picks = np.array(sorted(int(x) for x in picks.split()))
+        got, h, m = tier.step(picks, int(s))
+        assert got.tolist() == [int(x) for x in slots.split()], ln
+        assert (h, m) == (int(hits), int(misses))
+
+
+def test_clock_invariants_drifting_workload():
+    T, S, L, k = 60_000, 64, 1024, 512
+    picks = synth.drift_picks(1, T, S, L, k, 60, seed=77, window=8192, sigma_c=128)
+    n_slots = 1500
+    tier = oracle.ClockTier(n_slots, T, window=1)
+    for s in range(picks.shape[0]):
+        before = tier.pos.copy()
+        last_before = tier.last.copy()
+        slots, h, m = tier.step(picks[s, 0], s)
+        assert h + m == k
+        assert np.all(tier.pos[slots] == picks[s, 0])            # every pick resident
+        assert len(set(slots.tolist())) == k
+        occ = tier.pos[tier.pos >= 0]
+        assert occ.size <= n_slots and np.unique(occ).size == occ.size
+        # a slot used in the previous step (outside the W=1 window now) may be
+        # evicted, but never one that a hit of this step used
+        evicted = (before >= 0) & (tier.pos != before)
+        assert np.all(last_before[evicted] < s)
+        # slots used this step by hits are never the victims of this step's misses
+        hit_slots = slots[np.isin(picks[s, 0], before)]
+        assert np.all(tier.pos[hit_slots] == before[hit_slots])
+
+
+@pytest.mark.slow
+def test_drift_miss_rate_matches_pages():
+    """[P1] "The mechanism": misses run at 14-16% with a 2.5% hot buffer.  The
+    drifting-locality workload is calibrated so the oracle's CLOCK sees ~15%."""
+    T, S, L, k = 250_000, 64, 1024, 2048
+    picks = synth.drift_picks(1, T, S, L, k, 192, seed=1005)
+    tier = oracle.ClockTier(int(0.025 * T), T, window=1)
+    misses = picks_total = 0
+    for s in range(picks.shape[0]):
+        _, h, m = tier.step(picks[s, 0], s)
+        if s >= 64:
+            misses += m
+            picks_total += h + m
+    rate = misses / picks_total
+    assert 0.13 <= rate <= 0.17, rate
