@@ -1,0 +1,265 @@
+"""Benchmark of the sparse-KV decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config cfg2]
+
+A step is one layer-step: score (query sketch + sketch scan), select and
+attend for the whole batch of one attention layer, through the C ABI
+(sparsekv_step).  The default workload is 8 sequences x 250,000 tokens, 4 KV
+heads x 24 query heads, head_dim 256, int4 rank-64 sketch, int8 K/V, keep
+top-2048 + 64 sinks + 1024 tail.  Layers rotate over distinct buffers so the
+scanned bytes come from HBM, not the 256 MB Infinity Cache.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+import top_sparse_kv_amd as skv  # noqa: E402
+
+METRIC = "sparse decode layer-steps/s at 250K ctx; achieved HBM GB/s vs MI355X peak"
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print("[bench %.1fs]" % (time.monotonic() - T0), *a, file=sys.stderr, flush=True)
+
+
+T0 = time.monotonic()
+
+CONFIGS = {
+    "cfg2": dict(kind="token", B=8, T=250_000, n_kv=4, n_q=24, D=256, S=64, k=2048, L=1024,
+                 kv="i8", layers=8, seed=1002,
+                 workload="8 seq x 250,000 tokens; 4 KV x 24 q heads, head_dim 256; int4 rank-64 "
+                          "sketch; int8 K/V + fp16 row scales; top-2048 + 64 sinks + 1024 tail"),
+    "cfg4a": dict(kind="token", B=32, T=131_072, n_kv=4, n_q=24, D=256, S=64, k=2048, L=1024,
+                  kv="i8", layers=4, seed=1004,
+                  workload="32 seq x 131,072 tokens; cfg2 layer shape"),
+    "cfg3": dict(kind="block", B=1, T=1_048_576, n_kv=2, n_q=16, D=256, k=512, layers=12,
+                 seed=1003,
+                 workload="1 seq x 1,048,576 tokens; 12 QSA layers; 2 KV x 16 q heads, head_dim "
+                          "256, bf16 K/V; 128-d bf16 pooled key per 4-token block; top-512 blocks"),
+}
+
+
+class Layer:
+    """Device buffers of one layer plus the output buffers of its step."""
+
+    def __init__(self, cfg, li):
+        self.cfg = cfg
+        seed = cfg["seed"] + 7919 * li
+        if cfg["kind"] == "token":
+            c = synth.make_token_case(cfg["B"], cfg["T"], n_kv=cfg["n_kv"], n_q=cfg["n_q"],
+                                      D=cfg["D"], S=cfg["S"], k=cfg["k"], L=cfg["L"],
+                                      kv_format=cfg["kv"], seed=seed, device="cuda")
+            self.desc = skv.token_desc(c.B, c.T_max, c.n_kv, c.n_q, c.D, topk=c.k, n_sink=c.S,
+                                       n_tail=c.L,
+                                       kv_dtype=skv.SKV_KV_I8_ROWSCALE if cfg["kv"] == "i8" else skv.SKV_KV_F16)
+            self.q, self.basis = c.q, c.basis
+            self.ikeys, self.iscale, self.iq = c.codes, c.sk_scale, None
+            self.kv = skv.kv_view(c.k_cache, c.v_cache, c.k_scale, c.v_scale)
+            self.qs = torch.zeros((c.B, c.n_kv * c.R), dtype=torch.int8, device="cuda")
+            self.qsc = torch.zeros((c.B,), dtype=torch.float32, device="cuda")
+            self.keys = torch.zeros((c.B, c.T_max), dtype=torch.float64, device="cuda")
+        else:
+            c = synth.make_block_case(cfg["B"], cfg["T"], n_kv=cfg["n_kv"], n_q=cfg["n_q"],
+                                      D=cfg["D"], k=cfg["k"], seed=seed, device="cuda")
+            self.desc = skv.block_desc(c.B, c.T_max, c.n_kv, c.n_q, c.D, topk_blocks=c.k)
+            self.q, self.basis = c.q, None
+            self.ikeys, self.iscale, self.iq = c.kp, None, c.qi
+            self.kv = skv.kv_view(c.k_cache, c.v_cache)
+            self.qs = self.qsc = None
+            self.keys = torch.zeros((c.B, c.T_max // 4), dtype=torch.float64, device="cuda")
+        self.case = c
+        self.ctx = c.ctx_len
+        cap = skv.select_capacity(self.desc)
+        self.idx = torch.zeros((c.B, cap), dtype=torch.int32, device="cuda")
+        self.nsel = torch.zeros((c.B,), dtype=torch.int32, device="cuda")
+        self.out = torch.zeros((c.B, c.n_q, c.D), dtype=torch.float32, device="cuda")
+        self.sm = c.D ** -0.5
+
+    def step(self, ws):
+        skv.step(self.desc, self.ctx, self.q, self.basis, self.qs, self.qsc, self.iq, self.ikeys,
+                 self.iscale, self.keys, self.kv, self.idx, self.nsel, self.sm, self.out, ws)
+
+    def qsketch(self, ws):
+        skv.qsketch(self.desc, self.q, self.basis, self.qs, self.qsc, ws)
+
+    def score(self, ws):
+        iq = self.qs if self.iq is None else self.iq
+        skv.score(self.desc, self.ctx, iq, self.ikeys, self.iscale, self.keys, ws)
+
+    def topk(self, ws):
+        skv.topk(self.desc, self.ctx, self.keys, self.idx, self.nsel, ws)
+
+    def attend(self, ws):
+        skv.attend(self.desc, self.q, self.kv, self.idx, self.nsel, self.sm, self.out, ws)
+
+
+def algorithmic_bytes(cfg):
+    """Bytes the method must move per layer-step (what each stage reads/writes
+    at minimum): the scan, the gathered K/V rows (+ row scales), q, out."""
+    B, D, n_kv, n_q = cfg["B"], cfg["D"], cfg["n_kv"], cfg["n_q"]
+    if cfg["kind"] == "token":
+        n_cand = cfg["T"] - cfg["S"] - cfg["L"]
+        scan = B * n_cand * (n_kv * 64 // 2 + 2)
+        n_sel = cfg["S"] + cfg["k"] + cfg["L"]
+        eb, sb = (1, 2) if cfg["kv"] == "i8" else (2, 0)
+        gather = B * n_sel * n_kv * (D * eb + sb) * 2
+        basis = n_kv * D * 64 * 4
+    else:
+        scan = B * (cfg["T"] // 4) * 128 * 2
+        n_sel = 4 * cfg["k"]
+        gather = B * n_sel * n_kv * D * 2 * 2
+        basis = 0
+    qbytes = B * n_q * D * 2
+    out = B * n_q * D * 4
+    return dict(scan=scan, gather=gather, other=qbytes + out + basis,
+                total=scan + gather + qbytes + out + basis)
+
+
+def time_loop(fn, layers, ws, n):
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for i in range(n):
+        fn(layers[i % len(layers)], ws)
+    e1.record(st)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / 1e3   # seconds
+
+
+def cpu_baseline(layer: Layer, cfg):
+    """The CPU oracle timed on the host cores on one full layer-step of layer 0
+    (all sequences of the batch): query sketch, exact keys, selection and
+    attention.  Data movement to the host is not timed."""
+    import oracle
+    c = layer.case
+    t_total = 0.0
+    if cfg["kind"] == "token":
+        q = c.q.cpu().numpy()
+        basis = c.basis.cpu().numpy()
+        codes = c.codes.cpu().numpy()
+        sks = c.sk_scale.cpu().numpy()
+        t = time.perf_counter()
+        qs, _ = oracle.query_sketch(q, basis, c.group)
+        keys = oracle.sketch_keys(qs, codes, sks, c.lens, c.S, c.k, c.L)
+        sels = [oracle.select_tokens(keys[b], c.lens[b], c.S, c.k, c.L) for b in range(c.B)]
+        t_total += time.perf_counter() - t
+        for b in range(c.B):
+            ii = torch.from_numpy(sels[b]).cuda()
+            kr = c.k_cache[b].index_select(0, ii).cpu().numpy()
+            vr = c.v_cache[b].index_select(0, ii).cpu().numpy()
+            ks = c.k_scale[b].index_select(0, ii).cpu().numpy()
+            vs = c.v_scale[b].index_select(0, ii).cpu().numpy()
+            t = time.perf_counter()
+            oracle.sparse_attention(q[b], kr, vr, ks, vs, np.arange(sels[b].size), layer.sm,
+                                    c.group, "i8")
+            t_total += time.perf_counter() - t
+        sample = "one full layer-step of layer 0: %d sequences x %d tokens" % (c.B, c.T_max)
+    else:
+        def bits(x):
+            return x.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+        qi, kp, q = bits(c.qi), bits(c.kp), bits(c.q)
+        t = time.perf_counter()
+        keys = oracle.pooled_keys(qi, kp, c.lens)
+        sel = oracle.select_blocks(keys[0], c.lens[0], c.k)
+        t_total += time.perf_counter() - t
+        ii = torch.from_numpy(sel).cuda()
+        kr = bits(c.k_cache[0].index_select(0, ii))
+        vr = bits(c.v_cache[0].index_select(0, ii))
+        t = time.perf_counter()
+        oracle.sparse_attention(q[0], kr, vr, None, None, np.arange(sel.size), layer.sm, c.group, "bf16")
+        t_total += time.perf_counter() - t
+        sample = "one full layer-step of layer 0 (1 sequence x %d tokens)" % c.T_max
+    return dict(value=1.0 / t_total, unit="layer-steps/s", cores=1, kind="oracle", sample=sample,
+                seconds=t_total)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--config", default="cfg2", choices=sorted(CONFIGS))
+    ap.add_argument("--layers", type=int, default=0, help="rotating layer buffers (0 = config default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cfg = CONFIGS[args.config]
+    n_layers = args.layers or cfg["layers"]
+    log("generating %d layers of %s" % (n_layers, args.config))
+    layers = [Layer(cfg, li) for li in range(n_layers)]
+    torch.cuda.synchronize()
+    ws = skv.workspace(layers[0].desc)
+    log("warmup", args.warmup)
+    for i in range(args.warmup):
+        layers[i % n_layers].step(ws)
+    skv.check(ws)
+    log("timing %d layer-steps" % args.steps)
+    secs = time_loop(Layer.step, layers, ws, args.steps)
+    skv.check(ws)
+    nk = max(50, args.steps // 2)
+    kt = {}
+    for name in (["qsketch"] if cfg["kind"] == "token" else []) + ["score", "topk", "attend"]:
+        fn = getattr(Layer, name)
+        for i in range(5):
+            fn(layers[i % n_layers], ws)
+        kt[name] = time_loop(fn, layers, ws, nk) / nk
+    skv.check(ws)
+    ab = algorithmic_bytes(cfg)
+    value = args.steps / secs
+    score_s = kt["score"]
+    roof = dict(kernel="score_sketch" if cfg["kind"] == "token" else "score_pooled", bound="hbm",
+                achieved=round(ab["scan"] / score_s / 1e9, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                frac=round(ab["scan"] / score_s / 1e9 / PEAK_HBM_GBS, 4), traffic=None,
+                bytes_per_launch=ab["scan"], avg_launch_us=round(score_s * 1e6, 2))
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "layer-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * secs / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8" if cfg["kind"] == "token" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg["workload"], "name": args.config, "batch": cfg["B"],
+                   "ctx": cfg["T"], "rotating_layers": n_layers},
+        "step_hbm": {"algorithmic_bytes": ab["total"], "achieved_GBps": round(ab["total"] * value / 1e9, 1),
+                     "frac_of_peak": round(ab["total"] * value / 1e9 / PEAK_HBM_GBS, 4)},
+        "kernels_us": {k: round(v * 1e6, 2) for k, v in kt.items()},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cb = cpu_baseline(layers[0], cfg)
+        res["cpu_baseline"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in cb.items()}
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,300 @@
+/*
+ * sparsekv.h -- C ABI of the MI355X (gfx950) sparse-KV decode step.
+ *
+ * One decode step of one attention layer, for a batch of sequences, in three
+ * stages (page "8 agents x 250K context on two 3090s: sparse KV decode with a
+ * rank-64 key sketch and a host-RAM tier", section "The mechanism"; page
+ * "3.14M Context on 3x 3090: The Power of an Architecture That Puts KV Cache
+ * in Host RAM", sections "Why" and "What Needs to Stay in VRAM"):
+ *
+ *   score   a cheap indexer scores every past token through a rank-64 int4
+ *           key sketch (token mode) or every complete 4-token block through
+ *           a mean-pooled 128-dim bf16 indexer key (block mode);
+ *   select  a deterministic top-k keeps the best `topk` tokens (or blocks),
+ *           one pick per layer shared by all KV heads, joined with the sink
+ *           tokens and the recent tail (token mode) or the trailing partial
+ *           block (block mode); short sequences are attended densely;
+ *   attend  exact GQA softmax attention over only the selected K/V rows.
+ *
+ * plus an optional host-RAM KV tier: K/V stored at int4 in pinned host
+ * memory, read zero-copy by the GPU for the picked rows that miss a GPU hot
+ * buffer (2.5% of tokens, windowed CLOCK), turned back into int8 rows on fetch.
+ *
+ * Conventions shared by every call:
+ *  - All array arguments are DEVICE pointers unless stated otherwise, owned by
+ *    the caller, and must stay valid until the enqueued work has finished.
+ *    The library keeps no pointer after a step call returns.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Step
+ *    calls (qsketch, score, topk, attend, step, tier_resolve) only enqueue
+ *    kernels on that stream: they never synchronize, never allocate and never
+ *    record a memset, so they can be captured into a HIP graph.
+ *  - Errors found on the host (bad descriptor, NULL pointer, workspace too
+ *    small) return a status and enqueue nothing; sparsekv_last_error() gives
+ *    a thread-local message.  A failed kernel launch returns SKV_ERR_HIP.
+ *    Conditions only visible on the device (a ctx_len outside [0, max_ctx],
+ *    an index outside its array) are clamped or skipped by the kernels and
+ *    recorded as flag bits in the workspace; sparsekv_check() reads them.
+ *  - Calls are reentrant with distinct workspaces.  Two calls that share a
+ *    workspace, or a tier handle, must be ordered on one stream.
+ */
+#ifndef SPARSEKV_H
+#define SPARSEKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPARSEKV_ABI_VERSION 1
+
+typedef int32_t skv_status;
+enum {
+  SKV_OK = 0,
+  SKV_ERR_INVALID = 1,      /* bad argument or descriptor */
+  SKV_ERR_UNSUPPORTED = 2,  /* valid but not implemented (shape/dtype) */
+  SKV_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than sparsekv_workspace_size */
+  SKV_ERR_OOM = 4,          /* device or host allocation failed (tier_create only) */
+  SKV_ERR_HIP = 5,          /* a HIP runtime call or kernel launch failed */
+  SKV_ERR_HOST_MEMORY = 6,  /* host records not pinned/mappable for device access */
+  SKV_ERR_STATE = 7,        /* device flags were raised (see sparsekv_check) */
+};
+
+/* index (scoring) modes */
+enum { SKV_INDEX_SKETCH_INT4 = 0, SKV_INDEX_POOLED_BF16 = 1 };
+/* K/V storage formats */
+enum { SKV_KV_I8_ROWSCALE = 0, SKV_KV_F16 = 1, SKV_KV_BF16 = 2 };
+/* query formats */
+enum { SKV_Q_F16 = 0, SKV_Q_BF16 = 1 };
+
+/* device flag bits reported by sparsekv_check */
+enum {
+  SKV_FLAG_CTX_RANGE = 1u << 0,    /* a ctx_len was < 0 or > max_ctx (clamped) */
+  SKV_FLAG_INDEX_RANGE = 1u << 1,  /* attend: an index outside [0, rows) or n_sel > cap (skipped/clamped) */
+  SKV_FLAG_TOPK_SLOW = 1u << 2,    /* informational: a sequence needed the exact slow select path */
+  SKV_FLAG_TIER_INPUT = 1u << 3,   /* tier: a pick outside [0, ctx) or unsorted input (skipped) */
+};
+
+/*
+ * Layer descriptor (plain old data).
+ *
+ * Token mode (index_mode = SKV_INDEX_SKETCH_INT4): block = 1, rank = 64 (any
+ * even value), topk = tokens kept from the middle range [n_sink, T - n_tail);
+ * a sequence is dense (all T tokens attended) when T <= n_sink + topk + n_tail.
+ *
+ * Block mode (index_mode = SKV_INDEX_POOLED_BF16): block = 4, index_dim = 128
+ * (any multiple of 8), topk = blocks kept; n_sink = n_tail = 0.  Only the
+ * floor(T/4) complete blocks are scored; the T mod 4 trailing tokens are
+ * always attended; dense when floor(T/4) <= topk, i.e. T <= 4*topk + 3.
+ *
+ * T = ctx_len[b] counts the tokens in the cache including the current one.
+ * Supported: head_dim in {128, 256}, n_q_heads / n_kv_heads in [1, 16],
+ * K/V int8 + fp16 row scale or fp16 (token mode), bf16 (block mode).
+ */
+typedef struct {
+  uint32_t struct_size;   /* sizeof(skv_layer_desc) */
+  int32_t batch;          /* sequences B */
+  int32_t max_ctx;        /* per-sequence capacity (row stride) of every [B][max_ctx]... array */
+  int32_t n_kv_heads;     /* H_kv */
+  int32_t n_q_heads;      /* H_q (multiple of H_kv) */
+  int32_t head_dim;       /* D */
+  int32_t index_mode;     /* SKV_INDEX_* */
+  int32_t rank;           /* R: sketch rank per KV head (token mode) */
+  int32_t index_dim;      /* pooled indexer key width (block mode) */
+  int32_t block;          /* 1 (token mode) or 4 (block mode) */
+  int32_t topk;           /* budget: tokens (token mode) or blocks (block mode) */
+  int32_t n_sink;         /* S */
+  int32_t n_tail;         /* L */
+  int32_t kv_dtype;       /* SKV_KV_* */
+  int32_t q_dtype;        /* SKV_Q_* */
+} skv_layer_desc;
+
+/* A view of K/V rows: element (b, row, h, d) of K is at
+ *   k + ((b * rows + row) * n_kv_heads + h) * head_dim + d
+ * (page "3.14M Context on 3x 3090 ...", section "No Need to Rewrite the
+ * Kernel": rows are addressed by (token * n_kv_heads + kv_head) * head_dim).
+ * Row scales (SKV_KV_I8_ROWSCALE only) are fp16 at (b * rows + row) * n_kv_heads + h. */
+typedef struct {
+  const void* k;
+  const void* v;
+  const uint16_t* k_scale;
+  const uint16_t* v_scale;
+  int64_t rows;           /* rows per sequence (max_ctx for the plain cache) */
+} skv_kv_view;
+
+/* ---- library ------------------------------------------------------------ */
+
+int sparsekv_abi_version(void);
+const char* sparsekv_status_str(skv_status s);
+/* Thread-local detail of the last error returned on this thread ("" if none). */
+const char* sparsekv_last_error(void);
+
+/* Validates a descriptor on the host.  SKV_OK, SKV_ERR_INVALID or SKV_ERR_UNSUPPORTED. */
+skv_status sparsekv_validate(const skv_layer_desc* d);
+
+/* Largest number of positions select can emit per sequence:
+ * n_sink + topk + n_tail (token mode) or 4*topk + 3 (block mode). */
+skv_status sparsekv_select_capacity(const skv_layer_desc* d, int32_t* cap);
+
+/* Device workspace bytes the step calls need for this descriptor.  The caller
+ * allocates it once, 256-byte aligned, zero-fills it once (its first word is
+ * the device flag word that sparsekv_check reads and clears; every other byte
+ * is initialised by the calls that use it) and passes it to every step call. */
+skv_status sparsekv_workspace_size(const skv_layer_desc* d, size_t* bytes);
+
+/* ---- stage A1: query sketch (token mode) ----------------------------------
+ * Page "8 agents x 250K ...", section "The mechanism": every token is scored
+ * through a rank-R projection onto a frozen basis, one pick per layer shared
+ * by the KV heads; the query side is an int8 vector.
+ *   q        [B][H_q][D] fp16
+ *   basis    [H_kv][D][R] fp32
+ *   qs       [B][H_kv*R] int8 out:  clamp(rint(s/qscale), +-127) where, per KV
+ *            head h, s_h = sum over d ascending of (qbar_h[d] * basis_h[d][r])
+ *            with qbar_h = sum of the G query heads of h in ascending order,
+ *            all in fp32 with separately rounded multiplies and adds;
+ *   qs_scale [B] fp32 out: max|s| / 127 (0 when the sketch is all zero). */
+skv_status sparsekv_qsketch(const skv_layer_desc* d, const void* q, const float* basis,
+                            int8_t* qs, float* qs_scale, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- stage A2: exact ranking keys -----------------------------------------
+ * Token mode (page "8 agents x 250K ...", section "The mechanism"):
+ *   index_query = qs [B][H_kv*R] int8; index_keys = int4 codes
+ *   [B][max_ctx][H_kv*R/2] uint8 (element 2j in the low nibble of byte j,
+ *   two's complement); index_scale = per-token fp16 scale [B][max_ctx];
+ *   keys[b][t] = (double)(sum_i qs[i]*code_t[i]) * (double)scale_t  (exact)
+ *   for every middle token t in [n_sink, T - n_tail); keys is [B][max_ctx].
+ * Block mode (page "3.14M Context ...", sections "Why", "What Needs to Stay in
+ * VRAM"): index_query = [B][index_dim] bf16; index_keys = pooled keys
+ *   [B][max_ctx/4][index_dim] bf16; index_scale = NULL;
+ *   keys[b][j] = sum_i q[i]*kp_j[i] accumulated in fp64 for every complete
+ *   block j < floor(T/4); keys is [B][max_ctx/4].  The sum is exact (hence
+ *   identical to any other evaluation order) when every bf16 input is 0 or of
+ *   magnitude in [2^-8, 2^8).
+ * Other entries of keys are not written.  -0 is written as +0. */
+skv_status sparsekv_score(const skv_layer_desc* d, const int32_t* ctx_len,
+                          const void* index_query, const void* index_keys,
+                          const uint16_t* index_scale, double* keys,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* ---- stage A3: deterministic top-k + sinks/tail ---------------------------
+ * Pages: "8 agents x 250K ...", section "The mechanism" (deterministic top-k,
+ * sinks, tail, dense/sparse switch); "3.14M Context ...", section "Why" (dense
+ * until the context exceeds 4*block_topk+3, then exactly the budget).
+ * Keeps the `topk` candidates with the largest keys, equal keys going to the
+ * lower position, and writes for each sequence the ascending unique token
+ * positions to attend:
+ *   token mode: [0, S) + top-k of [S, T-L) + [T-L, T), or [0, T) when dense;
+ *   block mode: the 4 tokens of each kept block + [4*floor(T/4), T), or [0, T).
+ *   idx   [B][cap] int32 out (cap from sparsekv_select_capacity; entries past
+ *         n_sel[b] are unspecified); n_sel [B] int32 out. */
+skv_status sparsekv_topk(const skv_layer_desc* d, const int32_t* ctx_len, const double* keys,
+                         int32_t* idx, int32_t* n_sel, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- stage A4: exact GQA attention over the selected rows -----------------
+ * Page "8 agents x 250K ...", section "The mechanism" (exact attention on the
+ * kept tokens); page "3.14M Context ...", section "No Need to Rewrite the
+ * Kernel" (gather by row offset).
+ *   q    [B][H_q][D] fp16 (bf16 for bf16 K/V)
+ *   kv   rows to gather from; idx [B][cap] row indices, n_sel [B] counts
+ *   out  [B][H_q][D] fp32: for query head j of KV head h = j / (H_q/H_kv),
+ *        softmax over the n_sel rows of (q_j . k_row) * sm_scale, times V;
+ *        K/V int8 rows are code * fp16 row scale.  n_sel = 0 gives zeros. */
+skv_status sparsekv_attend(const skv_layer_desc* d, const void* q, const skv_kv_view* kv,
+                           const int32_t* idx, const int32_t* n_sel, float sm_scale, float* out,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* ---- the whole step --------------------------------------------------------
+ * A1..A4 in one call (token mode: basis, qs, qs_scale used; block mode: they
+ * may be NULL and index_query is the bf16 indexer query).  keys, idx, n_sel
+ * are written as by the separate calls. */
+skv_status sparsekv_step(const skv_layer_desc* d, const int32_t* ctx_len, const void* q,
+                         const float* basis, int8_t* qs, float* qs_scale,
+                         const void* index_query, const void* index_keys,
+                         const uint16_t* index_scale, double* keys,
+                         const skv_kv_view* kv, int32_t* idx, int32_t* n_sel,
+                         float sm_scale, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Synchronizes `stream`, returns the device flag bits raised since the last
+ * check in *flags (may be NULL) and clears them.  SKV_ERR_STATE if any bit
+ * other than SKV_FLAG_TOPK_SLOW was set.  Not capturable. */
+skv_status sparsekv_check(void* ws, size_t ws_bytes, void* stream, uint32_t* flags);
+
+/* ---- host-RAM tier (optional) ----------------------------------------------
+ * Page "8 agents x 250K ...", section "The mechanism": K/V of every token sit
+ * in pinned host RAM at int4 (64-dim groups, fp16 group scales, 272 B per
+ * token-head at head_dim 256); the GPU keeps the sketch, the sinks, the tail
+ * and a hot buffer of 2.5% of the tokens under windowed CLOCK; misses read only
+ * the picked rows over PCIe and are turned back into int8 rows.  Page "3.14M
+ * Context ...", section "No Need to Rewrite the Kernel": zero-copy access to
+ * mapped host memory needs no per-layer host synchronization.
+ *
+ * Host record of token t, KV head h (record bytes = 2 * (D/2 + 2*D/64)):
+ *   K: D/2 bytes of int4 codes (low nibble first) then D/64 fp16 group scales,
+ *   V: the same; records are [B][ctx][H_kv][record] token-major.
+ * Fetch turns a row into int8 with one fp16 scale s' = fp16(gmax*7/127),
+ * gmax the largest group scale, and r8 = clamp(rint(c*g / s'), +-127), each
+ * operation one fp32 IEEE operation (c*g and gmax*7 are exact).
+ *
+ * Resident rows per sequence (an skv_kv_view, int8 + fp16 row scales):
+ *   [0, S) sinks, [S, S+L) tail (position T-L+i), [S+L, S+L+n_slots) hot slots.
+ * The caller loads sinks and tail once with sparsekv_tier_load_resident.
+ *
+ * Windowed CLOCK, per sequence and step s: picked tokens already in the hot
+ * buffer are hits (ref=1, last=s); the misses, in ascending position order,
+ * each take the first slot the hand reaches that is empty, or unused for the
+ * last W steps (last <= s-W) and unreferenced -- a referenced slot outside
+ * the window has its reference cleared as the hand passes it. */
+typedef struct skv_tier skv_tier;
+
+typedef struct {
+  uint32_t struct_size;   /* sizeof(skv_tier_desc) */
+  skv_layer_desc layer;   /* token mode, SKV_KV_I8_ROWSCALE */
+  int32_t ctx;            /* tokens stored per sequence (T) */
+  int32_t n_slots;        /* hot slots per sequence; must exceed topk */
+  int32_t window;         /* W >= 1 */
+  void* host_records;     /* NULL: the library allocates pinned, device-mapped
+                             host memory; otherwise caller memory that is
+                             already pinned and mapped (e.g. hipHostMalloc) */
+} skv_tier_desc;
+
+typedef struct {
+  int64_t steps;          /* resolve calls */
+  int64_t picks;          /* middle positions resolved (sum over sequences) */
+  int64_t hits;
+  int64_t misses;
+  int64_t host_bytes;     /* bytes read from host memory = misses * H_kv * record */
+} skv_tier_stats;
+
+/* Allocates the tier (device slot state + resident rows; host records unless
+ * given).  Host call, synchronous.  SKV_ERR_OOM / SKV_ERR_HOST_MEMORY on failure. */
+skv_status sparsekv_tier_create(const skv_tier_desc* d, skv_tier** out);
+/* Host pointer of the host records (the caller fills them before resolving). */
+void* sparsekv_tier_host_records(skv_tier* t);
+/* Device view of the resident rows. */
+skv_status sparsekv_tier_resident(skv_tier* t, skv_kv_view* view);
+/* Copies the caller's sink+tail rows ([B][S+L][H_kv][D] int8 and
+ * [B][S+L][H_kv] fp16 scales, device) into resident rows [0, S+L). */
+skv_status sparsekv_tier_load_resident(skv_tier* t, const int8_t* k, const int8_t* v,
+                                       const uint16_t* k_scale, const uint16_t* v_scale,
+                                       void* stream);
+/* One step: for each sequence, resolves the selected positions idx[b][0..n_sel)
+ * (ascending) against the hot buffer, fetches the misses from host memory into
+ * their slots, and writes rows[b][i] = the resident row of idx[b][i].  The
+ * caller then runs sparsekv_attend on the resident view with rows, n_sel. */
+skv_status sparsekv_tier_resolve(skv_tier* t, const int32_t* idx, const int32_t* n_sel,
+                                 int32_t step, int32_t* rows, void* stream);
+/* Synchronizes `stream` and returns cumulative counters (host struct). */
+skv_status sparsekv_tier_stats(skv_tier* t, skv_tier_stats* out, void* stream);
+/* Synchronizes `stream` and copies the slot table to the host:
+ * slot_pos [B][n_slots] int32 (position held, -1 empty). */
+skv_status sparsekv_tier_slots(skv_tier* t, int32_t* slot_pos_host, void* stream);
+/* Empties the hot buffer and zeroes the counters (enqueued on stream). */
+skv_status sparsekv_tier_reset(skv_tier* t, void* stream);
+void sparsekv_tier_destroy(skv_tier* t);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSEKV_H */

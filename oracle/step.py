@@ -336,7 +336,8 @@ class ClockTier:
            otherwise                       -> evict its token and take it;
          a taken slot gets ref = 1, last = s, and the hand stops just past it.
     W = 1 pins exactly the slots used in the current step.  The buffer must
-    hold more slots than picks per step, so a victim is always found.
+    hold more slots than the picks of W consecutive steps, so a victim is
+    always found within two sweeps of the hand.
     """
 
     def __init__(self, n_slots: int, T: int, window: int = 1):
@@ -358,7 +359,11 @@ class ClockTier:
         self.last[slots[hit]] = s
         for i in np.nonzero(~hit)[0]:
             p = picks[i]
+            moves = 0
             while True:
+                moves += 1
+                if moves > 2 * self.n + 1:
+                    raise RuntimeError("no slot can be evicted: more slots pinned than exist")
                 x = self.hand
                 self.hand = (self.hand + 1) % self.n
                 if self.pos[x] < 0:

@@ -1,0 +1,145 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/sparsekv.h declares, and rejects bad descriptors and arguments on the
+host with the documented status before touching the device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparsekv.h")
+
+
+@pytest.fixture(scope="module")
+def skv():
+    from top_sparse_kv_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from top_sparse_kv_amd import build
+        build.build()
+    import top_sparse_kv_amd as m
+    m.lib()
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparsekv_\w+)\s*\(", text)))
+
+
+def test_header_declarations_are_exported(skv):
+    from top_sparse_kv_amd import _lib
+    names = declared_functions()
+    assert len(names) >= 20
+    lib = skv.lib()
+    bound = {n for n, _, _ in _lib.SIGNATURES}
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in bound, "binding lacks " + n
+
+
+def test_struct_sizes_match_header(skv):
+    # the C structs are plain int32 / pointer layouts; sizes pinned here
+    assert ctypes.sizeof(skv.LayerDesc) == 15 * 4
+    assert ctypes.sizeof(skv.KVView) == 5 * 8
+    assert skv.abi_version() == 1
+
+
+def test_capacity_and_workspace(skv):
+    d2 = skv.token_desc(8, 250_000, 4, 24, 256, topk=2048, n_sink=64, n_tail=1024)
+    d1 = skv.token_desc(1, 4096, 2, 8, 128, topk=256, n_sink=16, n_tail=128, kv_dtype=skv.SKV_KV_F16)
+    d3 = skv.block_desc(1, 1_048_576, 2, 16, 256, topk_blocks=512)
+    assert skv.select_capacity(d2) == 3136
+    assert skv.select_capacity(d1) == 400
+    assert skv.select_capacity(d3) == 2051
+    for d in (d1, d2, d3):
+        assert skv.workspace_size(d) > 0 and skv.workspace_size(d) % 256 == 0
+
+
+BAD = [
+    (dict(head_dim=192), 2),
+    (dict(n_q_heads=25), 1),
+    (dict(n_q_heads=4 * 17), 2),
+    (dict(topk=0), 2),
+    (dict(topk=5000), 2),
+    (dict(batch=0), 1),
+    (dict(max_ctx=0), 1),
+    (dict(block=4), 1),
+    (dict(rank=63), 2),
+    (dict(n_sink=-1), 1),
+    (dict(kv_dtype=2), 2),
+    (dict(q_dtype=1), 2),
+    (dict(index_mode=7), 1),
+    (dict(struct_size=8), 1),
+]
+
+
+@pytest.mark.parametrize("change,status", BAD)
+def test_bad_descriptor(skv, change, status):
+    d = skv.token_desc(8, 250_000, 4, 24, 256, topk=2048, n_sink=64, n_tail=1024)
+    for k, v in change.items():
+        setattr(d, k, v)
+    st = skv.lib().sparsekv_validate(ctypes.byref(d))
+    assert st == status, (change, st, skv.lib().sparsekv_last_error())
+    assert skv.lib().sparsekv_last_error()
+
+
+def test_bad_block_descriptor(skv):
+    d = skv.block_desc(1, 1 << 20, 2, 16, 256, topk_blocks=512)
+    d.n_sink = 4
+    assert skv.lib().sparsekv_validate(ctypes.byref(d)) == 2
+    d = skv.block_desc(1, 1 << 20, 2, 16, 256, topk_blocks=512)
+    d.kv_dtype = skv.SKV_KV_F16
+    assert skv.lib().sparsekv_validate(ctypes.byref(d)) == 2
+    d = skv.block_desc(1, 1 << 20, 2, 16, 256, index_dim=100, topk_blocks=512)
+    assert skv.lib().sparsekv_validate(ctypes.byref(d)) == 2
+
+
+def test_host_errors_before_any_device_work(skv):
+    """NULL pointers and a missing / short workspace are rejected on the host."""
+    lib = skv.lib()
+    d = skv.token_desc(2, 1000, 4, 24, 256, topk=64, n_sink=4, n_tail=8)
+    dummy = ctypes.c_void_p(0x1000)
+    # workspace missing
+    st = lib.sparsekv_score(ctypes.byref(d), dummy, dummy, dummy, dummy, dummy, None, 0, None)
+    assert st == 3
+    # workspace too small
+    st = lib.sparsekv_topk(ctypes.byref(d), dummy, dummy, dummy, dummy, ctypes.c_void_p(0x100000), 16, None)
+    assert st == 3
+    # NULL keys
+    need = skv.workspace_size(d)
+    st = lib.sparsekv_topk(ctypes.byref(d), dummy, None, dummy, dummy, ctypes.c_void_p(0x100000), need, None)
+    assert st == 1
+    # NULL kv view
+    st = lib.sparsekv_attend(ctypes.byref(d), dummy, None, dummy, dummy, 0.1, dummy,
+                             ctypes.c_void_p(0x100000), need, None)
+    assert st == 1
+    # qsketch is token-mode only
+    db = skv.block_desc(1, 4096, 2, 16, 256, topk_blocks=64)
+    st = lib.sparsekv_qsketch(ctypes.byref(db), dummy, dummy, dummy, dummy, None, 0, None)
+    assert st == 1
+    # misaligned workspace
+    st = lib.sparsekv_topk(ctypes.byref(d), dummy, dummy, dummy, dummy, ctypes.c_void_p(0x100010), need, None)
+    assert st == 3
+
+
+def test_tier_rejects_bad_descriptors(skv):
+    lib = skv.lib()
+    layer = skv.token_desc(2, 10_000, 4, 24, 256, topk=64, n_sink=4, n_tail=8)
+    h = ctypes.c_void_p()
+    for ctx, slots, window, status in ((0, 200, 1, 1), (20_000, 200, 1, 1), (10_000, 64, 1, 1),
+                                        (10_000, 200, 0, 1)):
+        td = skv.TierDesc(ctypes.sizeof(skv.TierDesc), layer, ctx, slots, window, None)
+        assert lib.sparsekv_tier_create(ctypes.byref(td), ctypes.byref(h)) == status
+    l2 = skv.token_desc(2, 10_000, 2, 8, 128, topk=64, n_sink=4, n_tail=8, kv_dtype=skv.SKV_KV_F16)
+    td = skv.TierDesc(ctypes.sizeof(skv.TierDesc), l2, 10_000, 200, 1, None)
+    assert lib.sparsekv_tier_create(ctypes.byref(td), ctypes.byref(h)) == 2
+
+
+def test_status_strings(skv):
+    lib = skv.lib()
+    for s in range(8):
+        assert lib.sparsekv_status_str(s)
+    assert lib.sparsekv_status_str(99) == b"unknown status"

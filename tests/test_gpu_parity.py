@@ -1,0 +1,265 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded bytes.  Index sets, query sketches and ranking keys must match
+bit for bit; attention outputs within 2e-3 max abs error of the fp64 oracle.
+
+Sizes span several score / select / attention tiles with ragged tails, the
+dense/sparse boundaries, empty and tiny sequences, and the full workload
+shapes (sampled sequences)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import (ATOL, block_desc_of, compare_keys, compare_out, compare_sel, need_gpu,
+                      np16, oracle_block, oracle_token, run_block_gpu, run_token_gpu, say,
+                      token_desc_of)
+
+pytestmark = pytest.mark.gpu
+
+
+def _cfg1(B=1, T=4096, lens=None, seed=1001, **kw):
+    return synth.make_token_case(B, T, lens, n_kv=2, n_q=8, D=128, S=16, k=256, L=128,
+                                 kv_format="f16", seed=seed, **kw)
+
+
+def _cfg2(B, T, lens=None, seed=1002, device="cpu", **kw):
+    return synth.make_token_case(B, T, lens, n_kv=4, n_q=24, D=256, S=64, k=2048, L=1024,
+                                 kv_format="i8", seed=seed, device=device, **kw)
+
+
+def _cfg3(B, T, lens=None, seed=1003, device="cpu", **kw):
+    return synth.make_block_case(B, T, lens, n_kv=2, n_q=16, D=256, k=512, seed=seed,
+                                 device=device, **kw)
+
+
+def _check_token(c, g, o, seqs=None, sm=None):
+    seqs = range(c.B) if seqs is None else seqs
+    assert np.array_equal(g["qs"], o["qs"]), "query sketch codes differ"
+    assert np.array_equal(g["qscale"].view(np.uint32), o["qscale"].view(np.uint32)), "qscale differs"
+    errs = []
+    for b in seqs:
+        T = c.lens[b]
+        compare_keys(g["keys"], o["keys"], b, c.S, max(c.S, T - c.L))
+        compare_sel(g, o, b)
+        errs.append(compare_out(g, o, b))
+        if len(c.needles[b]):
+            assert np.isin(c.needles[b].numpy(), g["idx"][b, :g["n_sel"][b]]).all()
+    return max(errs) if errs else 0.0
+
+
+def test_config1_tiny_layer():
+    skv = need_gpu()
+    c = _cfg1()
+    sm = 128 ** -0.5
+    say("cfg1 B=1 T=4096")
+    g = run_token_gpu(skv, c, sm)
+    o = oracle_token(c, sm)
+    err = _check_token(c, g, o)
+    say("cfg1 max err", err)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_config2_shape_ragged(fused):
+    """cfg-2 layer shape, 3 sequences with ragged lengths spanning several
+    score / histogram tiles, one dense sequence, plus the boundary lengths."""
+    skv = need_gpu()
+    lens = [40_000, 3_137, 17_001, 3_136, 3_135]
+    c = _cfg2(5, 40_960, lens)
+    sm = 256 ** -0.5
+    say("cfg2 ragged", lens, "fused", fused)
+    g = run_token_gpu(skv, c, sm, fused=fused)
+    o = oracle_token(c, sm)
+    err = _check_token(c, g, o)
+    assert g["n_sel"].tolist() == [3136, 3136, 3136, 3136, 3135]
+    say("cfg2 ragged max err", err)
+
+
+def test_config3_shape_boundaries():
+    """QSA layer shape in block mode; dense until T > 4*512+3 = 2051."""
+    skv = need_gpu()
+    lens = [65_536, 2_051, 2_052, 2_053, 30_001, 4]
+    c = _cfg3(len(lens), 65_536, lens)
+    sm = 256 ** -0.5
+    say("cfg3 boundaries", lens)
+    g = run_block_gpu(skv, c, sm)
+    o = oracle_block(c, sm)
+    for b in range(c.B):
+        compare_keys(g["keys"], o["keys"], b, 0, c.lens[b] // 4)
+        compare_sel(g, o, b)
+        compare_out(g, o, b)
+    assert g["n_sel"].tolist() == [2048, 2051, 2048, 2049, 2049, 4]
+    # needles (whole blocks) recovered
+    for blk in c.needles[0].tolist():
+        assert 4 * blk in set(g["idx"][0, :2048].tolist())
+
+
+def test_empty_and_tiny_sequences():
+    skv = need_gpu()
+    lens = [0, 1, 2, 399, 400, 401, 1000]
+    c = _cfg1(len(lens), 1024, lens, n_needles=0)
+    sm = 0.1
+    g = run_token_gpu(skv, c, sm)
+    o = oracle_token(c, sm)
+    _check_token(c, g, o)
+    assert g["n_sel"].tolist() == [0, 1, 2, 399, 400, 400, 400]
+    assert not g["out"][0].any()
+
+
+def test_topk_ties_and_degenerate_keys():
+    """Keys fed straight to sparsekv_topk: many exact ties, all-equal keys (the
+    exact slow path), negative keys, and a single huge key."""
+    skv = need_gpu()
+    B, T = 6, 50_000
+    S, k, L = 64, 2048, 1024
+    desc = skv.token_desc(B, T, 4, 24, 256, topk=k, n_sink=S, n_tail=L)
+    rng = np.random.default_rng(5)
+    keys = np.zeros((B, T))
+    keys[0] = rng.integers(-3, 4, size=T)                    # heavy ties
+    keys[1] = 0.0                                            # all equal -> slow path
+    keys[2] = -rng.random(T)                                 # all negative
+    keys[3] = rng.standard_normal(T)
+    keys[3, 12345] = 1e300
+    keys[4] = np.round(rng.standard_normal(T) * 8) / 8       # coarse grid, ties
+    keys[5] = -0.0                                           # negative zeros
+    kt = torch.from_numpy(keys).cuda()
+    ctx = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    cap = skv.select_capacity(desc)
+    idx = torch.zeros((B, cap), dtype=torch.int32, device="cuda")
+    nsel = torch.zeros((B,), dtype=torch.int32, device="cuda")
+    ws = skv.workspace(desc)
+    skv.topk(desc, ctx, kt, idx, nsel, ws)
+    flags = skv.check(ws)
+    assert flags & skv.SKV_FLAG_TOPK_SLOW
+    gi = idx.cpu().numpy()
+    for b in range(B):
+        want = oracle.select_tokens(keys[b], T, S, k, L)
+        assert nsel[b].item() == want.size
+        assert np.array_equal(gi[b, :want.size], want), "sequence %d" % b
+
+
+def test_determinism_and_graph_replay():
+    """Two eager runs are bitwise identical; a captured HIP graph of the whole
+    step replayed several times gives the eager result every time."""
+    skv = need_gpu()
+    c = _cfg2(3, 20_000, [20_000, 9_000, 3_000], device="cuda")
+    sm = 256 ** -0.5
+    a = run_token_gpu(skv, c, sm, fused=True)
+    b = run_token_gpu(skv, c, sm, fused=True)
+    for key in ("qs", "qscale", "idx", "n_sel", "out"):
+        assert np.array_equal(a[key], b[key]), key
+    desc = token_desc_of(skv, c)
+    cap = skv.select_capacity(desc)
+    ws = skv.workspace(desc)
+    qs = torch.zeros((c.B, 256), dtype=torch.int8, device="cuda")
+    qsc = torch.zeros((c.B,), dtype=torch.float32, device="cuda")
+    keys = torch.zeros((c.B, c.T_max), dtype=torch.float64, device="cuda")
+    idx = torch.zeros((c.B, cap), dtype=torch.int32, device="cuda")
+    nsel = torch.zeros((c.B,), dtype=torch.int32, device="cuda")
+    out = torch.zeros((c.B, c.n_q, c.D), dtype=torch.float32, device="cuda")
+    kv = skv.kv_view(c.k_cache, c.v_cache, c.k_scale, c.v_scale)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):   # warm-up on the capture stream
+        skv.step(desc, c.ctx_len, c.q, c.basis, qs, qsc, None, c.codes, c.sk_scale, keys, kv, idx,
+                 nsel, sm, out, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        skv.step(desc, c.ctx_len, c.q, c.basis, qs, qsc, None, c.codes, c.sk_scale, keys, kv, idx,
+                 nsel, sm, out, ws)
+    for rep in range(4):
+        out.zero_()
+        idx.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        _ = (out * 2).sum().item()   # unrelated eager work between replays
+        assert np.array_equal(out.cpu().numpy().astype(np.float64), a["out"]), "replay %d" % rep
+        for bb in range(c.B):
+            n = int(a["n_sel"][bb])
+            assert np.array_equal(idx.cpu().numpy()[bb, :n], a["idx"][bb, :n])
+
+
+def test_device_flags():
+    """Out-of-range ctx_len and attention indices are clamped/skipped and flagged."""
+    skv = need_gpu()
+    c = _cfg1(2, 1024, [1024, 500], n_needles=0)
+    desc = token_desc_of(skv, c)
+    cap = skv.select_capacity(desc)
+    ws = skv.workspace(desc)
+    ctx = torch.tensor([5000, 500], dtype=torch.int32, device="cuda")
+    qs = torch.zeros((2, 128), dtype=torch.int8, device="cuda")
+    keys = torch.zeros((2, 1024), dtype=torch.float64, device="cuda")
+    skv.score(desc, ctx, qs, c.codes.cuda(), c.sk_scale.cuda(), keys, ws)
+    with pytest.raises(skv.SkvError):
+        skv.check(ws)
+    idx = torch.full((2, cap), 7, dtype=torch.int32, device="cuda")
+    idx[0, 3] = 99_999
+    nsel = torch.tensor([10, 10], dtype=torch.int32, device="cuda")
+    out = torch.zeros((2, 8, 128), dtype=torch.float32, device="cuda")
+    kv = skv.kv_view(c.k_cache.cuda(), c.v_cache.cuda())
+    skv.attend(desc, c.q.cuda(), kv, idx, nsel, 0.1, out, ws)
+    with pytest.raises(skv.SkvError):
+        skv.check(ws)
+    assert skv.check(ws) == 0    # flags were cleared
+
+
+# ---------------------------------------------------------------------------
+# full workload sizes, generated on the device; sampled sequences checked
+# ---------------------------------------------------------------------------
+
+def test_full_config2_8x250k():
+    skv = need_gpu()
+    say("cfg2 full: generating 8 x 250,000")
+    c = _cfg2(8, 250_000, device="cuda")
+    sm = 256 ** -0.5
+    g = run_token_gpu(skv, c, sm, fused=True)
+    seqs = [0, 5]
+    say("cfg2 full: oracle on sequences", seqs)
+    o = oracle_token(c, sm, seqs)
+    err = _check_token(c, g, o, seqs)
+    assert g["n_sel"].tolist() == [3136] * 8
+    assert g["flags"] == 0
+    say("cfg2 full max err", err)
+
+
+def test_full_config3_1m():
+    skv = need_gpu()
+    say("cfg3 full: generating 1 x 1,048,576")
+    c = _cfg3(1, 1_048_576, device="cuda")
+    sm = 256 ** -0.5
+    g = run_block_gpu(skv, c, sm, fused=True)
+    o = oracle_block(c, sm)
+    compare_keys(g["keys"], o["keys"], 0, 0, 262_144)
+    compare_sel(g, o, 0)
+    err = compare_out(g, o, 0)
+    assert g["n_sel"][0] == 2048
+    say("cfg3 full max err", err)
+
+
+def test_full_config4a_32x128k():
+    skv = need_gpu()
+    say("cfg4a full: generating 32 x 131,072")
+    c = _cfg2(32, 131_072, seed=1004, device="cuda")
+    sm = 256 ** -0.5
+    g = run_token_gpu(skv, c, sm, fused=True)
+    seqs = [0, 17, 31]
+    o = oracle_token(c, sm, seqs)
+    _check_token(c, g, o, seqs)
+
+
+def test_full_config4b_mixed():
+    skv = need_gpu()
+    lens = synth.gen.mixed_lengths(32, 2048, 250_000, seed=1014)
+    lens[:3] = [3135, 3136, 3137]
+    say("cfg4b mixed lengths, min", min(lens), "max", max(lens))
+    c = _cfg2(32, 250_000, lens, seed=1014, device="cuda")
+    sm = 256 ** -0.5
+    g = run_token_gpu(skv, c, sm, fused=True)
+    seqs = [0, 1, 2] + [int(np.argmax(lens)), int(np.argmin(lens[3:])) + 3]
+    o = oracle_token(c, sm, seqs)
+    _check_token(c, g, o, seqs)
+    for b in range(32):
+        assert g["n_sel"][b] == min(lens[b], 3136)

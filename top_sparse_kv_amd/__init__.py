@@ -1,0 +1,219 @@
+"""Python binding of libsparsekv (the gfx950 sparse-KV decode step).
+
+Thin argument marshalling over the C ABI in include/sparsekv.h: every function
+here has the name of the C entry point it calls (without the sparsekv_
+prefix), takes torch tensors for device buffers, passes their addresses and
+the current HIP stream, and raises SkvError on a non-OK status.  All compute
+runs in the library's HIP kernels; torch only provides device memory and
+streams.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import (KVView, LayerDesc, TierDesc, TierStats, SKV_INDEX_SKETCH_INT4,  # noqa: F401
+                   SKV_INDEX_POOLED_BF16, SKV_KV_I8_ROWSCALE, SKV_KV_F16, SKV_KV_BF16, SKV_Q_F16,
+                   SKV_Q_BF16, SKV_FLAG_CTX_RANGE, SKV_FLAG_INDEX_RANGE, SKV_FLAG_TOPK_SLOW,
+                   SKV_FLAG_TIER_INPUT)
+
+
+class SkvError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("%s: %s" % (_lib.STATUS.get(status, status), msg))
+        self.status = status
+
+
+def lib():
+    return _lib.load()
+
+
+def _check(st: int):
+    if st != 0:
+        raise SkvError(st, (lib().sparsekv_last_error() or b"").decode())
+
+
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("device tensor expected")
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def token_desc(batch, max_ctx, n_kv_heads, n_q_heads, head_dim, *, rank=64, topk, n_sink, n_tail,
+               kv_dtype=SKV_KV_I8_ROWSCALE) -> LayerDesc:
+    return LayerDesc(ctypes.sizeof(LayerDesc), batch, max_ctx, n_kv_heads, n_q_heads, head_dim,
+                     SKV_INDEX_SKETCH_INT4, rank, 0, 1, topk, n_sink, n_tail, kv_dtype, SKV_Q_F16)
+
+
+def block_desc(batch, max_ctx, n_kv_heads, n_q_heads, head_dim, *, index_dim=128,
+               topk_blocks) -> LayerDesc:
+    return LayerDesc(ctypes.sizeof(LayerDesc), batch, max_ctx, n_kv_heads, n_q_heads, head_dim,
+                     SKV_INDEX_POOLED_BF16, 0, index_dim, 4, topk_blocks, 0, 0, SKV_KV_BF16,
+                     SKV_Q_BF16)
+
+
+def kv_view(k: torch.Tensor, v: torch.Tensor, k_scale=None, v_scale=None,
+            rows: Optional[int] = None) -> KVView:
+    """View of K/V rows shaped [B][rows][H_kv][D] (+ fp16 scales [B][rows][H_kv])."""
+    _dev(k, v, k_scale, v_scale)
+    return KVView(_p(k), _p(v), _p(k_scale), _p(v_scale), int(rows if rows is not None else k.shape[1]))
+
+
+def abi_version() -> int:
+    return lib().sparsekv_abi_version()
+
+
+def validate(desc: LayerDesc):
+    _check(lib().sparsekv_validate(ctypes.byref(desc)))
+
+
+def select_capacity(desc: LayerDesc) -> int:
+    c = _lib.c_i32()
+    _check(lib().sparsekv_select_capacity(ctypes.byref(desc), ctypes.byref(c)))
+    return c.value
+
+
+def workspace_size(desc: LayerDesc) -> int:
+    n = _lib.c_sz()
+    _check(lib().sparsekv_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def workspace(desc: LayerDesc, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace of the required size."""
+    return torch.zeros(workspace_size(desc), dtype=torch.uint8, device=device)
+
+
+def qsketch(desc, q, basis, qs, qs_scale, ws, stream=None):
+    _dev(q, basis, qs, qs_scale, ws)
+    _check(lib().sparsekv_qsketch(ctypes.byref(desc), _p(q), _p(basis), _p(qs), _p(qs_scale),
+                                  _p(ws), ws.numel(), _stream(stream)))
+
+
+def score(desc, ctx_len, index_query, index_keys, index_scale, keys, ws, stream=None):
+    _dev(ctx_len, index_query, index_keys, index_scale, keys, ws)
+    _check(lib().sparsekv_score(ctypes.byref(desc), _p(ctx_len), _p(index_query), _p(index_keys),
+                                _p(index_scale), _p(keys), _p(ws), ws.numel(), _stream(stream)))
+
+
+def topk(desc, ctx_len, keys, idx, n_sel, ws, stream=None):
+    _dev(ctx_len, keys, idx, n_sel, ws)
+    _check(lib().sparsekv_topk(ctypes.byref(desc), _p(ctx_len), _p(keys), _p(idx), _p(n_sel),
+                               _p(ws), ws.numel(), _stream(stream)))
+
+
+def attend(desc, q, kv: KVView, idx, n_sel, sm_scale, out, ws, stream=None):
+    _dev(q, idx, n_sel, out, ws)
+    _check(lib().sparsekv_attend(ctypes.byref(desc), _p(q), ctypes.byref(kv), _p(idx), _p(n_sel),
+                                 float(sm_scale), _p(out), _p(ws), ws.numel(), _stream(stream)))
+
+
+def step(desc, ctx_len, q, basis, qs, qs_scale, index_query, index_keys, index_scale, keys,
+         kv: KVView, idx, n_sel, sm_scale, out, ws, stream=None):
+    _dev(ctx_len, q, basis, qs, qs_scale, index_query, index_keys, index_scale, keys, idx, n_sel,
+         out, ws)
+    _check(lib().sparsekv_step(ctypes.byref(desc), _p(ctx_len), _p(q), _p(basis), _p(qs),
+                               _p(qs_scale), _p(index_query), _p(index_keys), _p(index_scale),
+                               _p(keys), ctypes.byref(kv), _p(idx), _p(n_sel), float(sm_scale),
+                               _p(out), _p(ws), ws.numel(), _stream(stream)))
+
+
+def check(ws, stream=None) -> int:
+    """Synchronizes, returns and clears the device flag bits; raises on error flags."""
+    f = _lib.c_u32()
+    st = lib().sparsekv_check(_p(ws), ws.numel(), _stream(stream), ctypes.byref(f))
+    if st not in (0, 7):
+        _check(st)
+    if st == 7:
+        raise SkvError(st, "device flags 0x%x" % f.value)
+    return f.value
+
+
+@dataclass
+class _TierHandle:
+    ptr: ctypes.c_void_p
+
+
+class Tier:
+    """Host-RAM KV tier with a GPU hot buffer (sparsekv_tier_*)."""
+
+    def __init__(self, layer: LayerDesc, ctx: int, n_slots: int, window: int = 1,
+                 host_records: Optional[int] = None):
+        self.layer = layer
+        d = TierDesc(ctypes.sizeof(TierDesc), layer, ctx, n_slots, window,
+                     ctypes.c_void_p(host_records) if host_records else None)
+        h = ctypes.c_void_p()
+        _check(lib().sparsekv_tier_create(ctypes.byref(d), ctypes.byref(h)))
+        self._h = h
+        self.ctx, self.n_slots, self.window = ctx, n_slots, window
+        D = layer.head_dim
+        self.record_bytes = 2 * (D // 2 + 2 * (D // 64))
+
+    def host_records(self):
+        """numpy uint8 view [B][ctx][H_kv][record] of the pinned host records."""
+        import numpy as np
+        ptr = lib().sparsekv_tier_host_records(self._h)
+        n = self.layer.batch * self.ctx * self.layer.n_kv_heads * self.record_bytes
+        buf = (ctypes.c_uint8 * n).from_address(ptr)
+        return np.frombuffer(buf, dtype=np.uint8).reshape(
+            self.layer.batch, self.ctx, self.layer.n_kv_heads, self.record_bytes)
+
+    def resident(self) -> KVView:
+        v = KVView()
+        _check(lib().sparsekv_tier_resident(self._h, ctypes.byref(v)))
+        return v
+
+    def load_resident(self, k, v, k_scale, v_scale, stream=None):
+        _dev(k, v, k_scale, v_scale)
+        _check(lib().sparsekv_tier_load_resident(self._h, _p(k), _p(v), _p(k_scale), _p(v_scale),
+                                                 _stream(stream)))
+
+    def resolve(self, idx, n_sel, step: int, rows, stream=None):
+        _dev(idx, n_sel, rows)
+        _check(lib().sparsekv_tier_resolve(self._h, _p(idx), _p(n_sel), int(step), _p(rows),
+                                           _stream(stream)))
+
+    def stats(self, stream=None) -> TierStats:
+        s = TierStats()
+        _check(lib().sparsekv_tier_stats(self._h, ctypes.byref(s), _stream(stream)))
+        return s
+
+    def slots(self, stream=None):
+        import numpy as np
+        out = np.empty((self.layer.batch, self.n_slots), dtype=np.int32)
+        _check(lib().sparsekv_tier_slots(self._h, out.ctypes.data_as(ctypes.c_void_p),
+                                         _stream(stream)))
+        return out
+
+    def reset(self, stream=None):
+        _check(lib().sparsekv_tier_reset(self._h, _stream(stream)))
+
+    def close(self):
+        if self._h:
+            lib().sparsekv_tier_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

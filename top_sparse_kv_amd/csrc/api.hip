@@ -1,0 +1,232 @@
+// C ABI entry points: host-side validation, workspace layout and launches.
+// Every check that can be made on the host is made before anything is
+// enqueued; device-side conditions are recorded in the workspace flag word.
+#include "skv_internal.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+namespace skv {
+
+static thread_local char g_err[512] = "";
+
+skv_status set_error(skv_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+static skv_status ok() {
+  g_err[0] = '\0';
+  return SKV_OK;
+}
+
+skv_status validate_desc(const skv_layer_desc* d) {
+  if (!d) return set_error(SKV_ERR_INVALID, "descriptor is NULL");
+  if (d->struct_size < sizeof(skv_layer_desc))
+    return set_error(SKV_ERR_INVALID, "struct_size %u < %zu", d->struct_size, sizeof(skv_layer_desc));
+  if (d->batch < 1) return set_error(SKV_ERR_INVALID, "batch %d < 1", d->batch);
+  if (d->max_ctx < 1) return set_error(SKV_ERR_INVALID, "max_ctx %d < 1", d->max_ctx);
+  if (d->n_kv_heads < 1 || d->n_q_heads < d->n_kv_heads || d->n_q_heads % d->n_kv_heads)
+    return set_error(SKV_ERR_INVALID, "n_q_heads %d must be a positive multiple of n_kv_heads %d",
+                     d->n_q_heads, d->n_kv_heads);
+  if (d->n_q_heads / d->n_kv_heads > 16)
+    return set_error(SKV_ERR_UNSUPPORTED, "query heads per KV head %d > 16", d->n_q_heads / d->n_kv_heads);
+  if (d->head_dim != 128 && d->head_dim != 256)
+    return set_error(SKV_ERR_UNSUPPORTED, "head_dim %d not in {128, 256}", d->head_dim);
+  if (d->topk < 1 || d->topk > kMaxTopk)
+    return set_error(SKV_ERR_UNSUPPORTED, "topk %d outside [1, %d]", d->topk, kMaxTopk);
+  if (d->n_sink < 0 || d->n_tail < 0) return set_error(SKV_ERR_INVALID, "negative n_sink / n_tail");
+  if (d->index_mode == SKV_INDEX_SKETCH_INT4) {
+    if (d->block != 1) return set_error(SKV_ERR_INVALID, "token mode needs block == 1 (got %d)", d->block);
+    if (d->rank < 1 || (d->n_kv_heads * d->rank) % 2)
+      return set_error(SKV_ERR_INVALID, "rank %d: n_kv_heads*rank must be even and positive", d->rank);
+    const int tb = d->n_kv_heads * d->rank / 2;
+    if (tb != 32 && tb != 64 && tb != 128 && tb != 256)
+      return set_error(SKV_ERR_UNSUPPORTED, "sketch bytes per token %d not in {32,64,128,256}", tb);
+    if (d->q_dtype != SKV_Q_F16) return set_error(SKV_ERR_UNSUPPORTED, "token mode needs fp16 queries");
+    if (d->kv_dtype == SKV_KV_I8_ROWSCALE) {
+      if (d->head_dim != 256) return set_error(SKV_ERR_UNSUPPORTED, "int8 K/V needs head_dim 256");
+    } else if (d->kv_dtype != SKV_KV_F16) {
+      return set_error(SKV_ERR_UNSUPPORTED, "token mode K/V must be int8+scale or fp16");
+    }
+    if ((int64_t)d->n_sink + d->topk + d->n_tail > (int64_t)1 << 20)
+      return set_error(SKV_ERR_UNSUPPORTED, "n_sink + topk + n_tail too large");
+  } else if (d->index_mode == SKV_INDEX_POOLED_BF16) {
+    if (d->block != 4) return set_error(SKV_ERR_INVALID, "block mode needs block == 4 (got %d)", d->block);
+    if (d->n_sink != 0 || d->n_tail != 0)
+      return set_error(SKV_ERR_UNSUPPORTED, "block mode has no sinks / tail");
+    if (d->index_dim != 64 && d->index_dim != 128 && d->index_dim != 256)
+      return set_error(SKV_ERR_UNSUPPORTED, "index_dim %d not in {64,128,256}", d->index_dim);
+    if (d->kv_dtype != SKV_KV_BF16 || d->q_dtype != SKV_Q_BF16)
+      return set_error(SKV_ERR_UNSUPPORTED, "block mode needs bf16 K/V and queries");
+  } else {
+    return set_error(SKV_ERR_INVALID, "index_mode %d unknown", d->index_mode);
+  }
+  return ok();
+}
+
+static skv_status check_ws(const skv_layer_desc* d, void* ws, size_t ws_bytes, WsLayout* L) {
+  *L = ws_layout(*d);
+  if (!ws) return set_error(SKV_ERR_WORKSPACE, "workspace is NULL");
+  if (ws_bytes < L->total)
+    return set_error(SKV_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, L->total);
+  if (((uintptr_t)ws) % 256) return set_error(SKV_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  return SKV_OK;
+}
+
+static skv_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return set_error(SKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+static skv_status check_kv(const skv_layer_desc* d, const skv_kv_view* kv) {
+  if (!kv || !kv->k || !kv->v) return set_error(SKV_ERR_INVALID, "kv view / k / v is NULL");
+  if (kv->rows < 1) return set_error(SKV_ERR_INVALID, "kv rows %lld < 1", (long long)kv->rows);
+  if (d->kv_dtype == SKV_KV_I8_ROWSCALE && (!kv->k_scale || !kv->v_scale))
+    return set_error(SKV_ERR_INVALID, "int8 K/V need k_scale and v_scale");
+  if ((((uintptr_t)kv->k) | ((uintptr_t)kv->v)) % 16)
+    return set_error(SKV_ERR_INVALID, "k / v must be 16-byte aligned");
+  return SKV_OK;
+}
+
+}  // namespace skv
+
+using namespace skv;
+
+extern "C" {
+
+int sparsekv_abi_version(void) { return SPARSEKV_ABI_VERSION; }
+
+const char* sparsekv_status_str(skv_status s) {
+  switch (s) {
+    case SKV_OK: return "ok";
+    case SKV_ERR_INVALID: return "invalid argument";
+    case SKV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case SKV_ERR_OOM: return "out of memory";
+    case SKV_ERR_HIP: return "HIP runtime error";
+    case SKV_ERR_HOST_MEMORY: return "host memory not pinned / mapped";
+    case SKV_ERR_STATE: return "device flags raised";
+    default: return "unknown status";
+  }
+}
+
+const char* sparsekv_last_error(void) { return g_err; }
+
+skv_status sparsekv_validate(const skv_layer_desc* d) { return validate_desc(d); }
+
+skv_status sparsekv_select_capacity(const skv_layer_desc* d, int32_t* cap) {
+  skv_status s = validate_desc(d);
+  if (s != SKV_OK) return s;
+  if (!cap) return set_error(SKV_ERR_INVALID, "cap is NULL");
+  *cap = select_capacity(*d);
+  return SKV_OK;
+}
+
+skv_status sparsekv_workspace_size(const skv_layer_desc* d, size_t* bytes) {
+  skv_status s = validate_desc(d);
+  if (s != SKV_OK) return s;
+  if (!bytes) return set_error(SKV_ERR_INVALID, "bytes is NULL");
+  *bytes = ws_layout(*d).total;
+  return SKV_OK;
+}
+
+skv_status sparsekv_qsketch(const skv_layer_desc* d, const void* q, const float* basis, int8_t* qs,
+                            float* qs_scale, void* ws, size_t ws_bytes, void* stream) {
+  skv_status s = validate_desc(d);
+  if (s != SKV_OK) return s;
+  (void)ws;
+  (void)ws_bytes;
+  if (d->index_mode != SKV_INDEX_SKETCH_INT4)
+    return set_error(SKV_ERR_INVALID, "qsketch is a token-mode stage");
+  if (!q || !basis || !qs || !qs_scale) return set_error(SKV_ERR_INVALID, "qsketch: NULL pointer");
+  return launched(launch_qsketch(*d, q, basis, qs, qs_scale, (hipStream_t)stream), "qsketch");
+}
+
+skv_status sparsekv_score(const skv_layer_desc* d, const int32_t* ctx_len, const void* index_query,
+                          const void* index_keys, const uint16_t* index_scale, double* keys,
+                          void* ws, size_t ws_bytes, void* stream) {
+  skv_status s = validate_desc(d);
+  if (s != SKV_OK) return s;
+  WsLayout L;
+  if ((s = check_ws(d, ws, ws_bytes, &L)) != SKV_OK) return s;
+  if (!ctx_len || !index_query || !index_keys || !keys)
+    return set_error(SKV_ERR_INVALID, "score: NULL pointer");
+  if (d->index_mode == SKV_INDEX_SKETCH_INT4 && !index_scale)
+    return set_error(SKV_ERR_INVALID, "score: token mode needs index_scale");
+  if (((uintptr_t)index_keys) % 16) return set_error(SKV_ERR_INVALID, "score: index_keys not 16-byte aligned");
+  return launched(launch_score(*d, ctx_len, index_query, index_keys, index_scale, keys,
+                               ws_ptr<uint32_t>(ws, L.flags), (hipStream_t)stream),
+                  "score");
+}
+
+skv_status sparsekv_topk(const skv_layer_desc* d, const int32_t* ctx_len, const double* keys,
+                         int32_t* idx, int32_t* n_sel, void* ws, size_t ws_bytes, void* stream) {
+  skv_status s = validate_desc(d);
+  if (s != SKV_OK) return s;
+  WsLayout L;
+  if ((s = check_ws(d, ws, ws_bytes, &L)) != SKV_OK) return s;
+  if (!ctx_len || !keys || !idx || !n_sel) return set_error(SKV_ERR_INVALID, "topk: NULL pointer");
+  return launched(launch_topk(*d, ctx_len, keys, idx, n_sel, ws, L, (hipStream_t)stream), "topk");
+}
+
+skv_status sparsekv_attend(const skv_layer_desc* d, const void* q, const skv_kv_view* kv,
+                           const int32_t* idx, const int32_t* n_sel, float sm_scale, float* out,
+                           void* ws, size_t ws_bytes, void* stream) {
+  skv_status s = validate_desc(d);
+  if (s != SKV_OK) return s;
+  WsLayout L;
+  if ((s = check_ws(d, ws, ws_bytes, &L)) != SKV_OK) return s;
+  if ((s = check_kv(d, kv)) != SKV_OK) return s;
+  if (!q || !idx || !n_sel || !out) return set_error(SKV_ERR_INVALID, "attend: NULL pointer");
+  if (((uintptr_t)q) % 16) return set_error(SKV_ERR_INVALID, "attend: q not 16-byte aligned");
+  return launched(launch_attend(*d, q, *kv, idx, n_sel, sm_scale, out, ws, L, (hipStream_t)stream),
+                  "attend");
+}
+
+skv_status sparsekv_step(const skv_layer_desc* d, const int32_t* ctx_len, const void* q,
+                         const float* basis, int8_t* qs, float* qs_scale, const void* index_query,
+                         const void* index_keys, const uint16_t* index_scale, double* keys,
+                         const skv_kv_view* kv, int32_t* idx, int32_t* n_sel, float sm_scale,
+                         float* out, void* ws, size_t ws_bytes, void* stream) {
+  skv_status s = validate_desc(d);
+  if (s != SKV_OK) return s;
+  WsLayout L;
+  if ((s = check_ws(d, ws, ws_bytes, &L)) != SKV_OK) return s;
+  if ((s = check_kv(d, kv)) != SKV_OK) return s;
+  if (!ctx_len || !q || !index_keys || !keys || !idx || !n_sel || !out)
+    return set_error(SKV_ERR_INVALID, "step: NULL pointer");
+  const bool tok = d->index_mode == SKV_INDEX_SKETCH_INT4;
+  if (tok && (!basis || !qs || !qs_scale || !index_scale))
+    return set_error(SKV_ERR_INVALID, "step: token mode needs basis, qs, qs_scale and index_scale");
+  if (!tok && !index_query) return set_error(SKV_ERR_INVALID, "step: block mode needs index_query");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (tok) e = launch_qsketch(*d, q, basis, qs, qs_scale, st);
+  if (e == hipSuccess)
+    e = launch_score(*d, ctx_len, tok ? (const void*)qs : index_query, index_keys, index_scale, keys,
+                     ws_ptr<uint32_t>(ws, L.flags), st);
+  if (e == hipSuccess) e = launch_topk(*d, ctx_len, keys, idx, n_sel, ws, L, st);
+  if (e == hipSuccess) e = launch_attend(*d, q, *kv, idx, n_sel, sm_scale, out, ws, L, st);
+  return launched(e, "step");
+}
+
+skv_status sparsekv_check(void* ws, size_t ws_bytes, void* stream, uint32_t* flags) {
+  if (!ws || ws_bytes < 4) return set_error(SKV_ERR_WORKSPACE, "check: workspace missing");
+  uint32_t f = 0, zero = 0;
+  hipStream_t st = (hipStream_t)stream;
+  if (hipStreamSynchronize(st) != hipSuccess ||
+      hipMemcpy(&f, ws, 4, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(ws, &zero, 4, hipMemcpyHostToDevice) != hipSuccess)
+    return set_error(SKV_ERR_HIP, "check: %s", hipGetErrorString(hipGetLastError()));
+  if (flags) *flags = f;
+  if (f & ~(uint32_t)SKV_FLAG_TOPK_SLOW)
+    return set_error(SKV_ERR_STATE, "device flags 0x%x", f);
+  return ok();
+}
+
+}  // extern "C"

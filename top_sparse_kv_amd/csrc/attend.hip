@@ -1,0 +1,408 @@
+// Stage A4: exact GQA attention over the selected K/V rows only.
+//
+// Page "8 agents x 250K context on two 3090s: sparse KV decode with a rank-64
+// key sketch and a host-RAM tier", section "The mechanism": exact attention
+// runs on the kept tokens only (int8 K/V there).  Page "3.14M Context on 3x
+// 3090: The Power of an Architecture That Puts KV Cache in Host RAM", section
+// "No Need to Rewrite the Kernel": the gather addresses row
+// (token * n_kv_heads + kv_head) * head_dim, so K/V may live anywhere the
+// GPU can address.
+//
+// Work split: one workgroup per (sequence, KV head, chunk of 256 selected
+// rows); each of its 4 waves runs an online softmax over 64 rows, 32 at a
+// time, for the G query heads of that KV head; the waves merge in LDS and the
+// workgroup writes one (max, sum, unnormalised output) partial; a second
+// kernel merges the chunks of each query head in fixed order.
+//
+// Inner step on the matrix cores (v_mfma_f32_16x16x32 f16 / bf16):
+//   logits^T[32 tok x 16 heads] = K[32 x D] . Q^T[D x 16]   (2 M-tiles of 16)
+//   O[16 heads x D]            += P[16 x 32 tok] . V[32 x D] (D/16 N-tiles)
+// Only G of the 16 head columns are real (the rest multiply zeros).  The
+// contraction index of an MFMA may be permuted freely as long as both operands
+// agree, which is used twice:
+//   * each lane reads one contiguous D/4 slice of a K row;
+//   * the QK accumulator leaves, in every lane, the 8 token probabilities of
+//     one head that the PV A-operand needs in that same lane (no shuffles);
+//     V columns are gathered to match with byte permutes.
+// int8 K/V are converted to fp16 exactly (offset-1152 trick: 0x64xx is 1024 +
+// the biased byte).  Probabilities are split into a high and a low fp16 (or
+// bf16) part and both are multiplied, so P keeps ~22 (or ~16) significant bits.
+// All accumulation is fp32; the output is fp32.
+#include "skv_internal.h"
+
+namespace skv {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+enum { KV_I8 = 0, KV_F16 = 1, KV_BF16 = 2 };
+constexpr int kAttThreads = 64 * kAttWaves;
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <bool BF>
+__device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (BF)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// two int8 values (already xor 0x80 in their bytes) -> exact fp16 pair
+__device__ __forceinline__ uint32_t i8pair_to_f16(uint32_t biased_dw, uint32_t sel) {
+  const uint32_t r = __builtin_amdgcn_perm(0x64646464u, biased_dw, sel);
+  f16x2 h = __builtin_bit_cast(f16x2, r);
+  h = h - (f16x2){(_Float16)1152.0f, (_Float16)1152.0f};
+  return __builtin_bit_cast(uint32_t, h);
+}
+// bytes 0..3 of a biased dword -> 4 fp16 (2 dwords)
+__device__ __forceinline__ void i8x4_to_f16(uint32_t biased_dw, uint32_t& lo, uint32_t& hi) {
+  lo = i8pair_to_f16(biased_dw, 0x04010400u);
+  hi = i8pair_to_f16(biased_dw, 0x04030402u);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rn(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+template <int KVT>
+struct Esize {
+  static constexpr int v = KVT == KV_I8 ? 1 : 2;
+};
+
+template <int KVT, int D>
+__global__ __launch_bounds__(kAttThreads) void attend_kernel(
+    const void* __restrict__ qv, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
+    const uint16_t* __restrict__ ksc, const uint16_t* __restrict__ vsc, int64_t rows,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ n_sel, int cap,
+    float scale_log2, int Hq, int Hkv, float* __restrict__ part_ml, float* __restrict__ part_o,
+    int n_chunks, uint32_t* __restrict__ flags) {
+  constexpr bool BF = KVT == KV_BF16;
+  constexpr int ES = Esize<KVT>::v;
+  constexpr int KSTEPS = D / 32;          // MFMA k-steps over head_dim
+  constexpr int NT = D / 16;              // PV N-tiles
+  constexpr int KB = D / 4 * ES;          // bytes of one lane's K slice
+  constexpr int VB = D / 16 * ES;         // bytes of one lane's V slice per token
+  constexpr int KV4 = KB / 16;            // 16-byte loads per K slice
+  constexpr int VV4 = VB / 16;            // 16-byte loads per V slice
+  __shared__ float s_m[kAttWaves][16];
+  __shared__ float s_l[kAttWaves][16];
+  extern __shared__ float s_o[];          // [kAttWaves][G][D]
+
+  const int h = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
+  const int G = Hq / Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i16 = lane & 15, g = lane >> 4;
+  int n = n_sel[b];
+  if (n < 0 || n > cap) {
+    if (threadIdx.x == 0 && c == 0 && h == 0) raise_flag(flags, SKV_FLAG_INDEX_RANGE);
+    n = n < 0 ? 0 : cap;
+  }
+  const int r0 = c * kAttRowsPerWG;
+  if (r0 >= n) return;
+  const int32_t* ib = idx + (size_t)b * cap;
+  const size_t row_stride = (size_t)Hkv * D * ES;   // bytes between consecutive rows
+
+  // Q as the B operand of the QK product: lane (head j = i16, group g), step s
+  // holds Q[j][g*D/4 + 8s .. +8]
+  u32x4 bq[KSTEPS];
+  {
+    const int j = i16;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(qv) + ((size_t)b * Hq + (size_t)h * G + (j < G ? j : 0)) * D + g * (D / 4);
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      u32x4 v = *reinterpret_cast<const u32x4*>(qp + 8 * s);
+      if (j >= G) v = (u32x4){0u, 0u, 0u, 0u};
+      bq[s] = v;
+    }
+  }
+
+  f32x4 o[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) o[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;   // running max of head i16 (log2 units), same in all 4 groups
+  float l_run = 0.0f;
+
+  const uint8_t* kbase = kc + ((size_t)b * rows * Hkv + h) * D * ES;
+  const uint8_t* vbase = vc + ((size_t)b * rows * Hkv + h) * D * ES;
+  const uint16_t* ksb = ksc ? ksc + (size_t)b * rows * Hkv + h : nullptr;
+  const uint16_t* vsb = vsc ? vsc + (size_t)b * rows * Hkv + h : nullptr;
+
+  for (int it = 0; it < kAttRowsPerWave / 32; ++it) {
+    const int rb = r0 + wave * kAttRowsPerWave + it * 32;
+    if (rb >= n) break;
+    // ---- token rows used by this lane ----
+    // QK A operand: M-tile mt row i16 -> selected row rb + 16*mt + i16
+    // (out-of-range rows load row 0 and are masked below through vok)
+    int ka[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int ri = rb + 16 * mt + i16;
+      int tok = ri < n ? ib[ri] : 0;
+      if (ri < n && (tok < 0 || (int64_t)tok >= rows)) {
+        raise_flag(flags, SKV_FLAG_INDEX_RANGE);
+        tok = 0;
+      }
+      ka[mt] = tok;
+    }
+    // the 8 tokens whose probabilities / V rows this lane handles:
+    // e' = 0..3 -> row rb + 4g + e', e' = 4..7 -> row rb + 16 + 4g + e'-4
+    int vt[8];
+    bool vok[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int ri = rb + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
+      int tok = ri < n ? ib[ri] : 0;
+      bool ok = ri < n && tok >= 0 && (int64_t)tok < rows;
+      if (!ok) tok = 0;
+      vt[e] = tok;
+      vok[e] = ok;
+    }
+    // ---- loads ----
+    u32x4 kraw[2][KV4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const u32x4* kp = reinterpret_cast<const u32x4*>(kbase + (size_t)ka[mt] * row_stride + g * KB);
+#pragma unroll
+      for (int x = 0; x < KV4; ++x) kraw[mt][x] = kp[x];
+    }
+    u32x4 vraw[8][VV4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const u32x4* vp = reinterpret_cast<const u32x4*>(vbase + (size_t)vt[e] * row_stride + i16 * VB);
+#pragma unroll
+      for (int x = 0; x < VV4; ++x) vraw[e][x] = vp[x];
+    }
+    float kscale[8], vscale[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (KVT == KV_I8) {
+        kscale[e] = half_bits_to_float(ksb[(size_t)vt[e] * Hkv]);
+        vscale[e] = half_bits_to_float(vsb[(size_t)vt[e] * Hkv]);
+      } else {
+        kscale[e] = 1.0f;
+        vscale[e] = 1.0f;
+      }
+    }
+
+    // ---- logits (transposed): 2 M-tiles of 16 tokens x 16 heads ----
+    f32x4 sacc[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        u32x4 a;
+        if constexpr (KVT == KV_I8) {
+          // step s uses bytes 8s..8s+7 of the lane's 64-byte slice
+          const u32x4 w = kraw[mt][s >> 1];
+          const uint32_t d0 = ((s & 1) ? w.z : w.x) ^ 0x80808080u;
+          const uint32_t d1 = ((s & 1) ? w.w : w.y) ^ 0x80808080u;
+          uint32_t a0, a1, a2, a3;
+          i8x4_to_f16(d0, a0, a1);
+          i8x4_to_f16(d1, a2, a3);
+          a = (u32x4){a0, a1, a2, a3};
+        } else {
+          a = kraw[mt][s];
+        }
+        acc = mfma<BF>(a, bq[s], acc);
+      }
+      sacc[mt] = acc;
+    }
+    // lane (head i16, group g) holds logits of rows 4g+e of each M-tile
+    float lg[8];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float sv = e < 4 ? sacc[0][e] : sacc[1][e - 4];
+      lg[e] = vok[e] ? sv * kscale[e] * scale_log2 : -INFINITY;
+      tmax = fmaxf(tmax, lg[e]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = m_new == -INFINITY ? 1.0f : exp2f(m_run - m_new);
+    float psum = 0.0f;
+    float pv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = lg[e] == -INFINITY ? 0.0f : exp2f(lg[e] - m_new);
+      psum += p;
+      pv[e] = p * vscale[e];
+    }
+    psum += __shfl_xor(psum, 16);
+    psum += __shfl_xor(psum, 32);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+
+    // P (A operand of PV): high and low parts
+    u32x4 phi, plo;
+    {
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        const float x0 = pv[2 * pp], x1 = pv[2 * pp + 1];
+        if constexpr (BF) {
+          const uint16_t h0 = f32_to_bf16_rn(x0), h1 = f32_to_bf16_rn(x1);
+          const float r0f = x0 - __uint_as_float((uint32_t)h0 << 16);
+          const float r1f = x1 - __uint_as_float((uint32_t)h1 << 16);
+          hw[pp] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+          lw[pp] = (uint32_t)f32_to_bf16_rn(r0f) | ((uint32_t)f32_to_bf16_rn(r1f) << 16);
+        } else {
+          const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+          const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
+          hw[pp] = __builtin_bit_cast(uint32_t, (f16x2){h0, h1});
+          lw[pp] = __builtin_bit_cast(uint32_t, (f16x2){l0, l1});
+        }
+      }
+      phi = (u32x4){hw[0], hw[1], hw[2], hw[3]};
+      plo = (u32x4){lw[0], lw[1], lw[2], lw[3]};
+    }
+    // rescale the running output rows (heads 4g+e) by their alpha
+    float arow[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) arow[e] = __shfl(alpha, 4 * g + e);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      o[t][0] *= arow[0];
+      o[t][1] *= arow[1];
+      o[t][2] *= arow[2];
+      o[t][3] *= arow[3];
+    }
+    // ---- PV: N-tile t holds column d = i16*(D/16) + t ----
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      uint32_t bw[4];
+      if constexpr (KVT == KV_I8) {
+        const int dw = t >> 2, by = t & 3;
+        const uint32_t sel = (uint32_t)by | (0x0Cu << 8) | ((uint32_t)(4 + by) << 16) | (0x0Cu << 24);
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          const uint32_t x = __builtin_amdgcn_perm(vraw[2 * pp + 1][0][dw], vraw[2 * pp][0][dw], sel) ^ 0x64806480u;
+          f16x2 hv = __builtin_bit_cast(f16x2, x);
+          hv = hv - (f16x2){(_Float16)1152.0f, (_Float16)1152.0f};
+          bw[pp] = __builtin_bit_cast(uint32_t, hv);
+        }
+      } else {
+        // 16-bit elements: element t is half (t&1) of dword t>>1 of the slice
+        const int dw = t >> 1;
+        const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp)
+          bw[pp] = __builtin_amdgcn_perm(vraw[2 * pp + 1][dw >> 2][dw & 3], vraw[2 * pp][dw >> 2][dw & 3], sel);
+      }
+      const u32x4 bv = (u32x4){bw[0], bw[1], bw[2], bw[3]};
+      o[t] = mfma<BF>(phi, bv, o[t]);
+      o[t] = mfma<BF>(plo, bv, o[t]);
+    }
+  }
+
+  // ---- merge the 4 waves of the workgroup in LDS ----
+  if (g == 0) {
+    s_m[wave][i16] = m_run;
+    s_l[wave][i16] = l_run;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int j = 4 * g + e;
+    if (j < G) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) s_o[((size_t)wave * G + j) * D + i16 * (D / 16) + t] = o[t][e];
+    }
+  }
+  __syncthreads();
+  const size_t pbase = ((size_t)b * Hkv + h) * n_chunks + c;
+  for (int x = threadIdx.x; x < G * D; x += blockDim.x) {
+    const int j = x / D, d = x % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kAttWaves; ++w) M = fmaxf(M, s_m[w][j]);
+    float acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kAttWaves; ++w) {
+      const float f = s_m[w][j] == -INFINITY ? 0.0f : exp2f(s_m[w][j] - M);
+      acc += s_o[((size_t)w * G + j) * D + d] * f;
+    }
+    part_o[(pbase * G + j) * D + d] = acc;
+    if (d == 0) {
+      float Ls = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kAttWaves; ++w)
+        Ls += s_m[w][j] == -INFINITY ? 0.0f : s_l[w][j] * exp2f(s_m[w][j] - M);
+      part_ml[(pbase * 16 + j) * 2 + 0] = M;
+      part_ml[(pbase * 16 + j) * 2 + 1] = Ls;
+    }
+  }
+}
+
+// merge the chunks of each (sequence, query head) in ascending chunk order
+__global__ __launch_bounds__(256) void attend_merge_kernel(
+    const float* __restrict__ part_ml, const float* __restrict__ part_o,
+    const int32_t* __restrict__ n_sel, int cap, int Hq, int Hkv, int D, int n_chunks,
+    float* __restrict__ out) {
+  const int jq = blockIdx.x, b = blockIdx.y;
+  const int G = Hq / Hkv;
+  const int h = jq / G, j = jq % G;
+  int n = n_sel[b];
+  n = n < 0 ? 0 : (n > cap ? cap : n);
+  const int nc = (n + kAttRowsPerWG - 1) / kAttRowsPerWG;
+  const size_t pb = ((size_t)b * Hkv + h) * n_chunks;
+  float M = -INFINITY;
+  for (int c = 0; c < nc; ++c) M = fmaxf(M, part_ml[((pb + c) * 16 + j) * 2]);
+  float Ls = 0.0f;
+  for (int c = 0; c < nc; ++c) {
+    const float m = part_ml[((pb + c) * 16 + j) * 2];
+    if (m != -INFINITY) Ls += part_ml[((pb + c) * 16 + j) * 2 + 1] * exp2f(m - M);
+  }
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float acc = 0.0f;
+    for (int c = 0; c < nc; ++c) {
+      const float m = part_ml[((pb + c) * 16 + j) * 2];
+      if (m != -INFINITY) acc += part_o[((pb + c) * G + j) * D + d] * exp2f(m - M);
+    }
+    out[((size_t)b * Hq + jq) * D + d] = Ls > 0.0f ? acc / Ls : 0.0f;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attend(const skv_layer_desc& d, const void* q, const skv_kv_view& kv,
+                         const int32_t* idx, const int32_t* n_sel, float sm_scale, float* out,
+                         void* ws, const WsLayout& Lw, hipStream_t st) {
+  uint32_t* flags = ws_ptr<uint32_t>(ws, Lw.flags);
+  float* part_ml = ws_ptr<float>(ws, Lw.att_ml);
+  float* part_o = ws_ptr<float>(ws, Lw.att_o);
+  const int cap = select_capacity(d);
+  const int G = d.n_q_heads / d.n_kv_heads;
+  const dim3 grid(d.n_kv_heads, Lw.n_att_chunks, d.batch);
+  const size_t lds = (size_t)kAttWaves * G * d.head_dim * sizeof(float);
+  const float sl = sm_scale * kLog2e;
+#define SKV_AT(KVT, DD)                                                                          \
+  hipLaunchKernelGGL((attend_kernel<KVT, DD>), grid, dim3(kAttThreads), lds, st, q,              \
+                     (const uint8_t*)kv.k, (const uint8_t*)kv.v, kv.k_scale, kv.v_scale, kv.rows, \
+                     idx, n_sel, cap, sl, d.n_q_heads, d.n_kv_heads, part_ml, part_o,             \
+                     Lw.n_att_chunks, flags)
+  const int kvt = d.kv_dtype == SKV_KV_I8_ROWSCALE ? KV_I8 : (d.kv_dtype == SKV_KV_F16 ? KV_F16 : KV_BF16);
+  if (kvt == KV_I8 && d.head_dim == 256) SKV_AT(KV_I8, 256);
+  else if (kvt == KV_I8 && d.head_dim == 128) SKV_AT(KV_I8, 128);
+  else if (kvt == KV_F16 && d.head_dim == 256) SKV_AT(KV_F16, 256);
+  else if (kvt == KV_F16 && d.head_dim == 128) SKV_AT(KV_F16, 128);
+  else if (kvt == KV_BF16 && d.head_dim == 256) SKV_AT(KV_BF16, 256);
+  else if (kvt == KV_BF16 && d.head_dim == 128) SKV_AT(KV_BF16, 128);
+  else return hipErrorInvalidValue;
+#undef SKV_AT
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attend_merge_kernel, dim3(d.n_q_heads, d.batch), dim3(256), 0, st, part_ml,
+                     part_o, n_sel, cap, d.n_q_heads, d.n_kv_heads, d.head_dim, Lw.n_att_chunks,
+                     out);
+  return hipGetLastError();
+}
+
+}  // namespace skv

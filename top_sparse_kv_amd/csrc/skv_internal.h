@@ -1,0 +1,135 @@
+// Internal declarations of the gfx950 sparse-KV library: workspace layout,
+// small device helpers and the kernel launchers used by api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/sparsekv.h"
+
+namespace skv {
+
+// ---------------------------------------------------------------------------
+// constants
+// ---------------------------------------------------------------------------
+constexpr int kHistBits = 13;                 // coarse-key histogram digit
+constexpr int kHistBins = 1 << kHistBits;     // 8192 bins
+constexpr int kListCap = 8192;                // candidate list capacity per sequence
+constexpr int kMaxTopk = 4096;                // largest budget the select kernel sorts in LDS
+constexpr int kHistChunk = 4096;              // keys per histogram / collect workgroup
+constexpr int kAttRowsPerWave = 64;           // selected rows per attention wave
+constexpr int kAttWaves = 4;                  // waves per attention workgroup
+constexpr int kAttRowsPerWG = kAttRowsPerWave * kAttWaves;
+constexpr int kScoreChunk = 2048;             // tokens per sketch-score workgroup
+constexpr int kPooledChunk = 1024;            // blocks per pooled-score workgroup
+
+// per-sequence select state (u32 words)
+struct TopkState {
+  uint32_t done;       // histogram workgroups finished
+  uint32_t beta;       // threshold bucket
+  uint32_t n_c;        // candidates with bucket >= beta
+  uint32_t list_count; // candidates written to the list
+  uint32_t mode;       // 0 fast, 1 dense, 2 slow (exact search over all keys), 3 empty
+  uint32_t pad[11];
+};
+enum { kModeFast = 0, kModeDense = 1, kModeSlow = 2 };
+
+// ---------------------------------------------------------------------------
+// workspace layout (host and device agree through this struct)
+// ---------------------------------------------------------------------------
+struct WsLayout {
+  size_t flags;        // uint32 flag word (+ padding)
+  size_t hist;         // [B][kHistBins] u32
+  size_t state;        // [B] TopkState
+  size_t lkey;         // [B][kListCap] u64 ordered keys
+  size_t lpos;         // [B][kListCap] u32 positions
+  size_t att_ml;       // [B][H_kv][n_chunks][16][2] f32  (m, l) per head row
+  size_t att_o;        // [B][H_kv][n_chunks][G][D] f32
+  size_t total;
+  int n_att_chunks;
+};
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline int select_capacity(const skv_layer_desc& d) {
+  return d.index_mode == SKV_INDEX_SKETCH_INT4 ? d.n_sink + d.topk + d.n_tail : 4 * d.topk + 3;
+}
+
+inline WsLayout ws_layout(const skv_layer_desc& d) {
+  WsLayout w{};
+  size_t off = 0;
+  const size_t B = (size_t)d.batch;
+  w.flags = off;  off = align_up(off + 256, 256);
+  w.hist = off;   off = align_up(off + B * kHistBins * 4, 256);
+  w.state = off;  off = align_up(off + B * sizeof(TopkState), 256);
+  w.lkey = off;   off = align_up(off + B * kListCap * 8, 256);
+  w.lpos = off;   off = align_up(off + B * kListCap * 4, 256);
+  const int cap = select_capacity(d);
+  w.n_att_chunks = (cap + kAttRowsPerWG - 1) / kAttRowsPerWG;
+  const int G = d.n_q_heads / d.n_kv_heads;
+  w.att_ml = off; off = align_up(off + B * d.n_kv_heads * w.n_att_chunks * 16 * 2 * 4, 256);
+  w.att_o = off;  off = align_up(off + B * d.n_kv_heads * w.n_att_chunks * (size_t)G * d.head_dim * 4, 256);
+  w.total = off;
+  return w;
+}
+
+template <typename T>
+inline T* ws_ptr(void* ws, size_t off) { return reinterpret_cast<T*>(reinterpret_cast<char*>(ws) + off); }
+
+// ---------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void raise_flag(uint32_t* flags, uint32_t bit) {
+  atomicOr(flags, bit);
+}
+
+// Clamp a device-side context length into [0, max_ctx], flagging bad values.
+__device__ __forceinline__ int clamp_ctx(const int32_t* ctx_len, int b, int max_ctx, uint32_t* flags) {
+  int T = ctx_len[b];
+  if (T < 0 || T > max_ctx) {
+    if (flags) raise_flag(flags, SKV_FLAG_CTX_RANGE);
+    T = T < 0 ? 0 : max_ctx;
+  }
+  return T;
+}
+
+// Order-preserving maps of floating point keys onto unsigned integers
+// (larger key -> larger integer).  -0 must already be canonicalised to +0.
+__device__ __forceinline__ uint64_t ordered_u64(double x) {
+  uint64_t u = (uint64_t)__double_as_longlong(x);
+  return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
+}
+__device__ __forceinline__ uint32_t ordered_u32(float x) {
+  uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+// Histogram digit of an exact key: top kHistBits of the order-preserving image
+// of the key rounded to fp32 (rounding is monotone, so digits are ordered).
+__device__ __forceinline__ uint32_t key_digit(double x) {
+  return ordered_u32(__double2float_rn(x)) >> (32 - kHistBits);
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t h) {
+  return __half2float(__ushort_as_half(h));
+}
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// launchers (each returns hipSuccess or the launch error)
+// ---------------------------------------------------------------------------
+hipError_t launch_qsketch(const skv_layer_desc& d, const void* q, const float* basis, int8_t* qs,
+                          float* qs_scale, hipStream_t st);
+hipError_t launch_score(const skv_layer_desc& d, const int32_t* ctx_len, const void* iq,
+                        const void* ik, const uint16_t* isc, double* keys, uint32_t* flags,
+                        hipStream_t st);
+hipError_t launch_topk(const skv_layer_desc& d, const int32_t* ctx_len, const double* keys,
+                       int32_t* idx, int32_t* n_sel, void* ws, const WsLayout& L, hipStream_t st);
+hipError_t launch_attend(const skv_layer_desc& d, const void* q, const skv_kv_view& kv,
+                         const int32_t* idx, const int32_t* n_sel, float sm_scale, float* out,
+                         void* ws, const WsLayout& L, hipStream_t st);
+
+}  // namespace skv

@@ -1,0 +1,504 @@
+// Host-RAM KV tier with a GPU hot buffer (stage A5).
+//
+// Page "8 agents x 250K context on two 3090s: sparse KV decode with a rank-64
+// key sketch and a host-RAM tier", section "The mechanism": the full K/V lives
+// in pinned host RAM at int4 (64-dim groups, fp16 scales, 272 B per
+// token-head), turned back into int8 rows when fetched; the GPU keeps the
+// sinks, the recent tail and a hot buffer of 2.5% of the tokens managed by
+// windowed CLOCK; hot-buffer misses read only the picked rows from pinned
+// memory over PCIe.  Page "3.14M Context on 3x 3090: The Power of an
+// Architecture That Puts KV Cache in Host RAM", sections "No Need to Rewrite
+// the Kernel": the GPU reads host-mapped memory directly (zero copy), which
+// needs no per-layer host synchronization and keeps the step capturable.
+//
+// Host memory: hipHostMalloc(mapped | portable) -- pinned at allocation --
+// rather than registering an existing anonymous mapping, and the kernel reads
+// it through the device address hipHostGetDevicePointer returns.
+//
+// Per step: tier_resolve (one workgroup per sequence) marks hits, then one
+// wave places the misses in ascending position order with the CLOCK hand,
+// holding a 64-slot window of the slot table in registers and resolving each
+// miss with one ballot; tier_fetch (many workgroups) reads the missed records
+// over PCIe and writes int8 rows + fp16 scales into their slots.
+#include "skv_internal.h"
+
+#include <new>
+#include <string.h>
+
+struct skv_tier {
+  skv_tier_desc desc;
+  int B, T, S, L, k, Hkv, D, n_slots, W, cap;
+  int rec_bytes;      // per token-head: K row + V row
+  int row_bytes;      // one K (or V) host row
+  void* host;         // host records (host address)
+  bool own_host;
+  const uint8_t* host_dev;  // device address of the host records
+  int64_t res_rows;   // S + L + n_slots
+  int8_t* res_k;
+  int8_t* res_v;
+  uint16_t* res_ks;
+  uint16_t* res_vs;
+  int32_t* slot_pos;     // [B][n_slots]
+  int32_t* slot_last;    // [B][n_slots]
+  int32_t* slot_ref;     // [B][n_slots]
+  int32_t* hand;         // [B]
+  int32_t* slot_of_pos;  // [B][T]
+  int32_t* miss_pos;     // [B][k]
+  int32_t* miss_slot;    // [B][k]
+  int32_t* miss_count;   // [B]
+  unsigned long long* counters;  // picks, hits, misses
+  uint32_t* flags;
+  int64_t steps;
+};
+
+namespace skv {
+namespace {
+
+constexpr int kResolveThreads = 1024;
+constexpr int kMaxSlots = 12288;     // slot table held in LDS
+constexpr int kNoStep = -(1 << 30);
+
+__global__ void tier_reset_kernel(int32_t* slot_pos, int32_t* slot_last, int32_t* slot_ref,
+                                  int32_t* hand, int32_t* slot_of_pos, unsigned long long* counters,
+                                  int B, int n_slots, int T) {
+  const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t nth = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = tid; i < (size_t)B * n_slots; i += nth) {
+    slot_pos[i] = -1;
+    slot_last[i] = kNoStep;
+    slot_ref[i] = 0;
+  }
+  for (size_t i = tid; i < (size_t)B * T; i += nth) slot_of_pos[i] = -1;
+  for (size_t i = tid; i < (size_t)B; i += nth) hand[i] = 0;
+  if (tid < 3) counters[tid] = 0ull;
+}
+
+__global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ n_sel, int32_t* __restrict__ rows,
+    int32_t* __restrict__ slot_pos, int32_t* __restrict__ slot_last, int32_t* __restrict__ slot_ref,
+    int32_t* __restrict__ hand_arr, int32_t* __restrict__ slot_of_pos,
+    int32_t* __restrict__ miss_pos, int32_t* __restrict__ miss_slot, int32_t* __restrict__ miss_count,
+    unsigned long long* __restrict__ counters, uint32_t* __restrict__ flags, int T, int S, int L,
+    int k, int n_slots, int W, int cap, int step) {
+  __shared__ int32_t s_pos[kMaxSlots];
+  __shared__ int32_t s_last[kMaxSlots];
+  __shared__ uint8_t s_ref[kMaxSlots];
+  __shared__ int32_t s_miss[kMaxTopk];
+  __shared__ uint32_t s_wsum[kResolveThreads / 64];
+  __shared__ int s_nm, s_nmid, s_bad;
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int32_t* sp = slot_pos + (size_t)b * n_slots;
+  int32_t* sl = slot_last + (size_t)b * n_slots;
+  int32_t* sr = slot_ref + (size_t)b * n_slots;
+  int32_t* sop = slot_of_pos + (size_t)b * T;
+  for (int i = threadIdx.x; i < n_slots; i += blockDim.x) {
+    s_pos[i] = sp[i];
+    s_last[i] = sl[i];
+    s_ref[i] = (uint8_t)sr[i];
+  }
+  if (threadIdx.x == 0) {
+    s_nm = 0;
+    s_nmid = 0;
+    s_bad = 0;
+  }
+  int n = n_sel[b];
+  if (n < 0 || n > cap) {
+    if (threadIdx.x == 0) raise_flag(flags, SKV_FLAG_TIER_INPUT);
+    n = n < 0 ? 0 : cap;
+  }
+  const int32_t* ib = idx + (size_t)b * cap;
+  int32_t* rb = rows + (size_t)b * cap;
+  __syncthreads();
+
+  // phase A: classify; hits refresh their slot; misses listed in input order
+  const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  for (int base = 0; base < n; base += blockDim.x) {
+    const int i = base + threadIdx.x;
+    bool miss = false;
+    if (i < n) {
+      const int p = ib[i];
+      const bool sorted = i == 0 || ib[i - 1] < p;
+      if (p < 0 || p >= T || !sorted) {
+        s_bad = 1;
+        rb[i] = 0;
+      } else if (p < S) {
+        rb[i] = p;
+      } else if (p >= T - L) {
+        rb[i] = S + (p - (T - L));
+      } else {
+        atomicAdd(&s_nmid, 1);
+        const int s = sop[p];
+        if (s >= 0) {
+          s_ref[s] = 1;
+          s_last[s] = step;
+          rb[i] = S + L + s;
+        } else {
+          miss = true;
+        }
+      }
+    }
+    const uint64_t m = __ballot(miss);
+    if (lane == 0) s_wsum[wave] = (uint32_t)__popcll(m);
+    __syncthreads();
+    int off = s_nm;
+    for (int w = 0; w < wave; ++w) off += (int)s_wsum[w];
+    if (miss) {
+      const int at = off + (int)__popcll(m & lt_mask);
+      if (at < k) {
+        s_miss[at] = i;
+      } else {
+        rb[i] = 0;      // more middle picks than the budget: not placed, flagged
+        s_bad = 1;
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int tot = 0;
+      for (int w = 0; w < (int)(blockDim.x >> 6); ++w) tot += (int)s_wsum[w];
+      s_nm += tot;
+    }
+    __syncthreads();
+  }
+  // a victim always exists when fewer slots are pinned than exist: at most the
+  // middle picks of this step plus those of the previous W-1 steps
+  const bool fits = (int64_t)s_nmid < (int64_t)n_slots;
+  const int nm = fits ? min(s_nm, k) : 0;
+  if (!fits) {
+    for (int mi = threadIdx.x; mi < min(s_nm, k); mi += blockDim.x) rb[s_miss[mi]] = 0;
+    if (threadIdx.x == 0) s_bad = 1;
+  }
+  __syncthreads();
+
+  // phase B: one wave places the misses in ascending order (windowed CLOCK)
+  if (wave == 0) {
+    int hand = hand_arr[b];
+    int wbase = hand - hand % 64;
+    int off = hand - wbase;
+    int myslot = wbase + lane;
+    bool valid = myslot < n_slots;
+    int mpos = valid ? s_pos[myslot] : -1;
+    int mlast = valid ? s_last[myslot] : kNoStep;
+    int mref = valid ? (int)s_ref[myslot] : 0;
+    const int old_limit = step - W;   // last <= step - W: outside the window
+    const int max_moves = 2 * (n_slots / 64 + 2);   // two full sweeps always find a victim
+    for (int mi = 0; mi < nm; ++mi) {
+      const int i = s_miss[mi];
+      const int p = ib[i];
+      int moves = 0;
+      while (true) {
+        const bool elig = valid && lane >= off;
+        const bool unpinned = mlast <= old_limit;
+        const bool victim = elig && (mpos < 0 || (unpinned && mref == 0));
+        const uint64_t vm = __ballot(victim);
+        const int v = vm ? (int)__ffsll((unsigned long long)vm) - 1 : 64;
+        // slots the hand passes before the victim lose their reference bit
+        if (elig && lane < v && mpos >= 0 && unpinned && mref == 1) mref = 0;
+        if (vm) {
+          if (lane == v) {
+            if (mpos >= 0) sop[mpos] = -1;
+            mpos = p;
+            mref = 1;
+            mlast = step;
+            sop[p] = myslot;
+            rb[i] = S + L + myslot;
+            miss_pos[(size_t)b * k + mi] = p;
+            miss_slot[(size_t)b * k + mi] = myslot;
+          }
+          off = v + 1;
+        } else {
+          off = 64;
+        }
+        if (!vm && ++moves > max_moves) {
+          // cannot happen when n_slots > window * topk; stop instead of spinning
+          if (lane == 0) {
+            rb[i] = 0;
+            s_bad = 1;
+          }
+          break;
+        }
+        if (off >= 64 || wbase + off >= n_slots) {
+          // write the window back and move to the next one
+          if (valid) {
+            s_pos[myslot] = mpos;
+            s_last[myslot] = mlast;
+            s_ref[myslot] = (uint8_t)mref;
+          }
+          wbase = wbase + 64 >= n_slots ? 0 : wbase + 64;
+          off = 0;
+          myslot = wbase + lane;
+          valid = myslot < n_slots;
+          mpos = valid ? s_pos[myslot] : -1;
+          mlast = valid ? s_last[myslot] : kNoStep;
+          mref = valid ? (int)s_ref[myslot] : 0;
+        }
+        if (vm) break;
+      }
+    }
+    if (valid) {
+      s_pos[myslot] = mpos;
+      s_last[myslot] = mlast;
+      s_ref[myslot] = (uint8_t)mref;
+    }
+    if (lane == 0) {
+      hand_arr[b] = wbase + off;
+      miss_count[b] = nm;
+      atomicAdd(&counters[0], (unsigned long long)s_nmid);
+      atomicAdd(&counters[1], (unsigned long long)(s_nmid - nm));
+      atomicAdd(&counters[2], (unsigned long long)nm);
+      if (s_bad) raise_flag(flags, SKV_FLAG_TIER_INPUT);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < n_slots; i += blockDim.x) {
+    sp[i] = s_pos[i];
+    sl[i] = s_last[i];
+    sr[i] = (int32_t)s_ref[i];
+  }
+}
+
+// Reads missed host records over PCIe and writes int8 rows into their slots.
+// One wave per (miss, KV head): lanes 0-31 the K row, 32-63 the V row, 8 dims each.
+__global__ __launch_bounds__(256) void tier_fetch_kernel(
+    const uint8_t* __restrict__ host, const int32_t* __restrict__ miss_pos,
+    const int32_t* __restrict__ miss_slot, const int32_t* __restrict__ miss_count,
+    int8_t* __restrict__ res_k, int8_t* __restrict__ res_v, uint16_t* __restrict__ res_ks,
+    uint16_t* __restrict__ res_vs, int T, int Hkv, int k, int64_t res_rows, int res_off) {
+  constexpr int D = 256;
+  constexpr int ROWB = D / 2 + 2 * (D / 64);   // 136
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5, ln = lane & 31;
+  const int nm = miss_count[b];
+  const int nwaves = gridDim.x * (blockDim.x >> 6);
+  for (int task = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); task < nm * Hkv; task += nwaves) {
+    const int mi = task / Hkv, h = task % Hkv;
+    const int p = miss_pos[(size_t)b * k + mi];
+    const int slot = miss_slot[(size_t)b * k + mi];
+    const uint8_t* row = host + (((size_t)b * T + p) * Hkv + h) * (2 * ROWB) + half * ROWB;
+    const uint32_t codes = *reinterpret_cast<const uint32_t*>(row + 4 * ln);
+    const uint2 sc = *reinterpret_cast<const uint2*>(row + D / 2);
+    const float g0 = half_bits_to_float((uint16_t)(sc.x & 0xFFFF));
+    const float g1 = half_bits_to_float((uint16_t)(sc.x >> 16));
+    const float g2 = half_bits_to_float((uint16_t)(sc.y & 0xFFFF));
+    const float g3 = half_bits_to_float((uint16_t)(sc.y >> 16));
+    const float gmax = fmaxf(fmaxf(g0, g1), fmaxf(g2, g3));
+    const __half sp_h = __float2half_rn(__fdiv_rn(gmax * 7.0f, 127.0f));
+    const float spf = __half2float(sp_h);
+    const int grp = ln >> 3;    // 8 dims per lane, 64 dims per group
+    const float gs = grp == 0 ? g0 : (grp == 1 ? g1 : (grp == 2 ? g2 : g3));
+    uint32_t out[2] = {0u, 0u};
+    if (spf != 0.0f) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        int c = (int)((codes >> (4 * e)) & 0xFu);
+        c = (c ^ 8) - 8;
+        float r = rintf(__fdiv_rn((float)c * gs, spf));
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        out[e >> 2] |= ((uint32_t)(uint8_t)(int8_t)(int)r) << (8 * (e & 3));
+      }
+    }
+    const size_t rr = ((size_t)b * res_rows + res_off + slot) * Hkv + h;
+    int8_t* dst = (half ? res_v : res_k) + rr * D + 8 * ln;
+    *reinterpret_cast<uint2*>(dst) = make_uint2(out[0], out[1]);
+    if (ln == 0) (half ? res_vs : res_ks)[rr] = __half_as_ushort(sp_h);
+  }
+}
+
+}  // namespace
+}  // namespace skv
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+namespace skv {
+skv_status set_error(skv_status s, const char* fmt, ...);
+skv_status validate_desc(const skv_layer_desc* d);
+}  // namespace skv
+
+using skv::set_error;
+
+static void tier_free(skv_tier* t) {
+  if (!t) return;
+  void* dev[] = {t->res_k, t->res_v, t->res_ks, t->res_vs, t->slot_pos, t->slot_last, t->slot_ref,
+                 t->hand, t->slot_of_pos, t->miss_pos, t->miss_slot, t->miss_count, t->counters,
+                 t->flags};
+  for (void* p : dev)
+    if (p) (void)hipFree(p);
+  if (t->own_host && t->host) (void)hipHostFree(t->host);
+  delete t;
+}
+
+extern "C" skv_status sparsekv_tier_create(const skv_tier_desc* d, skv_tier** out) {
+  if (!d || !out) return set_error(SKV_ERR_INVALID, "tier_create: NULL argument");
+  *out = nullptr;
+  if (d->struct_size < sizeof(skv_tier_desc))
+    return set_error(SKV_ERR_INVALID, "tier_create: struct_size %u < %zu", d->struct_size, sizeof(skv_tier_desc));
+  skv_status s = skv::validate_desc(&d->layer);
+  if (s != SKV_OK) return s;
+  const skv_layer_desc& L = d->layer;
+  if (L.index_mode != SKV_INDEX_SKETCH_INT4 || L.kv_dtype != SKV_KV_I8_ROWSCALE || L.head_dim != 256)
+    return set_error(SKV_ERR_UNSUPPORTED, "tier: needs token mode, int8 K/V rows and head_dim 256");
+  if (d->ctx < 1 || d->ctx > L.max_ctx)
+    return set_error(SKV_ERR_INVALID, "tier: ctx %d outside [1, max_ctx=%d]", d->ctx, L.max_ctx);
+  if (d->window < 1) return set_error(SKV_ERR_INVALID, "tier: window %d < 1", d->window);
+  if ((int64_t)d->n_slots <= (int64_t)d->window * L.topk || d->n_slots > skv::kMaxSlots)
+    return set_error(SKV_ERR_INVALID, "tier: n_slots %d must exceed window*topk = %lld and be <= %d",
+                     d->n_slots, (long long)d->window * L.topk, skv::kMaxSlots);
+  skv_tier* t = new (std::nothrow) skv_tier();
+  if (!t) return set_error(SKV_ERR_OOM, "tier: host allocation failed");
+  memset(t, 0, sizeof(*t));
+  t->desc = *d;
+  t->B = L.batch; t->T = d->ctx; t->S = L.n_sink; t->L = L.n_tail; t->k = L.topk;
+  t->Hkv = L.n_kv_heads; t->D = L.head_dim; t->n_slots = d->n_slots; t->W = d->window;
+  t->cap = skv::select_capacity(L);
+  t->row_bytes = t->D / 2 + 2 * (t->D / 64);
+  t->rec_bytes = 2 * t->row_bytes;
+  t->res_rows = (int64_t)t->S + t->L + t->n_slots;
+  const size_t host_bytes = (size_t)t->B * t->T * t->Hkv * t->rec_bytes;
+  if (d->host_records) {
+    t->host = d->host_records;
+    t->own_host = false;
+  } else {
+    if (hipHostMalloc(&t->host, host_bytes, hipHostMallocMapped | hipHostMallocPortable) != hipSuccess) {
+      t->host = nullptr;
+      tier_free(t);
+      return set_error(SKV_ERR_OOM, "tier: hipHostMalloc of %zu bytes failed", host_bytes);
+    }
+    t->own_host = true;
+    memset(t->host, 0, host_bytes);
+  }
+  void* hd = nullptr;
+  if (hipHostGetDevicePointer(&hd, t->host, 0) != hipSuccess || !hd) {
+    (void)hipGetLastError();
+    tier_free(t);
+    return set_error(SKV_ERR_HOST_MEMORY, "tier: host records are not pinned and device-mapped");
+  }
+  t->host_dev = (const uint8_t*)hd;
+  const size_t rr = (size_t)t->B * t->res_rows * t->Hkv;
+  const size_t ns = (size_t)t->B * t->n_slots;
+  bool ok = hipMalloc(&t->res_k, rr * t->D) == hipSuccess &&
+            hipMalloc(&t->res_v, rr * t->D) == hipSuccess &&
+            hipMalloc(&t->res_ks, rr * 2) == hipSuccess &&
+            hipMalloc(&t->res_vs, rr * 2) == hipSuccess &&
+            hipMalloc(&t->slot_pos, ns * 4) == hipSuccess &&
+            hipMalloc(&t->slot_last, ns * 4) == hipSuccess &&
+            hipMalloc(&t->slot_ref, ns * 4) == hipSuccess &&
+            hipMalloc(&t->hand, (size_t)t->B * 4) == hipSuccess &&
+            hipMalloc(&t->slot_of_pos, (size_t)t->B * t->T * 4) == hipSuccess &&
+            hipMalloc(&t->miss_pos, (size_t)t->B * t->k * 4) == hipSuccess &&
+            hipMalloc(&t->miss_slot, (size_t)t->B * t->k * 4) == hipSuccess &&
+            hipMalloc(&t->miss_count, (size_t)t->B * 4) == hipSuccess &&
+            hipMalloc(&t->counters, 3 * sizeof(unsigned long long)) == hipSuccess &&
+            hipMalloc(&t->flags, 256) == hipSuccess;
+  if (!ok) {
+    (void)hipGetLastError();
+    tier_free(t);
+    return set_error(SKV_ERR_OOM, "tier: device allocation failed");
+  }
+  if (hipMemset(t->res_k, 0, rr * t->D) != hipSuccess || hipMemset(t->res_v, 0, rr * t->D) != hipSuccess ||
+      hipMemset(t->res_ks, 0, rr * 2) != hipSuccess || hipMemset(t->res_vs, 0, rr * 2) != hipSuccess ||
+      hipMemset(t->flags, 0, 256) != hipSuccess) {
+    tier_free(t);
+    return set_error(SKV_ERR_HIP, "tier: initial clear failed");
+  }
+  hipLaunchKernelGGL(skv::tier_reset_kernel, dim3(256), dim3(256), 0, 0, t->slot_pos, t->slot_last,
+                     t->slot_ref, t->hand, t->slot_of_pos, t->counters, t->B, t->n_slots, t->T);
+  if (hipGetLastError() != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    tier_free(t);
+    return set_error(SKV_ERR_HIP, "tier: reset kernel failed");
+  }
+  *out = t;
+  return SKV_OK;
+}
+
+extern "C" void* sparsekv_tier_host_records(skv_tier* t) { return t ? t->host : nullptr; }
+
+extern "C" skv_status sparsekv_tier_resident(skv_tier* t, skv_kv_view* v) {
+  if (!t || !v) return set_error(SKV_ERR_INVALID, "tier_resident: NULL argument");
+  v->k = t->res_k;
+  v->v = t->res_v;
+  v->k_scale = t->res_ks;
+  v->v_scale = t->res_vs;
+  v->rows = t->res_rows;
+  return SKV_OK;
+}
+
+extern "C" skv_status sparsekv_tier_load_resident(skv_tier* t, const int8_t* k, const int8_t* v,
+                                                  const uint16_t* ks, const uint16_t* vs,
+                                                  void* stream) {
+  if (!t || !k || !v || !ks || !vs) return set_error(SKV_ERR_INVALID, "tier_load_resident: NULL argument");
+  hipStream_t st = (hipStream_t)stream;
+  const size_t nres = (size_t)(t->S + t->L);
+  if (nres == 0) return SKV_OK;
+  const size_t rowb = (size_t)t->Hkv * t->D;   // bytes of one resident row (all heads)
+  const size_t sclb = (size_t)t->Hkv * 2;
+  for (int b = 0; b < t->B; ++b) {
+    const size_t dst = (size_t)b * t->res_rows;
+    const size_t src = (size_t)b * nres;
+    if (hipMemcpyAsync(t->res_k + dst * rowb, k + src * rowb, nres * rowb, hipMemcpyDeviceToDevice, st) != hipSuccess ||
+        hipMemcpyAsync(t->res_v + dst * rowb, v + src * rowb, nres * rowb, hipMemcpyDeviceToDevice, st) != hipSuccess ||
+        hipMemcpyAsync(t->res_ks + dst * t->Hkv, ks + src * t->Hkv, nres * sclb, hipMemcpyDeviceToDevice, st) != hipSuccess ||
+        hipMemcpyAsync(t->res_vs + dst * t->Hkv, vs + src * t->Hkv, nres * sclb, hipMemcpyDeviceToDevice, st) != hipSuccess)
+      return set_error(SKV_ERR_HIP, "tier_load_resident: copy failed");
+  }
+  return SKV_OK;
+}
+
+extern "C" skv_status sparsekv_tier_resolve(skv_tier* t, const int32_t* idx, const int32_t* n_sel,
+                                            int32_t step, int32_t* rows, void* stream) {
+  if (!t || !idx || !n_sel || !rows) return set_error(SKV_ERR_INVALID, "tier_resolve: NULL argument");
+  hipStream_t st = (hipStream_t)stream;
+  hipLaunchKernelGGL(skv::tier_resolve_kernel, dim3(t->B), dim3(skv::kResolveThreads), 0, st, idx,
+                     n_sel, rows, t->slot_pos, t->slot_last, t->slot_ref, t->hand, t->slot_of_pos,
+                     t->miss_pos, t->miss_slot, t->miss_count, t->counters, t->flags, t->T, t->S,
+                     t->L, t->k, t->n_slots, t->W, t->cap, step);
+  if (hipGetLastError() != hipSuccess) return set_error(SKV_ERR_HIP, "tier_resolve: launch failed");
+  hipLaunchKernelGGL(skv::tier_fetch_kernel, dim3(128, t->B), dim3(256), 0, st, t->host_dev,
+                     t->miss_pos, t->miss_slot, t->miss_count, t->res_k, t->res_v, t->res_ks,
+                     t->res_vs, t->T, t->Hkv, t->k, t->res_rows, t->S + t->L);
+  if (hipGetLastError() != hipSuccess) return set_error(SKV_ERR_HIP, "tier_fetch: launch failed");
+  t->steps += 1;
+  return SKV_OK;
+}
+
+extern "C" skv_status sparsekv_tier_stats(skv_tier* t, skv_tier_stats* out, void* stream) {
+  if (!t || !out) return set_error(SKV_ERR_INVALID, "tier_stats: NULL argument");
+  unsigned long long c[3] = {0, 0, 0};
+  uint32_t fl = 0;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess ||
+      hipMemcpy(c, t->counters, sizeof(c), hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(&fl, t->flags, 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return set_error(SKV_ERR_HIP, "tier_stats: readback failed");
+  out->steps = t->steps;
+  out->picks = (int64_t)c[0];
+  out->hits = (int64_t)c[1];
+  out->misses = (int64_t)c[2];
+  out->host_bytes = (int64_t)c[2] * t->Hkv * t->rec_bytes;
+  if (fl) return set_error(SKV_ERR_STATE, "tier: device flags 0x%x (invalid selection input)", fl);
+  return SKV_OK;
+}
+
+extern "C" skv_status sparsekv_tier_slots(skv_tier* t, int32_t* slot_pos_host, void* stream) {
+  if (!t || !slot_pos_host) return set_error(SKV_ERR_INVALID, "tier_slots: NULL argument");
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess ||
+      hipMemcpy(slot_pos_host, t->slot_pos, (size_t)t->B * t->n_slots * 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return set_error(SKV_ERR_HIP, "tier_slots: readback failed");
+  return SKV_OK;
+}
+
+extern "C" skv_status sparsekv_tier_reset(skv_tier* t, void* stream) {
+  if (!t) return set_error(SKV_ERR_INVALID, "tier_reset: NULL argument");
+  hipLaunchKernelGGL(skv::tier_reset_kernel, dim3(256), dim3(256), 0, (hipStream_t)stream,
+                     t->slot_pos, t->slot_last, t->slot_ref, t->hand, t->slot_of_pos, t->counters,
+                     t->B, t->n_slots, t->T);
+  if (hipGetLastError() != hipSuccess) return set_error(SKV_ERR_HIP, "tier_reset: launch failed");
+  t->steps = 0;
+  return SKV_OK;
+}
+
+extern "C" void sparsekv_tier_destroy(skv_tier* t) {
+  if (!t) return;
+  (void)hipDeviceSynchronize();
+  tier_free(t);
+}
