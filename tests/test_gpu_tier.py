@@ -64,7 +64,7 @@ def _run(B, T, S, L, k, n_slots, n_steps, check_out_steps, seed, window=1, devic
                     want_rows = np.concatenate([np.arange(S), S + L + ref[b].slot_of[picks[s, b]],
                                                 S + np.arange(L)])
                     assert np.array_equal(gr[b], want_rows), "step %d seq %d rows" % (s, b)
-                    o = oracle.tier_attention(c.q[b].numpy(), rec_np[b], rk[b], rv[b], rks[b], rvs[b],
+                    o = oracle.tier_attention(c.q[b].cpu().numpy(), rec_np[b], rk[b], rv[b], rks[b], rvs[b],
                                               idx_np[b], T, S, L, sm, 6, 256)
                     err = float(np.max(np.abs(go[b] - o)))
                     assert err <= ATOL, "step %d seq %d err %g" % (s, b, err)

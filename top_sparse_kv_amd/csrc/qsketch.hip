@@ -11,6 +11,10 @@
 // The int8 codes are a decision taken on floating point values, so the
 // evaluation order is fixed and every operation is a separately rounded fp32
 // operation (no fused multiply-add): the codes are reproducible bit for bit.
+// Plain operators are used under `fp contract(off)` (library helpers such as
+// __fmul_rn can still be fused once inlined), and the two quotients are
+// computed in fp64 and rounded once to fp32, which equals the correctly
+// rounded fp32 quotient because 53 >= 2*24 + 2.
 #include "skv_internal.h"
 
 namespace skv {
@@ -35,7 +39,7 @@ __global__ __launch_bounds__(kQsThreads) void qsketch_kernel(
     const int h = i / D, dd = i % D;
     const __half* qp = q + ((size_t)b * Hq + (size_t)h * G) * D + dd;
     float acc = __half2float(qp[0]);
-    for (int j = 1; j < G; ++j) acc = __fadd_rn(acc, __half2float(qp[(size_t)j * D]));
+    for (int j = 1; j < G; ++j) acc = acc + __half2float(qp[(size_t)j * D]);
     qbar[i] = acc;
   }
   __syncthreads();
@@ -47,7 +51,10 @@ __global__ __launch_bounds__(kQsThreads) void qsketch_kernel(
     const float* bp = basis + (size_t)h * D * R + r;
     const float* qb = qbar + h * D;
     float s = 0.0f;
-    for (int dd = 0; dd < D; ++dd) s = __fadd_rn(s, __fmul_rn(qb[dd], bp[(size_t)dd * R]));
+    for (int dd = 0; dd < D; ++dd) {
+      const float p = qb[dd] * bp[(size_t)dd * R];
+      s = s + p;
+    }
     sval[i] = s;
     amax = fmaxf(amax, fabsf(s));
   }
@@ -58,11 +65,11 @@ __global__ __launch_bounds__(kQsThreads) void qsketch_kernel(
   amax = red[0];
   for (int w = 1; w < (int)(blockDim.x >> 6); ++w) amax = fmaxf(amax, red[w]);
 
-  const float scale = amax == 0.0f ? 0.0f : __fdiv_rn(amax, 127.0f);
+  const float scale = amax == 0.0f ? 0.0f : (float)((double)amax / 127.0);
   for (int i = threadIdx.x; i < n; i += blockDim.x) {
     int code = 0;
     if (amax != 0.0f) {
-      float r = rintf(__fdiv_rn(sval[i], scale));
+      float r = rintf((float)((double)sval[i] / (double)scale));
       r = fminf(fmaxf(r, -127.0f), 127.0f);
       code = (int)r;
     }

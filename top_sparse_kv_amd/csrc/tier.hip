@@ -283,7 +283,8 @@ __global__ __launch_bounds__(256) void tier_fetch_kernel(
     const float g2 = half_bits_to_float((uint16_t)(sc.y & 0xFFFF));
     const float g3 = half_bits_to_float((uint16_t)(sc.y >> 16));
     const float gmax = fmaxf(fmaxf(g0, g1), fmaxf(g2, g3));
-    const __half sp_h = __float2half_rn(__fdiv_rn(gmax * 7.0f, 127.0f));
+    // fp32 quotients via one fp64 divide + one rounding (= correctly rounded fp32)
+    const __half sp_h = __float2half_rn((float)((double)(gmax * 7.0f) / 127.0));
     const float spf = __half2float(sp_h);
     const int grp = ln >> 3;    // 8 dims per lane, 64 dims per group
     const float gs = grp == 0 ? g0 : (grp == 1 ? g1 : (grp == 2 ? g2 : g3));
@@ -293,7 +294,7 @@ __global__ __launch_bounds__(256) void tier_fetch_kernel(
       for (int e = 0; e < 8; ++e) {
         int c = (int)((codes >> (4 * e)) & 0xFu);
         c = (c ^ 8) - 8;
-        float r = rintf(__fdiv_rn((float)c * gs, spf));
+        float r = rintf((float)((double)((float)c * gs) / (double)spf));
         r = fminf(fmaxf(r, -127.0f), 127.0f);
         out[e >> 2] |= ((uint32_t)(uint8_t)(int8_t)(int)r) << (8 * (e & 3));
       }
