@@ -104,6 +104,11 @@ class Layer:
     def topk(self, ws):
         skv.topk(self.desc, self.ctx, self.keys, self.idx, self.nsel, ws)
 
+    def score_topk(self, ws):
+        iq = self.qs if self.iq is None else self.iq
+        skv.score_topk(self.desc, self.ctx, iq, self.ikeys, self.iscale, self.keys, self.idx,
+                       self.nsel, ws)
+
     def attend(self, ws):
         skv.attend(self.desc, self.q, self.kv, self.idx, self.nsel, self.sm, self.out, ws)
 
@@ -219,7 +224,8 @@ def main():
     skv.check(ws)
     nk = max(50, args.steps // 2)
     kt = {}
-    for name in (["qsketch"] if cfg["kind"] == "token" else []) + ["score", "topk", "attend"]:
+    for name in (["qsketch"] if cfg["kind"] == "token" else []) + ["score", "score_topk", "topk",
+                                                                   "attend"]:
         fn = getattr(Layer, name)
         for i in range(5):
             fn(layers[i % n_layers], ws)

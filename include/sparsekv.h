@@ -90,7 +90,8 @@ enum {
  *
  * T = ctx_len[b] counts the tokens in the cache including the current one.
  * Supported: head_dim in {128, 256}, n_q_heads / n_kv_heads in [1, 16],
- * K/V int8 + fp16 row scale or fp16 (token mode), bf16 (block mode).
+ * K/V int8 + fp16 row scale (head_dim 256) or fp16 (token mode), bf16 (block
+ * mode), topk <= 4096, at most 16384 selected positions per sequence.
  */
 typedef struct {
   uint32_t struct_size;   /* sizeof(skv_layer_desc) */
@@ -148,7 +149,7 @@ skv_status sparsekv_workspace_size(const skv_layer_desc* d, size_t* bytes);
  * through a rank-R projection onto a frozen basis, one pick per layer shared
  * by the KV heads; the query side is an int8 vector.
  *   q        [B][H_q][D] fp16
- *   basis    [H_kv][D][R] fp32
+ *   basis    [H_kv][D][R] fp32 (basis vector r of KV head h is basis[h][:][r])
  *   qs       [B][H_kv*R] int8 out:  clamp(rint(s/qscale), +-127) where, per KV
  *            head h, s_h = sum over d ascending of (qbar_h[d] * basis_h[d][r])
  *            with qbar_h = sum of the G query heads of h in ascending order,
@@ -190,6 +191,14 @@ skv_status sparsekv_score(const skv_layer_desc* d, const int32_t* ctx_len,
  *         n_sel[b] are unspecified); n_sel [B] int32 out. */
 skv_status sparsekv_topk(const skv_layer_desc* d, const int32_t* ctx_len, const double* keys,
                          int32_t* idx, int32_t* n_sel, void* ws, size_t ws_bytes, void* stream);
+
+/* Stages A2 + A3 in one call: writes keys (as sparsekv_score) and idx / n_sel
+ * (identical to sparsekv_topk on those keys), with the select stage's coarse
+ * histogram built while scoring instead of by a separate pass over the keys. */
+skv_status sparsekv_score_topk(const skv_layer_desc* d, const int32_t* ctx_len,
+                               const void* index_query, const void* index_keys,
+                               const uint16_t* index_scale, double* keys, int32_t* idx,
+                               int32_t* n_sel, void* ws, size_t ws_bytes, void* stream);
 
 /* ---- stage A4: exact GQA attention over the selected rows -----------------
  * Page "8 agents x 250K ...", section "The mechanism" (exact attention on the

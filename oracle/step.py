@@ -73,7 +73,8 @@ def unpack_int4(codes: np.ndarray) -> np.ndarray:
 
 
 def query_sketch(q: np.ndarray, basis: np.ndarray, group: int) -> Tuple[np.ndarray, np.ndarray]:
-    """q [B][H_q][D] fp16, basis [H_kv][D][R] fp32 -> (qs int8 [B][H_kv*R], qscale fp32 [B]).
+    """q [B][H_q][D] fp16, basis [H_kv][D][R] fp32 (basis vector r of KV head h
+    is basis[h][:, r]) -> (qs int8 [B][H_kv*R], qscale fp32 [B]).
 
     Reading: the G query heads of a KV head are summed (scoring is linear, so
     the shared pick of a KV head is the sum of its heads' scores); the summed
@@ -82,7 +83,7 @@ def query_sketch(q: np.ndarray, basis: np.ndarray, group: int) -> Tuple[np.ndarr
 
     Fixed fp32 evaluation order (both sides take the int8 decision in fp32):
       qbar = ((q_0 + q_1) + q_2) + ...            (fp32 adds, ascending head)
-      s    = 0;  for d ascending: s = s + (qbar_d * B_d)   (separately rounded
+      s    = 0;  for d ascending: s = s + (qbar_d * B_dr)   (separately rounded
              fp32 multiply and add; no fused multiply-add)
       qscale = amax / 127   (fp32, correctly rounded)
       qs   = clamp(rint(s / qscale), -127, 127), or 0 when amax == 0.

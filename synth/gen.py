@@ -107,9 +107,10 @@ def flush_bf16_domain(x: torch.Tensor) -> torch.Tensor:
 
 
 def orthonormal_basis(n_kv: int, D: int, R: int, seed: int) -> torch.Tensor:
-    """Seeded random orthonormal basis [n_kv][D][R] fp32 (QR of a Gaussian
-    matrix, computed on the CPU in fp64).  It stands in for the frozen
-    rank-64 eigenbasis of real post-RoPE keys, which is not available."""
+    """Seeded random orthonormal basis [n_kv][D][R] fp32 (basis vector r of KV
+    head h is column [h][:, r]); QR of a Gaussian matrix computed on the CPU in
+    fp64.  It stands in for the frozen rank-64 eigenbasis of real post-RoPE
+    keys, which is not available."""
     g = _gen("cpu", seed, _T_BASIS)
     a = torch.randn((n_kv, D, R), generator=g, dtype=torch.float64)
     out = torch.empty((n_kv, D, R), dtype=torch.float64)

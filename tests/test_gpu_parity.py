@@ -263,3 +263,41 @@ def test_full_config4b_mixed():
     _check_token(c, g, o, seqs)
     for b in range(32):
         assert g["n_sel"][b] == min(lens[b], 3136)
+
+
+@pytest.mark.parametrize("mode", ["token", "block"])
+def test_score_topk_matches_separate_calls(mode):
+    """The fused score+select entry point gives the keys and index sets of
+    sparsekv_score followed by sparsekv_topk, bit for bit."""
+    skv = need_gpu()
+    if mode == "token":
+        c = _cfg2(4, 60_000, [60_000, 30_000, 3_500, 3_100], device="cuda")
+        desc = token_desc_of(skv, c)
+        qs = torch.zeros((c.B, 256), dtype=torch.int8, device="cuda")
+        qsc = torch.zeros((c.B,), dtype=torch.float32, device="cuda")
+        ws = skv.workspace(desc)
+        skv.qsketch(desc, c.q, c.basis, qs, qsc, ws)
+        iq, ik, isc, nkeys = qs, c.codes, c.sk_scale, c.T_max
+    else:
+        c = _cfg3(3, 80_000, [80_000, 40_001, 2_055], device="cuda")
+        desc = block_desc_of(skv, c)
+        ws = skv.workspace(desc)
+        iq, ik, isc, nkeys = c.qi, c.kp, None, c.T_max // 4
+    cap = skv.select_capacity(desc)
+    res = []
+    for fused in (False, True):
+        keys = torch.full((c.B, nkeys), float("nan"), dtype=torch.float64, device="cuda")
+        idx = torch.full((c.B, cap), -1, dtype=torch.int32, device="cuda")
+        nsel = torch.zeros((c.B,), dtype=torch.int32, device="cuda")
+        if fused:
+            skv.score_topk(desc, c.ctx_len, iq, ik, isc, keys, idx, nsel, ws)
+        else:
+            skv.score(desc, c.ctx_len, iq, ik, isc, keys, ws)
+            skv.topk(desc, c.ctx_len, keys, idx, nsel, ws)
+        skv.check(ws)
+        res.append((keys.cpu().numpy(), idx.cpu().numpy(), nsel.cpu().numpy()))
+    (k0, i0, n0), (k1, i1, n1) = res
+    assert np.array_equal(k0, k1, equal_nan=True)
+    assert np.array_equal(n0, n1)
+    for b in range(c.B):
+        assert np.array_equal(i0[b, :n0[b]], i1[b, :n1[b]])

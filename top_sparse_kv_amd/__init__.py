@@ -121,6 +121,14 @@ def topk(desc, ctx_len, keys, idx, n_sel, ws, stream=None):
                                _p(ws), ws.numel(), _stream(stream)))
 
 
+def score_topk(desc, ctx_len, index_query, index_keys, index_scale, keys, idx, n_sel, ws,
+               stream=None):
+    _dev(ctx_len, index_query, index_keys, index_scale, keys, idx, n_sel, ws)
+    _check(lib().sparsekv_score_topk(ctypes.byref(desc), _p(ctx_len), _p(index_query),
+                                     _p(index_keys), _p(index_scale), _p(keys), _p(idx),
+                                     _p(n_sel), _p(ws), ws.numel(), _stream(stream)))
+
+
 def attend(desc, q, kv: KVView, idx, n_sel, sm_scale, out, ws, stream=None):
     _dev(q, idx, n_sel, out, ws)
     _check(lib().sparsekv_attend(ctypes.byref(desc), _p(q), ctypes.byref(kv), _p(idx), _p(n_sel),

@@ -63,6 +63,8 @@ SIGNATURES = [
     ("sparsekv_qsketch", c_i32, [P(LayerDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     ("sparsekv_score", c_i32, [P(LayerDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     ("sparsekv_topk", c_i32, [P(LayerDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    ("sparsekv_score_topk", c_i32, [P(LayerDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                    c_sz, c_vp]),
     ("sparsekv_attend", c_i32, [P(LayerDesc), c_vp, P(KVView), c_vp, c_vp, ctypes.c_float, c_vp,
                                 c_vp, c_sz, c_vp]),
     ("sparsekv_step", c_i32, [P(LayerDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,

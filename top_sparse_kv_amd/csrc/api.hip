@@ -66,6 +66,13 @@ skv_status validate_desc(const skv_layer_desc* d) {
   } else {
     return set_error(SKV_ERR_INVALID, "index_mode %d unknown", d->index_mode);
   }
+  {
+    const int64_t cand = d->index_mode == SKV_INDEX_SKETCH_INT4 ? d->max_ctx : d->max_ctx / 4;
+    if ((cand + kHistChunk - 1) / kHistChunk > 1024)
+      return set_error(SKV_ERR_UNSUPPORTED, "more than %d candidates per sequence", 1024 * kHistChunk);
+  }
+  if (select_capacity(*d) > 64 * kAttRowsPerWG)
+    return set_error(SKV_ERR_UNSUPPORTED, "select capacity %d > %d", select_capacity(*d), 64 * kAttRowsPerWG);
   return ok();
 }
 
@@ -174,6 +181,26 @@ skv_status sparsekv_topk(const skv_layer_desc* d, const int32_t* ctx_len, const 
   return launched(launch_topk(*d, ctx_len, keys, idx, n_sel, ws, L, (hipStream_t)stream), "topk");
 }
 
+skv_status sparsekv_score_topk(const skv_layer_desc* d, const int32_t* ctx_len,
+                               const void* index_query, const void* index_keys,
+                               const uint16_t* index_scale, double* keys, int32_t* idx,
+                               int32_t* n_sel, void* ws, size_t ws_bytes, void* stream) {
+  skv_status s = validate_desc(d);
+  if (s != SKV_OK) return s;
+  WsLayout L;
+  if ((s = check_ws(d, ws, ws_bytes, &L)) != SKV_OK) return s;
+  if (!ctx_len || !index_query || !index_keys || !keys || !idx || !n_sel)
+    return set_error(SKV_ERR_INVALID, "score_topk: NULL pointer");
+  if (d->index_mode == SKV_INDEX_SKETCH_INT4 && !index_scale)
+    return set_error(SKV_ERR_INVALID, "score_topk: token mode needs index_scale");
+  if (((uintptr_t)index_keys) % 16) return set_error(SKV_ERR_INVALID, "score_topk: index_keys not 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_score(*d, ctx_len, index_query, index_keys, index_scale, keys,
+                              ws_ptr<uint32_t>(ws, L.flags), st);
+  if (e == hipSuccess) e = launch_topk(*d, ctx_len, keys, idx, n_sel, ws, L, st);
+  return launched(e, "score_topk");
+}
+
 skv_status sparsekv_attend(const skv_layer_desc* d, const void* q, const skv_kv_view* kv,
                            const int32_t* idx, const int32_t* n_sel, float sm_scale, float* out,
                            void* ws, size_t ws_bytes, void* stream) {
@@ -205,11 +232,10 @@ skv_status sparsekv_step(const skv_layer_desc* d, const int32_t* ctx_len, const 
     return set_error(SKV_ERR_INVALID, "step: token mode needs basis, qs, qs_scale and index_scale");
   if (!tok && !index_query) return set_error(SKV_ERR_INVALID, "step: block mode needs index_query");
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = hipSuccess;
-  if (tok) e = launch_qsketch(*d, q, basis, qs, qs_scale, st);
+  hipError_t e = tok ? launch_qsketch(*d, q, basis, qs, qs_scale, st) : hipSuccess;
   if (e == hipSuccess)
-    e = launch_score(*d, ctx_len, tok ? (const void*)qs : index_query, index_keys, index_scale, keys,
-                     ws_ptr<uint32_t>(ws, L.flags), st);
+    e = launch_score(*d, ctx_len, tok ? (const void*)qs : index_query, index_keys, index_scale,
+                     keys, ws_ptr<uint32_t>(ws, L.flags), st);
   if (e == hipSuccess) e = launch_topk(*d, ctx_len, keys, idx, n_sel, ws, L, st);
   if (e == hipSuccess) e = launch_attend(*d, q, *kv, idx, n_sel, sm_scale, out, ws, L, st);
   return launched(e, "step");

@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
   constexpr int VV4 = VB / 16;            // 16-byte loads per V slice
   __shared__ float s_m[kAttWaves][16];
   __shared__ float s_l[kAttWaves][16];
-  extern __shared__ float s_o[];          // [kAttWaves][G][D]
+  extern __shared__ float s_o[];          // [kAttWaves][G][D + 4], d stored as (t, i16)
 
   const int h = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
   const int G = Hq / Hkv;
@@ -144,12 +144,12 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const int ri = rb + 16 * mt + i16;
-      int tok = ri < n ? ib[ri] : 0;
+      int tok = ib[min(ri, n - 1)];     // unconditional load (n >= 1 here)
       if (ri < n && (tok < 0 || (int64_t)tok >= rows)) {
         raise_flag(flags, SKV_FLAG_INDEX_RANGE);
         tok = 0;
       }
-      ka[mt] = tok;
+      ka[mt] = (ri < n && tok >= 0 && (int64_t)tok < rows) ? tok : 0;
     }
     // the 8 tokens whose probabilities / V rows this lane handles:
     // e' = 0..3 -> row rb + 4g + e', e' = 4..7 -> row rb + 16 + 4g + e'-4
@@ -158,10 +158,9 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int ri = rb + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
-      int tok = ri < n ? ib[ri] : 0;
-      bool ok = ri < n && tok >= 0 && (int64_t)tok < rows;
-      if (!ok) tok = 0;
-      vt[e] = tok;
+      int tok = ib[min(ri, n - 1)];     // unconditional load
+      const bool ok = ri < n && tok >= 0 && (int64_t)tok < rows;
+      vt[e] = ok ? tok : 0;
       vok[e] = ok;
     }
     // ---- loads ----
@@ -308,18 +307,20 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
     s_m[wave][i16] = m_run;
     s_l[wave][i16] = l_run;
   }
+  constexpr int DP = D + 4;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int j = 4 * g + e;
     if (j < G) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) s_o[((size_t)wave * G + j) * D + i16 * (D / 16) + t] = o[t][e];
+      for (int t = 0; t < NT; ++t) s_o[((size_t)wave * G + j) * DP + t * 16 + i16] = o[t][e];
     }
   }
   __syncthreads();
   const size_t pbase = ((size_t)b * Hkv + h) * n_chunks + c;
   for (int x = threadIdx.x; x < G * D; x += blockDim.x) {
-    const int j = x / D, d = x % D;
+    const int j = x / D, rem = x % D;                 // rem = t*16 + i16
+    const int d = (rem & 15) * (D / 16) + (rem >> 4);  // column i16*(D/16) + t
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kAttWaves; ++w) M = fmaxf(M, s_m[w][j]);
@@ -327,7 +328,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
 #pragma unroll
     for (int w = 0; w < kAttWaves; ++w) {
       const float f = s_m[w][j] == -INFINITY ? 0.0f : exp2f(s_m[w][j] - M);
-      acc += s_o[((size_t)w * G + j) * D + d] * f;
+      acc += s_o[((size_t)w * G + j) * DP + rem] * f;
     }
     part_o[(pbase * G + j) * D + d] = acc;
     if (d == 0) {
@@ -342,31 +343,42 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
 }
 
 // merge the chunks of each (sequence, query head) in ascending chunk order
+constexpr int kMaxChunks = 64;
+
 __global__ __launch_bounds__(256) void attend_merge_kernel(
     const float* __restrict__ part_ml, const float* __restrict__ part_o,
     const int32_t* __restrict__ n_sel, int cap, int Hq, int Hkv, int D, int n_chunks,
     float* __restrict__ out) {
+  __shared__ float s_f[kMaxChunks];
+  __shared__ float s_inv;
   const int jq = blockIdx.x, b = blockIdx.y;
   const int G = Hq / Hkv;
   const int h = jq / G, j = jq % G;
   int n = n_sel[b];
   n = n < 0 ? 0 : (n > cap ? cap : n);
-  const int nc = (n + kAttRowsPerWG - 1) / kAttRowsPerWG;
+  const int nc = min((n + kAttRowsPerWG - 1) / kAttRowsPerWG, kMaxChunks);
   const size_t pb = ((size_t)b * Hkv + h) * n_chunks;
-  float M = -INFINITY;
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, part_ml[((pb + c) * 16 + j) * 2]);
-  float Ls = 0.0f;
-  for (int c = 0; c < nc; ++c) {
-    const float m = part_ml[((pb + c) * 16 + j) * 2];
-    if (m != -INFINITY) Ls += part_ml[((pb + c) * 16 + j) * 2 + 1] * exp2f(m - M);
+  if (threadIdx.x < 64) {
+    const int c = threadIdx.x;
+    float m = -INFINITY, l = 0.0f;
+    if (c < nc) {
+      m = part_ml[((pb + c) * 16 + j) * 2];
+      l = part_ml[((pb + c) * 16 + j) * 2 + 1];
+    }
+    float M = m;
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const float f = (m == -INFINITY) ? 0.0f : exp2f(m - M);
+    float Ls = l * f;
+    for (int off = 32; off > 0; off >>= 1) Ls += __shfl_xor(Ls, off);
+    if (c < kMaxChunks) s_f[c] = f;
+    if (c == 0) s_inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
   }
+  __syncthreads();
+  const float inv = s_inv;
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
     float acc = 0.0f;
-    for (int c = 0; c < nc; ++c) {
-      const float m = part_ml[((pb + c) * 16 + j) * 2];
-      if (m != -INFINITY) acc += part_o[((pb + c) * G + j) * D + d] * exp2f(m - M);
-    }
-    out[((size_t)b * Hq + jq) * D + d] = Ls > 0.0f ? acc / Ls : 0.0f;
+    for (int c = 0; c < nc; ++c) acc += part_o[((pb + c) * G + j) * D + d] * s_f[c];
+    out[((size_t)b * Hq + jq) * D + d] = acc * inv;
   }
 }
 
@@ -381,7 +393,7 @@ hipError_t launch_attend(const skv_layer_desc& d, const void* q, const skv_kv_vi
   const int cap = select_capacity(d);
   const int G = d.n_q_heads / d.n_kv_heads;
   const dim3 grid(d.n_kv_heads, Lw.n_att_chunks, d.batch);
-  const size_t lds = (size_t)kAttWaves * G * d.head_dim * sizeof(float);
+  const size_t lds = (size_t)kAttWaves * G * (d.head_dim + 4) * sizeof(float);
   const float sl = sm_scale * kLog2e;
 #define SKV_AT(KVT, DD)                                                                          \
   hipLaunchKernelGGL((attend_kernel<KVT, DD>), grid, dim3(kAttThreads), lds, st, q,              \

@@ -23,7 +23,7 @@ namespace skv {
 namespace {
 
 constexpr int kScoreThreads = 256;
-constexpr int kScoreUnroll = 4;
+constexpr int kScoreUnroll = 8;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -39,6 +39,36 @@ __device__ __forceinline__ int dot32_i4(const u32x4 w, const uint32_t qe[4], con
     acc = __builtin_amdgcn_sdot4((int)qo[m], (int)(ws[m] & 0xF0F0F0F0u), acc, false);
   }
   return acc;
+}
+
+// Sum over aligned groups of LPT lanes (LPT in {2,4,8,16}) with DPP moves:
+// two quad permutes, then the half-row and row mirrors.  Every lane of the
+// group ends with the group total.
+template <int LPT>
+__device__ __forceinline__ int group_sum_i32(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);       // quad_perm [1,0,3,2]
+  if (LPT >= 4) v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // [2,3,0,1]
+  if (LPT >= 8) v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  if (LPT >= 16) v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false); // row_mirror
+  return v;
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_add_f64(double v) {
+  const long long u = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(u & 0xFFFFFFFF), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(u >> 32), CTRL, 0xF, 0xF, false);
+  return v + __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
+template <int LPB>
+__device__ __forceinline__ double group_sum_f64(double x) {
+  x = dpp_add_f64<0xB1>(x);
+  if (LPB >= 4) x = dpp_add_f64<0x4E>(x);
+  if (LPB >= 8) x = dpp_add_f64<0x141>(x);
+  if (LPB >= 16) x = dpp_add_f64<0x140>(x);
+  if (LPB >= 32) x += __shfl_xor(x, 16);
+  return x;
 }
 
 template <int LPT>  // lanes per token; a token's sketch is 16*LPT bytes
@@ -81,23 +111,22 @@ __global__ __launch_bounds__(kScoreThreads) void score_sketch_kernel(
   double* kbase = keys + (size_t)b * max_ctx;
   for (int base = t0 + wave * TPW + tw; base < t1; base += STEP * kScoreUnroll) {
     u32x4 w[kScoreUnroll];
+    uint16_t sc[kScoreUnroll];
+    // all loads issued unconditionally (past the end they re-read the last
+    // token; those results are dropped), so they are in flight together
 #pragma unroll
     for (int u = 0; u < kScoreUnroll; ++u) {
-      const int t = base + u * STEP;
-      if (t < t1)
-        w[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cbase + (size_t)t * TB));
-      else
-        w[u] = (u32x4){0u, 0u, 0u, 0u};
+      const int t = min(base + u * STEP, t1 - 1);
+      w[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cbase + (size_t)t * TB));
+      sc[u] = sbase[t];   // the token's scale, fetched with its codes
     }
 #pragma unroll
     for (int u = 0; u < kScoreUnroll; ++u) {
       const int t = base + u * STEP;
-      int acc = dot32_i4(w[u], qe, qo, 0);
-#pragma unroll
-      for (int off = 1; off < LPT; off <<= 1) acc += __shfl_xor(acc, off);
+      const int acc = group_sum_i32<LPT>(dot32_i4(w[u], qe, qo, 0));
       if (sub == 0 && t < t1) {
-        const double key = (double)(acc >> 4) * (double)half_bits_to_float(sbase[t]);
-        kbase[t] = key + 0.0;  // -0 -> +0
+        const double key = (double)(acc >> 4) * (double)half_bits_to_float(sc[u]) + 0.0;  // -0 -> +0
+        kbase[t] = key;
       }
     }
   }
@@ -129,11 +158,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_pooled_kernel(
     u32x4 w[kScoreUnroll];
 #pragma unroll
     for (int u = 0; u < kScoreUnroll; ++u) {
-      const int j = base + u * STEP;
-      if (j < j1)
-        w[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + (size_t)j * ID));
-      else
-        w[u] = (u32x4){0u, 0u, 0u, 0u};
+      const int j = min(base + u * STEP, j1 - 1);
+      w[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + (size_t)j * ID));
     }
 #pragma unroll
     for (int u = 0; u < kScoreUnroll; ++u) {
@@ -145,9 +171,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_pooled_kernel(
         acc = fma((double)__uint_as_float(ws[m] << 16), qd[2 * m], acc);
         acc = fma((double)__uint_as_float(ws[m] & 0xFFFF0000u), qd[2 * m + 1], acc);
       }
-#pragma unroll
-      for (int off = 1; off < LPB; off <<= 1) acc += __shfl_xor(acc, off);
-      if (sub == 0 && j < j1) kout[j] = acc + 0.0;
+      acc = group_sum_f64<LPB>(acc);
+      if (sub == 0 && j < j1) kout[j] = acc + 0.0;   // -0 -> +0
     }
   }
 }

@@ -14,37 +14,35 @@ namespace skv {
 // ---------------------------------------------------------------------------
 // constants
 // ---------------------------------------------------------------------------
-constexpr int kHistBits = 13;                 // coarse-key histogram digit
-constexpr int kHistBins = 1 << kHistBits;     // 8192 bins
+constexpr int kHistBits = 12;                 // coarse-key histogram digit (1/8 octave)
+constexpr int kHistBins = 1 << kHistBits;     // 4096 bins
 constexpr int kListCap = 8192;                // candidate list capacity per sequence
-constexpr int kMaxTopk = 4096;                // largest budget the select kernel sorts in LDS
-constexpr int kHistChunk = 4096;              // keys per histogram / collect workgroup
-constexpr int kAttRowsPerWave = 64;           // selected rows per attention wave
-constexpr int kAttWaves = 4;                  // waves per attention workgroup
+constexpr int kMaxTopk = 4096;                // largest budget the select kernel handles in LDS
+constexpr int kHistChunk = 2048;              // keys per collect workgroup
+constexpr int kSegCap = 128;                  // candidate slots per collect workgroup
+constexpr int kBitmapWords = 12288;           // LDS position bitmap (candidates <= 393,216)
+constexpr int kAttRowsPerWave = 32;           // selected rows per attention wave
+constexpr int kAttWaves = 8;                  // waves per attention workgroup
 constexpr int kAttRowsPerWG = kAttRowsPerWave * kAttWaves;
 constexpr int kScoreChunk = 2048;             // tokens per sketch-score workgroup
 constexpr int kPooledChunk = 1024;            // blocks per pooled-score workgroup
 
-// per-sequence select state (u32 words)
+// per-sequence select state written by the sample kernel (u32 words)
 struct TopkState {
-  uint32_t done;       // histogram workgroups finished
-  uint32_t beta;       // threshold bucket
-  uint32_t n_c;        // candidates with bucket >= beta
-  uint32_t list_count; // candidates written to the list
-  uint32_t mode;       // 0 fast, 1 dense, 2 slow (exact search over all keys), 3 empty
-  uint32_t pad[11];
+  uint32_t beta;       // threshold bucket: candidates with digit >= beta are collected
+  uint32_t pad[15];
 };
-enum { kModeFast = 0, kModeDense = 1, kModeSlow = 2 };
 
 // ---------------------------------------------------------------------------
 // workspace layout (host and device agree through this struct)
 // ---------------------------------------------------------------------------
 struct WsLayout {
   size_t flags;        // uint32 flag word (+ padding)
-  size_t hist;         // [B][kHistBins] u32
   size_t state;        // [B] TopkState
-  size_t lkey;         // [B][kListCap] u64 ordered keys
-  size_t lpos;         // [B][kListCap] u32 positions
+  size_t segcnt;       // [B][n_seg] u32 candidates found by each collect workgroup
+  size_t lkey;         // [B][n_seg][kSegCap] u64 ordered keys
+  size_t lpos;         // [B][n_seg][kSegCap] u32 positions
+  int n_seg;           // collect workgroups per sequence
   size_t att_ml;       // [B][H_kv][n_chunks][16][2] f32  (m, l) per head row
   size_t att_o;        // [B][H_kv][n_chunks][G][D] f32
   size_t total;
@@ -62,10 +60,13 @@ inline WsLayout ws_layout(const skv_layer_desc& d) {
   size_t off = 0;
   const size_t B = (size_t)d.batch;
   w.flags = off;  off = align_up(off + 256, 256);
-  w.hist = off;   off = align_up(off + B * kHistBins * 4, 256);
+  const int max_cand = d.index_mode == SKV_INDEX_SKETCH_INT4 ? d.max_ctx : d.max_ctx / 4;
+  w.n_seg = (max_cand + kHistChunk - 1) / kHistChunk;
+  if (w.n_seg < 1) w.n_seg = 1;
   w.state = off;  off = align_up(off + B * sizeof(TopkState), 256);
-  w.lkey = off;   off = align_up(off + B * kListCap * 8, 256);
-  w.lpos = off;   off = align_up(off + B * kListCap * 4, 256);
+  w.segcnt = off; off = align_up(off + B * w.n_seg * 4, 256);
+  w.lkey = off;   off = align_up(off + B * w.n_seg * kSegCap * 8, 256);
+  w.lpos = off;   off = align_up(off + B * w.n_seg * kSegCap * 4, 256);
   const int cap = select_capacity(d);
   w.n_att_chunks = (cap + kAttRowsPerWG - 1) / kAttRowsPerWG;
   const int G = d.n_q_heads / d.n_kv_heads;
@@ -123,9 +124,11 @@ __device__ __forceinline__ float bf16_bits_to_float(uint16_t h) {
 // ---------------------------------------------------------------------------
 hipError_t launch_qsketch(const skv_layer_desc& d, const void* q, const float* basis, int8_t* qs,
                           float* qs_scale, hipStream_t st);
+// keys only
 hipError_t launch_score(const skv_layer_desc& d, const int32_t* ctx_len, const void* iq,
                         const void* ik, const uint16_t* isc, double* keys, uint32_t* flags,
                         hipStream_t st);
+// select from keys: sample + collect + final
 hipError_t launch_topk(const skv_layer_desc& d, const int32_t* ctx_len, const double* keys,
                        int32_t* idx, int32_t* n_sel, void* ws, const WsLayout& L, hipStream_t st);
 hipError_t launch_attend(const skv_layer_desc& d, const void* q, const skv_kv_view& kv,
