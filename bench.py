@@ -31,6 +31,9 @@ import top_sparse_kv_amd as skv  # noqa: E402
 
 METRIC = "sparse decode layer-steps/s at 250K ctx; achieved HBM GB/s vs MI355X peak"
 PEAK_HBM_GBS = 8000.0
+CALIB_BYTES = 1 << 30          # plain streaming kernel used to scale FETCH_SIZE / WRITE_SIZE
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_sketch_cfg2_traffic.md")
+SCORE_SRC = os.path.join(ROOT, "top_sparse_kv_amd", "csrc", "score.hip")
 
 
 def log(*a):
@@ -147,6 +150,67 @@ def time_loop(fn, layers, ws, n):
     return e0.elapsed_time(e1) / 1e3   # seconds
 
 
+def source_hash(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def committed_traffic():
+    """HBM bytes per score launch from the committed counter summary, or None
+    when there is none or the kernel source changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            fields = dict(ln.split(":", 1) for ln in f.read().splitlines()
+                          if ln.startswith(("traffic_bytes_per_launch:", "score_hip_sha256_16:")))
+    except OSError:
+        return None
+    if fields.get("score_hip_sha256_16", "").strip() != source_hash(SCORE_SRC):
+        return None
+    try:
+        return int(float(fields["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def rocprof_summary(path, out):
+    """Writes a short text summary of a rocprofv3 csv: kernel stats (average
+    duration per library kernel) or counter collection (average value per
+    dispatch of each counter for the library kernels and the copy used for
+    calibration)."""
+    import collections
+    import csv
+    lines = []
+    if path.endswith("kernel_stats.csv"):
+        lines.append("| kernel | calls | avg us | min us | max us |")
+        lines.append("|---|---|---|---|---|")
+        for r in csv.DictReader(open(path)):
+            if "skv" in r["Name"]:
+                nm = r["Name"].replace("(anonymous namespace)::", "").split("(")[0]
+                lines.append("| %s | %s | %.2f | %.2f | %.2f |" % (
+                    nm, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                    float(r["MaxNs"]) / 1e3))
+    else:
+        agg = collections.defaultdict(lambda: collections.defaultdict(float))
+        disp = collections.defaultdict(set)
+        for r in csv.DictReader(open(path)):
+            nm = r.get("Kernel_Name", "")
+            if "skv" not in nm and "bitwise_not" not in nm:
+                continue
+            key = nm.replace("(anonymous namespace)::", "").split("(")[0][-70:]
+            agg[key][r["Counter_Name"]] += float(r["Counter_Value"])
+            disp[key].add(r.get("Dispatch_Id", ""))
+        lines.append("| kernel | dispatches | counter | average per dispatch |")
+        lines.append("|---|---|---|---|")
+        for key, cs in agg.items():
+            n = max(1, len(disp[key]))
+            for c, v in sorted(cs.items()):
+                lines.append("| %s | %d | %s | %.6g |" % (key, n, c, v / n))
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def cpu_baseline(layer: Layer, cfg):
     """The CPU oracle timed on the host cores on one full layer-step of layer 0
     (all sequences of the batch): query sketch, exact keys, selection and
@@ -202,7 +266,15 @@ def main():
     ap.add_argument("--config", default="cfg2", choices=sorted(CONFIGS))
     ap.add_argument("--layers", type=int, default=0, help="rotating layer buffers (0 = config default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB read + 1 GiB write stream (counter calibration)")
+    ap.add_argument("--rocprof-summary", metavar="CSV",
+                    help="summarise a rocprofv3 csv into --out and exit")
+    ap.add_argument("--out", default=None)
     args = ap.parse_args()
+    if args.rocprof_summary:
+        rocprof_summary(args.rocprof_summary, args.out or "/dev/stdout")
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -234,9 +306,10 @@ def main():
     ab = algorithmic_bytes(cfg)
     value = args.steps / secs
     score_s = kt["score"]
+    traffic = committed_traffic() if args.config == "cfg2" else None
     roof = dict(kernel="score_sketch" if cfg["kind"] == "token" else "score_pooled", bound="hbm",
                 achieved=round(ab["scan"] / score_s / 1e9, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                frac=round(ab["scan"] / score_s / 1e9 / PEAK_HBM_GBS, 4), traffic=None,
+                frac=round(ab["scan"] / score_s / 1e9 / PEAK_HBM_GBS, 4), traffic=traffic,
                 bytes_per_launch=ab["scan"], avg_launch_us=round(score_s * 1e6, 2))
     res = {
         "metric": METRIC,
@@ -258,6 +331,15 @@ def main():
         "kernels_us": {k: round(v * 1e6, 2) for k, v in kt.items()},
         "roofline": roof,
     }
+    if args.calib_copy:
+        # a plain stream of known size (reads CALIB_BYTES, writes CALIB_BYTES);
+        # bitwise_not is used nowhere else, so its counter rows are unambiguous
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
+        res["calib_copy_bytes"] = CALIB_BYTES
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         cb = cpu_baseline(layers[0], cfg)
