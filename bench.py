@@ -95,7 +95,7 @@ class Layer:
 
     def step(self, ws):
         skv.step(self.desc, self.ctx, self.q, self.basis, self.qs, self.qsc, self.iq, self.ikeys,
-                 self.iscale, self.keys, self.kv, self.idx, self.nsel, self.sm, self.out, ws)
+                 self.iscale, self.kv, self.idx, self.nsel, self.sm, self.out, ws)
 
     def qsketch(self, ws):
         skv.qsketch(self.desc, self.q, self.basis, self.qs, self.qsc, ws)
@@ -109,8 +109,7 @@ class Layer:
 
     def score_topk(self, ws):
         iq = self.qs if self.iq is None else self.iq
-        skv.score_topk(self.desc, self.ctx, iq, self.ikeys, self.iscale, self.keys, self.idx,
-                       self.nsel, ws)
+        skv.score_topk(self.desc, self.ctx, iq, self.ikeys, self.iscale, self.idx, self.nsel, ws)
 
     def attend(self, ws):
         skv.attend(self.desc, self.q, self.kv, self.idx, self.nsel, self.sm, self.out, ws)

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SPARSEKV_ABI_VERSION 1
+#define SPARSEKV_ABI_VERSION 2
 
 typedef int32_t skv_status;
 enum {
@@ -79,9 +79,10 @@ enum {
 /*
  * Layer descriptor (plain old data).
  *
- * Token mode (index_mode = SKV_INDEX_SKETCH_INT4): block = 1, rank = 64 (any
- * even value), topk = tokens kept from the middle range [n_sink, T - n_tail);
- * a sequence is dense (all T tokens attended) when T <= n_sink + topk + n_tail.
+ * Token mode (index_mode = SKV_INDEX_SKETCH_INT4): block = 1, rank = 64 (a
+ * multiple of 16 in [16, 256] with n_kv_heads*rank/2 in {32, 64, 128, 256}),
+ * topk = tokens kept from the middle range [n_sink, T - n_tail); a sequence
+ * is dense (all T tokens attended) when T <= n_sink + topk + n_tail.
  *
  * Block mode (index_mode = SKV_INDEX_POOLED_BF16): block = 4, index_dim = 128
  * (any multiple of 8), topk = blocks kept; n_sink = n_tail = 0.  Only the
@@ -154,7 +155,9 @@ skv_status sparsekv_workspace_size(const skv_layer_desc* d, size_t* bytes);
  *            head h, s_h = sum over d ascending of (qbar_h[d] * basis_h[d][r])
  *            with qbar_h = sum of the G query heads of h in ascending order,
  *            all in fp32 with separately rounded multiplies and adds;
- *   qs_scale [B] fp32 out: max|s| / 127 (0 when the sketch is all zero). */
+ *   qs_scale [B] fp32 out: max|s| / 127 (0 when the sketch is all zero).
+ * Uses the workspace (per-head partial sketches and an arrival counter that
+ * every call leaves at zero). */
 skv_status sparsekv_qsketch(const skv_layer_desc* d, const void* q, const float* basis,
                             int8_t* qs, float* qs_scale, void* ws, size_t ws_bytes, void* stream);
 
@@ -192,13 +195,17 @@ skv_status sparsekv_score(const skv_layer_desc* d, const int32_t* ctx_len,
 skv_status sparsekv_topk(const skv_layer_desc* d, const int32_t* ctx_len, const double* keys,
                          int32_t* idx, int32_t* n_sel, void* ws, size_t ws_bytes, void* stream);
 
-/* Stages A2 + A3 in one call: writes keys (as sparsekv_score) and idx / n_sel
- * (identical to sparsekv_topk on those keys), with the select stage's coarse
- * histogram built while scoring instead of by a separate pass over the keys. */
+/* Stages A2 + A3 in one call, without materializing the keys: idx / n_sel
+ * are identical to sparsekv_topk applied to the keys sparsekv_score would
+ * write.  The index is streamed once; the keys at or above a threshold
+ * estimated from a sample of the index are kept in the workspace as
+ * (key, position) candidates and the exact select runs on them (on every key,
+ * recomputed, in the rare case the candidates are fewer than topk; that case
+ * raises SKV_FLAG_TOPK_SLOW). */
 skv_status sparsekv_score_topk(const skv_layer_desc* d, const int32_t* ctx_len,
                                const void* index_query, const void* index_keys,
-                               const uint16_t* index_scale, double* keys, int32_t* idx,
-                               int32_t* n_sel, void* ws, size_t ws_bytes, void* stream);
+                               const uint16_t* index_scale, int32_t* idx, int32_t* n_sel,
+                               void* ws, size_t ws_bytes, void* stream);
 
 /* ---- stage A4: exact GQA attention over the selected rows -----------------
  * Page "8 agents x 250K ...", section "The mechanism" (exact attention on the
@@ -214,15 +221,16 @@ skv_status sparsekv_attend(const skv_layer_desc* d, const void* q, const skv_kv_
                            void* ws, size_t ws_bytes, void* stream);
 
 /* ---- the whole step --------------------------------------------------------
- * A1..A4 in one call (token mode: basis, qs, qs_scale used; block mode: they
- * may be NULL and index_query is the bf16 indexer query).  keys, idx, n_sel
- * are written as by the separate calls. */
+ * A1..A4 in one call: sparsekv_qsketch (token mode), sparsekv_score_topk and
+ * sparsekv_attend.  Token mode: basis, qs, qs_scale are used and qs / qs_scale
+ * written; block mode: they may be NULL and index_query is the bf16 indexer
+ * query.  qs, qs_scale, idx, n_sel, out are written as by the separate calls. */
 skv_status sparsekv_step(const skv_layer_desc* d, const int32_t* ctx_len, const void* q,
                          const float* basis, int8_t* qs, float* qs_scale,
                          const void* index_query, const void* index_keys,
-                         const uint16_t* index_scale, double* keys,
-                         const skv_kv_view* kv, int32_t* idx, int32_t* n_sel,
-                         float sm_scale, float* out, void* ws, size_t ws_bytes, void* stream);
+                         const uint16_t* index_scale, const skv_kv_view* kv, int32_t* idx,
+                         int32_t* n_sel, float sm_scale, float* out, void* ws, size_t ws_bytes,
+                         void* stream);
 
 /* Synchronizes `stream`, returns the device flag bits raised since the last
  * check in *flags (may be NULL) and clears them.  SKV_ERR_STATE if any bit

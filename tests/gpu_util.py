@@ -64,7 +64,9 @@ def run_token_gpu(skv, c: synth.TokenCase, sm_scale, *, fused=False, qs_in=None)
     kv = skv.kv_view(dev["k_cache"], dev["v_cache"], dev["k_scale"], dev["v_scale"])
     if fused:
         skv.step(desc, dev["ctx_len"], dev["q"], dev["basis"], qs, qsc, None, dev["codes"],
-                 dev["sk_scale"], keys, kv, idx, nsel, sm_scale, out, ws)
+                 dev["sk_scale"], kv, idx, nsel, sm_scale, out, ws)
+        # the fused step keeps no keys; score them separately for the key checks
+        skv.score(desc, dev["ctx_len"], qs, dev["codes"], dev["sk_scale"], keys, ws)
     else:
         skv.qsketch(desc, dev["q"], dev["basis"], qs, qsc, ws)
         qs_use = qs if qs_in is None else torch.from_numpy(qs_in).cuda()
@@ -88,8 +90,9 @@ def run_block_gpu(skv, c: synth.BlockCase, sm_scale, *, fused=False):
     out = torch.zeros((c.B, c.n_q, c.D), dtype=torch.float32, device="cuda")
     kv = skv.kv_view(dev["k_cache"], dev["v_cache"])
     if fused:
-        skv.step(desc, dev["ctx_len"], dev["q"], None, None, None, dev["qi"], dev["kp"], None, keys,
+        skv.step(desc, dev["ctx_len"], dev["q"], None, None, None, dev["qi"], dev["kp"], None,
                  kv, idx, nsel, sm_scale, out, ws)
+        skv.score(desc, dev["ctx_len"], dev["qi"], dev["kp"], None, keys, ws)
     else:
         skv.score(desc, dev["ctx_len"], dev["qi"], dev["kp"], None, keys, ws)
         skv.topk(desc, dev["ctx_len"], keys, idx, nsel, ws)

@@ -40,11 +40,29 @@ def test_header_declarations_are_exported(skv):
         assert n in bound, "binding lacks " + n
 
 
+def declared_arity():
+    """Parameter count of every function the header declares."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for name, params in re.findall(r"\b(sparsekv_\w+)\s*\(([^)]*)\)\s*;", text):
+        params = params.strip()
+        out[name] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
+
+
+def test_binding_arity_matches_header(skv):
+    from top_sparse_kv_amd import _lib
+    arity = declared_arity()
+    assert len(arity) == len(declared_functions())
+    for name, _, args in _lib.SIGNATURES:
+        assert arity[name] == len(args), (name, arity[name], len(args))
+
+
 def test_struct_sizes_match_header(skv):
     # the C structs are plain int32 / pointer layouts; sizes pinned here
     assert ctypes.sizeof(skv.LayerDesc) == 15 * 4
     assert ctypes.sizeof(skv.KVView) == 5 * 8
-    assert skv.abi_version() == 1
+    assert skv.abi_version() == 2
 
 
 def test_capacity_and_workspace(skv):

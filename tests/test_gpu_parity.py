@@ -154,7 +154,6 @@ def test_determinism_and_graph_replay():
     ws = skv.workspace(desc)
     qs = torch.zeros((c.B, 256), dtype=torch.int8, device="cuda")
     qsc = torch.zeros((c.B,), dtype=torch.float32, device="cuda")
-    keys = torch.zeros((c.B, c.T_max), dtype=torch.float64, device="cuda")
     idx = torch.zeros((c.B, cap), dtype=torch.int32, device="cuda")
     nsel = torch.zeros((c.B,), dtype=torch.int32, device="cuda")
     out = torch.zeros((c.B, c.n_q, c.D), dtype=torch.float32, device="cuda")
@@ -162,13 +161,13 @@ def test_determinism_and_graph_replay():
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):   # warm-up on the capture stream
-        skv.step(desc, c.ctx_len, c.q, c.basis, qs, qsc, None, c.codes, c.sk_scale, keys, kv, idx,
+        skv.step(desc, c.ctx_len, c.q, c.basis, qs, qsc, None, c.codes, c.sk_scale, kv, idx,
                  nsel, sm, out, ws)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        skv.step(desc, c.ctx_len, c.q, c.basis, qs, qsc, None, c.codes, c.sk_scale, keys, kv, idx,
+        skv.step(desc, c.ctx_len, c.q, c.basis, qs, qsc, None, c.codes, c.sk_scale, kv, idx,
                  nsel, sm, out, ws)
     for rep in range(4):
         out.zero_()
@@ -267,8 +266,8 @@ def test_full_config4b_mixed():
 
 @pytest.mark.parametrize("mode", ["token", "block"])
 def test_score_topk_matches_separate_calls(mode):
-    """The fused score+select entry point gives the keys and index sets of
-    sparsekv_score followed by sparsekv_topk, bit for bit."""
+    """The fused score+select entry point (no keys materialized) gives the
+    index sets of sparsekv_score followed by sparsekv_topk, bit for bit."""
     skv = need_gpu()
     if mode == "token":
         c = _cfg2(4, 60_000, [60_000, 30_000, 3_500, 3_100], device="cuda")
@@ -286,18 +285,71 @@ def test_score_topk_matches_separate_calls(mode):
     cap = skv.select_capacity(desc)
     res = []
     for fused in (False, True):
-        keys = torch.full((c.B, nkeys), float("nan"), dtype=torch.float64, device="cuda")
         idx = torch.full((c.B, cap), -1, dtype=torch.int32, device="cuda")
         nsel = torch.zeros((c.B,), dtype=torch.int32, device="cuda")
         if fused:
-            skv.score_topk(desc, c.ctx_len, iq, ik, isc, keys, idx, nsel, ws)
+            skv.score_topk(desc, c.ctx_len, iq, ik, isc, idx, nsel, ws)
         else:
+            keys = torch.full((c.B, nkeys), float("nan"), dtype=torch.float64, device="cuda")
             skv.score(desc, c.ctx_len, iq, ik, isc, keys, ws)
             skv.topk(desc, c.ctx_len, keys, idx, nsel, ws)
-        skv.check(ws)
-        res.append((keys.cpu().numpy(), idx.cpu().numpy(), nsel.cpu().numpy()))
-    (k0, i0, n0), (k1, i1, n1) = res
-    assert np.array_equal(k0, k1, equal_nan=True)
+        assert skv.check(ws) & skv.SKV_FLAG_TOPK_SLOW == 0
+        res.append((idx.cpu().numpy(), nsel.cpu().numpy()))
+    (i0, n0), (i1, n1) = res
     assert np.array_equal(n0, n1)
     for b in range(c.B):
         assert np.array_equal(i0[b, :n0[b]], i1[b, :n1[b]])
+
+
+def _fused_select_vs_oracle(skv, c, qs_np):
+    """sparsekv_score_topk with the given int8 query sketch against the oracle
+    select on the oracle's keys; returns the device flags."""
+    desc = token_desc_of(skv, c)
+    cap = skv.select_capacity(desc)
+    ws = skv.workspace(desc)
+    idx = torch.full((c.B, cap), -1, dtype=torch.int32, device="cuda")
+    nsel = torch.zeros((c.B,), dtype=torch.int32, device="cuda")
+    skv.score_topk(desc, c.ctx_len, torch.from_numpy(qs_np).cuda(), c.codes, c.sk_scale, idx, nsel, ws)
+    flags = skv.check(ws)
+    keys = oracle.sketch_keys(qs_np, c.codes.cpu().numpy(), c.sk_scale.cpu().numpy(), c.lens, c.S,
+                              c.k, c.L)
+    gi, gn = idx.cpu().numpy(), nsel.cpu().numpy()
+    for b in range(c.B):
+        sel = oracle.select_tokens(keys[b], c.lens[b], c.S, c.k, c.L)
+        assert gn[b] == sel.size
+        assert np.array_equal(gi[b, :gn[b]], sel), "seq %d" % b
+    return flags
+
+
+def test_fused_select_all_keys_equal():
+    """A zero query sketch makes every key 0: every candidate ties, there are
+    more candidates than the select holds in LDS, and the budget goes to the
+    lowest positions (the select over the candidate records in memory)."""
+    skv = need_gpu()
+    c = _cfg2(2, 40_000, [40_000, 25_000], device="cuda")
+    qs = np.zeros((c.B, 256), dtype=np.int8)
+    flags = _fused_select_vs_oracle(skv, c, qs)
+    assert flags & skv.SKV_FLAG_TOPK_SLOW
+
+
+def test_fused_select_sample_overshoot():
+    """Large keys planted only on the sampled lines make the threshold bucket
+    too high: fewer candidates than the budget survive it, and the select
+    recomputes every key of the sequence (the exact fallback)."""
+    skv = need_gpu()
+    c = _cfg2(1, 120_000, [120_000], n_needles=0, device="cuda")
+    qs = np.zeros((1, 256), dtype=np.int8)
+    qs[0, :] = 1
+    n = c.lens[0] - c.S - c.L
+    s = min(max(n // (4 * c.k), 1), 64)          # the sample takes every s-th line of 16
+    codes = c.codes.cpu().numpy()
+    scale = c.sk_scale.cpu().numpy().view(np.uint16).copy()
+    sampled = np.array([c.S + 16 * s * j + e for j in range(40) for e in range(16)])
+    assert s > 1 and sampled.size >= 400
+    # all codes +7 (nibbles 0x7 in both halves): dot = 7 * 256 with qs = 1
+    codes[0, sampled] = 0x77
+    scale[0, sampled] = np.float16(8.0).view(np.uint16)
+    c.codes.copy_(torch.from_numpy(codes))
+    c.sk_scale.copy_(torch.from_numpy(scale.view(np.float16)))
+    flags = _fused_select_vs_oracle(skv, c, qs)
+    assert flags & skv.SKV_FLAG_TOPK_SLOW

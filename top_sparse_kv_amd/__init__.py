@@ -121,12 +121,11 @@ def topk(desc, ctx_len, keys, idx, n_sel, ws, stream=None):
                                _p(ws), ws.numel(), _stream(stream)))
 
 
-def score_topk(desc, ctx_len, index_query, index_keys, index_scale, keys, idx, n_sel, ws,
-               stream=None):
-    _dev(ctx_len, index_query, index_keys, index_scale, keys, idx, n_sel, ws)
+def score_topk(desc, ctx_len, index_query, index_keys, index_scale, idx, n_sel, ws, stream=None):
+    _dev(ctx_len, index_query, index_keys, index_scale, idx, n_sel, ws)
     _check(lib().sparsekv_score_topk(ctypes.byref(desc), _p(ctx_len), _p(index_query),
-                                     _p(index_keys), _p(index_scale), _p(keys), _p(idx),
-                                     _p(n_sel), _p(ws), ws.numel(), _stream(stream)))
+                                     _p(index_keys), _p(index_scale), _p(idx), _p(n_sel), _p(ws),
+                                     ws.numel(), _stream(stream)))
 
 
 def attend(desc, q, kv: KVView, idx, n_sel, sm_scale, out, ws, stream=None):
@@ -135,14 +134,13 @@ def attend(desc, q, kv: KVView, idx, n_sel, sm_scale, out, ws, stream=None):
                                  float(sm_scale), _p(out), _p(ws), ws.numel(), _stream(stream)))
 
 
-def step(desc, ctx_len, q, basis, qs, qs_scale, index_query, index_keys, index_scale, keys,
-         kv: KVView, idx, n_sel, sm_scale, out, ws, stream=None):
-    _dev(ctx_len, q, basis, qs, qs_scale, index_query, index_keys, index_scale, keys, idx, n_sel,
-         out, ws)
+def step(desc, ctx_len, q, basis, qs, qs_scale, index_query, index_keys, index_scale, kv: KVView,
+         idx, n_sel, sm_scale, out, ws, stream=None):
+    _dev(ctx_len, q, basis, qs, qs_scale, index_query, index_keys, index_scale, idx, n_sel, out, ws)
     _check(lib().sparsekv_step(ctypes.byref(desc), _p(ctx_len), _p(q), _p(basis), _p(qs),
                                _p(qs_scale), _p(index_query), _p(index_keys), _p(index_scale),
-                               _p(keys), ctypes.byref(kv), _p(idx), _p(n_sel), float(sm_scale),
-                               _p(out), _p(ws), ws.numel(), _stream(stream)))
+                               ctypes.byref(kv), _p(idx), _p(n_sel), float(sm_scale), _p(out),
+                               _p(ws), ws.numel(), _stream(stream)))
 
 
 def check(ws, stream=None) -> int:

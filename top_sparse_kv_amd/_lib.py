@@ -63,11 +63,11 @@ SIGNATURES = [
     ("sparsekv_qsketch", c_i32, [P(LayerDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     ("sparsekv_score", c_i32, [P(LayerDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     ("sparsekv_topk", c_i32, [P(LayerDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
-    ("sparsekv_score_topk", c_i32, [P(LayerDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
-                                    c_sz, c_vp]),
+    ("sparsekv_score_topk", c_i32, [P(LayerDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz,
+                                    c_vp]),
     ("sparsekv_attend", c_i32, [P(LayerDesc), c_vp, P(KVView), c_vp, c_vp, ctypes.c_float, c_vp,
                                 c_vp, c_sz, c_vp]),
-    ("sparsekv_step", c_i32, [P(LayerDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+    ("sparsekv_step", c_i32, [P(LayerDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                               P(KVView), c_vp, c_vp, ctypes.c_float, c_vp, c_vp, c_sz, c_vp]),
     ("sparsekv_check", c_i32, [c_vp, c_sz, c_vp, P(c_u32)]),
     ("sparsekv_tier_create", c_i32, [P(TierDesc), P(c_vp)]),

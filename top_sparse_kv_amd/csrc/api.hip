@@ -42,8 +42,8 @@ skv_status validate_desc(const skv_layer_desc* d) {
   if (d->n_sink < 0 || d->n_tail < 0) return set_error(SKV_ERR_INVALID, "negative n_sink / n_tail");
   if (d->index_mode == SKV_INDEX_SKETCH_INT4) {
     if (d->block != 1) return set_error(SKV_ERR_INVALID, "token mode needs block == 1 (got %d)", d->block);
-    if (d->rank < 1 || (d->n_kv_heads * d->rank) % 2)
-      return set_error(SKV_ERR_INVALID, "rank %d: n_kv_heads*rank must be even and positive", d->rank);
+    if (d->rank < 16 || d->rank > 256 || d->rank % 16)
+      return set_error(SKV_ERR_UNSUPPORTED, "rank %d not a multiple of 16 in [16, 256]", d->rank);
     const int tb = d->n_kv_heads * d->rank / 2;
     if (tb != 32 && tb != 64 && tb != 128 && tb != 256)
       return set_error(SKV_ERR_UNSUPPORTED, "sketch bytes per token %d not in {32,64,128,256}", tb);
@@ -67,9 +67,10 @@ skv_status validate_desc(const skv_layer_desc* d) {
     return set_error(SKV_ERR_INVALID, "index_mode %d unknown", d->index_mode);
   }
   {
-    const int64_t cand = d->index_mode == SKV_INDEX_SKETCH_INT4 ? d->max_ctx : d->max_ctx / 4;
-    if ((cand + kHistChunk - 1) / kHistChunk > 1024)
-      return set_error(SKV_ERR_UNSUPPORTED, "more than %d candidates per sequence", 1024 * kHistChunk);
+    const int64_t cand = max_candidates(*d);
+    const int seg = d->index_mode == SKV_INDEX_SKETCH_INT4 ? kSegTok : kSegBlk;
+    if ((cand + seg - 1) / seg > kMaxSeg)
+      return set_error(SKV_ERR_UNSUPPORTED, "more than %d candidates per sequence", kMaxSeg * seg);
   }
   if (select_capacity(*d) > 64 * kAttRowsPerWG)
     return set_error(SKV_ERR_UNSUPPORTED, "select capacity %d > %d", select_capacity(*d), 64 * kAttRowsPerWG);
@@ -146,12 +147,12 @@ skv_status sparsekv_qsketch(const skv_layer_desc* d, const void* q, const float*
                             float* qs_scale, void* ws, size_t ws_bytes, void* stream) {
   skv_status s = validate_desc(d);
   if (s != SKV_OK) return s;
-  (void)ws;
-  (void)ws_bytes;
   if (d->index_mode != SKV_INDEX_SKETCH_INT4)
     return set_error(SKV_ERR_INVALID, "qsketch is a token-mode stage");
+  WsLayout L;
+  if ((s = check_ws(d, ws, ws_bytes, &L)) != SKV_OK) return s;
   if (!q || !basis || !qs || !qs_scale) return set_error(SKV_ERR_INVALID, "qsketch: NULL pointer");
-  return launched(launch_qsketch(*d, q, basis, qs, qs_scale, (hipStream_t)stream), "qsketch");
+  return launched(launch_qsketch(*d, q, basis, qs, qs_scale, ws, L, (hipStream_t)stream), "qsketch");
 }
 
 skv_status sparsekv_score(const skv_layer_desc* d, const int32_t* ctx_len, const void* index_query,
@@ -183,22 +184,20 @@ skv_status sparsekv_topk(const skv_layer_desc* d, const int32_t* ctx_len, const 
 
 skv_status sparsekv_score_topk(const skv_layer_desc* d, const int32_t* ctx_len,
                                const void* index_query, const void* index_keys,
-                               const uint16_t* index_scale, double* keys, int32_t* idx,
-                               int32_t* n_sel, void* ws, size_t ws_bytes, void* stream) {
+                               const uint16_t* index_scale, int32_t* idx, int32_t* n_sel,
+                               void* ws, size_t ws_bytes, void* stream) {
   skv_status s = validate_desc(d);
   if (s != SKV_OK) return s;
   WsLayout L;
   if ((s = check_ws(d, ws, ws_bytes, &L)) != SKV_OK) return s;
-  if (!ctx_len || !index_query || !index_keys || !keys || !idx || !n_sel)
+  if (!ctx_len || !index_query || !index_keys || !idx || !n_sel)
     return set_error(SKV_ERR_INVALID, "score_topk: NULL pointer");
   if (d->index_mode == SKV_INDEX_SKETCH_INT4 && !index_scale)
     return set_error(SKV_ERR_INVALID, "score_topk: token mode needs index_scale");
   if (((uintptr_t)index_keys) % 16) return set_error(SKV_ERR_INVALID, "score_topk: index_keys not 16-byte aligned");
-  hipStream_t st = (hipStream_t)stream;
-  hipError_t e = launch_score(*d, ctx_len, index_query, index_keys, index_scale, keys,
-                              ws_ptr<uint32_t>(ws, L.flags), st);
-  if (e == hipSuccess) e = launch_topk(*d, ctx_len, keys, idx, n_sel, ws, L, st);
-  return launched(e, "score_topk");
+  return launched(launch_score_select(*d, ctx_len, index_query, nullptr, nullptr, index_keys,
+                                      index_scale, idx, n_sel, ws, L, (hipStream_t)stream),
+                  "score_topk");
 }
 
 skv_status sparsekv_attend(const skv_layer_desc* d, const void* q, const skv_kv_view* kv,
@@ -217,7 +216,7 @@ skv_status sparsekv_attend(const skv_layer_desc* d, const void* q, const skv_kv_
 
 skv_status sparsekv_step(const skv_layer_desc* d, const int32_t* ctx_len, const void* q,
                          const float* basis, int8_t* qs, float* qs_scale, const void* index_query,
-                         const void* index_keys, const uint16_t* index_scale, double* keys,
+                         const void* index_keys, const uint16_t* index_scale,
                          const skv_kv_view* kv, int32_t* idx, int32_t* n_sel, float sm_scale,
                          float* out, void* ws, size_t ws_bytes, void* stream) {
   skv_status s = validate_desc(d);
@@ -225,18 +224,19 @@ skv_status sparsekv_step(const skv_layer_desc* d, const int32_t* ctx_len, const 
   WsLayout L;
   if ((s = check_ws(d, ws, ws_bytes, &L)) != SKV_OK) return s;
   if ((s = check_kv(d, kv)) != SKV_OK) return s;
-  if (!ctx_len || !q || !index_keys || !keys || !idx || !n_sel || !out)
+  if (!ctx_len || !q || !index_keys || !idx || !n_sel || !out)
     return set_error(SKV_ERR_INVALID, "step: NULL pointer");
+  if (((uintptr_t)index_keys) % 16) return set_error(SKV_ERR_INVALID, "step: index_keys not 16-byte aligned");
   const bool tok = d->index_mode == SKV_INDEX_SKETCH_INT4;
   if (tok && (!basis || !qs || !qs_scale || !index_scale))
     return set_error(SKV_ERR_INVALID, "step: token mode needs basis, qs, qs_scale and index_scale");
   if (!tok && !index_query) return set_error(SKV_ERR_INVALID, "step: block mode needs index_query");
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = tok ? launch_qsketch(*d, q, basis, qs, qs_scale, st) : hipSuccess;
+  // token mode: the projection here, its quantization in the sample kernel
+  hipError_t e = tok ? launch_qsketch_proj(*d, q, basis, ws, L, st) : hipSuccess;
   if (e == hipSuccess)
-    e = launch_score(*d, ctx_len, tok ? (const void*)qs : index_query, index_keys, index_scale,
-                     keys, ws_ptr<uint32_t>(ws, L.flags), st);
-  if (e == hipSuccess) e = launch_topk(*d, ctx_len, keys, idx, n_sel, ws, L, st);
+    e = launch_score_select(*d, ctx_len, tok ? nullptr : index_query, tok ? qs : nullptr,
+                            tok ? qs_scale : nullptr, index_keys, index_scale, idx, n_sel, ws, L, st);
   if (e == hipSuccess) e = launch_attend(*d, q, *kv, idx, n_sel, sm_scale, out, ws, L, st);
   return launched(e, "step");
 }

@@ -1,0 +1,438 @@
+// Device pieces shared by the score and select stages: the exact ranking key
+// of one candidate (token sketch or pooled block key), the candidate range of
+// a sequence, the sampling rule of the threshold estimate, candidate records
+// and DPP wave reductions / scans.
+#pragma once
+
+#include "skv_internal.h"
+
+namespace skv {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kLineKeys = 16;          // candidates per sample line
+constexpr int kSampleCap = 16384;      // sampled candidates per sequence, at most (+16)
+
+// Threshold digit of an exact key: the top 16 bits of the order-preserving
+// image of the key rounded to fp32 (rounding is monotone, so digits are
+// ordered); a bucket spans 1/128 of an octave.  Finite keys have digits in
+// [0x0080, 0xFF7F], so 0 marks an empty sample slot: it sorts below every
+// sample and only matters when the samples are fewer than needed.
+__device__ __forceinline__ uint32_t key_digit16(double x) {
+  return ordered_u32(__double2float_rn(x)) >> 16;
+}
+
+// ---------------------------------------------------------------------------
+// candidate range of a sequence
+// ---------------------------------------------------------------------------
+// Token mode ranks the middle tokens [S, T-L) (page "8 agents x 250K context
+// on two 3090s ...", section "The mechanism": the sinks and the tail are always
+// kept); block mode ranks the floor(T/4) complete blocks (page "3.14M Context
+// on 3x 3090 ...", section "Why": dense until T > 4*block_topk+3).
+struct Range {
+  int T, lo, n;   // candidates are positions lo .. lo+n (tokens or blocks)
+  bool dense;
+};
+
+__device__ __forceinline__ Range cand_range(int mode, int T, int S, int k, int L) {
+  Range r;
+  r.T = T;
+  if (mode == SKV_INDEX_SKETCH_INT4) {
+    r.dense = T <= S + k + L;
+    r.lo = S;
+    r.n = r.dense ? 0 : T - S - L;
+  } else {
+    const int nb = T / 4;
+    r.dense = nb <= k;
+    r.lo = 0;
+    r.n = r.dense ? 0 : nb;
+  }
+  return r;
+}
+
+__device__ __forceinline__ int ctx_of(const int32_t* ctx_len, int b, int max_ctx) {
+  const int T = ctx_len[b];
+  return T < 0 ? 0 : (T > max_ctx ? max_ctx : T);
+}
+
+// Sample: whole lines of 16 candidates, one line in every s; about 4k lines'
+// worth of keys, at most about 16K (every key when the sequence is short).
+__host__ __device__ __forceinline__ int sample_stride(int n, int k) {
+  int s = n / (4 * k);
+  const int s2 = (n + kSampleCap - 1) / kSampleCap;
+  s = s > s2 ? s : s2;
+  return s < 1 ? 1 : s;
+}
+__host__ __device__ __forceinline__ int sample_lines(int n, int k) {
+  const int lines = (n + kLineKeys - 1) / kLineKeys;
+  const int s = sample_stride(n, k);
+  return (lines + s - 1) / s;
+}
+
+// Samples that must lie at or above the threshold bucket: k when every key is
+// sampled, else the expected share of the top k plus 25%, four standard
+// deviations and 8 (the sample only steers speed; the select stays exact).
+__device__ __forceinline__ uint32_t sample_need(int n, int k) {
+  const int s = sample_stride(n, k);
+  if (s == 1) return (uint32_t)k;
+  const int lines = (n + kLineKeys - 1) / kLineKeys;
+  const int nsl = (lines + s - 1) / s;
+  const float e = (float)k * (float)nsl / (float)lines;
+  return (uint32_t)ceilf(1.25f * e + 4.0f * sqrtf(e) + 8.0f);
+}
+
+// ---------------------------------------------------------------------------
+// candidate records: (order-preserving key, position), 16 bytes
+// ---------------------------------------------------------------------------
+struct alignas(16) Cand {
+  uint32_t klo, khi, pos, pad;
+};
+__device__ __forceinline__ uint64_t cand_key(const Cand& c) { return ((uint64_t)c.khi << 32) | c.klo; }
+
+// ---------------------------------------------------------------------------
+// DPP helpers (all 64 lanes of the wave must be active)
+// ---------------------------------------------------------------------------
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWMASK, 0xF, true);
+}
+
+// inclusive prefix sum over the 64 lanes
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += dpp_u32<0x111>(v);           // row_shr:1
+  v += dpp_u32<0x112>(v);           // row_shr:2
+  v += dpp_u32<0x114>(v);           // row_shr:4
+  v += dpp_u32<0x118>(v);           // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
+}
+
+// bitwise AND / OR / max over the 64 lanes, returned in every lane
+__device__ __forceinline__ uint32_t wave_and(uint32_t v) {
+  v &= dpp_u32<0xB1>(v);
+  v &= dpp_u32<0x4E>(v);
+  v &= dpp_u32<0x141>(v);
+  v &= dpp_u32<0x140>(v);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 0) & (uint32_t)__builtin_amdgcn_readlane((int)v, 16) &
+         (uint32_t)__builtin_amdgcn_readlane((int)v, 32) & (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+}
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+  v |= dpp_u32<0xB1>(v);
+  v |= dpp_u32<0x4E>(v);
+  v |= dpp_u32<0x141>(v);
+  v |= dpp_u32<0x140>(v);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 0) | (uint32_t)__builtin_amdgcn_readlane((int)v, 16) |
+         (uint32_t)__builtin_amdgcn_readlane((int)v, 32) | (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+}
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+  v += dpp_u32<0xB1>(v);
+  v += dpp_u32<0x4E>(v);
+  v += dpp_u32<0x141>(v);
+  v += dpp_u32<0x140>(v);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 0) + (uint32_t)__builtin_amdgcn_readlane((int)v, 16) +
+         (uint32_t)__builtin_amdgcn_readlane((int)v, 32) + (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));
+  v = max(v, dpp_u32<0x4E>(v));
+  v = max(v, dpp_u32<0x141>(v));
+  v = max(v, dpp_u32<0x140>(v));
+  return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+
+// lanes below this one, as a 64-bit mask
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int lane = threadIdx.x & 63;
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Per-wave partials in LDS (16 slots; slots of absent waves are ignored) are
+// combined with all 16 reads issued at once -- a loop bounded by the wave
+// count would wait for each read in turn.
+__device__ __forceinline__ uint32_t lds_sum16(const uint32_t* red, int nw) {
+  uint32_t s = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    const uint32_t v = red[w];
+    s += w < nw ? v : 0u;
+  }
+  return s;
+}
+__device__ __forceinline__ uint32_t lds_max16(const uint32_t* red, int nw) {
+  uint32_t s = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    const uint32_t v = red[w];
+    s = max(s, w < nw ? v : 0u);
+  }
+  return s;
+}
+
+// Block-wide exclusive prefix sum of one value per thread, in thread order
+// (blockDim.x a multiple of 64, <= 1024).  `wsum` is LDS scratch of 16 words.
+// Contains barriers: every thread of the block must call it.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const uint32_t incl = wave_incl_scan(v);
+  __syncthreads();
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    const uint32_t s = wsum[w];
+    base += w < wave ? s : 0u;
+    tot += w < nw ? s : 0u;
+  }
+  if (total) *total = tot;
+  return base + incl - v;
+}
+
+// ---------------------------------------------------------------------------
+// exact keys
+// ---------------------------------------------------------------------------
+// Sum over aligned groups of N lanes (N in {2,4,8,16}); every lane of the
+// group ends with the group total.
+template <int N>
+__device__ __forceinline__ int group_sum_i32(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);                // quad_perm [1,0,3,2]
+  if (N >= 4) v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
+  if (N >= 8) v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);   // row_half_mirror
+  if (N >= 16) v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);  // row_mirror
+  return v;
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_add_f64(double v) {
+  const long long u = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(u & 0xFFFFFFFF), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(u >> 32), CTRL, 0xF, 0xF, false);
+  return v + __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
+template <int N>
+__device__ __forceinline__ double group_sum_f64(double x) {
+  x = dpp_add_f64<0xB1>(x);
+  if (N >= 4) x = dpp_add_f64<0x4E>(x);
+  if (N >= 8) x = dpp_add_f64<0x141>(x);
+  if (N >= 16) x = dpp_add_f64<0x140>(x);
+  if (N >= 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
+// int4 x int8 dot of 32 codes held in one 16-byte load.  The nibbles of each
+// 32-bit word are moved to the high half of their byte (x16, still a signed
+// int8), dotted with the matching query bytes, and the sum is divided by 16
+// at the end (exact: every term is a multiple of 16).
+__device__ __forceinline__ int dot32_i4(const u32x4 w, const uint32_t qe[4], const uint32_t qo[4], int acc) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    acc = __builtin_amdgcn_sdot4((int)qe[m], (int)((ws[m] << 4) & 0xF0F0F0F0u), acc, false);
+    acc = __builtin_amdgcn_sdot4((int)qo[m], (int)(ws[m] & 0xF0F0F0F0u), acc, false);
+  }
+  return acc;
+}
+
+// Token sketch source: a candidate is a token whose H_kv*R int4 codes (16*N
+// bytes) are read by N lanes, 16 bytes each, plus its fp16 scale.  The key is
+// the integer dot with the int8 query sketch times the scale, exact in fp64.
+template <int N>
+struct SketchSrc {
+  static constexpr int LANES = N;
+  static constexpr int QROW = 32 * N;      // bytes of one sequence's query row
+  uint32_t qe[4], qo[4];
+  const uint8_t* cbase;     // this lane's 16 bytes of token 0 of the sequence
+  const uint16_t* sbase;    // scales of the sequence
+
+  // qrow: the sequence's 32*N int8 query codes (global or LDS)
+  __device__ __forceinline__ void init(const void* qrow, const void* ik, const uint16_t* isc, int b,
+                                       int max_ctx, int sub) {
+    constexpr int TB = 16 * N;
+    // this lane's 32 query codes: even code positions of each 8-code word in
+    // qe, odd ones in qo (matching the low / high nibbles of the code bytes)
+    const uint8_t* qp = reinterpret_cast<const uint8_t*>(qrow) + 32 * sub;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      uint32_t e = 0, o = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        e |= (uint32_t)qp[8 * m + 2 * j] << (8 * j);
+        o |= (uint32_t)qp[8 * m + 2 * j + 1] << (8 * j);
+      }
+      qe[m] = e;
+      qo[m] = o;
+    }
+    cbase = reinterpret_cast<const uint8_t*>(ik) + (size_t)b * max_ctx * TB + 16 * sub;
+    sbase = isc + (size_t)b * max_ctx;
+  }
+  // raw data of candidate at position p (token index)
+  __device__ __forceinline__ u32x4 load(int p) const {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cbase + (size_t)p * (16 * N)));
+  }
+  __device__ __forceinline__ uint32_t load_aux(int p) const { return sbase[p]; }
+  // the key; every lane of the candidate's group must call it (DPP sum)
+  __device__ __forceinline__ double key(const u32x4 w, uint32_t aux) const {
+    const int acc = group_sum_i32<N>(dot32_i4(w, qe, qo, 0));
+    return (double)(acc >> 4) * (double)half_bits_to_float((uint16_t)aux) + 0.0;  // -0 -> +0
+  }
+};
+
+// Pooled block source: a candidate is a complete 4-token block whose bf16
+// pooled key (8*N values) is read by N lanes, 8 values each.  The key is the
+// fp64 sum of the exact fp32 products (exact in the bf16 domain [2^-8, 2^8)).
+template <int N>
+struct PooledSrc {
+  static constexpr int LANES = N;
+  static constexpr int QROW = 16 * N;      // bytes of one sequence's query row
+  double qd[8];
+  const uint16_t* kb;
+
+  // qrow: the sequence's 8*N bf16 indexer query values
+  __device__ __forceinline__ void init(const void* qrow, const void* ik, const uint16_t*, int b,
+                                       int max_ctx, int sub) {
+    constexpr int ID = 8 * N;
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(qrow);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qd[e] = (double)bf16_bits_to_float(q[8 * sub + e]);
+    kb = reinterpret_cast<const uint16_t*>(ik) + (size_t)b * (max_ctx / 4) * ID + 8 * sub;
+  }
+  __device__ __forceinline__ u32x4 load(int p) const {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + (size_t)p * (8 * N)));
+  }
+  __device__ __forceinline__ uint32_t load_aux(int) const { return 0u; }
+  __device__ __forceinline__ double key(const u32x4 w, uint32_t) const {
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    double acc = 0.0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      acc = fma((double)__uint_as_float(ws[m] << 16), qd[2 * m], acc);
+      acc = fma((double)__uint_as_float(ws[m] & 0xFFFF0000u), qd[2 * m + 1], acc);
+    }
+    return group_sum_f64<N>(acc) + 0.0;   // -0 -> +0
+  }
+};
+
+// ---------------------------------------------------------------------------
+// query sketch quantization (page "8 agents x 250K ...", section "The
+// mechanism": the query sketch is an int8 vector): one scale per sequence,
+// max|s|/127 correctly rounded to fp32, codes rint(s/scale) clamped to +-127,
+// the quotients computed in fp64 and rounded once (exact fp32 division).
+// ---------------------------------------------------------------------------
+// The n <= 2*blockDim.x values at sp (global) become codes q8[0..n) in LDS;
+// returns the scale.  Every thread of the block must call it.
+__device__ __forceinline__ float quantize_sketch(const float* sp, int n, int8_t* q8, uint32_t* red) {
+  const int t = threadIdx.x, nb = blockDim.x;
+  const float v0 = sp[min(t, n - 1)], v1 = sp[min(t + nb, n - 1)];   // unconditional loads
+  const bool ok0 = t < n, ok1 = t + nb < n;
+  // |x| >= 0, so its bit pattern orders like the value
+  uint32_t am = max(ok0 ? __float_as_uint(fabsf(v0)) : 0u, ok1 ? __float_as_uint(fabsf(v1)) : 0u);
+  am = wave_max(am);
+  if ((t & 63) == 0) red[t >> 6] = am;
+  __syncthreads();
+  am = lds_max16(red, nb >> 6);
+  const float amax = __uint_as_float(am);
+  const float scale = amax == 0.0f ? 0.0f : (float)((double)amax / 127.0);
+  auto code = [&](float v) -> int8_t {
+    if (amax == 0.0f) return 0;
+    float r = rintf((float)((double)v / (double)scale));
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int8_t)(int)r;
+  };
+  if (ok0) q8[t] = code(v0);
+  if (ok1) q8[t + nb] = code(v1);
+  __syncthreads();
+  return scale;
+}
+
+// ---------------------------------------------------------------------------
+// threshold digit from the sampled digits
+// ---------------------------------------------------------------------------
+// dg: the sequence's ns sampled digits (16 bits, 0 = empty slot), ns a
+// multiple of 8 and at most 16 * blockDim.x.  Returns the need-th largest
+// digit, which is the largest beta with at least `need` samples at or above
+// it -- or 0 (keep everything) when fewer than `need` samples exist, since
+// empty slots count as digit 0.  MSB-first radix select in 4-bit steps: each
+// thread counts its digits per nibble value with shifts into 4-bit fields
+// (vector ALU only: no per-digit condition masks), the counts are summed over
+// the block, and the first nibble whose count from the top reaches the
+// remainder is taken.  Every thread of the block must call it; red is LDS
+// scratch of 16*16 + 4 words.
+__device__ __forceinline__ uint32_t wg_beta(const uint16_t* dg, int ns, uint32_t need, uint32_t* red) {
+  const int nv = ns / 8;   // 16-byte chunks
+  const int t = threadIdx.x, nb = blockDim.x, nw = nb >> 6, lane = t & 63, wave = t >> 6;
+  uint32_t d[8];           // 16 digits, two per word
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int c = t + m * nb;
+    u32x4 v = reinterpret_cast<const u32x4*>(dg)[min(c, nv - 1)];   // unconditional
+    if (c >= nv) v = (u32x4){0u, 0u, 0u, 0u};
+    d[4 * m + 0] = v.x;
+    d[4 * m + 1] = v.y;
+    d[4 * m + 2] = v.z;
+    d[4 * m + 3] = v.w;
+  }
+  uint32_t prefix = 0, pmask = 0, rem = need;
+#pragma unroll 1
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t shift = 12u - 4u * (uint32_t)p;
+    // A counts digits 0..7, B digits 8..15: at most 8 per 4-bit field
+    uint64_t A = 0, B = 0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const uint32_t x = (e & 1) ? d[e >> 1] >> 16 : d[e >> 1] & 0xFFFFu;
+      const uint32_t ok = 1u - min((x ^ prefix) & pmask, 1u);
+      const uint64_t inc = (uint64_t)ok << (((x >> shift) & 15u) << 2);
+      if (e < 8) A += inc; else B += inc;
+    }
+    // repack the 16 counts into 16-bit fields of 4 words and sum over the wave
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t a = (uint32_t)(A >> (16 * q)) & 0xFFFFu, bq = (uint32_t)(B >> (16 * q)) & 0xFFFFu;
+      // fields f of a, bq: nibble counts of value 4q+f
+      const uint32_t lo = (a & 0xFu) + (bq & 0xFu) + ((((a >> 4) & 0xFu) + ((bq >> 4) & 0xFu)) << 16);
+      const uint32_t hi = ((a >> 8) & 0xFu) + ((bq >> 8) & 0xFu) + ((((a >> 12) & 0xFu) + ((bq >> 12) & 0xFu)) << 16);
+      const uint32_t slo = wave_sum(lo), shi = wave_sum(hi);
+      if (lane == 0) {
+        red[wave * 16 + 4 * q + 0] = slo & 0xFFFFu;
+        red[wave * 16 + 4 * q + 1] = slo >> 16;
+        red[wave * 16 + 4 * q + 2] = shi & 0xFFFFu;
+        red[wave * 16 + 4 * q + 3] = shi >> 16;
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lane r < 16 takes nibble value 15 - r, so an inclusive scan over the
+      // lanes counts from the top; the first lane reaching rem is the pick.
+      // (All lanes stay active: the scan, ballot and readlane need them.)
+      const int j = 15 - (lane & 15);
+      uint32_t v = 0;
+#pragma unroll
+      for (int w = 0; w < 16; ++w) {
+        const uint32_t x = red[w * 16 + j];
+        v += w < nw ? x : 0u;
+      }
+      if (lane >= 16) v = 0;
+      const uint32_t incl = wave_incl_scan(v);
+      const uint64_t m = __ballot(lane < 16 && incl >= rem);
+      const int r = m ? (int)__ffsll((unsigned long long)m) - 1 : 15;
+      const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)(incl - v), r);
+      if (lane == 0) {
+        red[257] = prefix | ((uint32_t)(15 - r) << shift);
+        red[258] = rem - above;
+      }
+    }
+    __syncthreads();
+    prefix = red[257];
+    pmask |= 15u << shift;
+    rem = red[258];
+    __syncthreads();   // red is rewritten by the next pass
+  }
+  return prefix;
+}
+
+}  // namespace skv

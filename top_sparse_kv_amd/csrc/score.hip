@@ -1,4 +1,4 @@
-// Stage A2: exact ranking keys for every candidate of every sequence.
+// Stage A2: exact ranking keys, and the streaming half of stage A3.
 //
 // Token mode -- page "8 agents x 250K context on two 3090s: sparse KV decode
 // with a rank-64 key sketch and a host-RAM tier", section "The mechanism":
@@ -13,168 +13,255 @@
 // scored against the bf16 indexer query each step; the sum is accumulated in
 // fp64, which is exact when the bf16 inputs lie in [2^-8, 2^8) or are 0.
 //
-// Both kernels are pure HBM streams: the sketch (130 B/token at H_kv*R = 256)
-// or the pooled keys (256 B/block) are read once, contiguously, with 16-byte
-// loads spread over the lanes of a token so each wavefront load covers 1 KB
-// of consecutive memory; several tokens per lane are in flight at once.
-#include "skv_internal.h"
+// The index (130 B/token at H_kv*R = 256, or 256 B/block) is the only array
+// read in full, so it is streamed once, with 16-byte loads spread over the
+// lanes of a candidate so that every wavefront load covers 1 KB of
+// consecutive memory; each wave keeps two batches of eight such loads in
+// flight.  Three kernels:
+//   score_kernel<keys>     writes every key (sparsekv_score);
+//   sample_kernel          the 16-bit digits (key rounded to fp32, 1/128
+//                          octave per bucket) of a sample of whole 16-candidate
+//                          lines, written to the workspace;
+//   beta_kernel            one workgroup per sequence finds, from the sampled
+//                          digits, the threshold digit beta (a binary search
+//                          with block-wide counts);
+//   score_kernel<collect>  every wave keeps, per 512-token (256-block)
+//                          segment, the candidates whose digit is >= beta, in
+//                          position order (ballot + popcount), as (key,
+//                          position) records; keys are never stored.
+// No workgroup waits for another and no atomics are used.
+#include "keys_common.h"
 
 namespace skv {
 namespace {
 
-constexpr int kScoreThreads = 256;
-constexpr int kScoreUnroll = 8;
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// int4 x int8 dot of 32 codes held in one 16-byte load.  The nibbles of each
-// 32-bit word are moved to the high half of their byte (x16, still a signed
-// int8), dotted with the matching query bytes, and the sum is divided by 16
-// at the end (exact: every term is a multiple of 16).
-__device__ __forceinline__ int dot32_i4(const u32x4 w, const uint32_t qe[4], const uint32_t qo[4], int acc) {
-  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    acc = __builtin_amdgcn_sdot4((int)qe[m], (int)((ws[m] << 4) & 0xF0F0F0F0u), acc, false);
-    acc = __builtin_amdgcn_sdot4((int)qo[m], (int)(ws[m] & 0xF0F0F0F0u), acc, false);
+// candidates whose key sparsekv_score writes (not restricted by the dense rule)
+__device__ __forceinline__ void key_range(int mode, int T, int S, int L, int& lo, int& n) {
+  if (mode == SKV_INDEX_SKETCH_INT4) {
+    lo = S;
+    n = T - L > S ? T - L - S : 0;
+  } else {
+    lo = 0;
+    n = T / 4;
   }
-  return acc;
 }
 
-// Sum over aligned groups of LPT lanes (LPT in {2,4,8,16}) with DPP moves:
-// two quad permutes, then the half-row and row mirrors.  Every lane of the
-// group ends with the group total.
-template <int LPT>
-__device__ __forceinline__ int group_sum_i32(int v) {
-  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);       // quad_perm [1,0,3,2]
-  if (LPT >= 4) v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // [2,3,0,1]
-  if (LPT >= 8) v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
-  if (LPT >= 16) v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false); // row_mirror
-  return v;
-}
-
-template <int CTRL>
-__device__ __forceinline__ double dpp_add_f64(double v) {
-  const long long u = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(u & 0xFFFFFFFF), CTRL, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(u >> 32), CTRL, 0xF, 0xF, false);
-  return v + __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
-}
-
-template <int LPB>
-__device__ __forceinline__ double group_sum_f64(double x) {
-  x = dpp_add_f64<0xB1>(x);
-  if (LPB >= 4) x = dpp_add_f64<0x4E>(x);
-  if (LPB >= 8) x = dpp_add_f64<0x141>(x);
-  if (LPB >= 16) x = dpp_add_f64<0x140>(x);
-  if (LPB >= 32) x += __shfl_xor(x, 16);
-  return x;
-}
-
-template <int LPT>  // lanes per token; a token's sketch is 16*LPT bytes
-__global__ __launch_bounds__(kScoreThreads) void score_sketch_kernel(
-    const int8_t* __restrict__ qs, const uint8_t* __restrict__ codes,
-    const uint16_t* __restrict__ scale, const int32_t* __restrict__ ctx_len,
-    double* __restrict__ keys, uint32_t* __restrict__ flags, int max_ctx, int S, int L,
-    int chunk) {
-  constexpr int TB = 16 * LPT;
-  constexpr int TPW = 64 / LPT;
-  constexpr int STEP = (kScoreThreads / 64) * TPW;
+template <class Src, bool COLLECT>
+__global__ __launch_bounds__(kThreads) void score_kernel(
+    const void* __restrict__ iq, const void* __restrict__ ik, const uint16_t* __restrict__ isc,
+    const int32_t* __restrict__ ctx_len, double* __restrict__ keys,
+    const TopkState* __restrict__ state, Cand* __restrict__ cand, uint32_t* __restrict__ segcnt,
+    uint32_t* __restrict__ flags, int mode, int max_ctx, int S, int k, int L, int n_seg,
+    int seg_items) {
+  constexpr int N = Src::LANES, IPW = 64 / N, PER_IT = kUnroll * IPW;
   const int b = blockIdx.y;
   const int T = clamp_ctx(ctx_len, b, max_ctx, blockIdx.x == 0 ? flags : nullptr);
-  const int lo = S;
-  const int hi = T - L > S ? T - L : S;
-  const int t0 = lo + blockIdx.x * chunk;
-  if (t0 >= hi) return;
-  const int t1 = min(hi, t0 + chunk);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int sub = lane % LPT, tw = lane / LPT;
-
-  // this lane's 32 query codes: even code positions of each 8-code word in
-  // qe, odd ones in qo (matching the low / high nibbles of the code bytes)
-  const uint8_t* qp = reinterpret_cast<const uint8_t*>(qs) + (size_t)b * (2 * TB) + 32 * sub;
-  uint32_t qe[4], qo[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    uint32_t e = 0, o = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      e |= (uint32_t)qp[8 * m + 2 * j] << (8 * j);
-      o |= (uint32_t)qp[8 * m + 2 * j + 1] << (8 * j);
-    }
-    qe[m] = e;
-    qo[m] = o;
+  int lo, n;
+  if (COLLECT) {
+    const Range r = cand_range(mode, T, S, k, L);
+    if (r.dense) return;
+    lo = r.lo;
+    n = r.n;
+  } else {
+    key_range(mode, T, S, L, lo, n);
   }
-
-  const uint8_t* cbase = codes + (size_t)b * max_ctx * TB + 16 * sub;
-  const uint16_t* sbase = scale + (size_t)b * max_ctx;
-  double* kbase = keys + (size_t)b * max_ctx;
-  for (int base = t0 + wave * TPW + tw; base < t1; base += STEP * kScoreUnroll) {
-    u32x4 w[kScoreUnroll];
-    uint16_t sc[kScoreUnroll];
-    // all loads issued unconditionally (past the end they re-read the last
-    // token; those results are dropped), so they are in flight together
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int seg = blockIdx.x * (kThreads / 64) + wave;
+  const int i0 = seg * seg_items;
+  if (i0 >= n) return;   // wave-uniform; there is no barrier below
+  const int i1 = min(n, i0 + seg_items);
+  const int sub = lane % N, tw = lane / N;
+  Src src;
+  src.init(reinterpret_cast<const uint8_t*>(iq) + (size_t)b * Src::QROW, ik, isc, b, max_ctx, sub);
+  u32x4 w[kUnroll];
+  uint32_t ax[kUnroll];
+  // loads issued unconditionally (past the end they re-read the last
+  // candidate; those results are dropped), so a batch is in flight together
+  auto load_batch = [&](int base, u32x4* wv, uint32_t* av) {
 #pragma unroll
-    for (int u = 0; u < kScoreUnroll; ++u) {
-      const int t = min(base + u * STEP, t1 - 1);
-      w[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cbase + (size_t)t * TB));
-      sc[u] = sbase[t];   // the token's scale, fetched with its codes
+    for (int u = 0; u < kUnroll; ++u) {
+      const int i = min(base + u * IPW + tw, i1 - 1);
+      wv[u] = src.load(lo + i);
+      av[u] = src.load_aux(lo + i);
     }
+  };
+  load_batch(i0, w, ax);
+  const uint32_t beta = COLLECT ? state[b].beta : 0u;   // read while the first loads fly
+  double* kout = keys + (size_t)b * (mode == SKV_INDEX_SKETCH_INT4 ? max_ctx : max_ctx / 4) + lo;
+  u32x4* cseg = reinterpret_cast<u32x4*>(cand + ((size_t)b * n_seg + seg) * seg_items);
+  const uint64_t lt = lanemask_lt();
+  uint32_t cnt = 0;
+  for (int base = i0; base < i1; base += PER_IT) {
+    u32x4 wn[kUnroll];
+    uint32_t an[kUnroll];
+    if (base + PER_IT < i1) load_batch(base + PER_IT, wn, an);   // next batch in flight
 #pragma unroll
-    for (int u = 0; u < kScoreUnroll; ++u) {
-      const int t = base + u * STEP;
-      const int acc = group_sum_i32<LPT>(dot32_i4(w[u], qe, qo, 0));
-      if (sub == 0 && t < t1) {
-        const double key = (double)(acc >> 4) * (double)half_bits_to_float(sc[u]) + 0.0;  // -0 -> +0
-        kbase[t] = key;
+    for (int u = 0; u < kUnroll; ++u) {
+      const int i = base + u * IPW + tw;
+      const double key = src.key(w[u], ax[u]);
+      if (!COLLECT) {
+        if (sub == 0 && i < i1) kout[i] = key;
+      } else {
+        const bool sel = sub == 0 && i < i1 && key_digit16(key) >= beta;
+        const uint64_t m = __ballot(sel);
+        if (sel) {
+          const uint64_t ok = ordered_u64(key);
+          const uint32_t rank = cnt + (uint32_t)__popcll(m & lt);
+          cseg[rank] = (u32x4){(uint32_t)ok, (uint32_t)(ok >> 32), (uint32_t)(lo + i), 0u};
+        }
+        cnt += (uint32_t)__popcll(m);
       }
     }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      w[u] = wn[u];
+      ax[u] = an[u];
+    }
+  }
+  if (COLLECT && lane == 0) segcnt[(size_t)b * n_seg + seg] = cnt;
+}
+
+// Sampled keys: line j of the sample is candidates [16*s*j, 16*s*j + 16).
+// Each wave computes PER_IT/16 lines with one batch of loads and writes their
+// digits.  In the fused step the query sketch is quantized here first (from
+// the fp32 sketch in the workspace) and workgroup 0 of each sequence writes
+// it out.
+template <class Src, bool FROM_PROJ>
+__global__ __launch_bounds__(kThreads) void sample_kernel(
+    const void* __restrict__ iq, const float* __restrict__ sproj, int8_t* __restrict__ qs_out,
+    float* __restrict__ qscale_out, int nq, const void* __restrict__ ik,
+    const uint16_t* __restrict__ isc, const int32_t* __restrict__ ctx_len,
+    uint16_t* __restrict__ sdig, int n_samp, int mode, int max_ctx, int S, int k, int L) {
+  constexpr int N = Src::LANES, IPW = 64 / N, PER_IT = kUnroll * IPW;
+  constexpr int LPW = PER_IT / kLineKeys;          // sample lines per wave
+  __shared__ int8_t q8[512];
+  __shared__ uint32_t red[16];
+  const int b = blockIdx.y;
+  const void* qrow;
+  if constexpr (FROM_PROJ) {
+    const float scale = quantize_sketch(sproj + (size_t)b * nq, nq, q8, red);
+    if (blockIdx.x == 0) {
+      for (int i = threadIdx.x; i < nq; i += kThreads) qs_out[(size_t)b * nq + i] = q8[i];
+      if (threadIdx.x == 0) qscale_out[b] = scale;
+    }
+    qrow = q8;
+  } else {
+    qrow = reinterpret_cast<const uint8_t*>(iq) + (size_t)b * Src::QROW;
+  }
+  const Range r = cand_range(mode, ctx_of(ctx_len, b, max_ctx), S, k, L);
+  if (r.dense) return;
+  const int s = sample_stride(r.n, k);
+  const int nsl = sample_lines(r.n, k);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j0 = (blockIdx.x * (kThreads / 64) + wave) * LPW;
+  if (j0 >= nsl) return;   // wave-uniform; no barrier below
+  const int sub = lane % N, tw = lane / N;
+  Src src;
+  src.init(qrow, ik, isc, b, max_ctx, sub);
+  u32x4 w[kUnroll];
+  uint32_t ax[kUnroll];
+  bool ok[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int o = u * IPW + tw;
+    const int j = j0 + o / kLineKeys;
+    const int i = j * s * kLineKeys + o % kLineKeys;
+    ok[u] = j < nsl && i < r.n;
+    const int ic = ok[u] ? i : r.n - 1;
+    w[u] = src.load(r.lo + ic);
+    ax[u] = src.load_aux(r.lo + ic);
+  }
+  uint16_t* dg = sdig + (size_t)b * n_samp * kLineKeys;
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int o = u * IPW + tw;
+    const int j = j0 + o / kLineKeys;
+    const double key = src.key(w[u], ax[u]);
+    if (sub == 0 && j < nsl)
+      dg[j * kLineKeys + o % kLineKeys] = ok[u] ? (uint16_t)key_digit16(key) : (uint16_t)0u;
   }
 }
 
-template <int LPB>  // lanes per pooled key; index_dim = 8*LPB bf16
-__global__ __launch_bounds__(kScoreThreads) void score_pooled_kernel(
-    const uint16_t* __restrict__ qi, const uint16_t* __restrict__ kp,
-    const int32_t* __restrict__ ctx_len, double* __restrict__ keys, uint32_t* __restrict__ flags,
-    int max_ctx, int chunk) {
-  constexpr int ID = 8 * LPB;
-  constexpr int BPW = 64 / LPB;
-  constexpr int STEP = (kScoreThreads / 64) * BPW;
-  const int b = blockIdx.y;
-  const int T = clamp_ctx(ctx_len, b, max_ctx, blockIdx.x == 0 ? flags : nullptr);
-  const int nb = T / 4;
-  const int nbmax = max_ctx / 4;
-  const int j0 = blockIdx.x * chunk;
-  if (j0 >= nb) return;
-  const int j1 = min(nb, j0 + chunk);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int sub = lane % LPB, tw = lane / LPB;
-  double qd[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) qd[e] = (double)bf16_bits_to_float(qi[(size_t)b * ID + 8 * sub + e]);
-  const uint16_t* kb = kp + (size_t)b * nbmax * ID + 8 * sub;
-  double* kout = keys + (size_t)b * nbmax;
-  for (int base = j0 + wave * BPW + tw; base < j1; base += STEP * kScoreUnroll) {
-    u32x4 w[kScoreUnroll];
-#pragma unroll
-    for (int u = 0; u < kScoreUnroll; ++u) {
-      const int j = min(base + u * STEP, j1 - 1);
-      w[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + (size_t)j * ID));
-    }
-#pragma unroll
-    for (int u = 0; u < kScoreUnroll; ++u) {
-      const int j = base + u * STEP;
-      const uint32_t ws[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
-      double acc = 0.0;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        acc = fma((double)__uint_as_float(ws[m] << 16), qd[2 * m], acc);
-        acc = fma((double)__uint_as_float(ws[m] & 0xFFFF0000u), qd[2 * m + 1], acc);
-      }
-      acc = group_sum_f64<LPB>(acc);
-      if (sub == 0 && j < j1) kout[j] = acc + 0.0;   // -0 -> +0
+// threshold digit of each sequence from its sampled digits
+__global__ __launch_bounds__(1024) void beta_kernel(const uint16_t* __restrict__ sdig, int n_samp,
+                                                     const int32_t* __restrict__ ctx_len,
+                                                     TopkState* __restrict__ state, int mode,
+                                                     int max_ctx, int S, int k, int L) {
+  __shared__ uint32_t red[16 * 16 + 4];
+  const int b = blockIdx.x;
+  const Range r = cand_range(mode, ctx_of(ctx_len, b, max_ctx), S, k, L);
+  if (r.dense) return;
+  const uint32_t beta = wg_beta(sdig + (size_t)b * n_samp * kLineKeys,
+                                sample_lines(r.n, k) * kLineKeys, sample_need(r.n, k), red);
+  if (threadIdx.x == 0) state[b].beta = beta;
+}
+
+template <class Src>
+hipError_t launch_token_or_block(const skv_layer_desc& d, const int32_t* ctx_len, const void* iq,
+                                 int8_t* qs_out, float* qscale_out, const void* ik,
+                                 const uint16_t* isc, double* keys, void* ws, const WsLayout* Lw,
+                                 uint32_t* flags, bool collect, hipStream_t st) {
+  const int mode = d.index_mode;
+  const int S = mode == SKV_INDEX_SKETCH_INT4 ? d.n_sink : 0;
+  const int L = mode == SKV_INDEX_SKETCH_INT4 ? d.n_tail : 0;
+  const int seg_items = mode == SKV_INDEX_SKETCH_INT4 ? kSegTok : kSegBlk;
+  const int n_seg = (max_candidates(d) + seg_items - 1) / seg_items;
+  const dim3 grid((n_seg + 3) / 4 > 0 ? (n_seg + 3) / 4 : 1, d.batch);
+  if (!collect) {
+    hipLaunchKernelGGL((score_kernel<Src, false>), grid, dim3(kThreads), 0, st, iq, ik, isc,
+                       ctx_len, keys, nullptr, nullptr, nullptr, flags, mode, d.max_ctx, S, d.topk,
+                       L, n_seg, seg_items);
+    return hipGetLastError();
+  }
+  constexpr int LPG = kUnroll * (64 / Src::LANES) / kLineKeys * (kThreads / 64);
+  const dim3 sgrid((Lw->n_samp + LPG - 1) / LPG, d.batch);
+  uint16_t* sdig = ws_ptr<uint16_t>(ws, Lw->sdig);
+  const int nq = d.n_kv_heads * d.rank;
+  if (qs_out)
+    hipLaunchKernelGGL((sample_kernel<Src, true>), sgrid, dim3(kThreads), 0, st, iq,
+                       ws_ptr<const float>(ws, Lw->sproj), qs_out, qscale_out, nq, ik, isc, ctx_len,
+                       sdig, Lw->n_samp, mode, d.max_ctx, S, d.topk, L);
+  else
+    hipLaunchKernelGGL((sample_kernel<Src, false>), sgrid, dim3(kThreads), 0, st, iq, nullptr,
+                       nullptr, nullptr, nq, ik, isc, ctx_len, sdig, Lw->n_samp, mode, d.max_ctx, S,
+                       d.topk, L);
+  TopkState* state = ws_ptr<TopkState>(ws, Lw->state);
+  hipLaunchKernelGGL(beta_kernel, dim3(d.batch), dim3(1024), 0, st, sdig, Lw->n_samp, ctx_len, state,
+                     mode, d.max_ctx, S, d.topk, L);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const void* iq_score = qs_out ? (const void*)qs_out : iq;
+  hipLaunchKernelGGL((score_kernel<Src, true>), grid, dim3(kThreads), 0, st, iq_score, ik, isc,
+                     ctx_len, nullptr, state, ws_ptr<Cand>(ws, Lw->cand),
+                     ws_ptr<uint32_t>(ws, Lw->segcnt), flags, mode, d.max_ctx, S, d.topk, L,
+                     Lw->n_seg, Lw->seg_items);
+  return hipGetLastError();
+}
+
+hipError_t launch_any(const skv_layer_desc& d, const int32_t* ctx_len, const void* iq,
+                      int8_t* qs_out, float* qscale_out, const void* ik, const uint16_t* isc,
+                      double* keys, void* ws, const WsLayout* Lw, uint32_t* flags, bool collect,
+                      hipStream_t st) {
+#define SKV_GO(SRC) return launch_token_or_block<SRC>(d, ctx_len, iq, qs_out, qscale_out, ik, isc, keys, ws, Lw, flags, collect, st)
+  if (d.index_mode == SKV_INDEX_SKETCH_INT4) {
+    switch (d.n_kv_heads * d.rank / 2) {   // sketch bytes per token = 16 * lanes
+      case 32: SKV_GO(SketchSrc<2>);
+      case 64: SKV_GO(SketchSrc<4>);
+      case 128: SKV_GO(SketchSrc<8>);
+      case 256: SKV_GO(SketchSrc<16>);
+      default: return hipErrorInvalidValue;
     }
   }
+  switch (d.index_dim) {   // pooled key bytes = 16 * lanes
+    case 64: SKV_GO(PooledSrc<8>);
+    case 128: SKV_GO(PooledSrc<16>);
+    case 256: SKV_GO(PooledSrc<32>);
+    default: return hipErrorInvalidValue;
+  }
+#undef SKV_GO
 }
 
 }  // namespace
@@ -182,39 +269,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_pooled_kernel(
 hipError_t launch_score(const skv_layer_desc& d, const int32_t* ctx_len, const void* iq,
                         const void* ik, const uint16_t* isc, double* keys, uint32_t* flags,
                         hipStream_t st) {
-  if (d.index_mode == SKV_INDEX_SKETCH_INT4) {
-    const int tb = d.n_kv_heads * d.rank / 2;
-    const int nchunk = (d.max_ctx + kScoreChunk - 1) / kScoreChunk;
-    const dim3 grid(nchunk > 0 ? nchunk : 1, d.batch);
-#define SKV_SK(LPT)                                                                        \
-  hipLaunchKernelGGL(score_sketch_kernel<LPT>, grid, dim3(kScoreThreads), 0, st,           \
-                     (const int8_t*)iq, (const uint8_t*)ik, isc, ctx_len, keys, flags,     \
-                     d.max_ctx, d.n_sink, d.n_tail, kScoreChunk)
-    switch (tb) {
-      case 32: SKV_SK(2); break;
-      case 64: SKV_SK(4); break;
-      case 128: SKV_SK(8); break;
-      case 256: SKV_SK(16); break;
-      default: return hipErrorInvalidValue;
-    }
-#undef SKV_SK
-  } else {
-    const int nbmax = d.max_ctx / 4;
-    const int nchunk = (nbmax + kPooledChunk - 1) / kPooledChunk;
-    const dim3 grid(nchunk > 0 ? nchunk : 1, d.batch);
-#define SKV_PK(LPB)                                                                         \
-  hipLaunchKernelGGL(score_pooled_kernel<LPB>, grid, dim3(kScoreThreads), 0, st,            \
-                     (const uint16_t*)iq, (const uint16_t*)ik, ctx_len, keys, flags,        \
-                     d.max_ctx, kPooledChunk)
-    switch (d.index_dim) {
-      case 64: SKV_PK(8); break;
-      case 128: SKV_PK(16); break;
-      case 256: SKV_PK(32); break;
-      default: return hipErrorInvalidValue;
-    }
-#undef SKV_PK
-  }
-  return hipGetLastError();
+  return launch_any(d, ctx_len, iq, nullptr, nullptr, ik, isc, keys, nullptr, nullptr, flags, false, st);
+}
+
+hipError_t launch_sample_collect(const skv_layer_desc& d, const int32_t* ctx_len, const void* iq,
+                                 int8_t* qs_out, float* qscale_out, const void* ik,
+                                 const uint16_t* isc, void* ws, const WsLayout& L, hipStream_t st) {
+  return launch_any(d, ctx_len, iq, qs_out, qscale_out, ik, isc, nullptr, ws, &L,
+                    ws_ptr<uint32_t>(ws, L.flags), true, st);
 }
 
 }  // namespace skv

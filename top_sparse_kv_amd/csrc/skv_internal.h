@@ -16,18 +16,16 @@ namespace skv {
 // ---------------------------------------------------------------------------
 constexpr int kHistBits = 12;                 // coarse-key histogram digit (1/8 octave)
 constexpr int kHistBins = 1 << kHistBits;     // 4096 bins
-constexpr int kListCap = 8192;                // candidate list capacity per sequence
-constexpr int kMaxTopk = 4096;                // largest budget the select kernel handles in LDS
-constexpr int kHistChunk = 2048;              // keys per collect workgroup
-constexpr int kSegCap = 128;                  // candidate slots per collect workgroup
-constexpr int kBitmapWords = 12288;           // LDS position bitmap (candidates <= 393,216)
+constexpr int kListCap = 8192;                // candidates the select kernel holds in LDS
+constexpr int kMaxTopk = 4096;                // largest budget
+constexpr int kMaxSeg = 4096;                 // candidate segments per sequence
+constexpr int kSegTok = 512;                  // candidates per segment, token mode
+constexpr int kSegBlk = 256;                  // candidates per segment, block mode
 constexpr int kAttRowsPerWave = 32;           // selected rows per attention wave
 constexpr int kAttWaves = 8;                  // waves per attention workgroup
 constexpr int kAttRowsPerWG = kAttRowsPerWave * kAttWaves;
-constexpr int kScoreChunk = 2048;             // tokens per sketch-score workgroup
-constexpr int kPooledChunk = 1024;            // blocks per pooled-score workgroup
 
-// per-sequence select state written by the sample kernel (u32 words)
+// per-sequence select state written by the sample stage (u32 words)
 struct TopkState {
   uint32_t beta;       // threshold bucket: candidates with digit >= beta are collected
   uint32_t pad[15];
@@ -38,11 +36,14 @@ struct TopkState {
 // ---------------------------------------------------------------------------
 struct WsLayout {
   size_t flags;        // uint32 flag word (+ padding)
-  size_t state;        // [B] TopkState
-  size_t segcnt;       // [B][n_seg] u32 candidates found by each collect workgroup
-  size_t lkey;         // [B][n_seg][kSegCap] u64 ordered keys
-  size_t lpos;         // [B][n_seg][kSegCap] u32 positions
-  int n_seg;           // collect workgroups per sequence
+  size_t state;        // [B] TopkState (sparsekv_topk path)
+  size_t sproj;        // [B][H_kv*R] f32 unquantized query sketch
+  size_t sdig;         // [B][n_samp*16] u16 sampled key digits
+  size_t segcnt;       // [B][n_seg] u32 candidates found in each segment
+  size_t cand;         // [B][n_seg*seg_items] Cand; also the fallback key buffer
+  int n_seg;           // segments per sequence
+  int seg_items;       // candidates per segment
+  int n_samp;          // largest number of sampled lines per sequence
   size_t att_ml;       // [B][H_kv][n_chunks][16][2] f32  (m, l) per head row
   size_t att_o;        // [B][H_kv][n_chunks][G][D] f32
   size_t total;
@@ -55,18 +56,32 @@ inline int select_capacity(const skv_layer_desc& d) {
   return d.index_mode == SKV_INDEX_SKETCH_INT4 ? d.n_sink + d.topk + d.n_tail : 4 * d.topk + 3;
 }
 
+inline int max_candidates(const skv_layer_desc& d) {
+  return d.index_mode == SKV_INDEX_SKETCH_INT4 ? d.max_ctx : d.max_ctx / 4;
+}
+
+// Sample lines of a sequence, at most: every line when short, never more than
+// 1024 lines (16K candidates).
+inline int max_sample_lines(int nmax) {
+  const int lines = (nmax + 15) / 16;
+  return lines < 1024 ? (lines > 0 ? lines : 1) : 1024;
+}
+
 inline WsLayout ws_layout(const skv_layer_desc& d) {
   WsLayout w{};
   size_t off = 0;
   const size_t B = (size_t)d.batch;
   w.flags = off;  off = align_up(off + 256, 256);
-  const int max_cand = d.index_mode == SKV_INDEX_SKETCH_INT4 ? d.max_ctx : d.max_ctx / 4;
-  w.n_seg = (max_cand + kHistChunk - 1) / kHistChunk;
+  const int max_cand = max_candidates(d);
+  w.seg_items = d.index_mode == SKV_INDEX_SKETCH_INT4 ? kSegTok : kSegBlk;
+  w.n_seg = (max_cand + w.seg_items - 1) / w.seg_items;
   if (w.n_seg < 1) w.n_seg = 1;
-  w.state = off;  off = align_up(off + B * sizeof(TopkState), 256);
-  w.segcnt = off; off = align_up(off + B * w.n_seg * 4, 256);
-  w.lkey = off;   off = align_up(off + B * w.n_seg * kSegCap * 8, 256);
-  w.lpos = off;   off = align_up(off + B * w.n_seg * kSegCap * 4, 256);
+  w.n_samp = max_sample_lines(max_cand);
+  w.state = off;   off = align_up(off + B * sizeof(TopkState), 256);
+  w.sproj = off;   off = align_up(off + B * (size_t)(d.n_kv_heads * (d.rank > 0 ? d.rank : 1)) * 4, 256);
+  w.sdig = off;    off = align_up(off + B * (size_t)w.n_samp * 16 * 2, 256);
+  w.segcnt = off;  off = align_up(off + B * w.n_seg * 4, 256);
+  w.cand = off;    off = align_up(off + B * (size_t)w.n_seg * w.seg_items * 16, 256);
   const int cap = select_capacity(d);
   w.n_att_chunks = (cap + kAttRowsPerWG - 1) / kAttRowsPerWG;
   const int G = d.n_q_heads / d.n_kv_heads;
@@ -122,15 +137,33 @@ __device__ __forceinline__ float bf16_bits_to_float(uint16_t h) {
 // ---------------------------------------------------------------------------
 // launchers (each returns hipSuccess or the launch error)
 // ---------------------------------------------------------------------------
+// query sketch, unquantized: sproj [B][H_kv*R] f32 in the workspace
+hipError_t launch_qsketch_proj(const skv_layer_desc& d, const void* q, const float* basis,
+                               void* ws, const WsLayout& L, hipStream_t st);
+// query sketch: projection + quantization into qs int8 / qs_scale
 hipError_t launch_qsketch(const skv_layer_desc& d, const void* q, const float* basis, int8_t* qs,
-                          float* qs_scale, hipStream_t st);
+                          float* qs_scale, void* ws, const WsLayout& L, hipStream_t st);
 // keys only
 hipError_t launch_score(const skv_layer_desc& d, const int32_t* ctx_len, const void* iq,
                         const void* ik, const uint16_t* isc, double* keys, uint32_t* flags,
                         hipStream_t st);
-// select from keys: sample + collect + final
+// select from materialized keys: sample + collect + final
 hipError_t launch_topk(const skv_layer_desc& d, const int32_t* ctx_len, const double* keys,
                        int32_t* idx, int32_t* n_sel, void* ws, const WsLayout& L, hipStream_t st);
+// score and select without materializing keys: sample (from the index) +
+// score/collect + final (which recomputes keys itself in the rare case the
+// candidates are too few)
+// sample + score/collect (score.hip); the final select is launched by launch_score_select.
+// Token mode with qs_out != NULL: the query sketch is quantized from sproj in
+// the workspace and written to qs_out / qscale_out; otherwise iq is the index
+// query (int8 sketch or bf16 indexer query).
+hipError_t launch_sample_collect(const skv_layer_desc& d, const int32_t* ctx_len, const void* iq,
+                                 int8_t* qs_out, float* qscale_out, const void* ik,
+                                 const uint16_t* isc, void* ws, const WsLayout& L, hipStream_t st);
+hipError_t launch_score_select(const skv_layer_desc& d, const int32_t* ctx_len, const void* iq,
+                               int8_t* qs_out, float* qscale_out, const void* ik,
+                               const uint16_t* isc, int32_t* idx, int32_t* n_sel, void* ws,
+                               const WsLayout& L, hipStream_t st);
 hipError_t launch_attend(const skv_layer_desc& d, const void* q, const skv_kv_view& kv,
                          const int32_t* idx, const int32_t* n_sel, float sm_scale, float* out,
                          void* ws, const WsLayout& L, hipStream_t st);

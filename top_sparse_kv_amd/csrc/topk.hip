@@ -12,75 +12,38 @@
 // (key, position) is a unique composite and the kept set is unique; the
 // kernels below find it without depending on workgroup scheduling.
 //
-// Three kernels, none of which uses a global atomic (same-address atomics
-// from many workgroups serialise in the memory system):
-//   sample   one workgroup per sequence histograms a 12-bit order-preserving
-//            digit of a strided sample of the keys (the digit is the key
-//            rounded to fp32, so one bucket spans 1/8 of an octave) and picks
-//            the bucket beta above which the sample predicts, with a margin,
-//            at least k keys;
-//   collect  workgroups of 2048 keys write the keys with digit >= beta into a
-//            segment of their own (at most kSegCap) and their count;
-//   final    one workgroup per sequence gathers the segments into LDS and runs
-//            an exact MSB-first radix select over the 96-bit composite
-//            (ordered key, ~position), stopping once the remaining bucket is
-//            kept whole; the kept positions are marked in an LDS bitmap and
-//            read back in order.
-// If the candidates cannot be used (a segment overflowed, fewer than k or more
-// than the LDS list holds -- degenerate data such as all-equal keys), the
-// final kernel runs the same exact radix select over every key of the
-// sequence in global memory and compacts in position order (slow path,
-// flagged as SKV_FLAG_TOPK_SLOW).  The sample only affects speed, never the
-// result.
-#include "select_common.h"
+// The select works on candidates: the keys whose 12-bit digit (the key
+// rounded to fp32, 1/8 octave per bucket) is at least a threshold bucket beta
+// estimated from a sample of whole 16-key lines.  Candidates are stored per
+// segment (512 tokens or 256 blocks, one wave each) in position order.  With
+// keys already in memory (sparsekv_topk) two kernels produce them:
+//   sample   one workgroup per sequence histograms the sampled digits -> beta;
+//   collect  one wave per segment keeps the digits >= beta, in order.
+// The fused path (score.hip) produces the same records straight from the
+// index.  Then, one workgroup per sequence:
+//   final    gathers the candidates into LDS (position order), runs an exact
+//            MSB-first radix select over the 96-bit composite (ordered key,
+//            ~position), stopping once the boundary bucket is kept whole, and
+//            writes the kept positions by an ordered prefix sum.
+// Fallbacks, flagged SKV_FLAG_TOPK_SLOW: more candidates than LDS holds ->
+// the same select over the records in global memory; fewer candidates than
+// the budget (the sample overestimated beta) -> the select over every key of
+// the sequence (recomputed from the index in the fused path).  The sample
+// only affects speed, never the result.
+#include "keys_common.h"
 
 namespace skv {
 namespace {
 
 constexpr int kSelThreads = 256;
-constexpr int kFinalThreads = 1024;
-constexpr int kKeysPerThread = kHistChunk / kSelThreads;   // 8
-constexpr int kMaxSeg = 1024;                              // segments per sequence
+constexpr int kFinalThreads = 1024;   // sample kernel of the keys path
+constexpr int kFT = 1024;             // final select kernel
+constexpr int kSegPT = kMaxSeg / kFT; // segment counts per thread
+constexpr int kGPT = kListCap / kFT;  // candidates per thread in the fast path
 
-struct Range {
-  int T, lo, n;   // candidates are keys[lo .. lo+n)
-  bool dense;
-  size_t stride;  // keys row stride
-};
-
-__device__ __forceinline__ Range cand_range(int mode, int T, int S, int k, int L, int max_ctx) {
-  Range r;
-  r.T = T;
-  if (mode == SKV_INDEX_SKETCH_INT4) {
-    r.stride = (size_t)max_ctx;
-    r.dense = T <= S + k + L;
-    r.lo = S;
-    r.n = r.dense ? 0 : T - S - L;
-  } else {
-    r.stride = (size_t)(max_ctx / 4);
-    const int nb = T / 4;
-    r.dense = nb <= k;
-    r.lo = 0;
-    r.n = r.dense ? 0 : nb;
-  }
-  return r;
-}
-
-__device__ __forceinline__ int ctx_of(const int32_t* ctx_len, int b, int max_ctx) {
-  int T = ctx_len[b];
-  return T < 0 ? 0 : (T > max_ctx ? max_ctx : T);
-}
-
-__device__ __forceinline__ double canon(double x) { return x + 0.0; }
-
-// The sample is whole 16-key lines (128 B) taken every s lines: about 8k
-// samples per sequence, every key (an exact histogram) when short.
-constexpr int kLineKeys = 16;
-__device__ __forceinline__ int sample_stride(int n, int k) {
-  int s = n / (8 * k);
-  return s < 1 ? 1 : (s > 16 ? 16 : s);
-}
-
+// ---------------------------------------------------------------------------
+// sample and collect from materialized keys
+// ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kFinalThreads) void topk_sample_kernel(
     const double* __restrict__ keys, const int32_t* __restrict__ ctx_len,
     TopkState* __restrict__ state, int mode, int max_ctx, int S, int k, int L) {
@@ -89,16 +52,13 @@ __global__ __launch_bounds__(kFinalThreads) void topk_sample_kernel(
   __shared__ uint32_t h[kHistBins];
   __shared__ uint32_t wsum[16];
   const int b = blockIdx.x;
-  const Range r = cand_range(mode, ctx_of(ctx_len, b, max_ctx), S, k, L, max_ctx);
+  const Range r = cand_range(mode, ctx_of(ctx_len, b, max_ctx), S, k, L);
   if (r.dense) return;
   const int s = sample_stride(r.n, k);
-  const int lines = (r.n + kLineKeys - 1) / kLineKeys;
-  const int nsl = (lines + s - 1) / s;               // sampled lines
-  const int nj = nsl * kLineKeys;                    // sample slots
+  const int nj = sample_lines(r.n, k) * kLineKeys;   // sample slots
   for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) h[i] = 0u;
   __syncthreads();
-  const double* kb = keys + (size_t)b * r.stride + r.lo;
-  uint32_t taken = 0;
+  const double* kb = keys + (size_t)b * (mode == SKV_INDEX_SKETCH_INT4 ? max_ctx : max_ctx / 4) + r.lo;
   for (int j0 = 0; j0 < nj; j0 += UNR * kFinalThreads) {
     double x[UNR];
     bool ok[UNR];
@@ -111,22 +71,10 @@ __global__ __launch_bounds__(kFinalThreads) void topk_sample_kernel(
     }
 #pragma unroll
     for (int u = 0; u < UNR; ++u)
-      if (ok[u]) {
-        atomicAdd(&h[key_digit(canon(x[u]))], 1u);
-        ++taken;
-      }
+      if (ok[u]) atomicAdd(&h[key_digit(x[u] + 0.0)], 1u);
   }
   __syncthreads();
-  // samples needed above beta: exactly k when every key is sampled, else the
-  // expected share of the top k plus 25% and four standard deviations
-  uint32_t need;
-  if (s == 1) {
-    need = (uint32_t)k;
-  } else {
-    const float e = (float)k * (float)nsl / (float)lines;
-    need = (uint32_t)ceilf(1.25f * e + 4.0f * sqrtf(e) + 8.0f);
-  }
-  (void)taken;
+  const uint32_t need = sample_need(r.n, k);
   const int top = kHistBins - PER * threadIdx.x;
   uint32_t cnt[PER];
   uint32_t mine = 0;
@@ -138,7 +86,7 @@ __global__ __launch_bounds__(kFinalThreads) void topk_sample_kernel(
   uint32_t total = 0;
   uint32_t cum = block_excl_scan(mine, wsum, &total);
   if (threadIdx.x == 0 && total < need) state[b].beta = 0u;   // keep everything
-  if (cum < need && cum + mine >= need) {
+  if (total >= need && cum < need && cum + mine >= need) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const uint32_t nxt = cum + cnt[j];
@@ -148,56 +96,54 @@ __global__ __launch_bounds__(kFinalThreads) void topk_sample_kernel(
   }
 }
 
+// one wave per segment; lane l holds the KPL consecutive keys l*KPL.. of it
+template <int KPL>
 __global__ __launch_bounds__(kSelThreads) void topk_collect_kernel(
     const double* __restrict__ keys, const int32_t* __restrict__ ctx_len,
-    const TopkState* __restrict__ state, uint32_t* __restrict__ segcnt,
-    uint64_t* __restrict__ lkey, uint32_t* __restrict__ lpos, int n_seg, int mode, int max_ctx,
-    int S, int k, int L) {
-  __shared__ uint32_t wsum[16];
+    const TopkState* __restrict__ state, uint32_t* __restrict__ segcnt, Cand* __restrict__ cand,
+    int n_seg, int mode, int max_ctx, int S, int k, int L) {
+  constexpr int SEG = 64 * KPL;
   const int b = blockIdx.y;
-  const Range r = cand_range(mode, ctx_of(ctx_len, b, max_ctx), S, k, L, max_ctx);
+  const Range r = cand_range(mode, ctx_of(ctx_len, b, max_ctx), S, k, L);
   if (r.dense) return;
-  const int c = blockIdx.x;
-  const int i0 = c * kHistChunk;
-  if (i0 >= r.n) return;
+  const int lane = threadIdx.x & 63;
+  const int seg = blockIdx.x * (kSelThreads / 64) + (threadIdx.x >> 6);
+  const int i0 = seg * SEG;
+  if (i0 >= r.n) return;   // wave-uniform
   const uint32_t beta = state[b].beta;
-  const double* kb = keys + (size_t)b * r.stride + r.lo;
-  const size_t seg = ((size_t)b * n_seg + c) * kSegCap;
-  double x[kKeysPerThread];
+  const double* kb = keys + (size_t)b * (mode == SKV_INDEX_SKETCH_INT4 ? max_ctx : max_ctx / 4) + r.lo;
+  double x[KPL];
 #pragma unroll
-  for (int u = 0; u < kKeysPerThread; ++u) {
-    const int i = i0 + u * kSelThreads + threadIdx.x;
-    x[u] = canon(kb[min(i, r.n - 1)]);   // unconditional load
-  }
-  uint32_t mine = 0;
-  uint32_t selm = 0;
+  for (int u = 0; u < KPL; ++u) x[u] = kb[min(i0 + lane * KPL + u, r.n - 1)] + 0.0;   // unconditional
+  uint32_t selm = 0, mine = 0;
 #pragma unroll
-  for (int u = 0; u < kKeysPerThread; ++u) {
-    const int i = i0 + u * kSelThreads + threadIdx.x;
+  for (int u = 0; u < KPL; ++u) {
+    const int i = i0 + lane * KPL + u;
     if (i < r.n && key_digit(x[u]) >= beta) {
       selm |= 1u << u;
       ++mine;
     }
   }
-  uint32_t total = 0;
-  uint32_t at = block_excl_scan(mine, wsum, &total);
+  const uint32_t incl = wave_incl_scan(mine);
+  uint32_t at = incl - mine;
+  u32x4* out = reinterpret_cast<u32x4*>(cand + ((size_t)b * n_seg + seg) * SEG);
 #pragma unroll
-  for (int u = 0; u < kKeysPerThread; ++u) {
+  for (int u = 0; u < KPL; ++u) {
     if (selm & (1u << u)) {
-      if (at < (uint32_t)kSegCap) {
-        lkey[seg + at] = ordered_u64(x[u]);
-        lpos[seg + at] = (uint32_t)(r.lo + i0 + u * kSelThreads + threadIdx.x);
-      }
+      const uint64_t ok = ordered_u64(x[u]);
+      if (at < (uint32_t)SEG)   // always true: at most one record per key
+        out[at] = (u32x4){(uint32_t)ok, (uint32_t)(ok >> 32), (uint32_t)(r.lo + i0 + lane * KPL + u), 0u};
       ++at;
     }
   }
-  if (threadIdx.x == 0) segcnt[(size_t)b * n_seg + c] = total;
+  if (lane == 63) segcnt[(size_t)b * n_seg + seg] = min(incl, (uint32_t)SEG);
 }
 
-// ---- exact radix select over unique 96-bit composites ----------------------
+// ---------------------------------------------------------------------------
+// exact radix select over unique 96-bit composites
+// ---------------------------------------------------------------------------
 // composite = (hi: order-preserving key, lo: ~position); larger composite =
 // larger key, or equal key and lower position.
-
 __device__ __forceinline__ uint32_t comp_digit(uint64_t hi, uint32_t lo, int dg) {
   return dg >= 4 ? (uint32_t)(hi >> (8 * (dg - 4))) & 0xFFu : (lo >> (8 * dg)) & 0xFFu;
 }
@@ -205,20 +151,19 @@ __device__ __forceinline__ uint32_t comp_digit(uint64_t hi, uint32_t lo, int dg)
 struct SelectShared {
   uint32_t hist[256];
   uint32_t wsum[16];
-  uint32_t and3[3], or3[3];
+  uint32_t wred[16][6];
   uint64_t pre_hi, mask_hi;
   uint32_t pre_lo, mask_lo;
   int need;
   int done;
-  int count;
-  int fast;
-  int total;
+  int dg0;
 };
 
 // MSB-first radix select of the k largest composites among n (0 < k <= n).
 // On return every element with (hi & mask_hi, lo & mask_lo) lexicographically
 // >= (pre_hi, pre_lo) is kept, and exactly k elements satisfy that.  The loop
-// stops once the remaining bucket is kept whole.  get(i, hi, lo) reads element i.
+// stops once the boundary bucket is kept whole.  get(i, hi, lo) reads element
+// i.  Every thread of the block must call it.
 template <class Get>
 __device__ void radix_select(Get get, int n, int k, SelectShared& sh) {
   // bytes on which all n composites agree are fixed without a histogram pass
@@ -231,57 +176,50 @@ __device__ void radix_select(Get get, int n, int k, SelectShared& sh) {
     a1 &= (uint32_t)hi;         o1 |= (uint32_t)hi;
     a2 &= lo;                   o2 |= lo;
   }
-  if (threadIdx.x == 0) {
-    sh.and3[0] = sh.and3[1] = sh.and3[2] = ~0u;
-    sh.or3[0] = sh.or3[1] = sh.or3[2] = 0u;
-    sh.pre_hi = 0;
-    sh.mask_hi = 0;
-    sh.pre_lo = 0;
-    sh.mask_lo = 0;
-    sh.need = k;
-    sh.done = (k == n);
-  }
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    a0 &= __shfl_xor(a0, off); a1 &= __shfl_xor(a1, off); a2 &= __shfl_xor(a2, off);
-    o0 |= __shfl_xor(o0, off); o1 |= __shfl_xor(o1, off); o2 |= __shfl_xor(o2, off);
+  a0 = wave_and(a0); a1 = wave_and(a1); a2 = wave_and(a2);
+  o0 = wave_or(o0);  o1 = wave_or(o1);  o2 = wave_or(o2);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  if (lane == 0) {
+    sh.wred[wave][0] = a0; sh.wred[wave][1] = a1; sh.wred[wave][2] = a2;
+    sh.wred[wave][3] = o0; sh.wred[wave][4] = o1; sh.wred[wave][5] = o2;
   }
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) {
-    atomicAnd(&sh.and3[0], a0); atomicAnd(&sh.and3[1], a1); atomicAnd(&sh.and3[2], a2);
-    atomicOr(&sh.or3[0], o0);   atomicOr(&sh.or3[1], o1);   atomicOr(&sh.or3[2], o2);
-  }
-  __syncthreads();
-  int dg0 = 11;
-  {
-    const uint64_t ahi = ((uint64_t)sh.and3[0] << 32) | sh.and3[1];
-    const uint64_t ohi = ((uint64_t)sh.or3[0] << 32) | sh.or3[1];
-    const uint32_t alo = sh.and3[2], olo = sh.or3[2];
-    uint64_t ph = 0, mh = 0;
-    uint32_t pl = 0, ml = 0;
-    while (dg0 >= 0 && n > 0) {
-      const uint32_t da = comp_digit(ahi, alo, dg0), dor = comp_digit(ohi, olo, dg0);
-      if (da != dor) break;
-      if (dg0 >= 4) {
-        ph |= (uint64_t)da << (8 * (dg0 - 4));
-        mh |= 0xFFull << (8 * (dg0 - 4));
-      } else {
-        pl |= da << (8 * dg0);
-        ml |= 0xFFu << (8 * dg0);
+  if (wave == 0) {
+    // lane w < nw holds wave w's values; a 16-lane DPP reduction combines them
+    const int w = lane < nw ? lane : 0;
+    a0 = sh.wred[w][0]; a1 = sh.wred[w][1]; a2 = sh.wred[w][2];
+    o0 = sh.wred[w][3]; o1 = sh.wred[w][4]; o2 = sh.wred[w][5];
+    a0 = wave_and(a0); a1 = wave_and(a1); a2 = wave_and(a2);
+    o0 = wave_or(o0);  o1 = wave_or(o1);  o2 = wave_or(o2);
+    if (lane == 0) {
+      const uint64_t ahi = ((uint64_t)a0 << 32) | a1, ohi = ((uint64_t)o0 << 32) | o1;
+      uint64_t ph = 0, mh = 0;
+      uint32_t pl = 0, ml = 0;
+      int dg = 11;
+      while (dg >= 0) {
+        const uint32_t da = comp_digit(ahi, a2, dg), dor = comp_digit(ohi, o2, dg);
+        if (da != dor) break;
+        if (dg >= 4) {
+          ph |= (uint64_t)da << (8 * (dg - 4));
+          mh |= 0xFFull << (8 * (dg - 4));
+        } else {
+          pl |= da << (8 * dg);
+          ml |= 0xFFu << (8 * dg);
+        }
+        --dg;
       }
-      --dg0;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
       sh.pre_hi = ph;
       sh.mask_hi = mh;
       sh.pre_lo = pl;
       sh.mask_lo = ml;
+      sh.need = k;
+      sh.done = (k == n) || dg < 0;
+      sh.dg0 = dg;
     }
-    __syncthreads();
   }
-  for (int dg = dg0; dg >= 0 && !sh.done; --dg) {
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) sh.hist[i] = 0u;
+  __syncthreads();
+  for (int dg = sh.dg0; dg >= 0 && !sh.done; --dg) {
+    if (threadIdx.x < 256) sh.hist[threadIdx.x] = 0u;
     __syncthreads();
     const uint64_t ph = sh.pre_hi, mh = sh.mask_hi;
     const uint32_t pl = sh.pre_lo, ml = sh.mask_lo;
@@ -294,7 +232,6 @@ __device__ void radix_select(Get get, int n, int k, SelectShared& sh) {
     __syncthreads();
     if (threadIdx.x < 64) {
       // lane l owns digits [252-4l, 255-4l], summed from the top
-      const int lane = threadIdx.x;
       uint32_t c4[4];
       uint32_t s = 0;
 #pragma unroll
@@ -302,12 +239,7 @@ __device__ void radix_select(Get get, int n, int k, SelectShared& sh) {
         c4[j] = sh.hist[255 - 4 * lane - j];
         s += c4[j];
       }
-      uint32_t incl = s;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t v = __shfl_up(incl, off);
-        if (lane >= off) incl += v;
-      }
+      const uint32_t incl = wave_incl_scan(s);
       const uint32_t excl = incl - s;
       const uint32_t need = (uint32_t)sh.need;
       if (excl < need && incl >= need) {
@@ -351,19 +283,61 @@ __device__ __forceinline__ void emit_position(int32_t* out, int mode, int S, int
   }
 }
 
-__global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
-    const double* __restrict__ keys, const int32_t* __restrict__ ctx_len,
-    const uint32_t* __restrict__ segcnt, const uint64_t* __restrict__ lkey,
-    const uint32_t* __restrict__ lpos, int32_t* __restrict__ idx, int32_t* __restrict__ n_sel,
-    uint32_t* __restrict__ flags, int n_seg, int mode, int max_ctx, int S, int k, int L, int cap) {
+// Writes the kept elements of [0, n) in index order (indices are in position
+// order), one block-wide prefix sum per round of blockDim.x elements.
+template <class Get>
+__device__ void ordered_emit(Get get, int n, int k, SelectShared& sh, int32_t* out, int mode,
+                             int S) {
+  uint32_t before = 0;
+  for (int base = 0; base < n; base += blockDim.x) {
+    const int i = base + threadIdx.x;
+    uint64_t hi = 0;
+    uint32_t lo = 0;
+    int pos = 0;
+    bool sel = false;
+    if (i < n) {
+      get(i, hi, lo, pos);
+      sel = kept(hi, lo, sh);
+    }
+    uint32_t tot = 0;
+    const uint32_t off = block_excl_scan(sel ? 1u : 0u, sh.wsum, &tot);
+    if (sel && before + off < (uint32_t)k) emit_position(out, mode, S, (int)(before + off), pos);
+    before += tot;
+  }
+}
+
+// segment of flattened candidate j: the last c with s_off[c] <= j (s_off is
+// non-decreasing and s_off[nparts] = total > j)
+__device__ __forceinline__ int seg_of(const uint32_t* s_off, int nparts, uint32_t j) {
+  int lo = 0, hi = nparts - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_off[mid] <= j) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+struct NoSrc {
+  static constexpr int LANES = 64;
+};
+
+// RECOMPUTE (the fused path): keys are recomputed from the index when the
+// candidates are too few.
+template <class Src, bool RECOMPUTE>
+__global__ __launch_bounds__(kFT) void topk_final_kernel(
+    const double* __restrict__ keys_in, const void* __restrict__ iq, const void* __restrict__ ik,
+    const uint16_t* __restrict__ isc, const int32_t* __restrict__ ctx_len,
+    const uint32_t* __restrict__ segcnt, Cand* __restrict__ cand, int32_t* __restrict__ idx,
+    int32_t* __restrict__ n_sel,
+    uint32_t* __restrict__ flags, int n_seg, int seg_items, int mode, int max_ctx, int S, int k,
+    int L, int cap) {
   __shared__ uint64_t s_key[kListCap];
   __shared__ uint32_t s_pos[kListCap];
-  __shared__ uint32_t s_bm[kBitmapWords];
   __shared__ uint32_t s_off[kMaxSeg + 1];
   __shared__ SelectShared sh;
   const int b = blockIdx.x;
   const int T = ctx_of(ctx_len, b, max_ctx);
-  const Range r = cand_range(mode, T, S, k, L, max_ctx);
+  const Range r = cand_range(mode, T, S, k, L);
   int32_t* out = idx + (size_t)b * cap;
   if (r.dense) {
     for (int i = threadIdx.x; i < T; i += blockDim.x) out[i] = i;
@@ -380,119 +354,155 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
     for (int i = threadIdx.x; i < T - 4 * nb; i += blockDim.x) out[4 * k + i] = 4 * nb + i;
     if (threadIdx.x == 0) n_sel[b] = 4 * k + (T - 4 * nb);
   }
-  // gather the segment counts; the candidates are usable when no segment
-  // overflowed and there are between k and kListCap of them
-  const int n_parts = (r.n + kHistChunk - 1) / kHistChunk;
-  const int words = (r.n + 31) / 32;
+  // segment offsets (n_parts <= kMaxSeg = kSegPT * blockDim.x)
+  const int n_parts = (r.n + seg_items - 1) / seg_items;
+  const uint32_t* sc = segcnt + (size_t)b * n_seg;
+  const Cand* cb = cand + (size_t)b * n_seg * seg_items;
+  uint32_t total;
   {
-    const int per = (n_parts + blockDim.x - 1) / blockDim.x;   // 1 unless n_parts > 1024
-    uint32_t mine = 0;
-    int over = 0;
-    for (int j = 0; j < per; ++j) {
-      const int c = threadIdx.x * per + j;
-      if (c < n_parts) {
-        const uint32_t v = segcnt[(size_t)b * n_seg + c];
-        over |= v > (uint32_t)kSegCap;
-        mine += v;
-      }
+    uint32_t cs[kSegPT], mine = 0;
+#pragma unroll
+    for (int j = 0; j < kSegPT; ++j) {
+      const int c = kSegPT * threadIdx.x + j;
+      const uint32_t v = sc[min(c, n_parts - 1)];   // unconditional
+      cs[j] = c < n_parts ? min(v, (uint32_t)seg_items) : 0u;
+      mine += cs[j];
     }
-    if (threadIdx.x == 0) sh.fast = 1;
-    uint32_t total = 0;
     uint32_t off = block_excl_scan(mine, sh.wsum, &total);
-    if (over) sh.fast = 0;
-    for (int j = 0; j < per; ++j) {
-      const int c = threadIdx.x * per + j;
-      if (c < n_parts && c <= kMaxSeg) {
-        s_off[c] = off;
-        off += min(segcnt[(size_t)b * n_seg + c], (uint32_t)kSegCap);
-      }
+#pragma unroll
+    for (int j = 0; j < kSegPT; ++j) {
+      const int c = kSegPT * threadIdx.x + j;
+      if (c < n_parts) s_off[c] = off;
+      off += cs[j];
     }
-    if (threadIdx.x == 0) {
-      s_off[min(n_parts, kMaxSeg)] = total;
-      sh.total = (int)total;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0 && (total < (uint32_t)k || total > (uint32_t)kListCap || words > kBitmapWords ||
-                             n_parts > kMaxSeg))
-      sh.fast = 0;
+    if (threadIdx.x == 0) s_off[n_parts] = total;
     __syncthreads();
   }
-  if (sh.fast) {
-    const int n = sh.total;
-    // 8 threads per segment, each moving up to kSegCap/8 entries with
-    // unconditional loads (clamped into the segment) so they overlap
-    constexpr int TPS = 8, PER = kSegCap / TPS;
-    for (int c = threadIdx.x / TPS; c < n_parts; c += blockDim.x / TPS) {
-      const int cnt = (int)(s_off[c + 1] - s_off[c]);   // s_off[n_parts] holds the total
-      const size_t base = ((size_t)b * n_seg + c) * kSegCap;
-      uint64_t kk[PER];
-      uint32_t pp[PER];
+
+  if (total >= (uint32_t)k && total <= (uint32_t)kListCap) {
+    // ---- fast path: every candidate in LDS, in position order ----
+    const int n = (int)total;
+    {
+      // thread t moves the contiguous run [kGPT*t, kGPT*(t+1)): one search for
+      // its first segment, then a walk; all its loads are issued together
+      const int j0 = kGPT * (int)threadIdx.x;
+      u32x4 rec[kGPT];
+      int c = seg_of(s_off, n_parts, (uint32_t)min(j0, n - 1));
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int e = (threadIdx.x % TPS) + TPS * j;
-        const int ec = e < cnt ? e : 0;
-        kk[j] = lkey[base + ec];
-        pp[j] = lpos[base + ec];
+      for (int m = 0; m < kGPT; ++m) {
+        const int j = min(j0 + m, n - 1);
+        while (c + 1 < n_parts && (int)s_off[c + 1] <= j) ++c;
+        const int e = min(max(j - (int)s_off[c], 0), seg_items - 1);   // in range by construction
+        rec[m] = reinterpret_cast<const u32x4*>(cb + (size_t)c * seg_items)[e];
       }
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int e = (threadIdx.x % TPS) + TPS * j;
-        if (e < cnt) {
-          s_key[s_off[c] + e] = kk[j];
-          s_pos[s_off[c] + e] = pp[j];
+      for (int m = 0; m < kGPT; ++m) {
+        const int j = j0 + m;
+        if (j < n) {
+          s_key[j] = ((uint64_t)rec[m].y << 32) | rec[m].x;
+          s_pos[j] = rec[m].z;
         }
       }
     }
-    for (int w = threadIdx.x; w < words; w += blockDim.x) s_bm[w] = 0u;
     __syncthreads();
     radix_select([&](int i, uint64_t& hi, uint32_t& lo) { hi = s_key[i]; lo = ~s_pos[i]; }, n, k, sh);
-    for (int i = threadIdx.x; i < n; i += blockDim.x)
-      if (kept(s_key[i], ~s_pos[i], sh)) {
-        const int ci = (int)s_pos[i] - r.lo;
-        atomicOr(&s_bm[ci >> 5], 1u << (ci & 31));
+    // ordered emission: thread t owns the contiguous run [t*per, (t+1)*per)
+    const int per = (n + kFT - 1) / kFT;   // <= kGPT <= 32
+    const int e0 = threadIdx.x * per, e1 = min(n, e0 + per);
+    uint32_t keep = 0, cnt = 0;
+    for (int e = e0; e < e1; ++e)
+      if (kept(s_key[e], ~s_pos[e], sh)) {
+        keep |= 1u << (e - e0);
+        ++cnt;
       }
-    __syncthreads();
-    // read the bitmap back in order: thread t owns a contiguous run of words
-    const int per = (words + blockDim.x - 1) / blockDim.x;
-    const int w0 = threadIdx.x * per;
-    const int w1 = min(words, w0 + per);
-    uint32_t cnt = 0;
-    for (int w = w0; w < w1; ++w) cnt += (uint32_t)__popc(s_bm[w]);
     int rank = (int)block_excl_scan(cnt, sh.wsum, nullptr);
-    for (int w = w0; w < w1; ++w) {
-      uint32_t bits = s_bm[w];
-      while (bits) {
-        const int bit = __ffs(bits) - 1;
-        bits &= bits - 1;
-        if (rank < k) emit_position(out, mode, S, rank, r.lo + 32 * w + bit);
+    for (int e = e0; e < e1; ++e)
+      if (keep & (1u << (e - e0))) {
+        if (rank < k) emit_position(out, mode, S, rank, (int)s_pos[e]);
         ++rank;
       }
-    }
     return;
   }
-  // exact path over every candidate key in global memory
+
   if (threadIdx.x == 0) raise_flag(flags, SKV_FLAG_TOPK_SLOW);
-  const double* kb = keys + (size_t)b * r.stride + r.lo;
-  const int lo0 = r.lo;
-  radix_select(
-      [&](int i, uint64_t& hi, uint32_t& lo) {
-        hi = ordered_u64(canon(kb[i]));
-        lo = ~(uint32_t)(lo0 + i);
-      },
-      r.n, k, sh);
-  // ordered compaction: positions come out ascending
-  if (threadIdx.x == 0) sh.count = 0;
-  __syncthreads();
-  for (int base = 0; base < r.n; base += blockDim.x) {
-    const int i = base + threadIdx.x;
-    const bool sel = i < r.n && kept(ordered_u64(canon(kb[i])), ~(uint32_t)(lo0 + i), sh);
-    const int before = sh.count;
-    const int off = (int)block_excl_scan(sel ? 1u : 0u, sh.wsum, nullptr);
-    if (sel && before + off < k) emit_position(out, mode, S, before + off, lo0 + i);
-    __syncthreads();
-    if (threadIdx.x == blockDim.x - 1) sh.count = before + off + (sel ? 1 : 0);
-    __syncthreads();
+  if (total >= (uint32_t)k) {
+    // ---- more candidates than LDS holds: the same select over the records ----
+    const int n = (int)total;
+    auto rec_of = [&](int j) -> u32x4 {
+      const int c = seg_of(s_off, n_parts, (uint32_t)j);
+      const int e = min(max(j - (int)s_off[c], 0), seg_items - 1);   // in range by construction
+      return reinterpret_cast<const u32x4*>(cb + (size_t)c * seg_items)[e];
+    };
+    radix_select([&](int i, uint64_t& hi, uint32_t& lo) {
+      const u32x4 v = rec_of(i);
+      hi = ((uint64_t)v.y << 32) | v.x;
+      lo = ~v.z;
+    }, n, k, sh);
+    ordered_emit([&](int i, uint64_t& hi, uint32_t& lo, int& pos) {
+      const u32x4 v = rec_of(i);
+      hi = ((uint64_t)v.y << 32) | v.x;
+      lo = ~v.z;
+      pos = (int)v.z;
+    }, n, k, sh, out, mode, S);
+    return;
   }
+
+  // ---- fewer candidates than the budget: the select over every key ----
+  const double* kb;
+  if constexpr (RECOMPUTE) {
+    // the sequence's record area holds 2 * n_seg * seg_items doubles >= r.n
+    double* kw = reinterpret_cast<double*>(cand + (size_t)b * n_seg * seg_items);
+    constexpr int N = Src::LANES, IPW = 64 / N, PER_IT = 8 * IPW;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int sub = lane % N, tw = lane / N;
+    Src src;
+    src.init(reinterpret_cast<const uint8_t*>(iq) + (size_t)b * Src::QROW, ik, isc, b, max_ctx, sub);
+    for (int base = wave * PER_IT; base < r.n; base += (kFT / 64) * PER_IT) {
+      u32x4 w[8];
+      uint32_t ax[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = min(base + u * IPW + tw, r.n - 1);
+        w[u] = src.load(r.lo + i);
+        ax[u] = src.load_aux(r.lo + i);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = base + u * IPW + tw;
+        const double key = src.key(w[u], ax[u]);
+        if (sub == 0 && i < r.n) kw[i] = key;
+      }
+    }
+    __threadfence_block();
+    __syncthreads();
+    kb = kw;
+  } else {
+    kb = keys_in + (size_t)b * (mode == SKV_INDEX_SKETCH_INT4 ? max_ctx : max_ctx / 4) + r.lo;
+  }
+  const int lo0 = r.lo;
+  radix_select([&](int i, uint64_t& hi, uint32_t& lo) {
+    hi = ordered_u64(kb[i] + 0.0);
+    lo = ~(uint32_t)(lo0 + i);
+  }, r.n, k, sh);
+  ordered_emit([&](int i, uint64_t& hi, uint32_t& lo, int& pos) {
+    hi = ordered_u64(kb[i] + 0.0);
+    lo = ~(uint32_t)(lo0 + i);
+    pos = lo0 + i;
+  }, r.n, k, sh, out, mode, S);
+}
+
+template <class Src, bool RECOMPUTE>
+hipError_t launch_final(const skv_layer_desc& d, const int32_t* ctx_len, const double* keys,
+                        const void* iq, const void* ik, const uint16_t* isc, int32_t* idx,
+                        int32_t* n_sel, void* ws, const WsLayout& Lw, hipStream_t st) {
+  const int mode = d.index_mode;
+  const int S = mode == SKV_INDEX_SKETCH_INT4 ? d.n_sink : 0;
+  const int L = mode == SKV_INDEX_SKETCH_INT4 ? d.n_tail : 0;
+  hipLaunchKernelGGL((topk_final_kernel<Src, RECOMPUTE>), dim3(d.batch), dim3(kFT), 0, st,
+                     keys, iq, ik, isc, ctx_len, ws_ptr<uint32_t>(ws, Lw.segcnt),
+                     ws_ptr<Cand>(ws, Lw.cand), idx, n_sel, ws_ptr<uint32_t>(ws, Lw.flags),
+                     Lw.n_seg, Lw.seg_items, mode, d.max_ctx, S, d.topk, L, select_capacity(d));
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -500,22 +510,50 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
 hipError_t launch_topk(const skv_layer_desc& d, const int32_t* ctx_len, const double* keys,
                        int32_t* idx, int32_t* n_sel, void* ws, const WsLayout& Lw,
                        hipStream_t st) {
-  uint32_t* flags = ws_ptr<uint32_t>(ws, Lw.flags);
-  TopkState* state = ws_ptr<TopkState>(ws, Lw.state);
-  uint32_t* segcnt = ws_ptr<uint32_t>(ws, Lw.segcnt);
-  uint64_t* lkey = ws_ptr<uint64_t>(ws, Lw.lkey);
-  uint32_t* lpos = ws_ptr<uint32_t>(ws, Lw.lpos);
   const int mode = d.index_mode;
   const int S = mode == SKV_INDEX_SKETCH_INT4 ? d.n_sink : 0;
   const int L = mode == SKV_INDEX_SKETCH_INT4 ? d.n_tail : 0;
+  TopkState* state = ws_ptr<TopkState>(ws, Lw.state);
   hipLaunchKernelGGL(topk_sample_kernel, dim3(d.batch), dim3(kFinalThreads), 0, st, keys, ctx_len,
                      state, mode, d.max_ctx, S, d.topk, L);
-  hipLaunchKernelGGL(topk_collect_kernel, dim3(Lw.n_seg, d.batch), dim3(kSelThreads), 0, st, keys,
-                     ctx_len, state, segcnt, lkey, lpos, Lw.n_seg, mode, d.max_ctx, S, d.topk, L);
-  hipLaunchKernelGGL(topk_final_kernel, dim3(d.batch), dim3(kFinalThreads), 0, st, keys, ctx_len,
-                     segcnt, lkey, lpos, idx, n_sel, flags, Lw.n_seg, mode, d.max_ctx, S, d.topk, L,
-                     select_capacity(d));
-  return hipGetLastError();
+  const dim3 grid((Lw.n_seg + 3) / 4, d.batch);
+  if (Lw.seg_items == kSegTok)
+    hipLaunchKernelGGL((topk_collect_kernel<kSegTok / 64>), grid, dim3(kSelThreads), 0, st, keys,
+                       ctx_len, state, ws_ptr<uint32_t>(ws, Lw.segcnt), ws_ptr<Cand>(ws, Lw.cand),
+                       Lw.n_seg, mode, d.max_ctx, S, d.topk, L);
+  else
+    hipLaunchKernelGGL((topk_collect_kernel<kSegBlk / 64>), grid, dim3(kSelThreads), 0, st, keys,
+                       ctx_len, state, ws_ptr<uint32_t>(ws, Lw.segcnt), ws_ptr<Cand>(ws, Lw.cand),
+                       Lw.n_seg, mode, d.max_ctx, S, d.topk, L);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_final<NoSrc, false>(d, ctx_len, keys, nullptr, nullptr, nullptr, idx, n_sel, ws, Lw, st);
+}
+
+hipError_t launch_score_select(const skv_layer_desc& d, const int32_t* ctx_len, const void* iq,
+                               int8_t* qs_out, float* qscale_out, const void* ik,
+                               const uint16_t* isc, int32_t* idx, int32_t* n_sel, void* ws,
+                               const WsLayout& Lw, hipStream_t st) {
+  hipError_t e = launch_sample_collect(d, ctx_len, iq, qs_out, qscale_out, ik, isc, ws, Lw, st);
+  if (e != hipSuccess) return e;
+  const void* qrows = qs_out ? (const void*)qs_out : iq;
+#define SKV_FIN(SRC) return launch_final<SRC, true>(d, ctx_len, nullptr, qrows, ik, isc, idx, n_sel, ws, Lw, st)
+  if (d.index_mode == SKV_INDEX_SKETCH_INT4) {
+    switch (d.n_kv_heads * d.rank / 2) {
+      case 32: SKV_FIN(SketchSrc<2>);
+      case 64: SKV_FIN(SketchSrc<4>);
+      case 128: SKV_FIN(SketchSrc<8>);
+      case 256: SKV_FIN(SketchSrc<16>);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (d.index_dim) {
+    case 64: SKV_FIN(PooledSrc<8>);
+    case 128: SKV_FIN(PooledSrc<16>);
+    case 256: SKV_FIN(PooledSrc<32>);
+    default: return hipErrorInvalidValue;
+  }
+#undef SKV_FIN
 }
 
 }  // namespace skv
