@@ -237,6 +237,17 @@ skv_status sparsekv_step(const skv_layer_desc* d, const int32_t* ctx_len, const 
  * other than SKV_FLAG_TOPK_SLOW was set.  Not capturable. */
 skv_status sparsekv_check(void* ws, size_t ws_bytes, void* stream, uint32_t* flags);
 
+/* ---- diagnostic kernel timer -------------------------------------------------
+ * For measurement only (not thread-safe, not capturable).  While enabled, every
+ * launch of the streaming score-and-collect kernel (the one that reads the whole
+ * index in sparsekv_score_topk / sparsekv_step) carries a start/stop event pair
+ * that its dispatch records (hipExtLaunchKernelGGL), so the pair spans the
+ * kernel's execution; up to 4096 launches are recorded.  Enabling again
+ * discards earlier records.  sparsekv_timer_read synchronizes on the recorded
+ * events and returns the summed kernel time (ms) and the number of launches. */
+skv_status sparsekv_timer_enable(int enable);
+skv_status sparsekv_timer_read(double* total_ms, int64_t* launches);
+
 /* ---- host-RAM tier (optional) ----------------------------------------------
  * Page "8 agents x 250K ...", section "The mechanism": K/V of every token sit
  * in pinned host RAM at int4 (64-dim groups, fp16 group scales, 272 B per

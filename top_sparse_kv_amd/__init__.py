@@ -143,6 +143,18 @@ def step(desc, ctx_len, q, basis, qs, qs_scale, index_query, index_keys, index_s
                                _p(ws), ws.numel(), _stream(stream)))
 
 
+def timer_enable(on: bool = True):
+    """Diagnostic: bracket each launch of the streaming score kernel with events."""
+    _check(lib().sparsekv_timer_enable(1 if on else 0))
+
+
+def timer_read():
+    """(total kernel milliseconds, launches) recorded since timer_enable."""
+    ms, n = ctypes.c_double(), _lib.c_i64()
+    _check(lib().sparsekv_timer_read(ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
+
+
 def check(ws, stream=None) -> int:
     """Synchronizes, returns and clears the device flag bits; raises on error flags."""
     f = _lib.c_u32()

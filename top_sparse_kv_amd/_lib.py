@@ -70,6 +70,8 @@ SIGNATURES = [
     ("sparsekv_step", c_i32, [P(LayerDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                               P(KVView), c_vp, c_vp, ctypes.c_float, c_vp, c_vp, c_sz, c_vp]),
     ("sparsekv_check", c_i32, [c_vp, c_sz, c_vp, P(c_u32)]),
+    ("sparsekv_timer_enable", c_i32, [c_i32]),
+    ("sparsekv_timer_read", c_i32, [P(ctypes.c_double), P(c_i64)]),
     ("sparsekv_tier_create", c_i32, [P(TierDesc), P(c_vp)]),
     ("sparsekv_tier_host_records", c_vp, [c_vp]),
     ("sparsekv_tier_resident", c_i32, [c_vp, P(KVView)]),

@@ -7,7 +7,33 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <vector>
+
 namespace skv {
+
+// ---- diagnostic kernel timer (not thread-safe, not for graph capture) ----
+namespace {
+struct KernelTimer {
+  bool on = false;
+  std::vector<hipEvent_t> ev;   // begin/end pairs
+  size_t used = 0;              // events recorded since enable
+  int64_t dropped = 0;
+};
+KernelTimer g_timer;
+constexpr size_t kTimerPairs = 4096;
+}  // namespace
+
+bool timer_next(hipEvent_t* start, hipEvent_t* stop) {
+  if (!g_timer.on) return false;
+  if (g_timer.used + 2 > g_timer.ev.size()) {
+    ++g_timer.dropped;
+    return false;
+  }
+  *start = g_timer.ev[g_timer.used];
+  *stop = g_timer.ev[g_timer.used + 1];
+  g_timer.used += 2;
+  return true;
+}
 
 static thread_local char g_err[512] = "";
 
@@ -239,6 +265,36 @@ skv_status sparsekv_step(const skv_layer_desc* d, const int32_t* ctx_len, const 
                             tok ? qs_scale : nullptr, index_keys, index_scale, idx, n_sel, ws, L, st);
   if (e == hipSuccess) e = launch_attend(*d, q, *kv, idx, n_sel, sm_scale, out, ws, L, st);
   return launched(e, "step");
+}
+
+skv_status sparsekv_timer_enable(int enable) {
+  if (enable && g_timer.ev.empty()) {
+    g_timer.ev.resize(2 * kTimerPairs);
+    for (auto& e : g_timer.ev)
+      if (hipEventCreate(&e) != hipSuccess) {
+        g_timer.ev.clear();
+        return set_error(SKV_ERR_HIP, "timer: event creation failed");
+      }
+  }
+  g_timer.on = enable != 0;
+  g_timer.used = 0;
+  g_timer.dropped = 0;
+  return ok();
+}
+
+skv_status sparsekv_timer_read(double* total_ms, int64_t* launches) {
+  if (!total_ms || !launches) return set_error(SKV_ERR_INVALID, "timer: NULL pointer");
+  double t = 0.0;
+  for (size_t i = 0; i + 1 < g_timer.used; i += 2) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(g_timer.ev[i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&ms, g_timer.ev[i], g_timer.ev[i + 1]) != hipSuccess)
+      return set_error(SKV_ERR_HIP, "timer: %s", hipGetErrorString(hipGetLastError()));
+    t += ms;
+  }
+  *total_ms = t;
+  *launches = (int64_t)(g_timer.used / 2);
+  return ok();
 }
 
 skv_status sparsekv_check(void* ws, size_t ws_bytes, void* stream, uint32_t* flags) {

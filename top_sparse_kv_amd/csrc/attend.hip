@@ -8,11 +8,14 @@
 // (token * n_kv_heads + kv_head) * head_dim, so K/V may live anywhere the
 // GPU can address.
 //
-// Work split: one workgroup per (sequence, KV head, chunk of 256 selected
-// rows); each of its 4 waves runs an online softmax over 64 rows, 32 at a
-// time, for the G query heads of that KV head; the waves merge in LDS and the
-// workgroup writes one (max, sum, unnormalised output) partial; a second
-// kernel merges the chunks of each query head in fixed order.
+// Work split: one workgroup per (sequence, KV head, chunk of 512 selected
+// rows), so that a 250K-token batch of 8 needs fewer workgroups than the GPU
+// has compute units; each of its 16 waves runs an online softmax over 32 rows
+// for the G query heads of that KV head.  The waves merge in two LDS stages
+// (wave w+8 into wave w, then the 8 survivors), which bounds the LDS at
+// 8*G*(D+4) floats, and the workgroup writes one (max, sum, unnormalised
+// output) partial; a second kernel merges the chunks of each query head in
+// fixed order.
 //
 // Inner step on the matrix cores (v_mfma_f32_16x16x32 f16 / bf16):
 //   logits^T[32 tok x 16 heads] = K[32 x D] . Q^T[D x 16]   (2 M-tiles of 16)
@@ -99,14 +102,24 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
   const int G = Hq / Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, g = lane >> 4;
+  const int r0 = c * kAttRowsPerWG;
+  const int rb = r0 + wave * kAttRowsPerWave;   // this wave's 32 selected rows
+  const int32_t* ib = idx + (size_t)b * cap;
+  // the row indices this lane uses are loaded together with n_sel (clamped into
+  // the array, masked by n below), saving a dependent round trip:
+  //   QK A operand: M-tile mt row i16 -> selected row rb + 16*mt + i16;
+  //   P / V: e = 0..3 -> row rb + 4g + e, e = 4..7 -> row rb + 16 + 4g + e-4
+  int tk[2], tv[8];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) tk[mt] = ib[min(rb + 16 * mt + i16, cap - 1)];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) tv[e] = ib[min(rb + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4)), cap - 1)];
   int n = n_sel[b];
   if (n < 0 || n > cap) {
     if (threadIdx.x == 0 && c == 0 && h == 0) raise_flag(flags, SKV_FLAG_INDEX_RANGE);
     n = n < 0 ? 0 : cap;
   }
-  const int r0 = c * kAttRowsPerWG;
   if (r0 >= n) return;
-  const int32_t* ib = idx + (size_t)b * cap;
   const size_t row_stride = (size_t)Hkv * D * ES;   // bytes between consecutive rows
 
   // Q as the B operand of the QK product: lane (head j = i16, group g), step s
@@ -134,31 +147,23 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
   const uint16_t* ksb = ksc ? ksc + (size_t)b * rows * Hkv + h : nullptr;
   const uint16_t* vsb = vsc ? vsc + (size_t)b * rows * Hkv + h : nullptr;
 
-  for (int it = 0; it < kAttRowsPerWave / 32; ++it) {
-    const int rb = r0 + wave * kAttRowsPerWave + it * 32;
-    if (rb >= n) break;
-    // ---- token rows used by this lane ----
-    // QK A operand: M-tile mt row i16 -> selected row rb + 16*mt + i16
-    // (out-of-range rows load row 0 and are masked below through vok)
+  static_assert(kAttRowsPerWave == 32, "one 32-row tile per wave");
+  if (rb < n) {
+    // out-of-range rows load row 0 and are masked through vok
     int ka[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const int ri = rb + 16 * mt + i16;
-      int tok = ib[min(ri, n - 1)];     // unconditional load (n >= 1 here)
-      if (ri < n && (tok < 0 || (int64_t)tok >= rows)) {
-        raise_flag(flags, SKV_FLAG_INDEX_RANGE);
-        tok = 0;
-      }
+      const int tok = tk[mt];
+      if (ri < n && (tok < 0 || (int64_t)tok >= rows)) raise_flag(flags, SKV_FLAG_INDEX_RANGE);
       ka[mt] = (ri < n && tok >= 0 && (int64_t)tok < rows) ? tok : 0;
     }
-    // the 8 tokens whose probabilities / V rows this lane handles:
-    // e' = 0..3 -> row rb + 4g + e', e' = 4..7 -> row rb + 16 + 4g + e'-4
     int vt[8];
     bool vok[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int ri = rb + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
-      int tok = ib[min(ri, n - 1)];     // unconditional load
+      const int tok = tv[e];
       const bool ok = ri < n && tok >= 0 && (int64_t)tok < rows;
       vt[e] = ok ? tok : 0;
       vok[e] = ok;
@@ -302,18 +307,61 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
     }
   }
 
-  // ---- merge the 4 waves of the workgroup in LDS ----
+  // ---- merge the 16 waves of the workgroup in LDS, in two stages ----
+  constexpr int DP = D + 4;
+  constexpr int HALF = kAttWaves / 2;
   if (g == 0) {
     s_m[wave][i16] = m_run;
     s_l[wave][i16] = l_run;
   }
-  constexpr int DP = D + 4;
+  if (wave >= HALF) {
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int j = 4 * g + e;
-    if (j < G) {
+    for (int e = 0; e < 4; ++e) {
+      const int j = 4 * g + e;
+      if (j < G) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) s_o[((size_t)wave * G + j) * DP + t * 16 + i16] = o[t][e];
+        for (int t = 0; t < NT; ++t) s_o[((size_t)(wave - HALF) * G + j) * DP + t * 16 + i16] = o[t][e];
+      }
+    }
+  }
+  __syncthreads();
+  if (wave < HALF) {
+    // wave w absorbs wave w + HALF: both rescaled to the larger running max
+    const float mp = s_m[wave + HALF][i16], lp = s_l[wave + HALF][i16];
+    const float M = fmaxf(m_run, mp);
+    const float aw = m_run == -INFINITY ? 0.0f : exp2f(m_run - M);
+    const float ap = mp == -INFINITY ? 0.0f : exp2f(mp - M);
+    float aw_row[4], ap_row[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      aw_row[e] = __shfl(aw, 4 * g + e);
+      ap_row[e] = __shfl(ap, 4 * g + e);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = 4 * g + e;
+      if (j < G) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          o[t][e] = o[t][e] * aw_row[e] + s_o[((size_t)wave * G + j) * DP + t * 16 + i16] * ap_row[e];
+      }
+    }
+    m_run = M;
+    l_run = l_run * aw + lp * ap;
+  }
+  __syncthreads();
+  if (wave < HALF) {
+    if (g == 0) {
+      s_m[wave][i16] = m_run;
+      s_l[wave][i16] = l_run;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = 4 * g + e;
+      if (j < G) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) s_o[((size_t)wave * G + j) * DP + t * 16 + i16] = o[t][e];
+      }
     }
   }
   __syncthreads();
@@ -323,10 +371,10 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
     const int d = (rem & 15) * (D / 16) + (rem >> 4);  // column i16*(D/16) + t
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kAttWaves; ++w) M = fmaxf(M, s_m[w][j]);
+    for (int w = 0; w < HALF; ++w) M = fmaxf(M, s_m[w][j]);
     float acc = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kAttWaves; ++w) {
+    for (int w = 0; w < HALF; ++w) {
       const float f = s_m[w][j] == -INFINITY ? 0.0f : exp2f(s_m[w][j] - M);
       acc += s_o[((size_t)w * G + j) * DP + rem] * f;
     }
@@ -334,7 +382,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
     if (d == 0) {
       float Ls = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kAttWaves; ++w)
+      for (int w = 0; w < HALF; ++w)
         Ls += s_m[w][j] == -INFINITY ? 0.0f : s_l[w][j] * exp2f(s_m[w][j] - M);
       part_ml[(pbase * 16 + j) * 2 + 0] = M;
       part_ml[(pbase * 16 + j) * 2 + 1] = Ls;
@@ -393,7 +441,7 @@ hipError_t launch_attend(const skv_layer_desc& d, const void* q, const skv_kv_vi
   const int cap = select_capacity(d);
   const int G = d.n_q_heads / d.n_kv_heads;
   const dim3 grid(d.n_kv_heads, Lw.n_att_chunks, d.batch);
-  const size_t lds = (size_t)kAttWaves * G * (d.head_dim + 4) * sizeof(float);
+  const size_t lds = (size_t)(kAttWaves / 2) * G * (d.head_dim + 4) * sizeof(float);
   const float sl = sm_scale * kLog2e;
 #define SKV_AT(KVT, DD)                                                                          \
   hipLaunchKernelGGL((attend_kernel<KVT, DD>), grid, dim3(kAttThreads), lds, st, q,              \

@@ -32,6 +32,8 @@
 // No workgroup waits for another and no atomics are used.
 #include "keys_common.h"
 
+#include <hip/hip_ext.h>
+
 namespace skv {
 namespace {
 
@@ -234,10 +236,17 @@ hipError_t launch_token_or_block(const skv_layer_desc& d, const int32_t* ctx_len
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const void* iq_score = qs_out ? (const void*)qs_out : iq;
-  hipLaunchKernelGGL((score_kernel<Src, true>), grid, dim3(kThreads), 0, st, iq_score, ik, isc,
-                     ctx_len, nullptr, state, ws_ptr<Cand>(ws, Lw->cand),
-                     ws_ptr<uint32_t>(ws, Lw->segcnt), flags, mode, d.max_ctx, S, d.topk, L,
-                     Lw->n_seg, Lw->seg_items);
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  if (timer_next(&ev0, &ev1))
+    hipExtLaunchKernelGGL((score_kernel<Src, true>), grid, dim3(kThreads), 0, st, ev0, ev1, 0,
+                          iq_score, ik, isc, ctx_len, (double*)nullptr, (const TopkState*)state,
+                          ws_ptr<Cand>(ws, Lw->cand), ws_ptr<uint32_t>(ws, Lw->segcnt), flags, mode,
+                          d.max_ctx, S, d.topk, L, Lw->n_seg, Lw->seg_items);
+  else
+    hipLaunchKernelGGL((score_kernel<Src, true>), grid, dim3(kThreads), 0, st, iq_score, ik, isc,
+                       ctx_len, nullptr, state, ws_ptr<Cand>(ws, Lw->cand),
+                       ws_ptr<uint32_t>(ws, Lw->segcnt), flags, mode, d.max_ctx, S, d.topk, L,
+                       Lw->n_seg, Lw->seg_items);
   return hipGetLastError();
 }
 

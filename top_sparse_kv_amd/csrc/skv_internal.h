@@ -22,7 +22,7 @@ constexpr int kMaxSeg = 4096;                 // candidate segments per sequence
 constexpr int kSegTok = 512;                  // candidates per segment, token mode
 constexpr int kSegBlk = 256;                  // candidates per segment, block mode
 constexpr int kAttRowsPerWave = 32;           // selected rows per attention wave
-constexpr int kAttWaves = 8;                  // waves per attention workgroup
+constexpr int kAttWaves = 16;                 // waves per attention workgroup
 constexpr int kAttRowsPerWG = kAttRowsPerWave * kAttWaves;
 
 // per-sequence select state written by the sample stage (u32 words)
@@ -133,6 +133,13 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t h) {
   return __uint_as_float(((uint32_t)h) << 16);
 }
+
+// ---------------------------------------------------------------------------
+// diagnostic kernel timer (sparsekv_timer_*): when enabled, the streaming
+// score kernel is launched with a start/stop event pair recorded by the
+// dispatch itself (hipExtLaunchKernelGGL); otherwise both are null
+// ---------------------------------------------------------------------------
+bool timer_next(hipEvent_t* start, hipEvent_t* stop);
 
 // ---------------------------------------------------------------------------
 // launchers (each returns hipSuccess or the launch error)
