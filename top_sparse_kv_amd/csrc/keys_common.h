@@ -82,10 +82,10 @@ __device__ __forceinline__ uint32_t sample_need(int n, int k) {
 }
 
 // ---------------------------------------------------------------------------
-// candidate records: (order-preserving key, position), 16 bytes
+// candidate records: (order-preserving key, position, 16-bit digit), 16 bytes
 // ---------------------------------------------------------------------------
 struct alignas(16) Cand {
-  uint32_t klo, khi, pos, pad;
+  uint32_t klo, khi, pos, digit;
 };
 __device__ __forceinline__ uint64_t cand_key(const Cand& c) { return ((uint64_t)c.khi << 32) | c.klo; }
 
@@ -356,16 +356,20 @@ __device__ __forceinline__ float quantize_sketch(const float* sp, int n, int8_t*
 // multiple of 8 and at most 16 * blockDim.x.  Returns the need-th largest
 // digit, which is the largest beta with at least `need` samples at or above
 // it -- or 0 (keep everything) when fewer than `need` samples exist, since
-// empty slots count as digit 0.  MSB-first radix select in 4-bit steps: each
-// thread counts its digits per nibble value with shifts into 4-bit fields
-// (vector ALU only: no per-digit condition masks), the counts are summed over
-// the block, and the first nibble whose count from the top reaches the
-// remainder is taken.  Every thread of the block must call it; red is LDS
-// scratch of 16*16 + 4 words.
+// empty slots count as digit 0.
+// The sampled top of the distribution is narrow, so it is found in a window
+// of 256 digit values (two octaves) below the largest sample: an LDS
+// histogram of the samples in the window (they spread over many bins, so
+// the atomics hardly collide), then one scan from the top.  If the window
+// holds fewer than the remaining count, the next window starts at the
+// largest sample below it.  Every thread of the block must call it; red is
+// LDS scratch of 256 + 32 words.
 __device__ __forceinline__ uint32_t wg_beta(const uint16_t* dg, int ns, uint32_t need, uint32_t* red) {
   const int nv = ns / 8;   // 16-byte chunks
   const int t = threadIdx.x, nb = blockDim.x, nw = nb >> 6, lane = t & 63, wave = t >> 6;
-  uint32_t d[8];           // 16 digits, two per word
+  uint32_t* hist = red;          // [256], bin i = digit top - i
+  uint32_t* wr = red + 256;      // [16] per-wave partials, [16..18] broadcast
+  uint32_t d[8];                 // 16 digits, two per word
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
     const int c = t + m * nb;
@@ -376,63 +380,68 @@ __device__ __forceinline__ uint32_t wg_beta(const uint16_t* dg, int ns, uint32_t
     d[4 * m + 2] = v.z;
     d[4 * m + 3] = v.w;
   }
-  uint32_t prefix = 0, pmask = 0, rem = need;
-#pragma unroll 1
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t shift = 12u - 4u * (uint32_t)p;
-    // A counts digits 0..7, B digits 8..15: at most 8 per 4-bit field
-    uint64_t A = 0, B = 0;
+  // largest digit strictly below `lim` (0 if none), over the block
+  auto max_below = [&](uint32_t lim) -> uint32_t {
+    uint32_t m = 0;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const uint32_t x = (e & 1) ? d[e >> 1] >> 16 : d[e >> 1] & 0xFFFFu;
-      const uint32_t ok = 1u - min((x ^ prefix) & pmask, 1u);
-      const uint64_t inc = (uint64_t)ok << (((x >> shift) & 15u) << 2);
-      if (e < 8) A += inc; else B += inc;
+      m = max(m, x < lim ? x : 0u);
     }
-    // repack the 16 counts into 16-bit fields of 4 words and sum over the wave
+    m = wave_max(m);
+    __syncthreads();
+    if (lane == 0) wr[wave] = m;
+    __syncthreads();
+    return lds_max16(wr, nw);
+  };
+  uint32_t top = max_below(0x10000u), rem = need;
+  for (;;) {
+    for (int i = t; i < 256; i += nb) hist[i] = 0u;
+    __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t a = (uint32_t)(A >> (16 * q)) & 0xFFFFu, bq = (uint32_t)(B >> (16 * q)) & 0xFFFFu;
-      // fields f of a, bq: nibble counts of value 4q+f
-      const uint32_t lo = (a & 0xFu) + (bq & 0xFu) + ((((a >> 4) & 0xFu) + ((bq >> 4) & 0xFu)) << 16);
-      const uint32_t hi = ((a >> 8) & 0xFu) + ((bq >> 8) & 0xFu) + ((((a >> 12) & 0xFu) + ((bq >> 12) & 0xFu)) << 16);
-      const uint32_t slo = wave_sum(lo), shi = wave_sum(hi);
-      if (lane == 0) {
-        red[wave * 16 + 4 * q + 0] = slo & 0xFFFFu;
-        red[wave * 16 + 4 * q + 1] = slo >> 16;
-        red[wave * 16 + 4 * q + 2] = shi & 0xFFFFu;
-        red[wave * 16 + 4 * q + 3] = shi >> 16;
-      }
+    for (int e = 0; e < 16; ++e) {
+      const uint32_t x = (e & 1) ? d[e >> 1] >> 16 : d[e >> 1] & 0xFFFFu;
+      const uint32_t dist = top - x;            // wraps for x > top
+      if (dist < 256u) atomicAdd(&hist[dist], 1u);
     }
     __syncthreads();
     if (wave == 0) {
-      // lane r < 16 takes nibble value 15 - r, so an inclusive scan over the
-      // lanes counts from the top; the first lane reaching rem is the pick.
-      // (All lanes stay active: the scan, ballot and readlane need them.)
-      const int j = 15 - (lane & 15);
-      uint32_t v = 0;
+      // lane l holds bins 4l..4l+3 (digits top-4l .. top-4l-3), top first
+      uint32_t c[4], s = 0;
 #pragma unroll
-      for (int w = 0; w < 16; ++w) {
-        const uint32_t x = red[w * 16 + j];
-        v += w < nw ? x : 0u;
+      for (int j = 0; j < 4; ++j) {
+        c[j] = hist[4 * lane + j];
+        s += c[j];
       }
-      if (lane >= 16) v = 0;
-      const uint32_t incl = wave_incl_scan(v);
-      const uint64_t m = __ballot(lane < 16 && incl >= rem);
-      const int r = m ? (int)__ffsll((unsigned long long)m) - 1 : 15;
-      const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)(incl - v), r);
+      const uint32_t incl = wave_incl_scan(s);
+      const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+      const uint64_t m = __ballot(incl >= rem);
+      const int l = m ? (int)__ffsll((unsigned long long)m) - 1 : 0;
+      uint32_t cum = incl - s, dist = 0;
+      bool found = false;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (!found && cum + c[j] >= rem) {
+          found = true;
+          dist = (uint32_t)(4 * lane + j);
+        }
+        cum += c[j];
+      }
+      const uint32_t dsel = (uint32_t)__builtin_amdgcn_readlane((int)dist, l);
       if (lane == 0) {
-        red[257] = prefix | ((uint32_t)(15 - r) << shift);
-        red[258] = rem - above;
+        wr[16] = m ? 1u : 0u;              // reached inside this window
+        wr[17] = top - dsel;               // the digit, if reached
+        wr[18] = tot;                      // samples in the window
       }
     }
     __syncthreads();
-    prefix = red[257];
-    pmask |= 15u << shift;
-    rem = red[258];
-    __syncthreads();   // red is rewritten by the next pass
+    const uint32_t hit = wr[16], val = wr[17], tot = wr[18];
+    __syncthreads();
+    if (hit) return val;
+    rem -= tot;
+    if (top < 256u) return 0u;             // every sample counted: fewer than need
+    top = max_below(top - 255u);
   }
-  return prefix;
 }
 
 }  // namespace skv

@@ -107,12 +107,13 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
       if (!COLLECT) {
         if (sub == 0 && i < i1) kout[i] = key;
       } else {
-        const bool sel = sub == 0 && i < i1 && key_digit16(key) >= beta;
+        const uint32_t dig = key_digit16(key);
+        const bool sel = sub == 0 && i < i1 && dig >= beta;
         const uint64_t m = __ballot(sel);
         if (sel) {
           const uint64_t ok = ordered_u64(key);
           const uint32_t rank = cnt + (uint32_t)__popcll(m & lt);
-          cseg[rank] = (u32x4){(uint32_t)ok, (uint32_t)(ok >> 32), (uint32_t)(lo + i), 0u};
+          cseg[rank] = (u32x4){(uint32_t)ok, (uint32_t)(ok >> 32), (uint32_t)(lo + i), dig};
         }
         cnt += (uint32_t)__popcll(m);
       }
@@ -192,7 +193,7 @@ __global__ __launch_bounds__(1024) void beta_kernel(const uint16_t* __restrict__
                                                      const int32_t* __restrict__ ctx_len,
                                                      TopkState* __restrict__ state, int mode,
                                                      int max_ctx, int S, int k, int L) {
-  __shared__ uint32_t red[16 * 16 + 4];
+  __shared__ uint32_t red[256 + 32];
   const int b = blockIdx.x;
   const Range r = cand_range(mode, ctx_of(ctx_len, b, max_ctx), S, k, L);
   if (r.dense) return;

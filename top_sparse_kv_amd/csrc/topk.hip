@@ -21,10 +21,12 @@
 //   collect  one wave per segment keeps the digits >= beta, in order.
 // The fused path (score.hip) produces the same records straight from the
 // index.  Then, one workgroup per sequence:
-//   final    gathers the candidates into LDS (position order), runs an exact
-//            MSB-first radix select over the 96-bit composite (ordered key,
-//            ~position), stopping once the boundary bucket is kept whole, and
-//            writes the kept positions by an ordered prefix sum.
+//   final    gathers the candidates into registers (position order), finds
+//            the 16-bit digit bin of the k-th largest with one LDS histogram
+//            (bins above it are kept whole), orders the members of that bin
+//            exactly by the composite (key, ~position) -- pairwise ranks when
+//            it is small, else an MSB-first radix select -- and writes the
+//            kept positions by an ordered prefix sum.
 // Fallbacks, flagged SKV_FLAG_TOPK_SLOW: more candidates than LDS holds ->
 // the same select over the records in global memory; fewer candidates than
 // the budget (the sample overestimated beta) -> the select over every key of
@@ -132,7 +134,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_collect_kernel(
     if (selm & (1u << u)) {
       const uint64_t ok = ordered_u64(x[u]);
       if (at < (uint32_t)SEG)   // always true: at most one record per key
-        out[at] = (u32x4){(uint32_t)ok, (uint32_t)(ok >> 32), (uint32_t)(r.lo + i0 + lane * KPL + u), 0u};
+        out[at] = (u32x4){(uint32_t)ok, (uint32_t)(ok >> 32), (uint32_t)(r.lo + i0 + lane * KPL + u),
+                          key_digit16(x[u])};
       ++at;
     }
   }
@@ -269,7 +272,7 @@ __device__ void radix_select(Get get, int n, int k, SelectShared& sh) {
 
 __device__ __forceinline__ bool kept(uint64_t hi, uint32_t lo, const SelectShared& sh) {
   const uint64_t h = hi & sh.mask_hi;
-  return h > sh.pre_hi || (h == sh.pre_hi && (lo & sh.mask_lo) >= sh.pre_lo);
+  return (h > sh.pre_hi) | ((h == sh.pre_hi) & ((lo & sh.mask_lo) >= sh.pre_lo));
 }
 
 // Output slot of the rank-th kept candidate (ascending): token mode after the
@@ -321,6 +324,8 @@ struct NoSrc {
   static constexpr int LANES = 64;
 };
 
+constexpr uint32_t kRankMax = 256;   // bucket sizes resolved by pairwise ranks
+
 // RECOMPUTE (the fused path): keys are recomputed from the index when the
 // candidates are too few.
 template <class Src, bool RECOMPUTE>
@@ -331,9 +336,10 @@ __global__ __launch_bounds__(kFT) void topk_final_kernel(
     int32_t* __restrict__ n_sel,
     uint32_t* __restrict__ flags, int n_seg, int seg_items, int mode, int max_ctx, int S, int k,
     int L, int cap) {
-  __shared__ uint64_t s_key[kListCap];
-  __shared__ uint32_t s_pos[kListCap];
+  __shared__ uint64_t s_bhi[kListCap + 8];
+  __shared__ uint32_t s_blo[kListCap + 8];
   __shared__ uint32_t s_off[kMaxSeg + 1];
+  __shared__ uint32_t s_hist[256 + 32];
   __shared__ SelectShared sh;
   const int b = blockIdx.x;
   const int T = ctx_of(ctx_len, b, max_ctx);
@@ -380,13 +386,14 @@ __global__ __launch_bounds__(kFT) void topk_final_kernel(
   }
 
   if (total >= (uint32_t)k && total <= (uint32_t)kListCap) {
-    // ---- fast path: every candidate in LDS, in position order ----
+    // ---- fast path: the candidates stay in registers, in position order ----
+    // Thread t holds the contiguous run [kGPT*t, kGPT*(t+1)): one search for
+    // its first segment, then a walk; all its loads are issued together.
     const int n = (int)total;
+    const int j0 = kGPT * (int)threadIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    u32x4 rec[kGPT];
     {
-      // thread t moves the contiguous run [kGPT*t, kGPT*(t+1)): one search for
-      // its first segment, then a walk; all its loads are issued together
-      const int j0 = kGPT * (int)threadIdx.x;
-      u32x4 rec[kGPT];
       int c = seg_of(s_off, n_parts, (uint32_t)min(j0, n - 1));
 #pragma unroll
       for (int m = 0; m < kGPT; ++m) {
@@ -395,30 +402,132 @@ __global__ __launch_bounds__(kFT) void topk_final_kernel(
         const int e = min(max(j - (int)s_off[c], 0), seg_items - 1);   // in range by construction
         rec[m] = reinterpret_cast<const u32x4*>(cb + (size_t)c * seg_items)[e];
       }
+    }
+    // The 16-bit digit (rec.w) is monotone in the key.  Bins count digits
+    // upward from the lowest one, the last bin takes everything from 255 up.
+    // The bin of the k-th largest candidate, fbin, splits the set: larger bins
+    // are kept whole, smaller ones dropped, and only the members of fbin need
+    // the exact (key, position) order.
+    uint32_t* wr = s_hist + 256;
+    {
+      uint32_t inv = 0;
 #pragma unroll
-      for (int m = 0; m < kGPT; ++m) {
-        const int j = j0 + m;
-        if (j < n) {
-          s_key[j] = ((uint64_t)rec[m].y << 32) | rec[m].x;
-          s_pos[j] = rec[m].z;
+      for (int m = 0; m < kGPT; ++m)
+        if (j0 + m < n) inv = max(inv, 0xFFFFu - rec[m].w);
+      inv = wave_max(inv);
+      if (lane == 0) wr[wave] = inv;
+      if (threadIdx.x < 256) s_hist[threadIdx.x] = 0u;
+    }
+    __syncthreads();
+    const uint32_t dmin = 0xFFFFu - lds_max16(wr, kFT / 64);
+    auto bin_of = [&](uint32_t dg) -> uint32_t { return min(dg - dmin, 255u); };
+#pragma unroll
+    for (int m = 0; m < kGPT; ++m)
+      if (j0 + m < n) atomicAdd(&s_hist[bin_of(rec[m].w)], 1u);
+    __syncthreads();
+    if (wave == 0) {
+      // lane l owns bins 255-4l .. 252-4l, counted from the top
+      uint32_t c[4], s = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[j] = s_hist[255 - 4 * lane - j];
+        s += c[j];
+      }
+      const uint32_t incl = wave_incl_scan(s);
+      const uint64_t hit = __ballot(incl >= (uint32_t)k);   // not empty: n >= k
+      const int l = (int)__ffsll((unsigned long long)hit) - 1;
+      uint32_t cum = incl - s, fb = 0, before = 0;
+      bool found = false;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (!found && cum + c[j] >= (uint32_t)k) {
+          found = true;
+          fb = (uint32_t)(255 - 4 * lane - j);
+          before = cum;
         }
+        cum += c[j];
+      }
+      const uint32_t fsel = (uint32_t)__builtin_amdgcn_readlane((int)fb, l);
+      const uint32_t bsel = (uint32_t)__builtin_amdgcn_readlane((int)before, l);
+      if (lane == 0) {
+        wr[16] = fsel;
+        wr[17] = bsel;
       }
     }
     __syncthreads();
-    radix_select([&](int i, uint64_t& hi, uint32_t& lo) { hi = s_key[i]; lo = ~s_pos[i]; }, n, k, sh);
-    // ordered emission: thread t owns the contiguous run [t*per, (t+1)*per)
-    const int per = (n + kFT - 1) / kFT;   // <= kGPT <= 32
-    const int e0 = threadIdx.x * per, e1 = min(n, e0 + per);
+    const uint32_t fbin = wr[16];
+    const uint32_t r = (uint32_t)k - wr[17];   // taken from bin fbin, >= 1
+    // the members of fbin, in position order, as composites (key, ~position)
+    uint32_t mine = 0;
+#pragma unroll
+    for (int m = 0; m < kGPT; ++m)
+      if (j0 + m < n && bin_of(rec[m].w) == fbin) ++mine;
+    uint32_t mb = 0;
+    uint32_t at = block_excl_scan(mine, sh.wsum, &mb);
+#pragma unroll
+    for (int m = 0; m < kGPT; ++m)
+      if (j0 + m < n && bin_of(rec[m].w) == fbin) {
+        s_bhi[at] = ((uint64_t)rec[m].y << 32) | rec[m].x;
+        s_blo[at] = ~rec[m].z;
+        ++at;
+      }
+    if (threadIdx.x < 8) {   // padding that never ranks above a member
+      s_bhi[mb + threadIdx.x] = 0ull;
+      s_blo[mb + threadIdx.x] = 0u;
+    }
+    __syncthreads();
+    if (mb <= kRankMax) {
+      // each member counts the members above it; rank r-1 is the threshold
+      if (threadIdx.x < mb) {
+        const uint64_t hi = s_bhi[threadIdx.x];
+        const uint32_t lo = s_blo[threadIdx.x];
+        uint32_t rank = 0;
+        for (uint32_t j = 0; j < mb; j += 8) {
+          uint64_t oh[8];
+          uint32_t ol[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            oh[u] = s_bhi[j + u];
+            ol[u] = s_blo[j + u];
+          }
+          // the two cases exclude each other; added without branches
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            rank += (uint32_t)(oh[u] > hi) + (uint32_t)((oh[u] == hi) & (ol[u] > lo));
+        }
+        if (rank == r - 1) {
+          sh.pre_hi = hi;
+          sh.pre_lo = lo;
+        }
+      }
+      if (threadIdx.x == 0) {
+        sh.mask_hi = ~0ull;
+        sh.mask_lo = ~0u;
+      }
+      __syncthreads();
+    } else {
+      radix_select([&](int i, uint64_t& hi, uint32_t& lo) {
+        hi = s_bhi[i];
+        lo = s_blo[i];
+      }, (int)mb, (int)r, sh);
+    }
+    // ordered emission of the kept candidates
     uint32_t keep = 0, cnt = 0;
-    for (int e = e0; e < e1; ++e)
-      if (kept(s_key[e], ~s_pos[e], sh)) {
-        keep |= 1u << (e - e0);
+#pragma unroll
+    for (int m = 0; m < kGPT; ++m) {
+      if (j0 + m >= n) continue;
+      const uint32_t bn = bin_of(rec[m].w);
+      if (bn > fbin ||
+          (bn == fbin && kept(((uint64_t)rec[m].y << 32) | rec[m].x, ~rec[m].z, sh))) {
+        keep |= 1u << m;
         ++cnt;
       }
+    }
     int rank = (int)block_excl_scan(cnt, sh.wsum, nullptr);
-    for (int e = e0; e < e1; ++e)
-      if (keep & (1u << (e - e0))) {
-        if (rank < k) emit_position(out, mode, S, rank, (int)s_pos[e]);
+#pragma unroll
+    for (int m = 0; m < kGPT; ++m)
+      if (keep & (1u << m)) {
+        if (rank < k) emit_position(out, mode, S, rank, (int)rec[m].z);
         ++rank;
       }
     return;
