@@ -10,12 +10,17 @@
 //
 // Work split: one workgroup per (sequence, KV head, chunk of 512 selected
 // rows), so that a 250K-token batch of 8 needs fewer workgroups than the GPU
-// has compute units; each of its 16 waves runs an online softmax over 32 rows
+// has compute units; each of its 16 waves runs a softmax tile over 32 rows
 // for the G query heads of that KV head.  The waves merge in two LDS stages
 // (wave w+8 into wave w, then the 8 survivors), which bounds the LDS at
 // 8*G*(D+4) floats, and the workgroup writes one (max, sum, unnormalised
 // output) partial; a second kernel merges the chunks of each query head in
 // fixed order.
+//
+// Latency: a wave reads its row indices, n_sel and Q in one round trip, then
+// issues every K, V and scale load of its tile in one batch (the per-row
+// scales one per lane, handed to the lanes that need them by cross-lane
+// reads), so the tile costs two dependent memory round trips.
 //
 // Inner step on the matrix cores (v_mfma_f32_16x16x32 f16 / bf16):
 //   logits^T[32 tok x 16 heads] = K[32 x D] . Q^T[D x 16]   (2 M-tiles of 16)
@@ -94,9 +99,14 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
   constexpr int VB = D / 16 * ES;         // bytes of one lane's V slice per token
   constexpr int KV4 = KB / 16;            // 16-byte loads per K slice
   constexpr int VV4 = VB / 16;            // 16-byte loads per V slice
+  constexpr int HALF = kAttWaves / 2;
+  constexpr int QP = D + 8;               // padded Q row (halves): conflict-free 16-byte reads
+  constexpr int QPT = (16 * D / 2 + kAttThreads - 1) / kAttThreads;   // Q dwords per thread
+  static_assert(kAttRowsPerWave == 32, "one 32-row tile per wave");
   __shared__ float s_m[kAttWaves][16];
   __shared__ float s_l[kAttWaves][16];
-  extern __shared__ float s_o[];          // [kAttWaves][G][D + 4], d stored as (t, i16)
+  __shared__ uint32_t s_q[16 * QP / 2];   // Q of the G heads, one row per head
+  extern __shared__ float s_o[];          // [HALF][G][D + 4]
 
   const int h = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
   const int G = Hq / Hkv;
@@ -105,41 +115,41 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
   const int r0 = c * kAttRowsPerWG;
   const int rb = r0 + wave * kAttRowsPerWave;   // this wave's 32 selected rows
   const int32_t* ib = idx + (size_t)b * cap;
-  // the row indices this lane uses are loaded together with n_sel (clamped into
-  // the array, masked by n below), saving a dependent round trip:
+  // The row indices this lane uses are loaded together with n_sel and Q
+  // (clamped into the array, masked by n below), saving dependent round trips:
   //   QK A operand: M-tile mt row i16 -> selected row rb + 16*mt + i16;
-  //   P / V: e = 0..3 -> row rb + 4g + e, e = 4..7 -> row rb + 16 + 4g + e-4
+  //   P / V: e = 0..3 -> row rb + 4g + e, e = 4..7 -> row rb + 16 + 4g + e-4;
+  //   scales: lane l loads the K (l < 32) or V (l >= 32) scale of row l % 32.
   int tk[2], tv[8];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) tk[mt] = ib[min(rb + 16 * mt + i16, cap - 1)];
 #pragma unroll
   for (int e = 0; e < 8; ++e) tv[e] = ib[min(rb + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4)), cap - 1)];
+  const int ts = ib[min(rb + (lane & 31), cap - 1)];
   int n = n_sel[b];
+  // the G query heads of this KV head pass through LDS (G*D/2 dwords)
+  const int qdw = G * D / 2;
+  uint32_t qd[QPT];
+  {
+    const uint32_t* qp = reinterpret_cast<const uint32_t*>(qv) + ((size_t)b * Hq + (size_t)h * G) * (D / 2);
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) qd[u] = qp[min((int)threadIdx.x + u * kAttThreads, qdw - 1)];
+  }
   if (n < 0 || n > cap) {
     if (threadIdx.x == 0 && c == 0 && h == 0) raise_flag(flags, SKV_FLAG_INDEX_RANGE);
     n = n < 0 ? 0 : cap;
   }
   if (r0 >= n) return;
+#pragma unroll
+  for (int u = 0; u < QPT; ++u) {
+    const int x = threadIdx.x + u * kAttThreads;
+    if (x < qdw) s_q[(x / (D / 2)) * (QP / 2) + x % (D / 2)] = qd[u];
+  }
+  __syncthreads();
   const size_t row_stride = (size_t)Hkv * D * ES;   // bytes between consecutive rows
 
-  // Q as the B operand of the QK product: lane (head j = i16, group g), step s
-  // holds Q[j][g*D/4 + 8s .. +8]
-  u32x4 bq[KSTEPS];
-  {
-    const int j = i16;
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(qv) + ((size_t)b * Hq + (size_t)h * G + (j < G ? j : 0)) * D + g * (D / 4);
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(qp + 8 * s);
-      if (j >= G) v = (u32x4){0u, 0u, 0u, 0u};
-      bq[s] = v;
-    }
-  }
-
   f32x4 o[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) o[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;   // running max of head i16 (log2 units), same in all 4 groups
+  float m_run = -INFINITY;   // max of head i16 (log2 units), same in all 4 groups
   float l_run = 0.0f;
 
   const uint8_t* kbase = kc + ((size_t)b * rows * Hkv + h) * D * ES;
@@ -147,7 +157,6 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
   const uint16_t* ksb = ksc ? ksc + (size_t)b * rows * Hkv + h : nullptr;
   const uint16_t* vsb = vsc ? vsc + (size_t)b * rows * Hkv + h : nullptr;
 
-  static_assert(kAttRowsPerWave == 32, "one 32-row tile per wave");
   if (rb < n) {
     // out-of-range rows load row 0 and are masked through vok
     int ka[2];
@@ -168,7 +177,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
       vt[e] = ok ? tok : 0;
       vok[e] = ok;
     }
-    // ---- loads ----
+    const int tsc = (rb + (lane & 31) < n && ts >= 0 && (int64_t)ts < rows) ? ts : 0;
+    // ---- every load of the tile, issued back to back ----
     u32x4 kraw[2][KV4];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
@@ -183,25 +193,36 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
 #pragma unroll
       for (int x = 0; x < VV4; ++x) vraw[e][x] = vp[x];
     }
+    uint16_t sbits = 0;
+    if constexpr (KVT == KV_I8) sbits = (lane < 32 ? ksb : vsb)[(size_t)tsc * Hkv];
+    // 16-bit K/V do not fit in registers all at once: the compiler interleaves
+    if constexpr (KVT == KV_I8) __builtin_amdgcn_sched_barrier(0);
     float kscale[8], vscale[8];
+    if constexpr (KVT == KV_I8) {
+      const float sc = half_bits_to_float(sbits);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if constexpr (KVT == KV_I8) {
-        kscale[e] = half_bits_to_float(ksb[(size_t)vt[e] * Hkv]);
-        vscale[e] = half_bits_to_float(vsb[(size_t)vt[e] * Hkv]);
-      } else {
+      for (int e = 0; e < 8; ++e) {
+        const int row = e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4);
+        kscale[e] = __shfl(sc, row);
+        vscale[e] = __shfl(sc, 32 + row);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
         kscale[e] = 1.0f;
         vscale[e] = 1.0f;
       }
     }
 
     // ---- logits (transposed): 2 M-tiles of 16 tokens x 16 heads ----
-    f32x4 sacc[2];
+    // B operand: lane (head j = i16, group g), step s holds Q[j][g*D/4 + 8s .. +8]
+    f32x4 sacc[2] = {(f32x4){0.f, 0.f, 0.f, 0.f}, (f32x4){0.f, 0.f, 0.f, 0.f}};
+    const u32x4* qrow = reinterpret_cast<const u32x4*>(s_q + min(i16, G - 1) * (QP / 2) + g * (D / 8));
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < KSTEPS; ++s) {
+      const u32x4 bq = i16 < G ? qrow[s] : (u32x4){0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
+      for (int mt = 0; mt < 2; ++mt) {
         u32x4 a;
         if constexpr (KVT == KV_I8) {
           // step s uses bytes 8s..8s+7 of the lane's 64-byte slice
@@ -215,9 +236,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
         } else {
           a = kraw[mt][s];
         }
-        acc = mfma<BF>(a, bq[s], acc);
+        sacc[mt] = mfma<BF>(a, bq, sacc[mt]);
       }
-      sacc[mt] = acc;
     }
     // lane (head i16, group g) holds logits of rows 4g+e of each M-tile
     float lg[8];
@@ -230,20 +250,18 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = m_new == -INFINITY ? 1.0f : exp2f(m_run - m_new);
     float psum = 0.0f;
     float pv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float p = lg[e] == -INFINITY ? 0.0f : exp2f(lg[e] - m_new);
+      const float p = lg[e] == -INFINITY ? 0.0f : exp2f(lg[e] - tmax);
       psum += p;
       pv[e] = p * vscale[e];
     }
     psum += __shfl_xor(psum, 16);
     psum += __shfl_xor(psum, 32);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    l_run = psum;
+    m_run = tmax;
 
     // P (A operand of PV): high and low parts
     u32x4 phi, plo;
@@ -268,17 +286,6 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
       phi = (u32x4){hw[0], hw[1], hw[2], hw[3]};
       plo = (u32x4){lw[0], lw[1], lw[2], lw[3]};
     }
-    // rescale the running output rows (heads 4g+e) by their alpha
-    float arow[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) arow[e] = __shfl(alpha, 4 * g + e);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      o[t][0] *= arow[0];
-      o[t][1] *= arow[1];
-      o[t][2] *= arow[2];
-      o[t][3] *= arow[3];
-    }
     // ---- PV: N-tile t holds column d = i16*(D/16) + t ----
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -302,14 +309,23 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
           bw[pp] = __builtin_amdgcn_perm(vraw[2 * pp + 1][dw >> 2][dw & 3], vraw[2 * pp][dw >> 2][dw & 3], sel);
       }
       const u32x4 bv = (u32x4){bw[0], bw[1], bw[2], bw[3]};
-      o[t] = mfma<BF>(phi, bv, o[t]);
+      o[t] = mfma<BF>(phi, bv, (f32x4){0.f, 0.f, 0.f, 0.f});
       o[t] = mfma<BF>(plo, bv, o[t]);
     }
+  } else {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) o[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
 
   // ---- merge the 16 waves of the workgroup in LDS, in two stages ----
+  // Wave w + HALF goes into wave w; then the HALF survivors are combined.  A
+  // slot holds G rows of D + 4 floats; lane (i16, g) owns columns
+  // i16*(D/16) .. +D/16 of heads 4g .. 4g+3, stored as float4 runs.
   constexpr int DP = D + 4;
-  constexpr int HALF = kAttWaves / 2;
+  constexpr int CPL = D / 16;   // columns per lane
+  auto slot_ptr = [&](int slot, int j) -> f32x4* {
+    return reinterpret_cast<f32x4*>(s_o + ((size_t)slot * G + j) * DP + i16 * CPL);
+  };
   if (g == 0) {
     s_m[wave][i16] = m_run;
     s_l[wave][i16] = l_run;
@@ -319,14 +335,16 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
     for (int e = 0; e < 4; ++e) {
       const int j = 4 * g + e;
       if (j < G) {
+        f32x4* dst = slot_ptr(wave - HALF, j);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) s_o[((size_t)(wave - HALF) * G + j) * DP + t * 16 + i16] = o[t][e];
+        for (int u = 0; u < CPL / 4; ++u)
+          dst[u] = (f32x4){o[4 * u][e], o[4 * u + 1][e], o[4 * u + 2][e], o[4 * u + 3][e]};
       }
     }
   }
   __syncthreads();
   if (wave < HALF) {
-    // wave w absorbs wave w + HALF: both rescaled to the larger running max
+    // wave w absorbs wave w + HALF: both rescaled to the larger max
     const float mp = s_m[wave + HALF][i16], lp = s_l[wave + HALF][i16];
     const float M = fmaxf(m_run, mp);
     const float aw = m_run == -INFINITY ? 0.0f : exp2f(m_run - M);
@@ -341,9 +359,13 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
     for (int e = 0; e < 4; ++e) {
       const int j = 4 * g + e;
       if (j < G) {
+        const f32x4* src = slot_ptr(wave, j);
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-          o[t][e] = o[t][e] * aw_row[e] + s_o[((size_t)wave * G + j) * DP + t * 16 + i16] * ap_row[e];
+        for (int u = 0; u < CPL / 4; ++u) {
+          const f32x4 x = src[u];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) o[4 * u + q][e] = o[4 * u + q][e] * aw_row[e] + x[q] * ap_row[e];
+        }
       }
     }
     m_run = M;
@@ -359,73 +381,82 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
     for (int e = 0; e < 4; ++e) {
       const int j = 4 * g + e;
       if (j < G) {
+        f32x4* dst = slot_ptr(wave, j);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) s_o[((size_t)wave * G + j) * DP + t * 16 + i16] = o[t][e];
+        for (int u = 0; u < CPL / 4; ++u)
+          dst[u] = (f32x4){o[4 * u][e], o[4 * u + 1][e], o[4 * u + 2][e], o[4 * u + 3][e]};
       }
     }
   }
   __syncthreads();
+  // per query head: the workgroup's max and sum, and each slot's factor
   const size_t pbase = ((size_t)b * Hkv + h) * n_chunks + c;
-  for (int x = threadIdx.x; x < G * D; x += blockDim.x) {
-    const int j = x / D, rem = x % D;                 // rem = t*16 + i16
-    const int d = (rem & 15) * (D / 16) + (rem >> 4);  // column i16*(D/16) + t
+  if (threadIdx.x < 16) {
+    const int j = threadIdx.x;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < HALF; ++w) M = fmaxf(M, s_m[w][j]);
-    float acc = 0.0f;
+    float Ls = 0.0f;
 #pragma unroll
     for (int w = 0; w < HALF; ++w) {
       const float f = s_m[w][j] == -INFINITY ? 0.0f : exp2f(s_m[w][j] - M);
-      acc += s_o[((size_t)w * G + j) * DP + rem] * f;
+      s_l[HALF + w][j] = f;   // rows HALF.. of s_l are free now
+      Ls += s_l[w][j] * f;
     }
-    part_o[(pbase * G + j) * D + d] = acc;
-    if (d == 0) {
-      float Ls = 0.0f;
-#pragma unroll
-      for (int w = 0; w < HALF; ++w)
-        Ls += s_m[w][j] == -INFINITY ? 0.0f : s_l[w][j] * exp2f(s_m[w][j] - M);
+    if (j < G) {
       part_ml[(pbase * 16 + j) * 2 + 0] = M;
       part_ml[(pbase * 16 + j) * 2 + 1] = Ls;
     }
   }
+  __syncthreads();
+  for (int x = threadIdx.x; x < G * D; x += blockDim.x) {
+    const int j = x / D, d = x % D;
+    float acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < HALF; ++w) acc += s_o[((size_t)w * G + j) * DP + d] * s_l[HALF + w][j];
+    part_o[(pbase * G + j) * D + d] = acc;
+  }
 }
 
 // merge the chunks of each (sequence, query head) in ascending chunk order
-constexpr int kMaxChunks = 64;
+constexpr int kMaxChunks = 256;   // one thread per chunk
 
 __global__ __launch_bounds__(256) void attend_merge_kernel(
     const float* __restrict__ part_ml, const float* __restrict__ part_o,
     const int32_t* __restrict__ n_sel, int cap, int Hq, int Hkv, int D, int n_chunks,
     float* __restrict__ out) {
   __shared__ float s_f[kMaxChunks];
-  __shared__ float s_inv;
+  __shared__ float s_red[2][4];
   const int jq = blockIdx.x, b = blockIdx.y;
   const int G = Hq / Hkv;
   const int h = jq / G, j = jq % G;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int n = n_sel[b];
   n = n < 0 ? 0 : (n > cap ? cap : n);
-  const int nc = min((n + kAttRowsPerWG - 1) / kAttRowsPerWG, kMaxChunks);
+  const int nc = min((n + kAttRowsPerWG - 1) / kAttRowsPerWG, n_chunks);
   const size_t pb = ((size_t)b * Hkv + h) * n_chunks;
-  if (threadIdx.x < 64) {
-    const int c = threadIdx.x;
-    float m = -INFINITY, l = 0.0f;
-    if (c < nc) {
-      m = part_ml[((pb + c) * 16 + j) * 2];
-      l = part_ml[((pb + c) * 16 + j) * 2 + 1];
-    }
-    float M = m;
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    const float f = (m == -INFINITY) ? 0.0f : exp2f(m - M);
-    float Ls = l * f;
-    for (int off = 32; off > 0; off >>= 1) Ls += __shfl_xor(Ls, off);
-    if (c < kMaxChunks) s_f[c] = f;
-    if (c == 0) s_inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+  const int c = threadIdx.x;   // one chunk per thread (n_chunks <= kMaxChunks)
+  float m = -INFINITY, l = 0.0f;
+  if (c < nc) {
+    m = part_ml[((pb + c) * 16 + j) * 2];
+    l = part_ml[((pb + c) * 16 + j) * 2 + 1];
   }
+  float M = m;
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if (lane == 0) s_red[0][wave] = M;
   __syncthreads();
-  const float inv = s_inv;
+  M = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
+  const float f = (m == -INFINITY) ? 0.0f : exp2f(m - M);
+  float Ls = l * f;
+  for (int off = 32; off > 0; off >>= 1) Ls += __shfl_xor(Ls, off);
+  if (lane == 0) s_red[1][wave] = Ls;
+  s_f[c] = f;
+  __syncthreads();
+  Ls = (s_red[1][0] + s_red[1][1]) + (s_red[1][2] + s_red[1][3]);
+  const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
     float acc = 0.0f;
-    for (int c = 0; c < nc; ++c) acc += part_o[((pb + c) * G + j) * D + d] * s_f[c];
+    for (int cc = 0; cc < nc; ++cc) acc += part_o[((pb + cc) * G + j) * D + d] * s_f[cc];
     out[((size_t)b * Hq + jq) * D + d] = acc * inv;
   }
 }
@@ -440,6 +471,7 @@ hipError_t launch_attend(const skv_layer_desc& d, const void* q, const skv_kv_vi
   float* part_o = ws_ptr<float>(ws, Lw.att_o);
   const int cap = select_capacity(d);
   const int G = d.n_q_heads / d.n_kv_heads;
+  if (Lw.n_att_chunks > kMaxChunks) return hipErrorInvalidValue;
   const dim3 grid(d.n_kv_heads, Lw.n_att_chunks, d.batch);
   const size_t lds = (size_t)(kAttWaves / 2) * G * (d.head_dim + 4) * sizeof(float);
   const float sl = sm_scale * kLog2e;
