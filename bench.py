@@ -51,6 +51,13 @@ CONFIGS = {
     "cfg4a": dict(kind="token", B=32, T=131_072, n_kv=4, n_q=24, D=256, S=64, k=2048, L=1024,
                   kv="i8", layers=4, seed=1004,
                   workload="32 seq x 131,072 tokens; cfg2 layer shape"),
+    "cfg4b": dict(kind="token", B=32, T=250_000, n_kv=4, n_q=24, D=256, S=64, k=2048, L=1024,
+                  kv="i8", layers=2, seed=1014, mixed=(2048, 250_000),
+                  workload="32 seq, lengths uniform in 2,048..250,000 (seeded); cfg2 layer shape"),
+    "cfg5": dict(kind="tier", B=4, T=250_000, n_kv=4, n_q=24, D=256, S=64, k=2048, L=1024,
+                 kv="i8", layers=1, seed=1005, warm_steps=64, steps=256,
+                 workload="4 seq x 250,000 tokens; cfg2 layer shape; int4 host-RAM K/V records read "
+                          "zero-copy, 2.5% hot slots (windowed CLOCK), drifting-locality picks"),
     "cfg3": dict(kind="block", B=1, T=1_048_576, n_kv=2, n_q=16, D=256, k=512, layers=12,
                  seed=1003,
                  workload="1 seq x 1,048,576 tokens; 12 QSA layers; 2 KV x 16 q heads, head_dim "
@@ -65,7 +72,10 @@ class Layer:
         self.cfg = cfg
         seed = cfg["seed"] + 7919 * li
         if cfg["kind"] == "token":
-            c = synth.make_token_case(cfg["B"], cfg["T"], n_kv=cfg["n_kv"], n_q=cfg["n_q"],
+            lens = None
+            if "mixed" in cfg:
+                lens = synth.gen.mixed_lengths(cfg["B"], cfg["mixed"][0], cfg["mixed"][1], seed=cfg["seed"])
+            c = synth.make_token_case(cfg["B"], cfg["T"], lens, n_kv=cfg["n_kv"], n_q=cfg["n_q"],
                                       D=cfg["D"], S=cfg["S"], k=cfg["k"], L=cfg["L"],
                                       kv_format=cfg["kv"], seed=seed, device="cuda")
             self.desc = skv.token_desc(c.B, c.T_max, c.n_kv, c.n_q, c.D, topk=c.k, n_sink=c.S,
@@ -116,16 +126,18 @@ class Layer:
         skv.attend(self.desc, self.q, self.kv, self.idx, self.nsel, self.sm, self.out, ws)
 
 
-def algorithmic_bytes(cfg):
+def algorithmic_bytes(cfg, lens=None):
     """Bytes the method must move per layer-step (what each stage reads/writes
-    at minimum): the scan, the gathered K/V rows (+ row scales), q, out."""
+    at minimum): the scan, the gathered K/V rows (+ row scales), q, out.  With
+    per-sequence lengths, a sequence at or below the dense switch reads no
+    sketch and gathers all of its rows."""
     B, D, n_kv, n_q = cfg["B"], cfg["D"], cfg["n_kv"], cfg["n_q"]
     if cfg["kind"] == "token":
-        n_cand = cfg["T"] - cfg["S"] - cfg["L"]
-        scan = B * n_cand * (n_kv * 64 // 2 + 2)
-        n_sel = cfg["S"] + cfg["k"] + cfg["L"]
+        lens = [cfg["T"]] * B if lens is None else [int(x) for x in lens]
+        cap = cfg["S"] + cfg["k"] + cfg["L"]
+        scan = sum((T - cfg["S"] - cfg["L"]) * (n_kv * 64 // 2 + 2) for T in lens if T > cap)
         eb, sb = (1, 2) if cfg["kv"] == "i8" else (2, 0)
-        gather = B * n_sel * n_kv * (D * eb + sb) * 2
+        gather = sum(min(T, cap) for T in lens) * n_kv * (D * eb + sb) * 2
         basis = n_kv * D * 64 * 4
     else:
         scan = B * (cfg["T"] // 4) * 128 * 2
@@ -280,6 +292,94 @@ def _cpu_baseline(layer: Layer, cfg, min_seconds=10.0, max_reps=20):
                 seconds=t_total)
 
 
+def bench_tier(cfg, args):
+    """Host-tier layer-step: the hot-buffer resolve (hits, windowed-CLOCK
+    victims, zero-copy int4 fetch and dequantisation of the misses) followed by
+    attention over the resolved rows, with picks from the seeded
+    drifting-locality schedule in place of the indexer's selection."""
+    B, T, S, L, k = cfg["B"], cfg["T"], cfg["S"], cfg["L"], cfg["k"]
+    warm = args.warmup if args.warmup_given else cfg["warm_steps"]
+    steps = args.steps if args.steps_given else cfg["steps"]
+    log("generating the host-tier case")
+    c = synth.make_tier_case(B, T, n_kv=cfg["n_kv"], n_q=cfg["n_q"], D=cfg["D"], S=S, k=k, L=L,
+                             seed=cfg["seed"], device="cuda")
+    picks = synth.drift_picks(B, T, S, L, k, warm + steps, seed=cfg["seed"],
+                              window=min(65536, (T - S - L) // 2), sigma_c=256.0)
+    desc = skv.token_desc(B, T, cfg["n_kv"], cfg["n_q"], cfg["D"], topk=k, n_sink=S, n_tail=L)
+    tier = skv.Tier(desc, T, c.n_slots, 1)
+    try:
+        tier.host_records()[:] = c.records.cpu().numpy()
+        tier.load_resident(c.res_k, c.res_v, c.res_ks, c.res_vs)
+        res = tier.resident()
+        cap = skv.select_capacity(desc)
+        idx_all = torch.from_numpy(np.concatenate([
+            np.broadcast_to(np.arange(S, dtype=np.int32), (warm + steps, B, S)), picks,
+            np.broadcast_to(np.arange(T - L, T, dtype=np.int32), (warm + steps, B, L))], axis=2).copy()).cuda()
+        ws = skv.workspace(desc)
+        rows = torch.zeros((B, cap), dtype=torch.int32, device="cuda")
+        nsel = torch.full((B,), cap, dtype=torch.int32, device="cuda")
+        out = torch.zeros((B, cfg["n_q"], cfg["D"]), dtype=torch.float32, device="cuda")
+        q = c.q.contiguous()
+        sm = cfg["D"] ** -0.5
+        log("warmup", warm)
+        for s_ in range(warm):
+            tier.resolve(idx_all[s_], nsel, s_, rows)
+            skv.attend(desc, q, res, rows, nsel, sm, out, ws)
+        st0 = tier.stats()
+        log("timing %d layer-steps" % steps)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for s_ in range(warm, warm + steps):
+            tier.resolve(idx_all[s_], nsel, s_, rows)
+            skv.attend(desc, q, res, rows, nsel, sm, out, ws)
+        e1.record()
+        e1.synchronize()
+        secs = e0.elapsed_time(e1) / 1e3
+        st1 = tier.stats()
+        # the resolve alone, on a replay of the same picks from a reset buffer
+        tier.reset()
+        for s_ in range(warm):
+            tier.resolve(idx_all[s_], nsel, s_, rows)
+        torch.cuda.synchronize()
+        e0.record()
+        for s_ in range(warm, warm + steps):
+            tier.resolve(idx_all[s_], nsel, s_, rows)
+        e1.record()
+        e1.synchronize()
+        rsecs = e0.elapsed_time(e1) / 1e3
+        assert skv.check(ws) == 0
+    finally:
+        tier.close()
+    hits, misses = st1.hits - st0.hits, st1.misses - st0.misses
+    hbytes = st1.host_bytes - st0.host_bytes
+    res_line = {
+        "metric": METRIC,
+        "value": round(steps / secs, 2),
+        "unit": "layer-steps/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(1e3 * secs / steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": cfg["workload"], "name": "cfg5", "batch": B, "ctx": T,
+                   "hot_slots_per_seq": c.n_slots},
+        "tier": {"miss_rate": round(misses / max(1, hits + misses), 4), "hits": hits, "misses": misses,
+                 "host_bytes_per_step": round(hbytes / steps),
+                 "pcie_GBps_over_step": round(hbytes / secs / 1e9, 2),
+                 "resolve_us": round(rsecs / steps * 1e6, 2),
+                 "pcie_GBps_during_resolve": round(hbytes / rsecs / 1e9, 2),
+                 "pcie_peak_GBps": 64.0},
+        "roofline": None,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res_line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -304,6 +404,11 @@ def main():
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     cfg = CONFIGS[args.config]
+    if cfg["kind"] == "tier":
+        args.warmup_given = "--warmup" in sys.argv
+        args.steps_given = "--steps" in sys.argv
+        bench_tier(cfg, args)
+        return
     n_layers = args.layers or cfg["layers"]
     log("generating %d layers of %s" % (n_layers, args.config))
     layers = [Layer(cfg, li) for li in range(n_layers)]
@@ -330,7 +435,7 @@ def main():
             fn(layers[i % n_layers], ws)
         kt[name] = time_loop(fn, layers, ws, nk) / nk
     skv.check(ws)
-    ab = algorithmic_bytes(cfg)
+    ab = algorithmic_bytes(cfg, layers[0].case.lens if cfg["kind"] == "token" else None)
     value = args.steps / secs
     # the dominant kernel of the step: the fused score-and-collect stream
     score_s = score_ms / 1e3 / max(1, score_n)
