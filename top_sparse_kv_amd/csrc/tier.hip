@@ -15,12 +15,22 @@
 // rather than registering an existing anonymous mapping, and the kernel reads
 // it through the device address hipHostGetDevicePointer returns.
 //
-// Per step: tier_resolve (one workgroup per sequence) marks hits, then one
-// wave places the misses in ascending position order with the CLOCK hand,
-// holding a 64-slot window of the slot table in registers and resolving each
-// miss with one ballot; tier_fetch (many workgroups) reads the missed records
-// over PCIe and writes int8 rows + fp16 scales into their slots.
-#include "skv_internal.h"
+// Per step: tier_resolve (one workgroup per sequence) marks hits, then places
+// the misses; tier_fetch (many workgroups) reads the missed records over PCIe
+// and writes int8 rows + fp16 scales into their slots.
+//
+// Placement in parallel.  Walking the slots in hand order from where the hand
+// stopped, a slot is "free" if it is empty or unpinned (last <= step - W) with
+// its reference bit clear, and "referenced" if it is occupied, unpinned and
+// has the bit set.  The hand takes free slots and clears the bits of the
+// referenced slots it passes; pinned slots (including those taken in this
+// step) are skipped.  So the m-th miss (ascending position) takes the m-th
+// free slot; if the misses outnumber the free slots, the hand completes the
+// sweep -- every referenced slot is then clear -- and the remaining misses
+// take the referenced slots in hand order; beyond those nothing can be
+// evicted (flagged).  One prefix sum over the slots, in hand order, gives
+// every rank at once.
+#include "keys_common.h"
 
 #include <new>
 #include <string.h>
@@ -83,9 +93,10 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
   __shared__ int32_t s_pos[kMaxSlots];
   __shared__ int32_t s_last[kMaxSlots];
   __shared__ uint8_t s_ref[kMaxSlots];
-  __shared__ int32_t s_miss[kMaxTopk];
+  __shared__ int32_t s_miss[kMaxTopk];   // input index of each miss
+  __shared__ int32_t s_mpos[kMaxTopk];   // its position (read by the serial placement)
   __shared__ uint32_t s_wsum[kResolveThreads / 64];
-  __shared__ int s_nm, s_nmid, s_bad;
+  __shared__ int s_nm, s_nmid, s_bad, s_tlast;
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int32_t* sp = slot_pos + (size_t)b * n_slots;
@@ -97,10 +108,12 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
     s_last[i] = sl[i];
     s_ref[i] = (uint8_t)sr[i];
   }
+  const int h0 = hand_arr[b];
   if (threadIdx.x == 0) {
     s_nm = 0;
     s_nmid = 0;
     s_bad = 0;
+    s_tlast = -1;
   }
   int n = n_sel[b];
   if (n < 0 || n > cap) {
@@ -115,9 +128,10 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
   const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   for (int base = 0; base < n; base += blockDim.x) {
     const int i = base + threadIdx.x;
-    bool miss = false;
+    bool miss = false, mid = false;
+    int p = 0;
     if (i < n) {
-      const int p = ib[i];
+      p = ib[i];
       const bool sorted = i == 0 || ib[i - 1] < p;
       if (p < 0 || p >= T || !sorted) {
         s_bad = 1;
@@ -127,7 +141,7 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
       } else if (p >= T - L) {
         rb[i] = S + (p - (T - L));
       } else {
-        atomicAdd(&s_nmid, 1);
+        mid = true;
         const int s = sop[p];
         if (s >= 0) {
           s_ref[s] = 1;
@@ -139,7 +153,11 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
       }
     }
     const uint64_t m = __ballot(miss);
-    if (lane == 0) s_wsum[wave] = (uint32_t)__popcll(m);
+    const uint64_t mm = __ballot(mid);
+    if (lane == 0) {
+      s_wsum[wave] = (uint32_t)__popcll(m);
+      atomicAdd(&s_nmid, (int)__popcll(mm));
+    }
     __syncthreads();
     int off = s_nm;
     for (int w = 0; w < wave; ++w) off += (int)s_wsum[w];
@@ -147,6 +165,7 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
       const int at = off + (int)__popcll(m & lt_mask);
       if (at < k) {
         s_miss[at] = i;
+        s_mpos[at] = p;
       } else {
         rb[i] = 0;      // more middle picks than the budget: not placed, flagged
         s_bad = 1;
@@ -170,85 +189,82 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
   }
   __syncthreads();
 
-  // phase B: one wave places the misses in ascending order (windowed CLOCK)
-  if (wave == 0) {
-    int hand = hand_arr[b];
-    int wbase = hand - hand % 64;
-    int off = hand - wbase;
-    int myslot = wbase + lane;
-    bool valid = myslot < n_slots;
-    int mpos = valid ? s_pos[myslot] : -1;
-    int mlast = valid ? s_last[myslot] : kNoStep;
-    int mref = valid ? (int)s_ref[myslot] : 0;
-    const int old_limit = step - W;   // last <= step - W: outside the window
-    const int max_moves = 2 * (n_slots / 64 + 2);   // two full sweeps always find a victim
-    for (int mi = 0; mi < nm; ++mi) {
-      const int i = s_miss[mi];
-      const int p = ib[i];
-      int moves = 0;
-      while (true) {
-        const bool elig = valid && lane >= off;
-        const bool unpinned = mlast <= old_limit;
-        const bool victim = elig && (mpos < 0 || (unpinned && mref == 0));
-        const uint64_t vm = __ballot(victim);
-        const int v = vm ? (int)__ffsll((unsigned long long)vm) - 1 : 64;
-        // slots the hand passes before the victim lose their reference bit
-        if (elig && lane < v && mpos >= 0 && unpinned && mref == 1) mref = 0;
-        if (vm) {
-          if (lane == v) {
-            if (mpos >= 0) sop[mpos] = -1;
-            mpos = p;
-            mref = 1;
-            mlast = step;
-            sop[p] = myslot;
-            rb[i] = S + L + myslot;
-            miss_pos[(size_t)b * k + mi] = p;
-            miss_slot[(size_t)b * k + mi] = myslot;
-          }
-          off = v + 1;
-        } else {
-          off = 64;
-        }
-        if (!vm && ++moves > max_moves) {
-          // cannot happen when n_slots > window * topk; stop instead of spinning
-          if (lane == 0) {
-            rb[i] = 0;
-            s_bad = 1;
-          }
-          break;
-        }
-        if (off >= 64 || wbase + off >= n_slots) {
-          // write the window back and move to the next one
-          if (valid) {
-            s_pos[myslot] = mpos;
-            s_last[myslot] = mlast;
-            s_ref[myslot] = (uint8_t)mref;
-          }
-          wbase = wbase + 64 >= n_slots ? 0 : wbase + 64;
-          off = 0;
-          myslot = wbase + lane;
-          valid = myslot < n_slots;
-          mpos = valid ? s_pos[myslot] : -1;
-          mlast = valid ? s_last[myslot] : kNoStep;
-          mref = valid ? (int)s_ref[myslot] : 0;
-        }
-        if (vm) break;
-      }
-    }
-    if (valid) {
-      s_pos[myslot] = mpos;
-      s_last[myslot] = mlast;
-      s_ref[myslot] = (uint8_t)mref;
-    }
-    if (lane == 0) {
-      hand_arr[b] = wbase + off;
-      miss_count[b] = nm;
-      atomicAdd(&counters[0], (unsigned long long)s_nmid);
-      atomicAdd(&counters[1], (unsigned long long)(s_nmid - nm));
-      atomicAdd(&counters[2], (unsigned long long)nm);
-      if (s_bad) raise_flag(flags, SKV_FLAG_TIER_INPUT);
+  // phase B: thread t owns the slots at hand distance [kRun*t, kRun*t + kRun)
+  constexpr int kRun = kMaxSlots / kResolveThreads;
+  const int old_limit = step - W;   // last <= step - W: outside the window
+  const int d0 = kRun * (int)threadIdx.x;
+  uint32_t fmask = 0, rmask = 0;
+#pragma unroll
+  for (int r = 0; r < kRun; ++r) {
+    const int t = d0 + r;
+    if (t < n_slots) {
+      const int j = h0 + t < n_slots ? h0 + t : h0 + t - n_slots;
+      const int ps = s_pos[j];
+      const bool unp = s_last[j] <= old_limit;
+      const int rf = s_ref[j];
+      fmask |= (uint32_t)(ps < 0 || (unp && rf == 0)) << r;
+      rmask |= (uint32_t)(ps >= 0 && unp && rf == 1) << r;
     }
   }
+  uint32_t both = 0;
+  const uint32_t pre = block_excl_scan((uint32_t)__popc(fmask) | ((uint32_t)__popc(rmask) << 16), s_wsum,
+                                       &both);
+  const int nfree = (int)(both & 0xFFFFu), nref = (int)(both >> 16);
+  const bool sweep = nm > nfree;   // the hand goes all the way round
+  const int placed = min(nm, nfree + nref);
+  int fr = (int)(pre & 0xFFFFu), rr = (int)(pre >> 16);
+  auto take = [&](int mi, int j, int t) {
+    const int p = s_mpos[mi], i = s_miss[mi];
+    const int old = s_pos[j];
+    if (old >= 0) sop[old] = -1;
+    s_pos[j] = p;
+    s_ref[j] = 1;
+    s_last[j] = step;
+    sop[p] = j;
+    rb[i] = S + L + j;
+    miss_pos[(size_t)b * k + mi] = p;
+    miss_slot[(size_t)b * k + mi] = j;
+    if (mi == placed - 1) s_tlast = t;
+  };
+  uint32_t rleft = 0;   // referenced slots not taken
+#pragma unroll
+  for (int r = 0; r < kRun; ++r) {
+    const int t = d0 + r;
+    const int j = h0 + t < n_slots ? h0 + t : h0 + t - n_slots;
+    if (fmask & (1u << r)) {
+      if (fr < placed) take(fr, j, t);
+      ++fr;
+    } else if (rmask & (1u << r)) {
+      const int mi = nfree + rr;
+      if (sweep && mi < placed) take(mi, j, t);
+      else rleft |= 1u << r;
+      ++rr;
+    }
+  }
+  __syncthreads();
+  // bits of the referenced slots the hand passed are cleared
+  const int tlast = s_tlast;
+#pragma unroll
+  for (int r = 0; r < kRun; ++r) {
+    const int t = d0 + r;
+    if ((rleft & (1u << r)) && (sweep || t < tlast)) {
+      const int j = h0 + t < n_slots ? h0 + t : h0 + t - n_slots;
+      s_ref[j] = 0;
+    }
+  }
+  // misses nothing could be evicted for (cannot happen when the slots
+  // outnumber the picks of W steps)
+  for (int mi = placed + (int)threadIdx.x; mi < nm; mi += blockDim.x) rb[s_miss[mi]] = 0;
+  if (threadIdx.x == 0) {
+    if (placed < nm) s_bad = 1;
+    if (placed > 0) hand_arr[b] = h0 + tlast + 1 < n_slots ? h0 + tlast + 1 : h0 + tlast + 1 - n_slots;
+    miss_count[b] = placed;
+    atomicAdd(&counters[0], (unsigned long long)s_nmid);
+    atomicAdd(&counters[1], (unsigned long long)(s_nmid - nm));
+    atomicAdd(&counters[2], (unsigned long long)nm);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && s_bad) raise_flag(flags, SKV_FLAG_TIER_INPUT);
   __syncthreads();
   for (int i = threadIdx.x; i < n_slots; i += blockDim.x) {
     sp[i] = s_pos[i];
