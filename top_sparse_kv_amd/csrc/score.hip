@@ -17,15 +17,15 @@
 // read in full, so it is streamed once, with 16-byte loads spread over the
 // lanes of a candidate so that every wavefront load covers 1 KB of
 // consecutive memory; each wave keeps two batches of eight such loads in
-// flight.  Three kernels:
+// flight.  The kernels:
 //   score_kernel<keys>     writes every key (sparsekv_score);
 //   sample_kernel          the 16-bit digits (key rounded to fp32, 1/128
 //                          octave per bucket) of a sample of whole 16-candidate
 //                          lines, written to the workspace;
 //   beta_kernel            one workgroup per sequence finds, from the sampled
-//                          digits, the threshold digit beta (a binary search
-//                          with block-wide counts);
-//   score_kernel<collect>  every wave keeps, per 512-token (256-block)
+//                          digits, the threshold digit beta (a 256-bin LDS
+//                          histogram window slid down from the largest digit);
+//   score_kernel<collect>  every wave keeps, per 256-token (256-block)
 //                          segment, the candidates whose digit is >= beta, in
 //                          position order (ballot + popcount), as (key,
 //                          position) records; keys are never stored.
@@ -212,7 +212,8 @@ hipError_t launch_token_or_block(const skv_layer_desc& d, const int32_t* ctx_len
   const int L = mode == SKV_INDEX_SKETCH_INT4 ? d.n_tail : 0;
   const int seg_items = mode == SKV_INDEX_SKETCH_INT4 ? kSegTok : kSegBlk;
   const int n_seg = (max_candidates(d) + seg_items - 1) / seg_items;
-  const dim3 grid((n_seg + 3) / 4 > 0 ? (n_seg + 3) / 4 : 1, d.batch);
+  constexpr int kWaves = kThreads / 64;   // one segment per wave
+  const dim3 grid((n_seg + kWaves - 1) / kWaves > 0 ? (n_seg + kWaves - 1) / kWaves : 1, d.batch);
   if (!collect) {
     hipLaunchKernelGGL((score_kernel<Src, false>), grid, dim3(kThreads), 0, st, iq, ik, isc,
                        ctx_len, keys, nullptr, nullptr, nullptr, flags, mode, d.max_ctx, S, d.topk,

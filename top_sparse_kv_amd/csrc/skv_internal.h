@@ -18,8 +18,8 @@ constexpr int kHistBits = 12;                 // coarse-key histogram digit (1/8
 constexpr int kHistBins = 1 << kHistBits;     // 4096 bins
 constexpr int kListCap = 8192;                // candidates the select kernel holds in LDS
 constexpr int kMaxTopk = 4096;                // largest budget
-constexpr int kMaxSeg = 4096;                 // candidate segments per sequence
-constexpr int kSegTok = 512;                  // candidates per segment, token mode
+constexpr int kMaxSeg = 8192;                 // candidate segments per sequence
+constexpr int kSegTok = 256;                  // candidates per segment, token mode (32 KB of sketch per wave)
 constexpr int kSegBlk = 256;                  // candidates per segment, block mode
 constexpr int kAttRowsPerWave = 32;           // selected rows per attention wave
 constexpr int kAttWaves = 16;                 // waves per attention workgroup
