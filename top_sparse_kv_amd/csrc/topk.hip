@@ -336,8 +336,8 @@ __global__ __launch_bounds__(kFT) void topk_final_kernel(
     int32_t* __restrict__ n_sel,
     uint32_t* __restrict__ flags, int n_seg, int seg_items, int mode, int max_ctx, int S, int k,
     int L, int cap) {
-  __shared__ uint64_t s_bhi[kListCap + 8];
-  __shared__ uint32_t s_blo[kListCap + 8];
+  __shared__ uint64_t s_bhi[kListCap + 64];
+  __shared__ uint32_t s_blo[kListCap + 64];
   __shared__ uint32_t s_off[kMaxSeg + 1];
   __shared__ uint32_t s_hist[256 + 32];
   __shared__ SelectShared sh;
@@ -471,34 +471,40 @@ __global__ __launch_bounds__(kFT) void topk_final_kernel(
         s_blo[at] = ~rec[m].z;
         ++at;
       }
-    if (threadIdx.x < 8) {   // padding that never ranks above a member
+    if (threadIdx.x < 64) {   // padding that never ranks above a member
       s_bhi[mb + threadIdx.x] = 0ull;
       s_blo[mb + threadIdx.x] = 0u;
     }
     __syncthreads();
     if (mb <= kRankMax) {
-      // each member counts the members above it; rank r-1 is the threshold
-      if (threadIdx.x < mb) {
-        const uint64_t hi = s_bhi[threadIdx.x];
-        const uint32_t lo = s_blo[threadIdx.x];
-        uint32_t rank = 0;
-        for (uint32_t j = 0; j < mb; j += 8) {
-          uint64_t oh[8];
-          uint32_t ol[8];
+      // each member counts the members above it (P threads per member, each
+      // over every P-th member); rank r-1 is the threshold
+      const int P = mb <= 64 ? 16 : (mb <= 128 ? 8 : 4);
+      const int m = (int)threadIdx.x / P, part = (int)threadIdx.x % P;
+      uint32_t rank = 0;
+      uint64_t hi = 0;
+      uint32_t lo = 0;
+      if (m < (int)mb) {
+        hi = s_bhi[m];
+        lo = s_blo[m];
+        for (int j = part; j < (int)mb; j += 4 * P) {
+          uint64_t oh[4];
+          uint32_t ol[4];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            oh[u] = s_bhi[j + u];
-            ol[u] = s_blo[j + u];
+          for (int u = 0; u < 4; ++u) {   // past mb: zero padding, never above a member
+            oh[u] = s_bhi[j + u * P];
+            ol[u] = s_blo[j + u * P];
           }
           // the two cases exclude each other; added without branches
 #pragma unroll
-          for (int u = 0; u < 8; ++u)
+          for (int u = 0; u < 4; ++u)
             rank += (uint32_t)(oh[u] > hi) + (uint32_t)((oh[u] == hi) & (ol[u] > lo));
         }
-        if (rank == r - 1) {
-          sh.pre_hi = hi;
-          sh.pre_lo = lo;
-        }
+      }
+      for (int o = 1; o < P; o <<= 1) rank += (uint32_t)__shfl_xor((int)rank, o);
+      if (m < (int)mb && part == 0 && rank == r - 1) {
+        sh.pre_hi = hi;
+        sh.pre_lo = lo;
       }
       if (threadIdx.x == 0) {
         sh.mask_hi = ~0ull;
