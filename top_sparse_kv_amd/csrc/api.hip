@@ -98,8 +98,9 @@ skv_status validate_desc(const skv_layer_desc* d) {
     if ((cand + seg - 1) / seg > kMaxSeg)
       return set_error(SKV_ERR_UNSUPPORTED, "more than %d candidates per sequence", kMaxSeg * seg);
   }
-  if (select_capacity(*d) > 64 * kAttRowsPerWG)
-    return set_error(SKV_ERR_UNSUPPORTED, "select capacity %d > %d", select_capacity(*d), 64 * kAttRowsPerWG);
+  if (select_capacity(*d) > kMaxAttChunks * att_rows_per_wg(*d))
+    return set_error(SKV_ERR_UNSUPPORTED, "select capacity %d > %d", select_capacity(*d),
+                     kMaxAttChunks * att_rows_per_wg(*d));
   return ok();
 }
 

@@ -8,12 +8,14 @@
 // (token * n_kv_heads + kv_head) * head_dim, so K/V may live anywhere the
 // GPU can address.
 //
-// Work split: one workgroup per (sequence, KV head, chunk of 512 selected
-// rows), so that a 250K-token batch of 8 needs fewer workgroups than the GPU
-// has compute units; each of its 16 waves runs a softmax tile over 32 rows
-// for the G query heads of that KV head.  The waves merge in two LDS stages
-// (wave w+8 into wave w, then the 8 survivors), which bounds the LDS at
-// 8*G*(D+4) floats, and the workgroup writes one (max, sum, unnormalised
+// Work split: one workgroup of W waves per (sequence, KV head, chunk of 32*W
+// selected rows); each wave runs a softmax tile over 32 rows for the G query
+// heads of that KV head.  W is the largest of 16, 8, 4 that still gives about
+// one workgroup per compute unit, else 2 (a 250K-token batch of 8 uses 16; a
+// single 1M-token sequence uses 2, so its few thousand rows are gathered by
+// many compute units rather than ten).  The waves merge in two LDS stages
+// (wave w+W/2 into wave w, then the W/2 survivors), which bounds the LDS at
+// (W/2)*G*(D+4) floats, and the workgroup writes one (max, sum, unnormalised
 // output) partial; a second kernel merges the chunks of each query head in
 // fixed order.
 //
@@ -48,7 +50,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 enum { KV_I8 = 0, KV_F16 = 1, KV_BF16 = 2 };
-constexpr int kAttThreads = 64 * kAttWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <bool BF>
@@ -84,8 +85,8 @@ struct Esize {
   static constexpr int v = KVT == KV_I8 ? 1 : 2;
 };
 
-template <int KVT, int D>
-__global__ __launch_bounds__(kAttThreads) void attend_kernel(
+template <int KVT, int D, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void attend_kernel(
     const void* __restrict__ qv, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
     const uint16_t* __restrict__ ksc, const uint16_t* __restrict__ vsc, int64_t rows,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ n_sel, int cap,
@@ -99,12 +100,13 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
   constexpr int VB = D / 16 * ES;         // bytes of one lane's V slice per token
   constexpr int KV4 = KB / 16;            // 16-byte loads per K slice
   constexpr int VV4 = VB / 16;            // 16-byte loads per V slice
-  constexpr int HALF = kAttWaves / 2;
+  constexpr int NTH = 64 * WAVES;
+  constexpr int HALF = WAVES / 2;
   constexpr int QP = D + 8;               // padded Q row (halves): conflict-free 16-byte reads
-  constexpr int QPT = (16 * D / 2 + kAttThreads - 1) / kAttThreads;   // Q dwords per thread
+  constexpr int QPT = (16 * D / 2 + NTH - 1) / NTH;   // Q dwords per thread
   static_assert(kAttRowsPerWave == 32, "one 32-row tile per wave");
-  __shared__ float s_m[kAttWaves][16];
-  __shared__ float s_l[kAttWaves][16];
+  __shared__ float s_m[WAVES][16];
+  __shared__ float s_l[WAVES][16];
   __shared__ uint32_t s_q[16 * QP / 2];   // Q of the G heads, one row per head
   extern __shared__ float s_o[];          // [HALF][G][D + 4]
 
@@ -112,7 +114,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
   const int G = Hq / Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, g = lane >> 4;
-  const int r0 = c * kAttRowsPerWG;
+  const int r0 = c * (kAttRowsPerWave * WAVES);
   const int rb = r0 + wave * kAttRowsPerWave;   // this wave's 32 selected rows
   const int32_t* ib = idx + (size_t)b * cap;
   // The row indices this lane uses are loaded together with n_sel and Q
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
   {
     const uint32_t* qp = reinterpret_cast<const uint32_t*>(qv) + ((size_t)b * Hq + (size_t)h * G) * (D / 2);
 #pragma unroll
-    for (int u = 0; u < QPT; ++u) qd[u] = qp[min((int)threadIdx.x + u * kAttThreads, qdw - 1)];
+    for (int u = 0; u < QPT; ++u) qd[u] = qp[min((int)threadIdx.x + u * NTH, qdw - 1)];
   }
   if (n < 0 || n > cap) {
     if (threadIdx.x == 0 && c == 0 && h == 0) raise_flag(flags, SKV_FLAG_INDEX_RANGE);
@@ -142,7 +144,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
   if (r0 >= n) return;
 #pragma unroll
   for (int u = 0; u < QPT; ++u) {
-    const int x = threadIdx.x + u * kAttThreads;
+    const int x = threadIdx.x + u * NTH;
     if (x < qdw) s_q[(x / (D / 2)) * (QP / 2) + x % (D / 2)] = qd[u];
   }
   __syncthreads();
@@ -419,12 +421,12 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(
 }
 
 // merge the chunks of each (sequence, query head) in ascending chunk order
-constexpr int kMaxChunks = 256;   // one thread per chunk
+constexpr int kMaxChunks = kMaxAttChunks;   // one thread per chunk
 
 __global__ __launch_bounds__(256) void attend_merge_kernel(
     const float* __restrict__ part_ml, const float* __restrict__ part_o,
     const int32_t* __restrict__ n_sel, int cap, int Hq, int Hkv, int D, int n_chunks,
-    float* __restrict__ out) {
+    int rows_per_chunk, float* __restrict__ out) {
   __shared__ float s_f[kMaxChunks];
   __shared__ float s_red[2][4];
   const int jq = blockIdx.x, b = blockIdx.y;
@@ -433,7 +435,7 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int n = n_sel[b];
   n = n < 0 ? 0 : (n > cap ? cap : n);
-  const int nc = min((n + kAttRowsPerWG - 1) / kAttRowsPerWG, n_chunks);
+  const int nc = min((n + rows_per_chunk - 1) / rows_per_chunk, n_chunks);
   const size_t pb = ((size_t)b * Hkv + h) * n_chunks;
   const int c = threadIdx.x;   // one chunk per thread (n_chunks <= kMaxChunks)
   float m = -INFINITY, l = 0.0f;
@@ -473,27 +475,36 @@ hipError_t launch_attend(const skv_layer_desc& d, const void* q, const skv_kv_vi
   const int G = d.n_q_heads / d.n_kv_heads;
   if (Lw.n_att_chunks > kMaxChunks) return hipErrorInvalidValue;
   const dim3 grid(d.n_kv_heads, Lw.n_att_chunks, d.batch);
-  const size_t lds = (size_t)(kAttWaves / 2) * G * (d.head_dim + 4) * sizeof(float);
+  const int waves = att_waves(d);
+  const size_t lds = (size_t)(waves / 2) * G * (d.head_dim + 4) * sizeof(float);
   const float sl = sm_scale * kLog2e;
-#define SKV_AT(KVT, DD)                                                                          \
-  hipLaunchKernelGGL((attend_kernel<KVT, DD>), grid, dim3(kAttThreads), lds, st, q,              \
+#define SKV_AT(KVT, DD, WV)                                                                        \
+  hipLaunchKernelGGL((attend_kernel<KVT, DD, WV>), grid, dim3(64 * WV), lds, st, q,              \
                      (const uint8_t*)kv.k, (const uint8_t*)kv.v, kv.k_scale, kv.v_scale, kv.rows, \
                      idx, n_sel, cap, sl, d.n_q_heads, d.n_kv_heads, part_ml, part_o,             \
                      Lw.n_att_chunks, flags)
+#define SKV_AT_W(KVT, DD)                                                                          \
+  do {                                                                                             \
+    if (waves == 16) SKV_AT(KVT, DD, 16);                                                          \
+    else if (waves == 8) SKV_AT(KVT, DD, 8);                                                       \
+    else if (waves == 4) SKV_AT(KVT, DD, 4);                                                       \
+    else SKV_AT(KVT, DD, 2);                                                                       \
+  } while (0)
   const int kvt = d.kv_dtype == SKV_KV_I8_ROWSCALE ? KV_I8 : (d.kv_dtype == SKV_KV_F16 ? KV_F16 : KV_BF16);
-  if (kvt == KV_I8 && d.head_dim == 256) SKV_AT(KV_I8, 256);
-  else if (kvt == KV_I8 && d.head_dim == 128) SKV_AT(KV_I8, 128);
-  else if (kvt == KV_F16 && d.head_dim == 256) SKV_AT(KV_F16, 256);
-  else if (kvt == KV_F16 && d.head_dim == 128) SKV_AT(KV_F16, 128);
-  else if (kvt == KV_BF16 && d.head_dim == 256) SKV_AT(KV_BF16, 256);
-  else if (kvt == KV_BF16 && d.head_dim == 128) SKV_AT(KV_BF16, 128);
+  if (kvt == KV_I8 && d.head_dim == 256) SKV_AT_W(KV_I8, 256);
+  else if (kvt == KV_I8 && d.head_dim == 128) SKV_AT_W(KV_I8, 128);
+  else if (kvt == KV_F16 && d.head_dim == 256) SKV_AT_W(KV_F16, 256);
+  else if (kvt == KV_F16 && d.head_dim == 128) SKV_AT_W(KV_F16, 128);
+  else if (kvt == KV_BF16 && d.head_dim == 256) SKV_AT_W(KV_BF16, 256);
+  else if (kvt == KV_BF16 && d.head_dim == 128) SKV_AT_W(KV_BF16, 128);
   else return hipErrorInvalidValue;
+#undef SKV_AT_W
 #undef SKV_AT
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attend_merge_kernel, dim3(d.n_q_heads, d.batch), dim3(256), 0, st, part_ml,
                      part_o, n_sel, cap, d.n_q_heads, d.n_kv_heads, d.head_dim, Lw.n_att_chunks,
-                     out);
+                     att_rows_per_wg(d), out);
   return hipGetLastError();
 }
 

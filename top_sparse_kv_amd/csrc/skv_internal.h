@@ -22,8 +22,7 @@ constexpr int kMaxSeg = 8192;                 // candidate segments per sequence
 constexpr int kSegTok = 256;                  // candidates per segment, token mode (32 KB of sketch per wave)
 constexpr int kSegBlk = 256;                  // candidates per segment, block mode
 constexpr int kAttRowsPerWave = 32;           // selected rows per attention wave
-constexpr int kAttWaves = 16;                 // waves per attention workgroup
-constexpr int kAttRowsPerWG = kAttRowsPerWave * kAttWaves;
+constexpr int kMaxAttChunks = 256;            // attention partials per (sequence, KV head)
 
 // per-sequence select state written by the sample stage (u32 words)
 struct TopkState {
@@ -56,6 +55,19 @@ inline int select_capacity(const skv_layer_desc& d) {
   return d.index_mode == SKV_INDEX_SKETCH_INT4 ? d.n_sink + d.topk + d.n_tail : 4 * d.topk + 3;
 }
 
+// Waves per attention workgroup (one 32-row tile each): the largest of 16,
+// 8, 4 that still gives at least 200 workgroups (about one per compute unit),
+// else 2, so a small batch is spread over the GPU instead of a few CUs.
+inline int att_waves(const skv_layer_desc& d) {
+  const int cap = select_capacity(d);
+  for (int w = 16; w > 2; w >>= 1) {
+    const int chunks = (cap + kAttRowsPerWave * w - 1) / (kAttRowsPerWave * w);
+    if ((int64_t)d.batch * d.n_kv_heads * chunks >= 200) return w;
+  }
+  return 2;
+}
+inline int att_rows_per_wg(const skv_layer_desc& d) { return kAttRowsPerWave * att_waves(d); }
+
 inline int max_candidates(const skv_layer_desc& d) {
   return d.index_mode == SKV_INDEX_SKETCH_INT4 ? d.max_ctx : d.max_ctx / 4;
 }
@@ -83,7 +95,7 @@ inline WsLayout ws_layout(const skv_layer_desc& d) {
   w.segcnt = off;  off = align_up(off + B * w.n_seg * 4, 256);
   w.cand = off;    off = align_up(off + B * (size_t)w.n_seg * w.seg_items * 16, 256);
   const int cap = select_capacity(d);
-  w.n_att_chunks = (cap + kAttRowsPerWG - 1) / kAttRowsPerWG;
+  w.n_att_chunks = (cap + att_rows_per_wg(d) - 1) / att_rows_per_wg(d);
   const int G = d.n_q_heads / d.n_kv_heads;
   w.att_ml = off; off = align_up(off + B * d.n_kv_heads * w.n_att_chunks * 16 * 2 * 4, 256);
   w.att_o = off;  off = align_up(off + B * d.n_kv_heads * w.n_att_chunks * (size_t)G * d.head_dim * 4, 256);
