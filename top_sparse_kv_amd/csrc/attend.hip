@@ -423,11 +423,16 @@ __global__ __launch_bounds__(64 * WAVES) void attend_kernel(
 // merge the chunks of each (sequence, query head) in ascending chunk order
 constexpr int kMaxChunks = kMaxAttChunks;   // one thread per chunk
 
+// Thread d owns output column d (D <= 256); the partials of the first
+// kMergeBatch chunks are loaded together with the (max, sum) pairs, before the
+// factors are known, so a small merge costs one round trip plus the reductions.
+constexpr int kMergeBatch = 16;
+
 __global__ __launch_bounds__(256) void attend_merge_kernel(
     const float* __restrict__ part_ml, const float* __restrict__ part_o,
     const int32_t* __restrict__ n_sel, int cap, int Hq, int Hkv, int D, int n_chunks,
     int rows_per_chunk, float* __restrict__ out) {
-  __shared__ float s_f[kMaxChunks];
+  __shared__ float s_f[kMaxChunks + kMergeBatch];
   __shared__ float s_red[2][4];
   const int jq = blockIdx.x, b = blockIdx.y;
   const int G = Hq / Hkv;
@@ -437,30 +442,40 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(
   n = n < 0 ? 0 : (n > cap ? cap : n);
   const int nc = min((n + rows_per_chunk - 1) / rows_per_chunk, n_chunks);
   const size_t pb = ((size_t)b * Hkv + h) * n_chunks;
+  const int d = min((int)threadIdx.x, D - 1);
+  const float* po = part_o + (pb * G + j) * D + d;   // chunk cc at po[cc * G * D]
+  const size_t cstride = (size_t)G * D;
+  float v[kMergeBatch];
+#pragma unroll
+  for (int u = 0; u < kMergeBatch; ++u) v[u] = po[(size_t)min(u, n_chunks - 1) * cstride];   // unconditional
   const int c = threadIdx.x;   // one chunk per thread (n_chunks <= kMaxChunks)
-  float m = -INFINITY, l = 0.0f;
-  if (c < nc) {
-    m = part_ml[((pb + c) * 16 + j) * 2];
-    l = part_ml[((pb + c) * 16 + j) * 2 + 1];
-  }
-  float M = m;
+  const float m = part_ml[((pb + min(c, n_chunks - 1)) * 16 + j) * 2];
+  const float l = part_ml[((pb + min(c, n_chunks - 1)) * 16 + j) * 2 + 1];
+  const bool live = c < nc && m != -INFINITY;
+  float M = live ? m : -INFINITY;
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   if (lane == 0) s_red[0][wave] = M;
   __syncthreads();
   M = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
-  const float f = (m == -INFINITY) ? 0.0f : exp2f(m - M);
-  float Ls = l * f;
+  const float f = live ? exp2f(m - M) : 0.0f;
+  float Ls = live ? l * f : 0.0f;
   for (int off = 32; off > 0; off >>= 1) Ls += __shfl_xor(Ls, off);
   if (lane == 0) s_red[1][wave] = Ls;
   s_f[c] = f;
   __syncthreads();
   Ls = (s_red[1][0] + s_red[1][1]) + (s_red[1][2] + s_red[1][3]);
   const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float acc = 0.0f;
-    for (int cc = 0; cc < nc; ++cc) acc += part_o[((pb + cc) * G + j) * D + d] * s_f[cc];
-    out[((size_t)b * Hq + jq) * D + d] = acc * inv;
+  // chunks in ascending order; factors past nc are 0
+  float acc = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kMergeBatch; ++u) acc += v[u] * (u < nc ? s_f[u] : 0.0f);
+  for (int cc = kMergeBatch; cc < nc; cc += kMergeBatch) {
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) v[u] = po[(size_t)min(cc + u, nc - 1) * cstride];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) acc += v[u] * (cc + u < nc ? s_f[cc + u] : 0.0f);
   }
+  if ((int)threadIdx.x < D) out[((size_t)b * Hq + jq) * D + threadIdx.x] = acc * inv;
 }
 
 }  // namespace

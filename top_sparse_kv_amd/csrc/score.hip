@@ -25,7 +25,7 @@
 //   beta_kernel            one workgroup per sequence finds, from the sampled
 //                          digits, the threshold digit beta (a 256-bin LDS
 //                          histogram window slid down from the largest digit);
-//   score_kernel<collect>  every wave keeps, per 256-token (256-block)
+//   score_kernel<collect>  every wave keeps, per 256-token (128-block)
 //                          segment, the candidates whose digit is >= beta, in
 //                          position order (ballot + popcount), as (key,
 //                          position) records; keys are never stored.

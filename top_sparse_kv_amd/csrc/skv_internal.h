@@ -20,7 +20,7 @@ constexpr int kListCap = 8192;                // candidates the select kernel ho
 constexpr int kMaxTopk = 4096;                // largest budget
 constexpr int kMaxSeg = 8192;                 // candidate segments per sequence
 constexpr int kSegTok = 256;                  // candidates per segment, token mode (32 KB of sketch per wave)
-constexpr int kSegBlk = 256;                  // candidates per segment, block mode
+constexpr int kSegBlk = 128;                  // candidates per segment, block mode (32 KB of keys per wave)
 constexpr int kAttRowsPerWave = 32;           // selected rows per attention wave
 constexpr int kMaxAttChunks = 256;            // attention partials per (sequence, KV head)
 

@@ -15,7 +15,7 @@
 // The select works on candidates: the keys whose 12-bit digit (the key
 // rounded to fp32, 1/8 octave per bucket) is at least a threshold bucket beta
 // estimated from a sample of whole 16-key lines.  Candidates are stored per
-// segment (256 tokens or 256 blocks, one wave each) in position order.  With
+// segment (256 tokens or 128 blocks, one wave each) in position order.  With
 // keys already in memory (sparsekv_topk) two kernels produce them:
 //   sample   one workgroup per sequence histograms the sampled digits -> beta;
 //   collect  one wave per segment keeps the digits >= beta, in order.
