@@ -244,6 +244,7 @@ __device__ __forceinline__ int dot32_i4(const u32x4 w, const uint32_t qe[4], con
 template <int N>
 struct SketchSrc {
   static constexpr int LANES = N;
+  static constexpr bool HAS_AUX = true;    // integer dot times a per-token fp16 scale
   static constexpr int QROW = 32 * N;      // bytes of one sequence's query row
   uint32_t qe[4], qo[4];
   const uint8_t* cbase;     // this lane's 16 bytes of token 0 of the sequence
@@ -275,11 +276,20 @@ struct SketchSrc {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cbase + (size_t)p * (16 * N)));
   }
   __device__ __forceinline__ uint32_t load_aux(int p) const { return sbase[p]; }
-  // the key; every lane of the candidate's group must call it (DPP sum)
-  __device__ __forceinline__ double key(const u32x4 w, uint32_t aux) const {
-    const int acc = group_sum_i32<N>(dot32_i4(w, qe, qo, 0));
-    return (double)(acc >> 4) * (double)half_bits_to_float((uint16_t)aux) + 0.0;  // -0 -> +0
+  // the integer dot; every lane of the candidate's group must call it (DPP sum)
+  __device__ __forceinline__ int dot(const u32x4 w) const {
+    return group_sum_i32<N>(dot32_i4(w, qe, qo, 0)) >> 4;
   }
+  // the key from the dot: exact in fp64 (at most 19 + 11 significant bits)
+  __device__ __forceinline__ double key_of(int d, uint32_t aux) const {
+    return (double)d * (double)half_bits_to_float((uint16_t)aux) + 0.0;  // -0 -> +0
+  }
+  // the key's 16-bit digit without fp64: the key rounded to fp32 equals the
+  // fp32 product of the (exact) fp32 dot and scale, which is rounded once
+  __device__ __forceinline__ uint32_t digit_of(int d, uint32_t aux) const {
+    return ordered_u32((float)d * half_bits_to_float((uint16_t)aux) + 0.0f) >> 16;
+  }
+  __device__ __forceinline__ double key(const u32x4 w, uint32_t aux) const { return key_of(dot(w), aux); }
 };
 
 // Pooled block source: a candidate is a complete 4-token block whose bf16
@@ -288,6 +298,7 @@ struct SketchSrc {
 template <int N>
 struct PooledSrc {
   static constexpr int LANES = N;
+  static constexpr bool HAS_AUX = false;
   static constexpr int QROW = 16 * N;      // bytes of one sequence's query row
   double qd[8];
   const uint16_t* kb;

@@ -103,10 +103,24 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int i = base + u * IPW + tw;
-      const double key = src.key(w[u], ax[u]);
-      if (!COLLECT) {
+      if constexpr (!COLLECT) {
+        const double key = src.key(w[u], ax[u]);
         if (sub == 0 && i < i1) kout[i] = key;
+      } else if constexpr (Src::HAS_AUX) {
+        // token sketch: the digit from the fp32 product; the exact fp64 key
+        // only for the kept candidates
+        const int dt = src.dot(w[u]);
+        const uint32_t dig = src.digit_of(dt, ax[u]);
+        const bool sel = sub == 0 && i < i1 && dig >= beta;
+        const uint64_t m = __ballot(sel);
+        if (sel) {
+          const uint64_t ok = ordered_u64(src.key_of(dt, ax[u]));
+          const uint32_t rank = cnt + (uint32_t)__popcll(m & lt);
+          cseg[rank] = (u32x4){(uint32_t)ok, (uint32_t)(ok >> 32), (uint32_t)(lo + i), dig};
+        }
+        cnt += (uint32_t)__popcll(m);
       } else {
+        const double key = src.key(w[u], ax[u]);
         const uint32_t dig = key_digit16(key);
         const bool sel = sub == 0 && i < i1 && dig >= beta;
         const uint64_t m = __ballot(sel);
@@ -182,9 +196,10 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(
   for (int u = 0; u < kUnroll; ++u) {
     const int o = u * IPW + tw;
     const int j = j0 + o / kLineKeys;
-    const double key = src.key(w[u], ax[u]);
-    if (sub == 0 && j < nsl)
-      dg[j * kLineKeys + o % kLineKeys] = ok[u] ? (uint16_t)key_digit16(key) : (uint16_t)0u;
+    uint32_t dig;
+    if constexpr (Src::HAS_AUX) dig = src.digit_of(src.dot(w[u]), ax[u]);
+    else dig = key_digit16(src.key(w[u], ax[u]));
+    if (sub == 0 && j < nsl) dg[j * kLineKeys + o % kLineKeys] = ok[u] ? (uint16_t)dig : (uint16_t)0u;
   }
 }
 
