@@ -276,9 +276,11 @@ struct SketchSrc {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cbase + (size_t)p * (16 * N)));
   }
   __device__ __forceinline__ uint32_t load_aux(int p) const { return sbase[p]; }
+  // this lane's share of 16x the integer dot (its 32 codes)
+  __device__ __forceinline__ int partial(const u32x4 w) const { return dot32_i4(w, qe, qo, 0); }
   // the integer dot; every lane of the candidate's group must call it (DPP sum)
   __device__ __forceinline__ int dot(const u32x4 w) const {
-    return group_sum_i32<N>(dot32_i4(w, qe, qo, 0)) >> 4;
+    return group_sum_i32<N>(partial(w)) >> 4;
   }
   // the key from the dot: exact in fp64 (at most 19 + 11 significant bits)
   __device__ __forceinline__ double key_of(int d, uint32_t aux) const {

@@ -59,6 +59,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
     uint32_t* __restrict__ flags, int mode, int max_ctx, int S, int k, int L, int n_seg,
     int seg_items) {
   constexpr int N = Src::LANES, IPW = 64 / N, PER_IT = kUnroll * IPW;
+  constexpr bool TRANS = COLLECT && Src::HAS_AUX && N == 8;   // see the transposed collect below
   const int b = blockIdx.y;
   const int T = clamp_ctx(ctx_len, b, max_ctx, blockIdx.x == 0 ? flags : nullptr);
   int lo, n;
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
     for (int u = 0; u < kUnroll; ++u) {
       const int i = min(base + u * IPW + tw, i1 - 1);
       wv[u] = src.load(lo + i);
-      av[u] = src.load_aux(lo + i);
+      if constexpr (!TRANS) av[u] = src.load_aux(lo + i);
     }
   };
   load_batch(i0, w, ax);
@@ -96,6 +97,67 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
   u32x4* cseg = reinterpret_cast<u32x4*>(cand + ((size_t)b * n_seg + seg) * seg_items);
   const uint64_t lt = lanemask_lt();
   uint32_t cnt = 0;
+  if constexpr (TRANS) {
+    // Transposed collect: the 8 partial dots of a lane (one per load) are
+    // reduced over the 8 lanes of its group by a butterfly (mirror / quad
+    // swaps), which leaves lane (tw, sub) with the whole dot of load sub, i.e.
+    // candidate o = 8*sub + tw of the batch.  Digit, selection and ballot then
+    // run once per batch, and the ballot is transposed (8x8 bits) into
+    // candidate order for the ranks.  Each lane reads the scale of its own
+    // candidate.
+    const int o = 8 * sub + tw;
+    uint32_t sc = src.load_aux(lo + min(i0 + o, i1 - 1));
+    const uint32_t b2 = (sub >> 2) & 1, b1 = (sub >> 1) & 1, b0 = sub & 1;
+    const uint64_t below = (1ull << o) - 1ull;
+    for (int base = i0; base < i1; base += PER_IT) {
+      u32x4 wn[kUnroll];
+      uint32_t scn = 0;
+      if (base + PER_IT < i1) {   // next batch in flight
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) wn[u] = src.load(lo + min(base + PER_IT + u * IPW + tw, i1 - 1));
+        scn = src.load_aux(lo + min(base + PER_IT + o, i1 - 1));
+      }
+      int p[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) p[u] = src.partial(w[u]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {   // partner 7 - sub: opposite bit 2
+        const int keep = b2 ? p[j + 4] : p[j], send = b2 ? p[j] : p[j + 4];
+        p[j] = keep + (int)dpp_u32<0x141>((uint32_t)send);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {   // partner sub ^ 2
+        const int keep = b1 ? p[j + 2] : p[j], send = b1 ? p[j] : p[j + 2];
+        p[j] = keep + (int)dpp_u32<0x4E>((uint32_t)send);
+      }
+      {                               // partner sub ^ 1
+        const int keep = b0 ? p[1] : p[0], send = b0 ? p[0] : p[1];
+        p[0] = keep + (int)dpp_u32<0xB1>((uint32_t)send);
+      }
+      const int dt = p[0] >> 4;
+      const int i = base + o;
+      const uint32_t dig = src.digit_of(dt, sc);
+      const bool sel = i < i1 && dig >= beta;
+      uint64_t x = __ballot(sel);   // bit 8*tw + sub
+      uint64_t t = (x ^ (x >> 7)) & 0x00AA00AA00AA00AAull;
+      x = x ^ t ^ (t << 7);
+      t = (x ^ (x >> 14)) & 0x0000CCCC0000CCCCull;
+      x = x ^ t ^ (t << 14);
+      t = (x ^ (x >> 28)) & 0x00000000F0F0F0F0ull;
+      x = x ^ t ^ (t << 28);          // bit o = 8*sub + tw
+      if (sel) {
+        const uint64_t ok = ordered_u64(src.key_of(dt, sc));
+        const uint32_t rank = cnt + (uint32_t)__popcll(x & below);
+        cseg[rank] = (u32x4){(uint32_t)ok, (uint32_t)(ok >> 32), (uint32_t)(lo + i), dig};
+      }
+      cnt += (uint32_t)__popcll(x);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) w[u] = wn[u];
+      sc = scn;
+    }
+    if (lane == 0) segcnt[(size_t)b * n_seg + seg] = cnt;
+    return;
+  }
   for (int base = i0; base < i1; base += PER_IT) {
     u32x4 wn[kUnroll];
     uint32_t an[kUnroll];
