@@ -107,6 +107,45 @@ def test_empty_and_tiny_sequences():
     assert not g["out"][0].any()
 
 
+@pytest.mark.parametrize("fused", [True, False])
+def test_other_head_shapes(fused):
+    """Sketch widths other than the cfg-2 one: 2 KV heads (64-byte rows, 4
+    lanes per token) with 16 query heads each, and 8 KV heads (256-byte rows,
+    16 lanes per token) with one query head each, fp16 K/V at head_dim 128."""
+    skv = need_gpu()
+    sm = 0.0625
+    c = synth.make_token_case(2, 30_000, [30_000, 21_111], n_kv=2, n_q=32, D=256, S=16, k=512,
+                              L=256, kv_format="i8", seed=71)
+    say("2 KV x 16 q heads, fused", fused)
+    g = run_token_gpu(skv, c, sm, fused=fused)
+    _check_token(c, g, oracle_token(c, sm))
+    c = synth.make_token_case(2, 30_000, [30_000, 9_999], n_kv=8, n_q=8, D=128, S=8, k=1024,
+                              L=64, kv_format="f16", seed=72)
+    say("8 KV x 1 q head, fused", fused)
+    g = run_token_gpu(skv, c, sm, fused=fused)
+    _check_token(c, g, oracle_token(c, sm))
+
+
+def test_largest_context_and_budget():
+    """The largest supported context (2,097,152 tokens: 8192 segments of 256)
+    with the largest budget (k = 4096), cfg-2 layer shape, one sequence."""
+    skv = need_gpu()
+    T = 2_097_152
+    say("largest context: generating 1 x", T)
+    c = synth.make_token_case(1, T, None, n_kv=4, n_q=24, D=256, S=64, k=4096, L=1024,
+                              kv_format="i8", seed=73, device="cuda")
+    sm = 256 ** -0.5
+    g = run_token_gpu(skv, c, sm, fused=True)
+    say("largest context: oracle")
+    o = oracle_token(c, sm)
+    err = _check_token(c, g, o)
+    assert g["n_sel"].tolist() == [64 + 4096 + 1024]
+    # at this budget the candidates can outnumber the 8192 the fast select
+    # holds; the exact slower path then runs and raises the informational flag
+    assert g["flags"] & ~skv.SKV_FLAG_TOPK_SLOW == 0
+    say("largest context max err", err, "flags", g["flags"])
+
+
 def test_topk_ties_and_degenerate_keys():
     """Keys fed straight to sparsekv_topk: many exact ties, all-equal keys (the
     exact slow path), negative keys, and a single huge key."""
