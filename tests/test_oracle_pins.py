@@ -472,3 +472,81 @@ def test_drift_miss_rate_matches_pages():
             picks_total += h + m
     rate = misses / picks_total
     assert 0.13 <= rate <= 0.17, rate
+
+
+# --------------------------------------------------------------------------
+# append: the new token's int8 K/V rows and int4 key sketch
+# --------------------------------------------------------------------------
+
+def _kv(ln):
+    return dict(f.split("=", 1) for f in ln.split()[1:])
+
+
+def test_append_fixture():
+    for ln in _lines("append_rows.txt"):
+        f = _kv(ln)
+        if ln.startswith("row "):
+            x = np.array([float(v) for v in f["x"].split(",")], dtype=np.float16)[None]
+            codes, s16 = oracle.append.row_i8(x)
+            assert int(s16.view(np.uint16)[0]) == int(f["scale"], 16), ln
+            assert codes[0].tolist() == [int(v) for v in f["codes"].split(",")], ln
+        else:
+            k = np.array([float(v) for v in f["k"].split(",")], dtype=np.float16)[None]
+            cols = [int(v) for v in f["cols"].split(",")]
+            basis = np.zeros((1, k.shape[1], len(cols)), dtype=np.float32)
+            for r, c in enumerate(cols):
+                basis[0, c, r] = 1.0
+            packed, s16 = oracle.append.key_sketch(k, basis)
+            assert int(np.array([s16]).view(np.uint16)[0]) == int(f["scale"], 16), ln
+            assert packed.tolist() == [int(f["bytes"], 16)], ln
+
+
+def test_append_row_invariants():
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((200, 256)) * rng.uniform(0.01, 30, (200, 1))).astype(np.float16)
+    codes, s16 = oracle.append.row_i8(x)
+    s = s16.astype(np.float64)
+    xf = x.astype(np.float64)
+    assert np.abs(codes).max() <= 127
+    # the largest element lands on +-127 (up to the fp16 rounding of the scale)
+    big = np.abs(codes[np.arange(200), np.abs(xf).argmax(axis=1)])
+    assert (big >= 126).all()
+    off = np.abs(codes) < 127
+    err = np.abs(xf - s[:, None] * codes)
+    assert (err[off] <= 0.5 * np.broadcast_to(s[:, None], err.shape)[off] * (1 + 1e-6)).all()
+
+
+def test_append_sketch_projection_bound():
+    """The fp32 projection stays within the fp32 rounding bound of the fp64
+    projection, and the int4 codes round-trip through oracle.unpack_int4."""
+    rng = np.random.default_rng(6)
+    basis = synth.orthonormal_basis(4, 256, 64, 9).numpy().astype(np.float32)
+    for _ in range(5):
+        k = rng.standard_normal((4, 256)).astype(np.float16)
+        packed, s16 = oracle.append.key_sketch(k, basis)
+        c = oracle.unpack_int4(packed[None])[0].astype(np.float64)
+        v64 = np.einsum("hd,hdr->hr", k.astype(np.float64), basis.astype(np.float64)).reshape(-1)
+        s = float(s16)
+        assert s > 0 and np.abs(c).max() == 7
+        # |v - s*c| <= s/2 + the fp32 accumulation error of 256 terms
+        bound = 0.5 * s + 256 * 2.0 ** -23 * np.abs(k.astype(np.float64)).sum(axis=1).max()
+        assert np.abs(v64 - s * c).max() <= bound * (1 + 1e-9)
+
+
+def test_append_bookkeeping():
+    B, T, Hkv, D, R = 3, 10, 2, 8, 4
+    rng = np.random.default_rng(7)
+    caches = dict(codes=np.zeros((B, T, Hkv * R // 2), np.uint8), sk_scale=np.zeros((B, T), np.float16),
+                  k=np.zeros((B, T, Hkv, D), np.int8), v=np.zeros((B, T, Hkv, D), np.int8),
+                  k_scale=np.zeros((B, T, Hkv), np.float16), v_scale=np.zeros((B, T, Hkv), np.float16))
+    before = {n: a.copy() for n, a in caches.items()}
+    basis = rng.standard_normal((Hkv, D, R)).astype(np.float32)
+    kn = rng.standard_normal((B, Hkv, D)).astype(np.float16)
+    vn = rng.standard_normal((B, Hkv, D)).astype(np.float16)
+    ctx = oracle.append.append_tokens(np.array([0, 4, T]), kn, vn, basis, caches, T)
+    assert ctx.tolist() == [1, 5, T]
+    for n, a in caches.items():
+        changed = np.argwhere((a != before[n]).reshape(B, T, -1).any(axis=2))
+        assert set(map(tuple, changed.tolist())) <= {(0, 0), (1, 4)}, n
+    kq, ks = oracle.append.row_i8(kn[1])
+    assert np.array_equal(caches["k"][1, 4], kq) and np.array_equal(caches["k_scale"][1, 4], ks)
