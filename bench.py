@@ -435,6 +435,24 @@ def main():
             fn(layers[i % n_layers], ws)
         kt[name] = time_loop(fn, layers, ws, nk) / nk
     skv.check(ws)
+    if cfg["kind"] == "token":
+        # the decode-step append (new token's K/V rows and key sketch), written
+        # 2000 rows before the end so every call lands inside the cache; runs
+        # after the step timings because it overwrites cache rows
+        L0 = layers[0]
+        c0 = L0.case
+        g = torch.Generator(device="cuda").manual_seed(7)
+        k_new = torch.randn((c0.B, c0.n_kv, c0.D), generator=g, device="cuda").to(torch.float16)
+        v_new = torch.randn((c0.B, c0.n_kv, c0.D), generator=g, device="cuda").to(torch.float16)
+        ctx_a = (L0.ctx - 2000).clamp(min=0).to(torch.int32).contiguous()
+
+        def append_call(layer, ws_):
+            skv.append(layer.desc, ctx_a, k_new, v_new, layer.basis, layer.kv, layer.ikeys,
+                       layer.iscale, ws_)
+        for _ in range(5):
+            append_call(L0, ws)
+        kt["append"] = time_loop(append_call, [L0], ws, nk) / nk
+        skv.check(ws)
     ab = algorithmic_bytes(cfg, layers[0].case.lens if cfg["kind"] == "token" else None)
     value = args.steps / secs
     # the dominant kernel of the step: the fused score-and-collect stream

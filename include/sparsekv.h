@@ -232,6 +232,30 @@ skv_status sparsekv_step(const skv_layer_desc* d, const int32_t* ctx_len, const 
                          int32_t* n_sel, float sm_scale, float* out, void* ws, size_t ws_bytes,
                          void* stream);
 
+/* ---- append: the new token of every sequence into the caches ---------------
+ * Page "8 agents x 250K ...", section "The mechanism" (int8 K/V rows with a
+ * per-row scale, int4 rank-64 key sketch with one fp16 scale per token); page
+ * "3.14M Context ...", section "No Need to Rewrite the Kernel" (the paged cache
+ * update writes the new rows in place each step).  Token mode only.
+ *   ctx_len     [B] int32, read and written: the token goes to row ctx_len[b]
+ *               of sequence b, then ctx_len[b] += 1; a sequence already at
+ *               max_ctx is left unchanged and raises SKV_FLAG_CTX_RANGE
+ *   k_new,v_new [B][H_kv][D] fp16: the new token's key and value rows
+ *   basis       [H_kv][D][R] fp32, the frozen sketch basis
+ *   kv          the cache (rows >= max_ctx): int8 rows + fp16 row scales,
+ *               scale = fp16(fp32(amax/127)), code = clamp(rint(x/scale), +-127)
+ *               (zero row -> scale 0); fp16 K/V caches get the rows as they are
+ *   index_keys  [B][max_ctx][H_kv*R/2] u8, index_scale [B][max_ctx] fp16: the
+ *               sketch v[h*R+r] = sum over d ascending of k_h[d]*B_h[d][r]
+ *               (fp32, no fused multiply-add), scale fp16(fp32(amax/7)) over
+ *               all H_kv*R values, codes clamp(rint(v/scale), +-7), element 2j
+ *               in the low nibble of byte j
+ * Quotients are correctly rounded fp32.  Uses the workspace's flag word only. */
+skv_status sparsekv_append(const skv_layer_desc* d, int32_t* ctx_len, const void* k_new,
+                           const void* v_new, const float* basis, const skv_kv_view* kv,
+                           void* index_keys, uint16_t* index_scale, void* ws, size_t ws_bytes,
+                           void* stream);
+
 /* Synchronizes `stream`, returns the device flag bits raised since the last
  * check in *flags (may be NULL) and clears them.  SKV_ERR_STATE if any bit
  * other than SKV_FLAG_TOPK_SLOW was set.  Not capturable. */

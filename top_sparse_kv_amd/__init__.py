@@ -143,6 +143,15 @@ def step(desc, ctx_len, q, basis, qs, qs_scale, index_query, index_keys, index_s
                                _p(ws), ws.numel(), _stream(stream)))
 
 
+def append(desc, ctx_len, k_new, v_new, basis, kv: KVView, index_keys, index_scale, ws, stream=None):
+    """Writes the new token of every sequence at row ctx_len[b] (K/V rows,
+    key sketch) and advances ctx_len (sparsekv_append)."""
+    _dev(ctx_len, k_new, v_new, basis, index_keys, index_scale, ws)
+    _check(lib().sparsekv_append(ctypes.byref(desc), _p(ctx_len), _p(k_new), _p(v_new), _p(basis),
+                                 ctypes.byref(kv), _p(index_keys), _p(index_scale), _p(ws), ws.numel(),
+                                 _stream(stream)))
+
+
 def timer_enable(on: bool = True):
     """Diagnostic: bracket each launch of the streaming score kernel with events."""
     _check(lib().sparsekv_timer_enable(1 if on else 0))
@@ -155,13 +164,14 @@ def timer_read():
     return ms.value, n.value
 
 
-def check(ws, stream=None) -> int:
-    """Synchronizes, returns and clears the device flag bits; raises on error flags."""
+def check(ws, stream=None, raise_on_error: bool = True) -> int:
+    """Synchronizes, returns and clears the device flag bits; raises on error
+    flags unless raise_on_error is False."""
     f = _lib.c_u32()
     st = lib().sparsekv_check(_p(ws), ws.numel(), _stream(stream), ctypes.byref(f))
     if st not in (0, 7):
         _check(st)
-    if st == 7:
+    if st == 7 and raise_on_error:
         raise SkvError(st, "device flags 0x%x" % f.value)
     return f.value
 

@@ -268,6 +268,26 @@ skv_status sparsekv_step(const skv_layer_desc* d, const int32_t* ctx_len, const 
   return launched(e, "step");
 }
 
+skv_status sparsekv_append(const skv_layer_desc* d, int32_t* ctx_len, const void* k_new,
+                           const void* v_new, const float* basis, const skv_kv_view* kv,
+                           void* index_keys, uint16_t* index_scale, void* ws, size_t ws_bytes,
+                           void* stream) {
+  skv_status s = validate_desc(d);
+  if (s != SKV_OK) return s;
+  if (d->index_mode != SKV_INDEX_SKETCH_INT4)
+    return set_error(SKV_ERR_UNSUPPORTED, "append: token mode only");
+  WsLayout L;
+  if ((s = check_ws(d, ws, ws_bytes, &L)) != SKV_OK) return s;
+  if ((s = check_kv(d, kv)) != SKV_OK) return s;
+  if (!ctx_len || !k_new || !v_new || !basis || !index_keys || !index_scale)
+    return set_error(SKV_ERR_INVALID, "append: NULL pointer");
+  if (kv->rows < d->max_ctx)
+    return set_error(SKV_ERR_INVALID, "append: kv rows %lld < max_ctx %d", (long long)kv->rows, d->max_ctx);
+  return launched(launch_append(*d, ctx_len, k_new, v_new, basis, *kv, index_keys, index_scale, ws, L,
+                                (hipStream_t)stream),
+                  "append");
+}
+
 skv_status sparsekv_timer_enable(int enable) {
   if (enable && g_timer.ev.empty()) {
     g_timer.ev.resize(2 * kTimerPairs);

@@ -1,0 +1,151 @@
+// The decode-step append: the new token of every sequence is written into the
+// caches the step reads.
+//
+// Page "8 agents x 250K context on two 3090s: sparse KV decode with a rank-64
+// key sketch and a host-RAM tier", section "The mechanism": every token has
+// int8 K/V rows with a per-row scale and an int4 rank-64 sketch of its keys on
+// a frozen basis with one fp16 scale.  Page "3.14M Context on 3x 3090: The
+// Power of an Architecture That Puts KV Cache in Host RAM", section "No Need
+// to Rewrite the Kernel": the paged cache update writes the new rows in place
+// each step.
+//
+// Encodings (the pages give none; the plainest rounding, in a fixed fp32
+// order so the integer codes are reproducible bit for bit):
+//   int8 row   scale = fp16(fp32(amax / 127)), codes = clamp(rint(x / scale), +-127)
+//   key sketch v[h*R + r] = sum over d ascending of k_h[d] * B_h[d][r] (fp32,
+//              product and sum rounded separately); scale = fp16(fp32(amax / 7))
+//              over all H_kv*R values; codes clamp(rint(v / scale), +-7), element
+//              2j in the low nibble of byte j
+//   position   row ctx_len[b], then ctx_len[b] += 1 (a full sequence is left as
+//              it is and flagged)
+// Quotients are computed in fp64 and rounded once, which is the correctly
+// rounded fp32 quotient.
+//
+// One workgroup of 512 threads per sequence: the 2*H_kv rows go to the waves
+// (a row's amax by a DPP max over the wave), then thread i computes sketch
+// value i from the K rows staged in LDS.
+#include "keys_common.h"
+
+namespace skv {
+namespace {
+
+constexpr int kAppThreads = 512;
+constexpr int kAppMaxHkv = 32;   // H_kv * R <= 512 with R >= 16
+
+__device__ __forceinline__ float quot_rn(float a, float c) { return (float)((double)a / (double)c); }
+
+template <int D, bool I8>
+__global__ __launch_bounds__(kAppThreads) void append_kernel(
+    int32_t* __restrict__ ctx_len, const __half* __restrict__ k_new, const __half* __restrict__ v_new,
+    const float* __restrict__ basis, uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
+    uint16_t* __restrict__ ksc, uint16_t* __restrict__ vsc, int64_t rows,
+    uint8_t* __restrict__ codes, uint16_t* __restrict__ sk_scale, int Hkv, int R, int max_ctx,
+    uint32_t* __restrict__ flags) {
+#pragma clang fp contract(off)
+  constexpr int PL = D / 64;   // row values per lane
+  __shared__ float s_k[kAppMaxHkv * D];
+  __shared__ int8_t s_c[kAppThreads];
+  __shared__ uint32_t s_red[16];
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = kAppThreads / 64;
+  const int t = ctx_len[b];
+  if (t < 0 || t >= max_ctx) {   // the same t in every thread: the whole workgroup leaves
+    if (threadIdx.x == 0) raise_flag(flags, SKV_FLAG_CTX_RANGE);
+    return;
+  }
+  // ---- K and V rows: wave w takes rows w, w + nw, ... (K rows first) ----
+  for (int row = wave; row < 2 * Hkv; row += nw) {
+    const bool isv = row >= Hkv;
+    const int h = isv ? row - Hkv : row;
+    const __half* src = (isv ? v_new : k_new) + ((size_t)b * Hkv + h) * D + lane * PL;
+    float x[PL];
+#pragma unroll
+    for (int e = 0; e < PL; ++e) x[e] = __half2float(src[e]);
+    if (!isv) {
+#pragma unroll
+      for (int e = 0; e < PL; ++e) s_k[h * D + lane * PL + e] = x[e];
+    }
+    const size_t rr = ((size_t)b * rows + t) * Hkv + h;   // cache row of (b, t, h)
+    if constexpr (I8) {
+      float am = 0.0f;
+#pragma unroll
+      for (int e = 0; e < PL; ++e) am = fmaxf(am, fabsf(x[e]));
+      am = __uint_as_float(wave_max(__float_as_uint(am)));   // non-negative: bit order = value order
+      const __half s16 = __float2half_rn(quot_rn(am, 127.0f));
+      const float s = __half2float(s16);
+      uint32_t packed = 0;
+#pragma unroll
+      for (int e = 0; e < PL; ++e) {
+        const float q = s > 0.0f ? fminf(fmaxf(rintf(quot_rn(x[e], s)), -127.0f), 127.0f) : 0.0f;
+        packed |= (uint32_t)(uint8_t)(int8_t)(int)q << (8 * e);
+      }
+      uint8_t* dst = (isv ? vc : kc) + rr * D + lane * PL;
+      if constexpr (PL == 4) *reinterpret_cast<uint32_t*>(dst) = packed;
+      else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)packed;
+      if (lane == 0) (isv ? vsc : ksc)[rr] = __half_as_ushort(s16);
+    } else {
+      __half* dst = reinterpret_cast<__half*>(isv ? vc : kc) + rr * D + lane * PL;
+#pragma unroll
+      for (int e = 0; e < PL; ++e) dst[e] = src[e];
+    }
+  }
+  __syncthreads();
+  // ---- key sketch: thread i computes value i = h*R + r ----
+  const int n = Hkv * R;
+  const int i = threadIdx.x;
+  float v = 0.0f;
+  if (i < n) {
+    const int h = i / R, r = i % R;
+    const float* bp = basis + (size_t)h * D * R + r;
+    const float* kp = s_k + h * D;
+    for (int d0 = 0; d0 < D; d0 += 16) {
+      float bv[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) bv[u] = bp[(size_t)(d0 + u) * R];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v = v + kp[d0 + u] * bv[u];
+    }
+  }
+  uint32_t am = i < n ? __float_as_uint(fabsf(v)) : 0u;
+  am = wave_max(am);
+  if (lane == 0) s_red[wave] = am;
+  __syncthreads();
+  const float amax = __uint_as_float(lds_max16(s_red, nw));
+  const __half s16 = __float2half_rn(quot_rn(amax, 7.0f));
+  const float s = __half2float(s16);
+  if (i < n) s_c[i] = (int8_t)(int)(s > 0.0f ? fminf(fmaxf(rintf(quot_rn(v, s)), -7.0f), 7.0f) : 0.0f);
+  __syncthreads();
+  if (i < n / 2) {
+    const uint32_t lo = (uint32_t)s_c[2 * i] & 0xFu, hi = (uint32_t)s_c[2 * i + 1] & 0xFu;
+    codes[((size_t)b * max_ctx + t) * (n / 2) + i] = (uint8_t)(lo | (hi << 4));
+  }
+  if (threadIdx.x == 0) {
+    sk_scale[(size_t)b * max_ctx + t] = __half_as_ushort(s16);
+    ctx_len[b] = t + 1;   // every thread read t before the barriers above
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(const skv_layer_desc& d, int32_t* ctx_len, const void* k_new,
+                         const void* v_new, const float* basis, const skv_kv_view& kv,
+                         void* index_keys, uint16_t* index_scale, void* ws, const WsLayout& L,
+                         hipStream_t st) {
+  uint32_t* flags = ws_ptr<uint32_t>(ws, L.flags);
+  const bool i8 = d.kv_dtype == SKV_KV_I8_ROWSCALE;
+  if (d.n_kv_heads > kAppMaxHkv || d.n_kv_heads * d.rank > kAppThreads) return hipErrorInvalidValue;
+#define SKV_AP(DD, I8)                                                                           \
+  hipLaunchKernelGGL((append_kernel<DD, I8>), dim3(d.batch), dim3(kAppThreads), 0, st, ctx_len,  \
+                     (const __half*)k_new, (const __half*)v_new, basis, (uint8_t*)kv.k,           \
+                     (uint8_t*)kv.v, (uint16_t*)kv.k_scale, (uint16_t*)kv.v_scale, kv.rows,       \
+                     (uint8_t*)index_keys, index_scale, d.n_kv_heads, d.rank, d.max_ctx, flags)
+  if (d.head_dim == 256 && i8) SKV_AP(256, true);
+  else if (d.head_dim == 256) SKV_AP(256, false);
+  else if (d.head_dim == 128 && i8) SKV_AP(128, true);
+  else if (d.head_dim == 128) SKV_AP(128, false);
+  else return hipErrorInvalidValue;
+#undef SKV_AP
+  return hipGetLastError();
+}
+
+}  // namespace skv
