@@ -113,3 +113,59 @@ PINS = {
     "key_sketch": "unit-column basis copies coordinates (hand fixture), fp64 projection within the fp32 rounding bound, nibble round trip through oracle.unpack_int4",
     "append_tokens": "row and ctx_len bookkeeping on a toy cache: only row ctx_len[b] changes, full sequences untouched",
 }
+
+
+# ----------------------------------------------------------------------------
+# block mode: bf16 K/V rows, pooled indexer key when a 4-token block completes
+# ----------------------------------------------------------------------------
+# Page "3.14M Context on 3x 3090 ...", sections "Why" and "What Needs to Stay
+# in VRAM": the indexer key of a 4-token block is the mean of its tokens' raw
+# indexer keys (compress ratio 4), stored as bf16.  Reading: the sum of the
+# four bf16 raw keys is exact (fp64), divided by 4 (exact), rounded to bf16
+# (nearest even), then kept in the domain the scores are exact in: 0 when its
+# magnitude is below 2^-8, clamped to +-255.
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float64 -> bf16 bit patterns, round to nearest even (via fp32, exact
+    for the values used here: fp64 -> fp32 is exact for sums of four bf16)."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def pooled_from_raw(raw4: np.ndarray) -> np.ndarray:
+    """raw4: bf16 bit patterns [4][index_dim] -> pooled key bf16 bits [index_dim]."""
+    from .step import bf16_to_f64
+    m = bf16_to_f64(raw4).sum(axis=0) / 4.0
+    y = bf16_to_f64(bf16_bits(m))
+    y = np.where(np.abs(y) < 2.0 ** -8, 0.0, y)
+    y = np.clip(y, -255.0, 255.0)
+    return bf16_bits(y)
+
+
+def append_block_tokens(ctx_len, k_new, v_new, raw_new, stage, caches, max_ctx):
+    """Block mode: writes the bf16 K/V rows (bit patterns) of the new token,
+    puts its raw indexer key (bf16 bits [B][index_dim]) in stage[b][t % 4] and,
+    when t % 4 == 3, the pooled key of block t // 4 into caches['kp'];
+    returns the new ctx_len.  stage (uint16 [B][4][index_dim]) is updated in
+    place; caches: 'k', 'v' uint16 [B][max_ctx][H_kv][D], 'kp' uint16
+    [B][max_ctx // 4][index_dim]."""
+    ctx = np.asarray(ctx_len, dtype=np.int64).copy()
+    for b in range(ctx.size):
+        t = int(ctx[b])
+        if t < 0 or t >= max_ctx:
+            continue
+        caches["k"][b, t] = k_new[b]
+        caches["v"][b, t] = v_new[b]
+        stage[b, t % 4] = raw_new[b]
+        if t % 4 == 3:
+            caches["kp"][b, t // 4] = pooled_from_raw(stage[b])
+        ctx[b] = t + 1
+    return ctx.astype(np.int32)
+
+
+PINS.update({
+    "pooled_from_raw": "hand-worked fixture (exact mean, round to even, flush below 2^-8, clamp at 255), agreement with an exact-fraction mean",
+    "append_block_tokens": "staging slot t % 4, pooled key only on t % 4 == 3, full sequences untouched",
+})

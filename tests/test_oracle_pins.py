@@ -550,3 +550,61 @@ def test_append_bookkeeping():
         assert set(map(tuple, changed.tolist())) <= {(0, 0), (1, 4)}, n
     kq, ks = oracle.append.row_i8(kn[1])
     assert np.array_equal(caches["k"][1, 4], kq) and np.array_equal(caches["k_scale"][1, 4], ks)
+
+
+def _bf16_bits_torch(vals):
+    return torch.tensor(vals, dtype=torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_pooled_key_fixture():
+    for ln in _lines("append_rows.txt"):
+        if not ln.startswith("pool "):
+            continue
+        f = _kv(ln)
+        raw = _bf16_bits_torch([float(v) for v in f["raw"].split(",")])
+        raw4 = np.repeat(raw[:, None], 3, axis=1)          # 3 identical columns
+        got = oracle.append.pooled_from_raw(raw4)
+        assert got.tolist() == [int(f["bits"], 16)] * 3, ln
+
+
+def test_pooled_key_exact_mean():
+    """Against an exact-fraction mean rounded to nearest-even bf16 by hand."""
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((4, 512)) * rng.choice([0.01, 1.0, 50.0], (4, 512))
+    raw = _bf16_bits_torch(x.ravel().tolist()).reshape(4, 512)
+    got = oracle.append.pooled_from_raw(raw)
+    vals = oracle.bf16_to_f64(raw)
+    for i in range(512):
+        m = sum(Fraction(float(v)) for v in vals[:, i]) / 4
+        # nearest bf16 by exhaustive neighbour search around the fp64 value
+        t = torch.tensor([float(m)], dtype=torch.float64)
+        c0 = t.to(torch.float32).to(torch.bfloat16).to(torch.float64).item()
+        ulp = 2.0 ** (np.floor(np.log2(abs(c0))) - 7) if c0 != 0 else 2.0 ** -133
+        cands = [c0 - ulp, c0, c0 + ulp]
+        best = min(cands, key=lambda c: (abs(Fraction(c) - m), int(torch.tensor([c]).to(torch.bfloat16).view(torch.int16).item()) & 1))
+        want = 0.0 if abs(best) < 2.0 ** -8 else max(-255.0, min(255.0, best))
+        assert oracle.bf16_to_f64(got[i:i + 1])[0] == want, (i, float(m), best)
+
+
+def test_append_block_bookkeeping():
+    B, T, Hkv, D, ID = 2, 12, 1, 4, 8
+    rng = np.random.default_rng(9)
+    caches = dict(k=np.zeros((B, T, Hkv, D), np.uint16), v=np.zeros((B, T, Hkv, D), np.uint16),
+                  kp=np.zeros((B, T // 4, ID), np.uint16))
+    stage = np.zeros((B, 4, ID), np.uint16)
+    ctx = np.array([1, T])
+    raws = []
+    for step in range(3):
+        kn = rng.integers(0, 1 << 15, (B, Hkv, D)).astype(np.uint16)
+        vn = rng.integers(0, 1 << 15, (B, Hkv, D)).astype(np.uint16)
+        raw = _bf16_bits_torch(rng.standard_normal(B * ID).tolist()).reshape(B, ID)
+        raws.append(raw[0].copy())
+        ctx = oracle.append.append_block_tokens(ctx, kn, vn, raw, stage, caches, T)
+        assert np.array_equal(caches["k"][0, step + 1], kn[0])
+        assert not caches["k"][1].any()                       # full sequence untouched
+        if step < 2:
+            assert not caches["kp"][0].any()                  # block 0 not complete yet
+    assert ctx.tolist() == [4, T]
+    # block 0 = tokens 0..3: slot 0 was never written in this test (zeros), 1..3 from the steps
+    want = oracle.append.pooled_from_raw(np.stack([np.zeros(ID, np.uint16)] + raws))
+    assert np.array_equal(caches["kp"][0, 0], want)
