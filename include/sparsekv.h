@@ -256,6 +256,25 @@ skv_status sparsekv_append(const skv_layer_desc* d, int32_t* ctx_len, const void
                            void* index_keys, uint16_t* index_scale, void* ws, size_t ws_bytes,
                            void* stream);
 
+/* Block mode (page "3.14M Context ...", sections "Why" and "What Needs to
+ * Stay in VRAM": a 4-token block's indexer key is the mean of its tokens' raw
+ * indexer keys, bf16).
+ *   ctx_len      [B] int32, read and written as in sparsekv_append
+ *   k_new,v_new  [B][H_kv][D] bf16, stored as they are in the bf16 cache kv
+ *   index_raw    [B][index_dim] bf16: the new token's raw indexer key
+ *   index_stage  [B][4][index_dim] bf16, caller-owned and kept per layer
+ *                across steps: row t % 4 receives the raw key of token t
+ *                (after a prefill that ends inside a block it must hold that
+ *                block's raw keys)
+ *   index_keys   [B][max_ctx/4][index_dim] bf16: when t % 4 == 3 the pooled
+ *                key of block t/4 = the exact mean of the four staged keys,
+ *                rounded to nearest-even bf16, 0 below 2^-8 in magnitude,
+ *                clamped to +-255 (the domain in which scores are exact) */
+skv_status sparsekv_append_block(const skv_layer_desc* d, int32_t* ctx_len, const void* k_new,
+                                 const void* v_new, const void* index_raw, void* index_stage,
+                                 const skv_kv_view* kv, void* index_keys, void* ws,
+                                 size_t ws_bytes, void* stream);
+
 /* Synchronizes `stream`, returns the device flag bits raised since the last
  * check in *flags (may be NULL) and clears them.  SKV_ERR_STATE if any bit
  * other than SKV_FLAG_TOPK_SLOW was set.  Not capturable. */

@@ -126,12 +126,14 @@ PINS = {
 # magnitude is below 2^-8, clamped to +-255.
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
-    """float64 -> bf16 bit patterns, round to nearest even (via fp32, exact
-    for the values used here: fp64 -> fp32 is exact for sums of four bf16)."""
-    f = np.asarray(x, dtype=np.float64).astype(np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return r.astype(np.uint16)
+    """float64 (finite, within the fp32 exponent range) -> bf16 bit patterns,
+    rounded once to nearest even: the fp64 significand is rounded to bf16's 8
+    bits directly on the bit pattern, after which the conversion to fp32 and
+    the truncation to the top 16 bits are exact."""
+    u = np.asarray(x, dtype=np.float64).view(np.uint64)
+    u = ((u + np.uint64((1 << 44) - 1) + ((u >> np.uint64(45)) & np.uint64(1))) >> np.uint64(45)) << np.uint64(45)
+    f = u.view(np.float64).astype(np.float32)
+    return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
 def pooled_from_raw(raw4: np.ndarray) -> np.ndarray:

@@ -106,3 +106,52 @@ def test_step_after_append():
     sm = 256 ** -0.5
     gs = run_token_gpu(skv, c, sm, fused=True)
     _check_token(c, gs, oracle_token(c, sm))
+
+
+def _u16(t):
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def test_append_block_mode():
+    """Block mode: seven appends to a sequence that starts inside a block
+    (two blocks complete), one full sequence; every byte against the oracle,
+    then a step over the appended caches."""
+    from gpu_util import block_desc_of, oracle_block, run_block_gpu
+    from test_gpu_parity import _cfg3
+    skv = need_gpu()
+    c = _cfg3(2, 4096, [2049, 4096])
+    desc = block_desc_of(skv, c)
+    ws = skv.workspace(desc)
+    kc, vc, kp = c.k_cache.cuda().clone(), c.v_cache.cuda().clone(), c.kp.cuda().clone()
+    stage = torch.zeros((2, 4, c.index_dim), dtype=torch.bfloat16, device="cuda")
+    ctx = c.ctx_len.cuda().clone()
+    kv = skv.kv_view(kc, vc)
+    o = dict(k=_u16(c.k_cache).copy(), v=_u16(c.v_cache).copy(), kp=_u16(c.kp).copy())
+    ostage = np.zeros((2, 4, c.index_dim), np.uint16)
+    octx = c.ctx_len.numpy()
+    g = torch.Generator().manual_seed(92)
+    flags = 0
+    for step in range(7):
+        kn = torch.randn((2, c.n_kv, c.D), generator=g).to(torch.bfloat16)
+        vn = torch.randn((2, c.n_kv, c.D), generator=g).to(torch.bfloat16)
+        raw = (torch.randn((2, c.index_dim), generator=g) * 3).to(torch.bfloat16)
+        skv.append_block(desc, ctx, kn.cuda(), vn.cuda(), raw.cuda(), stage, kv, kp, ws)
+        flags |= skv.check(ws, raise_on_error=False)
+        octx = oracle.append.append_block_tokens(octx, _u16(kn), _u16(vn), _u16(raw), ostage, o, c.T_max)
+        assert ctx.cpu().tolist() == octx.tolist()
+        assert np.array_equal(_u16(kc.cpu()), o["k"]) and np.array_equal(_u16(vc.cpu()), o["v"])
+        assert np.array_equal(_u16(kp.cpu()), o["kp"]), "pooled keys, step %d" % step
+        assert np.array_equal(_u16(stage.cpu()), ostage)
+    assert octx.tolist() == [2056, 4096] and flags == skv.SKV_FLAG_CTX_RANGE
+    assert o["kp"][0, 512].any() and o["kp"][0, 513].any()
+    c.k_cache, c.v_cache, c.kp = kc.cpu(), vc.cpu(), kp.cpu()
+    c.ctx_len = torch.from_numpy(octx.astype(np.int32))
+    c.lens = octx.tolist()
+    sm = 256 ** -0.5
+    gs = run_block_gpu(skv, c, sm, fused=True)
+    os_ = oracle_block(c, sm)
+    from gpu_util import compare_keys, compare_out, compare_sel
+    for b in range(2):
+        compare_keys(gs["keys"], os_["keys"], b, 0, c.lens[b] // 4)
+        compare_sel(gs, os_, b)
+        compare_out(gs, os_, b)

@@ -152,6 +152,17 @@ def append(desc, ctx_len, k_new, v_new, basis, kv: KVView, index_keys, index_sca
                                  _stream(stream)))
 
 
+def append_block(desc, ctx_len, k_new, v_new, index_raw, index_stage, kv: KVView, index_keys, ws,
+                 stream=None):
+    """Block mode: bf16 K/V rows of the new token, its raw indexer key staged,
+    the pooled key when its block completes, ctx_len advanced
+    (sparsekv_append_block)."""
+    _dev(ctx_len, k_new, v_new, index_raw, index_stage, index_keys, ws)
+    _check(lib().sparsekv_append_block(ctypes.byref(desc), _p(ctx_len), _p(k_new), _p(v_new),
+                                       _p(index_raw), _p(index_stage), ctypes.byref(kv),
+                                       _p(index_keys), _p(ws), ws.numel(), _stream(stream)))
+
+
 def timer_enable(on: bool = True):
     """Diagnostic: bracket each launch of the streaming score kernel with events."""
     _check(lib().sparsekv_timer_enable(1 if on else 0))

@@ -71,6 +71,8 @@ SIGNATURES = [
                               P(KVView), c_vp, c_vp, ctypes.c_float, c_vp, c_vp, c_sz, c_vp]),
     ("sparsekv_append", c_i32, [P(LayerDesc), c_vp, c_vp, c_vp, c_vp, P(KVView), c_vp, c_vp, c_vp,
                                 c_sz, c_vp]),
+    ("sparsekv_append_block", c_i32, [P(LayerDesc), c_vp, c_vp, c_vp, c_vp, c_vp, P(KVView), c_vp,
+                                      c_vp, c_sz, c_vp]),
     ("sparsekv_check", c_i32, [c_vp, c_sz, c_vp, P(c_u32)]),
     ("sparsekv_timer_enable", c_i32, [c_i32]),
     ("sparsekv_timer_read", c_i32, [P(ctypes.c_double), P(c_i64)]),

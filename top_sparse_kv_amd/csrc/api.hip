@@ -288,6 +288,27 @@ skv_status sparsekv_append(const skv_layer_desc* d, int32_t* ctx_len, const void
                   "append");
 }
 
+skv_status sparsekv_append_block(const skv_layer_desc* d, int32_t* ctx_len, const void* k_new,
+                                 const void* v_new, const void* index_raw, void* index_stage,
+                                 const skv_kv_view* kv, void* index_keys, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  skv_status s = validate_desc(d);
+  if (s != SKV_OK) return s;
+  if (d->index_mode != SKV_INDEX_POOLED_BF16)
+    return set_error(SKV_ERR_UNSUPPORTED, "append_block: block mode only");
+  WsLayout L;
+  if ((s = check_ws(d, ws, ws_bytes, &L)) != SKV_OK) return s;
+  if ((s = check_kv(d, kv)) != SKV_OK) return s;
+  if (!ctx_len || !k_new || !v_new || !index_raw || !index_stage || !index_keys)
+    return set_error(SKV_ERR_INVALID, "append_block: NULL pointer");
+  if (kv->rows < d->max_ctx)
+    return set_error(SKV_ERR_INVALID, "append_block: kv rows %lld < max_ctx %d", (long long)kv->rows,
+                     d->max_ctx);
+  return launched(launch_append_block(*d, ctx_len, k_new, v_new, index_raw, index_stage, *kv,
+                                      index_keys, ws, L, (hipStream_t)stream),
+                  "append_block");
+}
+
 skv_status sparsekv_timer_enable(int enable) {
   if (enable && g_timer.ev.empty()) {
     g_timer.ev.resize(2 * kTimerPairs);

@@ -125,7 +125,77 @@ __global__ __launch_bounds__(kAppThreads) void append_kernel(
   }
 }
 
+// Block mode (page "3.14M Context on 3x 3090 ...", sections "Why" and "What
+// Needs to Stay in VRAM": the indexer key of a 4-token block is the mean of its
+// tokens' raw keys, bf16): bf16 K/V rows are stored as they are; the raw key
+// goes to staging row t % 4, and at t % 4 == 3 the pooled key of block t / 4 is
+// the exact mean of the four (fp64 sum of four bf16 values is exact; / 4 is
+// exact), rounded to nearest-even bf16, 0 below 2^-8 in magnitude, clamped to
+// +-255.  One workgroup of 256 threads per sequence.
+// nearest-even bf16 of a double, rounded once: the fp64 significand is
+// rounded to 8 bits on the bit pattern; the result converts to fp32 exactly
+__device__ __forceinline__ uint16_t bf16_rn_bits(double x) {
+  unsigned long long u = (unsigned long long)__double_as_longlong(x);
+  u = ((u + ((1ull << 44) - 1ull) + ((u >> 45) & 1ull)) >> 45) << 45;
+  return (uint16_t)(__float_as_uint((float)__longlong_as_double((long long)u)) >> 16);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void append_block_kernel(
+    int32_t* __restrict__ ctx_len, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, const uint16_t* __restrict__ raw_new,
+    uint16_t* __restrict__ stage, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
+    int64_t rows, uint16_t* __restrict__ kp, int Hkv, int ID, int max_ctx,
+    uint32_t* __restrict__ flags) {
+  const int b = blockIdx.x;
+  const int t = ctx_len[b];
+  if (t < 0 || t >= max_ctx) {
+    if (threadIdx.x == 0) raise_flag(flags, SKV_FLAG_CTX_RANGE);
+    return;
+  }
+  const size_t rr = ((size_t)b * rows + t) * Hkv;
+  for (int i = threadIdx.x; i < Hkv * D; i += blockDim.x) {
+    kc[rr * D + i] = k_new[(size_t)b * Hkv * D + i];
+    vc[rr * D + i] = v_new[(size_t)b * Hkv * D + i];
+  }
+  uint16_t* st = stage + (size_t)b * 4 * ID;
+  const uint16_t* raw = raw_new + (size_t)b * ID;
+  const int slot = t & 3;
+  for (int i = threadIdx.x; i < ID; i += blockDim.x) {
+    const uint16_t x = raw[i];
+    st[slot * ID + i] = x;
+    if (slot == 3) {
+      double sum = 0.0;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) sum += (double)bf16_bits_to_float(st[j * ID + i]);
+      sum += (double)bf16_bits_to_float(x);
+      float y = bf16_bits_to_float(bf16_rn_bits(sum * 0.25));   // the exact mean, rounded once
+      y = fabsf(y) < 0.00390625f ? 0.0f : fminf(fmaxf(y, -255.0f), 255.0f);
+      kp[((size_t)b * (max_ctx / 4) + (t >> 2)) * ID + i] = (uint16_t)(__float_as_uint(y) >> 16);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) ctx_len[b] = t + 1;   // every thread read t before the barrier
+}
+
 }  // namespace
+
+hipError_t launch_append_block(const skv_layer_desc& d, int32_t* ctx_len, const void* k_new,
+                               const void* v_new, const void* raw_new, void* stage,
+                               const skv_kv_view& kv, void* index_keys, void* ws, const WsLayout& L,
+                               hipStream_t st) {
+  uint32_t* flags = ws_ptr<uint32_t>(ws, L.flags);
+#define SKV_APB(DD)                                                                              \
+  hipLaunchKernelGGL((append_block_kernel<DD>), dim3(d.batch), dim3(256), 0, st, ctx_len,        \
+                     (const uint16_t*)k_new, (const uint16_t*)v_new, (const uint16_t*)raw_new,   \
+                     (uint16_t*)stage, (uint16_t*)kv.k, (uint16_t*)kv.v, kv.rows,                \
+                     (uint16_t*)index_keys, d.n_kv_heads, d.index_dim, d.max_ctx, flags)
+  if (d.head_dim == 256) SKV_APB(256);
+  else if (d.head_dim == 128) SKV_APB(128);
+  else return hipErrorInvalidValue;
+#undef SKV_APB
+  return hipGetLastError();
+}
 
 hipError_t launch_append(const skv_layer_desc& d, int32_t* ctx_len, const void* k_new,
                          const void* v_new, const float* basis, const skv_kv_view& kv,

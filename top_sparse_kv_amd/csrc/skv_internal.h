@@ -186,6 +186,10 @@ hipError_t launch_score_select(const skv_layer_desc& d, const int32_t* ctx_len, 
 hipError_t launch_attend(const skv_layer_desc& d, const void* q, const skv_kv_view& kv,
                          const int32_t* idx, const int32_t* n_sel, float sm_scale, float* out,
                          void* ws, const WsLayout& L, hipStream_t st);
+hipError_t launch_append_block(const skv_layer_desc& d, int32_t* ctx_len, const void* k_new,
+                               const void* v_new, const void* raw_new, void* stage,
+                               const skv_kv_view& kv, void* index_keys, void* ws, const WsLayout& L,
+                               hipStream_t st);
 hipError_t launch_append(const skv_layer_desc& d, int32_t* ctx_len, const void* k_new,
                          const void* v_new, const float* basis, const skv_kv_view& kv,
                          void* index_keys, uint16_t* index_scale, void* ws, const WsLayout& L,
