@@ -72,10 +72,13 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
     key_range(mode, T, S, L, lo, n);
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int seg = blockIdx.x * (kThreads / 64) + wave;
+  // transposed collect: one workgroup per segment, one batch per wave;
+  // otherwise one segment per wave
+  const int seg = TRANS ? blockIdx.x : blockIdx.x * (kThreads / 64) + wave;
   const int i0 = seg * seg_items;
-  if (i0 >= n) return;   // wave-uniform; there is no barrier below
+  if (i0 >= n) return;   // workgroup-uniform (transposed) or wave-uniform (no barrier)
   const int i1 = min(n, i0 + seg_items);
+  const int first = TRANS ? i0 + PER_IT * wave : i0;
   const int sub = lane % N, tw = lane / N;
   Src src;
   src.init(reinterpret_cast<const uint8_t*>(iq) + (size_t)b * Src::QROW, ik, isc, b, max_ctx, sub);
@@ -91,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
       if constexpr (!TRANS) av[u] = src.load_aux(lo + i);
     }
   };
-  load_batch(i0, w, ax);
+  load_batch(first, w, ax);
   const uint32_t beta = COLLECT ? state[b].beta : 0u;   // read while the first loads fly
   double* kout = keys + (size_t)b * (mode == SKV_INDEX_SKETCH_INT4 ? max_ctx : max_ctx / 4) + lo;
   u32x4* cseg = reinterpret_cast<u32x4*>(cand + ((size_t)b * n_seg + seg) * seg_items);
@@ -101,61 +104,62 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
     // Transposed collect: the 8 partial dots of a lane (one per load) are
     // reduced over the 8 lanes of its group by a butterfly (mirror / quad
     // swaps), which leaves lane (tw, sub) with the whole dot of load sub, i.e.
-    // candidate o = 8*sub + tw of the batch.  Digit, selection and ballot then
-    // run once per batch, and the ballot is transposed (8x8 bits) into
+    // candidate o = 8*sub + tw of the wave's batch.  Digit, selection and
+    // ballot then run once, and the ballot is transposed (8x8 bits) into
     // candidate order for the ranks.  Each lane reads the scale of its own
-    // candidate.
+    // candidate.  The four waves of the workgroup cover the segment's four
+    // batches; their counts are exchanged in LDS so that the records land in
+    // position order.  Short per-wave work (8 KB) lets the dispatcher keep
+    // the HBM queues full to the end of the stream.
+    static_assert(PER_IT * (kThreads / 64) == kSegTok, "one batch per wave");
+    __shared__ uint32_t s_cnt[kThreads / 64];
     const int o = 8 * sub + tw;
-    uint32_t sc = src.load_aux(lo + min(i0 + o, i1 - 1));
+    const uint32_t sc = src.load_aux(lo + min(first + o, i1 - 1));
     const uint32_t b2 = (sub >> 2) & 1, b1 = (sub >> 1) & 1, b0 = sub & 1;
     const uint64_t below = (1ull << o) - 1ull;
-    for (int base = i0; base < i1; base += PER_IT) {
-      u32x4 wn[kUnroll];
-      uint32_t scn = 0;
-      if (base + PER_IT < i1) {   // next batch in flight
+    int p[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) wn[u] = src.load(lo + min(base + PER_IT + u * IPW + tw, i1 - 1));
-        scn = src.load_aux(lo + min(base + PER_IT + o, i1 - 1));
-      }
-      int p[kUnroll];
+    for (int u = 0; u < kUnroll; ++u) p[u] = src.partial(w[u]);
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) p[u] = src.partial(w[u]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {   // partner 7 - sub: opposite bit 2
-        const int keep = b2 ? p[j + 4] : p[j], send = b2 ? p[j] : p[j + 4];
-        p[j] = keep + (int)dpp_u32<0x141>((uint32_t)send);
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {   // partner sub ^ 2
-        const int keep = b1 ? p[j + 2] : p[j], send = b1 ? p[j] : p[j + 2];
-        p[j] = keep + (int)dpp_u32<0x4E>((uint32_t)send);
-      }
-      {                               // partner sub ^ 1
-        const int keep = b0 ? p[1] : p[0], send = b0 ? p[0] : p[1];
-        p[0] = keep + (int)dpp_u32<0xB1>((uint32_t)send);
-      }
-      const int dt = p[0] >> 4;
-      const int i = base + o;
-      const uint32_t dig = src.digit_of(dt, sc);
-      const bool sel = i < i1 && dig >= beta;
-      uint64_t x = __ballot(sel);   // bit 8*tw + sub
-      uint64_t t = (x ^ (x >> 7)) & 0x00AA00AA00AA00AAull;
-      x = x ^ t ^ (t << 7);
-      t = (x ^ (x >> 14)) & 0x0000CCCC0000CCCCull;
-      x = x ^ t ^ (t << 14);
-      t = (x ^ (x >> 28)) & 0x00000000F0F0F0F0ull;
-      x = x ^ t ^ (t << 28);          // bit o = 8*sub + tw
-      if (sel) {
-        const uint64_t ok = ordered_u64(src.key_of(dt, sc));
-        const uint32_t rank = cnt + (uint32_t)__popcll(x & below);
-        cseg[rank] = (u32x4){(uint32_t)ok, (uint32_t)(ok >> 32), (uint32_t)(lo + i), dig};
-      }
-      cnt += (uint32_t)__popcll(x);
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) w[u] = wn[u];
-      sc = scn;
+    for (int j = 0; j < 4; ++j) {   // partner 7 - sub: opposite bit 2
+      const int keep = b2 ? p[j + 4] : p[j], send = b2 ? p[j] : p[j + 4];
+      p[j] = keep + (int)dpp_u32<0x141>((uint32_t)send);
     }
-    if (lane == 0) segcnt[(size_t)b * n_seg + seg] = cnt;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {   // partner sub ^ 2
+      const int keep = b1 ? p[j + 2] : p[j], send = b1 ? p[j] : p[j + 2];
+      p[j] = keep + (int)dpp_u32<0x4E>((uint32_t)send);
+    }
+    {                               // partner sub ^ 1
+      const int keep = b0 ? p[1] : p[0], send = b0 ? p[0] : p[1];
+      p[0] = keep + (int)dpp_u32<0xB1>((uint32_t)send);
+    }
+    const int dt = p[0] >> 4;
+    const int i = first + o;
+    const uint32_t dig = src.digit_of(dt, sc);
+    const bool sel = i < i1 && dig >= beta;
+    uint64_t x = __ballot(sel);   // bit 8*tw + sub
+    uint64_t t = (x ^ (x >> 7)) & 0x00AA00AA00AA00AAull;
+    x = x ^ t ^ (t << 7);
+    t = (x ^ (x >> 14)) & 0x0000CCCC0000CCCCull;
+    x = x ^ t ^ (t << 14);
+    t = (x ^ (x >> 28)) & 0x00000000F0F0F0F0ull;
+    x = x ^ t ^ (t << 28);          // bit o = 8*sub + tw
+    if (lane == 0) s_cnt[wave] = (uint32_t)__popcll(x);
+    __syncthreads();
+    uint32_t off = 0, tot = 0;
+#pragma unroll
+    for (int v = 0; v < kThreads / 64; ++v) {
+      const uint32_t c = s_cnt[v];
+      off += v < wave ? c : 0u;
+      tot += c;
+    }
+    if (sel) {
+      const uint64_t ok = ordered_u64(src.key_of(dt, sc));
+      cseg[off + (uint32_t)__popcll(x & below)] =
+          (u32x4){(uint32_t)ok, (uint32_t)(ok >> 32), (uint32_t)(lo + i), dig};
+    }
+    if (threadIdx.x == 0) segcnt[(size_t)b * n_seg + seg] = tot;
     return;
   }
   for (int base = i0; base < i1; base += PER_IT) {
@@ -290,7 +294,7 @@ hipError_t launch_token_or_block(const skv_layer_desc& d, const int32_t* ctx_len
   const int seg_items = mode == SKV_INDEX_SKETCH_INT4 ? kSegTok : kSegBlk;
   const int n_seg = (max_candidates(d) + seg_items - 1) / seg_items;
   constexpr int kWaves = kThreads / 64;   // one segment per wave
-  const dim3 grid((n_seg + kWaves - 1) / kWaves > 0 ? (n_seg + kWaves - 1) / kWaves : 1, d.batch);
+  dim3 grid((n_seg + kWaves - 1) / kWaves > 0 ? (n_seg + kWaves - 1) / kWaves : 1, d.batch);
   if (!collect) {
     hipLaunchKernelGGL((score_kernel<Src, false>), grid, dim3(kThreads), 0, st, iq, ik, isc,
                        ctx_len, keys, nullptr, nullptr, nullptr, flags, mode, d.max_ctx, S, d.topk,
@@ -315,6 +319,8 @@ hipError_t launch_token_or_block(const skv_layer_desc& d, const int32_t* ctx_len
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const void* iq_score = qs_out ? (const void*)qs_out : iq;
+  // the transposed collect (8-lane sketch rows) runs one workgroup per segment
+  if (Src::HAS_AUX && Src::LANES == 8) grid.x = Lw->n_seg;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   if (timer_next(&ev0, &ev1))
     hipExtLaunchKernelGGL((score_kernel<Src, true>), grid, dim3(kThreads), 0, st, ev0, ev1, 0,
