@@ -8,3 +8,4 @@ code with it.
 from .step import *  # noqa: F401,F403
 from .step import PINS  # noqa: F401
 from . import append  # noqa: F401
+from . import multiquery  # noqa: F401

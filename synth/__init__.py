@@ -18,6 +18,7 @@ from .gen import (  # noqa: F401
     make_block_case,
     make_tier_case,
     drift_picks,
+    multi_queries,
     orthonormal_basis,
     pack_int4,
     flush_bf16_domain,

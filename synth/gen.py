@@ -34,6 +34,7 @@ _MUL = 1_000_003
 # tensor ids for sub-seeding
 _T_Q, _T_BASIS, _T_SKETCH, _T_K, _T_V, _T_NEEDLE = 1, 2, 3, 4, 5, 6
 _T_QI, _T_RAWIDX, _T_HK, _T_HV, _T_RK, _T_RV, _T_DRIFT, _T_LEN = 7, 8, 9, 10, 11, 12, 13, 14
+_T_MQ = 15
 
 
 def _subseed(seed: int, *ids: int) -> int:
@@ -135,6 +136,12 @@ def mixed_lengths(B: int, lo: int, hi: int, seed: int) -> List[int]:
     """Sequence lengths drawn uniformly from the integers in [lo, hi]."""
     g = _gen("cpu", seed, _T_LEN)
     return torch.randint(lo, hi + 1, (B,), generator=g).tolist()
+
+
+def multi_queries(B: int, M: int, n_q: int, D: int, seed: int, device="cpu") -> torch.Tensor:
+    """Queries of M tokens per sequence (a verification step): N(0, 1) -> fp16
+    [B][M][n_q][D]."""
+    return _randn("cpu", seed, (_T_MQ,), (B, M, n_q, D)).to(torch.float16).to(device)
 
 
 # ----------------------------------------------------------------------------

@@ -608,3 +608,111 @@ def test_append_block_bookkeeping():
     # block 0 = tokens 0..3: slot 0 was never written in this test (zeros), 1..3 from the steps
     want = oracle.append.pooled_from_raw(np.stack([np.zeros(ID, np.uint16)] + raws))
     assert np.array_equal(caches["kp"][0, 0], want)
+
+
+# --------------------------------------------------------------------------
+# multi-query decode (verification tokens)
+# --------------------------------------------------------------------------
+
+def _mq_case(T, lens, M, S, k, L, seed, fmt="i8"):
+    c = synth.make_token_case(len(lens), T, lens, n_kv=2, n_q=6, D=64, S=S, k=k, L=L,
+                              kv_format=fmt, n_needles=0, seed=seed)
+    q = synth.multi_queries(len(lens), M, 6, 64, seed)
+    return c, q
+
+
+def _run_mq(c, q, M, fmt="i8", sm=0.125):
+    ks = None if c.k_scale is None else c.k_scale.numpy()
+    vs = None if c.v_scale is None else c.v_scale.numpy()
+    return oracle.multiquery.token_step_multi(
+        q.numpy(), c.basis.numpy(), c.codes.numpy(), c.sk_scale.numpy(), c.k_cache.numpy(),
+        c.v_cache.numpy(), ks, vs, c.lens, M=M, S=c.S, k_top=c.k, L=c.L, group=c.group,
+        sm_scale=sm, fmt=fmt)
+
+
+@pytest.mark.parametrize("fmt", ["i8", "f16"])
+def test_multi_dense_equals_causal_attention(fmt):
+    """With every query below the budget, the M outputs equal torch's fp64
+    scaled_dot_product_attention of the M queries over the cache with a causal
+    mask (query j sees positions 0 .. T-M+j)."""
+    M, T = 5, 60
+    c, q = _mq_case(T, [T, T - 9], M, S=4, k=50, L=8, seed=31, fmt=fmt)
+    _, _, idx, out = _run_mq(c, q, M, fmt)
+    for b in range(c.B):
+        Tb = c.lens[b]
+        kd = c.k_cache[b, :Tb].double()
+        vd = c.v_cache[b, :Tb].double()
+        if fmt == "i8":
+            kd = kd * c.k_scale[b, :Tb].double().unsqueeze(-1)
+            vd = vd * c.v_scale[b, :Tb].double().unsqueeze(-1)
+        kk = kd.permute(1, 0, 2).repeat_interleave(c.group, dim=0)   # [H_q][T][D]
+        vv = vd.permute(1, 0, 2).repeat_interleave(c.group, dim=0)
+        qq = q[b].double().permute(1, 0, 2)                          # [H_q][M][D]
+        pos = torch.arange(Tb)
+        mask = pos[None, :] <= (Tb - M + torch.arange(M))[:, None]   # [M][T]
+        ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, attn_mask=mask,
+                                                               scale=0.125)
+        np.testing.assert_allclose(out[b], ref.permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+        for j in range(M):
+            assert np.array_equal(idx[b][j], np.arange(Tb - M + 1 + j))
+
+
+def test_multi_last_query_is_the_single_step():
+    """The last query token sees the whole cache: its pick and output are the
+    single-query step's at ctx_len."""
+    M, T = 4, 700
+    c, q = _mq_case(T, [T, 613], M, S=8, k=64, L=16, seed=32)
+    qs, qsc, idx, out = _run_mq(c, q, M)
+    ks, vs = c.k_scale.numpy(), c.v_scale.numpy()
+    s_qs, s_qsc, _, s_idx, s_out = oracle.token_step(
+        q[:, M - 1].numpy(), c.basis.numpy(), c.codes.numpy(), c.sk_scale.numpy(),
+        c.k_cache.numpy(), c.v_cache.numpy(), ks, vs, c.lens, S=c.S, k_top=c.k, L=c.L,
+        group=c.group, sm_scale=0.125, fmt="i8")
+    assert np.array_equal(qs[:, M - 1], s_qs) and np.array_equal(qsc[:, M - 1], s_qsc)
+    for b in range(c.B):
+        assert np.array_equal(idx[b][M - 1], s_idx[b])
+        assert np.array_equal(out[b, M - 1], s_out[b])
+
+
+def test_multi_picks_stay_causal():
+    """Every pick of query j lies in its context T_j = T-M+1+j, holds its own
+    sinks and tail, and has min(T_j, S+k+L) positions; a budget threshold
+    crossed inside one step (S+k+L = 28, T = 30, M = 4) leaves the first two
+    queries dense and the last two sparse; a context shorter than M leaves the
+    first queries empty."""
+    S, k, L, M = 4, 16, 8, 4
+    c, q = _mq_case(40, [30, 3], M, S=S, k=k, L=L, seed=33)
+    _, _, idx, out = _run_mq(c, q, M)
+    assert oracle.multiquery.query_contexts(30, M) == [27, 28, 29, 30]
+    assert oracle.multiquery.query_contexts(3, M) == [0, 1, 2, 3]
+    for b in range(c.B):
+        for j, Tj in enumerate(oracle.multiquery.query_contexts(c.lens[b], M)):
+            sel = idx[b][j]
+            assert len(sel) == min(Tj, S + k + L)
+            assert np.all(np.diff(sel) > 0) and (len(sel) == 0 or sel[-1] < Tj)
+            if Tj > S + k + L:
+                assert set(range(S)) <= set(sel.tolist())
+                assert set(range(Tj - L, Tj)) <= set(sel.tolist())
+            else:
+                assert np.array_equal(sel, np.arange(Tj))
+            if Tj == 0:
+                assert not out[b, j].any()
+    assert [len(idx[0][j]) for j in range(M)] == [27, 28, 28, 28]
+
+
+def test_multi_equal_queries_nested_picks():
+    """M copies of one query: each step of the causal context moves one
+    position from the tail into the ranked middle, so consecutive picks differ
+    by at most that position coming in and one ranked position going out."""
+    S, k, L, M, T = 4, 32, 8, 6, 900
+    c, _ = _mq_case(T, [T], M, S=S, k=k, L=L, seed=34)
+    q1 = synth.multi_queries(1, 1, 6, 64, 35)
+    q = q1.expand(1, M, 6, 64).contiguous()
+    _, _, idx, _ = _run_mq(c, q, M)
+    for j in range(M - 1):
+        Tj = T - M + 1 + j
+        mid_a = set(idx[0][j].tolist()) - set(range(S)) - set(range(Tj - L, Tj))
+        mid_b = set(idx[0][j + 1].tolist()) - set(range(S)) - set(range(Tj + 1 - L, Tj + 1))
+        assert len(mid_a) == len(mid_b) == k
+        assert mid_b - mid_a <= {Tj - L}
+        assert len(mid_a - mid_b) == len(mid_b - mid_a)
