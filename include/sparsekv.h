@@ -232,6 +232,35 @@ skv_status sparsekv_step(const skv_layer_desc* d, const int32_t* ctx_len, const 
                          int32_t* n_sel, float sm_scale, float* out, void* ws, size_t ws_bytes,
                          void* stream);
 
+/* ---- the step with several query tokens per sequence ------------------------
+ * Page "8 agents x 250K ...", section "What shipped" (decoding with MTP-7
+ * speculation: one step verifies the drafted tokens with the current one) and
+ * section "The mechanism"; page "vLLM's Hybrid HiSparse Triples Concurrent
+ * Requests on Million-Token Contexts", section "Where the tradeoffs bite"
+ * (every verification token has its own pick).  Token mode only, with
+ * H_kv*R/2 in {64, 128, 256} sketch bytes per token.
+ *   n_query  M in [1, 16]: the query tokens of each sequence are the last M
+ *            positions of its cache (ctx_len[b] = T counts them); query j
+ *            sees the causal context T_j = T - M + 1 + j (0 if negative) and
+ *            gets exactly what sparsekv_step computes for a single query at
+ *            ctx_len T_j: its own int8 sketch and scale, its own top-k over
+ *            [n_sink, T_j - n_tail), sinks and tail of T_j, dense when
+ *            T_j <= n_sink + topk + n_tail, and exact attention (T_j = 0:
+ *            nothing selected, zero output)
+ *   q        [B][M][H_q][D] fp16
+ *   qs       [B][M][H_kv*R] int8 (16-byte aligned), qs_scale [B][M] fp32: written
+ *   idx      [B][M][cap], n_sel [B][M], out [B][M][H_q][D] fp32: written
+ *   ws       sparsekv_workspace_size_multi(d, M) bytes, 256-byte aligned
+ * The sketch is read once per step for all M queries (an int8 matrix-core
+ * contraction of the codes with the M query sketches).  Other arguments and
+ * errors as sparsekv_step. */
+skv_status sparsekv_workspace_size_multi(const skv_layer_desc* d, int32_t n_query, size_t* bytes);
+skv_status sparsekv_step_multi(const skv_layer_desc* d, int32_t n_query, const int32_t* ctx_len,
+                               const void* q, const float* basis, int8_t* qs, float* qs_scale,
+                               const void* index_keys, const uint16_t* index_scale,
+                               const skv_kv_view* kv, int32_t* idx, int32_t* n_sel, float sm_scale,
+                               float* out, void* ws, size_t ws_bytes, void* stream);
+
 /* ---- append: the new token of every sequence into the caches ---------------
  * Page "8 agents x 250K ...", section "The mechanism" (int8 K/V rows with a
  * per-row scale, int4 rank-64 key sketch with one fp16 scale per token); page

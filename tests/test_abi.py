@@ -161,3 +161,36 @@ def test_status_strings(skv):
     for s in range(8):
         assert lib.sparsekv_status_str(s)
     assert lib.sparsekv_status_str(99) == b"unknown status"
+
+
+def test_multi_query_host_checks(skv):
+    """The multi-query step takes 1..16 query tokens per sequence in token mode
+    (64, 128 or 256 sketch bytes per token); its workspace holds one virtual
+    sequence per query; bad arguments are rejected on the host."""
+    lib = skv.lib()
+    d = skv.token_desc(8, 250_000, 4, 24, 256, topk=2048, n_sink=64, n_tail=1024)
+    one = skv.workspace_size(d)
+    assert skv.workspace_size_multi(d, 1) == one
+    w8 = skv.workspace_size_multi(d, 8)
+    assert w8 > 4 * one and w8 % 256 == 0
+    n = skv._lib.c_sz()
+    for m in (0, 17, -1):
+        assert lib.sparsekv_workspace_size_multi(ctypes.byref(d), m, ctypes.byref(n)) == 2
+    db = skv.block_desc(1, 4096, 2, 16, 256, topk_blocks=64)
+    assert lib.sparsekv_workspace_size_multi(ctypes.byref(db), 4, ctypes.byref(n)) == 2
+    d32 = skv.token_desc(2, 4096, 1, 8, 128, rank=64, topk=64, n_sink=4, n_tail=8,
+                         kv_dtype=skv.SKV_KV_F16)   # 32 sketch bytes per token
+    assert lib.sparsekv_workspace_size_multi(ctypes.byref(d32), 4, ctypes.byref(n)) == 2
+    dummy = ctypes.c_void_p(0x1000)
+    kv = skv.KVView(dummy, dummy, dummy, dummy, 250_000)
+    args = [dummy] * 7   # ctx_len, q, basis, qs, qs_scale, index_keys, index_scale
+    # workspace too small (sized for one query)
+    st = lib.sparsekv_step_multi(ctypes.byref(d), 8, *args, ctypes.byref(kv), dummy, dummy, 0.1,
+                                 dummy, ctypes.c_void_p(0x100000), one, None)
+    assert st == 3
+    # NULL query
+    a2 = list(args)
+    a2[1] = None
+    st = lib.sparsekv_step_multi(ctypes.byref(d), 8, *a2, ctypes.byref(kv), dummy, dummy, 0.1,
+                                 dummy, ctypes.c_void_p(0x100000), w8, None)
+    assert st == 1

@@ -143,6 +143,30 @@ def step(desc, ctx_len, q, basis, qs, qs_scale, index_query, index_keys, index_s
                                _p(ws), ws.numel(), _stream(stream)))
 
 
+def workspace_size_multi(desc: LayerDesc, n_query: int) -> int:
+    n = _lib.c_sz()
+    _check(lib().sparsekv_workspace_size_multi(ctypes.byref(desc), int(n_query), ctypes.byref(n)))
+    return n.value
+
+
+def workspace_multi(desc: LayerDesc, n_query: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace for sparsekv_step_multi with n_query queries per sequence."""
+    return torch.zeros(workspace_size_multi(desc, n_query), dtype=torch.uint8, device=device)
+
+
+def step_multi(desc, n_query, ctx_len, q, basis, qs, qs_scale, index_keys, index_scale, kv: KVView,
+               idx, n_sel, sm_scale, out, ws, stream=None):
+    """n_query query tokens per sequence (the cache's last positions), each with
+    its own pick at its causal context (sparsekv_step_multi).  q [B][M][H_q][D];
+    qs [B][M][H_kv*R], qs_scale [B][M], idx [B][M][cap], n_sel [B][M],
+    out [B][M][H_q][D]."""
+    _dev(ctx_len, q, basis, qs, qs_scale, index_keys, index_scale, idx, n_sel, out, ws)
+    _check(lib().sparsekv_step_multi(ctypes.byref(desc), int(n_query), _p(ctx_len), _p(q), _p(basis),
+                                     _p(qs), _p(qs_scale), _p(index_keys), _p(index_scale),
+                                     ctypes.byref(kv), _p(idx), _p(n_sel), float(sm_scale), _p(out),
+                                     _p(ws), ws.numel(), _stream(stream)))
+
+
 def append(desc, ctx_len, k_new, v_new, basis, kv: KVView, index_keys, index_scale, ws, stream=None):
     """Writes the new token of every sequence at row ctx_len[b] (K/V rows,
     key sketch) and advances ctx_len (sparsekv_append)."""

@@ -20,7 +20,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsparsekv.so")
-SOURCES = ["api.hip", "qsketch.hip", "score.hip", "topk.hip", "attend.hip", "tier.hip", "append.hip"]
+SOURCES = ["api.hip", "qsketch.hip", "score.hip", "score_multi.hip", "topk.hip", "attend.hip", "tier.hip",
+           "append.hip"]
 ARCH = "gfx950"
 
 

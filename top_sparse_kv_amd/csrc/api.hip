@@ -170,6 +170,59 @@ skv_status sparsekv_workspace_size(const skv_layer_desc* d, size_t* bytes) {
   return SKV_OK;
 }
 
+// the layer with n_query query tokens per sequence seen as batch*n_query
+// virtual sequences (token mode)
+static skv_status multi_desc(const skv_layer_desc* d, int32_t n_query, skv_layer_desc* dv) {
+  skv_status s = validate_desc(d);
+  if (s != SKV_OK) return s;
+  if (d->index_mode != SKV_INDEX_SKETCH_INT4)
+    return set_error(SKV_ERR_UNSUPPORTED, "multi-query step: token mode only");
+  if (n_query < 1 || n_query > kMaxQueries)
+    return set_error(SKV_ERR_UNSUPPORTED, "n_query %d outside [1, %d]", n_query, kMaxQueries);
+  const int tb = d->n_kv_heads * d->rank / 2;
+  if (tb != 64 && tb != 128 && tb != 256)
+    return set_error(SKV_ERR_UNSUPPORTED, "multi-query step: sketch bytes per token %d not in {64,128,256}", tb);
+  if ((int64_t)d->batch * n_query > (1 << 20))
+    return set_error(SKV_ERR_UNSUPPORTED, "batch * n_query too large");
+  *dv = *d;
+  dv->batch = d->batch * n_query;
+  return validate_desc(dv);
+}
+
+skv_status sparsekv_workspace_size_multi(const skv_layer_desc* d, int32_t n_query, size_t* bytes) {
+  skv_layer_desc dv;
+  skv_status s = multi_desc(d, n_query, &dv);
+  if (s != SKV_OK) return s;
+  if (!bytes) return set_error(SKV_ERR_INVALID, "bytes is NULL");
+  *bytes = ws_layout(dv).total;
+  return SKV_OK;
+}
+
+skv_status sparsekv_step_multi(const skv_layer_desc* d, int32_t n_query, const int32_t* ctx_len,
+                               const void* q, const float* basis, int8_t* qs, float* qs_scale,
+                               const void* index_keys, const uint16_t* index_scale,
+                               const skv_kv_view* kv, int32_t* idx, int32_t* n_sel, float sm_scale,
+                               float* out, void* ws, size_t ws_bytes, void* stream) {
+  skv_layer_desc dv;
+  skv_status s = multi_desc(d, n_query, &dv);
+  if (s != SKV_OK) return s;
+  WsLayout L;
+  if ((s = check_ws(&dv, ws, ws_bytes, &L)) != SKV_OK) return s;
+  if ((s = check_kv(d, kv)) != SKV_OK) return s;
+  if (!ctx_len || !q || !basis || !qs || !qs_scale || !index_keys || !index_scale || !idx || !n_sel || !out)
+    return set_error(SKV_ERR_INVALID, "step_multi: NULL pointer");
+  if ((((uintptr_t)index_keys) | ((uintptr_t)qs)) % 16)
+    return set_error(SKV_ERR_INVALID, "step_multi: index_keys and qs must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_qsketch_proj(dv, q, basis, ws, L, st);
+  if (e == hipSuccess)
+    e = launch_sample_collect_multi(dv, n_query, ctx_len, qs, qs_scale, index_keys, index_scale, ws, L, st);
+  if (e == hipSuccess)
+    e = launch_final_multi(dv, n_query, ctx_len, qs, index_keys, index_scale, idx, n_sel, ws, L, st);
+  if (e == hipSuccess) e = launch_attend(dv, q, *kv, idx, n_sel, sm_scale, out, ws, L, st, n_query);
+  return launched(e, "step_multi");
+}
+
 skv_status sparsekv_qsketch(const skv_layer_desc* d, const void* q, const float* basis, int8_t* qs,
                             float* qs_scale, void* ws, size_t ws_bytes, void* stream) {
   skv_status s = validate_desc(d);

@@ -91,7 +91,7 @@ __global__ __launch_bounds__(64 * WAVES) void attend_kernel(
     const uint16_t* __restrict__ ksc, const uint16_t* __restrict__ vsc, int64_t rows,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ n_sel, int cap,
     float scale_log2, int Hq, int Hkv, float* __restrict__ part_ml, float* __restrict__ part_o,
-    int n_chunks, uint32_t* __restrict__ flags) {
+    int n_chunks, uint32_t* __restrict__ flags, int mq) {
   constexpr bool BF = KVT == KV_BF16;
   constexpr int ES = Esize<KVT>::v;
   constexpr int KSTEPS = D / 32;          // MFMA k-steps over head_dim
@@ -154,10 +154,13 @@ __global__ __launch_bounds__(64 * WAVES) void attend_kernel(
   float m_run = -INFINITY;   // max of head i16 (log2 units), same in all 4 groups
   float l_run = 0.0f;
 
-  const uint8_t* kbase = kc + ((size_t)b * rows * Hkv + h) * D * ES;
-  const uint8_t* vbase = vc + ((size_t)b * rows * Hkv + h) * D * ES;
-  const uint16_t* ksb = ksc ? ksc + (size_t)b * rows * Hkv + h : nullptr;
-  const uint16_t* vsb = vsc ? vsc + (size_t)b * rows * Hkv + h : nullptr;
+  // b is a virtual sequence (query b % mq of sequence b / mq): its rows are
+  // those of sequence b / mq
+  const size_t bk = (size_t)(b / mq);
+  const uint8_t* kbase = kc + (bk * rows * Hkv + h) * D * ES;
+  const uint8_t* vbase = vc + (bk * rows * Hkv + h) * D * ES;
+  const uint16_t* ksb = ksc ? ksc + bk * rows * Hkv + h : nullptr;
+  const uint16_t* vsb = vsc ? vsc + bk * rows * Hkv + h : nullptr;
 
   if (rb < n) {
     // out-of-range rows load row 0 and are masked through vok
@@ -482,7 +485,7 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(
 
 hipError_t launch_attend(const skv_layer_desc& d, const void* q, const skv_kv_view& kv,
                          const int32_t* idx, const int32_t* n_sel, float sm_scale, float* out,
-                         void* ws, const WsLayout& Lw, hipStream_t st) {
+                         void* ws, const WsLayout& Lw, hipStream_t st, int mq) {
   uint32_t* flags = ws_ptr<uint32_t>(ws, Lw.flags);
   float* part_ml = ws_ptr<float>(ws, Lw.att_ml);
   float* part_o = ws_ptr<float>(ws, Lw.att_o);
@@ -497,7 +500,7 @@ hipError_t launch_attend(const skv_layer_desc& d, const void* q, const skv_kv_vi
   hipLaunchKernelGGL((attend_kernel<KVT, DD, WV>), grid, dim3(64 * WV), lds, st, q,              \
                      (const uint8_t*)kv.k, (const uint8_t*)kv.v, kv.k_scale, kv.v_scale, kv.rows, \
                      idx, n_sel, cap, sl, d.n_q_heads, d.n_kv_heads, part_ml, part_o,             \
-                     Lw.n_att_chunks, flags)
+                     Lw.n_att_chunks, flags, mq)
 #define SKV_AT_W(KVT, DD)                                                                          \
   do {                                                                                             \
     if (waves == 16) SKV_AT(KVT, DD, 16);                                                          \

@@ -55,6 +55,15 @@ __device__ __forceinline__ int ctx_of(const int32_t* ctx_len, int b, int max_ctx
   return T < 0 ? 0 : (T > max_ctx ? max_ctx : T);
 }
 
+// A step with mq query tokens per sequence (the last mq positions of the
+// cache, which ctx_len counts): virtual sequence v is query j = v % mq of
+// sequence v / mq, whose causal context is T - mq + 1 + j tokens (0 when the
+// cache is shorter than the step).  mq = 1 is the ordinary decode step.
+__device__ __forceinline__ int ctx_of_query(const int32_t* ctx_len, int v, int mq, int max_ctx) {
+  const int T = ctx_of(ctx_len, v / mq, max_ctx) - (mq - 1 - v % mq);
+  return T < 0 ? 0 : T;
+}
+
 // Sample: whole lines of 16 candidates, one line in every s; about 4k lines'
 // worth of keys, at most about 16K (every key when the sequence is short).
 __host__ __device__ __forceinline__ int sample_stride(int n, int k) {

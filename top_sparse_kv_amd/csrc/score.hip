@@ -269,15 +269,17 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(
   }
 }
 
-// threshold digit of each sequence from its sampled digits
+// Threshold digit of each (virtual) sequence from its sampled digits.  With
+// mq query tokens per sequence the sample is laid out for the last query's
+// (largest) candidate range, shared by the sequence's queries.
 __global__ __launch_bounds__(1024) void beta_kernel(const uint16_t* __restrict__ sdig, int n_samp,
                                                      const int32_t* __restrict__ ctx_len,
                                                      TopkState* __restrict__ state, int mode,
-                                                     int max_ctx, int S, int k, int L) {
+                                                     int max_ctx, int S, int k, int L, int mq) {
   __shared__ uint32_t red[256 + 32];
   const int b = blockIdx.x;
-  const Range r = cand_range(mode, ctx_of(ctx_len, b, max_ctx), S, k, L);
-  if (r.dense) return;
+  if (cand_range(mode, ctx_of_query(ctx_len, b, mq, max_ctx), S, k, L).dense) return;
+  const Range r = cand_range(mode, ctx_of(ctx_len, b / mq, max_ctx), S, k, L);
   const uint32_t beta = wg_beta(sdig + (size_t)b * n_samp * kLineKeys,
                                 sample_lines(r.n, k) * kLineKeys, sample_need(r.n, k), red);
   if (threadIdx.x == 0) state[b].beta = beta;
@@ -315,7 +317,7 @@ hipError_t launch_token_or_block(const skv_layer_desc& d, const int32_t* ctx_len
                        d.topk, L);
   TopkState* state = ws_ptr<TopkState>(ws, Lw->state);
   hipLaunchKernelGGL(beta_kernel, dim3(d.batch), dim3(1024), 0, st, sdig, Lw->n_samp, ctx_len, state,
-                     mode, d.max_ctx, S, d.topk, L);
+                     mode, d.max_ctx, S, d.topk, L, 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const void* iq_score = qs_out ? (const void*)qs_out : iq;
@@ -371,6 +373,17 @@ hipError_t launch_sample_collect(const skv_layer_desc& d, const int32_t* ctx_len
                                  const uint16_t* isc, void* ws, const WsLayout& L, hipStream_t st) {
   return launch_any(d, ctx_len, iq, qs_out, qscale_out, ik, isc, nullptr, ws, &L,
                     ws_ptr<uint32_t>(ws, L.flags), true, st);
+}
+
+hipError_t launch_beta(const skv_layer_desc& dv, int mq, const int32_t* ctx_len, void* ws,
+                       const WsLayout& L, hipStream_t st) {
+  const int mode = dv.index_mode;
+  const int S = mode == SKV_INDEX_SKETCH_INT4 ? dv.n_sink : 0;
+  const int Lt = mode == SKV_INDEX_SKETCH_INT4 ? dv.n_tail : 0;
+  hipLaunchKernelGGL(beta_kernel, dim3(dv.batch), dim3(1024), 0, st, ws_ptr<const uint16_t>(ws, L.sdig),
+                     L.n_samp, ctx_len, ws_ptr<TopkState>(ws, L.state), mode, dv.max_ctx, S, dv.topk,
+                     Lt, mq);
+  return hipGetLastError();
 }
 
 }  // namespace skv

@@ -23,6 +23,7 @@ constexpr int kSegTok = 256;                  // candidates per segment, token m
 constexpr int kSegBlk = 128;                  // candidates per segment, block mode (32 KB of keys per wave)
 constexpr int kAttRowsPerWave = 32;           // selected rows per attention wave
 constexpr int kMaxAttChunks = 256;            // attention partials per (sequence, KV head)
+constexpr int kMaxQueries = 16;               // query tokens per sequence in one step (MFMA tile width)
 
 // per-sequence select state written by the sample stage (u32 words)
 struct TopkState {
@@ -183,9 +184,24 @@ hipError_t launch_score_select(const skv_layer_desc& d, const int32_t* ctx_len, 
                                int8_t* qs_out, float* qscale_out, const void* ik,
                                const uint16_t* isc, int32_t* idx, int32_t* n_sel, void* ws,
                                const WsLayout& L, hipStream_t st);
+// d.batch counts virtual sequences: mq query tokens per sequence, whose K/V
+// rows are those of sequence b / mq (mq = 1: the ordinary step)
 hipError_t launch_attend(const skv_layer_desc& d, const void* q, const skv_kv_view& kv,
                          const int32_t* idx, const int32_t* n_sel, float sm_scale, float* out,
-                         void* ws, const WsLayout& L, hipStream_t st);
+                         void* ws, const WsLayout& L, hipStream_t st, int mq = 1);
+// multi-query step (token sketch): dv.batch = batch * mq virtual sequences.
+// Sample + threshold + score/collect with all mq queries of a sequence per
+// pass over its sketch (score.hip), then the per-query final select (topk.hip).
+hipError_t launch_sample_collect_multi(const skv_layer_desc& dv, int mq, const int32_t* ctx_len,
+                                       int8_t* qs_out, float* qscale_out, const void* ik,
+                                       const uint16_t* isc, void* ws, const WsLayout& L,
+                                       hipStream_t st);
+// threshold digits of the dv.batch virtual sequences from the sampled digits
+hipError_t launch_beta(const skv_layer_desc& dv, int mq, const int32_t* ctx_len, void* ws,
+                       const WsLayout& L, hipStream_t st);
+hipError_t launch_final_multi(const skv_layer_desc& dv, int mq, const int32_t* ctx_len,
+                              const int8_t* qs, const void* ik, const uint16_t* isc, int32_t* idx,
+                              int32_t* n_sel, void* ws, const WsLayout& L, hipStream_t st);
 hipError_t launch_append_block(const skv_layer_desc& d, int32_t* ctx_len, const void* k_new,
                                const void* v_new, const void* raw_new, void* stage,
                                const skv_kv_view& kv, void* index_keys, void* ws, const WsLayout& L,

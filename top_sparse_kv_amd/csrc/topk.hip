@@ -335,14 +335,14 @@ __global__ __launch_bounds__(kFT) void topk_final_kernel(
     const uint32_t* __restrict__ segcnt, Cand* __restrict__ cand, int32_t* __restrict__ idx,
     int32_t* __restrict__ n_sel,
     uint32_t* __restrict__ flags, int n_seg, int seg_items, int mode, int max_ctx, int S, int k,
-    int L, int cap) {
+    int L, int cap, int mq) {
   __shared__ uint64_t s_bhi[kListCap + 64];
   __shared__ uint32_t s_blo[kListCap + 64];
   __shared__ uint32_t s_off[kMaxSeg + 1];
   __shared__ uint32_t s_hist[256 + 32];
   __shared__ SelectShared sh;
-  const int b = blockIdx.x;
-  const int T = ctx_of(ctx_len, b, max_ctx);
+  const int b = blockIdx.x;   // virtual sequence: query b % mq of sequence b / mq
+  const int T = ctx_of_query(ctx_len, b, mq, max_ctx);
   const Range r = cand_range(mode, T, S, k, L);
   int32_t* out = idx + (size_t)b * cap;
   if (r.dense) {
@@ -571,7 +571,8 @@ __global__ __launch_bounds__(kFT) void topk_final_kernel(
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sub = lane % N, tw = lane / N;
     Src src;
-    src.init(reinterpret_cast<const uint8_t*>(iq) + (size_t)b * Src::QROW, ik, isc, b, max_ctx, sub);
+    src.init(reinterpret_cast<const uint8_t*>(iq) + (size_t)b * Src::QROW, ik, isc, b / mq, max_ctx,
+             sub);
     for (int base = wave * PER_IT; base < r.n; base += (kFT / 64) * PER_IT) {
       u32x4 w[8];
       uint32_t ax[8];
@@ -606,17 +607,18 @@ __global__ __launch_bounds__(kFT) void topk_final_kernel(
   }, r.n, k, sh, out, mode, S);
 }
 
+// d.batch counts virtual sequences (mq query tokens per sequence)
 template <class Src, bool RECOMPUTE>
 hipError_t launch_final(const skv_layer_desc& d, const int32_t* ctx_len, const double* keys,
                         const void* iq, const void* ik, const uint16_t* isc, int32_t* idx,
-                        int32_t* n_sel, void* ws, const WsLayout& Lw, hipStream_t st) {
+                        int32_t* n_sel, void* ws, const WsLayout& Lw, hipStream_t st, int mq = 1) {
   const int mode = d.index_mode;
   const int S = mode == SKV_INDEX_SKETCH_INT4 ? d.n_sink : 0;
   const int L = mode == SKV_INDEX_SKETCH_INT4 ? d.n_tail : 0;
   hipLaunchKernelGGL((topk_final_kernel<Src, RECOMPUTE>), dim3(d.batch), dim3(kFT), 0, st,
                      keys, iq, ik, isc, ctx_len, ws_ptr<uint32_t>(ws, Lw.segcnt),
                      ws_ptr<Cand>(ws, Lw.cand), idx, n_sel, ws_ptr<uint32_t>(ws, Lw.flags),
-                     Lw.n_seg, Lw.seg_items, mode, d.max_ctx, S, d.topk, L, select_capacity(d));
+                     Lw.n_seg, Lw.seg_items, mode, d.max_ctx, S, d.topk, L, select_capacity(d), mq);
   return hipGetLastError();
 }
 
@@ -643,6 +645,17 @@ hipError_t launch_topk(const skv_layer_desc& d, const int32_t* ctx_len, const do
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_final<NoSrc, false>(d, ctx_len, keys, nullptr, nullptr, nullptr, idx, n_sel, ws, Lw, st);
+}
+
+hipError_t launch_final_multi(const skv_layer_desc& dv, int mq, const int32_t* ctx_len,
+                              const int8_t* qs, const void* ik, const uint16_t* isc, int32_t* idx,
+                              int32_t* n_sel, void* ws, const WsLayout& Lw, hipStream_t st) {
+  switch (dv.n_kv_heads * dv.rank / 2) {
+    case 64: return launch_final<SketchSrc<4>, true>(dv, ctx_len, nullptr, qs, ik, isc, idx, n_sel, ws, Lw, st, mq);
+    case 128: return launch_final<SketchSrc<8>, true>(dv, ctx_len, nullptr, qs, ik, isc, idx, n_sel, ws, Lw, st, mq);
+    case 256: return launch_final<SketchSrc<16>, true>(dv, ctx_len, nullptr, qs, ik, isc, idx, n_sel, ws, Lw, st, mq);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_score_select(const skv_layer_desc& d, const int32_t* ctx_len, const void* iq,
