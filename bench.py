@@ -54,6 +54,10 @@ CONFIGS = {
     "cfg4b": dict(kind="token", B=32, T=250_000, n_kv=4, n_q=24, D=256, S=64, k=2048, L=1024,
                   kv="i8", layers=2, seed=1014, mixed=(2048, 250_000),
                   workload="32 seq, lengths uniform in 2,048..250,000 (seeded); cfg2 layer shape"),
+    "cfg2m": dict(kind="token", B=8, T=250_000, n_kv=4, n_q=24, D=256, S=64, k=2048, L=1024,
+                  kv="i8", layers=8, seed=1002, M=8,
+                  workload="8 seq x 250,000 tokens, 8 query tokens each (current + 7 drafted, "
+                           "one pick per query at its causal context); cfg2 layer shape"),
     "cfg5": dict(kind="tier", B=4, T=250_000, n_kv=4, n_q=24, D=256, S=64, k=2048, L=1024,
                  kv="i8", layers=1, seed=1005, warm_steps=64, steps=256,
                  workload="4 seq x 250,000 tokens; cfg2 layer shape; int4 host-RAM K/V records read "
@@ -99,14 +103,37 @@ class Layer:
         self.case = c
         self.ctx = c.ctx_len
         cap = skv.select_capacity(self.desc)
+        self.M = cfg.get("M", 0)
+        if self.M:
+            # several query tokens per sequence (sparsekv_step_multi)
+            M, nq = self.M, c.n_kv * c.R
+            self.mq = synth.multi_queries(c.B, M, c.n_q, c.D, seed, device="cuda")
+            self.mqs = torch.zeros((c.B, M, nq), dtype=torch.int8, device="cuda")
+            self.mqsc = torch.zeros((c.B, M), dtype=torch.float32, device="cuda")
+            self.midx = torch.zeros((c.B, M, cap), dtype=torch.int32, device="cuda")
+            self.mnsel = torch.zeros((c.B, M), dtype=torch.int32, device="cuda")
+            self.mout = torch.zeros((c.B, M, c.n_q, c.D), dtype=torch.float32, device="cuda")
         self.idx = torch.zeros((c.B, cap), dtype=torch.int32, device="cuda")
         self.nsel = torch.zeros((c.B,), dtype=torch.int32, device="cuda")
         self.out = torch.zeros((c.B, c.n_q, c.D), dtype=torch.float32, device="cuda")
         self.sm = c.D ** -0.5
 
     def step(self, ws):
+        if self.M:
+            skv.step_multi(self.desc, self.M, self.ctx, self.mq, self.basis, self.mqs, self.mqsc,
+                           self.ikeys, self.iscale, self.kv, self.midx, self.mnsel, self.sm,
+                           self.mout, ws)
+            return
         skv.step(self.desc, self.ctx, self.q, self.basis, self.qs, self.qsc, self.iq, self.ikeys,
                  self.iscale, self.kv, self.idx, self.nsel, self.sm, self.out, ws)
+
+    def union_rows(self):
+        """Distinct (sequence, row) pairs the last multi-query step attended:
+        the rows a step must gather at least once."""
+        n = self.mnsel.cpu().numpy()
+        idx = self.midx.cpu().numpy()
+        return sum(len(np.unique(np.concatenate([idx[b, j, :n[b, j]] for j in range(self.M)])))
+                   for b in range(self.case.B))
 
     def qsketch(self, ws):
         skv.qsketch(self.desc, self.q, self.basis, self.qs, self.qsc, ws)
@@ -148,6 +175,16 @@ def algorithmic_bytes(cfg, lens=None):
     out = B * n_q * D * 4
     return dict(scan=scan, gather=gather, other=qbytes + out + basis,
                 total=scan + gather + qbytes + out + basis)
+
+
+def algorithmic_bytes_multi(cfg, union_rows):
+    """Multi-query step: the sketch is scanned once for all queries; the K/V
+    rows attended by any query of a sequence are gathered at least once."""
+    B, D, n_kv, n_q, M = cfg["B"], cfg["D"], cfg["n_kv"], cfg["n_q"], cfg["M"]
+    scan = B * (cfg["T"] - cfg["S"] - cfg["L"]) * (n_kv * 64 // 2 + 2)
+    gather = union_rows * n_kv * (D + 2) * 2
+    other = B * M * n_q * D * (2 + 4) + n_kv * D * 64 * 4
+    return dict(scan=scan, gather=gather, other=other, total=scan + gather + other)
 
 
 def time_loop(fn, layers, ws, n):
@@ -243,6 +280,24 @@ def _cpu_baseline(layer: Layer, cfg, min_seconds=10.0, max_reps=20):
     import oracle
     c = layer.case
     t_total, reps, rows = 0.0, 0, None
+    if cfg.get("M"):
+        # one sequence (of the batch) x M query tokens per repetition
+        M, b = cfg["M"], 0
+        host = [x[b:b + 1].cpu().numpy() for x in (c.codes, c.sk_scale, c.k_cache, c.v_cache,
+                                                     c.k_scale, c.v_scale)]
+        qm = layer.mq[b:b + 1].cpu().numpy()
+        basis = c.basis.cpu().numpy()
+        while reps < max_reps and (reps == 0 or t_total < min_seconds):
+            t = time.perf_counter()
+            oracle.multiquery.token_step_multi(qm, basis, *host, [c.lens[b]], M=M, S=c.S,
+                                               k_top=c.k, L=c.L, group=c.group, sm_scale=layer.sm,
+                                               fmt="i8")
+            t_total += time.perf_counter() - t
+            reps += 1
+        return dict(value=reps / t_total / c.B, unit="layer-steps/s", cores=1, kind="oracle",
+                    sample="%d repetitions of sequence 0 of layer 0 (%d query tokens x %d tokens); "
+                           "value scaled to the %d-sequence batch" % (reps, M, c.T_max, c.B),
+                    seconds=t_total)
     if cfg["kind"] == "token":
         q = c.q.cpu().numpy()
         basis = c.basis.cpu().numpy()
@@ -413,7 +468,8 @@ def main():
     log("generating %d layers of %s" % (n_layers, args.config))
     layers = [Layer(cfg, li) for li in range(n_layers)]
     torch.cuda.synchronize()
-    ws = skv.workspace(layers[0].desc)
+    multi = cfg.get("M", 0)
+    ws = skv.workspace_multi(layers[0].desc, multi) if multi else skv.workspace(layers[0].desc)
     log("warmup", args.warmup)
     for i in range(args.warmup):
         layers[i % n_layers].step(ws)
@@ -428,14 +484,14 @@ def main():
     skv.timer_enable(False)
     nk = max(50, args.steps // 2)
     kt = {}
-    for name in (["qsketch"] if cfg["kind"] == "token" else []) + ["score", "score_topk", "topk",
-                                                                   "attend"]:
+    for name in [] if multi else (["qsketch"] if cfg["kind"] == "token" else []) + [
+            "score", "score_topk", "topk", "attend"]:
         fn = getattr(Layer, name)
         for i in range(5):
             fn(layers[i % n_layers], ws)
         kt[name] = time_loop(fn, layers, ws, nk) / nk
     skv.check(ws)
-    if cfg["kind"] == "token":
+    if cfg["kind"] == "token" and not multi:
         # the decode-step append (new token's K/V rows and key sketch), written
         # 2000 rows before the end so every call lands inside the cache; runs
         # after the step timings because it overwrites cache rows
@@ -453,12 +509,16 @@ def main():
             append_call(L0, ws)
         kt["append"] = time_loop(append_call, [L0], ws, nk) / nk
         skv.check(ws)
-    ab = algorithmic_bytes(cfg, layers[0].case.lens if cfg["kind"] == "token" else None)
+    if multi:
+        layers[0].step(ws)
+        ab = algorithmic_bytes_multi(cfg, layers[0].union_rows())
+    else:
+        ab = algorithmic_bytes(cfg, layers[0].case.lens if cfg["kind"] == "token" else None)
     value = args.steps / secs
     # the dominant kernel of the step: the fused score-and-collect stream
     score_s = score_ms / 1e3 / max(1, score_n)
     traffic = committed_traffic() if args.config == "cfg2" else None
-    roof = dict(kernel="score_collect", bound="hbm",
+    roof = dict(kernel="score_collect_multi" if multi else "score_collect", bound="hbm",
                 achieved=round(ab["scan"] / score_s / 1e9, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                 frac=round(ab["scan"] / score_s / 1e9 / PEAK_HBM_GBS, 4), traffic=traffic,
                 bytes_per_launch=ab["scan"], avg_launch_us=round(score_s * 1e6, 2),
@@ -476,13 +536,17 @@ def main():
         "vs_baseline": None,
         "dtype": "i8" if cfg["kind"] == "token" else "bf16",
         "data": "synthetic",
-        "config": {"workload": cfg["workload"], "name": args.config, "batch": cfg["B"],
-                   "ctx": cfg["T"], "rotating_layers": n_layers},
+        "config": dict({"workload": cfg["workload"], "name": args.config, "batch": cfg["B"],
+                        "ctx": cfg["T"], "rotating_layers": n_layers},
+                       **({"query_tokens_per_seq": multi} if multi else {})),
         "step_hbm": {"algorithmic_bytes": ab["total"], "achieved_GBps": round(ab["total"] * value / 1e9, 1),
                      "frac_of_peak": round(ab["total"] * value / 1e9 / PEAK_HBM_GBS, 4)},
         "kernels_us": {k: round(v * 1e6, 2) for k, v in kt.items()},
         "roofline": roof,
     }
+    if multi:
+        res["query_tokens_per_s"] = round(value * cfg["B"] * multi, 1)
+        res["step_hbm"]["union_rows"] = int(ab["gather"] // (cfg["n_kv"] * (cfg["D"] + 2) * 2))
     if args.calib_copy:
         # a plain stream of known size (reads CALIB_BYTES, writes CALIB_BYTES);
         # bitwise_not is used nowhere else, so its counter rows are unambiguous

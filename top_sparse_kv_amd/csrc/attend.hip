@@ -91,7 +91,7 @@ __global__ __launch_bounds__(64 * WAVES) void attend_kernel(
     const uint16_t* __restrict__ ksc, const uint16_t* __restrict__ vsc, int64_t rows,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ n_sel, int cap,
     float scale_log2, int Hq, int Hkv, float* __restrict__ part_ml, float* __restrict__ part_o,
-    int n_chunks, uint32_t* __restrict__ flags, int mq) {
+    int n_chunks, uint32_t* __restrict__ flags, int mq, int n_keys) {
   constexpr bool BF = KVT == KV_BF16;
   constexpr int ES = Esize<KVT>::v;
   constexpr int KSTEPS = D / 32;          // MFMA k-steps over head_dim
@@ -110,7 +110,25 @@ __global__ __launch_bounds__(64 * WAVES) void attend_kernel(
   __shared__ uint32_t s_q[16 * QP / 2];   // Q of the G heads, one row per head
   extern __shared__ float s_o[];          // [HALF][G][D + 4]
 
-  const int h = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
+  // Workgroup -> (KV head h, chunk c, virtual sequence b).  One query per
+  // sequence: the 3-D grid.  Several: workgroups are dealt to the 8 XCDs in
+  // turn (linear id mod 8), each XCD with its own L2, and the mq queries of
+  // one (sequence, head, chunk) get ids that land on one XCD back to back, so
+  // the rows they share (sinks, and the tail that moves by one position per
+  // query) tend to be read from HBM once.
+  int h, c, b;
+  if (mq == 1) {
+    h = blockIdx.x;
+    c = blockIdx.y;
+    b = blockIdx.z;
+  } else {
+    const int xcd = blockIdx.x & 7, s = blockIdx.x >> 3;
+    const int key = (s / mq) * 8 + xcd;   // (sequence, chunk, head), head fastest
+    if (key >= n_keys) return;            // padding of the last round; before any barrier
+    h = key % Hkv;
+    c = (key / Hkv) % n_chunks;
+    b = (key / Hkv / n_chunks) * mq + s % mq;
+  }
   const int G = Hq / Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, g = lane >> 4;
@@ -492,7 +510,11 @@ hipError_t launch_attend(const skv_layer_desc& d, const void* q, const skv_kv_vi
   const int cap = select_capacity(d);
   const int G = d.n_q_heads / d.n_kv_heads;
   if (Lw.n_att_chunks > kMaxChunks) return hipErrorInvalidValue;
-  const dim3 grid(d.n_kv_heads, Lw.n_att_chunks, d.batch);
+  // one workgroup per (sequence, chunk, head) and query; several queries:
+  // a 1-D grid padded to whole rounds of 8 (sequence, chunk, head) keys
+  const int n_keys = d.batch / mq * Lw.n_att_chunks * d.n_kv_heads;
+  const dim3 grid = mq == 1 ? dim3(d.n_kv_heads, Lw.n_att_chunks, d.batch)
+                            : dim3((unsigned)(((n_keys + 7) / 8) * 8 * mq));
   const int waves = att_waves(d);
   const size_t lds = (size_t)(waves / 2) * G * (d.head_dim + 4) * sizeof(float);
   const float sl = sm_scale * kLog2e;
@@ -500,7 +522,7 @@ hipError_t launch_attend(const skv_layer_desc& d, const void* q, const skv_kv_vi
   hipLaunchKernelGGL((attend_kernel<KVT, DD, WV>), grid, dim3(64 * WV), lds, st, q,              \
                      (const uint8_t*)kv.k, (const uint8_t*)kv.v, kv.k_scale, kv.v_scale, kv.rows, \
                      idx, n_sel, cap, sl, d.n_q_heads, d.n_kv_heads, part_ml, part_o,             \
-                     Lw.n_att_chunks, flags, mq)
+                     Lw.n_att_chunks, flags, mq, n_keys)
 #define SKV_AT_W(KVT, DD)                                                                          \
   do {                                                                                             \
     if (waves == 16) SKV_AT(KVT, DD, 16);                                                          \

@@ -37,6 +37,8 @@
 //                         records, the per-wave counts exchanged in LDS.
 #include "keys_common.h"
 
+#include <hip/hip_ext.h>
+
 namespace skv {
 namespace {
 
@@ -191,7 +193,22 @@ __global__ __launch_bounds__(kThreads) void score_multi_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15, g = lane >> 4;
   const int first = i0 + 64 * wave;
-  // the wave's 64 tokens, issued before anything else
+  // the scale, the query rows and then the wave's 64 tokens: loads return in
+  // order, so the LDS staging before the barrier waits only for the first
+  // ones and the tiles can start as their codes arrive
+  const uint32_t sc_l = isc[(size_t)b * max_ctx + r.lo + min(first + lane, i1 - 1)];
+  const QueryRange qr = query_range(T, mq, j, S, k, L);
+  const uint32_t beta = qr.active ? state[(size_t)b * mq + j].beta : 0xFFFFFFFFu;
+  {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(qs + (size_t)b * mq * NQ);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(s_q);
+#pragma unroll
+    for (int u = 0; u < kMaxQueries * NQ / 4 / kThreads; ++u) {
+      const int i = threadIdx.x + u * kThreads;
+      const uint32_t v = src[min(i, mq * NQ / 4 - 1)];   // unconditional
+      dst[i] = i < mq * NQ / 4 ? v : 0u;
+    }
+  }
   const uint8_t* cb = ik + (size_t)b * max_ctx * TB + 16 * g;
   u32x4 w[kTiles][NL];
 #pragma unroll
@@ -201,15 +218,6 @@ __global__ __launch_bounds__(kThreads) void score_multi_kernel(
     for (int m = 0; m < NL; ++m)
       w[t][m] = __builtin_nontemporal_load(
           reinterpret_cast<const u32x4*>(cb + (size_t)(r.lo + i) * TB + 64 * m));
-  }
-  const uint32_t sc_l = isc[(size_t)b * max_ctx + r.lo + min(first + lane, i1 - 1)];
-  const QueryRange qr = query_range(T, mq, j, S, k, L);
-  const uint32_t beta = qr.active ? state[(size_t)b * mq + j].beta : 0xFFFFFFFFu;
-  {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(qs + (size_t)b * mq * NQ);
-    uint32_t* dst = reinterpret_cast<uint32_t*>(s_q);
-    for (int i = threadIdx.x; i < kMaxQueries * NQ / 4; i += kThreads)
-      dst[i] = i < mq * NQ / 4 ? src[i] : 0u;
   }
   __syncthreads();
   MqTile<TB> tile;
@@ -274,6 +282,36 @@ __global__ __launch_bounds__(kThreads) void score_multi_kernel(
   }
 }
 
+template <int TB>
+hipError_t launch_multi_tb(const skv_layer_desc& dv, int mq, const int32_t* ctx_len, int8_t* qs_out,
+                           float* qscale_out, const uint8_t* ik, const uint16_t* isc, void* ws,
+                           const WsLayout& L, hipStream_t st) {
+  const int B = dv.batch / mq;
+  const dim3 sgrid((L.n_samp + kTiles * (kThreads / 64) - 1) / (kTiles * (kThreads / 64)), B);
+  hipLaunchKernelGGL((sample_multi_kernel<TB>), sgrid, dim3(kThreads), 0, st,
+                     ws_ptr<const float>(ws, L.sproj), qs_out, qscale_out, mq, ik, isc, ctx_len,
+                     ws_ptr<uint16_t>(ws, L.sdig), L.n_samp, dv.max_ctx, dv.n_sink, dv.topk,
+                     dv.n_tail);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = launch_beta(dv, mq, ctx_len, ws, L, st);
+  if (e != hipSuccess) return e;
+  const dim3 grid(L.n_seg, B);
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  if (timer_next(&ev0, &ev1))
+    hipExtLaunchKernelGGL((score_multi_kernel<TB>), grid, dim3(kThreads), 0, st, ev0, ev1, 0,
+                          (const int8_t*)qs_out, ik, isc, ctx_len, ws_ptr<const TopkState>(ws, L.state),
+                          ws_ptr<Cand>(ws, L.cand), ws_ptr<uint32_t>(ws, L.segcnt),
+                          ws_ptr<uint32_t>(ws, L.flags), dv.max_ctx, dv.n_sink, dv.topk, dv.n_tail,
+                          L.n_seg, mq);
+  else
+    hipLaunchKernelGGL((score_multi_kernel<TB>), grid, dim3(kThreads), 0, st, (const int8_t*)qs_out,
+                       ik, isc, ctx_len, ws_ptr<const TopkState>(ws, L.state),
+                       ws_ptr<Cand>(ws, L.cand), ws_ptr<uint32_t>(ws, L.segcnt),
+                       ws_ptr<uint32_t>(ws, L.flags), dv.max_ctx, dv.n_sink, dv.topk, dv.n_tail,
+                       L.n_seg, mq);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_sample_collect_multi(const skv_layer_desc& dv, int mq, const int32_t* ctx_len,
@@ -282,34 +320,13 @@ hipError_t launch_sample_collect_multi(const skv_layer_desc& dv, int mq, const i
                                        hipStream_t st) {
   if (mq < 1 || mq > kMaxQueries || dv.batch % mq || dv.index_mode != SKV_INDEX_SKETCH_INT4)
     return hipErrorInvalidValue;
-  const int B = dv.batch / mq;
-  const int TB = dv.n_kv_heads * dv.rank / 2;
-  const dim3 sgrid((L.n_samp + kTiles * (kThreads / 64) - 1) / (kTiles * (kThreads / 64)), B);
-  const dim3 grid(L.n_seg, B);
-  const float* sproj = ws_ptr<const float>(ws, L.sproj);
-  uint16_t* sdig = ws_ptr<uint16_t>(ws, L.sdig);
   const uint8_t* ikb = reinterpret_cast<const uint8_t*>(ik);
-#define SKV_MQ(TBV)                                                                                \
-  do {                                                                                             \
-    hipLaunchKernelGGL((sample_multi_kernel<TBV>), sgrid, dim3(kThreads), 0, st, sproj, qs_out,   \
-                       qscale_out, mq, ikb, isc, ctx_len, sdig, L.n_samp, dv.max_ctx, dv.n_sink,  \
-                       dv.topk, dv.n_tail);                                                        \
-    hipError_t e_ = hipGetLastError();                                                             \
-    if (e_ == hipSuccess) e_ = launch_beta(dv, mq, ctx_len, ws, L, st);                            \
-    if (e_ != hipSuccess) return e_;                                                               \
-    hipLaunchKernelGGL((score_multi_kernel<TBV>), grid, dim3(kThreads), 0, st, qs_out, ikb, isc,  \
-                       ctx_len, ws_ptr<const TopkState>(ws, L.state), ws_ptr<Cand>(ws, L.cand),    \
-                       ws_ptr<uint32_t>(ws, L.segcnt), ws_ptr<uint32_t>(ws, L.flags),              \
-                       dv.max_ctx, dv.n_sink, dv.topk, dv.n_tail, L.n_seg, mq);                    \
-  } while (0)
-  switch (TB) {
-    case 64: SKV_MQ(64); break;
-    case 128: SKV_MQ(128); break;
-    case 256: SKV_MQ(256); break;
+  switch (dv.n_kv_heads * dv.rank / 2) {
+    case 64: return launch_multi_tb<64>(dv, mq, ctx_len, qs_out, qscale_out, ikb, isc, ws, L, st);
+    case 128: return launch_multi_tb<128>(dv, mq, ctx_len, qs_out, qscale_out, ikb, isc, ws, L, st);
+    case 256: return launch_multi_tb<256>(dv, mq, ctx_len, qs_out, qscale_out, ikb, isc, ws, L, st);
     default: return hipErrorInvalidValue;
   }
-#undef SKV_MQ
-  return hipGetLastError();
 }
 
 }  // namespace skv
