@@ -9,3 +9,4 @@ from .step import *  # noqa: F401,F403
 from .step import PINS  # noqa: F401
 from . import append  # noqa: F401
 from . import multiquery  # noqa: F401
+from . import prefill  # noqa: F401

@@ -19,6 +19,7 @@ from .gen import (  # noqa: F401
     make_tier_case,
     drift_picks,
     multi_queries,
+    prefill_picks,
     orthonormal_basis,
     pack_int4,
     flush_bf16_domain,

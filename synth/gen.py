@@ -35,6 +35,7 @@ _MUL = 1_000_003
 _T_Q, _T_BASIS, _T_SKETCH, _T_K, _T_V, _T_NEEDLE = 1, 2, 3, 4, 5, 6
 _T_QI, _T_RAWIDX, _T_HK, _T_HV, _T_RK, _T_RV, _T_DRIFT, _T_LEN = 7, 8, 9, 10, 11, 12, 13, 14
 _T_MQ = 15
+_T_PICKS = 16
 
 
 def _subseed(seed: int, *ids: int) -> int:
@@ -142,6 +143,33 @@ def multi_queries(B: int, M: int, n_q: int, D: int, seed: int, device="cpu") -> 
     """Queries of M tokens per sequence (a verification step): N(0, 1) -> fp16
     [B][M][n_q][D]."""
     return _randn("cpu", seed, (_T_MQ,), (B, M, n_q, D)).to(torch.float16).to(device)
+
+
+def prefill_picks(P: int, T: int, k_blocks: int, seed: int):
+    """Selections of P prefill tokens at positions T-P .. T-1 (block mode): query
+    p (context T_p = T-P+1+p) takes k_blocks distinct complete blocks drawn
+    uniformly from [0, T_p // 4) -- all of them while there are at most
+    k_blocks -- expanded to 4 tokens each, plus the tokens of its partial
+    block.  Returns (idx int32 [P][4*k_blocks+3], n_sel int32 [P])."""
+    g = np.random.default_rng(_subseed(seed, _T_PICKS))
+    cap = 4 * k_blocks + 3
+    idx = np.zeros((P, cap), dtype=np.int32)
+    n_sel = np.zeros(P, dtype=np.int32)
+    for p in range(P):
+        Tp = T - P + 1 + p
+        nb = Tp // 4
+        if nb <= k_blocks:
+            blocks = np.arange(nb)
+        else:
+            blocks = np.unique(g.integers(0, nb, size=k_blocks + k_blocks // 4 + 16))
+            while blocks.size < k_blocks:
+                blocks = np.unique(np.concatenate([blocks, g.integers(0, nb, size=k_blocks)]))
+            blocks = np.sort(g.permutation(blocks)[:k_blocks])
+        toks = (4 * blocks[:, None] + np.arange(4)[None, :]).reshape(-1)
+        toks = np.concatenate([toks, np.arange(4 * nb, Tp)])
+        idx[p, :toks.size] = toks
+        n_sel[p] = toks.size
+    return idx, n_sel
 
 
 # ----------------------------------------------------------------------------

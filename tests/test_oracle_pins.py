@@ -716,3 +716,59 @@ def test_multi_equal_queries_nested_picks():
         assert len(mid_a) == len(mid_b) == k
         assert mid_b - mid_a <= {Tj - L}
         assert len(mid_a - mid_b) == len(mid_b - mid_a)
+
+
+# --------------------------------------------------------------------------
+# prefill attention over host-resident K/V
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt", ["bf16", "f16"])
+def test_prefill_attention_is_masked_sdpa(fmt):
+    """Each prefill query attends exactly its own listed rows: all P outputs at
+    once equal torch's fp64 SDPA with a boolean mask built from the lists; an
+    empty list gives zeros."""
+    T, P, n_kv, n_q, D = 700, 12, 2, 8, 64
+    g = torch.Generator().manual_seed(41)
+    k = torch.randn((T, n_kv, D), generator=g)
+    v = torch.randn((T, n_kv, D), generator=g)
+    q = torch.randn((P, n_q, D), generator=g)
+    idx, n_sel = synth.prefill_picks(P, T, 24, 42)
+    n_sel[3] = 0
+    lists = [idx[p, :n_sel[p]].astype(np.int64) for p in range(P)]
+    if fmt == "bf16":
+        kb, vb, qb = (x.to(torch.bfloat16) for x in (k, v, q))
+        args = [x.view(torch.int16).numpy().view(np.uint16) for x in (qb, kb, vb)]
+    else:
+        kb, vb, qb = (x.to(torch.float16) for x in (k, v, q))
+        args = [x.numpy() for x in (qb, kb, vb)]
+    out = oracle.prefill.prefill_attention(args[0], args[1], args[2], lists, 0.125, n_q // n_kv, fmt)
+    mask = torch.zeros((P, T), dtype=torch.bool)
+    for p in range(P):
+        mask[p, lists[p]] = True
+    kk = kb.double().permute(1, 0, 2).repeat_interleave(n_q // n_kv, dim=0)   # [H_q][T][D]
+    vv = vb.double().permute(1, 0, 2).repeat_interleave(n_q // n_kv, dim=0)
+    qq = qb.double().permute(1, 0, 2)                                          # [H_q][P][D]
+    ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, attn_mask=mask, scale=0.125)
+    ref = ref.permute(1, 0, 2).numpy()
+    for p in range(P):
+        if n_sel[p] == 0:
+            assert not out[p].any()
+        else:
+            np.testing.assert_allclose(out[p], ref[p], rtol=0, atol=1e-12)
+
+
+def test_prefill_transfer_closed_forms():
+    """[P4] "The Downside to Keep in Mind": a 4096-token prefill chunk whose
+    tokens each fetch their own 2048 picks moves 4096 x 2048 x 24 KiB (K and V,
+    2 KV heads x 256 x bf16, 12 layers) = 192 GiB (the page prints 204 GiB,
+    kept as an unreconciled figure); 256 such chunks for 1 Mi tokens take about
+    half an hour at 26 GB/s; the chunk loop moves each history row once,
+    independent of the working-buffer size."""
+    per_layer = oracle.prefill.per_token_transfer_bytes([2048] * 4096, 2, 256, 2)
+    assert 12 * per_layer == 192 * 1024 * MiB
+    minutes = 256 * 12 * per_layer / 26e9 / 60
+    assert 25 <= minutes <= 40
+    T = 1 << 20
+    once = oracle.prefill.chunked_transfer_bytes(T, 2, 256, 2)
+    assert once == 2 * 1024 * MiB and 12 * once == 24 * 1024 * MiB
+    assert per_layer // once == 8   # 4096 x 2048 picks vs 1 Mi rows
