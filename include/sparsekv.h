@@ -261,6 +261,43 @@ skv_status sparsekv_step_multi(const skv_layer_desc* d, int32_t n_query, const i
                                const skv_kv_view* kv, int32_t* idx, int32_t* n_sel, float sm_scale,
                                float* out, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- prefill attention over K/V rows in host memory -------------------------
+ * Page "3.14M Context ...", sections "What Needs to Stay in VRAM" (K and V in
+ * host RAM) and "The Downside to Keep in Mind": every prefill token has its
+ * own pick, so the history is streamed once in fixed-size chunks through a
+ * small device buffer, all queries are computed against each chunk and their
+ * partial softmax results merged.  The bytes copied are the history once,
+ * whatever chunk_bytes is.
+ *   d          layer shape: n_kv_heads, n_q_heads, head_dim; kv_dtype SKV_KV_F16
+ *              or SKV_KV_BF16 with the matching q_dtype
+ *   n_query    P >= 1 query tokens
+ *   q          device [P][H_q][D] fp16 / bf16
+ *   idx        device [P][cap] int32: query p's picked positions, ascending and
+ *              < n_tokens, in its first n_sel[p] entries (n_sel device [P])
+ *   host_k, host_v  host [n_tokens][H_kv][D] rows (fp16 / bf16); pinned memory
+ *              (hipHostMalloc) is copied by DMA, pageable memory is staged by
+ *              the runtime
+ *   chunk_buf  device working buffer of chunk_bytes, 16-byte aligned: chunks of
+ *              floor(chunk_bytes / (2*H_kv*D*2)) tokens' K and V rows
+ *   out        device [P][H_q][D] fp32: softmax of (q_j . k_t)*sm_scale over
+ *              query p's listed rows t, times V (KV head of query head j is
+ *              j / (H_q/H_kv)); zeros when n_sel[p] = 0
+ *   ws         sparsekv_prefill_workspace_size(d, P) bytes, 256-byte aligned: a
+ *              flag word (read by sparsekv_check), then the running (max, sum)
+ *              and accumulator of every query head
+ * Enqueues on `stream` a state reset, then per chunk two host-to-device copies
+ * and one kernel, then the normalisation; returns without waiting.  The host
+ * rows and all buffers must stay valid until the stream has passed them.  An
+ * index outside [0, n_tokens) or n_sel outside [0, cap] is skipped / clamped
+ * and raises SKV_FLAG_INDEX_RANGE; so does a list entry found outside the
+ * chunk being processed (an unsorted list). */
+skv_status sparsekv_prefill_workspace_size(const skv_layer_desc* d, int32_t n_query, size_t* bytes);
+skv_status sparsekv_prefill_attend(const skv_layer_desc* d, int32_t n_query, const void* q,
+                                   const int32_t* idx, const int32_t* n_sel, int32_t cap,
+                                   const void* host_k, const void* host_v, int64_t n_tokens,
+                                   void* chunk_buf, size_t chunk_bytes, float sm_scale, float* out,
+                                   void* ws, size_t ws_bytes, void* stream);
+
 /* ---- append: the new token of every sequence into the caches ---------------
  * Page "8 agents x 250K ...", section "The mechanism" (int8 K/V rows with a
  * per-row scale, int4 rank-64 key sketch with one fp16 scale per token); page

@@ -167,6 +167,29 @@ def step_multi(desc, n_query, ctx_len, q, basis, qs, qs_scale, index_keys, index
                                      _p(ws), ws.numel(), _stream(stream)))
 
 
+def prefill_workspace_size(desc: LayerDesc, n_query: int) -> int:
+    n = _lib.c_sz()
+    _check(lib().sparsekv_prefill_workspace_size(ctypes.byref(desc), int(n_query), ctypes.byref(n)))
+    return n.value
+
+
+def prefill_attend(desc, q, idx, n_sel, host_k, host_v, chunk_buf, sm_scale, out, ws, stream=None):
+    """Attention of P prefill queries over their picked rows of K/V held in host
+    memory, streamed once through chunk_buf (sparsekv_prefill_attend).  q
+    [P][H_q][D], idx [P][cap], n_sel [P], out [P][H_q][D] on the device;
+    host_k / host_v [T][H_kv][D] host tensors (pinned for DMA)."""
+    _dev(q, idx, n_sel, chunk_buf, out, ws)
+    for t in (host_k, host_v):
+        if t.is_cuda or not t.is_contiguous():
+            raise ValueError("host_k / host_v must be contiguous host tensors")
+    _check(lib().sparsekv_prefill_attend(ctypes.byref(desc), q.shape[0], _p(q), _p(idx), _p(n_sel),
+                                         idx.shape[1], ctypes.c_void_p(host_k.data_ptr()),
+                                         ctypes.c_void_p(host_v.data_ptr()), host_k.shape[0],
+                                         _p(chunk_buf), chunk_buf.numel() * chunk_buf.element_size(),
+                                         float(sm_scale), _p(out), _p(ws), ws.numel(),
+                                         _stream(stream)))
+
+
 def append(desc, ctx_len, k_new, v_new, basis, kv: KVView, index_keys, index_scale, ws, stream=None):
     """Writes the new token of every sequence at row ctx_len[b] (K/V rows,
     key sketch) and advances ctx_len (sparsekv_append)."""

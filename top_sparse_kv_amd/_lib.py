@@ -72,6 +72,9 @@ SIGNATURES = [
     ("sparsekv_workspace_size_multi", c_i32, [P(LayerDesc), c_i32, P(c_sz)]),
     ("sparsekv_step_multi", c_i32, [P(LayerDesc), c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                     P(KVView), c_vp, c_vp, ctypes.c_float, c_vp, c_vp, c_sz, c_vp]),
+    ("sparsekv_prefill_workspace_size", c_i32, [P(LayerDesc), c_i32, P(c_sz)]),
+    ("sparsekv_prefill_attend", c_i32, [P(LayerDesc), c_i32, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp,
+                                        c_i64, c_vp, c_sz, ctypes.c_float, c_vp, c_vp, c_sz, c_vp]),
     ("sparsekv_append", c_i32, [P(LayerDesc), c_vp, c_vp, c_vp, c_vp, P(KVView), c_vp, c_vp, c_vp,
                                 c_sz, c_vp]),
     ("sparsekv_append_block", c_i32, [P(LayerDesc), c_vp, c_vp, c_vp, c_vp, c_vp, P(KVView), c_vp,

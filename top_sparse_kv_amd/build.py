@@ -21,7 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsparsekv.so")
 SOURCES = ["api.hip", "qsketch.hip", "score.hip", "score_multi.hip", "topk.hip", "attend.hip", "tier.hip",
-           "append.hip"]
+           "append.hip", "prefill.hip"]
 ARCH = "gfx950"
 
 

@@ -6,6 +6,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
+#include <stdint.h>
 
 #include <vector>
 
@@ -221,6 +222,49 @@ skv_status sparsekv_step_multi(const skv_layer_desc* d, int32_t n_query, const i
     e = launch_final_multi(dv, n_query, ctx_len, qs, index_keys, index_scale, idx, n_sel, ws, L, st);
   if (e == hipSuccess) e = launch_attend(dv, q, *kv, idx, n_sel, sm_scale, out, ws, L, st, n_query);
   return launched(e, "step_multi");
+}
+
+static skv_status prefill_desc(const skv_layer_desc* d, int32_t n_query) {
+  skv_status s = validate_desc(d);
+  if (s != SKV_OK) return s;
+  if (d->kv_dtype != SKV_KV_F16 && d->kv_dtype != SKV_KV_BF16)
+    return set_error(SKV_ERR_UNSUPPORTED, "prefill: K/V rows must be fp16 or bf16");
+  if ((d->kv_dtype == SKV_KV_BF16) != (d->q_dtype == SKV_Q_BF16))
+    return set_error(SKV_ERR_UNSUPPORTED, "prefill: queries must have the K/V element type");
+  if (n_query < 1) return set_error(SKV_ERR_INVALID, "prefill: n_query %d < 1", n_query);
+  return SKV_OK;
+}
+
+skv_status sparsekv_prefill_workspace_size(const skv_layer_desc* d, int32_t n_query, size_t* bytes) {
+  skv_status s = prefill_desc(d, n_query);
+  if (s != SKV_OK) return s;
+  if (!bytes) return set_error(SKV_ERR_INVALID, "bytes is NULL");
+  *bytes = prefill_workspace_bytes(*d, n_query);
+  return ok();
+}
+
+skv_status sparsekv_prefill_attend(const skv_layer_desc* d, int32_t n_query, const void* q,
+                                   const int32_t* idx, const int32_t* n_sel, int32_t cap,
+                                   const void* host_k, const void* host_v, int64_t n_tokens,
+                                   void* chunk_buf, size_t chunk_bytes, float sm_scale, float* out,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  skv_status s = prefill_desc(d, n_query);
+  if (s != SKV_OK) return s;
+  if (!q || !idx || !n_sel || !host_k || !host_v || !chunk_buf || !out || !ws)
+    return set_error(SKV_ERR_INVALID, "prefill: NULL pointer");
+  if (cap < 1) return set_error(SKV_ERR_INVALID, "prefill: cap %d < 1", cap);
+  if (n_tokens < 1 || n_tokens > INT32_MAX)
+    return set_error(SKV_ERR_INVALID, "prefill: n_tokens %lld outside [1, 2^31)", (long long)n_tokens);
+  if (prefill_chunk_tokens(*d, chunk_bytes) < 1)
+    return set_error(SKV_ERR_INVALID, "prefill: chunk buffer of %zu bytes holds no token", chunk_bytes);
+  if (((uintptr_t)chunk_buf) % 16) return set_error(SKV_ERR_INVALID, "prefill: chunk buffer not 16-byte aligned");
+  if (ws_bytes < prefill_workspace_bytes(*d, n_query))
+    return set_error(SKV_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes,
+                     prefill_workspace_bytes(*d, n_query));
+  if (((uintptr_t)ws) % 256) return set_error(SKV_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  return launched(launch_prefill(*d, n_query, q, idx, n_sel, cap, host_k, host_v, n_tokens, chunk_buf,
+                                 chunk_bytes, sm_scale, out, ws, (hipStream_t)stream),
+                  "prefill");
 }
 
 skv_status sparsekv_qsketch(const skv_layer_desc* d, const void* q, const float* basis, int8_t* qs,

@@ -211,4 +211,14 @@ hipError_t launch_append(const skv_layer_desc& d, int32_t* ctx_len, const void* 
                          void* index_keys, uint16_t* index_scale, void* ws, const WsLayout& L,
                          hipStream_t st);
 
+// sparse prefill attention over host-resident K/V (prefill.hip): workspace
+// = flag word + per query head (max, sum) + accumulator; chunk tokens that a
+// working buffer of chunk_bytes holds (K and V rows of fp16 / bf16)
+size_t prefill_workspace_bytes(const skv_layer_desc& d, int n_query);
+size_t prefill_chunk_tokens(const skv_layer_desc& d, size_t chunk_bytes);
+hipError_t launch_prefill(const skv_layer_desc& d, int n_query, const void* q, const int32_t* idx,
+                          const int32_t* n_sel, int cap, const void* host_k, const void* host_v,
+                          int64_t n_tokens, void* chunk_buf, size_t chunk_bytes, float sm_scale,
+                          float* out, void* ws, hipStream_t st);
+
 }  // namespace skv
