@@ -58,6 +58,11 @@ CONFIGS = {
                   kv="i8", layers=8, seed=1002, M=8,
                   workload="8 seq x 250,000 tokens, 8 query tokens each (current + 7 drafted, "
                            "one pick per query at its causal context); cfg2 layer shape"),
+    "cfg3p": dict(kind="prefill", T=1_048_576, P=4096, n_kv=2, n_q=16, D=256, k=512,
+                  chunk_mib=256, seed=1003,
+                  workload="prefill of 4096 tokens at a 1,048,576-token history, one QSA layer "
+                           "(2 KV x 16 q heads, head_dim 256, bf16 K/V in pinned host memory); "
+                           "512 picked blocks per query; 256 MiB device working buffer"),
     "cfg5": dict(kind="tier", B=4, T=250_000, n_kv=4, n_q=24, D=256, S=64, k=2048, L=1024,
                  kv="i8", layers=1, seed=1005, warm_steps=64, steps=256,
                  workload="4 seq x 250,000 tokens; cfg2 layer shape; int4 host-RAM K/V records read "
@@ -347,6 +352,110 @@ def _cpu_baseline(layer: Layer, cfg, min_seconds=10.0, max_reps=20):
                 seconds=t_total)
 
 
+PCIE5_X16_GBS = 64.0   # PCIe 5.0 x16, one direction (nominal)
+
+
+def bench_prefill(cfg, args):
+    """Prefill attention over host-resident K/V: one call streams the history
+    once through the working buffer and attends every prefill query's picks
+    (seeded uniform block picks stand in for the indexer's selection)."""
+    T, P, n_kv, n_q, D, kb = cfg["T"], cfg["P"], cfg["n_kv"], cfg["n_q"], cfg["D"], cfg["k"]
+    log("generating %d x %d x %d bf16 K and V in pinned host memory" % (T, n_kv, D))
+    host = []
+    for tid in (1, 2):
+        t = torch.empty((T, n_kv, D), dtype=torch.bfloat16, pin_memory=True)
+        g = torch.Generator(device="cuda").manual_seed(cfg["seed"] * 10 + tid)
+        step = 1 << 18
+        for a in range(0, T, step):
+            t[a:a + step].copy_(torch.randn((min(step, T - a), n_kv, D), generator=g, device="cuda")
+                                .to(torch.bfloat16))
+        host.append(t)
+    g = torch.Generator(device="cuda").manual_seed(cfg["seed"] * 10 + 3)
+    q = torch.randn((P, n_q, D), generator=g, device="cuda").to(torch.bfloat16)
+    idx_np, nsel_np = synth.prefill_picks(P, T, kb, cfg["seed"])
+    idx, nsel = torch.from_numpy(idx_np).cuda(), torch.from_numpy(nsel_np).cuda()
+    desc = skv.block_desc(1, T, n_kv, n_q, D, topk_blocks=kb)
+    chunk_mib = args.chunk_mib or cfg["chunk_mib"]
+    buf = torch.empty((chunk_mib << 20,), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros((skv.prefill_workspace_size(desc, P),), dtype=torch.uint8, device="cuda")
+    out = torch.zeros((P, n_q, D), dtype=torch.float32, device="cuda")
+    sm = D ** -0.5
+
+    def call():
+        skv.prefill_attend(desc, q, idx, nsel, host[0], host[1], buf, sm, out, ws)
+
+    for _ in range(max(1, args.warmup)):
+        call()
+    skv.check(ws)
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(args.steps):
+        call()
+    e1.record(st)
+    e1.synchronize()
+    secs = e0.elapsed_time(e1) / 1e3
+    skv.check(ws)
+    # a plain pinned host-to-device copy of the same bytes, for reference
+    dev = torch.empty((T, n_kv, D), dtype=torch.bfloat16, device="cuda")
+    for _ in range(2):
+        dev.copy_(host[0], non_blocking=True)
+        dev.copy_(host[1], non_blocking=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(3):
+        dev.copy_(host[0], non_blocking=True)
+        dev.copy_(host[1], non_blocking=True)
+    e1.record(st)
+    e1.synchronize()
+    copy_s = e0.elapsed_time(e1) / 1e3 / 3
+    host_bytes = 2 * T * n_kv * D * 2
+    per = secs / args.steps
+    naive = int(nsel_np.astype(np.int64).sum()) * n_kv * D * 2 * 2
+    res = {
+        "metric": METRIC + " (prefill: layer-chunks/s)",
+        "value": round(1.0 / per, 3),
+        "unit": "layer-chunks/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(per * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg["workload"], "name": args.config, "history": T,
+                   "prefill_tokens": P, "buffer_mib": chunk_mib},
+        "prefill_tokens_per_s": round(P / per, 1),
+        "host_bytes_per_call": host_bytes,
+        "per_token_fetch_bytes": naive,
+        "roofline": {"kernel": "prefill (host-to-device chunk copies)", "bound": "pcie",
+                     "achieved": round(host_bytes / per / 1e9, 2), "peak": PCIE5_X16_GBS,
+                     "unit": "GB/s", "frac": round(host_bytes / per / 1e9 / PCIE5_X16_GBS, 4),
+                     "traffic": None, "plain_copy_GBps": round(host_bytes / copy_s / 1e9, 2)},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        import oracle
+        from threadpoolctl import threadpool_limits
+        kk, vv = (h.view(torch.int16).numpy().view(np.uint16) for h in host)
+        qq = q.cpu().view(torch.int16).numpy().view(np.uint16)
+        t_total, reps, n = 0.0, 0, 64
+        with threadpool_limits(limits=1):
+            while reps < 20 and (reps == 0 or t_total < 10.0):
+                qs = list(range((reps * n) % P, (reps * n) % P + n))
+                lists = [idx_np[p, :nsel_np[p]].astype(np.int64) for p in qs]
+                t0 = time.perf_counter()
+                oracle.prefill.prefill_attention(qq[qs], kk, vv, lists, sm, n_q // n_kv, "bf16")
+                t_total += time.perf_counter() - t0
+                reps += 1
+        res["cpu_baseline"] = {"value": round(reps * n / t_total / P, 5), "unit": "layer-chunks/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": "%d batches of %d of the %d prefill queries (rows read from "
+                                         "host memory); value scaled to all %d" % (reps, n, P, P),
+                               "seconds": round(t_total, 3)}
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
 def bench_tier(cfg, args):
     """Host-tier layer-step: the hot-buffer resolve (hits, windowed-CLOCK
     victims, zero-copy int4 fetch and dequantisation of the misses) followed by
@@ -443,6 +552,8 @@ def main():
     ap.add_argument("--config", default="cfg2", choices=sorted(CONFIGS))
     ap.add_argument("--layers", type=int, default=0, help="rotating layer buffers (0 = config default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--chunk-mib", type=int, default=0,
+                    help="prefill: device working buffer in MiB (0 = config default)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB read + 1 GiB write stream (counter calibration)")
     ap.add_argument("--rocprof-summary", metavar="CSV",
@@ -459,6 +570,9 @@ def main():
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     cfg = CONFIGS[args.config]
+    if cfg["kind"] == "prefill":
+        bench_prefill(cfg, args)
+        return
     if cfg["kind"] == "tier":
         args.warmup_given = "--warmup" in sys.argv
         args.steps_given = "--steps" in sys.argv

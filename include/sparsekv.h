@@ -277,17 +277,23 @@ skv_status sparsekv_step_multi(const skv_layer_desc* d, int32_t n_query, const i
  *   host_k, host_v  host [n_tokens][H_kv][D] rows (fp16 / bf16); pinned memory
  *              (hipHostMalloc) is copied by DMA, pageable memory is staged by
  *              the runtime
- *   chunk_buf  device working buffer of chunk_bytes, 16-byte aligned: chunks of
- *              floor(chunk_bytes / (2*H_kv*D*2)) tokens' K and V rows
+ *   chunk_buf  device working buffer of chunk_bytes, 16-byte aligned, used as two
+ *              halves: chunks of floor(chunk_bytes / (4*H_kv*D*2)) tokens' K and
+ *              V rows, one half filled while the other is read
  *   out        device [P][H_q][D] fp32: softmax of (q_j . k_t)*sm_scale over
  *              query p's listed rows t, times V (KV head of query head j is
  *              j / (H_q/H_kv)); zeros when n_sel[p] = 0
  *   ws         sparsekv_prefill_workspace_size(d, P) bytes, 256-byte aligned: a
  *              flag word (read by sparsekv_check), then the running (max, sum)
  *              and accumulator of every query head
- * Enqueues on `stream` a state reset, then per chunk two host-to-device copies
- * and one kernel, then the normalisation; returns without waiting.  The host
- * rows and all buffers must stay valid until the stream has passed them.  An
+ * Enqueues on `stream` a state reset, per chunk one kernel and the
+ * normalisation; the host-to-device copies run on a copy stream the library
+ * keeps per device, ordered against `stream` by events (a copy starts after
+ * the work already on `stream`; every kernel waits for its chunk's copy; a
+ * half is refilled after the kernel that read it).  Returns without waiting;
+ * once `stream` has passed the call, all of its work is done.  The host rows
+ * and all buffers must stay valid until then.  Calls from several host
+ * threads on one device are serialised while they enqueue.  An
  * index outside [0, n_tokens) or n_sel outside [0, cap] is skipped / clamped
  * and raises SKV_FLAG_INDEX_RANGE; so does a list entry found outside the
  * chunk being processed (an unsorted list). */

@@ -37,8 +37,8 @@ def _desc(skv, n_kv, n_q, D, fmt, max_ctx):
 
 def _run(skv, desc, k, v, q, idx, n_sel, chunk_tokens, sm, raise_on_error=True):
     P, n_q, D = q.shape
-    row = 2 * k.shape[1] * D * 2
-    buf = torch.empty((chunk_tokens * row,), dtype=torch.uint8, device="cuda")
+    row = 2 * k.shape[1] * D * 2          # K and V rows of one token
+    buf = torch.empty((2 * chunk_tokens * row,), dtype=torch.uint8, device="cuda")   # two halves
     ws = torch.zeros((skv.prefill_workspace_size(desc, P),), dtype=torch.uint8, device="cuda")
     out = torch.full((P, n_q, D), float("nan"), dtype=torch.float32, device="cuda")
     skv.prefill_attend(desc, q.cuda(), torch.from_numpy(idx).cuda(), torch.from_numpy(n_sel).cuda(),
@@ -68,7 +68,7 @@ def test_prefill_matches_oracle_any_chunking(fmt, n_kv, n_q, D):
     sm = D ** -0.5
     ref = _oracle(k, v, q, idx, n_sel, sm, n_q // n_kv, fmt, list(range(P)))
     outs = []
-    for ct in (700, 1024, 5003, 9000, 37):
+    for ct in (700, 1024, 5003, 9000, 37, 1):
         say("prefill", fmt, n_kv, n_q, D, "chunk tokens", ct)
         got, flags = _run(skv, desc, k, v, q, idx, n_sel, ct, sm)
         assert flags == 0
@@ -111,7 +111,7 @@ def test_prefill_large_history_sampled():
     say("prefill large: generating")
     k, v, q, idx, n_sel = _case(T, P, 2, 16, 256, 512, "bf16", 3103)
     desc = _desc(skv, 2, 16, 256, "bf16", T)
-    ct = (32 << 20) // (2 * 2 * 256 * 2)
+    ct = (32 << 20) // (2 * 2 * 2 * 256 * 2)   # 32 MiB in two halves
     got, flags = _run(skv, desc, k, v, q, idx, n_sel, ct, 0.0625)
     assert flags == 0
     queries = [0, 1, 100, 255, 256, 300, 400, 500, 509, 510, 511, 77]

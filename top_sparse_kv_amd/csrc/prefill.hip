@@ -11,11 +11,12 @@
 // results are merged chunk after chunk.  The bytes crossing the host link
 // are the history once, whatever the buffer size.
 //
-// Per call (all on the caller's stream): reset of the running state, then per
-// chunk one DMA copy of its K rows and one of its V rows into the buffer and
-// one kernel, then the normalisation.  The kernels are light next to the
-// copies (a chunk of 16K tokens of 2 KiB is ~0.3 ms of PCIe), so copy and
-// compute are simply serialised.
+// Per call: reset of the running state, then per chunk one DMA copy of its K
+// rows and one of its V rows into one half of the buffer and one kernel, then
+// the normalisation.  Copies run on a copy stream of the library's own and
+// kernels on the caller's stream, ordered by events: the copy of chunk i + 1
+// overlaps the kernel of chunk i, and a half is refilled only after the
+// kernel that read it (chunk i - 2) has finished.
 //
 // prefill_chunk_kernel: one wave per (query, KV head).  The query's rows in
 // [c0, c1) are found by a 64-way search of its ascending list (two rounds for
@@ -23,9 +24,10 @@
 // and V of each row and of the G query heads, the dots are summed over the
 // wave (xor butterfly), and the running (max, sum, accumulator) of each query
 // head is updated in base 2 and kept in the workspace between chunks.
-#include "skv_internal.h"
+#include "keys_common.h"
 
 #include <algorithm>
+#include <mutex>
 
 namespace skv {
 namespace {
@@ -40,10 +42,17 @@ __device__ __forceinline__ float elem_to_float(uint16_t v) {
   else return half_bits_to_float(v);
 }
 
+// sum over the 64 lanes, in every lane: DPP butterfly within each row of 16,
+// then the four row sums
 __device__ __forceinline__ float wave_sum_f(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  x += __uint_as_float(dpp_u32<0xB1>(__float_as_uint(x)));    // quad xor 1
+  x += __uint_as_float(dpp_u32<0x4E>(__float_as_uint(x)));    // quad xor 2
+  x += __uint_as_float(dpp_u32<0x141>(__float_as_uint(x)));   // half-row mirror
+  x += __uint_as_float(dpp_u32<0x140>(__float_as_uint(x)));   // row mirror
+  return (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)) +
+          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16))) +
+         (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32)) +
+          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48)));
 }
 
 // first index in list[0, n) whose value is >= x (list ascending); the whole
@@ -195,9 +204,38 @@ size_t prefill_workspace_bytes(const skv_layer_desc& d, int n_query) {
   return 256 + align_up(nh * 2 * 4, 256) + align_up(nh * (size_t)d.head_dim * 4, 256);
 }
 
+// tokens per chunk: the buffer holds two chunks (K and V rows of each)
 size_t prefill_chunk_tokens(const skv_layer_desc& d, size_t chunk_bytes) {
-  return chunk_bytes / (2 * (size_t)d.n_kv_heads * d.head_dim * 2);
+  return chunk_bytes / (2 * 2 * (size_t)d.n_kv_heads * d.head_dim * 2);
 }
+
+namespace {
+// per device: the copy stream and the events that order it against the
+// caller's stream (created on first use, kept until the process ends)
+struct PrefillStreams {
+  hipStream_t copy = nullptr;
+  hipEvent_t start = nullptr, copied[2] = {nullptr, nullptr}, done[2] = {nullptr, nullptr};
+};
+constexpr int kMaxDevices = 64;
+PrefillStreams g_pf[kMaxDevices];
+std::mutex g_pf_mu;
+
+hipError_t prefill_streams(PrefillStreams** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  PrefillStreams& r = g_pf[dev];
+  if (!r.copy) {
+    e = hipStreamCreateWithFlags(&r.copy, hipStreamNonBlocking);
+    hipEvent_t* evs[5] = {&r.start, &r.copied[0], &r.copied[1], &r.done[0], &r.done[1]};
+    for (int i = 0; i < 5 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(evs[i], hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+  }
+  *out = &r;
+  return hipSuccess;
+}
+}  // namespace
 
 hipError_t launch_prefill(const skv_layer_desc& d, int n_query, const void* q, const int32_t* idx,
                           const int32_t* n_sel, int cap, const void* host_k, const void* host_v,
@@ -210,26 +248,42 @@ hipError_t launch_prefill(const skv_layer_desc& d, int n_query, const void* q, c
   float* acc = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + 256 + align_up((size_t)nh * 8, 256));
   const int64_t C = (int64_t)prefill_chunk_tokens(d, chunk_bytes);
   const size_t row_bytes = (size_t)Hkv * D * 2;   // one token's K (or V) rows
-  uint16_t* kbuf = reinterpret_cast<uint16_t*>(chunk_buf);
-  uint16_t* vbuf = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(chunk_buf) + C * row_bytes);
+  uint16_t* kbuf = reinterpret_cast<uint16_t*>(chunk_buf);   // [2 halves][K rows, V rows] of C tokens
   const int fill_blocks = (int)std::min<int64_t>((nh * D + 255) / 256, 4096);
+  std::lock_guard<std::mutex> lock(g_pf_mu);   // the copy stream and events are shared per device
+  PrefillStreams* ps = nullptr;
+  hipError_t e = prefill_streams(&ps);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(prefill_reset_kernel, dim3(fill_blocks), dim3(256), 0, st, ml, acc, nh, D);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
+  // copies start after the work already on the caller's stream (which may
+  // still read this buffer)
+  if (e == hipSuccess) e = hipEventRecord(ps->start, st);
+  if (e == hipSuccess) e = hipStreamWaitEvent(ps->copy, ps->start, 0);
   const bool bf = d.kv_dtype == SKV_KV_BF16;
   const float sl = sm_scale * kLog2eP;
-  for (int64_t c0 = 0; c0 < n_tokens && e == hipSuccess; c0 += C) {
+  int64_t i = 0;
+  for (int64_t c0 = 0; c0 < n_tokens && e == hipSuccess; c0 += C, ++i) {
     const int64_t c1 = std::min<int64_t>(n_tokens, c0 + C);
     const size_t bytes = (size_t)(c1 - c0) * row_bytes;
-    e = hipMemcpyAsync(kbuf, reinterpret_cast<const char*>(host_k) + (size_t)c0 * row_bytes, bytes,
-                       hipMemcpyHostToDevice, st);
+    const int half = (int)(i & 1);
+    uint16_t* kh = kbuf + (size_t)half * 2 * C * (row_bytes / 2);
+    uint16_t* vh = kh + (size_t)C * (row_bytes / 2);
+    // refill this half once the kernel of chunk i - 2 has read it
+    if (i >= 2) e = hipStreamWaitEvent(ps->copy, ps->done[half], 0);
     if (e == hipSuccess)
-      e = hipMemcpyAsync(vbuf, reinterpret_cast<const char*>(host_v) + (size_t)c0 * row_bytes, bytes,
-                         hipMemcpyHostToDevice, st);
+      e = hipMemcpyAsync(kh, reinterpret_cast<const char*>(host_k) + (size_t)c0 * row_bytes, bytes,
+                         hipMemcpyHostToDevice, ps->copy);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(vh, reinterpret_cast<const char*>(host_v) + (size_t)c0 * row_bytes, bytes,
+                         hipMemcpyHostToDevice, ps->copy);
+    if (e == hipSuccess) e = hipEventRecord(ps->copied[half], ps->copy);
+    if (e == hipSuccess) e = hipStreamWaitEvent(st, ps->copied[half], 0);
     if (e != hipSuccess) break;
     const dim3 grid(n_query, Hkv);
 #define SKV_PF(ET, DD, GG)                                                                         \
   hipLaunchKernelGGL((prefill_chunk_kernel<ET, DD, GG>), grid, dim3(64), 0, st, (const uint16_t*)q,  \
-                     idx, n_sel, cap, kbuf, vbuf, (int)c0, (int)c1, (int)(c1 == n_tokens), sl, Hq, Hkv, ml, acc, flags)
+                     idx, n_sel, cap, kh, vh, (int)c0, (int)c1, (int)(c1 == n_tokens), sl, Hq, Hkv, ml, acc, flags)
 #define SKV_PF_G(ET, DD)                                                                           \
   do {                                                                                             \
     if (Hq / Hkv <= 8) SKV_PF(ET, DD, 8);                                                          \
@@ -242,6 +296,7 @@ hipError_t launch_prefill(const skv_layer_desc& d, int n_query, const void* q, c
 #undef SKV_PF_G
 #undef SKV_PF
     e = hipGetLastError();
+    if (e == hipSuccess) e = hipEventRecord(ps->done[half], st);
   }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(prefill_finish_kernel, dim3(fill_blocks), dim3(256), 0, st, ml, acc, out, nh, D);
