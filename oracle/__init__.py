@@ -10,3 +10,4 @@ from .step import PINS  # noqa: F401
 from . import append  # noqa: F401
 from . import multiquery  # noqa: F401
 from . import prefill  # noqa: F401
+from . import residency  # noqa: F401

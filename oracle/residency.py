@@ -1,0 +1,73 @@
+"""CPU oracle of the LRU hot buffer (HiSparse-style residency) of one sequence.
+TEST INFRASTRUCTURE ONLY (same rules as oracle.step: only the tests, the
+entry point's smoke check and the benchmark's CPU-baseline leg may use it; the
+GPU library shares no code with it).
+
+Source: page "vLLM's Hybrid HiSparse Triples Concurrent Requests on
+Million-Token Contexts", section "Three residency states, one block pool"
+(mixed residency: the tail stays on the GPU and is never evicted, older rows
+live in host memory, the rows the indexer wants sit in a hot buffer; one
+resolver reads resident rows in place, refreshes the LRU entry of a hot row,
+and copies a missed row from pinned host memory into an LRU slot) and the
+list after "What it composes with" (hot buffers default to 2x top-K rows per
+request).
+
+Reading (the page names LRU but gives no tie rules): each slot holds a
+position and the step it was last used.  At step s, with the picked middle
+positions in ascending order:
+  1. every pick already in the buffer is a hit and its slot's last use
+     becomes s;
+  2. the misses need as many victims: the slots not used in step s, oldest
+     last use first, an empty slot counting as older than every used one and
+     equal last uses taken in slot order;
+  3. the misses, in ascending position, fill the victims in ascending slot
+     order (where a row lands inside the buffer is not specified; this order
+     makes the placement one prefix sum), and those slots' last use becomes s.
+The buffer must hold at least the picks of one step.
+"""
+
+from __future__ import annotations
+
+from typing import Tuple
+
+import numpy as np
+
+EMPTY = -(1 << 40)
+
+
+class LruTier:
+    def __init__(self, n_slots: int, T: int):
+        self.n = int(n_slots)
+        self.pos = np.full(self.n, -1, dtype=np.int64)
+        self.last = np.full(self.n, EMPTY, dtype=np.int64)
+        self.slot_of = np.full(T, -1, dtype=np.int64)
+
+    def step(self, picks: np.ndarray, s: int) -> Tuple[np.ndarray, int, int]:
+        """picks: ascending middle positions.  Returns (slot per pick, hits, misses)."""
+        picks = np.asarray(picks, dtype=np.int64)
+        assert picks.size <= self.n
+        slots = self.slot_of[picks].copy()
+        hit = slots >= 0
+        self.last[slots[hit]] = s
+        miss = np.nonzero(~hit)[0]
+        if miss.size:
+            free = np.nonzero(self.last < s)[0]                 # not used in this step
+            order = np.lexsort((free, self.last[free]))          # oldest first, then slot order
+            victims = np.sort(free[order[:miss.size]])
+            for i, x in zip(miss.tolist(), victims.tolist()):
+                if self.pos[x] >= 0:
+                    self.slot_of[self.pos[x]] = -1
+                p = picks[i]
+                self.pos[x] = p
+                self.last[x] = s
+                self.slot_of[p] = x
+                slots[i] = x
+        n_hit = int(hit.sum())
+        return slots, n_hit, int(picks.size - n_hit)
+
+
+PINS = {
+    "LruTier": "hand-traced fixture tests/golden/lru_trace.txt; hits + misses = picks; occupancy "
+               "never above capacity; a slot used in the current step is never evicted; no kept "
+               "unused slot is older than an evicted one; nothing is evicted while a slot is empty",
+}

@@ -772,3 +772,50 @@ def test_prefill_transfer_closed_forms():
     once = oracle.prefill.chunked_transfer_bytes(T, 2, 256, 2)
     assert once == 2 * 1024 * MiB and 12 * once == 24 * 1024 * MiB
     assert per_layer // once == 8   # 4096 x 2048 picks vs 1 Mi rows
+
+
+# --------------------------------------------------------------------------
+# LRU hot buffer (HiSparse-style residency)
+# --------------------------------------------------------------------------
+
+def test_lru_fixture():
+    lines = list(_lines("lru_trace.txt"))
+    n = int(lines[0].split()[1])
+    tier = oracle.residency.LruTier(n, 100)
+    for ln in lines[1:]:
+        if ln.startswith("final"):
+            assert tier.pos.tolist() == [int(x) for x in ln.split()[1:]]
+            continue
+        s, picks, slots, hits, misses = (p.strip() for p in ln.split("|"))
+        picks = np.array(sorted(int(x) for x in picks.split()))
+        got, h, m = tier.step(picks, int(s))
+        assert got.tolist() == [int(x) for x in slots.split()], ln
+        assert (h, m) == (int(hits), int(misses))
+
+
+def test_lru_invariants_drifting_workload():
+    """Over a drifting-locality pick schedule: hits + misses = picks, the
+    buffer never holds more than its slots, no slot used in the current step
+    is evicted, nothing is evicted while a slot is empty, and no slot kept
+    unused is older than an evicted one (ties by slot index)."""
+    T, S, L, k = 60_000, 64, 1024, 512
+    picks = synth.drift_picks(1, T, S, L, k, 60, seed=44, window=8192, sigma_c=256.0)
+    n_slots = 2 * k
+    tier = oracle.residency.LruTier(n_slots, T)
+    for s in range(60):
+        p = np.asarray(picks[s][0], dtype=np.int64)
+        before_pos = tier.pos.copy()
+        before_last = tier.last.copy()
+        slots, h, m = tier.step(p, s)
+        assert h + m == p.size and (tier.pos >= 0).sum() <= n_slots
+        assert len(set(slots.tolist())) == p.size
+        changed = np.nonzero(tier.pos != before_pos)[0]
+        evicted = [x for x in changed.tolist() if before_pos[x] >= 0]
+        if evicted:
+            assert (tier.pos >= 0).all()                         # no slot left empty
+            used_now = set(slots.tolist())
+            kept_unused = [x for x in range(n_slots) if x not in used_now]
+            oldest_kept = min(((before_last[x], x) for x in kept_unused), default=None)
+            newest_evicted = max((before_last[x], x) for x in evicted)
+            assert oldest_kept is None or newest_evicted < oldest_kept
+        assert set(tier.pos[tier.pos >= 0].tolist()) >= set(p.tolist())
