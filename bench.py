@@ -63,6 +63,16 @@ CONFIGS = {
                   workload="prefill of 4096 tokens at a 1,048,576-token history, one QSA layer "
                            "(2 KV x 16 q heads, head_dim 256, bf16 K/V in pinned host memory); "
                            "512 picked blocks per query; 256 MiB device working buffer"),
+    "cfg5l": dict(kind="tier", B=4, T=250_000, n_kv=4, n_q=24, D=256, S=64, k=2048, L=1024,
+                  kv="i8", layers=1, seed=1005, warm_steps=64, steps=256, policy="lru", slots=4096,
+                  workload="4 seq x 250,000 tokens; cfg2 layer shape; int4 host-RAM K/V records read "
+                           "zero-copy, LRU hot buffer of 2 x top-k = 4,096 slots, drifting-locality "
+                           "picks"),
+    "cfg5c": dict(kind="tier", B=4, T=250_000, n_kv=4, n_q=24, D=256, S=64, k=2048, L=1024,
+                  kv="i8", layers=1, seed=1005, warm_steps=64, steps=256, slots=4096,
+                  workload="4 seq x 250,000 tokens; cfg2 layer shape; int4 host-RAM K/V records read "
+                           "zero-copy, windowed-CLOCK hot buffer of 4,096 slots (the LRU line's "
+                           "capacity), drifting-locality picks"),
     "cfg5": dict(kind="tier", B=4, T=250_000, n_kv=4, n_q=24, D=256, S=64, k=2048, L=1024,
                  kv="i8", layers=1, seed=1005, warm_steps=64, steps=256,
                  workload="4 seq x 250,000 tokens; cfg2 layer shape; int4 host-RAM K/V records read "
@@ -470,7 +480,9 @@ def bench_tier(cfg, args):
     picks = synth.drift_picks(B, T, S, L, k, warm + steps, seed=cfg["seed"],
                               window=min(65536, (T - S - L) // 2), sigma_c=256.0)
     desc = skv.token_desc(B, T, cfg["n_kv"], cfg["n_q"], cfg["D"], topk=k, n_sink=S, n_tail=L)
-    tier = skv.Tier(desc, T, c.n_slots, 1)
+    n_slots = cfg.get("slots", c.n_slots)
+    lru = cfg.get("policy") == "lru"
+    tier = skv.Tier(desc, T, n_slots, 1, policy=skv.SKV_TIER_LRU if lru else skv.SKV_TIER_CLOCK)
     try:
         tier.host_records()[:] = c.records.cpu().numpy()
         tier.load_resident(c.res_k, c.res_v, c.res_ks, c.res_vs)
@@ -530,8 +542,8 @@ def bench_tier(cfg, args):
         "vs_baseline": None,
         "dtype": "i8",
         "data": "synthetic",
-        "config": {"workload": cfg["workload"], "name": "cfg5", "batch": B, "ctx": T,
-                   "hot_slots_per_seq": c.n_slots},
+        "config": {"workload": cfg["workload"], "name": args.config, "batch": B, "ctx": T,
+                   "hot_slots_per_seq": n_slots, "policy": "lru" if lru else "windowed-clock"},
         "tier": {"miss_rate": round(misses / max(1, hits + misses), 4), "hits": hits, "misses": misses,
                  "host_bytes_per_step": round(hbytes / steps),
                  "pcie_GBps_over_step": round(hbytes / secs / 1e9, 2),

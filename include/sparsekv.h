@@ -390,6 +390,17 @@ skv_status sparsekv_timer_read(double* total_ms, int64_t* launches);
  * the window has its reference cleared as the hand passes it. */
 typedef struct skv_tier skv_tier;
 
+/* Hot-buffer policies.  SKV_TIER_CLOCK: the windowed CLOCK above.
+ * SKV_TIER_LRU -- page "vLLM's Hybrid HiSparse Triples Concurrent Requests on
+ * Million-Token Contexts", section "Three residency states, one block pool"
+ * (a hot row's LRU entry is refreshed on use, a miss copies its row into an
+ * LRU slot; hot buffers of 2x top-K rows by default): hits set the slot's last
+ * use to the step; the misses take the slots not used in this step, oldest
+ * last use first (an empty slot before any used one, equal last uses in slot
+ * order), and fill them in ascending slot order in ascending position order.
+ * window is ignored; n_slots >= topk. */
+enum { SKV_TIER_CLOCK = 0, SKV_TIER_LRU = 1 };
+
 typedef struct {
   uint32_t struct_size;   /* sizeof(skv_tier_desc) */
   skv_layer_desc layer;   /* token mode, SKV_KV_I8_ROWSCALE */
@@ -399,6 +410,8 @@ typedef struct {
   void* host_records;     /* NULL: the library allocates pinned, device-mapped
                              host memory; otherwise caller memory that is
                              already pinned and mapped (e.g. hipHostMalloc) */
+  int32_t policy;         /* SKV_TIER_*; a struct_size that ends before this
+                             field means SKV_TIER_CLOCK */
 } skv_tier_desc;
 
 typedef struct {

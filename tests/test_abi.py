@@ -194,3 +194,18 @@ def test_multi_query_host_checks(skv):
     st = lib.sparsekv_step_multi(ctypes.byref(d), 8, *a2, ctypes.byref(kv), dummy, dummy, 0.1,
                                  dummy, ctypes.c_void_p(0x100000), w8, None)
     assert st == 1
+
+
+def test_tier_policy_checks(skv):
+    """LRU tiers need topk <= n_slots <= the LDS slot table; an unknown policy is
+    rejected; a descriptor that ends before the policy field means CLOCK."""
+    lib = skv.lib()
+    layer = skv.token_desc(2, 10_000, 4, 24, 256, topk=64, n_sink=4, n_tail=8)
+    h = ctypes.c_void_p()
+    td = skv.TierDesc(ctypes.sizeof(skv.TierDesc), layer, 10_000, 63, 1, None, skv.SKV_TIER_LRU)
+    assert lib.sparsekv_tier_create(ctypes.byref(td), ctypes.byref(h)) == 1
+    td = skv.TierDesc(ctypes.sizeof(skv.TierDesc), layer, 10_000, 200, 1, None, 7)
+    assert lib.sparsekv_tier_create(ctypes.byref(td), ctypes.byref(h)) == 1
+    td = skv.TierDesc(ctypes.sizeof(skv.TierDesc) - 8, layer, 10_000, 60, 1, None, skv.SKV_TIER_LRU)
+    # read as CLOCK: 60 slots do not exceed window * topk = 64
+    assert lib.sparsekv_tier_create(ctypes.byref(td), ctypes.byref(h)) == 1

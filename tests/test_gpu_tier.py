@@ -1,6 +1,7 @@
-"""GPU parity of the host-RAM tier: slot assignment of the windowed CLOCK,
-hit / miss counts and host bytes must equal the oracle's exactly, every step;
-attention over the resolved rows within 2e-3 of the fp64 oracle."""
+"""GPU parity of the host-RAM tier: slot assignment of the windowed CLOCK and
+of the LRU hot buffer, hit / miss counts and host bytes must equal the
+oracle's exactly, every step; attention over the resolved rows within 2e-3 of
+the fp64 oracle."""
 
 import numpy as np
 import pytest
@@ -13,14 +14,16 @@ from gpu_util import ATOL, need_gpu, say
 pytestmark = pytest.mark.gpu
 
 
-def _run(B, T, S, L, k, n_slots, n_steps, check_out_steps, seed, window=1, device="cpu"):
+def _run(B, T, S, L, k, n_slots, n_steps, check_out_steps, seed, window=1, device="cpu",
+         lru=False):
     skv = need_gpu()
-    say("tier B=%d T=%d k=%d slots=%d steps=%d" % (B, T, k, n_slots, n_steps))
+    say("tier B=%d T=%d k=%d slots=%d steps=%d lru=%s" % (B, T, k, n_slots, n_steps, lru))
     c = synth.make_tier_case(B, T, n_kv=4, n_q=24, D=256, S=S, k=k, L=L, seed=seed, device=device)
     picks = synth.drift_picks(B, T, S, L, k, n_steps, seed=seed,
                               window=min(65536, (T - S - L) // 2), sigma_c=256.0)
     desc = skv.token_desc(B, T, 4, 24, 256, topk=k, n_sink=S, n_tail=L)
-    tier = skv.Tier(desc, T, n_slots, window)
+    tier = skv.Tier(desc, T, n_slots, window,
+                    policy=skv.SKV_TIER_LRU if lru else skv.SKV_TIER_CLOCK)
     try:
         tier.host_records()[:] = c.records.cpu().numpy()
         tier.load_resident(c.res_k.cuda(), c.res_v.cuda(), c.res_ks.cuda(), c.res_vs.cuda())
@@ -32,7 +35,8 @@ def _run(B, T, S, L, k, n_slots, n_steps, check_out_steps, seed, window=1, devic
         out = torch.zeros((B, 24, 256), dtype=torch.float32, device="cuda")
         q = c.q.cuda()
         sm = 256 ** -0.5
-        ref = [oracle.ClockTier(n_slots, T, window=window) for _ in range(B)]
+        ref = [oracle.residency.LruTier(n_slots, T) if lru else oracle.ClockTier(n_slots, T, window=window)
+               for _ in range(B)]
         rec_np = c.records.cpu().numpy()
         rk, rv = c.res_k.cpu().numpy(), c.res_v.cpu().numpy()
         rks, rvs = c.res_ks.cpu().numpy(), c.res_vs.cpu().numpy()
@@ -90,3 +94,23 @@ def test_tier_full_config5():
     h, m = _run(B=4, T=250_000, S=64, L=1024, k=2048, n_slots=6250, n_steps=40,
                 check_out_steps={0, 39}, seed=1005, device="cuda")
     say("tier cfg5 miss rate over 40 steps", m / (h + m))
+
+
+def test_tier_lru_small():
+    """LRU hot buffer of 2 x top-k slots (the HiSparse default)."""
+    h, m = _run(B=2, T=40_000, S=64, L=1024, k=256, n_slots=512, n_steps=24,
+                check_out_steps={0, 7, 23}, seed=57, lru=True)
+    say("tier lru small miss rate", m / (h + m))
+
+
+def test_tier_lru_exact_capacity():
+    """n_slots = top-k: every slot not hit this step is a candidate."""
+    _run(B=1, T=20_000, S=16, L=128, k=200, n_slots=200, n_steps=12, check_out_steps={11},
+         seed=58, lru=True)
+
+
+def test_tier_lru_full_config5():
+    """Config-5 shape with the LRU policy at 2 x 2048 = 4096 slots."""
+    h, m = _run(B=4, T=250_000, S=64, L=1024, k=2048, n_slots=4096, n_steps=40,
+                check_out_steps={0, 39}, seed=1005, device="cuda", lru=True)
+    say("tier lru cfg5 miss rate over 40 steps", m / (h + m))

@@ -20,7 +20,7 @@ from . import _lib
 from ._lib import (KVView, LayerDesc, TierDesc, TierStats, SKV_INDEX_SKETCH_INT4,  # noqa: F401
                    SKV_INDEX_POOLED_BF16, SKV_KV_I8_ROWSCALE, SKV_KV_F16, SKV_KV_BF16, SKV_Q_F16,
                    SKV_Q_BF16, SKV_FLAG_CTX_RANGE, SKV_FLAG_INDEX_RANGE, SKV_FLAG_TOPK_SLOW,
-                   SKV_FLAG_TIER_INPUT)
+                   SKV_FLAG_TIER_INPUT, SKV_TIER_CLOCK, SKV_TIER_LRU)
 
 
 class SkvError(RuntimeError):
@@ -240,13 +240,14 @@ class _TierHandle:
 
 
 class Tier:
-    """Host-RAM KV tier with a GPU hot buffer (sparsekv_tier_*)."""
+    """Host-RAM KV tier with a GPU hot buffer (sparsekv_tier_*); policy
+    SKV_TIER_CLOCK (windowed CLOCK) or SKV_TIER_LRU."""
 
     def __init__(self, layer: LayerDesc, ctx: int, n_slots: int, window: int = 1,
-                 host_records: Optional[int] = None):
+                 host_records: Optional[int] = None, policy: int = SKV_TIER_CLOCK):
         self.layer = layer
         d = TierDesc(ctypes.sizeof(TierDesc), layer, ctx, n_slots, window,
-                     ctypes.c_void_p(host_records) if host_records else None)
+                     ctypes.c_void_p(host_records) if host_records else None, policy)
         h = ctypes.c_void_p()
         _check(lib().sparsekv_tier_create(ctypes.byref(d), ctypes.byref(h)))
         self._h = h

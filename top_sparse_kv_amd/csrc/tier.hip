@@ -30,14 +30,24 @@
 // take the referenced slots in hand order; beyond those nothing can be
 // evicted (flagged).  One prefix sum over the slots, in hand order, gives
 // every rank at once.
+//
+// LRU policy (page "vLLM's Hybrid HiSparse Triples Concurrent Requests on
+// Million-Token Contexts", section "Three residency states, one block pool"):
+// hits refresh the slot's last use; the misses need as many victims, the
+// oldest slots not used in this step.  The victims' last-use bound is found
+// by a 4 x 8-bit radix select over the ages (LDS histograms), the slots at
+// exactly that age are taken in slot order, and the misses fill the victims
+// in slot order: two prefix sums over the slots in index order.
 #include "keys_common.h"
 
+#include <algorithm>
 #include <new>
+#include <stddef.h>
 #include <string.h>
 
 struct skv_tier {
   skv_tier_desc desc;
-  int B, T, S, L, k, Hkv, D, n_slots, W, cap;
+  int B, T, S, L, k, Hkv, D, n_slots, W, cap, policy;
   int rec_bytes;      // per token-head: K row + V row
   int row_bytes;      // one K (or V) host row
   void* host;         // host records (host address)
@@ -83,6 +93,7 @@ __global__ void tier_reset_kernel(int32_t* slot_pos, int32_t* slot_last, int32_t
   if (tid < 3) counters[tid] = 0ull;
 }
 
+template <int POLICY>
 __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ n_sel, int32_t* __restrict__ rows,
     int32_t* __restrict__ slot_pos, int32_t* __restrict__ slot_last, int32_t* __restrict__ slot_ref,
@@ -180,8 +191,10 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
     __syncthreads();
   }
   // a victim always exists when fewer slots are pinned than exist: at most the
-  // middle picks of this step plus those of the previous W-1 steps
-  const bool fits = (int64_t)s_nmid < (int64_t)n_slots;
+  // middle picks of this step plus those of the previous W-1 steps (LRU: the
+  // slots not used in this step are the candidates)
+  const bool fits = POLICY == SKV_TIER_LRU ? (int64_t)s_nmid <= (int64_t)n_slots
+                                           : (int64_t)s_nmid < (int64_t)n_slots;
   const int nm = fits ? min(s_nm, k) : 0;
   if (!fits) {
     for (int mi = threadIdx.x; mi < min(s_nm, k); mi += blockDim.x) rb[s_miss[mi]] = 0;
@@ -189,8 +202,134 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
   }
   __syncthreads();
 
-  // phase B: thread t owns the slots at hand distance [kRun*t, kRun*t + kRun)
   constexpr int kRun = kMaxSlots / kResolveThreads;
+  if constexpr (POLICY == SKV_TIER_LRU) {
+    // phase B (LRU): age key u = last - kNoStep of the slots not used in this
+    // step; v = the nm-th smallest u, need = how many slots of age v are taken
+    __shared__ uint32_t s_hist[256];
+    __shared__ uint32_t s_sel[2];
+    uint32_t v = 0, need = (uint32_t)nm;
+    // ages relative to the oldest candidate: leading rounds whose digit is 0
+    // for every candidate are skipped (usually one round is left)
+    uint32_t umin = 0xFFFFFFFFu, umax = 0u;
+    for (int j = threadIdx.x; j < n_slots; j += blockDim.x)
+      if (s_last[j] < step) {
+        const uint32_t u = (uint32_t)(s_last[j] - kNoStep);
+        umin = min(umin, u);
+        umax = max(umax, u);
+      }
+    umin = ~wave_max(~umin);
+    umax = wave_max(umax);
+    if (lane == 0) {
+      s_hist[wave] = umin;
+      s_hist[16 + wave] = umax;
+    }
+    __syncthreads();
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+      umin = min(umin, s_hist[w]);
+      umax = max(umax, s_hist[16 + w]);
+    }
+    __syncthreads();
+    const uint32_t span = umax >= umin ? umax - umin : 0u;
+    const int top_bits = span ? 32 - __clz((int)span) : 0;
+    if (nm > 0) {
+      for (int shift = 24; shift >= 0; shift -= 8) {
+        if (shift > 0 && shift >= top_bits) continue;   // digit 0 for every candidate
+        for (int i = threadIdx.x; i < 256; i += blockDim.x) s_hist[i] = 0u;
+        __syncthreads();
+        for (int j = threadIdx.x; j < n_slots; j += blockDim.x) {
+          if (s_last[j] < step) {
+            const uint32_t u = (uint32_t)(s_last[j] - kNoStep) - umin;
+            if (((uint64_t)(u ^ v) >> (shift + 8)) == 0) atomicAdd(&s_hist[(u >> shift) & 255u], 1u);
+          }
+        }
+        __syncthreads();
+        if (wave == 0) {
+          // lane l scans bins 4l..4l+3; the lane whose range holds the need-th
+          // candidate picks the bin
+          const uint32_t c0 = s_hist[4 * lane], c1 = s_hist[4 * lane + 1], c2 = s_hist[4 * lane + 2],
+                         c3 = s_hist[4 * lane + 3];
+          const uint32_t tot = c0 + c1 + c2 + c3;
+          const uint32_t incl = wave_incl_scan(tot), excl = incl - tot;
+          const uint64_t hit = __ballot(excl < need && need <= incl);
+          // hit is never empty: the candidates number at least need
+          if (hit && lane == (int)__ffsll((unsigned long long)hit) - 1) {
+            uint32_t cum = excl;
+            int bin = 4 * lane;
+            if (cum + c0 < need) { cum += c0; ++bin;
+              if (cum + c1 < need) { cum += c1; ++bin;
+                if (cum + c2 < need) { cum += c2; ++bin; } } }
+            s_sel[0] = v | ((uint32_t)bin << shift);
+            s_sel[1] = need - cum;
+          }
+        }
+        __syncthreads();
+        v = s_sel[0];
+        need = s_sel[1];
+        __syncthreads();
+      }
+    }
+    // thread t owns slots [kRun*t, kRun*t + kRun): index order
+    const int d0 = kRun * (int)threadIdx.x;
+    uint32_t ltm = 0, eqm = 0;
+#pragma unroll
+    for (int r = 0; r < kRun; ++r) {
+      const int j = d0 + r;
+      if (nm > 0 && j < n_slots && s_last[j] < step) {
+        const uint32_t u = (uint32_t)(s_last[j] - kNoStep) - umin;
+        ltm |= (uint32_t)(u < v) << r;
+        eqm |= (uint32_t)(u == v) << r;
+      }
+    }
+    uint32_t eq_before = block_excl_scan((uint32_t)__popc(eqm), s_wsum, nullptr);
+    uint32_t vm = ltm;
+#pragma unroll
+    for (int r = 0; r < kRun; ++r)
+      if (eqm & (1u << r)) {
+        if (eq_before < need) vm |= 1u << r;
+        ++eq_before;
+      }
+    uint32_t n_victims = 0;
+    uint32_t vr = block_excl_scan((uint32_t)__popc(vm), s_wsum, &n_victims);
+#pragma unroll
+    for (int r = 0; r < kRun; ++r) {
+      if (vm & (1u << r)) {
+        const int j = d0 + r, mi = (int)vr++;
+        if (mi < nm) {   // the victims are exactly nm; kept as a guard
+          const int p = s_mpos[mi], i = s_miss[mi];
+          const int old = s_pos[j];
+          if (old >= 0) sop[old] = -1;
+          s_pos[j] = p;
+          s_last[j] = step;
+          sop[p] = j;
+          rb[i] = S + L + j;
+          miss_pos[(size_t)b * k + mi] = p;
+          miss_slot[(size_t)b * k + mi] = j;
+        }
+      }
+    }
+    // fewer candidates than misses only if a step number was reused (its
+    // slots then look used in this step): the rest are not placed, flagged
+    const int placed = min(nm, (int)n_victims);
+    for (int mi = placed + (int)threadIdx.x; mi < nm; mi += blockDim.x) rb[s_miss[mi]] = 0;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      miss_count[b] = placed;
+      atomicAdd(&counters[0], (unsigned long long)s_nmid);
+      atomicAdd(&counters[1], (unsigned long long)(s_nmid - nm));
+      atomicAdd(&counters[2], (unsigned long long)nm);
+      if (s_bad || placed < nm) raise_flag(flags, SKV_FLAG_TIER_INPUT);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < n_slots; i += blockDim.x) {
+      sp[i] = s_pos[i];
+      sl[i] = s_last[i];
+      sr[i] = (int32_t)s_ref[i];
+    }
+    return;
+  }
+
+  // phase B: thread t owns the slots at hand distance [kRun*t, kRun*t + kRun)
   const int old_limit = step - W;   // last <= step - W: outside the window
   const int d0 = kRun * (int)threadIdx.x;
   uint32_t fmask = 0, rmask = 0;
@@ -349,8 +488,12 @@ static void tier_free(skv_tier* t) {
 extern "C" skv_status sparsekv_tier_create(const skv_tier_desc* d, skv_tier** out) {
   if (!d || !out) return set_error(SKV_ERR_INVALID, "tier_create: NULL argument");
   *out = nullptr;
-  if (d->struct_size < sizeof(skv_tier_desc))
-    return set_error(SKV_ERR_INVALID, "tier_create: struct_size %u < %zu", d->struct_size, sizeof(skv_tier_desc));
+  constexpr size_t kMinDesc = offsetof(skv_tier_desc, policy);
+  if (d->struct_size < kMinDesc)
+    return set_error(SKV_ERR_INVALID, "tier_create: struct_size %u < %zu", d->struct_size, kMinDesc);
+  const int policy = d->struct_size >= sizeof(skv_tier_desc) ? d->policy : SKV_TIER_CLOCK;
+  if (policy != SKV_TIER_CLOCK && policy != SKV_TIER_LRU)
+    return set_error(SKV_ERR_INVALID, "tier_create: policy %d unknown", policy);
   skv_status s = skv::validate_desc(&d->layer);
   if (s != SKV_OK) return s;
   const skv_layer_desc& L = d->layer;
@@ -358,14 +501,21 @@ extern "C" skv_status sparsekv_tier_create(const skv_tier_desc* d, skv_tier** ou
     return set_error(SKV_ERR_UNSUPPORTED, "tier: needs token mode, int8 K/V rows and head_dim 256");
   if (d->ctx < 1 || d->ctx > L.max_ctx)
     return set_error(SKV_ERR_INVALID, "tier: ctx %d outside [1, max_ctx=%d]", d->ctx, L.max_ctx);
-  if (d->window < 1) return set_error(SKV_ERR_INVALID, "tier: window %d < 1", d->window);
-  if ((int64_t)d->n_slots <= (int64_t)d->window * L.topk || d->n_slots > skv::kMaxSlots)
-    return set_error(SKV_ERR_INVALID, "tier: n_slots %d must exceed window*topk = %lld and be <= %d",
-                     d->n_slots, (long long)d->window * L.topk, skv::kMaxSlots);
+  if (policy == SKV_TIER_LRU) {
+    if (d->n_slots < L.topk || d->n_slots > skv::kMaxSlots)
+      return set_error(SKV_ERR_INVALID, "tier: n_slots %d must be in [topk = %d, %d]", d->n_slots,
+                       L.topk, skv::kMaxSlots);
+  } else {
+    if (d->window < 1) return set_error(SKV_ERR_INVALID, "tier: window %d < 1", d->window);
+    if ((int64_t)d->n_slots <= (int64_t)d->window * L.topk || d->n_slots > skv::kMaxSlots)
+      return set_error(SKV_ERR_INVALID, "tier: n_slots %d must exceed window*topk = %lld and be <= %d",
+                       d->n_slots, (long long)d->window * L.topk, skv::kMaxSlots);
+  }
   skv_tier* t = new (std::nothrow) skv_tier();
   if (!t) return set_error(SKV_ERR_OOM, "tier: host allocation failed");
   memset(t, 0, sizeof(*t));
-  t->desc = *d;
+  memcpy(&t->desc, d, std::min<size_t>(d->struct_size, sizeof(skv_tier_desc)));
+  t->policy = policy;
   t->B = L.batch; t->T = d->ctx; t->S = L.n_sink; t->L = L.n_tail; t->k = L.topk;
   t->Hkv = L.n_kv_heads; t->D = L.head_dim; t->n_slots = d->n_slots; t->W = d->window;
   t->cap = skv::select_capacity(L);
@@ -466,10 +616,16 @@ extern "C" skv_status sparsekv_tier_resolve(skv_tier* t, const int32_t* idx, con
                                             int32_t step, int32_t* rows, void* stream) {
   if (!t || !idx || !n_sel || !rows) return set_error(SKV_ERR_INVALID, "tier_resolve: NULL argument");
   hipStream_t st = (hipStream_t)stream;
-  hipLaunchKernelGGL(skv::tier_resolve_kernel, dim3(t->B), dim3(skv::kResolveThreads), 0, st, idx,
-                     n_sel, rows, t->slot_pos, t->slot_last, t->slot_ref, t->hand, t->slot_of_pos,
-                     t->miss_pos, t->miss_slot, t->miss_count, t->counters, t->flags, t->T, t->S,
-                     t->L, t->k, t->n_slots, t->W, t->cap, step);
+  if (t->policy == SKV_TIER_LRU)
+    hipLaunchKernelGGL(skv::tier_resolve_kernel<SKV_TIER_LRU>, dim3(t->B), dim3(skv::kResolveThreads), 0,
+                       st, idx, n_sel, rows, t->slot_pos, t->slot_last, t->slot_ref, t->hand,
+                       t->slot_of_pos, t->miss_pos, t->miss_slot, t->miss_count, t->counters, t->flags,
+                       t->T, t->S, t->L, t->k, t->n_slots, t->W, t->cap, step);
+  else
+    hipLaunchKernelGGL(skv::tier_resolve_kernel<SKV_TIER_CLOCK>, dim3(t->B), dim3(skv::kResolveThreads),
+                       0, st, idx, n_sel, rows, t->slot_pos, t->slot_last, t->slot_ref, t->hand,
+                       t->slot_of_pos, t->miss_pos, t->miss_slot, t->miss_count, t->counters, t->flags,
+                       t->T, t->S, t->L, t->k, t->n_slots, t->W, t->cap, step);
   if (hipGetLastError() != hipSuccess) return set_error(SKV_ERR_HIP, "tier_resolve: launch failed");
   hipLaunchKernelGGL(skv::tier_fetch_kernel, dim3(128, t->B), dim3(256), 0, st, t->host_dev,
                      t->miss_pos, t->miss_slot, t->miss_count, t->res_k, t->res_v, t->res_ks,
