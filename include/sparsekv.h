@@ -156,8 +156,7 @@ skv_status sparsekv_workspace_size(const skv_layer_desc* d, size_t* bytes);
  *            with qbar_h = sum of the G query heads of h in ascending order,
  *            all in fp32 with separately rounded multiplies and adds;
  *   qs_scale [B] fp32 out: max|s| / 127 (0 when the sketch is all zero).
- * Uses the workspace (per-head partial sketches and an arrival counter that
- * every call leaves at zero). */
+ * Uses the workspace (the fp32 sketch before quantization). */
 skv_status sparsekv_qsketch(const skv_layer_desc* d, const void* q, const float* basis,
                             int8_t* qs, float* qs_scale, void* ws, size_t ws_bytes, void* stream);
 

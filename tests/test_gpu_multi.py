@@ -180,3 +180,54 @@ def test_multi_query_full_8x250k():
     say("multi full: oracle on sequences 2, 7")
     err = _compare(g, _oracle_multi(c, q, M, sm, [2, 7]), M)
     say("multi full max err", err)
+
+
+def test_multi_query_determinism_and_graph_replay():
+    """Two eager runs are bitwise identical; a captured HIP graph of the
+    multi-query step, replayed several times with eager work in between,
+    gives the eager result every time."""
+    skv = need_gpu()
+    M = 6
+    lens = [15_000, 3_200, 7_777]
+    c = _case(3, 15_360, lens, seed=2107, device="cuda")
+    q = synth.multi_queries(3, M, 24, 256, 2107, device="cuda")
+    sm = 256 ** -0.5
+    a = _run_multi(skv, c, q, M, sm)
+    b = _run_multi(skv, c, q, M, sm)
+    for key in ("qs", "qscale", "idx", "n_sel", "out"):
+        assert np.array_equal(a[key], b[key]), key
+    desc = token_desc_of(skv, c)
+    cap = skv.select_capacity(desc)
+    ws = skv.workspace_multi(desc, M)
+    qs = torch.zeros((c.B, M, 256), dtype=torch.int8, device="cuda")
+    qsc = torch.zeros((c.B, M), dtype=torch.float32, device="cuda")
+    idx = torch.zeros((c.B, M, cap), dtype=torch.int32, device="cuda")
+    nsel = torch.zeros((c.B, M), dtype=torch.int32, device="cuda")
+    out = torch.zeros((c.B, M, c.n_q, c.D), dtype=torch.float32, device="cuda")
+    kv = skv.kv_view(c.k_cache, c.v_cache, c.k_scale, c.v_scale)
+
+    def call():
+        skv.step_multi(desc, M, c.ctx_len, q, c.basis, qs, qsc, c.codes, c.sk_scale, kv, idx, nsel,
+                       sm, out, ws)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):   # warm-up on the capture stream
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for rep in range(4):
+        out.zero_()
+        idx.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        _ = (out * 2).sum().item()   # unrelated eager work between replays
+        assert np.array_equal(out.cpu().numpy().astype(np.float64), a["out"]), "replay %d" % rep
+        gi = idx.cpu().numpy()
+        for bb in range(c.B):
+            for j in range(M):
+                n = int(a["n_sel"][bb, j])
+                assert np.array_equal(gi[bb, j, :n], a["idx"][bb, j, :n])
+    assert skv.check(ws) == 0
