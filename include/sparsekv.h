@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SPARSEKV_ABI_VERSION 2
+#define SPARSEKV_ABI_VERSION 3   /* 3: multi-query step, prefill over host K/V, tier policy field */
 
 typedef int32_t skv_status;
 enum {
