@@ -155,3 +155,29 @@ def test_append_block_mode():
         compare_keys(gs["keys"], os_["keys"], b, 0, c.lens[b] // 4)
         compare_sel(gs, os_, b)
         compare_out(gs, os_, b)
+
+
+def test_multi_query_step_after_appends():
+    """A verification step as served: the current token and 4 drafted ones are
+    appended (5 appends), then the multi-query step verifies all 5 at their
+    causal contexts; must match the oracle on the appended caches."""
+    from test_gpu_multi import _compare as _compare_multi, _oracle_multi, _run_multi
+    skv = need_gpu()
+    M = 5
+    c = synth.make_token_case(2, 20_000, [12_000, 3_134], n_kv=4, n_q=24, D=256, S=64, k=2048,
+                              L=1024, kv_format="i8", n_needles=0, seed=87)
+    for r in range(M):
+        k_new, v_new = _new_rows(2, 4, 256, 88 + r)
+        g, gctx, _ = _append_gpu(skv, c, k_new, v_new)
+        o, octx = _append_oracle(c, k_new, v_new)
+        _compare(g, gctx, o, octx, "i8")
+        c.codes, c.sk_scale = g["codes"], g["sk_scale"]
+        c.k_cache, c.v_cache, c.k_scale, c.v_scale = g["k_cache"], g["v_cache"], g["k_scale"], g["v_scale"]
+        c.ctx_len = gctx.to(torch.int32)
+        c.lens = gctx.tolist()
+    assert c.lens == [12_005, 3_139]     # the second sequence crosses S+k+L = 3136 within the step
+    q = synth.multi_queries(2, M, 24, 256, 89)
+    sm = 256 ** -0.5
+    gm = _run_multi(skv, c, q, M, sm)
+    _compare_multi(gm, _oracle_multi(c, q, M, sm, range(2)), M)
+    assert gm["n_sel"][1].tolist() == [3135, 3136, 3136, 3136, 3136]
