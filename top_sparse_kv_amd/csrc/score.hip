@@ -40,6 +40,15 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kUnroll = 8;
 
+// The collect launches one workgroup per segment, one load batch per wave,
+// where a segment is exactly four batches: the token sketch at 8 lanes per
+// token (transposed collect) and the pooled key at 16 lanes per block.
+template <class Src>
+constexpr bool segment_per_workgroup() {
+  constexpr int per_it = kUnroll * (64 / Src::LANES);
+  return Src::HAS_AUX ? Src::LANES == 8 : per_it * (kThreads / 64) == kSegBlk;
+}
+
 // candidates whose key sparsekv_score writes (not restricted by the dense rule)
 __device__ __forceinline__ void key_range(int mode, int T, int S, int L, int& lo, int& n) {
   if (mode == SKV_INDEX_SKETCH_INT4) {
@@ -60,6 +69,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
     int seg_items) {
   constexpr int N = Src::LANES, IPW = 64 / N, PER_IT = kUnroll * IPW;
   constexpr bool TRANS = COLLECT && Src::HAS_AUX && N == 8;   // see the transposed collect below
+  constexpr bool SPLIT = COLLECT && !Src::HAS_AUX && segment_per_workgroup<Src>();   // pooled, one batch per wave
   const int b = blockIdx.y;
   const int T = clamp_ctx(ctx_len, b, max_ctx, blockIdx.x == 0 ? flags : nullptr);
   int lo, n;
@@ -74,11 +84,11 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // transposed collect: one workgroup per segment, one batch per wave;
   // otherwise one segment per wave
-  const int seg = TRANS ? blockIdx.x : blockIdx.x * (kThreads / 64) + wave;
+  const int seg = TRANS || SPLIT ? blockIdx.x : blockIdx.x * (kThreads / 64) + wave;
   const int i0 = seg * seg_items;
   if (i0 >= n) return;   // workgroup-uniform (transposed) or wave-uniform (no barrier)
   const int i1 = min(n, i0 + seg_items);
-  const int first = TRANS ? i0 + PER_IT * wave : i0;
+  const int first = TRANS || SPLIT ? i0 + PER_IT * wave : i0;
   const int sub = lane % N, tw = lane / N;
   Src src;
   src.init(reinterpret_cast<const uint8_t*>(iq) + (size_t)b * Src::QROW, ik, isc, b, max_ctx, sub);
@@ -158,6 +168,42 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
       const uint64_t ok = ordered_u64(src.key_of(dt, sc));
       cseg[off + (uint32_t)__popcll(x & below)] =
           (u32x4){(uint32_t)ok, (uint32_t)(ok >> 32), (uint32_t)(lo + i), dig};
+    }
+    if (threadIdx.x == 0) segcnt[(size_t)b * n_seg + seg] = tot;
+    return;
+  }
+  if constexpr (SPLIT) {
+    // Pooled keys, one workgroup per 128-block segment: wave w scores the
+    // segment's batch w (32 blocks); the four counts go through LDS so that
+    // the records stay in position order.  Short per-wave work keeps more
+    // loads in flight when the batch holds few sequences.
+    __shared__ uint32_t s_cnt2[kThreads / 64];
+    uint64_t mu[kUnroll], oku[kUnroll];
+    uint32_t digu[kUnroll], tot_w = 0;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int i = first + u * IPW + tw;
+      const double key = src.key(w[u], ax[u]);
+      digu[u] = key_digit16(key);
+      oku[u] = ordered_u64(key);
+      mu[u] = __ballot(sub == 0 && i < i1 && digu[u] >= beta);
+      tot_w += (uint32_t)__popcll(mu[u]);
+    }
+    if (lane == 0) s_cnt2[wave] = tot_w;
+    __syncthreads();
+    uint32_t run = 0, tot = 0;
+#pragma unroll
+    for (int v = 0; v < kThreads / 64; ++v) {
+      const uint32_t c = s_cnt2[v];
+      run += v < wave ? c : 0u;
+      tot += c;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if ((mu[u] >> lane) & 1ull)
+        cseg[run + (uint32_t)__popcll(mu[u] & lt)] =
+            (u32x4){(uint32_t)oku[u], (uint32_t)(oku[u] >> 32), (uint32_t)(lo + first + u * IPW + tw), digu[u]};
+      run += (uint32_t)__popcll(mu[u]);
     }
     if (threadIdx.x == 0) segcnt[(size_t)b * n_seg + seg] = tot;
     return;
@@ -321,8 +367,9 @@ hipError_t launch_token_or_block(const skv_layer_desc& d, const int32_t* ctx_len
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const void* iq_score = qs_out ? (const void*)qs_out : iq;
-  // the transposed collect (8-lane sketch rows) runs one workgroup per segment
-  if (Src::HAS_AUX && Src::LANES == 8) grid.x = Lw->n_seg;
+  // the transposed token collect and the 16-lane pooled collect run one
+  // workgroup per segment
+  if (segment_per_workgroup<Src>()) grid.x = Lw->n_seg;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   if (timer_next(&ev0, &ev1))
     hipExtLaunchKernelGGL((score_kernel<Src, true>), grid, dim3(kThreads), 0, st, ev0, ev1, 0,
