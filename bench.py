@@ -73,6 +73,10 @@ CONFIGS = {
                   workload="4 seq x 250,000 tokens; cfg2 layer shape; int4 host-RAM K/V records read "
                            "zero-copy, windowed-CLOCK hot buffer of 4,096 slots (the LRU line's "
                            "capacity), drifting-locality picks"),
+    "cfg2a": dict(kind="append", B=8, T=250_000, n_kv=4, n_q=24, D=256, S=64, k=2048, L=1024,
+                  kv="i8", layers=1, seed=1002,
+                  workload="decode-step append for 8 seq x 250,000 tokens (cfg2 layer shape): the "
+                           "new token's int8 K/V rows + scales and its int4 key sketch"),
     "cfg5": dict(kind="tier", B=4, T=250_000, n_kv=4, n_q=24, D=256, S=64, k=2048, L=1024,
                  kv="i8", layers=1, seed=1005, warm_steps=64, steps=256,
                  workload="4 seq x 250,000 tokens; cfg2 layer shape; int4 host-RAM K/V records read "
@@ -365,6 +369,75 @@ def _cpu_baseline(layer: Layer, cfg, min_seconds=10.0, max_reps=20):
 PCIE5_X16_GBS = 64.0   # PCIe 5.0 x16, one direction (nominal)
 
 
+def bench_append(cfg, args):
+    """The decode-step append alone: every sequence's new token written at
+    ctx_len - 2000 (inside the cache), timed by the kernel's own dispatches."""
+    L0 = Layer(dict(cfg, kind="token"), 0)
+    c0 = L0.case
+    ws = skv.workspace(L0.desc)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    k_new = torch.randn((c0.B, c0.n_kv, c0.D), generator=g, device="cuda").to(torch.float16)
+    v_new = torch.randn((c0.B, c0.n_kv, c0.D), generator=g, device="cuda").to(torch.float16)
+    ctx_a = (L0.ctx - 2000).clamp(min=0).to(torch.int32).contiguous()
+
+    def call(layer, ws_):
+        skv.append(layer.desc, ctx_a, k_new, v_new, layer.basis, layer.kv, layer.ikeys,
+                   layer.iscale, ws_)
+    for _ in range(max(5, args.warmup)):
+        call(L0, ws)
+    secs = time_loop(call, [L0], ws, args.steps)
+    skv.timer_enable(True)
+    time_loop(call, [L0], ws, args.steps)
+    a_ms, a_n = skv.timer_read()
+    skv.timer_enable(False)
+    skv.check(ws)
+    B, H, D = c0.B, c0.n_kv, c0.D
+    # what one call must move: the new rows (fp16) and the basis in; int8 rows,
+    # row scales, sketch codes and scale out; ctx_len in and out
+    alg = B * H * D * 2 * 2 + H * D * 64 * 4 + B * (H * D * 2 + H * 2 * 2 + H * 32 + 2) + B * 8
+    a_s = a_ms / 1e3 / max(1, a_n)
+    res = {
+        "metric": METRIC + " (append: calls/s)", "value": round(args.steps / secs, 2),
+        "unit": "appends/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(1e3 * secs / args.steps, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "i8", "data": "synthetic",
+        "config": {"workload": cfg["workload"], "name": args.config, "batch": B, "ctx": cfg["T"]},
+        "roofline": {"kernel": "append", "bound": "hbm", "achieved": round(alg / a_s / 1e9, 2),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(alg / a_s / 1e9 / PEAK_HBM_GBS, 5), "traffic": None,
+                     "bytes_per_launch": alg, "avg_launch_us": round(a_s * 1e6, 2),
+                     "launches_timed": a_n,
+                     "note": "one workgroup per sequence: launch- and latency-bound"},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        import oracle
+        from threadpoolctl import threadpool_limits
+        caches = {"codes": c0.codes[:, -2100:].cpu().numpy().copy(),
+                  "sk_scale": c0.sk_scale[:, -2100:].cpu().numpy().copy(),
+                  "k": c0.k_cache[:, -2100:].cpu().numpy().copy(),
+                  "v": c0.v_cache[:, -2100:].cpu().numpy().copy(),
+                  "k_scale": c0.k_scale[:, -2100:].cpu().numpy().copy(),
+                  "v_scale": c0.v_scale[:, -2100:].cpu().numpy().copy()}
+        kn, vn, basis = k_new.cpu().numpy(), v_new.cpu().numpy(), c0.basis.cpu().numpy()
+        ctx0 = np.full(B, 100, dtype=np.int32)   # rows inside the host copy of the last 2100 rows
+        t_total, reps = 0.0, 0
+        with threadpool_limits(limits=1):
+            while reps < 5000 and (reps == 0 or t_total < 10.0):
+                t0 = time.perf_counter()
+                oracle.append.append_tokens(ctx0, kn, vn, basis, caches, 2100)
+                t_total += time.perf_counter() - t0
+                reps += 1
+        res["cpu_baseline"] = {"value": round(reps / t_total, 3), "unit": "appends/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": "%d appends of all %d sequences into a host copy of the "
+                                         "caches' last rows" % (reps, B),
+                               "seconds": round(t_total, 3)}
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
 def bench_prefill(cfg, args):
     """Prefill attention over host-resident K/V: one call streams the history
     once through the working buffer and attends every prefill query's picks
@@ -524,7 +597,21 @@ def bench_tier(cfg, args):
         e1.record()
         e1.synchronize()
         rsecs = e0.elapsed_time(e1) / 1e3
+        # the host-record fetch kernel alone, timed by its own dispatches (a
+        # third replay of the same picks: the same misses)
+        tier.reset()
+        for s_ in range(warm):
+            tier.resolve(idx_all[s_], nsel, s_, rows)
+        skv.timer_enable(True)
+        for s_ in range(warm, warm + steps):
+            tier.resolve(idx_all[s_], nsel, s_, rows)
+        f_ms, f_n = skv.timer_read()
+        skv.timer_enable(False)
         assert skv.check(ws) == 0
+        cpu = None
+        if not args.no_cpu_baseline:
+            log("cpu baseline (oracle)")
+            cpu = _tier_cpu_baseline(cfg, c, picks, warm, tier.host_records()[0], lru, n_slots)
     finally:
         tier.close()
     hits, misses = st1.hits - st0.hits, st1.misses - st0.misses
@@ -551,9 +638,48 @@ def bench_tier(cfg, args):
                  "pcie_GBps_during_resolve": round(hbytes / rsecs / 1e9, 2),
                  "pcie_peak_GBps": 64.0},
         "roofline": None,
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
+    if f_n:
+        f_s = f_ms / 1e3 / f_n
+        per = hbytes / steps
+        res_line["roofline"] = {"kernel": "tier_fetch", "bound": "pcie",
+                                "achieved": round(per / f_s / 1e9, 2), "peak": PCIE5_X16_GBS,
+                                "unit": "GB/s", "frac": round(per / f_s / 1e9 / PCIE5_X16_GBS, 4),
+                                "traffic": None, "bytes_per_launch": round(per),
+                                "avg_launch_us": round(f_s * 1e6, 2), "launches_timed": f_n}
     print(json.dumps(res_line), flush=True)
+
+
+def _tier_cpu_baseline(cfg, c, picks, warm, records_b, lru, n_slots, min_seconds=10.0):
+    """The oracle's host-tier layer-step on sequence 0 (hot-buffer resolve with
+    its policy, then attention over the resident rows and the fetched host
+    records), after the same warm-up; scaled to the whole batch."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    B, T, S, L, k = cfg["B"], cfg["T"], cfg["S"], cfg["L"], cfg["k"]
+    tier = oracle.residency.LruTier(n_slots, T) if lru else oracle.ClockTier(n_slots, T, window=1)
+    for s_ in range(warm):
+        tier.step(picks[s_, 0], s_)
+    q = c.q[0].cpu().numpy()
+    rk, rv = c.res_k[0].cpu().numpy(), c.res_v[0].cpu().numpy()
+    rks, rvs = c.res_ks[0].cpu().numpy(), c.res_vs[0].cpu().numpy()
+    sm = cfg["D"] ** -0.5
+    t_total, reps = 0.0, 0
+    with threadpool_limits(limits=1):
+        while reps < 40 and (reps == 0 or t_total < min_seconds) and warm + reps < picks.shape[0]:
+            s_ = warm + reps
+            idx = np.concatenate([np.arange(S), picks[s_, 0], np.arange(T - L, T)])
+            t0 = time.perf_counter()
+            tier.step(picks[s_, 0], s_)
+            oracle.tier_attention(q, records_b, rk, rv, rks, rvs, idx, T, S, L, sm,
+                                  cfg["n_q"] // cfg["n_kv"], cfg["D"])
+            t_total += time.perf_counter() - t0
+            reps += 1
+    return {"value": round(reps / t_total / B, 4), "unit": "layer-steps/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "%d steps of sequence 0 (resolve + attention), scaled to the %d-sequence batch"
+                      % (reps, B), "seconds": round(t_total, 3)}
 
 
 def main():
@@ -584,6 +710,9 @@ def main():
     cfg = CONFIGS[args.config]
     if cfg["kind"] == "prefill":
         bench_prefill(cfg, args)
+        return
+    if cfg["kind"] == "append":
+        bench_append(cfg, args)
         return
     if cfg["kind"] == "tier":
         args.warmup_given = "--warmup" in sys.argv

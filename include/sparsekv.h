@@ -353,10 +353,12 @@ skv_status sparsekv_check(void* ws, size_t ws_bytes, void* stream, uint32_t* fla
 
 /* ---- diagnostic kernel timer -------------------------------------------------
  * For measurement only (not thread-safe, not capturable).  While enabled, every
- * launch of the streaming score-and-collect kernel (the one that reads the whole
- * index in sparsekv_score_topk / sparsekv_step) carries a start/stop event pair
- * that its dispatch records (hipExtLaunchKernelGGL), so the pair spans the
- * kernel's execution; up to 4096 launches are recorded.  Enabling again
+ * launch of the dominant kernel of a call carries a start/stop event pair that
+ * its dispatch records (hipExtLaunchKernelGGL), so the pair spans the kernel's
+ * execution: the streaming score-and-collect kernel (the one that reads the
+ * whole index in sparsekv_score_topk, sparsekv_step, sparsekv_step_multi), the
+ * host-record fetch of sparsekv_tier_resolve and the kernel of sparsekv_append;
+ * up to 4096 launches are recorded.  Enabling again
  * discards earlier records.  sparsekv_timer_read synchronizes on the recorded
  * events and returns the summed kernel time (ms) and the number of launches. */
 skv_status sparsekv_timer_enable(int enable);

@@ -26,6 +26,8 @@
 // value i from the K rows staged in LDS.
 #include "keys_common.h"
 
+#include <hip/hip_ext.h>
+
 namespace skv {
 namespace {
 
@@ -204,11 +206,23 @@ hipError_t launch_append(const skv_layer_desc& d, int32_t* ctx_len, const void* 
   uint32_t* flags = ws_ptr<uint32_t>(ws, L.flags);
   const bool i8 = d.kv_dtype == SKV_KV_I8_ROWSCALE;
   if (d.n_kv_heads > kAppMaxHkv || d.n_kv_heads * d.rank > kAppThreads) return hipErrorInvalidValue;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  const bool timed = timer_next(&ev0, &ev1);   // diagnostic timer (sparsekv_timer_enable)
 #define SKV_AP(DD, I8)                                                                           \
-  hipLaunchKernelGGL((append_kernel<DD, I8>), dim3(d.batch), dim3(kAppThreads), 0, st, ctx_len,  \
-                     (const __half*)k_new, (const __half*)v_new, basis, (uint8_t*)kv.k,           \
-                     (uint8_t*)kv.v, (uint16_t*)kv.k_scale, (uint16_t*)kv.v_scale, kv.rows,       \
-                     (uint8_t*)index_keys, index_scale, d.n_kv_heads, d.rank, d.max_ctx, flags)
+  do {                                                                                           \
+    if (timed)                                                                                   \
+      hipExtLaunchKernelGGL((append_kernel<DD, I8>), dim3(d.batch), dim3(kAppThreads), 0, st,    \
+                            ev0, ev1, 0, ctx_len, (const __half*)k_new, (const __half*)v_new,    \
+                            basis, (uint8_t*)kv.k, (uint8_t*)kv.v, (uint16_t*)kv.k_scale,        \
+                            (uint16_t*)kv.v_scale, kv.rows, (uint8_t*)index_keys, index_scale,   \
+                            d.n_kv_heads, d.rank, d.max_ctx, flags);                             \
+    else                                                                                         \
+      hipLaunchKernelGGL((append_kernel<DD, I8>), dim3(d.batch), dim3(kAppThreads), 0, st,       \
+                         ctx_len, (const __half*)k_new, (const __half*)v_new, basis,             \
+                         (uint8_t*)kv.k, (uint8_t*)kv.v, (uint16_t*)kv.k_scale,                  \
+                         (uint16_t*)kv.v_scale, kv.rows, (uint8_t*)index_keys, index_scale,      \
+                         d.n_kv_heads, d.rank, d.max_ctx, flags);                                \
+  } while (0)
   if (d.head_dim == 256 && i8) SKV_AP(256, true);
   else if (d.head_dim == 256) SKV_AP(256, false);
   else if (d.head_dim == 128 && i8) SKV_AP(128, true);

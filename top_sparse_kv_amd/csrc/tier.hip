@@ -40,6 +40,8 @@
 // in slot order: two prefix sums over the slots in index order.
 #include "keys_common.h"
 
+#include <hip/hip_ext.h>
+
 #include <algorithm>
 #include <new>
 #include <stddef.h>
@@ -627,9 +629,15 @@ extern "C" skv_status sparsekv_tier_resolve(skv_tier* t, const int32_t* idx, con
                        t->slot_of_pos, t->miss_pos, t->miss_slot, t->miss_count, t->counters, t->flags,
                        t->T, t->S, t->L, t->k, t->n_slots, t->W, t->cap, step);
   if (hipGetLastError() != hipSuccess) return set_error(SKV_ERR_HIP, "tier_resolve: launch failed");
-  hipLaunchKernelGGL(skv::tier_fetch_kernel, dim3(128, t->B), dim3(256), 0, st, t->host_dev,
-                     t->miss_pos, t->miss_slot, t->miss_count, t->res_k, t->res_v, t->res_ks,
-                     t->res_vs, t->T, t->Hkv, t->k, t->res_rows, t->S + t->L);
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  if (skv::timer_next(&ev0, &ev1))   // diagnostic timer (sparsekv_timer_enable)
+    hipExtLaunchKernelGGL(skv::tier_fetch_kernel, dim3(128, t->B), dim3(256), 0, st, ev0, ev1, 0,
+                          t->host_dev, t->miss_pos, t->miss_slot, t->miss_count, t->res_k, t->res_v,
+                          t->res_ks, t->res_vs, t->T, t->Hkv, t->k, t->res_rows, t->S + t->L);
+  else
+    hipLaunchKernelGGL(skv::tier_fetch_kernel, dim3(128, t->B), dim3(256), 0, st, t->host_dev,
+                       t->miss_pos, t->miss_slot, t->miss_count, t->res_k, t->res_v, t->res_ks,
+                       t->res_vs, t->T, t->Hkv, t->k, t->res_rows, t->S + t->L);
   if (hipGetLastError() != hipSuccess) return set_error(SKV_ERR_HIP, "tier_fetch: launch failed");
   t->steps += 1;
   return SKV_OK;
