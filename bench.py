@@ -737,6 +737,11 @@ def main():
     time_loop(Layer.step, layers, ws, max(50, args.steps // 2))
     score_ms, score_n = skv.timer_read()
     skv.timer_enable(False)
+    # the attention kernel (gather + softmax tiles), same step loop
+    skv.timer_enable(skv.SKV_TIMER_ATTEND)
+    time_loop(Layer.step, layers, ws, max(50, args.steps // 2))
+    att_ms, att_n = skv.timer_read()
+    skv.timer_enable(False)
     nk = max(50, args.steps // 2)
     kt = {}
     for name in [] if multi else (["qsketch"] if cfg["kind"] == "token" else []) + [
@@ -778,6 +783,19 @@ def main():
                 frac=round(ab["scan"] / score_s / 1e9 / PEAK_HBM_GBS, 4), traffic=traffic,
                 bytes_per_launch=ab["scan"], avg_launch_us=round(score_s * 1e6, 2),
                 launches_timed=score_n)
+    # the attention kernel: the K/V rows (+ row scales) it must gather at
+    # least once (with several queries, the union of a sequence's picks) and
+    # the query rows it reads
+    att_s = att_ms / 1e3 / max(1, att_n)
+    att_bytes = ab["gather"] + cfg["B"] * max(1, multi) * cfg["n_q"] * cfg["D"] * 2
+    att = dict(kernel="attend", bound="hbm", achieved=round(att_bytes / att_s / 1e9, 1),
+               peak=PEAK_HBM_GBS, unit="GB/s",
+               frac=round(att_bytes / att_s / 1e9 / PEAK_HBM_GBS, 4), traffic=None,
+               bytes_per_launch=att_bytes, avg_launch_us=round(att_s * 1e6, 2),
+               launches_timed=att_n)
+    if multi and att_s > score_s:
+        # several queries: the per-query gathers outweigh the one shared scan
+        roof, att = att, roof
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -798,6 +816,7 @@ def main():
                      "frac_of_peak": round(ab["total"] * value / 1e9 / PEAK_HBM_GBS, 4)},
         "kernels_us": {k: round(v * 1e6, 2) for k, v in kt.items()},
         "roofline": roof,
+        "other_kernel": att,
     }
     if multi:
         res["query_tokens_per_s"] = round(value * cfg["B"] * multi, 1)

@@ -353,14 +353,19 @@ skv_status sparsekv_check(void* ws, size_t ws_bytes, void* stream, uint32_t* fla
 
 /* ---- diagnostic kernel timer -------------------------------------------------
  * For measurement only (not thread-safe, not capturable).  While enabled, every
- * launch of the dominant kernel of a call carries a start/stop event pair that
- * its dispatch records (hipExtLaunchKernelGGL), so the pair spans the kernel's
- * execution: the streaming score-and-collect kernel (the one that reads the
- * whole index in sparsekv_score_topk, sparsekv_step, sparsekv_step_multi), the
- * host-record fetch of sparsekv_tier_resolve and the kernel of sparsekv_append;
- * up to 4096 launches are recorded.  Enabling again
+ * launch of one kind of kernel carries a start/stop event pair that its
+ * dispatch records (hipExtLaunchKernelGGL), so the pair spans the kernel's
+ * execution.  enable = 0 turns the timer off; SKV_TIMER_ATTEND times the
+ * attention kernel (sparsekv_attend, sparsekv_step, sparsekv_step_multi; not
+ * the merge of its partials); any other nonzero value (SKV_TIMER_STREAM) times
+ * the dominant kernel of a call: the streaming score-and-collect kernel (the
+ * one that reads the whole index in sparsekv_score_topk, sparsekv_step,
+ * sparsekv_step_multi), the host-record fetch of sparsekv_tier_resolve and the
+ * kernel of sparsekv_append.  Up to 4096 launches are recorded.  Enabling again
  * discards earlier records.  sparsekv_timer_read synchronizes on the recorded
  * events and returns the summed kernel time (ms) and the number of launches. */
+#define SKV_TIMER_STREAM 1
+#define SKV_TIMER_ATTEND 2
 skv_status sparsekv_timer_enable(int enable);
 skv_status sparsekv_timer_read(double* total_ms, int64_t* launches);
 

@@ -20,7 +20,8 @@ from . import _lib
 from ._lib import (KVView, LayerDesc, TierDesc, TierStats, SKV_INDEX_SKETCH_INT4,  # noqa: F401
                    SKV_INDEX_POOLED_BF16, SKV_KV_I8_ROWSCALE, SKV_KV_F16, SKV_KV_BF16, SKV_Q_F16,
                    SKV_Q_BF16, SKV_FLAG_CTX_RANGE, SKV_FLAG_INDEX_RANGE, SKV_FLAG_TOPK_SLOW,
-                   SKV_FLAG_TIER_INPUT, SKV_TIER_CLOCK, SKV_TIER_LRU)
+                   SKV_FLAG_TIER_INPUT, SKV_TIER_CLOCK, SKV_TIER_LRU,
+                   SKV_TIMER_STREAM, SKV_TIMER_ATTEND)
 
 
 class SkvError(RuntimeError):
@@ -210,9 +211,12 @@ def append_block(desc, ctx_len, k_new, v_new, index_raw, index_stage, kv: KVView
                                        _p(index_keys), _p(ws), ws.numel(), _stream(stream)))
 
 
-def timer_enable(on: bool = True):
-    """Diagnostic: bracket each launch of the streaming score kernel with events."""
-    _check(lib().sparsekv_timer_enable(1 if on else 0))
+def timer_enable(on=True):
+    """Diagnostic: bracket each launch of one kind of kernel with events.
+    False / 0: off; SKV_TIMER_ATTEND: the attention kernel; True or
+    SKV_TIMER_STREAM: the streaming kernel of each call."""
+    kind = 0 if not on else (SKV_TIMER_ATTEND if on == SKV_TIMER_ATTEND else SKV_TIMER_STREAM)
+    _check(lib().sparsekv_timer_enable(kind))
 
 
 def timer_read():

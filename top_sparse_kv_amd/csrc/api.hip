@@ -15,7 +15,7 @@ namespace skv {
 // ---- diagnostic kernel timer (not thread-safe, not for graph capture) ----
 namespace {
 struct KernelTimer {
-  bool on = false;
+  int kind = 0;                 // 0: off, else the kind of kernel timed
   std::vector<hipEvent_t> ev;   // begin/end pairs
   size_t used = 0;              // events recorded since enable
   int64_t dropped = 0;
@@ -24,8 +24,8 @@ KernelTimer g_timer;
 constexpr size_t kTimerPairs = 4096;
 }  // namespace
 
-bool timer_next(hipEvent_t* start, hipEvent_t* stop) {
-  if (!g_timer.on) return false;
+bool timer_next(int kind, hipEvent_t* start, hipEvent_t* stop) {
+  if (g_timer.kind != kind) return false;
   if (g_timer.used + 2 > g_timer.ev.size()) {
     ++g_timer.dropped;
     return false;
@@ -415,7 +415,7 @@ skv_status sparsekv_timer_enable(int enable) {
         return set_error(SKV_ERR_HIP, "timer: event creation failed");
       }
   }
-  g_timer.on = enable != 0;
+  g_timer.kind = enable == 0 ? 0 : (enable == SKV_TIMER_ATTEND ? SKV_TIMER_ATTEND : SKV_TIMER_STREAM);
   g_timer.used = 0;
   g_timer.dropped = 0;
   return ok();

@@ -207,7 +207,7 @@ hipError_t launch_append(const skv_layer_desc& d, int32_t* ctx_len, const void* 
   const bool i8 = d.kv_dtype == SKV_KV_I8_ROWSCALE;
   if (d.n_kv_heads > kAppMaxHkv || d.n_kv_heads * d.rank > kAppThreads) return hipErrorInvalidValue;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
-  const bool timed = timer_next(&ev0, &ev1);   // diagnostic timer (sparsekv_timer_enable)
+  const bool timed = timer_next(kTimerStream, &ev0, &ev1);   // diagnostic timer (sparsekv_timer_enable)
 #define SKV_AP(DD, I8)                                                                           \
   do {                                                                                           \
     if (timed)                                                                                   \

@@ -10,10 +10,11 @@
 //
 // Work split: one workgroup of W waves per (sequence, KV head, chunk of 32*W
 // selected rows); each wave runs a softmax tile over 32 rows for the G query
-// heads of that KV head.  W is the largest of 16, 8, 4 that still gives about
-// one workgroup per compute unit, else 2 (a 250K-token batch of 8 uses 16; a
+// heads of that KV head.  W is the largest of 8, 4 that still gives about
+// one workgroup per compute unit, else 2 (a 250K-token batch of 8 uses 8; a
 // single 1M-token sequence uses 2, so its few thousand rows are gathered by
-// many compute units rather than ten).  The waves merge in two LDS stages
+// many compute units rather than ten).  With 8 waves two workgroups share a
+// compute unit, so one gathers while the other merges.  The waves merge in two LDS stages
 // (wave w+W/2 into wave w, then the W/2 survivors), which bounds the LDS at
 // (W/2)*G*(D+4) floats, and the workgroup writes one (max, sum, unnormalised
 // output) partial; a second kernel merges the chunks of each query head in
@@ -39,6 +40,8 @@
 // bf16) part and both are multiplied, so P keeps ~22 (or ~16) significant bits.
 // All accumulation is fp32; the output is fp32.
 #include "skv_internal.h"
+
+#include <hip/hip_ext.h>
 
 namespace skv {
 namespace {
@@ -340,7 +343,7 @@ __global__ __launch_bounds__(64 * WAVES) void attend_kernel(
     for (int t = 0; t < NT; ++t) o[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- merge the 16 waves of the workgroup in LDS, in two stages ----
+  // ---- merge the W waves of the workgroup in LDS, in two stages ----
   // Wave w + HALF goes into wave w; then the HALF survivors are combined.  A
   // slot holds G rows of D + 4 floats; lane (i16, g) owns columns
   // i16*(D/16) .. +D/16 of heads 4g .. 4g+3, stored as float4 runs.
@@ -518,11 +521,19 @@ hipError_t launch_attend(const skv_layer_desc& d, const void* q, const skv_kv_vi
   const int waves = att_waves(d);
   const size_t lds = (size_t)(waves / 2) * G * (d.head_dim + 4) * sizeof(float);
   const float sl = sm_scale * kLog2e;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  const bool timed = timer_next(kTimerAttend, &ev0, &ev1);   // diagnostic timer
+#define SKV_AT_ARGS                                                                                \
+  q, (const uint8_t*)kv.k, (const uint8_t*)kv.v, kv.k_scale, kv.v_scale, kv.rows, idx, n_sel, cap,  \
+      sl, d.n_q_heads, d.n_kv_heads, part_ml, part_o, Lw.n_att_chunks, flags, mq, n_keys
 #define SKV_AT(KVT, DD, WV)                                                                        \
-  hipLaunchKernelGGL((attend_kernel<KVT, DD, WV>), grid, dim3(64 * WV), lds, st, q,              \
-                     (const uint8_t*)kv.k, (const uint8_t*)kv.v, kv.k_scale, kv.v_scale, kv.rows, \
-                     idx, n_sel, cap, sl, d.n_q_heads, d.n_kv_heads, part_ml, part_o,             \
-                     Lw.n_att_chunks, flags, mq, n_keys)
+  do {                                                                                             \
+    if (timed)                                                                                     \
+      hipExtLaunchKernelGGL((attend_kernel<KVT, DD, WV>), grid, dim3(64 * WV), lds, st, ev0, ev1, \
+                            0, SKV_AT_ARGS);                                                       \
+    else                                                                                           \
+      hipLaunchKernelGGL((attend_kernel<KVT, DD, WV>), grid, dim3(64 * WV), lds, st, SKV_AT_ARGS); \
+  } while (0)
 #define SKV_AT_W(KVT, DD)                                                                          \
   do {                                                                                             \
     if (waves == 16) SKV_AT(KVT, DD, 16);                                                          \
@@ -540,6 +551,7 @@ hipError_t launch_attend(const skv_layer_desc& d, const void* q, const skv_kv_vi
   else return hipErrorInvalidValue;
 #undef SKV_AT_W
 #undef SKV_AT
+#undef SKV_AT_ARGS
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attend_merge_kernel, dim3(d.n_q_heads, d.batch), dim3(256), 0, st, part_ml,

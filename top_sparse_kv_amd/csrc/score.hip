@@ -371,7 +371,7 @@ hipError_t launch_token_or_block(const skv_layer_desc& d, const int32_t* ctx_len
   // workgroup per segment
   if (segment_per_workgroup<Src>()) grid.x = Lw->n_seg;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
-  if (timer_next(&ev0, &ev1))
+  if (timer_next(kTimerStream, &ev0, &ev1))
     hipExtLaunchKernelGGL((score_kernel<Src, true>), grid, dim3(kThreads), 0, st, ev0, ev1, 0,
                           iq_score, ik, isc, ctx_len, (double*)nullptr, (const TopkState*)state,
                           ws_ptr<Cand>(ws, Lw->cand), ws_ptr<uint32_t>(ws, Lw->segcnt), flags, mode,

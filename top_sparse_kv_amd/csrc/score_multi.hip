@@ -297,7 +297,7 @@ hipError_t launch_multi_tb(const skv_layer_desc& dv, int mq, const int32_t* ctx_
   if (e != hipSuccess) return e;
   const dim3 grid(L.n_seg, B);
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
-  if (timer_next(&ev0, &ev1))
+  if (timer_next(kTimerStream, &ev0, &ev1))
     hipExtLaunchKernelGGL((score_multi_kernel<TB>), grid, dim3(kThreads), 0, st, ev0, ev1, 0,
                           (const int8_t*)qs_out, ik, isc, ctx_len, ws_ptr<const TopkState>(ws, L.state),
                           ws_ptr<Cand>(ws, L.cand), ws_ptr<uint32_t>(ws, L.segcnt),

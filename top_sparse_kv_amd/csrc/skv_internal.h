@@ -56,16 +56,20 @@ inline int select_capacity(const skv_layer_desc& d) {
   return d.index_mode == SKV_INDEX_SKETCH_INT4 ? d.n_sink + d.topk + d.n_tail : 4 * d.topk + 3;
 }
 
-// Waves per attention workgroup (one 32-row tile each): the largest of 16,
-// 8, 4 that still gives at least 200 workgroups (about one per compute unit),
-// else 2, so a small batch is spread over the GPU instead of a few CUs.
+// Waves per attention workgroup (one 32-row tile each): the largest of 8 and
+// 4 that still gives at least 200 workgroups (about one per compute unit),
+// else 2, so a small batch is spread over the GPU instead of a few CUs; more
+// waves (up to 16) only where the capacity would need more than
+// kMaxAttChunks chunks.  Two 8-wave workgroups per compute unit let one
+// gather while the other merges, which 16-wave workgroups (one per compute
+// unit) cannot.
 inline int att_waves(const skv_layer_desc& d) {
   const int cap = select_capacity(d);
-  for (int w = 16; w > 2; w >>= 1) {
-    const int chunks = (cap + kAttRowsPerWave * w - 1) / (kAttRowsPerWave * w);
-    if ((int64_t)d.batch * d.n_kv_heads * chunks >= 200) return w;
-  }
-  return 2;
+  auto chunks = [cap](int w) { return (cap + kAttRowsPerWave * w - 1) / (kAttRowsPerWave * w); };
+  int w = 8;
+  while (w > 2 && (int64_t)d.batch * d.n_kv_heads * chunks(w) < 200) w >>= 1;
+  while (w < 16 && chunks(w) > kMaxAttChunks) w <<= 1;
+  return w;
 }
 inline int att_rows_per_wg(const skv_layer_desc& d) { return kAttRowsPerWave * att_waves(d); }
 
@@ -148,11 +152,13 @@ __device__ __forceinline__ float bf16_bits_to_float(uint16_t h) {
 }
 
 // ---------------------------------------------------------------------------
-// diagnostic kernel timer (sparsekv_timer_*): when enabled, the streaming
-// score kernel is launched with a start/stop event pair recorded by the
-// dispatch itself (hipExtLaunchKernelGGL); otherwise both are null
+// diagnostic kernel timer (sparsekv_timer_*): when it is enabled for the
+// given kind, the kernel is launched with a start/stop event pair recorded by
+// the dispatch itself (hipExtLaunchKernelGGL); otherwise both stay null
 // ---------------------------------------------------------------------------
-bool timer_next(hipEvent_t* start, hipEvent_t* stop);
+constexpr int kTimerStream = SKV_TIMER_STREAM;   // the call's streaming kernel
+constexpr int kTimerAttend = SKV_TIMER_ATTEND;   // the attention kernel
+bool timer_next(int kind, hipEvent_t* start, hipEvent_t* stop);
 
 // ---------------------------------------------------------------------------
 // launchers (each returns hipSuccess or the launch error)

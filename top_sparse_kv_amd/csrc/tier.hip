@@ -630,7 +630,7 @@ extern "C" skv_status sparsekv_tier_resolve(skv_tier* t, const int32_t* idx, con
                        t->T, t->S, t->L, t->k, t->n_slots, t->W, t->cap, step);
   if (hipGetLastError() != hipSuccess) return set_error(SKV_ERR_HIP, "tier_resolve: launch failed");
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
-  if (skv::timer_next(&ev0, &ev1))   // diagnostic timer (sparsekv_timer_enable)
+  if (skv::timer_next(skv::kTimerStream, &ev0, &ev1))   // diagnostic timer (sparsekv_timer_enable)
     hipExtLaunchKernelGGL(skv::tier_fetch_kernel, dim3(128, t->B), dim3(256), 0, st, ev0, ev1, 0,
                           t->host_dev, t->miss_pos, t->miss_slot, t->miss_count, t->res_k, t->res_v,
                           t->res_ks, t->res_vs, t->T, t->Hkv, t->k, t->res_rows, t->S + t->L);
