@@ -171,3 +171,64 @@ PINS.update({
     "pooled_from_raw": "hand-worked fixture (exact mean, round to even, flush below 2^-8, clamp at 255), agreement with an exact-fraction mean",
     "append_block_tokens": "staging slot t % 4, pooled key only on t % 4 == 3, full sequences untouched",
 })
+
+
+# ----------------------------------------------------------------------------
+# host tier: the append also writes the token's host record and moves the tail
+# ----------------------------------------------------------------------------
+# Page "8 agents x 250K ...", section "The mechanism": the full K/V of every
+# token lives in host RAM as int4 with 64-dim groups and fp16 group scales; the
+# GPU keeps the sinks and the most recent tokens (the tail) as int8 rows.
+# Reading (the page gives no encoding): a group's scale is
+# g = fp16( fp32(amax / 7) ) and its codes clamp(rint(x / g), +-7) (0 when
+# g == 0), x / g a correctly rounded fp32 quotient; the row is the D/2 code
+# bytes (element 2j in the low nibble of byte j) followed by the D/64 fp16
+# group scales.  Appending position T of a sequence: its host record is the
+# K row then the V row in that format, the tail loses position T - L and gains
+# T as an int8 row (the int8 row rule above), the key sketch is written as in
+# the plain append, and the context becomes T + 1.
+
+HOST_GROUP = 64
+
+
+def host_row_i4(x16: np.ndarray) -> np.ndarray:
+    """fp16 row [D] (D a multiple of 64) -> host row bytes [D/2 + 2*(D/64)]."""
+    x = np.asarray(x16, dtype=np.float16).astype(np.float32)
+    D = x.size
+    ng = D // HOST_GROUP
+    codes = np.zeros(D, dtype=np.int8)
+    scales = np.zeros(ng, dtype=np.float16)
+    for g in range(ng):
+        xs = x[g * HOST_GROUP:(g + 1) * HOST_GROUP]
+        s16 = np.float16(_fp32_quotient(np.abs(xs).max(), 7.0))
+        s = np.float32(s16)
+        scales[g] = s16
+        if s > 0:
+            codes[g * HOST_GROUP:(g + 1) * HOST_GROUP] = np.clip(np.rint(xs / s), -7, 7)
+    return np.concatenate([pack_int4(codes), scales.view(np.uint8)])
+
+
+def tier_append_token(T, records_b, res_k, res_v, res_ks, res_vs, S, L, k16, v16):
+    """Appends position T of one sequence in the host-tier layout; returns T + 1.
+
+    records_b: uint8 [capacity][H_kv][2 * row bytes] (K row then V row), updated
+    in place; res_k / res_v int8 [S+L][H_kv][D] and res_ks / res_vs fp16
+    [S+L][H_kv] hold the sinks then the tail in position order (T-L .. T-1),
+    updated in place.  k16, v16: fp16 [H_kv][D]."""
+    H = k16.shape[0]
+    for h in range(H):
+        kr, vr = host_row_i4(k16[h]), host_row_i4(v16[h])
+        records_b[T, h] = np.concatenate([kr, vr])
+    if L > 0:
+        kq, ks = row_i8(k16)
+        vq, vs = row_i8(v16)
+        for a, new in ((res_k, kq), (res_v, vq), (res_ks, ks), (res_vs, vs)):
+            a[S:S + L - 1] = a[S + 1:S + L].copy()
+            a[S + L - 1] = new
+    return T + 1
+
+
+PINS.update({
+    "host_row_i4": "hand-worked fixture (tests/golden/host_record_i4.txt): exact scales, ties to even, zero group, nibble order; |x - g*c| <= g/2 off the clamp; the group amax maps to +-7; decoding through oracle.host_row_dequant stays within its rounding bound",
+    "tier_append_token": "tail shift on a toy layout: sinks untouched, the tail holds the last L appended rows in position order, the record of position T only; ring-free position bookkeeping",
+})

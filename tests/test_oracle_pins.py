@@ -819,3 +819,110 @@ def test_lru_invariants_drifting_workload():
             newest_evicted = max((before_last[x], x) for x in evicted)
             assert oldest_kept is None or newest_evicted < oldest_kept
         assert set(tier.pos[tier.pos >= 0].tolist()) >= set(p.tolist())
+
+
+# --------------------------------------------------------------------------
+# host record of an appended token (tier append)
+# --------------------------------------------------------------------------
+
+def _group_values(spec):
+    x = np.zeros(64, dtype=np.float16)
+    if spec.startswith("all:"):
+        x[:] = float(spec[4:])
+    elif spec:
+        for item in spec.split(","):
+            i, v = item.split(":")
+            x[int(i)] = float(v)
+    return x
+
+
+def _group_bytes(spec):
+    items = spec.split(",")
+    out = []
+    for it in items:
+        if it.endswith("..."):
+            b = int(it[:-3], 16)
+            out += [b] * (32 - len(out))
+        else:
+            out.append(int(it, 16))
+    assert len(out) == 32
+    return out
+
+
+def test_host_record_fixture():
+    groups = [_kv(ln) for ln in _lines("host_record_i4.txt") if ln.startswith("group ")]
+    assert len(groups) == 4
+    row = np.concatenate([_group_values(g["nz"]) for g in groups])
+    got = oracle.append.host_row_i4(row)
+    assert got.size == 256 // 2 + 2 * 4
+    for gi, g in enumerate(groups):
+        assert got[32 * gi:32 * gi + 32].tolist() == _group_bytes(g["bytes"]), gi
+        assert int(got[128:].view(np.uint16)[gi]) == int(g["scale"], 16), gi
+
+
+def test_host_record_invariants():
+    """Codes decoded by oracle.unpack_int4 (written independently of the
+    packer) reconstruct each group within half a step; the largest element of
+    a group lands on +-7; the fetch decoder (oracle.host_row_dequant) turns the
+    record into an int8 row within its own rounding bound."""
+    rng = np.random.default_rng(31)
+    D = 256
+    for trial in range(60):
+        x = (rng.standard_normal(D) * rng.uniform(0.001, 40.0, D // 64).repeat(64)).astype(np.float16)
+        if trial % 10 == 0:
+            x[64:128] = 0
+        rec = oracle.append.host_row_i4(x)
+        c = oracle.unpack_int4(rec[:D // 2]).astype(np.float64)
+        g = rec[D // 2:].view(np.float16).astype(np.float64)
+        xf = x.astype(np.float64)
+        for gi in range(D // 64):
+            xs, cs, gs = xf[64 * gi:64 * gi + 64], c[64 * gi:64 * gi + 64], g[gi]
+            amax = np.abs(xs).max()
+            if amax == 0:
+                assert gs == 0 and not cs.any()
+                continue
+            assert abs(gs - amax / 7) <= amax / 7 * 2.0 ** -11 * 1.0001   # one fp16 rounding
+            assert np.abs(cs).max() <= 7 and np.abs(cs[np.argmax(np.abs(xs))]) == 7
+            assert np.all(np.abs(xs - gs * cs) <= gs / 2 * (1 + 1e-6))
+        r8, sp = oracle.host_row_dequant(rec, D)
+        gmax = g.max()
+        if gmax > 0:
+            recon = r8.astype(np.float64) * float(sp)
+            assert np.all(np.abs(xf - recon) <= g.repeat(64) / 2 + float(sp) / 2 + 1e-9 + gmax * 2.0 ** -9)
+
+
+def test_tier_append_token_layout():
+    """Five appends on a toy tier (S=2, L=3, one KV head, D=64): the sinks stay,
+    the tail holds the last three appended int8 rows in position order, and
+    only the appended positions' records are written."""
+    rng = np.random.default_rng(32)
+    S, L, H, D, cap, T0 = 2, 3, 1, 64, 20, 10
+    rb = D // 2 + 2 * (D // 64)
+    rec = np.zeros((cap, H, 2 * rb), dtype=np.uint8)
+    res_k = np.arange((S + L) * H * D, dtype=np.int64).reshape(S + L, H, D).astype(np.int8)
+    res_v = -res_k
+    res_ks = np.arange(S + L, dtype=np.float16).reshape(S + L, 1) + np.float16(1)
+    res_vs = res_ks * np.float16(2)
+    sinks = (res_k[:S].copy(), res_v[:S].copy(), res_ks[:S].copy(), res_vs[:S].copy())
+    T = T0
+    news = []
+    for _ in range(5):
+        k16 = rng.standard_normal((H, D)).astype(np.float16)
+        v16 = rng.standard_normal((H, D)).astype(np.float16)
+        T = oracle.append.tier_append_token(T, rec, res_k, res_v, res_ks, res_vs, S, L, k16, v16)
+        news.append((k16, v16))
+    assert T == T0 + 5
+    for a, b in zip((res_k[:S], res_v[:S], res_ks[:S], res_vs[:S]), sinks):
+        assert np.array_equal(a, b)
+    for i, (k16, v16) in enumerate(news[-L:]):
+        kq, ks = oracle.append.row_i8(k16)
+        vq, vs = oracle.append.row_i8(v16)
+        assert np.array_equal(res_k[S + i], kq) and np.array_equal(res_ks[S + i], ks)
+        assert np.array_equal(res_v[S + i], vq) and np.array_equal(res_vs[S + i], vs)
+    for p in range(cap):
+        if T0 <= p < T:
+            k16, v16 = news[p - T0]
+            want = np.concatenate([oracle.append.host_row_i4(k16[0]), oracle.append.host_row_i4(v16[0])])
+            assert np.array_equal(rec[p, 0], want)
+        else:
+            assert not rec[p].any()
