@@ -47,7 +47,8 @@
 extern "C" {
 #endif
 
-#define SPARSEKV_ABI_VERSION 3   /* 3: multi-query step, prefill over host K/V, tier policy field */
+#define SPARSEKV_ABI_VERSION 4   /* 3: multi-query step, prefill over host K/V, tier policy field;
+                                    4: tier append (host records sized by max_ctx, tail ring) */
 
 typedef int32_t skv_status;
 enum {
@@ -361,7 +362,7 @@ skv_status sparsekv_check(void* ws, size_t ws_bytes, void* stream, uint32_t* fla
  * the dominant kernel of a call: the streaming score-and-collect kernel (the
  * one that reads the whole index in sparsekv_score_topk, sparsekv_step,
  * sparsekv_step_multi), the host-record fetch of sparsekv_tier_resolve and the
- * kernel of sparsekv_append.  Up to 4096 launches are recorded.  Enabling again
+ * kernel of sparsekv_append and sparsekv_tier_append.  Up to 4096 launches are recorded.  Enabling again
  * discards earlier records.  sparsekv_timer_read synchronizes on the recorded
  * events and returns the summed kernel time (ms) and the number of launches. */
 #define SKV_TIMER_STREAM 1
@@ -380,14 +381,20 @@ skv_status sparsekv_timer_read(double* total_ms, int64_t* launches);
  *
  * Host record of token t, KV head h (record bytes = 2 * (D/2 + 2*D/64)):
  *   K: D/2 bytes of int4 codes (low nibble first) then D/64 fp16 group scales,
- *   V: the same; records are [B][ctx][H_kv][record] token-major.
+ *   V: the same; records are [B][max_ctx][H_kv][record] token-major (the
+ *   layer's max_ctx is the tier's capacity; the caller fills positions
+ *   [0, ctx), sparsekv_tier_append writes the later ones).
  * Fetch turns a row into int8 with one fp16 scale s' = fp16(gmax*7/127),
  * gmax the largest group scale, and r8 = clamp(rint(c*g / s'), +-127), each
  * operation one fp32 IEEE operation (c*g and gmax*7 are exact).
  *
  * Resident rows per sequence (an skv_kv_view, int8 + fp16 row scales):
- *   [0, S) sinks, [S, S+L) tail (position T-L+i), [S+L, S+L+n_slots) hot slots.
- * The caller loads sinks and tail once with sparsekv_tier_load_resident.
+ *   [0, S) sinks, [S, S+L) tail, [S+L, S+L+n_slots) hot slots.  The tail is a
+ *   ring anchored at the creation context ctx0 = desc.ctx: tail position p
+ *   sits in row S + ((p - ctx0) mod L), so at creation row S+i holds position
+ *   ctx0-L+i.  The caller loads sinks and tail once, before any append, with
+ *   sparsekv_tier_load_resident.  Each sequence's context T starts at ctx0 and
+ *   is kept on the device; sparsekv_tier_append advances it.
  *
  * Windowed CLOCK, per sequence and step s: picked tokens already in the hot
  * buffer are hits (ref=1, last=s); the misses, in ascending position order,
@@ -410,7 +417,7 @@ enum { SKV_TIER_CLOCK = 0, SKV_TIER_LRU = 1 };
 typedef struct {
   uint32_t struct_size;   /* sizeof(skv_tier_desc) */
   skv_layer_desc layer;   /* token mode, SKV_KV_I8_ROWSCALE */
-  int32_t ctx;            /* tokens stored per sequence (T) */
+  int32_t ctx;            /* tokens per sequence at creation (ctx0 <= layer.max_ctx) */
   int32_t n_slots;        /* hot slots per sequence; must exceed topk */
   int32_t window;         /* W >= 1 */
   void* host_records;     /* NULL: the library allocates pinned, device-mapped
@@ -446,6 +453,25 @@ skv_status sparsekv_tier_load_resident(skv_tier* t, const int8_t* k, const int8_
  * caller then runs sparsekv_attend on the resident view with rows, n_sel. */
 skv_status sparsekv_tier_resolve(skv_tier* t, const int32_t* idx, const int32_t* n_sel,
                                  int32_t step, int32_t* rows, void* stream);
+/* Decode-step append for a tier (page "8 agents x 250K ...", section "The
+ * mechanism": every token's K/V also goes to host RAM as int4 in 64-dim groups;
+ * the GPU keeps the sinks and the recent tail).  For every sequence b the new
+ * token goes to position T = ctx_len[b], which must equal the tier's context
+ * of b: its host record (group scale g = fp16(fp32(amax/7)), codes
+ * clamp(rint(x/g), +-7), K row then V row, as above) is written into host
+ * memory through its device address; its int8 rows + fp16 row scales (the
+ * rule of sparsekv_append) replace tail position T-L in ring row
+ * S + ((T - ctx0) mod L) (none when L = 0); its key sketch is written to
+ * index_keys / index_scale row T as by sparsekv_append; then T and ctx_len[b]
+ * become T+1.  k_new, v_new: fp16 [B][H_kv][D]; basis fp32 [H_kv][D][R];
+ * index_keys [B][max_ctx][H_kv*R/2], index_scale fp16 [B][max_ctx]; ctx_len
+ * int32 [B] device, in/out.  A sequence at capacity (T >= max_ctx) or whose
+ * ctx_len differs from the tier's context is left unchanged and flagged
+ * (SKV_FLAG_CTX_RANGE / SKV_FLAG_TIER_INPUT, reported by sparsekv_tier_stats).
+ * Enqueued on stream; calls on one tier must not overlap. */
+skv_status sparsekv_tier_append(skv_tier* t, int32_t* ctx_len, const void* k_new,
+                                const void* v_new, const float* basis, void* index_keys,
+                                uint16_t* index_scale, void* stream);
 /* Synchronizes `stream` and returns cumulative counters (host struct). */
 skv_status sparsekv_tier_stats(skv_tier* t, skv_tier_stats* out, void* stream);
 /* Synchronizes `stream` and copies the slot table to the host:

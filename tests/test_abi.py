@@ -62,7 +62,7 @@ def test_struct_sizes_match_header(skv):
     # the C structs are plain int32 / pointer layouts; sizes pinned here
     assert ctypes.sizeof(skv.LayerDesc) == 15 * 4
     assert ctypes.sizeof(skv.KVView) == 5 * 8
-    assert skv.abi_version() == 3
+    assert skv.abi_version() == 4
 
 
 def test_capacity_and_workspace(skv):
@@ -209,3 +209,12 @@ def test_tier_policy_checks(skv):
     td = skv.TierDesc(ctypes.sizeof(skv.TierDesc) - 8, layer, 10_000, 60, 1, None, skv.SKV_TIER_LRU)
     # read as CLOCK: 60 slots do not exceed window * topk = 64
     assert lib.sparsekv_tier_create(ctypes.byref(td), ctypes.byref(h)) == 1
+
+
+def test_tier_append_null_checks(skv):
+    """sparsekv_tier_append rejects a NULL tier or buffer before enqueueing anything."""
+    lib = skv.lib()
+    dummy = ctypes.c_void_p(0x1000)
+    assert lib.sparsekv_tier_append(None, dummy, dummy, dummy, dummy, dummy, dummy, None) == 1
+    assert lib.sparsekv_tier_append(dummy, None, dummy, dummy, dummy, dummy, dummy, None) == 1
+    assert lib.sparsekv_tier_append(dummy, dummy, dummy, dummy, None, dummy, dummy, None) == 1

@@ -260,13 +260,23 @@ class Tier:
         self.record_bytes = 2 * (D // 2 + 2 * (D // 64))
 
     def host_records(self):
-        """numpy uint8 view [B][ctx][H_kv][record] of the pinned host records."""
+        """numpy uint8 view [B][max_ctx][H_kv][record] of the pinned host
+        records (the caller fills positions below the creation context)."""
         import numpy as np
         ptr = lib().sparsekv_tier_host_records(self._h)
-        n = self.layer.batch * self.ctx * self.layer.n_kv_heads * self.record_bytes
+        cap = self.layer.max_ctx
+        n = self.layer.batch * cap * self.layer.n_kv_heads * self.record_bytes
         buf = (ctypes.c_uint8 * n).from_address(ptr)
         return np.frombuffer(buf, dtype=np.uint8).reshape(
-            self.layer.batch, self.ctx, self.layer.n_kv_heads, self.record_bytes)
+            self.layer.batch, cap, self.layer.n_kv_heads, self.record_bytes)
+
+    def append(self, ctx_len, k_new, v_new, basis, index_keys, index_scale, stream=None):
+        """sparsekv_tier_append: the new token of every sequence (fp16 k_new,
+        v_new [B][H_kv][D]) into the host records, the tail ring and the key
+        sketch; ctx_len (device int32 [B]) must equal the tier's context."""
+        _dev(ctx_len, k_new, v_new, basis, index_keys, index_scale)
+        _check(lib().sparsekv_tier_append(self._h, _p(ctx_len), _p(k_new), _p(v_new), _p(basis),
+                                          _p(index_keys), _p(index_scale), _stream(stream)))
 
     def resident(self) -> KVView:
         v = KVView()

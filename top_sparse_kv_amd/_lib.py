@@ -89,6 +89,7 @@ SIGNATURES = [
     ("sparsekv_tier_resident", c_i32, [c_vp, P(KVView)]),
     ("sparsekv_tier_load_resident", c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     ("sparsekv_tier_resolve", c_i32, [c_vp, c_vp, c_vp, c_i32, c_vp, c_vp]),
+    ("sparsekv_tier_append", c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     ("sparsekv_tier_stats", c_i32, [c_vp, P(TierStats), c_vp]),
     ("sparsekv_tier_slots", c_i32, [c_vp, c_vp, c_vp]),
     ("sparsekv_tier_reset", c_i32, [c_vp, c_vp]),

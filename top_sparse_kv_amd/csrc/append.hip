@@ -24,6 +24,16 @@
 // One workgroup of 512 threads per sequence: the 2*H_kv rows go to the waves
 // (a row's amax by a DPP max over the wave), then thread i computes sketch
 // value i from the K rows staged in LDS.
+//
+// Host tier (same page, same section: every token's K/V also lives in host RAM
+// as int4 in 64-dim groups with fp16 group scales; the GPU keeps sinks and
+// tail): the same kernel then also writes the token's host record (group
+// scale fp16(fp32(amax / 7)), codes clamp(rint(x / g), +-7), the D/2 code
+// bytes then the D/64 scales, K row then V row) through the device address of
+// the mapped host memory, and writes the int8 rows into the tail ring of the
+// resident rows (position p at row S + ((p - anchor) mod L)) instead of row p
+// of a full cache.  The tier's own per-sequence context must equal ctx_len;
+// both advance together.
 #include "keys_common.h"
 
 #include <hip/hip_ext.h>
@@ -36,15 +46,17 @@ constexpr int kAppMaxHkv = 32;   // H_kv * R <= 512 with R >= 16
 
 __device__ __forceinline__ float quot_rn(float a, float c) { return (float)((double)a / (double)c); }
 
+
 template <int D, bool I8>
 __global__ __launch_bounds__(kAppThreads) void append_kernel(
     int32_t* __restrict__ ctx_len, const __half* __restrict__ k_new, const __half* __restrict__ v_new,
     const float* __restrict__ basis, uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
     uint16_t* __restrict__ ksc, uint16_t* __restrict__ vsc, int64_t rows,
     uint8_t* __restrict__ codes, uint16_t* __restrict__ sk_scale, int Hkv, int R, int max_ctx,
-    uint32_t* __restrict__ flags) {
+    uint32_t* __restrict__ flags, AppendTarget tg) {
 #pragma clang fp contract(off)
   constexpr int PL = D / 64;   // row values per lane
+  constexpr int HROW = D / 2 + 2 * (D / 64);   // host bytes of one K (or V) row
   __shared__ float s_k[kAppMaxHkv * D];
   __shared__ int8_t s_c[kAppThreads];
   __shared__ uint32_t s_red[16];
@@ -54,6 +66,19 @@ __global__ __launch_bounds__(kAppThreads) void append_kernel(
   if (t < 0 || t >= max_ctx) {   // the same t in every thread: the whole workgroup leaves
     if (threadIdx.x == 0) raise_flag(flags, SKV_FLAG_CTX_RANGE);
     return;
+  }
+  if (tg.tier_ctx && tg.tier_ctx[b] != t) {   // the tier and the caller disagree
+    if (threadIdx.x == 0) raise_flag(flags, SKV_FLAG_TIER_INPUT);
+    return;
+  }
+  // cache row of position t: row t of a full cache, a ring row of a tier's
+  // tail, or none (a tier without a tail)
+  int crow = t;
+  if (tg.ring_len == 0) {
+    crow = -1;
+  } else if (tg.ring_len > 0) {
+    int r = (t - tg.ring_anchor) % tg.ring_len;
+    crow = tg.ring_base + (r < 0 ? r + tg.ring_len : r);
   }
   // ---- K and V rows: wave w takes rows w, w + nw, ... (K rows first) ----
   for (int row = wave; row < 2 * Hkv; row += nw) {
@@ -67,7 +92,29 @@ __global__ __launch_bounds__(kAppThreads) void append_kernel(
 #pragma unroll
       for (int e = 0; e < PL; ++e) s_k[h * D + lane * PL + e] = x[e];
     }
-    const size_t rr = ((size_t)b * rows + t) * Hkv + h;   // cache row of (b, t, h)
+    if constexpr (I8 && D == 256) {
+      if (tg.host) {
+        // host record: 16 lanes per 64-dim group; lane l packs elements 4l..4l+3
+        float gm = 0.0f;
+#pragma unroll
+        for (int e = 0; e < PL; ++e) gm = fmaxf(gm, fabsf(x[e]));
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) gm = fmaxf(gm, __shfl_xor(gm, o));
+        const __half g16 = __float2half_rn(quot_rn(gm, 7.0f));
+        const float g = __half2float(g16);
+        uint32_t nib = 0;
+#pragma unroll
+        for (int e = 0; e < PL; ++e) {
+          const float c = g > 0.0f ? fminf(fmaxf(rintf(quot_rn(x[e], g)), -7.0f), 7.0f) : 0.0f;
+          nib |= ((uint32_t)(int)c & 0xFu) << (4 * e);
+        }
+        uint8_t* hr = tg.host + (((size_t)b * tg.host_ctx + t) * Hkv + h) * (2 * HROW) + (isv ? HROW : 0);
+        *reinterpret_cast<uint16_t*>(hr + 2 * lane) = (uint16_t)nib;
+        if ((lane & 15) == 0) *reinterpret_cast<uint16_t*>(hr + D / 2 + 2 * (lane >> 4)) = __half_as_ushort(g16);
+      }
+    }
+    if (crow < 0) continue;   // a tier without a tail keeps no int8 row
+    const size_t rr = ((size_t)b * rows + crow) * Hkv + h;   // cache row of (b, t, h)
     if constexpr (I8) {
       float am = 0.0f;
 #pragma unroll
@@ -124,6 +171,7 @@ __global__ __launch_bounds__(kAppThreads) void append_kernel(
   if (threadIdx.x == 0) {
     sk_scale[(size_t)b * max_ctx + t] = __half_as_ushort(s16);
     ctx_len[b] = t + 1;   // every thread read t before the barriers above
+    if (tg.tier_ctx) tg.tier_ctx[b] = t + 1;
   }
 }
 
@@ -206,6 +254,7 @@ hipError_t launch_append(const skv_layer_desc& d, int32_t* ctx_len, const void* 
   uint32_t* flags = ws_ptr<uint32_t>(ws, L.flags);
   const bool i8 = d.kv_dtype == SKV_KV_I8_ROWSCALE;
   if (d.n_kv_heads > kAppMaxHkv || d.n_kv_heads * d.rank > kAppThreads) return hipErrorInvalidValue;
+  const AppendTarget tg{nullptr, nullptr, 0, 0, -1, 0};   // a full cache: row = position
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   const bool timed = timer_next(kTimerStream, &ev0, &ev1);   // diagnostic timer (sparsekv_timer_enable)
 #define SKV_AP(DD, I8)                                                                           \
@@ -215,13 +264,13 @@ hipError_t launch_append(const skv_layer_desc& d, int32_t* ctx_len, const void* 
                             ev0, ev1, 0, ctx_len, (const __half*)k_new, (const __half*)v_new,    \
                             basis, (uint8_t*)kv.k, (uint8_t*)kv.v, (uint16_t*)kv.k_scale,        \
                             (uint16_t*)kv.v_scale, kv.rows, (uint8_t*)index_keys, index_scale,   \
-                            d.n_kv_heads, d.rank, d.max_ctx, flags);                             \
+                            d.n_kv_heads, d.rank, d.max_ctx, flags, tg);                         \
     else                                                                                         \
       hipLaunchKernelGGL((append_kernel<DD, I8>), dim3(d.batch), dim3(kAppThreads), 0, st,       \
                          ctx_len, (const __half*)k_new, (const __half*)v_new, basis,             \
                          (uint8_t*)kv.k, (uint8_t*)kv.v, (uint16_t*)kv.k_scale,                  \
                          (uint16_t*)kv.v_scale, kv.rows, (uint8_t*)index_keys, index_scale,      \
-                         d.n_kv_heads, d.rank, d.max_ctx, flags);                                \
+                         d.n_kv_heads, d.rank, d.max_ctx, flags, tg);                            \
   } while (0)
   if (d.head_dim == 256 && i8) SKV_AP(256, true);
   else if (d.head_dim == 256) SKV_AP(256, false);
@@ -229,6 +278,30 @@ hipError_t launch_append(const skv_layer_desc& d, int32_t* ctx_len, const void* 
   else if (d.head_dim == 128) SKV_AP(128, false);
   else return hipErrorInvalidValue;
 #undef SKV_AP
+  return hipGetLastError();
+}
+
+hipError_t launch_tier_append(const skv_layer_desc& d, int32_t* ctx_len, const void* k_new,
+                              const void* v_new, const float* basis, const skv_kv_view& resident,
+                              void* index_keys, uint16_t* index_scale, uint32_t* flags,
+                              const AppendTarget& tg, hipStream_t st) {
+  if (d.head_dim != 256 || d.kv_dtype != SKV_KV_I8_ROWSCALE || d.n_kv_heads > kAppMaxHkv ||
+      d.n_kv_heads * d.rank > kAppThreads || !tg.tier_ctx || !tg.host)
+    return hipErrorInvalidValue;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  const bool timed = timer_next(kTimerStream, &ev0, &ev1);   // diagnostic timer (sparsekv_timer_enable)
+  if (timed)
+    hipExtLaunchKernelGGL((append_kernel<256, true>), dim3(d.batch), dim3(kAppThreads), 0, st, ev0,
+                          ev1, 0, ctx_len, (const __half*)k_new, (const __half*)v_new, basis,
+                          (uint8_t*)resident.k, (uint8_t*)resident.v, (uint16_t*)resident.k_scale,
+                          (uint16_t*)resident.v_scale, resident.rows, (uint8_t*)index_keys,
+                          index_scale, d.n_kv_heads, d.rank, d.max_ctx, flags, tg);
+  else
+    hipLaunchKernelGGL((append_kernel<256, true>), dim3(d.batch), dim3(kAppThreads), 0, st, ctx_len,
+                       (const __half*)k_new, (const __half*)v_new, basis, (uint8_t*)resident.k,
+                       (uint8_t*)resident.v, (uint16_t*)resident.k_scale,
+                       (uint16_t*)resident.v_scale, resident.rows, (uint8_t*)index_keys,
+                       index_scale, d.n_kv_heads, d.rank, d.max_ctx, flags, tg);
   return hipGetLastError();
 }
 

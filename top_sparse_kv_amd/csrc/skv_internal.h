@@ -212,6 +212,20 @@ hipError_t launch_append_block(const skv_layer_desc& d, int32_t* ctx_len, const 
                                const void* v_new, const void* raw_new, void* stage,
                                const skv_kv_view& kv, void* index_keys, void* ws, const WsLayout& L,
                                hipStream_t st);
+// Where an append writes besides the key sketch: a full cache (ring_len < 0:
+// row = position) or a host tier's resident tail ring and host records.
+struct AppendTarget {
+  int32_t* tier_ctx;   // per-sequence context of the tier (nullptr: no tier)
+  uint8_t* host;       // device address of the host records (nullptr: none)
+  int64_t host_ctx;    // positions per sequence in the host records
+  int ring_base;       // first tail row
+  int ring_len;        // tail rows (< 0: no ring; 0: no tail)
+  int ring_anchor;     // position held by row ring_base (positions congruent mod ring_len)
+};
+hipError_t launch_tier_append(const skv_layer_desc& d, int32_t* ctx_len, const void* k_new,
+                              const void* v_new, const float* basis, const skv_kv_view& resident,
+                              void* index_keys, uint16_t* index_scale, uint32_t* flags,
+                              const AppendTarget& tg, hipStream_t st);
 hipError_t launch_append(const skv_layer_desc& d, int32_t* ctx_len, const void* k_new,
                          const void* v_new, const float* basis, const skv_kv_view& kv,
                          void* index_keys, uint16_t* index_scale, void* ws, const WsLayout& L,

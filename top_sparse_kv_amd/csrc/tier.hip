@@ -44,12 +44,15 @@
 
 #include <algorithm>
 #include <new>
+#include <vector>
 #include <stddef.h>
 #include <string.h>
 
 struct skv_tier {
   skv_tier_desc desc;
-  int B, T, S, L, k, Hkv, D, n_slots, W, cap, policy;
+  int B, S, L, k, Hkv, D, n_slots, W, cap, policy;
+  int T0;             // context at creation: the tail ring's anchor
+  int cap_ctx;        // positions per sequence the tier can hold (layer max_ctx)
   int rec_bytes;      // per token-head: K row + V row
   int row_bytes;      // one K (or V) host row
   void* host;         // host records (host address)
@@ -64,7 +67,9 @@ struct skv_tier {
   int32_t* slot_last;    // [B][n_slots]
   int32_t* slot_ref;     // [B][n_slots]
   int32_t* hand;         // [B]
-  int32_t* slot_of_pos;  // [B][T]
+  int32_t* slot_of_pos;  // [B][cap_ctx]
+  int32_t* ctx_dev;      // [B] context of each sequence (advanced by sparsekv_tier_append)
+  int64_t appends;       // sparsekv_tier_append calls
   int32_t* miss_pos;     // [B][k]
   int32_t* miss_slot;    // [B][k]
   int32_t* miss_count;   // [B]
@@ -82,7 +87,7 @@ constexpr int kNoStep = -(1 << 30);
 
 __global__ void tier_reset_kernel(int32_t* slot_pos, int32_t* slot_last, int32_t* slot_ref,
                                   int32_t* hand, int32_t* slot_of_pos, unsigned long long* counters,
-                                  int B, int n_slots, int T) {
+                                  int B, int n_slots, int cap_ctx) {
   const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t nth = (size_t)gridDim.x * blockDim.x;
   for (size_t i = tid; i < (size_t)B * n_slots; i += nth) {
@@ -90,7 +95,7 @@ __global__ void tier_reset_kernel(int32_t* slot_pos, int32_t* slot_last, int32_t
     slot_last[i] = kNoStep;
     slot_ref[i] = 0;
   }
-  for (size_t i = tid; i < (size_t)B * T; i += nth) slot_of_pos[i] = -1;
+  for (size_t i = tid; i < (size_t)B * cap_ctx; i += nth) slot_of_pos[i] = -1;
   for (size_t i = tid; i < (size_t)B; i += nth) hand[i] = 0;
   if (tid < 3) counters[tid] = 0ull;
 }
@@ -101,7 +106,8 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
     int32_t* __restrict__ slot_pos, int32_t* __restrict__ slot_last, int32_t* __restrict__ slot_ref,
     int32_t* __restrict__ hand_arr, int32_t* __restrict__ slot_of_pos,
     int32_t* __restrict__ miss_pos, int32_t* __restrict__ miss_slot, int32_t* __restrict__ miss_count,
-    unsigned long long* __restrict__ counters, uint32_t* __restrict__ flags, int T, int S, int L,
+    unsigned long long* __restrict__ counters, uint32_t* __restrict__ flags,
+    const int32_t* __restrict__ tier_ctx, int T0, int cap_ctx, int S, int L,
     int k, int n_slots, int W, int cap, int step) {
   __shared__ int32_t s_pos[kMaxSlots];
   __shared__ int32_t s_last[kMaxSlots];
@@ -115,7 +121,8 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
   int32_t* sp = slot_pos + (size_t)b * n_slots;
   int32_t* sl = slot_last + (size_t)b * n_slots;
   int32_t* sr = slot_ref + (size_t)b * n_slots;
-  int32_t* sop = slot_of_pos + (size_t)b * T;
+  int32_t* sop = slot_of_pos + (size_t)b * cap_ctx;
+  const int T = tier_ctx[b];   // this sequence's context (sinks, middle, tail ring)
   for (int i = threadIdx.x; i < n_slots; i += blockDim.x) {
     s_pos[i] = sp[i];
     s_last[i] = sl[i];
@@ -152,7 +159,8 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
       } else if (p < S) {
         rb[i] = p;
       } else if (p >= T - L) {
-        rb[i] = S + (p - (T - L));
+        const int r = (p - T0) % L;   // tail ring anchored at the creation context
+        rb[i] = S + (r < 0 ? r + L : r);
       } else {
         mid = true;
         const int s = sop[p];
@@ -420,7 +428,7 @@ __global__ __launch_bounds__(256) void tier_fetch_kernel(
     const uint8_t* __restrict__ host, const int32_t* __restrict__ miss_pos,
     const int32_t* __restrict__ miss_slot, const int32_t* __restrict__ miss_count,
     int8_t* __restrict__ res_k, int8_t* __restrict__ res_v, uint16_t* __restrict__ res_ks,
-    uint16_t* __restrict__ res_vs, int T, int Hkv, int k, int64_t res_rows, int res_off) {
+    uint16_t* __restrict__ res_vs, int64_t host_ctx, int Hkv, int k, int64_t res_rows, int res_off) {
   constexpr int D = 256;
   constexpr int ROWB = D / 2 + 2 * (D / 64);   // 136
   const int b = blockIdx.y;
@@ -432,7 +440,7 @@ __global__ __launch_bounds__(256) void tier_fetch_kernel(
     const int mi = task / Hkv, h = task % Hkv;
     const int p = miss_pos[(size_t)b * k + mi];
     const int slot = miss_slot[(size_t)b * k + mi];
-    const uint8_t* row = host + (((size_t)b * T + p) * Hkv + h) * (2 * ROWB) + half * ROWB;
+    const uint8_t* row = host + (((size_t)b * host_ctx + p) * Hkv + h) * (2 * ROWB) + half * ROWB;
     const uint32_t codes = *reinterpret_cast<const uint32_t*>(row + 4 * ln);
     const uint2 sc = *reinterpret_cast<const uint2*>(row + D / 2);
     const float g0 = half_bits_to_float((uint16_t)(sc.x & 0xFFFF));
@@ -479,8 +487,8 @@ using skv::set_error;
 static void tier_free(skv_tier* t) {
   if (!t) return;
   void* dev[] = {t->res_k, t->res_v, t->res_ks, t->res_vs, t->slot_pos, t->slot_last, t->slot_ref,
-                 t->hand, t->slot_of_pos, t->miss_pos, t->miss_slot, t->miss_count, t->counters,
-                 t->flags};
+                 t->hand, t->slot_of_pos, t->ctx_dev, t->miss_pos, t->miss_slot, t->miss_count,
+                 t->counters, t->flags};
   for (void* p : dev)
     if (p) (void)hipFree(p);
   if (t->own_host && t->host) (void)hipHostFree(t->host);
@@ -518,13 +526,13 @@ extern "C" skv_status sparsekv_tier_create(const skv_tier_desc* d, skv_tier** ou
   memset(t, 0, sizeof(*t));
   memcpy(&t->desc, d, std::min<size_t>(d->struct_size, sizeof(skv_tier_desc)));
   t->policy = policy;
-  t->B = L.batch; t->T = d->ctx; t->S = L.n_sink; t->L = L.n_tail; t->k = L.topk;
+  t->B = L.batch; t->T0 = d->ctx; t->cap_ctx = L.max_ctx; t->S = L.n_sink; t->L = L.n_tail; t->k = L.topk;
   t->Hkv = L.n_kv_heads; t->D = L.head_dim; t->n_slots = d->n_slots; t->W = d->window;
   t->cap = skv::select_capacity(L);
   t->row_bytes = t->D / 2 + 2 * (t->D / 64);
   t->rec_bytes = 2 * t->row_bytes;
   t->res_rows = (int64_t)t->S + t->L + t->n_slots;
-  const size_t host_bytes = (size_t)t->B * t->T * t->Hkv * t->rec_bytes;
+  const size_t host_bytes = (size_t)t->B * t->cap_ctx * t->Hkv * t->rec_bytes;
   if (d->host_records) {
     t->host = d->host_records;
     t->own_host = false;
@@ -554,7 +562,8 @@ extern "C" skv_status sparsekv_tier_create(const skv_tier_desc* d, skv_tier** ou
             hipMalloc(&t->slot_last, ns * 4) == hipSuccess &&
             hipMalloc(&t->slot_ref, ns * 4) == hipSuccess &&
             hipMalloc(&t->hand, (size_t)t->B * 4) == hipSuccess &&
-            hipMalloc(&t->slot_of_pos, (size_t)t->B * t->T * 4) == hipSuccess &&
+            hipMalloc(&t->slot_of_pos, (size_t)t->B * t->cap_ctx * 4) == hipSuccess &&
+            hipMalloc(&t->ctx_dev, (size_t)t->B * 4) == hipSuccess &&
             hipMalloc(&t->miss_pos, (size_t)t->B * t->k * 4) == hipSuccess &&
             hipMalloc(&t->miss_slot, (size_t)t->B * t->k * 4) == hipSuccess &&
             hipMalloc(&t->miss_count, (size_t)t->B * 4) == hipSuccess &&
@@ -571,8 +580,15 @@ extern "C" skv_status sparsekv_tier_create(const skv_tier_desc* d, skv_tier** ou
     tier_free(t);
     return set_error(SKV_ERR_HIP, "tier: initial clear failed");
   }
+  {
+    std::vector<int32_t> c0((size_t)t->B, t->T0);
+    if (hipMemcpy(t->ctx_dev, c0.data(), c0.size() * 4, hipMemcpyHostToDevice) != hipSuccess) {
+      tier_free(t);
+      return set_error(SKV_ERR_HIP, "tier: context upload failed");
+    }
+  }
   hipLaunchKernelGGL(skv::tier_reset_kernel, dim3(256), dim3(256), 0, 0, t->slot_pos, t->slot_last,
-                     t->slot_ref, t->hand, t->slot_of_pos, t->counters, t->B, t->n_slots, t->T);
+                     t->slot_ref, t->hand, t->slot_of_pos, t->counters, t->B, t->n_slots, t->cap_ctx);
   if (hipGetLastError() != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
     tier_free(t);
     return set_error(SKV_ERR_HIP, "tier: reset kernel failed");
@@ -597,6 +613,8 @@ extern "C" skv_status sparsekv_tier_load_resident(skv_tier* t, const int8_t* k, 
                                                   const uint16_t* ks, const uint16_t* vs,
                                                   void* stream) {
   if (!t || !k || !v || !ks || !vs) return set_error(SKV_ERR_INVALID, "tier_load_resident: NULL argument");
+  if (t->appends)
+    return set_error(SKV_ERR_STATE, "tier_load_resident: the tier has appended tokens (load the creation context only)");
   hipStream_t st = (hipStream_t)stream;
   const size_t nres = (size_t)(t->S + t->L);
   if (nres == 0) return SKV_OK;
@@ -622,24 +640,44 @@ extern "C" skv_status sparsekv_tier_resolve(skv_tier* t, const int32_t* idx, con
     hipLaunchKernelGGL(skv::tier_resolve_kernel<SKV_TIER_LRU>, dim3(t->B), dim3(skv::kResolveThreads), 0,
                        st, idx, n_sel, rows, t->slot_pos, t->slot_last, t->slot_ref, t->hand,
                        t->slot_of_pos, t->miss_pos, t->miss_slot, t->miss_count, t->counters, t->flags,
-                       t->T, t->S, t->L, t->k, t->n_slots, t->W, t->cap, step);
+                       t->ctx_dev, t->T0, t->cap_ctx, t->S, t->L, t->k, t->n_slots, t->W, t->cap, step);
   else
     hipLaunchKernelGGL(skv::tier_resolve_kernel<SKV_TIER_CLOCK>, dim3(t->B), dim3(skv::kResolveThreads),
                        0, st, idx, n_sel, rows, t->slot_pos, t->slot_last, t->slot_ref, t->hand,
                        t->slot_of_pos, t->miss_pos, t->miss_slot, t->miss_count, t->counters, t->flags,
-                       t->T, t->S, t->L, t->k, t->n_slots, t->W, t->cap, step);
+                       t->ctx_dev, t->T0, t->cap_ctx, t->S, t->L, t->k, t->n_slots, t->W, t->cap, step);
   if (hipGetLastError() != hipSuccess) return set_error(SKV_ERR_HIP, "tier_resolve: launch failed");
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   if (skv::timer_next(skv::kTimerStream, &ev0, &ev1))   // diagnostic timer (sparsekv_timer_enable)
     hipExtLaunchKernelGGL(skv::tier_fetch_kernel, dim3(128, t->B), dim3(256), 0, st, ev0, ev1, 0,
                           t->host_dev, t->miss_pos, t->miss_slot, t->miss_count, t->res_k, t->res_v,
-                          t->res_ks, t->res_vs, t->T, t->Hkv, t->k, t->res_rows, t->S + t->L);
+                          t->res_ks, t->res_vs, (int64_t)t->cap_ctx, t->Hkv, t->k, t->res_rows, t->S + t->L);
   else
     hipLaunchKernelGGL(skv::tier_fetch_kernel, dim3(128, t->B), dim3(256), 0, st, t->host_dev,
                        t->miss_pos, t->miss_slot, t->miss_count, t->res_k, t->res_v, t->res_ks,
-                       t->res_vs, t->T, t->Hkv, t->k, t->res_rows, t->S + t->L);
+                       t->res_vs, (int64_t)t->cap_ctx, t->Hkv, t->k, t->res_rows, t->S + t->L);
   if (hipGetLastError() != hipSuccess) return set_error(SKV_ERR_HIP, "tier_fetch: launch failed");
   t->steps += 1;
+  return SKV_OK;
+}
+
+extern "C" skv_status sparsekv_tier_append(skv_tier* t, int32_t* ctx_len, const void* k_new,
+                                           const void* v_new, const float* basis, void* index_keys,
+                                           uint16_t* index_scale, void* stream) {
+  if (!t || !ctx_len || !k_new || !v_new || !basis || !index_keys || !index_scale)
+    return set_error(SKV_ERR_INVALID, "tier_append: NULL argument");
+  const skv::AppendTarget tg{t->ctx_dev, const_cast<uint8_t*>(t->host_dev), (int64_t)t->cap_ctx, t->S,
+                             t->L, t->T0};
+  skv_kv_view res;
+  res.k = t->res_k;
+  res.v = t->res_v;
+  res.k_scale = t->res_ks;
+  res.v_scale = t->res_vs;
+  res.rows = t->res_rows;
+  if (skv::launch_tier_append(t->desc.layer, ctx_len, k_new, v_new, basis, res, index_keys,
+                              index_scale, t->flags, tg, (hipStream_t)stream) != hipSuccess)
+    return set_error(SKV_ERR_HIP, "tier_append: launch failed");
+  t->appends += 1;
   return SKV_OK;
 }
 
@@ -656,7 +694,7 @@ extern "C" skv_status sparsekv_tier_stats(skv_tier* t, skv_tier_stats* out, void
   out->hits = (int64_t)c[1];
   out->misses = (int64_t)c[2];
   out->host_bytes = (int64_t)c[2] * t->Hkv * t->rec_bytes;
-  if (fl) return set_error(SKV_ERR_STATE, "tier: device flags 0x%x (invalid selection input)", fl);
+  if (fl) return set_error(SKV_ERR_STATE, "tier: device flags 0x%x (invalid selection or append input)", fl);
   return SKV_OK;
 }
 
@@ -672,7 +710,7 @@ extern "C" skv_status sparsekv_tier_reset(skv_tier* t, void* stream) {
   if (!t) return set_error(SKV_ERR_INVALID, "tier_reset: NULL argument");
   hipLaunchKernelGGL(skv::tier_reset_kernel, dim3(256), dim3(256), 0, (hipStream_t)stream,
                      t->slot_pos, t->slot_last, t->slot_ref, t->hand, t->slot_of_pos, t->counters,
-                     t->B, t->n_slots, t->T);
+                     t->B, t->n_slots, t->cap_ctx);
   if (hipGetLastError() != hipSuccess) return set_error(SKV_ERR_HIP, "tier_reset: launch failed");
   t->steps = 0;
   return SKV_OK;
