@@ -77,6 +77,11 @@ CONFIGS = {
                   kv="i8", layers=1, seed=1002,
                   workload="decode-step append for 8 seq x 250,000 tokens (cfg2 layer shape): the "
                            "new token's int8 K/V rows + scales and its int4 key sketch"),
+    "cfg5a": dict(kind="tier_append", B=4, T=250_000, n_kv=4, n_q=24, D=256, S=64, k=2048, L=1024,
+                  kv="i8", layers=1, seed=1005,
+                  workload="decode-step append for the host tier, 4 seq x 250,000 tokens (cfg5 "
+                           "shape): the new token's int4 host record written zero-copy, its int8 "
+                           "rows into the tail ring, its int4 key sketch"),
     "cfg5": dict(kind="tier", B=4, T=250_000, n_kv=4, n_q=24, D=256, S=64, k=2048, L=1024,
                  kv="i8", layers=1, seed=1005, warm_steps=64, steps=256,
                  workload="4 seq x 250,000 tokens; cfg2 layer shape; int4 host-RAM K/V records read "
@@ -438,6 +443,93 @@ def bench_append(cfg, args):
     print(json.dumps(res), flush=True)
 
 
+def bench_tier_append(cfg, args):
+    """The decode-step append of the host tier alone: every sequence's new
+    token goes into its host record (zero-copy), the tail ring and the key
+    sketch; timed by the kernel's own dispatches and by the host clock."""
+    B, T, H, D, S, L, k = cfg["B"], cfg["T"], cfg["n_kv"], cfg["D"], cfg["S"], cfg["k"], cfg["L"]
+    R = 64
+    n_calls = max(5, args.warmup) + 2 * args.steps
+    cap = T + n_calls
+    log("generating the host-tier case")
+    c = synth.make_tier_case(B, T, n_kv=H, n_q=cfg["n_q"], D=D, S=S, k=k, L=L, seed=cfg["seed"],
+                             device="cuda")
+    desc = skv.token_desc(B, cap, H, cfg["n_q"], D, topk=k, n_sink=S, n_tail=L)
+    tier = skv.Tier(desc, T, c.n_slots, 1)
+    try:
+        tier.host_records()[:, :T] = c.records.cpu().numpy()
+        tier.load_resident(c.res_k, c.res_v, c.res_ks, c.res_vs)
+        basis = synth.orthonormal_basis(H, D, R, cfg["seed"]).cuda()
+        codes = torch.zeros((B, cap, H * R // 2), dtype=torch.uint8, device="cuda")
+        sksc = torch.zeros((B, cap), dtype=torch.float16, device="cuda")
+        ctx = torch.full((B,), T, dtype=torch.int32, device="cuda")
+        g = torch.Generator(device="cuda").manual_seed(7)
+        k_new = torch.randn((B, H, D), generator=g, device="cuda").to(torch.float16)
+        v_new = torch.randn((B, H, D), generator=g, device="cuda").to(torch.float16)
+
+        def call(_layer, _ws):
+            tier.append(ctx, k_new, v_new, basis, codes, sksc)
+        for _ in range(max(5, args.warmup)):
+            call(None, None)
+        secs = time_loop(call, [None], None, args.steps)
+        skv.timer_enable(True)
+        time_loop(call, [None], None, args.steps)
+        a_ms, a_n = skv.timer_read()
+        skv.timer_enable(False)
+        tier.stats()                              # raises on any tier flag
+        assert int(ctx[0].item()) == T + n_calls
+    finally:
+        tier.close()
+    rec = 2 * (D // 2 + 2 * (D // 64))
+    host_bytes = B * H * rec
+    # what one call must move: the new rows (fp16) and the basis in; int8 rows,
+    # row scales, sketch codes and scale to the GPU, the records to host memory
+    dev_bytes = B * H * D * 2 * 2 + H * D * R * 4 + B * (H * D * 2 + H * 2 * 2 + H * R // 2 + 2) + B * 8
+    a_s = a_ms / 1e3 / max(1, a_n)
+    res = {
+        "metric": METRIC + " (tier append: calls/s)", "value": round(args.steps / secs, 2),
+        "unit": "appends/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(1e3 * secs / args.steps, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "i8", "data": "synthetic",
+        "config": {"workload": cfg["workload"], "name": args.config, "batch": B, "ctx": T},
+        "roofline": {"kernel": "tier_append", "bound": "hbm",
+                     "achieved": round((dev_bytes + host_bytes) / a_s / 1e9, 2),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round((dev_bytes + host_bytes) / a_s / 1e9 / PEAK_HBM_GBS, 5),
+                     "traffic": None, "bytes_per_launch": dev_bytes + host_bytes,
+                     "host_bytes_per_launch": host_bytes, "avg_launch_us": round(a_s * 1e6, 2),
+                     "launches_timed": a_n,
+                     "note": "one workgroup per sequence: launch- and latency-bound"},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        import oracle
+        from threadpoolctl import threadpool_limits
+        rb = rec
+        rec_np = np.zeros((B, 64, H, rb), dtype=np.uint8)          # the rows an append writes
+        rk, rv = c.res_k.cpu().numpy(), c.res_v.cpu().numpy()
+        rks, rvs = c.res_ks.cpu().numpy(), c.res_vs.cpu().numpy()
+        kn, vn, bas = k_new.cpu().numpy(), v_new.cpu().numpy(), basis.cpu().numpy()
+        t_total, reps = 0.0, 0
+        with threadpool_limits(limits=1):
+            while reps < 5000 and (reps == 0 or t_total < 10.0):
+                t0 = time.perf_counter()
+                for b in range(B):
+                    oracle.append.key_sketch(kn[b], bas)
+                    oracle.append.tier_append_token(reps % 64, rec_np[b], rk[b], rv[b], rks[b],
+                                                    rvs[b], S, L, kn[b], vn[b])
+                t_total += time.perf_counter() - t0
+                reps += 1
+        res["cpu_baseline"] = {"value": round(reps / t_total, 3), "unit": "appends/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": "%d appends of all %d sequences (record, tail, sketch) "
+                                         "into host copies" % (reps, B),
+                               "seconds": round(t_total, 3)}
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
 def bench_prefill(cfg, args):
     """Prefill attention over host-resident K/V: one call streams the history
     once through the working buffer and attends every prefill query's picks
@@ -710,6 +802,9 @@ def main():
     cfg = CONFIGS[args.config]
     if cfg["kind"] == "prefill":
         bench_prefill(cfg, args)
+        return
+    if cfg["kind"] == "tier_append":
+        bench_tier_append(cfg, args)
         return
     if cfg["kind"] == "append":
         bench_append(cfg, args)
