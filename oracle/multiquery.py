@@ -82,3 +82,37 @@ PINS = {
         "queries give nested picks that differ by at most the one newly ranked "
         "position; a budget threshold crossed inside one step"),
 }
+
+
+# ----------------------------------------------------------------------------
+# several query tokens through the host tier
+# ----------------------------------------------------------------------------
+# [P2] section "Where the tradeoffs bite": with multi-token verification the
+# hot buffer must hold the rows of every verification token at once.
+# Reading: the M pick lists of a sequence are resolved one after another with
+# the same step number, each as a single-query step of the tier's policy
+# (oracle.ClockTier / oracle.residency.LruTier); the rows placed for an
+# earlier list are then marked used in this step, so a later list finds them
+# and cannot evict them.  Positions are classified against the tier's context
+# T (sinks below S, tail from T - L on, the middle in between), so a later
+# query's tail positions below T - L are middle rows of the tier.
+
+
+def tier_resolve_lists(tier, lists, T: int, S: int, L: int, s: int):
+    """tier: a ClockTier or LruTier of one sequence; lists: ascending position
+    lists, one per query token.  Returns (slot per middle pick of each list,
+    hits, misses), the slots in list order."""
+    out, hits, misses = [], 0, 0
+    for lst in lists:
+        p = np.asarray(lst, dtype=np.int64)
+        mid = p[(p >= S) & (p < T - L)]
+        slots, h, m = tier.step(mid, s)
+        out.append(slots)
+        hits += h
+        misses += m
+    return out, hits, misses
+
+
+PINS.update({
+    "tier_resolve_lists": "one list equals the single-query step; after the step every middle pick of every list is resident in the slot reported for it; a position shared by several lists is fetched at most once; with the hot buffer only just above the step's distinct rows nothing a list placed is evicted by a later one (a per-list step number would evict)",
+})

@@ -52,6 +52,8 @@ class LruTier:
         miss = np.nonzero(~hit)[0]
         if miss.size:
             free = np.nonzero(self.last < s)[0]                 # not used in this step
+            if free.size < miss.size:
+                raise RuntimeError("the rows used in this step exceed the hot buffer")
             order = np.lexsort((free, self.last[free]))          # oldest first, then slot order
             victims = np.sort(free[order[:miss.size]])
             for i, x in zip(miss.tolist(), victims.tolist()):

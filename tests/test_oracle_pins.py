@@ -926,3 +926,79 @@ def test_tier_append_token_layout():
             assert np.array_equal(rec[p, 0], want)
         else:
             assert not rec[p].any()
+
+
+# --------------------------------------------------------------------------
+# several query tokens through the host tier
+# --------------------------------------------------------------------------
+
+def _overlapping_lists(rng, M, T, S, L, k, shared):
+    """M ascending middle lists sharing `shared` positions of each list."""
+    base = rng.choice(np.arange(S, T - L), k, replace=False)
+    lists = []
+    for _ in range(M):
+        own = rng.choice(np.setdiff1d(np.arange(S, T - L), base), k - shared, replace=False)
+        lists.append(np.sort(np.concatenate([base[:shared], own])))
+    return lists
+
+
+@pytest.mark.parametrize("lru", [False, True])
+def test_tier_lists_single_equals_step(lru):
+    rng = np.random.default_rng(61)
+    T, S, L, k, n = 5000, 16, 32, 64, 160
+    mk = (lambda: oracle.residency.LruTier(n, T)) if lru else (lambda: oracle.ClockTier(n, T, window=1))
+    a, b = mk(), mk()
+    for s in range(12):
+        lst = np.sort(rng.choice(np.arange(S, T - L), k, replace=False))
+        sl_a, h_a, m_a = a.step(lst, s)
+        (sl_b,), h_b, m_b = oracle.multiquery.tier_resolve_lists(b, [lst], T, S, L, s)
+        assert np.array_equal(sl_a, sl_b) and (h_a, m_a) == (h_b, m_b)
+
+
+@pytest.mark.parametrize("lru", [False, True])
+def test_tier_lists_all_resident_and_fetched_once(lru):
+    """After a step that filled the hot buffer with other rows, lists sharing
+    positions: every pick of every list is resident afterwards in the slot
+    reported for it, and a shared position is fetched once."""
+    rng = np.random.default_rng(62)
+    T, S, L, k, M, shared = 20_000, 16, 32, 64, 4, 40
+    lists = _overlapping_lists(rng, M, T, S, L, k, shared)
+    distinct = np.unique(np.concatenate(lists))
+    n = distinct.size + 1
+    tier = oracle.residency.LruTier(n, T) if lru else oracle.ClockTier(n, T, window=1)
+    filler = np.sort(rng.choice(np.setdiff1d(np.arange(S, T - L), distinct), n - 1, replace=False))
+    tier.step(filler, 0)
+    slots, h, m = oracle.multiquery.tier_resolve_lists(tier, lists, T, S, L, 1)
+    assert m == distinct.size and h == sum(l.size for l in lists) - distinct.size
+    for sl, l in zip(slots, lists):
+        assert np.array_equal(tier.pos[sl], l)
+
+
+@pytest.mark.parametrize("lru", [False, True])
+def test_tier_lists_must_fit_together(lru):
+    """Each list fits the hot buffer but their union does not: resolving them
+    at one step is refused (the buffer cannot hold every query's rows at
+    once), whereas a step number per list would quietly evict rows an earlier
+    query still needs."""
+    rng = np.random.default_rng(63)
+    T, S, L, k, M, shared = 20_000, 16, 32, 64, 4, 40
+    lists = _overlapping_lists(rng, M, T, S, L, k, shared)
+    n = np.unique(np.concatenate(lists)).size - 1
+    mk = (lambda: oracle.residency.LruTier(n, T)) if lru else (lambda: oracle.ClockTier(n, T, window=1))
+    with pytest.raises(RuntimeError):
+        oracle.multiquery.tier_resolve_lists(mk(), lists, T, S, L, 0)
+    tier = mk()
+    for j, l in enumerate(lists):
+        tier.step(l, j)
+    assert not np.isin(lists[0], tier.pos).all()
+
+
+def test_tier_lists_classify_against_tier_context():
+    """A later query's tail position below T - L is a middle row of the tier."""
+    T, S, L = 1000, 4, 8
+    tier = oracle.ClockTier(20, T, window=1)
+    lists = [np.concatenate([np.arange(S), [100, 200], np.arange(T - 1 - L, T - 1)]),
+             np.concatenate([np.arange(S), [100, 300], np.arange(T - L, T)])]
+    slots, h, m = oracle.multiquery.tier_resolve_lists(tier, lists, T, S, L, 0)
+    assert [sl.size for sl in slots] == [3, 2]        # T - 1 - L is middle for the tier
+    assert (h, m) == (1, 4)
