@@ -48,7 +48,8 @@ extern "C" {
 #endif
 
 #define SPARSEKV_ABI_VERSION 4   /* 3: multi-query step, prefill over host K/V, tier policy field;
-                                    4: tier append (host records sized by max_ctx, tail ring) */
+                                    4: tier append (host records sized by max_ctx, tail ring),
+                                       multi-query tier resolve and attention */
 
 typedef int32_t skv_status;
 enum {
@@ -260,6 +261,14 @@ skv_status sparsekv_step_multi(const skv_layer_desc* d, int32_t n_query, const i
                                const void* index_keys, const uint16_t* index_scale,
                                const skv_kv_view* kv, int32_t* idx, int32_t* n_sel, float sm_scale,
                                float* out, void* ws, size_t ws_bytes, void* stream);
+/* The attention of sparsekv_step_multi alone: query token j of sequence b
+ * (q [B][n_query][H_q][D], same dtype rules as sparsekv_attend) attends the
+ * rows idx[b][j][0..n_sel[b][j]) of sequence b's K/V view; out fp32
+ * [B][n_query][H_q][D].  Workspace: sparsekv_workspace_size_multi. */
+skv_status sparsekv_attend_multi(const skv_layer_desc* d, int32_t n_query, const void* q,
+                                 const skv_kv_view* kv, const int32_t* idx, const int32_t* n_sel,
+                                 float sm_scale, float* out, void* ws, size_t ws_bytes,
+                                 void* stream);
 
 /* ---- prefill attention over K/V rows in host memory -------------------------
  * Page "3.14M Context ...", sections "What Needs to Stay in VRAM" (K and V in
@@ -453,6 +462,24 @@ skv_status sparsekv_tier_load_resident(skv_tier* t, const int8_t* k, const int8_
  * caller then runs sparsekv_attend on the resident view with rows, n_sel. */
 skv_status sparsekv_tier_resolve(skv_tier* t, const int32_t* idx, const int32_t* n_sel,
                                  int32_t step, int32_t* rows, void* stream);
+/* Several query tokens per sequence (a step verifying drafted tokens; page "8
+ * agents x 250K ...", which serves with multi-token prediction, and page
+ * "vLLM's Hybrid HiSparse ...", which notes that the hot buffer must then hold
+ * the rows of every query at once): idx [B][n_query][cap] and n_sel
+ * [B][n_query] hold one ascending pick list per query token (e.g. from
+ * sparsekv_step_multi), rows [B][n_query][cap] receives the resident row of
+ * each pick.  The lists of a sequence are resolved one after another at the
+ * same step number, each as by sparsekv_tier_resolve, so the rows an earlier
+ * list placed are used in this step: a later list finds them (hits) and
+ * cannot evict them, and every row any query needs is resident when the
+ * attention (sparsekv_attend_multi on the resident view) runs.  Positions are
+ * classified against the tier's context T: a later query's tail positions
+ * below T-L are middle rows here.  If the distinct middle rows of the step do
+ * not fit the hot buffer, the misses that find no slot get row 0 and
+ * SKV_FLAG_TIER_INPUT is raised.  1 <= n_query <= 16. */
+skv_status sparsekv_tier_resolve_multi(skv_tier* t, int32_t n_query, const int32_t* idx,
+                                       const int32_t* n_sel, int32_t step, int32_t* rows,
+                                       void* stream);
 /* Decode-step append for a tier (page "8 agents x 250K ...", section "The
  * mechanism": every token's K/V also goes to host RAM as int4 in 64-dim groups;
  * the GPU keeps the sinks and the recent tail).  For every sequence b the new

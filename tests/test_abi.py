@@ -218,3 +218,27 @@ def test_tier_append_null_checks(skv):
     assert lib.sparsekv_tier_append(None, dummy, dummy, dummy, dummy, dummy, dummy, None) == 1
     assert lib.sparsekv_tier_append(dummy, None, dummy, dummy, dummy, dummy, dummy, None) == 1
     assert lib.sparsekv_tier_append(dummy, dummy, dummy, dummy, None, dummy, dummy, None) == 1
+
+
+def test_tier_resolve_multi_and_attend_multi_checks(skv):
+    """Host-side refusals, nothing enqueued: NULL arguments, a query count
+    outside [1, 16], a workspace sized for one query token."""
+    lib = skv.lib()
+    dummy = ctypes.c_void_p(0x1000)
+    assert lib.sparsekv_tier_resolve_multi(None, 4, dummy, dummy, 0, dummy, None) == 1
+    assert lib.sparsekv_tier_resolve_multi(dummy, 4, None, dummy, 0, dummy, None) == 1
+    for m in (0, 17):
+        assert lib.sparsekv_tier_resolve_multi(dummy, m, dummy, dummy, 0, dummy, None) == 2
+    d = skv.token_desc(4, 250_000, 4, 24, 256, topk=2048, n_sink=64, n_tail=1024)
+    kv = skv.KVView(dummy, dummy, dummy, dummy, 250_000)
+    one = skv.workspace_size(d)
+    four = skv.workspace_size_multi(d, 4)
+    st = lib.sparsekv_attend_multi(ctypes.byref(d), 4, dummy, ctypes.byref(kv), dummy, dummy, 0.1,
+                                   dummy, ctypes.c_void_p(0x100000), one, None)
+    assert st == 3 and four > one
+    st = lib.sparsekv_attend_multi(ctypes.byref(d), 4, None, ctypes.byref(kv), dummy, dummy, 0.1,
+                                   dummy, ctypes.c_void_p(0x100000), four, None)
+    assert st == 1
+    st = lib.sparsekv_attend_multi(ctypes.byref(d), 0, dummy, ctypes.byref(kv), dummy, dummy, 0.1,
+                                   dummy, ctypes.c_void_p(0x100000), four, None)
+    assert st == 2

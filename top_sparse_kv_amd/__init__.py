@@ -129,6 +129,15 @@ def score_topk(desc, ctx_len, index_query, index_keys, index_scale, idx, n_sel, 
                                      ws.numel(), _stream(stream)))
 
 
+def attend_multi(desc, n_query, q, kv: KVView, idx, n_sel, sm_scale, out, ws, stream=None):
+    """sparsekv_attend_multi: q [B][n_query][H_q][D], idx [B][n_query][cap],
+    n_sel [B][n_query], out fp32 [B][n_query][H_q][D]; ws from workspace_multi."""
+    _dev(q, idx, n_sel, out, ws)
+    _check(lib().sparsekv_attend_multi(ctypes.byref(desc), int(n_query), _p(q), ctypes.byref(kv),
+                                       _p(idx), _p(n_sel), float(sm_scale), _p(out), _p(ws),
+                                       ws.numel(), _stream(stream)))
+
+
 def attend(desc, q, kv: KVView, idx, n_sel, sm_scale, out, ws, stream=None):
     _dev(q, idx, n_sel, out, ws)
     _check(lib().sparsekv_attend(ctypes.byref(desc), _p(q), ctypes.byref(kv), _p(idx), _p(n_sel),
@@ -292,6 +301,13 @@ class Tier:
         _dev(idx, n_sel, rows)
         _check(lib().sparsekv_tier_resolve(self._h, _p(idx), _p(n_sel), int(step), _p(rows),
                                            _stream(stream)))
+
+    def resolve_multi(self, n_query: int, idx, n_sel, step: int, rows, stream=None):
+        """sparsekv_tier_resolve_multi: idx [B][n_query][cap], n_sel
+        [B][n_query], rows [B][n_query][cap] (device int32)."""
+        _dev(idx, n_sel, rows)
+        _check(lib().sparsekv_tier_resolve_multi(self._h, int(n_query), _p(idx), _p(n_sel),
+                                                 int(step), _p(rows), _stream(stream)))
 
     def stats(self, stream=None) -> TierStats:
         s = TierStats()

@@ -74,6 +74,8 @@ SIGNATURES = [
     ("sparsekv_workspace_size_multi", c_i32, [P(LayerDesc), c_i32, P(c_sz)]),
     ("sparsekv_step_multi", c_i32, [P(LayerDesc), c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                     P(KVView), c_vp, c_vp, ctypes.c_float, c_vp, c_vp, c_sz, c_vp]),
+    ("sparsekv_attend_multi", c_i32, [P(LayerDesc), c_i32, c_vp, P(KVView), c_vp, c_vp,
+                                      ctypes.c_float, c_vp, c_vp, c_sz, c_vp]),
     ("sparsekv_prefill_workspace_size", c_i32, [P(LayerDesc), c_i32, P(c_sz)]),
     ("sparsekv_prefill_attend", c_i32, [P(LayerDesc), c_i32, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp,
                                         c_i64, c_vp, c_sz, ctypes.c_float, c_vp, c_vp, c_sz, c_vp]),
@@ -89,6 +91,7 @@ SIGNATURES = [
     ("sparsekv_tier_resident", c_i32, [c_vp, P(KVView)]),
     ("sparsekv_tier_load_resident", c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     ("sparsekv_tier_resolve", c_i32, [c_vp, c_vp, c_vp, c_i32, c_vp, c_vp]),
+    ("sparsekv_tier_resolve_multi", c_i32, [c_vp, c_i32, c_vp, c_vp, c_i32, c_vp, c_vp]),
     ("sparsekv_tier_append", c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     ("sparsekv_tier_stats", c_i32, [c_vp, P(TierStats), c_vp]),
     ("sparsekv_tier_slots", c_i32, [c_vp, c_vp, c_vp]),

@@ -224,6 +224,23 @@ skv_status sparsekv_step_multi(const skv_layer_desc* d, int32_t n_query, const i
   return launched(e, "step_multi");
 }
 
+skv_status sparsekv_attend_multi(const skv_layer_desc* d, int32_t n_query, const void* q,
+                                 const skv_kv_view* kv, const int32_t* idx, const int32_t* n_sel,
+                                 float sm_scale, float* out, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  skv_layer_desc dv;
+  skv_status s = multi_desc(d, n_query, &dv);
+  if (s != SKV_OK) return s;
+  WsLayout L;
+  if ((s = check_ws(&dv, ws, ws_bytes, &L)) != SKV_OK) return s;
+  if ((s = check_kv(d, kv)) != SKV_OK) return s;
+  if (!q || !idx || !n_sel || !out) return set_error(SKV_ERR_INVALID, "attend_multi: NULL pointer");
+  if (((uintptr_t)q) % 16) return set_error(SKV_ERR_INVALID, "attend_multi: q not 16-byte aligned");
+  return launched(launch_attend(dv, q, *kv, idx, n_sel, sm_scale, out, ws, L, (hipStream_t)stream,
+                                n_query),
+                  "attend_multi");
+}
+
 static skv_status prefill_desc(const skv_layer_desc* d, int32_t n_query) {
   skv_status s = validate_desc(d);
   if (s != SKV_OK) return s;

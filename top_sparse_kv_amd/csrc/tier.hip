@@ -70,8 +70,9 @@ struct skv_tier {
   int32_t* slot_of_pos;  // [B][cap_ctx]
   int32_t* ctx_dev;      // [B] context of each sequence (advanced by sparsekv_tier_append)
   int64_t appends;       // sparsekv_tier_append calls
-  int32_t* miss_pos;     // [B][k]
-  int32_t* miss_slot;    // [B][k]
+  int mstride;           // misses per sequence the arrays below hold
+  int32_t* miss_pos;     // [B][mstride]
+  int32_t* miss_slot;    // [B][mstride]
   int32_t* miss_count;   // [B]
   unsigned long long* counters;  // picks, hits, misses
   uint32_t* flags;
@@ -83,6 +84,9 @@ namespace {
 
 constexpr int kResolveThreads = 1024;
 constexpr int kMaxSlots = 12288;     // slot table held in LDS
+// misses of one pick list: its middle picks (those of a later query token of a
+// sequence include up to kMaxQueries - 1 of its tail positions)
+constexpr int kMaxListMisses = kMaxTopk + kMaxQueries;
 constexpr int kNoStep = -(1 << 30);
 
 __global__ void tier_reset_kernel(int32_t* slot_pos, int32_t* slot_last, int32_t* slot_ref,
@@ -108,14 +112,14 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
     int32_t* __restrict__ miss_pos, int32_t* __restrict__ miss_slot, int32_t* __restrict__ miss_count,
     unsigned long long* __restrict__ counters, uint32_t* __restrict__ flags,
     const int32_t* __restrict__ tier_ctx, int T0, int cap_ctx, int S, int L,
-    int k, int n_slots, int W, int cap, int step) {
+    int k, int n_slots, int W, int cap, int step, int mq, int mstride) {
   __shared__ int32_t s_pos[kMaxSlots];
   __shared__ int32_t s_last[kMaxSlots];
   __shared__ uint8_t s_ref[kMaxSlots];
-  __shared__ int32_t s_miss[kMaxTopk];   // input index of each miss
-  __shared__ int32_t s_mpos[kMaxTopk];   // its position (read by the serial placement)
+  __shared__ int32_t s_miss[kMaxListMisses];   // input index of each miss
+  __shared__ int32_t s_mpos[kMaxListMisses];   // its position (read by the serial placement)
   __shared__ uint32_t s_wsum[kResolveThreads / 64];
-  __shared__ int s_nm, s_nmid, s_bad, s_tlast;
+  __shared__ int s_nm, s_nmid, s_bad, s_tlast, s_hand, s_moff;
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int32_t* sp = slot_pos + (size_t)b * n_slots;
@@ -128,20 +132,32 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
     s_last[i] = sl[i];
     s_ref[i] = (uint8_t)sr[i];
   }
-  const int h0 = hand_arr[b];
+  if (threadIdx.x == 0) {
+    s_bad = 0;
+    s_hand = hand_arr[b];
+    s_moff = 0;
+  }
+  __syncthreads();
+  // The mq pick lists of the sequence (several query tokens) are resolved one
+  // after another at the same step: rows placed for an earlier list are used
+  // in this step, so a later list finds them (hit) and cannot evict them.
+  const int km = k + mq - 1;   // middle picks of one list relative to this context
+  for (int qj = 0; qj < mq; ++qj) {
+  const int h0 = s_hand;
+  const int moff = s_moff;
+  int n = n_sel[(size_t)b * mq + qj];
+  __syncthreads();   // every thread has read the previous list's hand and offset
   if (threadIdx.x == 0) {
     s_nm = 0;
     s_nmid = 0;
-    s_bad = 0;
     s_tlast = -1;
   }
-  int n = n_sel[b];
   if (n < 0 || n > cap) {
     if (threadIdx.x == 0) raise_flag(flags, SKV_FLAG_TIER_INPUT);
     n = n < 0 ? 0 : cap;
   }
-  const int32_t* ib = idx + (size_t)b * cap;
-  int32_t* rb = rows + (size_t)b * cap;
+  const int32_t* ib = idx + ((size_t)b * mq + qj) * cap;
+  int32_t* rb = rows + ((size_t)b * mq + qj) * cap;
   __syncthreads();
 
   // phase A: classify; hits refresh their slot; misses listed in input order
@@ -184,7 +200,7 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
     for (int w = 0; w < wave; ++w) off += (int)s_wsum[w];
     if (miss) {
       const int at = off + (int)__popcll(m & lt_mask);
-      if (at < k) {
+      if (at < km) {
         s_miss[at] = i;
         s_mpos[at] = p;
       } else {
@@ -205,9 +221,9 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
   // slots not used in this step are the candidates)
   const bool fits = POLICY == SKV_TIER_LRU ? (int64_t)s_nmid <= (int64_t)n_slots
                                            : (int64_t)s_nmid < (int64_t)n_slots;
-  const int nm = fits ? min(s_nm, k) : 0;
+  const int nm = fits ? min(s_nm, km) : 0;
   if (!fits) {
-    for (int mi = threadIdx.x; mi < min(s_nm, k); mi += blockDim.x) rb[s_miss[mi]] = 0;
+    for (int mi = threadIdx.x; mi < min(s_nm, km); mi += blockDim.x) rb[s_miss[mi]] = 0;
     if (threadIdx.x == 0) s_bad = 1;
   }
   __syncthreads();
@@ -313,8 +329,8 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
           s_last[j] = step;
           sop[p] = j;
           rb[i] = S + L + j;
-          miss_pos[(size_t)b * k + mi] = p;
-          miss_slot[(size_t)b * k + mi] = j;
+          miss_pos[(size_t)b * mstride + moff + mi] = p;
+          miss_slot[(size_t)b * mstride + moff + mi] = j;
         }
       }
     }
@@ -324,20 +340,14 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
     for (int mi = placed + (int)threadIdx.x; mi < nm; mi += blockDim.x) rb[s_miss[mi]] = 0;
     __syncthreads();
     if (threadIdx.x == 0) {
-      miss_count[b] = placed;
+      s_moff = moff + placed;
       atomicAdd(&counters[0], (unsigned long long)s_nmid);
       atomicAdd(&counters[1], (unsigned long long)(s_nmid - nm));
       atomicAdd(&counters[2], (unsigned long long)nm);
-      if (s_bad || placed < nm) raise_flag(flags, SKV_FLAG_TIER_INPUT);
+      if (placed < nm) s_bad = 1;
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < n_slots; i += blockDim.x) {
-      sp[i] = s_pos[i];
-      sl[i] = s_last[i];
-      sr[i] = (int32_t)s_ref[i];
-    }
-    return;
-  }
+  } else {
 
   // phase B: thread t owns the slots at hand distance [kRun*t, kRun*t + kRun)
   const int old_limit = step - W;   // last <= step - W: outside the window
@@ -371,8 +381,8 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
     s_last[j] = step;
     sop[p] = j;
     rb[i] = S + L + j;
-    miss_pos[(size_t)b * k + mi] = p;
-    miss_slot[(size_t)b * k + mi] = j;
+    miss_pos[(size_t)b * mstride + moff + mi] = p;
+    miss_slot[(size_t)b * mstride + moff + mi] = j;
     if (mi == placed - 1) s_tlast = t;
   };
   uint32_t rleft = 0;   // referenced slots not taken
@@ -406,15 +416,20 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
   for (int mi = placed + (int)threadIdx.x; mi < nm; mi += blockDim.x) rb[s_miss[mi]] = 0;
   if (threadIdx.x == 0) {
     if (placed < nm) s_bad = 1;
-    if (placed > 0) hand_arr[b] = h0 + tlast + 1 < n_slots ? h0 + tlast + 1 : h0 + tlast + 1 - n_slots;
-    miss_count[b] = placed;
+    if (placed > 0) s_hand = h0 + tlast + 1 < n_slots ? h0 + tlast + 1 : h0 + tlast + 1 - n_slots;
+    s_moff = moff + placed;
     atomicAdd(&counters[0], (unsigned long long)s_nmid);
     atomicAdd(&counters[1], (unsigned long long)(s_nmid - nm));
     atomicAdd(&counters[2], (unsigned long long)nm);
   }
   __syncthreads();
-  if (threadIdx.x == 0 && s_bad) raise_flag(flags, SKV_FLAG_TIER_INPUT);
-  __syncthreads();
+  }   // policy
+  }   // pick lists
+  if (threadIdx.x == 0) {
+    miss_count[b] = s_moff;
+    hand_arr[b] = s_hand;
+    if (s_bad) raise_flag(flags, SKV_FLAG_TIER_INPUT);
+  }
   for (int i = threadIdx.x; i < n_slots; i += blockDim.x) {
     sp[i] = s_pos[i];
     sl[i] = s_last[i];
@@ -428,7 +443,7 @@ __global__ __launch_bounds__(256) void tier_fetch_kernel(
     const uint8_t* __restrict__ host, const int32_t* __restrict__ miss_pos,
     const int32_t* __restrict__ miss_slot, const int32_t* __restrict__ miss_count,
     int8_t* __restrict__ res_k, int8_t* __restrict__ res_v, uint16_t* __restrict__ res_ks,
-    uint16_t* __restrict__ res_vs, int64_t host_ctx, int Hkv, int k, int64_t res_rows, int res_off) {
+    uint16_t* __restrict__ res_vs, int64_t host_ctx, int Hkv, int mstride, int64_t res_rows, int res_off) {
   constexpr int D = 256;
   constexpr int ROWB = D / 2 + 2 * (D / 64);   // 136
   const int b = blockIdx.y;
@@ -438,8 +453,8 @@ __global__ __launch_bounds__(256) void tier_fetch_kernel(
   const int nwaves = gridDim.x * (blockDim.x >> 6);
   for (int task = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); task < nm * Hkv; task += nwaves) {
     const int mi = task / Hkv, h = task % Hkv;
-    const int p = miss_pos[(size_t)b * k + mi];
-    const int slot = miss_slot[(size_t)b * k + mi];
+    const int p = miss_pos[(size_t)b * mstride + mi];
+    const int slot = miss_slot[(size_t)b * mstride + mi];
     const uint8_t* row = host + (((size_t)b * host_ctx + p) * Hkv + h) * (2 * ROWB) + half * ROWB;
     const uint32_t codes = *reinterpret_cast<const uint32_t*>(row + 4 * ln);
     const uint2 sc = *reinterpret_cast<const uint2*>(row + D / 2);
@@ -529,6 +544,7 @@ extern "C" skv_status sparsekv_tier_create(const skv_tier_desc* d, skv_tier** ou
   t->B = L.batch; t->T0 = d->ctx; t->cap_ctx = L.max_ctx; t->S = L.n_sink; t->L = L.n_tail; t->k = L.topk;
   t->Hkv = L.n_kv_heads; t->D = L.head_dim; t->n_slots = d->n_slots; t->W = d->window;
   t->cap = skv::select_capacity(L);
+  t->mstride = skv::kMaxQueries * (t->k + skv::kMaxQueries);
   t->row_bytes = t->D / 2 + 2 * (t->D / 64);
   t->rec_bytes = 2 * t->row_bytes;
   t->res_rows = (int64_t)t->S + t->L + t->n_slots;
@@ -564,8 +580,8 @@ extern "C" skv_status sparsekv_tier_create(const skv_tier_desc* d, skv_tier** ou
             hipMalloc(&t->hand, (size_t)t->B * 4) == hipSuccess &&
             hipMalloc(&t->slot_of_pos, (size_t)t->B * t->cap_ctx * 4) == hipSuccess &&
             hipMalloc(&t->ctx_dev, (size_t)t->B * 4) == hipSuccess &&
-            hipMalloc(&t->miss_pos, (size_t)t->B * t->k * 4) == hipSuccess &&
-            hipMalloc(&t->miss_slot, (size_t)t->B * t->k * 4) == hipSuccess &&
+            hipMalloc(&t->miss_pos, (size_t)t->B * t->mstride * 4) == hipSuccess &&
+            hipMalloc(&t->miss_slot, (size_t)t->B * t->mstride * 4) == hipSuccess &&
             hipMalloc(&t->miss_count, (size_t)t->B * 4) == hipSuccess &&
             hipMalloc(&t->counters, 3 * sizeof(unsigned long long)) == hipSuccess &&
             hipMalloc(&t->flags, 256) == hipSuccess;
@@ -632,33 +648,48 @@ extern "C" skv_status sparsekv_tier_load_resident(skv_tier* t, const int8_t* k, 
   return SKV_OK;
 }
 
-extern "C" skv_status sparsekv_tier_resolve(skv_tier* t, const int32_t* idx, const int32_t* n_sel,
-                                            int32_t step, int32_t* rows, void* stream) {
+static skv_status tier_resolve_lists(skv_tier* t, int32_t n_query, const int32_t* idx,
+                                     const int32_t* n_sel, int32_t step, int32_t* rows,
+                                     void* stream) {
   if (!t || !idx || !n_sel || !rows) return set_error(SKV_ERR_INVALID, "tier_resolve: NULL argument");
+  if (n_query < 1 || n_query > skv::kMaxQueries)
+    return set_error(SKV_ERR_UNSUPPORTED, "tier_resolve: n_query %d outside [1, %d]", n_query,
+                     skv::kMaxQueries);
   hipStream_t st = (hipStream_t)stream;
-  if (t->policy == SKV_TIER_LRU)
-    hipLaunchKernelGGL(skv::tier_resolve_kernel<SKV_TIER_LRU>, dim3(t->B), dim3(skv::kResolveThreads), 0,
-                       st, idx, n_sel, rows, t->slot_pos, t->slot_last, t->slot_ref, t->hand,
-                       t->slot_of_pos, t->miss_pos, t->miss_slot, t->miss_count, t->counters, t->flags,
-                       t->ctx_dev, t->T0, t->cap_ctx, t->S, t->L, t->k, t->n_slots, t->W, t->cap, step);
-  else
-    hipLaunchKernelGGL(skv::tier_resolve_kernel<SKV_TIER_CLOCK>, dim3(t->B), dim3(skv::kResolveThreads),
-                       0, st, idx, n_sel, rows, t->slot_pos, t->slot_last, t->slot_ref, t->hand,
-                       t->slot_of_pos, t->miss_pos, t->miss_slot, t->miss_count, t->counters, t->flags,
-                       t->ctx_dev, t->T0, t->cap_ctx, t->S, t->L, t->k, t->n_slots, t->W, t->cap, step);
+#define SKV_RESOLVE(POL)                                                                           \
+  hipLaunchKernelGGL(skv::tier_resolve_kernel<POL>, dim3(t->B), dim3(skv::kResolveThreads), 0, st, \
+                     idx, n_sel, rows, t->slot_pos, t->slot_last, t->slot_ref, t->hand,            \
+                     t->slot_of_pos, t->miss_pos, t->miss_slot, t->miss_count, t->counters,        \
+                     t->flags, t->ctx_dev, t->T0, t->cap_ctx, t->S, t->L, t->k, t->n_slots, t->W,  \
+                     t->cap, step, n_query, t->mstride)
+  if (t->policy == SKV_TIER_LRU) SKV_RESOLVE(SKV_TIER_LRU);
+  else SKV_RESOLVE(SKV_TIER_CLOCK);
+#undef SKV_RESOLVE
   if (hipGetLastError() != hipSuccess) return set_error(SKV_ERR_HIP, "tier_resolve: launch failed");
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   if (skv::timer_next(skv::kTimerStream, &ev0, &ev1))   // diagnostic timer (sparsekv_timer_enable)
     hipExtLaunchKernelGGL(skv::tier_fetch_kernel, dim3(128, t->B), dim3(256), 0, st, ev0, ev1, 0,
                           t->host_dev, t->miss_pos, t->miss_slot, t->miss_count, t->res_k, t->res_v,
-                          t->res_ks, t->res_vs, (int64_t)t->cap_ctx, t->Hkv, t->k, t->res_rows, t->S + t->L);
+                          t->res_ks, t->res_vs, (int64_t)t->cap_ctx, t->Hkv, t->mstride, t->res_rows,
+                          t->S + t->L);
   else
     hipLaunchKernelGGL(skv::tier_fetch_kernel, dim3(128, t->B), dim3(256), 0, st, t->host_dev,
                        t->miss_pos, t->miss_slot, t->miss_count, t->res_k, t->res_v, t->res_ks,
-                       t->res_vs, (int64_t)t->cap_ctx, t->Hkv, t->k, t->res_rows, t->S + t->L);
+                       t->res_vs, (int64_t)t->cap_ctx, t->Hkv, t->mstride, t->res_rows, t->S + t->L);
   if (hipGetLastError() != hipSuccess) return set_error(SKV_ERR_HIP, "tier_fetch: launch failed");
   t->steps += 1;
   return SKV_OK;
+}
+
+extern "C" skv_status sparsekv_tier_resolve(skv_tier* t, const int32_t* idx, const int32_t* n_sel,
+                                            int32_t step, int32_t* rows, void* stream) {
+  return tier_resolve_lists(t, 1, idx, n_sel, step, rows, stream);
+}
+
+extern "C" skv_status sparsekv_tier_resolve_multi(skv_tier* t, int32_t n_query, const int32_t* idx,
+                                                  const int32_t* n_sel, int32_t step, int32_t* rows,
+                                                  void* stream) {
+  return tier_resolve_lists(t, n_query, idx, n_sel, step, rows, stream);
 }
 
 extern "C" skv_status sparsekv_tier_append(skv_tier* t, int32_t* ctx_len, const void* k_new,
