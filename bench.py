@@ -82,6 +82,12 @@ CONFIGS = {
                   workload="decode-step append for the host tier, 4 seq x 250,000 tokens (cfg5 "
                            "shape): the new token's int4 host record written zero-copy, its int8 "
                            "rows into the tail ring, its int4 key sketch"),
+    "cfg5m": dict(kind="tier", B=4, T=250_000, n_kv=4, n_q=24, D=256, S=64, k=2048, L=1024,
+                  kv="i8", layers=1, seed=1005, warm_steps=64, steps=256, M=4, share=0.9,
+                  workload="4 seq x 250,000 tokens, 4 query tokens each (current + 3 drafted, "
+                           "90% of each draft's picks shared with the current token's); cfg2 layer "
+                           "shape; int4 host-RAM K/V records read zero-copy, 2.5% hot slots "
+                           "(windowed CLOCK) holding every query's rows, drifting-locality picks"),
     "cfg5": dict(kind="tier", B=4, T=250_000, n_kv=4, n_q=24, D=256, S=64, k=2048, L=1024,
                  kv="i8", layers=1, seed=1005, warm_steps=64, steps=256,
                  workload="4 seq x 250,000 tokens; cfg2 layer shape; int4 host-RAM K/V records read "
@@ -639,11 +645,15 @@ def bench_tier(cfg, args):
     B, T, S, L, k = cfg["B"], cfg["T"], cfg["S"], cfg["L"], cfg["k"]
     warm = args.warmup if args.warmup_given else cfg["warm_steps"]
     steps = args.steps if args.steps_given else cfg["steps"]
+    M = cfg.get("M", 1)
     log("generating the host-tier case")
     c = synth.make_tier_case(B, T, n_kv=cfg["n_kv"], n_q=cfg["n_q"], D=cfg["D"], S=S, k=k, L=L,
                              seed=cfg["seed"], device="cuda")
-    picks = synth.drift_picks(B, T, S, L, k, warm + steps, seed=cfg["seed"],
-                              window=min(65536, (T - S - L) // 2), sigma_c=256.0)
+    # M query tokens: the last M positions; picks below the first one's middle end
+    T1 = T - M + 1
+    picks = synth.drift_picks(B, T1, S, L, k, warm + steps, seed=cfg["seed"],
+                              window=min(65536, (T1 - S - L) // 2), sigma_c=256.0)
+    mpicks = synth.draft_picks(picks, M, cfg["share"], cfg["seed"]) if M > 1 else picks[:, :, None]
     desc = skv.token_desc(B, T, cfg["n_kv"], cfg["n_q"], cfg["D"], topk=k, n_sink=S, n_tail=L)
     n_slots = cfg.get("slots", c.n_slots)
     lru = cfg.get("policy") == "lru"
@@ -653,27 +663,51 @@ def bench_tier(cfg, args):
         tier.load_resident(c.res_k, c.res_v, c.res_ks, c.res_vs)
         res = tier.resident()
         cap = skv.select_capacity(desc)
-        idx_all = torch.from_numpy(np.concatenate([
-            np.broadcast_to(np.arange(S, dtype=np.int32), (warm + steps, B, S)), picks,
-            np.broadcast_to(np.arange(T - L, T, dtype=np.int32), (warm + steps, B, L))], axis=2).copy()).cuda()
-        ws = skv.workspace(desc)
-        rows = torch.zeros((B, cap), dtype=torch.int32, device="cuda")
-        nsel = torch.full((B,), cap, dtype=torch.int32, device="cuda")
-        out = torch.zeros((B, cfg["n_q"], cfg["D"]), dtype=torch.float32, device="cuda")
-        q = c.q.contiguous()
+        nst = warm + steps
+        if M == 1:
+            idx_all = torch.from_numpy(np.concatenate([
+                np.broadcast_to(np.arange(S, dtype=np.int32), (nst, B, S)), picks,
+                np.broadcast_to(np.arange(T - L, T, dtype=np.int32), (nst, B, L))], axis=2).copy()).cuda()
+            ws = skv.workspace(desc)
+            rows = torch.zeros((B, cap), dtype=torch.int32, device="cuda")
+            nsel = torch.full((B,), cap, dtype=torch.int32, device="cuda")
+            out = torch.zeros((B, cfg["n_q"], cfg["D"]), dtype=torch.float32, device="cuda")
+            q = c.q.contiguous()
+        else:
+            tails = np.stack([np.arange(T1 + j - L, T1 + j, dtype=np.int32) for j in range(M)])
+            idx_all = torch.from_numpy(np.concatenate([
+                np.broadcast_to(np.arange(S, dtype=np.int32), (nst, B, M, S)), mpicks,
+                np.broadcast_to(tails, (nst, B, M, L))], axis=3).copy()).cuda()
+            ws = skv.workspace_multi(desc, M)
+            rows = torch.zeros((B, M, cap), dtype=torch.int32, device="cuda")
+            nsel = torch.full((B, M), cap, dtype=torch.int32, device="cuda")
+            out = torch.zeros((B, M, cfg["n_q"], cfg["D"]), dtype=torch.float32, device="cuda")
+            q = synth.multi_queries(B, M, cfg["n_q"], cfg["D"], cfg["seed"], device="cuda")
         sm = cfg["D"] ** -0.5
+
+        def resolve(s_):
+            if M == 1:
+                tier.resolve(idx_all[s_], nsel, s_, rows)
+            else:
+                tier.resolve_multi(M, idx_all[s_], nsel, s_, rows)
+
+        def attend():
+            if M == 1:
+                skv.attend(desc, q, res, rows, nsel, sm, out, ws)
+            else:
+                skv.attend_multi(desc, M, q, res, rows, nsel, sm, out, ws)
         log("warmup", warm)
         for s_ in range(warm):
-            tier.resolve(idx_all[s_], nsel, s_, rows)
-            skv.attend(desc, q, res, rows, nsel, sm, out, ws)
+            resolve(s_)
+            attend()
         st0 = tier.stats()
         log("timing %d layer-steps" % steps)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for s_ in range(warm, warm + steps):
-            tier.resolve(idx_all[s_], nsel, s_, rows)
-            skv.attend(desc, q, res, rows, nsel, sm, out, ws)
+            resolve(s_)
+            attend()
         e1.record()
         e1.synchronize()
         secs = e0.elapsed_time(e1) / 1e3
@@ -681,11 +715,11 @@ def bench_tier(cfg, args):
         # the resolve alone, on a replay of the same picks from a reset buffer
         tier.reset()
         for s_ in range(warm):
-            tier.resolve(idx_all[s_], nsel, s_, rows)
+            resolve(s_)
         torch.cuda.synchronize()
         e0.record()
         for s_ in range(warm, warm + steps):
-            tier.resolve(idx_all[s_], nsel, s_, rows)
+            resolve(s_)
         e1.record()
         e1.synchronize()
         rsecs = e0.elapsed_time(e1) / 1e3
@@ -693,17 +727,18 @@ def bench_tier(cfg, args):
         # third replay of the same picks: the same misses)
         tier.reset()
         for s_ in range(warm):
-            tier.resolve(idx_all[s_], nsel, s_, rows)
+            resolve(s_)
         skv.timer_enable(True)
         for s_ in range(warm, warm + steps):
-            tier.resolve(idx_all[s_], nsel, s_, rows)
+            resolve(s_)
         f_ms, f_n = skv.timer_read()
         skv.timer_enable(False)
         assert skv.check(ws) == 0
         cpu = None
         if not args.no_cpu_baseline:
             log("cpu baseline (oracle)")
-            cpu = _tier_cpu_baseline(cfg, c, picks, warm, tier.host_records()[0], lru, n_slots)
+            cpu = _tier_cpu_baseline(cfg, c, mpicks, warm, tier.host_records()[0], lru, n_slots,
+                                     q[0].cpu().numpy() if M > 1 else None)
     finally:
         tier.close()
     hits, misses = st1.hits - st0.hits, st1.misses - st0.misses
@@ -721,8 +756,9 @@ def bench_tier(cfg, args):
         "vs_baseline": None,
         "dtype": "i8",
         "data": "synthetic",
-        "config": {"workload": cfg["workload"], "name": args.config, "batch": B, "ctx": T,
-                   "hot_slots_per_seq": n_slots, "policy": "lru" if lru else "windowed-clock"},
+        "config": dict({"workload": cfg["workload"], "name": args.config, "batch": B, "ctx": T,
+                        "hot_slots_per_seq": n_slots, "policy": "lru" if lru else "windowed-clock"},
+                       **({"query_tokens_per_seq": M} if M > 1 else {})),
         "tier": {"miss_rate": round(misses / max(1, hits + misses), 4), "hits": hits, "misses": misses,
                  "host_bytes_per_step": round(hbytes / steps),
                  "pcie_GBps_over_step": round(hbytes / secs / 1e9, 2),
@@ -732,6 +768,8 @@ def bench_tier(cfg, args):
         "roofline": None,
         "cpu_baseline": cpu,
     }
+    if M > 1:
+        res_line["query_tokens_per_s"] = round(steps / secs * B * M, 1)
     if f_n:
         f_s = f_ms / 1e3 / f_n
         per = hbytes / steps
@@ -743,35 +781,44 @@ def bench_tier(cfg, args):
     print(json.dumps(res_line), flush=True)
 
 
-def _tier_cpu_baseline(cfg, c, picks, warm, records_b, lru, n_slots, min_seconds=10.0):
+def _tier_cpu_baseline(cfg, c, lists, warm, records_b, lru, n_slots, qm=None, min_seconds=10.0):
     """The oracle's host-tier layer-step on sequence 0 (hot-buffer resolve with
     its policy, then attention over the resident rows and the fetched host
-    records), after the same warm-up; scaled to the whole batch."""
+    records; with several query tokens each query's list and attention),
+    after the same warm-up; scaled to the whole batch.  lists: middle picks
+    [n_steps][B][M][k]; qm: fp16 [M][H_q][D] queries of sequence 0 (M > 1)."""
     import oracle
     from threadpoolctl import threadpool_limits
-    B, T, S, L, k = cfg["B"], cfg["T"], cfg["S"], cfg["L"], cfg["k"]
+    B, T, S, L = cfg["B"], cfg["T"], cfg["S"], cfg["L"]
+    M = lists.shape[2]
+    T1 = T - M + 1
     tier = oracle.residency.LruTier(n_slots, T) if lru else oracle.ClockTier(n_slots, T, window=1)
+
+    def full(s_, j):
+        return np.concatenate([np.arange(S), lists[s_, 0, j], np.arange(T1 + j - L, T1 + j)])
     for s_ in range(warm):
-        tier.step(picks[s_, 0], s_)
-    q = c.q[0].cpu().numpy()
+        oracle.multiquery.tier_resolve_lists(tier, [full(s_, j) for j in range(M)], T, S, L, s_)
+    qs = [c.q[0].cpu().numpy()] if M == 1 else [qm[j] for j in range(M)]
     rk, rv = c.res_k[0].cpu().numpy(), c.res_v[0].cpu().numpy()
     rks, rvs = c.res_ks[0].cpu().numpy(), c.res_vs[0].cpu().numpy()
     sm = cfg["D"] ** -0.5
     t_total, reps = 0.0, 0
     with threadpool_limits(limits=1):
-        while reps < 40 and (reps == 0 or t_total < min_seconds) and warm + reps < picks.shape[0]:
+        while reps < 40 and (reps == 0 or t_total < min_seconds) and warm + reps < lists.shape[0]:
             s_ = warm + reps
-            idx = np.concatenate([np.arange(S), picks[s_, 0], np.arange(T - L, T)])
+            idx = [full(s_, j) for j in range(M)]
             t0 = time.perf_counter()
-            tier.step(picks[s_, 0], s_)
-            oracle.tier_attention(q, records_b, rk, rv, rks, rvs, idx, T, S, L, sm,
-                                  cfg["n_q"] // cfg["n_kv"], cfg["D"])
+            oracle.multiquery.tier_resolve_lists(tier, idx, T, S, L, s_)
+            for j in range(M):
+                oracle.tier_attention(qs[j], records_b, rk, rv, rks, rvs, idx[j], T, S, L, sm,
+                                      cfg["n_q"] // cfg["n_kv"], cfg["D"])
             t_total += time.perf_counter() - t0
             reps += 1
     return {"value": round(reps / t_total / B, 4), "unit": "layer-steps/s", "cores": 1,
             "kind": "oracle",
-            "sample": "%d steps of sequence 0 (resolve + attention), scaled to the %d-sequence batch"
-                      % (reps, B), "seconds": round(t_total, 3)}
+            "sample": "%d steps of sequence 0 (resolve + attention%s), scaled to the %d-sequence batch"
+                      % (reps, "" if M == 1 else " of its %d query tokens" % M, B),
+            "seconds": round(t_total, 3)}
 
 
 def main():

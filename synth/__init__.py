@@ -18,6 +18,7 @@ from .gen import (  # noqa: F401
     make_block_case,
     make_tier_case,
     drift_picks,
+    draft_picks,
     multi_queries,
     prefill_picks,
     orthonormal_basis,

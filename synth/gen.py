@@ -36,6 +36,7 @@ _T_Q, _T_BASIS, _T_SKETCH, _T_K, _T_V, _T_NEEDLE = 1, 2, 3, 4, 5, 6
 _T_QI, _T_RAWIDX, _T_HK, _T_HV, _T_RK, _T_RV, _T_DRIFT, _T_LEN = 7, 8, 9, 10, 11, 12, 13, 14
 _T_MQ = 15
 _T_PICKS = 16
+_T_DRAFT = 17
 
 
 def _subseed(seed: int, *ids: int) -> int:
@@ -461,4 +462,34 @@ def drift_picks(B: int, T: int, S: int, L: int, k: int, n_steps: int, seed: int,
                             break
             cur = np.array(sorted(have), dtype=np.int64)
             out[s, b] = cur
+    return out
+
+
+def draft_picks(base: np.ndarray, M: int, share: float, seed: int) -> np.ndarray:
+    """Pick lists of M query tokens per sequence and step, int32
+    [n_steps][B][M][k], each row sorted: query 0 takes the base picks
+    ([n_steps][B][k], e.g. drift_picks); each later query (a drafted token)
+    keeps a random round(share * k) of them and replaces the rest with
+    positions drawn uniformly between the smallest and largest base pick,
+    rejecting duplicates.  All positions stay inside the base picks' range."""
+    rng = np.random.Generator(np.random.PCG64(_subseed(seed, _T_DRAFT)))
+    n_steps, B, k = base.shape
+    n_keep = int(round(share * k))
+    out = np.empty((n_steps, B, M, k), dtype=np.int32)
+    for s in range(n_steps):
+        for b in range(B):
+            bs = np.sort(base[s, b].astype(np.int64))
+            out[s, b, 0] = bs
+            lo, hi = int(bs[0]), int(bs[-1]) + 1
+            for j in range(1, M):
+                kept = bs[np.sort(rng.choice(k, n_keep, replace=False))]
+                need = k - n_keep
+                got = np.zeros(0, dtype=np.int64)
+                while got.size < need:
+                    cand = rng.integers(lo, hi, size=3 * need + 16)
+                    pos = np.searchsorted(bs, cand)
+                    fresh = cand[(pos >= k) | (bs[np.minimum(pos, k - 1)] != cand)]
+                    got = np.unique(np.concatenate([got, fresh]))
+                got = rng.permutation(got)[:need]
+                out[s, b, j] = np.sort(np.concatenate([kept, got]))
     return out

@@ -104,7 +104,9 @@ __global__ void tier_reset_kernel(int32_t* slot_pos, int32_t* slot_last, int32_t
   if (tid < 3) counters[tid] = 0ull;
 }
 
-template <int POLICY>
+// MULTI: several pick lists per sequence (mq of them); one list compiles to
+// straight-line code without the loop's live state
+template <int POLICY, bool MULTI>
 __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ n_sel, int32_t* __restrict__ rows,
     int32_t* __restrict__ slot_pos, int32_t* __restrict__ slot_last, int32_t* __restrict__ slot_ref,
@@ -126,28 +128,26 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
   int32_t* sl = slot_last + (size_t)b * n_slots;
   int32_t* sr = slot_ref + (size_t)b * n_slots;
   int32_t* sop = slot_of_pos + (size_t)b * cap_ctx;
+  // scalars first: their loads overlap the slot-table copy
   const int T = tier_ctx[b];   // this sequence's context (sinks, middle, tail ring)
+  int hand = hand_arr[b];
+  int n_next = n_sel[(size_t)b * mq];
+  int moff = 0;   // misses placed by the earlier lists
   for (int i = threadIdx.x; i < n_slots; i += blockDim.x) {
     s_pos[i] = sp[i];
     s_last[i] = sl[i];
     s_ref[i] = (uint8_t)sr[i];
   }
-  if (threadIdx.x == 0) {
-    s_bad = 0;
-    s_hand = hand_arr[b];
-    s_moff = 0;
-  }
-  __syncthreads();
+  if (threadIdx.x == 0) s_bad = 0;
   // The mq pick lists of the sequence (several query tokens) are resolved one
   // after another at the same step: rows placed for an earlier list are used
   // in this step, so a later list finds them (hit) and cannot evict them.
+  if (!MULTI) mq = 1;
   const int km = k + mq - 1;   // middle picks of one list relative to this context
-  for (int qj = 0; qj < mq; ++qj) {
-  const int h0 = s_hand;
-  const int moff = s_moff;
-  int n = n_sel[(size_t)b * mq + qj];
-  __syncthreads();   // every thread has read the previous list's hand and offset
-  if (threadIdx.x == 0) {
+  for (int qj = 0; qj < (MULTI ? mq : 1); ++qj) {
+  const int h0 = hand;
+  int n = n_next;
+  if (threadIdx.x == 0) {   // nobody reads these between the previous list's last barrier and the next
     s_nm = 0;
     s_nmid = 0;
     s_tlast = -1;
@@ -341,6 +341,7 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
     __syncthreads();
     if (threadIdx.x == 0) {
       s_moff = moff + placed;
+      s_hand = h0;
       atomicAdd(&counters[0], (unsigned long long)s_nmid);
       atomicAdd(&counters[1], (unsigned long long)(s_nmid - nm));
       atomicAdd(&counters[2], (unsigned long long)nm);
@@ -416,7 +417,7 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
   for (int mi = placed + (int)threadIdx.x; mi < nm; mi += blockDim.x) rb[s_miss[mi]] = 0;
   if (threadIdx.x == 0) {
     if (placed < nm) s_bad = 1;
-    if (placed > 0) s_hand = h0 + tlast + 1 < n_slots ? h0 + tlast + 1 : h0 + tlast + 1 - n_slots;
+    s_hand = placed > 0 ? (h0 + tlast + 1 < n_slots ? h0 + tlast + 1 : h0 + tlast + 1 - n_slots) : h0;
     s_moff = moff + placed;
     atomicAdd(&counters[0], (unsigned long long)s_nmid);
     atomicAdd(&counters[1], (unsigned long long)(s_nmid - nm));
@@ -424,10 +425,13 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
   }
   __syncthreads();
   }   // policy
+  hand = s_hand;
+  moff = s_moff;
+  if (qj + 1 < mq) n_next = n_sel[(size_t)b * mq + qj + 1];
   }   // pick lists
   if (threadIdx.x == 0) {
-    miss_count[b] = s_moff;
-    hand_arr[b] = s_hand;
+    miss_count[b] = moff;
+    hand_arr[b] = hand;
     if (s_bad) raise_flag(flags, SKV_FLAG_TIER_INPUT);
   }
   for (int i = threadIdx.x; i < n_slots; i += blockDim.x) {
@@ -657,13 +661,20 @@ static skv_status tier_resolve_lists(skv_tier* t, int32_t n_query, const int32_t
                      skv::kMaxQueries);
   hipStream_t st = (hipStream_t)stream;
 #define SKV_RESOLVE(POL)                                                                           \
-  hipLaunchKernelGGL(skv::tier_resolve_kernel<POL>, dim3(t->B), dim3(skv::kResolveThreads), 0, st, \
+  hipLaunchKernelGGL((skv::tier_resolve_kernel<POL, MUL>), dim3(t->B), dim3(skv::kResolveThreads), 0, st, \
                      idx, n_sel, rows, t->slot_pos, t->slot_last, t->slot_ref, t->hand,            \
                      t->slot_of_pos, t->miss_pos, t->miss_slot, t->miss_count, t->counters,        \
                      t->flags, t->ctx_dev, t->T0, t->cap_ctx, t->S, t->L, t->k, t->n_slots, t->W,  \
                      t->cap, step, n_query, t->mstride)
-  if (t->policy == SKV_TIER_LRU) SKV_RESOLVE(SKV_TIER_LRU);
-  else SKV_RESOLVE(SKV_TIER_CLOCK);
+  if (n_query == 1) {
+    constexpr bool MUL = false;
+    if (t->policy == SKV_TIER_LRU) SKV_RESOLVE(SKV_TIER_LRU);
+    else SKV_RESOLVE(SKV_TIER_CLOCK);
+  } else {
+    constexpr bool MUL = true;
+    if (t->policy == SKV_TIER_LRU) SKV_RESOLVE(SKV_TIER_LRU);
+    else SKV_RESOLVE(SKV_TIER_CLOCK);
+  }
 #undef SKV_RESOLVE
   if (hipGetLastError() != hipSuccess) return set_error(SKV_ERR_HIP, "tier_resolve: launch failed");
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
