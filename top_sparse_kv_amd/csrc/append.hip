@@ -47,7 +47,9 @@ constexpr int kAppMaxHkv = 32;   // H_kv * R <= 512 with R >= 16
 __device__ __forceinline__ float quot_rn(float a, float c) { return (float)((double)a / (double)c); }
 
 
-template <int D, bool I8>
+// TIER: also the host record and the tail ring (AppendTarget); the plain
+// cache append compiles without those paths
+template <int D, bool I8, bool TIER>
 __global__ __launch_bounds__(kAppThreads) void append_kernel(
     int32_t* __restrict__ ctx_len, const __half* __restrict__ k_new, const __half* __restrict__ v_new,
     const float* __restrict__ basis, uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
@@ -67,14 +69,15 @@ __global__ __launch_bounds__(kAppThreads) void append_kernel(
     if (threadIdx.x == 0) raise_flag(flags, SKV_FLAG_CTX_RANGE);
     return;
   }
-  if (tg.tier_ctx && tg.tier_ctx[b] != t) {   // the tier and the caller disagree
+  if (TIER && tg.tier_ctx[b] != t) {   // the tier and the caller disagree
     if (threadIdx.x == 0) raise_flag(flags, SKV_FLAG_TIER_INPUT);
     return;
   }
   // cache row of position t: row t of a full cache, a ring row of a tier's
   // tail, or none (a tier without a tail)
   int crow = t;
-  if (tg.ring_len == 0) {
+  if (!TIER) {
+  } else if (tg.ring_len == 0) {
     crow = -1;
   } else if (tg.ring_len > 0) {
     int r = (t - tg.ring_anchor) % tg.ring_len;
@@ -92,8 +95,8 @@ __global__ __launch_bounds__(kAppThreads) void append_kernel(
 #pragma unroll
       for (int e = 0; e < PL; ++e) s_k[h * D + lane * PL + e] = x[e];
     }
-    if constexpr (I8 && D == 256) {
-      if (tg.host) {
+    if constexpr (TIER && I8 && D == 256) {
+      {
         // host record: 16 lanes per 64-dim group; lane l packs elements 4l..4l+3
         float gm = 0.0f;
 #pragma unroll
@@ -113,7 +116,7 @@ __global__ __launch_bounds__(kAppThreads) void append_kernel(
         if ((lane & 15) == 0) *reinterpret_cast<uint16_t*>(hr + D / 2 + 2 * (lane >> 4)) = __half_as_ushort(g16);
       }
     }
-    if (crow < 0) continue;   // a tier without a tail keeps no int8 row
+    if (TIER && crow < 0) continue;   // a tier without a tail keeps no int8 row
     const size_t rr = ((size_t)b * rows + crow) * Hkv + h;   // cache row of (b, t, h)
     if constexpr (I8) {
       float am = 0.0f;
@@ -171,7 +174,7 @@ __global__ __launch_bounds__(kAppThreads) void append_kernel(
   if (threadIdx.x == 0) {
     sk_scale[(size_t)b * max_ctx + t] = __half_as_ushort(s16);
     ctx_len[b] = t + 1;   // every thread read t before the barriers above
-    if (tg.tier_ctx) tg.tier_ctx[b] = t + 1;
+    if (TIER) tg.tier_ctx[b] = t + 1;
   }
 }
 
@@ -260,13 +263,13 @@ hipError_t launch_append(const skv_layer_desc& d, int32_t* ctx_len, const void* 
 #define SKV_AP(DD, I8)                                                                           \
   do {                                                                                           \
     if (timed)                                                                                   \
-      hipExtLaunchKernelGGL((append_kernel<DD, I8>), dim3(d.batch), dim3(kAppThreads), 0, st,    \
+      hipExtLaunchKernelGGL((append_kernel<DD, I8, false>), dim3(d.batch), dim3(kAppThreads), 0, st,    \
                             ev0, ev1, 0, ctx_len, (const __half*)k_new, (const __half*)v_new,    \
                             basis, (uint8_t*)kv.k, (uint8_t*)kv.v, (uint16_t*)kv.k_scale,        \
                             (uint16_t*)kv.v_scale, kv.rows, (uint8_t*)index_keys, index_scale,   \
                             d.n_kv_heads, d.rank, d.max_ctx, flags, tg);                         \
     else                                                                                         \
-      hipLaunchKernelGGL((append_kernel<DD, I8>), dim3(d.batch), dim3(kAppThreads), 0, st,       \
+      hipLaunchKernelGGL((append_kernel<DD, I8, false>), dim3(d.batch), dim3(kAppThreads), 0, st,       \
                          ctx_len, (const __half*)k_new, (const __half*)v_new, basis,             \
                          (uint8_t*)kv.k, (uint8_t*)kv.v, (uint16_t*)kv.k_scale,                  \
                          (uint16_t*)kv.v_scale, kv.rows, (uint8_t*)index_keys, index_scale,      \
@@ -291,13 +294,13 @@ hipError_t launch_tier_append(const skv_layer_desc& d, int32_t* ctx_len, const v
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   const bool timed = timer_next(kTimerStream, &ev0, &ev1);   // diagnostic timer (sparsekv_timer_enable)
   if (timed)
-    hipExtLaunchKernelGGL((append_kernel<256, true>), dim3(d.batch), dim3(kAppThreads), 0, st, ev0,
+    hipExtLaunchKernelGGL((append_kernel<256, true, true>), dim3(d.batch), dim3(kAppThreads), 0, st, ev0,
                           ev1, 0, ctx_len, (const __half*)k_new, (const __half*)v_new, basis,
                           (uint8_t*)resident.k, (uint8_t*)resident.v, (uint16_t*)resident.k_scale,
                           (uint16_t*)resident.v_scale, resident.rows, (uint8_t*)index_keys,
                           index_scale, d.n_kv_heads, d.rank, d.max_ctx, flags, tg);
   else
-    hipLaunchKernelGGL((append_kernel<256, true>), dim3(d.batch), dim3(kAppThreads), 0, st, ctx_len,
+    hipLaunchKernelGGL((append_kernel<256, true, true>), dim3(d.batch), dim3(kAppThreads), 0, st, ctx_len,
                        (const __half*)k_new, (const __half*)v_new, basis, (uint8_t*)resident.k,
                        (uint8_t*)resident.v, (uint16_t*)resident.k_scale,
                        (uint16_t*)resident.v_scale, resident.rows, (uint8_t*)index_keys,
