@@ -881,7 +881,8 @@ def main():
     skv.timer_enable(False)
     # the attention kernel (gather + softmax tiles), same step loop
     skv.timer_enable(skv.SKV_TIMER_ATTEND)
-    time_loop(Layer.step, layers, ws, max(50, args.steps // 2))
+    att_steps = max(50, args.steps // 2)
+    time_loop(Layer.step, layers, ws, att_steps)
     att_ms, att_n = skv.timer_read()
     skv.timer_enable(False)
     nk = max(50, args.steps // 2)
@@ -928,13 +929,13 @@ def main():
     # the attention kernel: the K/V rows (+ row scales) it must gather at
     # least once (with several queries, the union of a sequence's picks) and
     # the query rows it reads
-    att_s = att_ms / 1e3 / max(1, att_n)
+    att_s = att_ms / 1e3 / att_steps   # one attention launch per step
     att_bytes = ab["gather"] + cfg["B"] * max(1, multi) * cfg["n_q"] * cfg["D"] * 2
     att = dict(kernel="attend", bound="hbm", achieved=round(att_bytes / att_s / 1e9, 1),
                peak=PEAK_HBM_GBS, unit="GB/s",
                frac=round(att_bytes / att_s / 1e9 / PEAK_HBM_GBS, 4), traffic=None,
                bytes_per_launch=att_bytes, avg_launch_us=round(att_s * 1e6, 2),
-               launches_timed=att_n)
+               launches_timed=att_n, launches_per_step=round(att_n / att_steps, 2))
     if multi and att_s > score_s:
         # several queries: the per-query gathers outweigh the one shared scan
         roof, att = att, roof
