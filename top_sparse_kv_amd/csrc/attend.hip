@@ -88,7 +88,9 @@ struct Esize {
   static constexpr int v = KVT == KV_I8 ? 1 : 2;
 };
 
-template <int KVT, int D, int WAVES>
+// ONE: the waves' partials merge in one stage (a slot per wave), else in two
+// (half the slots); one stage when W slots of G rows fit the LDS budget
+template <int KVT, int D, int WAVES, bool ONE>
 __global__ __launch_bounds__(64 * WAVES) void attend_kernel(
     const void* __restrict__ qv, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
     const uint16_t* __restrict__ ksc, const uint16_t* __restrict__ vsc, int64_t rows,
@@ -111,7 +113,7 @@ __global__ __launch_bounds__(64 * WAVES) void attend_kernel(
   __shared__ float s_m[WAVES][16];
   __shared__ float s_l[WAVES][16];
   __shared__ uint32_t s_q[16 * QP / 2];   // Q of the G heads, one row per head
-  extern __shared__ float s_o[];          // [HALF][G][D + 4]
+  extern __shared__ float s_o[];          // [W or HALF][G][D + 4]
 
   // Workgroup -> (KV head h, chunk c, virtual sequence b).  One query per
   // sequence: the 3-D grid.  Several: workgroups are dealt to the 8 XCDs in
@@ -343,8 +345,9 @@ __global__ __launch_bounds__(64 * WAVES) void attend_kernel(
     for (int t = 0; t < NT; ++t) o[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- merge the W waves of the workgroup in LDS, in two stages ----
-  // Wave w + HALF goes into wave w; then the HALF survivors are combined.  A
+  // ---- merge the W waves of the workgroup in LDS ----
+  // One stage (ONE), or two: wave w + HALF goes into wave w, then the HALF
+  // survivors are combined.  A
   // slot holds G rows of D + 4 floats; lane (i16, g) owns columns
   // i16*(D/16) .. +D/16 of heads 4g .. 4g+3, stored as float4 runs.
   constexpr int DP = D + 4;
@@ -352,6 +355,57 @@ __global__ __launch_bounds__(64 * WAVES) void attend_kernel(
   auto slot_ptr = [&](int slot, int j) -> f32x4* {
     return reinterpret_cast<f32x4*>(s_o + ((size_t)slot * G + j) * DP + i16 * CPL);
   };
+  if constexpr (ONE) {
+    if (g == 0) {
+      s_m[wave][i16] = m_run;
+      s_l[wave][i16] = l_run;
+    }
+    __syncthreads();
+    // every wave rescales its accumulators to the workgroup's max of each
+    // head and writes them to its own slot; the slots are summed in wave order
+    float Mw = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) Mw = fmaxf(Mw, s_m[w][i16]);
+    const float fw = m_run == -INFINITY ? 0.0f : exp2f(m_run - Mw);
+    float f_row[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f_row[e] = __shfl(fw, 4 * g + e);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = 4 * g + e;
+      if (j < G) {
+        f32x4* dst = slot_ptr(wave, j);
+#pragma unroll
+        for (int u = 0; u < CPL / 4; ++u)
+          dst[u] = (f32x4){o[4 * u][e] * f_row[e], o[4 * u + 1][e] * f_row[e],
+                           o[4 * u + 2][e] * f_row[e], o[4 * u + 3][e] * f_row[e]};
+      }
+    }
+    const size_t pbase = ((size_t)b * Hkv + h) * n_chunks + c;
+    if (threadIdx.x < 16) {
+      const int j = threadIdx.x;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) M = fmaxf(M, s_m[w][j]);
+      float Ls = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w)
+        Ls += s_m[w][j] == -INFINITY ? 0.0f : s_l[w][j] * exp2f(s_m[w][j] - M);
+      if (j < G) {
+        part_ml[(pbase * 16 + j) * 2 + 0] = M;
+        part_ml[(pbase * 16 + j) * 2 + 1] = Ls;
+      }
+    }
+    __syncthreads();
+    for (int x = threadIdx.x; x < G * D; x += blockDim.x) {
+      const int j = x / D, d = x % D;
+      float acc = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) acc += s_o[((size_t)w * G + j) * DP + d];
+      part_o[(pbase * G + j) * D + d] = acc;
+    }
+    return;
+  }
   if (g == 0) {
     s_m[wave][i16] = m_run;
     s_l[wave][i16] = l_run;
@@ -519,20 +573,30 @@ hipError_t launch_attend(const skv_layer_desc& d, const void* q, const skv_kv_vi
   const dim3 grid = mq == 1 ? dim3(d.n_kv_heads, Lw.n_att_chunks, d.batch)
                             : dim3((unsigned)(((n_keys + 7) / 8) * 8 * mq));
   const int waves = att_waves(d);
-  const size_t lds = (size_t)(waves / 2) * G * (d.head_dim + 4) * sizeof(float);
+  // one-stage merge when a slot per wave stays within 52 KB of LDS (two
+  // workgroups per compute unit with the static arrays)
+  const size_t lds1 = (size_t)waves * G * (d.head_dim + 4) * sizeof(float);
+  const bool one = lds1 <= 52 * 1024;
+  const size_t lds = one ? lds1 : lds1 / 2;
   const float sl = sm_scale * kLog2e;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   const bool timed = timer_next(kTimerAttend, &ev0, &ev1);   // diagnostic timer
 #define SKV_AT_ARGS                                                                                \
   q, (const uint8_t*)kv.k, (const uint8_t*)kv.v, kv.k_scale, kv.v_scale, kv.rows, idx, n_sel, cap,  \
       sl, d.n_q_heads, d.n_kv_heads, part_ml, part_o, Lw.n_att_chunks, flags, mq, n_keys
-#define SKV_AT(KVT, DD, WV)                                                                        \
+#define SKV_AT_O(KVT, DD, WV, ON)                                                                   \
   do {                                                                                             \
     if (timed)                                                                                     \
-      hipExtLaunchKernelGGL((attend_kernel<KVT, DD, WV>), grid, dim3(64 * WV), lds, st, ev0, ev1, \
-                            0, SKV_AT_ARGS);                                                       \
+      hipExtLaunchKernelGGL((attend_kernel<KVT, DD, WV, ON>), grid, dim3(64 * WV), lds, st, ev0,   \
+                            ev1, 0, SKV_AT_ARGS);                                                  \
     else                                                                                           \
-      hipLaunchKernelGGL((attend_kernel<KVT, DD, WV>), grid, dim3(64 * WV), lds, st, SKV_AT_ARGS); \
+      hipLaunchKernelGGL((attend_kernel<KVT, DD, WV, ON>), grid, dim3(64 * WV), lds, st,           \
+                         SKV_AT_ARGS);                                                             \
+  } while (0)
+#define SKV_AT(KVT, DD, WV)                                                                        \
+  do {                                                                                             \
+    if (one) SKV_AT_O(KVT, DD, WV, true);                                                          \
+    else SKV_AT_O(KVT, DD, WV, false);                                                             \
   } while (0)
 #define SKV_AT_W(KVT, DD)                                                                          \
   do {                                                                                             \
@@ -551,6 +615,7 @@ hipError_t launch_attend(const skv_layer_desc& d, const void* q, const skv_kv_vi
   else return hipErrorInvalidValue;
 #undef SKV_AT_W
 #undef SKV_AT
+#undef SKV_AT_O
 #undef SKV_AT_ARGS
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
