@@ -242,3 +242,13 @@ def test_tier_resolve_multi_and_attend_multi_checks(skv):
     st = lib.sparsekv_attend_multi(ctypes.byref(d), 0, dummy, ctypes.byref(kv), dummy, dummy, 0.1,
                                    dummy, ctypes.c_void_p(0x100000), four, None)
     assert st == 2
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py measures one GPU: --gpus above 1 exits with a message (no GPU needed)."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
