@@ -120,14 +120,41 @@ __global__ __launch_bounds__(kThreads) void sample_multi_kernel(
     int S, int k, int L) {
   constexpr int NQ = 2 * TB, NL = TB / 64;
   __shared__ __align__(16) int8_t s_q[kMaxQueries * NQ];
-  __shared__ uint32_t red[16];
   const int b = blockIdx.y;
-  // the M query sketches of the sequence, one int8 scale each
-  for (int j = 0; j < mq; ++j) {
-    const float scale = quantize_sketch(sproj + ((size_t)b * mq + j) * NQ, NQ, s_q + j * NQ, red);
-    if (blockIdx.x == 0) {
-      for (int i = threadIdx.x; i < NQ; i += kThreads) qs_out[((size_t)b * mq + j) * NQ + i] = s_q[j * NQ + i];
-      if (threadIdx.x == 0) qscale_out[(size_t)b * mq + j] = scale;
+  // the M query sketches of the sequence, one int8 scale each (the rule of
+  // quantize_sketch: scale = amax / 127 rounded once, codes rint(v / scale)
+  // clamped to +-127): wave w quantizes queries w, w + 4, ..., all of their
+  // values loaded first, the maximum taken over the wave
+  {
+    constexpr int VPL = NQ / 64, RPW = kMaxQueries / (kThreads / 64);
+    const int ln = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    float v[RPW][VPL];
+#pragma unroll
+    for (int u = 0; u < RPW; ++u) {
+      const int j = min(wv + u * (kThreads / 64), mq - 1);   // unconditional
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) v[u][e] = sproj[((size_t)b * mq + j) * NQ + ln + 64 * e];
+    }
+#pragma unroll
+    for (int u = 0; u < RPW; ++u) {
+      const int j = wv + u * (kThreads / 64);
+      if (j >= mq) break;   // wave-uniform
+      uint32_t am = 0;
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) am = max(am, __float_as_uint(fabsf(v[u][e])));
+      const float amax = __uint_as_float(wave_max(am));
+      const float scale = amax == 0.0f ? 0.0f : (float)((double)amax / 127.0);
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) {
+        int8_t c = 0;
+        if (amax != 0.0f) {
+          float rr = rintf((float)((double)v[u][e] / (double)scale));
+          c = (int8_t)(int)fminf(fmaxf(rr, -127.0f), 127.0f);
+        }
+        s_q[j * NQ + ln + 64 * e] = c;
+        if (blockIdx.x == 0) qs_out[((size_t)b * mq + j) * NQ + ln + 64 * e] = c;
+      }
+      if (blockIdx.x == 0 && ln == 0) qscale_out[(size_t)b * mq + j] = scale;
     }
   }
   for (int i = threadIdx.x; i < (kMaxQueries - mq) * NQ; i += kThreads) s_q[mq * NQ + i] = 0;
