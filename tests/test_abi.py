@@ -252,3 +252,22 @@ def test_bench_refuses_several_gpus():
     r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_header_is_plain_c(tmp_path):
+    """include/sparsekv.h compiles as strict C99 (plain pointers and sizes, no
+    C++ or HIP types in the boundary), and as C++17."""
+    import shutil
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    src = tmp_path / "use.c"
+    src.write_text('#include "sparsekv.h"\n'
+                   "int main(void) { return sparsekv_abi_version() == SPARSEKV_ABI_VERSION ? 0 : 1; }\n")
+    for cc, std in (("gcc", "-std=c99"), ("g++", "-std=c++17")):
+        if shutil.which(cc) is None:
+            pytest.skip("%s not available" % cc)
+        lang = ["-x", "c++"] if cc == "g++" else []
+        r = subprocess.run([cc, std, "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only",
+                            *lang, "-I", os.path.join(root, "include"), str(src)],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
