@@ -110,7 +110,7 @@ def append_tokens(ctx_len, k_new, v_new, basis, caches, max_ctx, kv_format="i8")
 
 PINS = {
     "row_i8": "hand-worked fixture (tests/golden/append_rows.txt), zero row, |x - s*c| <= s/2 off the clamp, amax code +-127",
-    "key_sketch": "unit-column basis copies coordinates (hand fixture), fp64 projection within the fp32 rounding bound, nibble round trip through oracle.unpack_int4",
+    "key_sketch": "unit-column basis copies coordinates (hand fixture); non-unit bases whose fp16 scale or codes change under a fused multiply-add or another summation order (hand-derived, tests/golden/append_rows.txt); fp64 projection within the fp32 rounding bound; nibble round trip through oracle.unpack_int4",
     "append_tokens": "row and ctx_len bookkeeping on a toy cache: only row ctx_len[b] changes, full sequences untouched",
 }
 
@@ -168,7 +168,7 @@ def append_block_tokens(ctx_len, k_new, v_new, raw_new, stage, caches, max_ctx):
 
 
 PINS.update({
-    "pooled_from_raw": "hand-worked fixture (exact mean, round to even, flush below 2^-8, clamp at 255), agreement with an exact-fraction mean",
+    "pooled_from_raw": "hand-worked fixture (exact mean, round to even, flush below 2^-8, clamp at 255), agreement with an exact-fraction mean; rounding the mean through fp32 first gives the same bits for every in-domain input (proof in the design notes), so no fixture can separate the two",
     "append_block_tokens": "staging slot t % 4, pooled key only on t % 4 == 3, full sequences untouched",
 })
 

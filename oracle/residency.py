@@ -9,8 +9,8 @@ Million-Token Contexts", section "Three residency states, one block pool"
 live in host memory, the rows the indexer wants sit in a hot buffer; one
 resolver reads resident rows in place, refreshes the LRU entry of a hot row,
 and copies a missed row from pinned host memory into an LRU slot) and the
-list after "What it composes with" (hot buffers default to 2x top-K rows per
-request).
+list after "What it composes with" (the default hot-buffer size per request is
+twice the number of rows the indexer picks).
 
 Reading (the page names LRU but gives no tie rules): each slot holds a
 position and the step it was last used.  At step s, with the picked middle

@@ -291,8 +291,8 @@ def dense_attention(q_b, k_b, v_b, ks_b, vs_b, T, sm_scale, group, fmt):
 # ----------------------------------------------------------------------------
 # A5  host tier   [P1] "The mechanism": int4 host copy with 64-dim groups and
 #     fp16 scales (272 B per token-head) turned back into int8 rows on fetch;
-#     a GPU hot buffer of 2.5% of tokens under windowed CLOCK; misses read
-#     only the picked rows from pinned host memory.
+#     a GPU hot buffer of 2.5% of tokens under windowed CLOCK; a token missing
+#     from the buffer is fetched by itself from the pinned host copy.
 # ----------------------------------------------------------------------------
 
 HOST_GROUP = 64
@@ -478,13 +478,14 @@ def block_step(q, qi, kp, k, v, lens, *, k_blocks, group, sm_scale,
 
 # What pins each function (tests/test_oracle_pins.py):
 PINS = {
-    "query_sketch": "identity-basis hand example, exact scale invariance, fp64 projection bound, orthonormal round trip",
+    "query_sketch": "identity-basis hand example; non-unit bases whose fp32 scale bits change under a fused multiply-add, another summation order or an fp64 sum (hand-derived, tests/golden/query_sketch.txt); orthonormal round trip with a permuted Hadamard basis; exact scale invariance; fp64 projection bound",
     "sketch_keys": "hand-decoded nibble fixture, exact-rational product check, needles recovered",
     "pooled_keys": "exact rational sum (fractions) on random in-domain data, needles recovered",
     "select_tokens/select_blocks": "brute-force rank counting, all-equal keys, thresholds 400/401, 3136/3137, 2051/2052, budget constancy",
     "attention_rows": "torch fp64 scaled_dot_product_attention on the dense case, one row -> v, q=0 -> mean of v, dense == sparse bitwise",
     "host_row_dequant": "hand-worked fixture, |r8| <= 127, monotone in the code within a group",
-    "ClockTier": "hand-traced fixture, hits+misses=picks, window-pinned slots never evicted, occupancy",
+    "ClockTier": "hand-traced fixtures with W = 1 and W = 2 (the W = 2 trace separates the window from W = 1 and from a '>=' window test), hits+misses=picks, window-pinned slots never evicted, occupancy",
+    "tier_attention": "equal bit for bit to sparse_attention over a plain int8 cache holding the rows the host records decode to (codes derived in exact rationals); hand-worked position -> row table for sinks, the first middle row, the tail boundary T-L and the last position",
     "byte counts": "4 MiB / 48 MiB, 64 MiB, 130 B, 272 B, 27.75 / 27.00 / 0.75 KiB closed forms",
     "attention output values": "parity unpinned by the pages (they print no worked values); pinned by the library routine and special cases above",
 }

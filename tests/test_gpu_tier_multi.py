@@ -121,25 +121,36 @@ def test_tier_multi_eight_queries_after_appends():
          appends=7)
 
 
-def test_tier_multi_over_capacity_flagged():
-    """Lists that fit one by one but not together: the step is flagged."""
+@pytest.mark.parametrize("lru", [False, True])
+def test_tier_multi_over_capacity_flagged(lru):
+    """Lists that fit one by one but not together: the step is flagged, and the
+    slot table it leaves is the same on every run (LRU: the misses outnumber
+    the slots not used in the step, so every such slot is taken in slot order)."""
     skv = need_gpu()
     B, T, S, L, k, M = 1, 6000, 16, 32, 64, 4
+    say("tier multi over capacity lru=%s" % lru)
     c = synth.make_tier_case(B, T, n_kv=H, n_q=NQ, D=D, S=S, k=k, L=L, seed=5103)
     desc = skv.token_desc(B, T, H, NQ, D, topk=k, n_sink=S, n_tail=L)
-    tier = skv.Tier(desc, T, 100, 1)
-    try:
-        tier.host_records()[:] = c.records.numpy()
-        tier.load_resident(c.res_k.cuda(), c.res_v.cuda(), c.res_ks.cuda(), c.res_vs.cuda())
-        lists = _lists(np.random.default_rng(5103), T, M, S, L, k, shared=8)   # ~232 distinct rows
-        cap = skv.select_capacity(desc)
-        rows = torch.zeros((B, M, cap), dtype=torch.int32, device="cuda")
-        nsel = torch.full((B, M), cap, dtype=torch.int32, device="cuda")
-        tier.resolve_multi(M, torch.from_numpy(np.stack(lists)[None]).cuda(), nsel, 0, rows)
-        with pytest.raises(skv.SkvError, match="0x8"):
-            tier.stats()
-    finally:
-        tier.close()
+    lists = _lists(np.random.default_rng(5103), T, M, S, L, k, shared=8)   # ~232 distinct rows
+    tables = []
+    for _ in range(2):
+        tier = skv.Tier(desc, T, 100, 1, policy=skv.SKV_TIER_LRU if lru else skv.SKV_TIER_CLOCK)
+        try:
+            tier.host_records()[:] = c.records.numpy()
+            tier.load_resident(c.res_k.cuda(), c.res_v.cuda(), c.res_ks.cuda(), c.res_vs.cuda())
+            cap = skv.select_capacity(desc)
+            rows = torch.zeros((B, M, cap), dtype=torch.int32, device="cuda")
+            nsel = torch.full((B, M), cap, dtype=torch.int32, device="cuda")
+            # one list first, then all four at the next step number
+            tier.resolve_multi(1, torch.from_numpy(np.stack(lists[:1])[None]).cuda(), nsel[:, :1].contiguous(), 0,
+                               rows[:, :1].contiguous())
+            tier.resolve_multi(M, torch.from_numpy(np.stack(lists)[None]).cuda(), nsel, 1, rows)
+            with pytest.raises(skv.SkvError, match="0x8"):
+                tier.stats()
+            tables.append(tier.slots().copy())
+        finally:
+            tier.close()
+    assert np.array_equal(tables[0], tables[1])
 
 
 def test_tier_multi_full_config5():

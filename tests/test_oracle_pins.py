@@ -119,6 +119,8 @@ def _parse_sketch_case(ln):
 
 def test_query_sketch_fixture():
     for ln in _lines("query_sketch.txt"):
+        if ln.startswith("basis "):
+            continue
         q, basis, G, expect = _parse_sketch_case(ln)
         qs, qscale = oracle.query_sketch(q, basis, G)
         assert qs[0].tolist() == expect, ln
@@ -126,6 +128,48 @@ def test_query_sketch_fixture():
             assert qscale[0] == 0
         else:
             assert qscale[0] > 0
+
+
+def _hexf(v):
+    return [float.fromhex(x) for x in v.split(",")]
+
+
+def test_query_sketch_nonunit_basis_fixture():
+    """Hand-derived cases (tests/golden/query_sketch.txt, "basis" lines) whose
+    fp32 scale changes if the products are fused into the sums or the sum is
+    taken in another order (or in fp64)."""
+    n = 0
+    for ln in _lines("query_sketch.txt"):
+        if not ln.startswith("basis "):
+            continue
+        kv = dict(p.split("=", 1) for p in ln.split()[2:])
+        G, D = int(kv["group"]), int(kv["D"])
+        q = np.array([_hexf(r) for r in kv["q"].split(";")], dtype=np.float64)
+        assert np.array_equal(q.astype(np.float16).astype(np.float64), q), ln   # fp16-exact inputs
+        basis = np.array(_hexf(kv["col"]), dtype=np.float64).reshape(1, D, 1)
+        assert np.array_equal(basis.astype(np.float32).astype(np.float64), basis), ln
+        qs, qscale = oracle.query_sketch(q.astype(np.float16).reshape(1, G, D), basis.astype(np.float32), G)
+        assert qs[0].tolist() == [int(x) for x in kv["expect"].split(",")], ln
+        assert int(np.asarray(qscale[0], dtype=np.float32).view(np.uint32)) == int(kv["qscale"], 16), ln
+        n += 1
+    assert n == 2
+
+
+def test_query_sketch_orthonormal_round_trip():
+    """A query in the span of an orthonormal basis projects back onto its
+    coordinates.  The basis is a 4x4 Hadamard matrix / 2 with its columns
+    permuted (orthonormal, entries +-0.5, not symmetric, so projecting with the
+    transposed basis fails); every product and sum is exact in fp32."""
+    H = 0.5 * np.array([[1, 1, 1, 1], [1, -1, 1, -1], [1, 1, -1, -1], [1, -1, -1, 1]], dtype=np.float64)
+    Bm = H[:, [2, 0, 3, 1]]
+    assert np.allclose(Bm.T @ Bm, np.eye(4)) and not np.allclose(Bm, Bm.T)
+    c = np.array([8.0, -4.0, 2.0, 6.0])
+    q = (Bm @ c).reshape(1, 1, 4)        # the query whose coordinates are c
+    qs, qscale = oracle.query_sketch(q.astype(np.float16), Bm.reshape(1, 4, 4).astype(np.float32), 1)
+    # s = c exactly; amax = 8, qscale = fp32(8/127); codes rint(c * 127/8):
+    # 127, -63.5 -> -64 (half to even), 31.75 -> 32, 95.25 -> 95
+    assert float(qscale[0]) == float(np.float32(8.0) / np.float32(127.0))
+    assert qs[0].tolist() == [127, -64, 32, 95]
 
 
 def test_query_sketch_scale_invariance():
@@ -419,6 +463,83 @@ def test_host_dequant_invariants():
             assert np.all(np.sign(r) * np.sign(c) >= 0)     # sign preserved
 
 
+def _rint_half_even(x: Fraction) -> int:
+    n = x.numerator // x.denominator
+    r = x - n
+    if r > Fraction(1, 2) or (r == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return n
+
+
+def _host_row(codes, gscales):
+    return np.concatenate([synth.pack_int4(torch.from_numpy(np.asarray(codes, np.int8))).numpy(),
+                           np.array(gscales, dtype=np.float16).view(np.uint8)])
+
+
+def test_tier_attention_equals_plain_cache():
+    """oracle.tier_attention over host records equals oracle.sparse_attention
+    over a plain int8 cache holding the rows those records decode to, bit for
+    bit.  Group scales 127 * 2^-j make the fetched row scale s' = fp16(127 * 7 /
+    127) = 7 exactly, so the expected int8 codes rint(c * g_j / 7) are computed
+    here in exact rational arithmetic, independently of host_row_dequant."""
+    rng = np.random.default_rng(31)
+    n_kv, G, D, T, S, L = 2, 2, 256, 40, 4, 6
+    ng = D // 64
+    gs = [127.0 * 2.0 ** -j for j in range(ng)]
+    rb = D // 2 + 2 * ng
+    records = np.zeros((T, n_kv, 2 * rb), dtype=np.uint8)
+    k8 = np.zeros((T, n_kv, D), np.int8)
+    v8 = np.zeros((T, n_kv, D), np.int8)
+    ks = np.zeros((T, n_kv), np.float16)
+    vs = np.zeros((T, n_kv), np.float16)
+    for p in range(S, T - L):
+        for h in range(n_kv):
+            for part, dst, sdst in ((0, k8, ks), (1, v8, vs)):
+                c = rng.integers(-7, 8, size=D)
+                records[p, h, part * rb:(part + 1) * rb] = _host_row(c, gs)
+                dst[p, h] = [max(-127, min(127, _rint_half_even(Fraction(int(c[i])) * Fraction(gs[i // 64]) / 7)))
+                             for i in range(D)]
+                sdst[p, h] = 7.0
+    # resident rows: the sinks, then the tail in position order
+    res_k = rng.integers(-127, 128, size=(S + L, n_kv, D)).astype(np.int8)
+    res_v = rng.integers(-127, 128, size=(S + L, n_kv, D)).astype(np.int8)
+    res_ks = rng.uniform(0.001, 0.02, size=(S + L, n_kv)).astype(np.float16)
+    res_vs = rng.uniform(0.001, 0.02, size=(S + L, n_kv)).astype(np.float16)
+    pos = list(range(S)) + list(range(T - L, T))
+    for r, p in enumerate(pos):
+        k8[p], v8[p], ks[p], vs[p] = res_k[r], res_v[r], res_ks[r], res_vs[r]
+    q = rng.standard_normal((n_kv * G, D)).astype(np.float16)
+    sm = D ** -0.5
+    for idx in (np.arange(T), np.array([0, 3, 4, 5, 17, 33, 34, 39]), np.array([6, 20, 21, 33])):
+        a = oracle.tier_attention(q, records, res_k, res_v, res_ks, res_vs, idx, T, S, L, sm, G, D)
+        b = oracle.sparse_attention(q, k8, v8, ks, vs, idx, sm, G, "i8")
+        assert np.array_equal(a, b)
+
+
+def test_tier_attention_position_rows():
+    """Hand-worked map from positions to rows (T = 12, S = 2, L = 3, D = 64,
+    one head): attending a single position returns its V row exactly.
+    Resident rows 0..4 hold the sinks 0, 1 and the tail 9, 10, 11, each V row
+    the constant 10 + row (scale 1); middle positions 2..8 come from host
+    records with V codes c = p - 5 and group scale 127, decoded with s' = 7 to
+    rint(c * 127 / 7) = 18c for |c| <= 3 (18.14c rounded), so value 7 * 18c.
+    K codes are all 0 (equal logits)."""
+    T, S, L, D = 12, 2, 3, 64
+    rb = D // 2 + 2
+    records = np.zeros((T, 1, 2 * rb), dtype=np.uint8)
+    for p in range(S, T - L):
+        records[p, 0, :rb] = _host_row(np.zeros(D, np.int8), [127.0])
+        records[p, 0, rb:] = _host_row(np.full(D, p - 5, np.int8), [127.0])
+    res_k = np.zeros((S + L, 1, D), np.int8)
+    res_v = np.array([np.full((1, D), 10 + r, np.int8) for r in range(S + L)])
+    ones = np.ones((S + L, 1), np.float16)
+    q = np.ones((1, D), np.float16)
+    expect = {0: 10, 1: 11, 2: -378, 3: -252, 4: -126, 5: 0, 6: 126, 7: 252, 8: 378, 9: 12, 10: 13, 11: 14}
+    for p, val in expect.items():
+        o = oracle.tier_attention(q, records, res_k, res_v, ones, ones, np.array([p]), T, S, L, 0.125, 1, D)
+        assert np.all(o == val), (p, o[0, :4])
+
+
 def test_clock_fixture():
     lines = list(_lines("clock_trace.txt"))
     n = int(lines[0].split()[1])
@@ -432,6 +553,27 @@ def test_clock_fixture():
         got, h, m = tier.step(picks, int(s))
         assert got.tolist() == [int(x) for x in slots.split()], ln
         assert (h, m) == (int(hits), int(misses))
+
+
+def test_clock_fixture_window_two():
+    """Hand trace with W = 2 (tests/golden/clock_trace_w2.txt): slots used in
+    the previous step stay pinned, which changes the victims of step 3 against
+    W = 1, and a '>=' window test would pin every slot at step 2."""
+    lines = list(_lines("clock_trace_w2.txt"))
+    head = lines[0].split()
+    assert head[0] == "slots" and head[2] == "window"
+    tier = oracle.ClockTier(int(head[1]), 100, window=int(head[3]))
+    for ln in lines[1:]:
+        if ln.startswith("final"):
+            assert tier.pos.tolist() == [int(x) for x in ln.split()[1:]]
+            continue
+        s, picks, slots, hits, misses = (p.strip() for p in ln.split("|"))
+        picks = np.array(sorted(int(x) for x in picks.split()))
+        got, h, m = tier.step(picks, int(s))
+        expect = dict(zip((int(x) for x in sorted(int(y) for y in ln.split("|")[1].split())),
+                          (int(x) for x in slots.split())))
+        assert got.tolist() == [expect[int(p)] for p in picks], ln
+        assert (h, m) == (int(hits), int(misses)), ln
 
 
 def test_clock_invariants_drifting_workload():
@@ -497,6 +639,14 @@ def test_append_fixture():
             for r, c in enumerate(cols):
                 basis[0, c, r] = 1.0
             packed, s16 = oracle.append.key_sketch(k, basis)
+            assert int(np.array([s16]).view(np.uint16)[0]) == int(f["scale"], 16), ln
+            assert packed.tolist() == [int(f["bytes"], 16)], ln
+        elif ln.startswith("sketchb "):
+            k = np.array([float(v) for v in f["k"].split(",")], dtype=np.float16)[None]
+            cols = [_hexf(f["col0"]), _hexf(f["col1"])]
+            basis = np.array(cols, dtype=np.float64).T[None]          # [1][D][2]
+            assert np.array_equal(basis.astype(np.float32).astype(np.float64), basis), ln
+            packed, s16 = oracle.append.key_sketch(k, basis.astype(np.float32))
             assert int(np.array([s16]).view(np.uint16)[0]) == int(f["scale"], 16), ln
             assert packed.tolist() == [int(f["bytes"], 16)], ln
 

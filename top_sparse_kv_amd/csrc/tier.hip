@@ -5,8 +5,8 @@
 // in pinned host RAM at int4 (64-dim groups, fp16 scales, 272 B per
 // token-head), turned back into int8 rows when fetched; the GPU keeps the
 // sinks, the recent tail and a hot buffer of 2.5% of the tokens managed by
-// windowed CLOCK; hot-buffer misses read only the picked rows from pinned
-// memory over PCIe.  Page "3.14M Context on 3x 3090: The Power of an
+// windowed CLOCK; a token missing from the hot buffer is fetched alone, by a
+// direct GPU read of its host record across PCIe.  Page "3.14M Context on 3x 3090: The Power of an
 // Architecture That Puts KV Cache in Host RAM", sections "No Need to Rewrite
 // the Kernel": the GPU reads host-mapped memory directly (zero copy), which
 // needs no per-layer host synchronization and keeps the step capturable.
@@ -237,28 +237,40 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
     uint32_t v = 0, need = (uint32_t)nm;
     // ages relative to the oldest candidate: leading rounds whose digit is 0
     // for every candidate are skipped (usually one round is left)
-    uint32_t umin = 0xFFFFFFFFu, umax = 0u;
+    uint32_t umin = 0xFFFFFFFFu, umax = 0u, ncand = 0u;
     for (int j = threadIdx.x; j < n_slots; j += blockDim.x)
       if (s_last[j] < step) {
         const uint32_t u = (uint32_t)(s_last[j] - kNoStep);
         umin = min(umin, u);
         umax = max(umax, u);
+        ++ncand;
       }
     umin = ~wave_max(~umin);
     umax = wave_max(umax);
+    ncand = wave_sum(ncand);
     if (lane == 0) {
       s_hist[wave] = umin;
       s_hist[16 + wave] = umax;
+      s_hist[32 + wave] = ncand;
     }
     __syncthreads();
+    ncand = 0u;
     for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
       umin = min(umin, s_hist[w]);
       umax = max(umax, s_hist[16 + w]);
+      ncand += s_hist[32 + w];
     }
     __syncthreads();
     const uint32_t span = umax >= umin ? umax - umin : 0u;
     const int top_bits = span ? 32 - __clz((int)span) : 0;
-    if (nm > 0) {
+    // Fewer candidates than misses (pick lists of one step that do not fit
+    // together, or a reused step number): every candidate is a victim, taken
+    // in slot order, and the misses left over are flagged below -- the slot
+    // table that remains does not depend on anything but the inputs.
+    if (nm > 0 && ncand <= (uint32_t)nm) {
+      v = 0xFFFFFFFFu;
+      need = 0u;
+    } else if (nm > 0) {
       for (int shift = 24; shift >= 0; shift -= 8) {
         if (shift > 0 && shift >= top_bits) continue;   // digit 0 for every candidate
         for (int i = threadIdx.x; i < 256; i += blockDim.x) s_hist[i] = 0u;
