@@ -372,19 +372,22 @@ def test_fused_select_all_keys_equal():
 
 
 def test_fused_select_sample_overshoot():
-    """Large keys planted only on the sampled lines make the threshold bucket
-    too high: fewer candidates than the budget survive it, and the select
-    recomputes every key of the sequence (the exact fallback)."""
+    """Large keys planted on three of the sixteen keys of every sampled line
+    make the threshold too high: every sampled workgroup's largest digits are
+    planted ones, yet the planted keys are fewer than the budget, so the
+    select recomputes every key of the sequence (the exact fallback)."""
     skv = need_gpu()
     c = _cfg2(1, 120_000, [120_000], n_needles=0, device="cuda")
     qs = np.zeros((1, 256), dtype=np.int8)
     qs[0, :] = 1
     n = c.lens[0] - c.S - c.L
-    s = min(max(n // (4 * c.k), 1), 64)          # the sample takes every s-th line of 16
+    s = max(n // (4 * c.k), 1)                    # the sample takes every s-th line of 16
+    lines = (n + 15) // 16
+    nsl = (lines + s - 1) // s
     codes = c.codes.cpu().numpy()
     scale = c.sk_scale.cpu().numpy().view(np.uint16).copy()
-    sampled = np.array([c.S + 16 * s * j + e for j in range(40) for e in range(16)])
-    assert s > 1 and sampled.size >= 400
+    sampled = np.array([c.S + 16 * s * j + e for j in range(nsl) for e in range(3)])
+    assert s == 14 and 1000 < sampled.size < c.k
     # all codes +7 (nibbles 0x7 in both halves): dot = 7 * 256 with qs = 1
     codes[0, sampled] = 0x77
     scale[0, sampled] = np.float16(8.0).view(np.uint16)

@@ -336,7 +336,7 @@ skv_status sparsekv_score_topk(const skv_layer_desc* d, const int32_t* ctx_len,
   if (d->index_mode == SKV_INDEX_SKETCH_INT4 && !index_scale)
     return set_error(SKV_ERR_INVALID, "score_topk: token mode needs index_scale");
   if (((uintptr_t)index_keys) % 16) return set_error(SKV_ERR_INVALID, "score_topk: index_keys not 16-byte aligned");
-  return launched(launch_score_select(*d, ctx_len, index_query, nullptr, nullptr, index_keys,
+  return launched(launch_score_select(*d, ctx_len, index_query, nullptr, nullptr, nullptr, nullptr, index_keys,
                                       index_scale, idx, n_sel, ws, L, (hipStream_t)stream),
                   "score_topk");
 }
@@ -373,10 +373,10 @@ skv_status sparsekv_step(const skv_layer_desc* d, const int32_t* ctx_len, const 
     return set_error(SKV_ERR_INVALID, "step: token mode needs basis, qs, qs_scale and index_scale");
   if (!tok && !index_query) return set_error(SKV_ERR_INVALID, "step: block mode needs index_query");
   hipStream_t st = (hipStream_t)stream;
-  // token mode: the projection here, its quantization in the sample kernel
+  // token mode: the projection here, its quantization in the front kernel
   hipError_t e = tok ? launch_qsketch_proj(*d, q, basis, ws, L, st) : hipSuccess;
   if (e == hipSuccess)
-    e = launch_score_select(*d, ctx_len, tok ? nullptr : index_query, tok ? qs : nullptr,
+    e = launch_score_select(*d, ctx_len, tok ? nullptr : index_query, q, basis, tok ? qs : nullptr,
                             tok ? qs_scale : nullptr, index_keys, index_scale, idx, n_sel, ws, L, st);
   if (e == hipSuccess) e = launch_attend(*d, q, *kv, idx, n_sel, sm_scale, out, ws, L, st);
   return launched(e, "step");

@@ -65,11 +65,15 @@ __device__ __forceinline__ int ctx_of_query(const int32_t* ctx_len, int v, int m
 }
 
 // Sample: whole lines of 16 candidates, one line in every s; about 4k lines'
-// worth of keys, at most about 16K (every key when the sequence is short).
+// worth of keys, at most about 16K, and at least every (k/256)-th line, so
+// that a sample never holds more than about 256 keys of the top k expected
+// (every key when the sequence is short and k <= 256).
 __host__ __device__ __forceinline__ int sample_stride(int n, int k) {
   int s = n / (4 * k);
   const int s2 = (n + kSampleCap - 1) / kSampleCap;
+  const int s3 = (k + 255) / 256;
   s = s > s2 ? s : s2;
+  s = s > s3 ? s : s3;
   return s < 1 ? 1 : s;
 }
 __host__ __device__ __forceinline__ int sample_lines(int n, int k) {
@@ -81,13 +85,42 @@ __host__ __device__ __forceinline__ int sample_lines(int n, int k) {
 // Samples that must lie at or above the threshold bucket: k when every key is
 // sampled, else the expected share of the top k plus 25%, four standard
 // deviations and 8 (the sample only steers speed; the select stays exact).
-__device__ __forceinline__ uint32_t sample_need(int n, int k) {
+// The stride rule above keeps it at most about 420.
+__host__ __device__ __forceinline__ uint32_t sample_need(int n, int k) {
   const int s = sample_stride(n, k);
   if (s == 1) return (uint32_t)k;
   const int lines = (n + kLineKeys - 1) / kLineKeys;
   const int nsl = (lines + s - 1) / s;
   const float e = (float)k * (float)nsl / (float)lines;
   return (uint32_t)ceilf(1.25f * e + 4.0f * sqrtf(e) + 8.0f);
+}
+
+// ---------------------------------------------------------------------------
+// front of the fused step: the sample is read by workgroups of kFrontThreads,
+// each covering kFrontLines<LANES> consecutive sample lines, and each leaves
+// a summary row of its largest sampled digits (summary_q of them); the
+// threshold is the need-th largest digit over all rows of a sequence
+// ---------------------------------------------------------------------------
+constexpr int kFrontThreads = 512;
+// loads per lane of a front workgroup: 8 (a workgroup covers 32 lines or more
+// for lanes <= 8), 16 for wider keys (16 lines at 32 lanes)
+__host__ __device__ constexpr int front_unroll(int lanes) { return lanes >= 16 ? 16 : 8; }
+__host__ __device__ constexpr int front_lines(int lanes) {   // sample lines per front workgroup
+  return (kFrontThreads / 64) * front_unroll(lanes) * (64 / lanes) / kLineKeys;
+}
+__host__ __device__ __forceinline__ int front_wgs(int nsl, int lanes) {
+  return (nsl + front_lines(lanes) - 1) / front_lines(lanes);
+}
+// digits kept per front workgroup: 1.5 times its share of the needed samples
+// plus 8, rounded up to a multiple of 8, at most its sample (a workgroup
+// holding more of the sequence's top samples than that only lowers the
+// threshold, i.e. adds candidates).  With the stride rule above, all rows of a
+// sequence hold at most 1024 digits (2048 with 32-lane keys).
+__host__ __device__ __forceinline__ int summary_q(uint32_t need, int nwg, int lanes) {
+  int q = (int)((3u * need + 2u * (uint32_t)nwg - 1u) / (2u * (uint32_t)nwg)) + 8;
+  q = (q + 7) & ~7;
+  const int m = front_lines(lanes) * kLineKeys;
+  return q < m ? q : m;
 }
 
 // ---------------------------------------------------------------------------
@@ -262,7 +295,16 @@ struct SketchSrc {
   // qrow: the sequence's 32*N int8 query codes (global or LDS)
   __device__ __forceinline__ void init(const void* qrow, const void* ik, const uint16_t* isc, int b,
                                        int max_ctx, int sub) {
+    init_data(ik, isc, b, max_ctx, sub);
+    init_query(qrow, sub);
+  }
+  __device__ __forceinline__ void init_data(const void* ik, const uint16_t* isc, int b, int max_ctx,
+                                            int sub) {
     constexpr int TB = 16 * N;
+    cbase = reinterpret_cast<const uint8_t*>(ik) + (size_t)b * max_ctx * TB + 16 * sub;
+    sbase = isc + (size_t)b * max_ctx;
+  }
+  __device__ __forceinline__ void init_query(const void* qrow, int sub) {
     // this lane's 32 query codes: even code positions of each 8-code word in
     // qe, odd ones in qo (matching the low / high nibbles of the code bytes)
     const uint8_t* qp = reinterpret_cast<const uint8_t*>(qrow) + 32 * sub;
@@ -277,8 +319,6 @@ struct SketchSrc {
       qe[m] = e;
       qo[m] = o;
     }
-    cbase = reinterpret_cast<const uint8_t*>(ik) + (size_t)b * max_ctx * TB + 16 * sub;
-    sbase = isc + (size_t)b * max_ctx;
   }
   // raw data of candidate at position p (token index)
   __device__ __forceinline__ u32x4 load(int p) const {
@@ -315,13 +355,19 @@ struct PooledSrc {
   const uint16_t* kb;
 
   // qrow: the sequence's 8*N bf16 indexer query values
-  __device__ __forceinline__ void init(const void* qrow, const void* ik, const uint16_t*, int b,
+  __device__ __forceinline__ void init(const void* qrow, const void* ik, const uint16_t* isc, int b,
                                        int max_ctx, int sub) {
+    init_data(ik, isc, b, max_ctx, sub);
+    init_query(qrow, sub);
+  }
+  __device__ __forceinline__ void init_data(const void* ik, const uint16_t*, int b, int max_ctx, int sub) {
     constexpr int ID = 8 * N;
+    kb = reinterpret_cast<const uint16_t*>(ik) + (size_t)b * (max_ctx / 4) * ID + 8 * sub;
+  }
+  __device__ __forceinline__ void init_query(const void* qrow, int sub) {
     const uint16_t* q = reinterpret_cast<const uint16_t*>(qrow);
 #pragma unroll
     for (int e = 0; e < 8; ++e) qd[e] = (double)bf16_bits_to_float(q[8 * sub + e]);
-    kb = reinterpret_cast<const uint16_t*>(ik) + (size_t)b * (max_ctx / 4) * ID + 8 * sub;
   }
   __device__ __forceinline__ u32x4 load(int p) const {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + (size_t)p * (8 * N)));
@@ -369,6 +415,84 @@ __device__ __forceinline__ float quantize_sketch(const float* sp, int n, int8_t*
   if (ok1) q8[t + nb] = code(v1);
   __syncthreads();
   return scale;
+}
+
+// ---------------------------------------------------------------------------
+// the need-th largest of m 16-bit digits, by one wave
+// ---------------------------------------------------------------------------
+// LDS operations of one wave complete in issue order; this keeps the compiler
+// from reordering them across the point (no barrier: other waves may be gone)
+__device__ __forceinline__ void wave_lds_order() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// dg: m digits (global or LDS), 16-byte aligned; 0 marks an empty slot.  Lane
+// l holds chunks l, l+64, ... of 8 digits (V chunks per lane, m <= 512*V).
+// hist: 256 words of LDS owned by this wave.  Two passes of a 256-bin
+// histogram (high byte, then the low byte inside the chosen high-byte bin),
+// each scanned from the top by a wave prefix sum.  Returns the largest t with
+// at least `need` digits >= t, or 0 when fewer than need digits are nonzero
+// (keep everything).  Every lane of the wave must call it.
+template <int V>
+__device__ __forceinline__ uint32_t wave_kth_largest(const uint16_t* dg, int m, uint32_t need,
+                                                     uint32_t* hist) {
+  const int lane = threadIdx.x & 63;
+  uint32_t d[8 * V];
+#pragma unroll
+  for (int c = 0; c < V; ++c) {
+    const int ch = c * 64 + lane, nch = (m + 7) / 8;
+    u32x4 v = reinterpret_cast<const u32x4*>(dg)[min(ch, nch - 1)];   // unconditional
+    if (ch >= nch) v = (u32x4){0u, 0u, 0u, 0u};
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) d[8 * c + e] = (w4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+  }
+  uint32_t tau = 0, rem = need;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hist[4 * lane + j] = 0u;
+    wave_lds_order();
+#pragma unroll
+    for (int e = 0; e < 8 * V; ++e) {
+      const uint32_t x = d[e];
+      if (pass == 0) {
+        if (x) atomicAdd(&hist[x >> 8], 1u);
+      } else if (x && (x >> 8) == (tau >> 8)) {
+        atomicAdd(&hist[x & 255u], 1u);
+      }
+    }
+    wave_lds_order();
+    // lane l owns bins 255-4l .. 252-4l, counted from the top
+    uint32_t c[4], t = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      c[j] = hist[255 - 4 * lane - j];
+      t += c[j];
+    }
+    const uint32_t incl = wave_incl_scan(t);
+    const uint64_t hit = __ballot(incl >= rem);
+    if (!hit) return 0u;                       // fewer than need nonzero digits
+    const int l = (int)__ffsll((unsigned long long)hit) - 1;
+    uint32_t cum = incl - t, bin = 0, before = 0;
+    bool found = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (!found && cum + c[j] >= rem) {
+        found = true;
+        bin = (uint32_t)(255 - 4 * lane - j);
+        before = cum;
+      }
+      cum += c[j];
+    }
+    bin = (uint32_t)__builtin_amdgcn_readlane((int)bin, l);
+    before = (uint32_t)__builtin_amdgcn_readlane((int)before, l);
+    tau = pass == 0 ? bin << 8 : (tau & 0xFF00u) | bin;
+    rem -= before;
+    wave_lds_order();
+  }
+  return tau;
 }
 
 // ---------------------------------------------------------------------------

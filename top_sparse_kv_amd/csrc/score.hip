@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
   // otherwise one segment per wave
   const int seg = TRANS || SPLIT ? blockIdx.x : blockIdx.x * (kThreads / 64) + wave;
   const int i0 = seg * seg_items;
-  if (i0 >= n) return;   // workgroup-uniform (transposed) or wave-uniform (no barrier)
+  if (i0 >= n) return;   // workgroup-uniform (transposed) or wave-uniform (no barrier below)
   const int i1 = min(n, i0 + seg_items);
   const int first = TRANS || SPLIT ? i0 + PER_IT * wave : i0;
   const int sub = lane % N, tw = lane / N;
@@ -253,66 +253,126 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
   if (COLLECT && lane == 0) segcnt[(size_t)b * n_seg + seg] = cnt;
 }
 
-// Sampled keys: line j of the sample is candidates [16*s*j, 16*s*j + 16).
-// Each wave computes PER_IT/16 lines with one batch of loads and writes their
-// digits.  In the fused step the query sketch is quantized here first (from
-// the fp32 sketch in the workspace) and workgroup 0 of each sequence writes
-// it out.
+// Front of the fused step: the sample of the threshold estimate.  Workgroup w
+// of sequence b reads sample lines [w*LPG, (w+1)*LPG) (line j = candidates
+// [16*s*j, 16*s*j + 16)), issuing those loads first.  Token mode with
+// FROM_PROJ: the fp32 query sketch in the workspace is quantized here (one
+// int8 scale per sequence) and workgroup 0 writes it out.  Then the 16-bit
+// digits of its sampled keys, and a summary row: the q largest of them (as a
+// multiset, unordered; empty sample slots count as digit 0).  The threshold
+// kernel takes the need-th largest digit over the rows of a sequence; a row
+// holding more of the sequence's top samples than q can only lower that
+// threshold (more candidates).
 template <class Src, bool FROM_PROJ>
-__global__ __launch_bounds__(kThreads) void sample_kernel(
+__global__ __launch_bounds__(kFrontThreads) void front_kernel(
     const void* __restrict__ iq, const float* __restrict__ sproj, int8_t* __restrict__ qs_out,
-    float* __restrict__ qscale_out, int nq, const void* __restrict__ ik,
-    const uint16_t* __restrict__ isc, const int32_t* __restrict__ ctx_len,
-    uint16_t* __restrict__ sdig, int n_samp, int mode, int max_ctx, int S, int k, int L) {
-  constexpr int N = Src::LANES, IPW = 64 / N, PER_IT = kUnroll * IPW;
-  constexpr int LPW = PER_IT / kLineKeys;          // sample lines per wave
+    float* __restrict__ qscale_out, const void* __restrict__ ik, const uint16_t* __restrict__ isc,
+    const int32_t* __restrict__ ctx_len, uint16_t* __restrict__ summ, int summ_stride, int mode,
+    int max_ctx, int S, int k, int L) {
+  constexpr int N = Src::LANES, IPW = 64 / N, FU = front_unroll(N), PER_IT = FU * IPW;
+  constexpr int LPW = PER_IT / kLineKeys;                   // sample lines per wave
+  constexpr int NWV = kFrontThreads / 64;
+  constexpr int LPG = LPW * NWV;                            // sample lines per workgroup
+  constexpr int MW = LPG * kLineKeys;                       // sample slots per workgroup
+  constexpr int NQ = 32 * N;                                // int8 query sketch values (token mode)
+  static_assert(LPG == front_lines(N), "front geometry");
   __shared__ int8_t q8[512];
-  __shared__ uint32_t red[16];
-  const int b = blockIdx.y;
-  const void* qrow;
-  if constexpr (FROM_PROJ) {
-    const float scale = quantize_sketch(sproj + (size_t)b * nq, nq, q8, red);
-    if (blockIdx.x == 0) {
-      for (int i = threadIdx.x; i < nq; i += kThreads) qs_out[(size_t)b * nq + i] = q8[i];
-      if (threadIdx.x == 0) qscale_out[b] = scale;
-    }
-    qrow = q8;
-  } else {
-    qrow = reinterpret_cast<const uint8_t*>(iq) + (size_t)b * Src::QROW;
-  }
-  const Range r = cand_range(mode, ctx_of(ctx_len, b, max_ctx), S, k, L);
-  if (r.dense) return;
-  const int s = sample_stride(r.n, k);
-  const int nsl = sample_lines(r.n, k);
+  __shared__ __attribute__((aligned(16))) uint16_t s_dig[MW];
+  __shared__ uint32_t s_red[32];
+  __shared__ uint32_t s_hist[256];
+  const int b = blockIdx.y, w = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int j0 = (blockIdx.x * (kThreads / 64) + wave) * LPW;
-  if (j0 >= nsl) return;   // wave-uniform; no barrier below
+  const Range r = cand_range(mode, ctx_of(ctx_len, b, max_ctx), S, k, L);
+  const int s = r.dense ? 1 : sample_stride(r.n, k);
+  const int nsl = r.dense ? 0 : sample_lines(r.n, k);
+  const int nwg = front_wgs(nsl, N);
+  if (w >= nwg && !(FROM_PROJ && w == 0)) return;   // workgroup-uniform
   const int sub = lane % N, tw = lane / N;
   Src src;
-  src.init(qrow, ik, isc, b, max_ctx, sub);
-  u32x4 w[kUnroll];
-  uint32_t ax[kUnroll];
-  bool ok[kUnroll];
+  src.init_data(ik, isc, b, max_ctx, sub);
+  // the sample loads go out first (clamped: past the sample they re-read a
+  // valid candidate, dropped below)
+  const int j0 = (w * NWV + wave) * LPW;
+  u32x4 wv[FU];
+  uint32_t ax[FU];
+  bool ok[FU];
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
+  for (int u = 0; u < FU; ++u) {
     const int o = u * IPW + tw;
     const int j = j0 + o / kLineKeys;
     const int i = j * s * kLineKeys + o % kLineKeys;
     ok[u] = j < nsl && i < r.n;
-    const int ic = ok[u] ? i : r.n - 1;
-    w[u] = src.load(r.lo + ic);
+    const int ic = ok[u] ? i : (r.n > 0 ? r.n - 1 : 0);
+    wv[u] = src.load(r.lo + ic);
     ax[u] = src.load_aux(r.lo + ic);
   }
-  uint16_t* dg = sdig + (size_t)b * n_samp * kLineKeys;
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const int o = u * IPW + tw;
-    const int j = j0 + o / kLineKeys;
-    uint32_t dig;
-    if constexpr (Src::HAS_AUX) dig = src.digit_of(src.dot(w[u]), ax[u]);
-    else dig = key_digit16(src.key(w[u], ax[u]));
-    if (sub == 0 && j < nsl) dg[j * kLineKeys + o % kLineKeys] = ok[u] ? (uint16_t)dig : (uint16_t)0u;
+  const void* qrow;
+  if constexpr (FROM_PROJ) {
+    const float scale = quantize_sketch(sproj + (size_t)b * NQ, NQ, q8, s_red);
+    if (w == 0) {
+      for (int i = threadIdx.x; i < NQ; i += kFrontThreads) qs_out[(size_t)b * NQ + i] = q8[i];
+      if (threadIdx.x == 0) qscale_out[b] = scale;
+    }
+    if (w >= nwg) return;   // workgroup-uniform: dense sequence, sketch written
+    qrow = q8;
+  } else {
+    qrow = reinterpret_cast<const uint8_t*>(iq) + (size_t)b * Src::QROW;
   }
+  src.init_query(qrow, sub);
+#pragma unroll
+  for (int u = 0; u < FU; ++u) {
+    uint32_t dig;
+    if constexpr (Src::HAS_AUX) dig = src.digit_of(src.dot(wv[u]), ax[u]);
+    else dig = key_digit16(src.key(wv[u], ax[u]));
+    if (sub == 0) s_dig[wave * PER_IT + u * IPW + tw] = ok[u] ? (uint16_t)dig : (uint16_t)0u;
+  }
+  // the q largest digits of the workgroup, by wave 0: tau = the q-th largest,
+  // the digits above it compacted by a wave prefix sum, then tau repeated
+  const int qw = summary_q(sample_need(r.n, k), nwg, N);
+  __syncthreads();
+  if (wave != 0) return;
+  constexpr int V = (MW + 511) / 512;   // 8-digit chunks per lane
+  const uint32_t tau = wave_kth_largest<V>(s_dig, MW, (uint32_t)qw, s_hist);
+  uint16_t* row = summ + (size_t)b * summ_stride + (size_t)w * qw;
+  uint32_t at = 0;
+#pragma unroll
+  for (int c = 0; c < V; ++c) {
+    const int ch = c * 64 + lane;
+    const u32x4 v = ch < MW / 8 ? reinterpret_cast<const u32x4*>(s_dig)[ch] : (u32x4){0u, 0u, 0u, 0u};
+    const uint32_t dw[4] = {v.x, v.y, v.z, v.w};
+    uint32_t gt = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gt += (uint32_t)(((dw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) > tau);
+    const uint32_t incl = wave_incl_scan(gt);
+    uint32_t o = at + incl - gt;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t x = (dw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+      if (x > tau) row[o++] = (uint16_t)x;
+    }
+    at += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  }
+  for (int i = (int)at + lane; i < qw; i += 64) row[i] = (uint16_t)tau;
+}
+
+// Threshold digit of each sequence: the need-th largest digit over the
+// summary rows the front kernel left (at most 2048 digits, summary_q), by one
+// wave per sequence.
+template <int LANES>
+__global__ __launch_bounds__(64) void summary_beta_kernel(const uint16_t* __restrict__ summ,
+                                                          int summ_stride,
+                                                          const int32_t* __restrict__ ctx_len,
+                                                          TopkState* __restrict__ state, int mode,
+                                                          int max_ctx, int S, int k, int L) {
+  const int b = blockIdx.x;
+  const Range r = cand_range(mode, ctx_of(ctx_len, b, max_ctx), S, k, L);
+  if (r.dense) return;
+  const int nwg = front_wgs(sample_lines(r.n, k), LANES);
+  const uint32_t need = sample_need(r.n, k);
+  const int m = nwg * summary_q(need, nwg, LANES);
+  __shared__ uint32_t hist[256];
+  const uint32_t beta = wave_kth_largest<4>(summ + (size_t)b * summ_stride, min(m, 2048), need, hist);
+  if (threadIdx.x == 0) state[b].beta = beta;
 }
 
 // Threshold digit of each (virtual) sequence from its sampled digits.  With
@@ -333,9 +393,10 @@ __global__ __launch_bounds__(1024) void beta_kernel(const uint16_t* __restrict__
 
 template <class Src>
 hipError_t launch_token_or_block(const skv_layer_desc& d, const int32_t* ctx_len, const void* iq,
-                                 int8_t* qs_out, float* qscale_out, const void* ik,
-                                 const uint16_t* isc, double* keys, void* ws, const WsLayout* Lw,
-                                 uint32_t* flags, bool collect, hipStream_t st) {
+                                 const void* q, const float* basis, int8_t* qs_out,
+                                 float* qscale_out, const void* ik, const uint16_t* isc, double* keys,
+                                 void* ws, const WsLayout* Lw, uint32_t* flags, bool collect,
+                                 hipStream_t st) {
   const int mode = d.index_mode;
   const int S = mode == SKV_INDEX_SKETCH_INT4 ? d.n_sink : 0;
   const int L = mode == SKV_INDEX_SKETCH_INT4 ? d.n_tail : 0;
@@ -349,21 +410,21 @@ hipError_t launch_token_or_block(const skv_layer_desc& d, const int32_t* ctx_len
                        L, n_seg, seg_items);
     return hipGetLastError();
   }
-  constexpr int LPG = kUnroll * (64 / Src::LANES) / kLineKeys * (kThreads / 64);
-  const dim3 sgrid((Lw->n_samp + LPG - 1) / LPG, d.batch);
-  uint16_t* sdig = ws_ptr<uint16_t>(ws, Lw->sdig);
-  const int nq = d.n_kv_heads * d.rank;
+  // the front kernel: grid wide enough for the largest sample of a sequence
+  const dim3 fgrid(front_wgs(Lw->n_samp, Src::LANES), d.batch);
+  uint16_t* summ = ws_ptr<uint16_t>(ws, Lw->sdig);
+  const int summ_stride = Lw->summ_stride;
   if (qs_out)
-    hipLaunchKernelGGL((sample_kernel<Src, true>), sgrid, dim3(kThreads), 0, st, iq,
-                       ws_ptr<const float>(ws, Lw->sproj), qs_out, qscale_out, nq, ik, isc, ctx_len,
-                       sdig, Lw->n_samp, mode, d.max_ctx, S, d.topk, L);
+    hipLaunchKernelGGL((front_kernel<Src, true>), fgrid, dim3(kFrontThreads), 0, st, nullptr,
+                       ws_ptr<const float>(ws, Lw->sproj), qs_out, qscale_out, ik, isc, ctx_len, summ,
+                       summ_stride, mode, d.max_ctx, S, d.topk, L);
   else
-    hipLaunchKernelGGL((sample_kernel<Src, false>), sgrid, dim3(kThreads), 0, st, iq, nullptr,
-                       nullptr, nullptr, nq, ik, isc, ctx_len, sdig, Lw->n_samp, mode, d.max_ctx, S,
+    hipLaunchKernelGGL((front_kernel<Src, false>), fgrid, dim3(kFrontThreads), 0, st, iq, nullptr,
+                       nullptr, nullptr, ik, isc, ctx_len, summ, summ_stride, mode, d.max_ctx, S,
                        d.topk, L);
   TopkState* state = ws_ptr<TopkState>(ws, Lw->state);
-  hipLaunchKernelGGL(beta_kernel, dim3(d.batch), dim3(1024), 0, st, sdig, Lw->n_samp, ctx_len, state,
-                     mode, d.max_ctx, S, d.topk, L, 1);
+  hipLaunchKernelGGL(summary_beta_kernel<Src::LANES>, dim3(d.batch), dim3(64), 0, st,
+                     (const uint16_t*)summ, summ_stride, ctx_len, state, mode, d.max_ctx, S, d.topk, L);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const void* iq_score = qs_out ? (const void*)qs_out : iq;
@@ -384,11 +445,11 @@ hipError_t launch_token_or_block(const skv_layer_desc& d, const int32_t* ctx_len
   return hipGetLastError();
 }
 
-hipError_t launch_any(const skv_layer_desc& d, const int32_t* ctx_len, const void* iq,
-                      int8_t* qs_out, float* qscale_out, const void* ik, const uint16_t* isc,
-                      double* keys, void* ws, const WsLayout* Lw, uint32_t* flags, bool collect,
-                      hipStream_t st) {
-#define SKV_GO(SRC) return launch_token_or_block<SRC>(d, ctx_len, iq, qs_out, qscale_out, ik, isc, keys, ws, Lw, flags, collect, st)
+hipError_t launch_any(const skv_layer_desc& d, const int32_t* ctx_len, const void* iq, const void* q,
+                      const float* basis, int8_t* qs_out, float* qscale_out, const void* ik,
+                      const uint16_t* isc, double* keys, void* ws, const WsLayout* Lw, uint32_t* flags,
+                      bool collect, hipStream_t st) {
+#define SKV_GO(SRC) return launch_token_or_block<SRC>(d, ctx_len, iq, q, basis, qs_out, qscale_out, ik, isc, keys, ws, Lw, flags, collect, st)
   if (d.index_mode == SKV_INDEX_SKETCH_INT4) {
     switch (d.n_kv_heads * d.rank / 2) {   // sketch bytes per token = 16 * lanes
       case 32: SKV_GO(SketchSrc<2>);
@@ -412,13 +473,15 @@ hipError_t launch_any(const skv_layer_desc& d, const int32_t* ctx_len, const voi
 hipError_t launch_score(const skv_layer_desc& d, const int32_t* ctx_len, const void* iq,
                         const void* ik, const uint16_t* isc, double* keys, uint32_t* flags,
                         hipStream_t st) {
-  return launch_any(d, ctx_len, iq, nullptr, nullptr, ik, isc, keys, nullptr, nullptr, flags, false, st);
+  return launch_any(d, ctx_len, iq, nullptr, nullptr, nullptr, nullptr, ik, isc, keys, nullptr, nullptr,
+                    flags, false, st);
 }
 
 hipError_t launch_sample_collect(const skv_layer_desc& d, const int32_t* ctx_len, const void* iq,
-                                 int8_t* qs_out, float* qscale_out, const void* ik,
-                                 const uint16_t* isc, void* ws, const WsLayout& L, hipStream_t st) {
-  return launch_any(d, ctx_len, iq, qs_out, qscale_out, ik, isc, nullptr, ws, &L,
+                                 const void* q, const float* basis, int8_t* qs_out, float* qscale_out,
+                                 const void* ik, const uint16_t* isc, void* ws, const WsLayout& L,
+                                 hipStream_t st) {
+  return launch_any(d, ctx_len, iq, q, basis, qs_out, qscale_out, ik, isc, nullptr, ws, &L,
                     ws_ptr<uint32_t>(ws, L.flags), true, st);
 }
 

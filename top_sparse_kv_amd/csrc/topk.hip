@@ -659,10 +659,10 @@ hipError_t launch_final_multi(const skv_layer_desc& dv, int mq, const int32_t* c
 }
 
 hipError_t launch_score_select(const skv_layer_desc& d, const int32_t* ctx_len, const void* iq,
-                               int8_t* qs_out, float* qscale_out, const void* ik,
-                               const uint16_t* isc, int32_t* idx, int32_t* n_sel, void* ws,
-                               const WsLayout& Lw, hipStream_t st) {
-  hipError_t e = launch_sample_collect(d, ctx_len, iq, qs_out, qscale_out, ik, isc, ws, Lw, st);
+                               const void* q, const float* basis, int8_t* qs_out, float* qscale_out,
+                               const void* ik, const uint16_t* isc, int32_t* idx, int32_t* n_sel,
+                               void* ws, const WsLayout& Lw, hipStream_t st) {
+  hipError_t e = launch_sample_collect(d, ctx_len, iq, q, basis, qs_out, qscale_out, ik, isc, ws, Lw, st);
   if (e != hipSuccess) return e;
   const void* qrows = qs_out ? (const void*)qs_out : iq;
 #define SKV_FIN(SRC) return launch_final<SRC, true>(d, ctx_len, nullptr, qrows, ik, isc, idx, n_sel, ws, Lw, st)
