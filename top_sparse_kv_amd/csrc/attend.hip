@@ -115,17 +115,23 @@ __global__ __launch_bounds__(64 * WAVES) void attend_kernel(
   __shared__ uint32_t s_q[16 * QP / 2];   // Q of the G heads, one row per head
   extern __shared__ float s_o[];          // [W or HALF][G][D + 4]
 
-  // Workgroup -> (KV head h, chunk c, virtual sequence b).  One query per
-  // sequence: the 3-D grid.  Several: workgroups are dealt to the 8 XCDs in
-  // turn (linear id mod 8), each XCD with its own L2, and the mq queries of
-  // one (sequence, head, chunk) get ids that land on one XCD back to back, so
-  // the rows they share (sinks, and the tail that moves by one position per
-  // query) tend to be read from HBM once.
+  // Workgroup -> (KV head h, chunk c, virtual sequence b).  Workgroups are
+  // dealt to the 8 XCDs in turn (linear id mod 8), each XCD with its own L2.
+  // One query per sequence: the H_kv heads of a (sequence, chunk) get ids
+  // that land on one XCD.  Several: the mq queries of one (sequence, head,
+  // chunk) do, so the rows they share (sinks, and the tail that moves by one
+  // position per query) tend to be read from HBM once.
   int h, c, b;
   if (mq == 1) {
-    h = blockIdx.x;
-    c = blockIdx.y;
-    b = blockIdx.z;
+    // the H_kv heads of one (sequence, chunk) share an XCD: they read the same
+    // row indices and the same row-scale sectors (scales of all heads of a
+    // token are adjacent), which that XCD's L2 then serves once
+    const int xcd = blockIdx.x & 7, s = blockIdx.x >> 3;
+    const int key = (s / Hkv) * 8 + xcd;  // (sequence, chunk), chunk fastest
+    if (key >= n_keys) return;            // padding of the last round; before any barrier
+    h = s % Hkv;
+    c = key % n_chunks;
+    b = key / n_chunks;
   } else {
     const int xcd = blockIdx.x & 7, s = blockIdx.x >> 3;
     const int key = (s / mq) * 8 + xcd;   // (sequence, chunk, head), head fastest
@@ -350,10 +356,20 @@ __global__ __launch_bounds__(64 * WAVES) void attend_kernel(
   // survivors are combined.  A
   // slot holds G rows of D + 4 floats; lane (i16, g) owns columns
   // i16*(D/16) .. +D/16 of heads 4g .. 4g+3, stored as float4 runs.
+  // Inside its run, lane i16 stores float4 u at position (u + i16/4) mod
+  // (D/64): the 16 lanes of one store then hit 16 different 16-byte bank
+  // groups instead of a handful (runs are 64 bytes apart).
   constexpr int DP = D + 4;
   constexpr int CPL = D / 16;   // columns per lane
-  auto slot_ptr = [&](int slot, int j) -> f32x4* {
-    return reinterpret_cast<f32x4*>(s_o + ((size_t)slot * G + j) * DP + i16 * CPL);
+  constexpr int NU = CPL / 4;   // float4 per lane and row (a power of two)
+  static_assert((NU & (NU - 1)) == 0, "swizzle");
+  auto slot_at = [&](int slot, int j, int u) -> f32x4* {
+    return reinterpret_cast<f32x4*>(s_o + ((size_t)slot * G + j) * DP + i16 * CPL) + ((u + (i16 >> 2)) & (NU - 1));
+  };
+  // LDS offset (floats, inside a row) of column d under that swizzle
+  auto col_of = [](int d) -> int {
+    const int gi = d / CPL, w = d % CPL;
+    return gi * CPL + 4 * (((w >> 2) + (gi >> 2)) & (NU - 1)) + (w & 3);
   };
   if constexpr (ONE) {
     if (g == 0) {
@@ -374,11 +390,10 @@ __global__ __launch_bounds__(64 * WAVES) void attend_kernel(
     for (int e = 0; e < 4; ++e) {
       const int j = 4 * g + e;
       if (j < G) {
-        f32x4* dst = slot_ptr(wave, j);
 #pragma unroll
-        for (int u = 0; u < CPL / 4; ++u)
-          dst[u] = (f32x4){o[4 * u][e] * f_row[e], o[4 * u + 1][e] * f_row[e],
-                           o[4 * u + 2][e] * f_row[e], o[4 * u + 3][e] * f_row[e]};
+        for (int u = 0; u < NU; ++u)
+          *slot_at(wave, j, u) = (f32x4){o[4 * u][e] * f_row[e], o[4 * u + 1][e] * f_row[e],
+                                         o[4 * u + 2][e] * f_row[e], o[4 * u + 3][e] * f_row[e]};
       }
     }
     const size_t pbase = ((size_t)b * Hkv + h) * n_chunks + c;
@@ -401,7 +416,7 @@ __global__ __launch_bounds__(64 * WAVES) void attend_kernel(
       const int j = x / D, d = x % D;
       float acc = 0.0f;
 #pragma unroll
-      for (int w = 0; w < WAVES; ++w) acc += s_o[((size_t)w * G + j) * DP + d];
+      for (int w = 0; w < WAVES; ++w) acc += s_o[((size_t)w * G + j) * DP + col_of(d)];
       part_o[(pbase * G + j) * D + d] = acc;
     }
     return;
@@ -415,10 +430,9 @@ __global__ __launch_bounds__(64 * WAVES) void attend_kernel(
     for (int e = 0; e < 4; ++e) {
       const int j = 4 * g + e;
       if (j < G) {
-        f32x4* dst = slot_ptr(wave - HALF, j);
 #pragma unroll
-        for (int u = 0; u < CPL / 4; ++u)
-          dst[u] = (f32x4){o[4 * u][e], o[4 * u + 1][e], o[4 * u + 2][e], o[4 * u + 3][e]};
+        for (int u = 0; u < NU; ++u)
+          *slot_at(wave - HALF, j, u) = (f32x4){o[4 * u][e], o[4 * u + 1][e], o[4 * u + 2][e], o[4 * u + 3][e]};
       }
     }
   }
@@ -439,10 +453,9 @@ __global__ __launch_bounds__(64 * WAVES) void attend_kernel(
     for (int e = 0; e < 4; ++e) {
       const int j = 4 * g + e;
       if (j < G) {
-        const f32x4* src = slot_ptr(wave, j);
 #pragma unroll
-        for (int u = 0; u < CPL / 4; ++u) {
-          const f32x4 x = src[u];
+        for (int u = 0; u < NU; ++u) {
+          const f32x4 x = *slot_at(wave, j, u);
 #pragma unroll
           for (int q = 0; q < 4; ++q) o[4 * u + q][e] = o[4 * u + q][e] * aw_row[e] + x[q] * ap_row[e];
         }
@@ -461,10 +474,9 @@ __global__ __launch_bounds__(64 * WAVES) void attend_kernel(
     for (int e = 0; e < 4; ++e) {
       const int j = 4 * g + e;
       if (j < G) {
-        f32x4* dst = slot_ptr(wave, j);
 #pragma unroll
-        for (int u = 0; u < CPL / 4; ++u)
-          dst[u] = (f32x4){o[4 * u][e], o[4 * u + 1][e], o[4 * u + 2][e], o[4 * u + 3][e]};
+        for (int u = 0; u < NU; ++u)
+          *slot_at(wave, j, u) = (f32x4){o[4 * u][e], o[4 * u + 1][e], o[4 * u + 2][e], o[4 * u + 3][e]};
       }
     }
   }
@@ -493,7 +505,7 @@ __global__ __launch_bounds__(64 * WAVES) void attend_kernel(
     const int j = x / D, d = x % D;
     float acc = 0.0f;
 #pragma unroll
-    for (int w = 0; w < HALF; ++w) acc += s_o[((size_t)w * G + j) * DP + d] * s_l[HALF + w][j];
+    for (int w = 0; w < HALF; ++w) acc += s_o[((size_t)w * G + j) * DP + col_of(d)] * s_l[HALF + w][j];
     part_o[(pbase * G + j) * D + d] = acc;
   }
 }
@@ -567,10 +579,13 @@ hipError_t launch_attend(const skv_layer_desc& d, const void* q, const skv_kv_vi
   const int cap = select_capacity(d);
   const int G = d.n_q_heads / d.n_kv_heads;
   if (Lw.n_att_chunks > kMaxChunks) return hipErrorInvalidValue;
-  // one workgroup per (sequence, chunk, head) and query; several queries:
-  // a 1-D grid padded to whole rounds of 8 (sequence, chunk, head) keys
-  const int n_keys = d.batch / mq * Lw.n_att_chunks * d.n_kv_heads;
-  const dim3 grid = mq == 1 ? dim3(d.n_kv_heads, Lw.n_att_chunks, d.batch)
+  // one workgroup per (sequence, chunk, head) and query, a 1-D grid padded to
+  // whole rounds of 8 keys: one query, keys (sequence, chunk) with the H_kv
+  // heads of a key on one XCD; several queries, keys (sequence, chunk, head)
+  // with the mq queries of a key on one XCD
+  const int n_keys = mq == 1 ? d.batch * Lw.n_att_chunks
+                             : d.batch / mq * Lw.n_att_chunks * d.n_kv_heads;
+  const dim3 grid = mq == 1 ? dim3((unsigned)(((n_keys + 7) / 8) * 8 * d.n_kv_heads))
                             : dim3((unsigned)(((n_keys + 7) / 8) * 8 * mq));
   const int waves = att_waves(d);
   // one-stage merge when a slot per wave stays within 52 KB of LDS (two

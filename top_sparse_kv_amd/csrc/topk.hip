@@ -328,17 +328,28 @@ constexpr uint32_t kRankMax = 256;   // bucket sizes resolved by pairwise ranks
 
 // RECOMPUTE (the fused path): keys are recomputed from the index when the
 // candidates are too few.
+constexpr int kFetch = 4;                   // records read with each segment count
+constexpr int kFetch2 = 12;                 // records read in the second batch of a longer segment
+constexpr int kOneTripSegs = 2 * kFT;       // segments the one-round-trip path covers
+// LDS of the final select, shared by its paths (bytes): the one-trip path's
+// candidate arrays (key, position, digit) plus a member list, or the other
+// paths' register-gather lists and segment offsets
+constexpr size_t kFastBytes = (size_t)kListCap * 14 + 320 * 12;
+constexpr size_t kOldBytes = (size_t)(kListCap + 64) * 12 + (size_t)(kMaxSeg + 1) * 4;
+constexpr size_t kSelLds = kFastBytes > kOldBytes ? kFastBytes : kOldBytes;
+
 template <class Src, bool RECOMPUTE>
 __global__ __launch_bounds__(kFT) void topk_final_kernel(
     const double* __restrict__ keys_in, const void* __restrict__ iq, const void* __restrict__ ik,
     const uint16_t* __restrict__ isc, const int32_t* __restrict__ ctx_len,
-    const uint32_t* __restrict__ segcnt, Cand* __restrict__ cand, int32_t* __restrict__ idx,
-    int32_t* __restrict__ n_sel,
+    const uint32_t* __restrict__ segcnt, Cand* __restrict__ cand, const TopkState* __restrict__ state,
+    int32_t* __restrict__ idx, int32_t* __restrict__ n_sel,
     uint32_t* __restrict__ flags, int n_seg, int seg_items, int mode, int max_ctx, int S, int k,
     int L, int cap, int mq) {
-  __shared__ uint64_t s_bhi[kListCap + 64];
-  __shared__ uint32_t s_blo[kListCap + 64];
-  __shared__ uint32_t s_off[kMaxSeg + 1];
+  __shared__ uint64_t s_mem[(kSelLds + 7) / 8];
+  uint64_t* s_bhi = s_mem;                                                   // [kListCap + 64]
+  uint32_t* s_blo = reinterpret_cast<uint32_t*>(s_bhi + kListCap + 64);      // [kListCap + 64]
+  uint32_t* s_off = s_blo + kListCap + 64;                                   // [kMaxSeg + 1]
   __shared__ uint32_t s_hist[256 + 32];
   __shared__ SelectShared sh;
   const int b = blockIdx.x;   // virtual sequence: query b % mq of sequence b / mq
@@ -360,10 +371,186 @@ __global__ __launch_bounds__(kFT) void topk_final_kernel(
     for (int i = threadIdx.x; i < T - 4 * nb; i += blockDim.x) out[4 * k + i] = 4 * nb + i;
     if (threadIdx.x == 0) n_sel[b] = 4 * k + (T - 4 * nb);
   }
-  // segment offsets (n_parts <= kMaxSeg = kSegPT * blockDim.x)
   const int n_parts = (r.n + seg_items - 1) / seg_items;
   const uint32_t* sc = segcnt + (size_t)b * n_seg;
   const Cand* cb = cand + (size_t)b * n_seg * seg_items;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+  if (n_parts <= kOneTripSegs) {
+    // ---- per 1024 segments: each thread reads one segment's count together
+    // with its first kFetch records (a segment averages a few candidates), a
+    // block prefix sum places them in LDS in position order, and the longer
+    // segments read the rest in one more batch ----
+    uint64_t* c_key = s_mem;                                                  // [kListCap]
+    uint32_t* c_pos = reinterpret_cast<uint32_t*>(c_key + kListCap);          // [kListCap]
+    uint16_t* c_dig = reinterpret_cast<uint16_t*>(c_pos + kListCap);          // [kListCap]
+    uint64_t* m_hi = reinterpret_cast<uint64_t*>(c_dig + kListCap);           // [320]
+    uint32_t* m_lo = reinterpret_cast<uint32_t*>(m_hi + 320);                 // [320]
+    uint32_t total = 0;
+    bool fits = true;
+    for (int r0 = 0; r0 < n_parts; r0 += kFT) {   // workgroup-uniform
+      const int seg = r0 + (int)threadIdx.x;
+      const int segc = min(seg, n_parts - 1);
+      const u32x4* src = reinterpret_cast<const u32x4*>(cb + (size_t)segc * seg_items);
+      uint32_t cnt = sc[segc];
+      u32x4 rr[kFetch];
+#pragma unroll
+      for (int m = 0; m < kFetch; ++m) rr[m] = src[m];   // unconditional, inside the segment
+      cnt = seg < n_parts ? min(cnt, (uint32_t)seg_items) : 0u;
+      uint32_t tot = 0;
+      const uint32_t off = total + block_excl_scan(cnt, sh.wsum, &tot);
+      if (total + tot > (uint32_t)kListCap) {   // uniform: more candidates than LDS holds
+        fits = false;
+        break;
+      }
+#pragma unroll
+      for (int m = 0; m < kFetch; ++m)
+        if ((uint32_t)m < cnt) {
+          c_key[off + m] = ((uint64_t)rr[m].y << 32) | rr[m].x;
+          c_pos[off + m] = rr[m].z;
+          c_dig[off + m] = (uint16_t)rr[m].w;
+        }
+      // longer segments: the next kFetch2 records in one batch, then (rare)
+      // further batches
+      for (uint32_t m0 = kFetch; m0 < cnt; m0 += kFetch2) {
+        u32x4 r2[kFetch2];
+#pragma unroll
+        for (int m = 0; m < kFetch2; ++m) r2[m] = src[min(m0 + (uint32_t)m, cnt - 1)];
+#pragma unroll
+        for (int m = 0; m < kFetch2; ++m)
+          if (m0 + (uint32_t)m < cnt) {
+            c_key[off + m0 + m] = ((uint64_t)r2[m].y << 32) | r2[m].x;
+            c_pos[off + m0 + m] = r2[m].z;
+            c_dig[off + m0 + m] = (uint16_t)r2[m].w;
+          }
+      }
+      total += tot;
+    }
+    __syncthreads();
+    if (fits && total >= (uint32_t)k) {
+      const int n = (int)total;
+      // digits relative to the threshold every candidate passed (12-bit in
+      // the keys path, 16-bit elsewhere); bins count up from it, the last bin
+      // open; the bin of the k-th largest (fbin) is the only one ranked
+      const uint32_t dlo = RECOMPUTE ? state[b].beta : state[b].beta << 4;
+      auto bin_of = [&](uint32_t dg) -> uint32_t { return dg >= dlo ? min(dg - dlo, 255u) : 0u; };
+      const int PT = (n + kFT - 1) / kFT;   // candidates per thread, a contiguous run
+      const int j0 = PT * (int)threadIdx.x;
+      if (threadIdx.x < 256) s_hist[threadIdx.x] = 0u;
+      if (threadIdx.x == 0) s_hist[258] = 0u;
+      __syncthreads();
+      for (int m = 0; m < PT; ++m)
+        if (j0 + m < n) atomicAdd(&s_hist[bin_of(c_dig[j0 + m])], 1u);
+      __syncthreads();
+      uint32_t* wr = s_hist + 256;
+      if (wave == 0) {
+        uint32_t c[4], t = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          c[j] = s_hist[255 - 4 * lane - j];
+          t += c[j];
+        }
+        const uint32_t incl = wave_incl_scan(t);
+        const uint64_t hit = __ballot(incl >= (uint32_t)k);   // not empty: n >= k
+        const int l = (int)__ffsll((unsigned long long)hit) - 1;
+        uint32_t cum = incl - t, fb = 0, before = 0, fbc = 0;
+        bool found = false;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (!found && cum + c[j] >= (uint32_t)k) {
+            found = true;
+            fb = (uint32_t)(255 - 4 * lane - j);
+            before = cum;
+            fbc = c[j];
+          }
+          cum += c[j];
+        }
+        if (lane == l) {
+          wr[0] = fb;       // the bin of the k-th largest
+          wr[1] = before;   // candidates in the bins above it
+          wr[3] = fbc;      // members of that bin
+        }
+      }
+      __syncthreads();
+      const uint32_t fbin = wr[0], rk = (uint32_t)k - wr[1], mb = wr[3];
+      if (mb <= kRankMax) {
+        // the members of fbin, appended in any order, ranked pairwise
+        for (int m = 0; m < PT; ++m)
+          if (j0 + m < n && bin_of(c_dig[j0 + m]) == fbin) {
+            const uint32_t at = atomicAdd(&wr[2], 1u);
+            m_hi[at] = c_key[j0 + m];
+            m_lo[at] = ~c_pos[j0 + m];
+          }
+        if (threadIdx.x < 64) {   // padding that never ranks above a member
+          m_hi[mb + threadIdx.x] = 0ull;
+          m_lo[mb + threadIdx.x] = 0u;
+        }
+        __syncthreads();
+        const int P = mb <= 64 ? 16 : (mb <= 128 ? 8 : 4);
+        const int mm = (int)threadIdx.x / P, part = (int)threadIdx.x % P;
+        uint32_t rank = 0;
+        uint64_t hi = 0;
+        uint32_t lo = 0;
+        if (mm < (int)mb) {
+          hi = m_hi[mm];
+          lo = m_lo[mm];
+          for (int j = part; j < (int)mb; j += 4 * P) {
+            uint64_t oh[4];
+            uint32_t ol[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              oh[u] = m_hi[j + u * P];
+              ol[u] = m_lo[j + u * P];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              rank += (uint32_t)(oh[u] > hi) + (uint32_t)((oh[u] == hi) & (ol[u] > lo));
+          }
+        }
+        for (int o = 1; o < P; o <<= 1) rank += (uint32_t)__shfl_xor((int)rank, o);
+        if (mm < (int)mb && part == 0 && rank == rk - 1) {
+          sh.pre_hi = hi;
+          sh.pre_lo = lo;
+        }
+        if (threadIdx.x == 0) {
+          sh.mask_hi = ~0ull;
+          sh.mask_lo = ~0u;
+        }
+        __syncthreads();
+      } else {
+        // a wide bin: radix select over all candidates, non-members as zeros
+        radix_select([&](int i, uint64_t& hi, uint32_t& lo) {
+          const bool mem = bin_of(c_dig[i]) == fbin;
+          hi = mem ? c_key[i] : 0ull;
+          lo = mem ? ~c_pos[i] : 0u;
+        }, n, (int)rk, sh);
+      }
+      // ordered emission of the kept candidates (runs are in position order)
+      uint32_t cnt = 0;
+      for (int m = 0; m < PT; ++m) {
+        const int i = j0 + m;
+        if (i < n) {
+          const uint32_t bn = bin_of(c_dig[i]);
+          cnt += (uint32_t)(bn > fbin || (bn == fbin && kept(c_key[i], ~c_pos[i], sh)));
+        }
+      }
+      int rank = (int)block_excl_scan(cnt, sh.wsum, nullptr);
+      for (int m = 0; m < PT; ++m) {
+        const int i = j0 + m;
+        if (i < n) {
+          const uint32_t bn = bin_of(c_dig[i]);
+          if (bn > fbin || (bn == fbin && kept(c_key[i], ~c_pos[i], sh))) {
+            if (rank < k) emit_position(out, mode, S, rank, (int)c_pos[i]);
+            ++rank;
+          }
+        }
+      }
+      return;
+    }
+    __syncthreads();   // the LDS is reused below
+  }
+
+  // segment offsets (n_parts <= kMaxSeg = kSegPT * blockDim.x)
   uint32_t total;
   {
     uint32_t cs[kSegPT], mine = 0;
@@ -391,7 +578,6 @@ __global__ __launch_bounds__(kFT) void topk_final_kernel(
     // its first segment, then a walk; all its loads are issued together.
     const int n = (int)total;
     const int j0 = kGPT * (int)threadIdx.x;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     u32x4 rec[kGPT];
     {
       int c = seg_of(s_off, n_parts, (uint32_t)min(j0, n - 1));
@@ -568,7 +754,6 @@ __global__ __launch_bounds__(kFT) void topk_final_kernel(
     // the sequence's record area holds 2 * n_seg * seg_items doubles >= r.n
     double* kw = reinterpret_cast<double*>(cand + (size_t)b * n_seg * seg_items);
     constexpr int N = Src::LANES, IPW = 64 / N, PER_IT = 8 * IPW;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sub = lane % N, tw = lane / N;
     Src src;
     src.init(reinterpret_cast<const uint8_t*>(iq) + (size_t)b * Src::QROW, ik, isc, b / mq, max_ctx,
@@ -617,7 +802,8 @@ hipError_t launch_final(const skv_layer_desc& d, const int32_t* ctx_len, const d
   const int L = mode == SKV_INDEX_SKETCH_INT4 ? d.n_tail : 0;
   hipLaunchKernelGGL((topk_final_kernel<Src, RECOMPUTE>), dim3(d.batch), dim3(kFT), 0, st,
                      keys, iq, ik, isc, ctx_len, ws_ptr<uint32_t>(ws, Lw.segcnt),
-                     ws_ptr<Cand>(ws, Lw.cand), idx, n_sel, ws_ptr<uint32_t>(ws, Lw.flags),
+                     ws_ptr<Cand>(ws, Lw.cand), ws_ptr<const TopkState>(ws, Lw.state), idx, n_sel,
+                     ws_ptr<uint32_t>(ws, Lw.flags),
                      Lw.n_seg, Lw.seg_items, mode, d.max_ctx, S, d.topk, L, select_capacity(d), mq);
   return hipGetLastError();
 }
