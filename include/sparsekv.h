@@ -47,9 +47,10 @@
 extern "C" {
 #endif
 
-#define SPARSEKV_ABI_VERSION 4   /* 3: multi-query step, prefill over host K/V, tier policy field;
+#define SPARSEKV_ABI_VERSION 5   /* 3: multi-query step, prefill over host K/V, tier policy field;
                                     4: tier append (host records sized by max_ctx, tail ring),
-                                       multi-query tier resolve and attention */
+                                       multi-query tier resolve and attention;
+                                    5: the step without a workspace argument */
 
 typedef int32_t skv_status;
 enum {
@@ -232,6 +233,32 @@ skv_status sparsekv_step(const skv_layer_desc* d, const int32_t* ctx_len, const 
                          const uint16_t* index_scale, const skv_kv_view* kv, int32_t* idx,
                          int32_t* n_sel, float sm_scale, float* out, void* ws, size_t ws_bytes,
                          void* stream);
+
+/* ---- the whole step without a workspace argument ----------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Computes
+ * exactly what sparsekv_step computes, with the same arguments except
+ * ws / ws_bytes, in a device array of SKV_NOALLOC_SCRATCH_BYTES inside the
+ * library (one per device, kept until the process ends) instead of a caller
+ * workspace; nothing is allocated.
+ *   flags   device uint32 (may be NULL): receives this call's device flag
+ *           word (the bits sparsekv_check reports for sparsekv_step); the
+ *           library's copy is cleared at the end of every call
+ *   errors  SKV_ERR_WORKSPACE when the layer needs more scratch than the array
+ *           holds (sparsekv_workspace_size(d) > SKV_NOALLOC_SCRATCH_BYTES: in
+ *           token mode batch x max_ctx above about 4M tokens); otherwise as
+ *           sparsekv_step
+ * Runs on the device current at the call (the stream must belong to it).
+ * Every call on one device uses the same array: calls ordered on one stream
+ * are safe, calls that overlap in time on one device (other streams, other
+ * host threads) race and give wrong results. */
+#define SKV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+skv_status sparsekv_step_noalloc(const skv_layer_desc* d, const int32_t* ctx_len, const void* q,
+                                 const float* basis, int8_t* qs, float* qs_scale,
+                                 const void* index_query, const void* index_keys,
+                                 const uint16_t* index_scale, const skv_kv_view* kv, int32_t* idx,
+                                 int32_t* n_sel, float sm_scale, float* out, uint32_t* flags,
+                                 void* stream);
 
 /* ---- the step with several query tokens per sequence ------------------------
  * Page "8 agents x 250K ...", section "What shipped" (decoding with MTP-7

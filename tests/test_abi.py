@@ -62,7 +62,7 @@ def test_struct_sizes_match_header(skv):
     # the C structs are plain int32 / pointer layouts; sizes pinned here
     assert ctypes.sizeof(skv.LayerDesc) == 15 * 4
     assert ctypes.sizeof(skv.KVView) == 5 * 8
-    assert skv.abi_version() == 4
+    assert skv.abi_version() == 5
 
 
 def test_capacity_and_workspace(skv):

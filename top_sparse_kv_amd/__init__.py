@@ -153,6 +153,18 @@ def step(desc, ctx_len, q, basis, qs, qs_scale, index_query, index_keys, index_s
                                _p(ws), ws.numel(), _stream(stream)))
 
 
+def step_noalloc(desc, ctx_len, q, basis, qs, qs_scale, index_query, index_keys, index_scale,
+                 kv: KVView, idx, n_sel, sm_scale, out, flags=None, stream=None):
+    """sparsekv_step without a workspace: the library's own device scratch is
+    used.  flags (optional int32/uint32 device tensor of >= 1 element) receives
+    the call's device flag word."""
+    _dev(ctx_len, q, basis, qs, qs_scale, index_query, index_keys, index_scale, idx, n_sel, out, flags)
+    _check(lib().sparsekv_step_noalloc(ctypes.byref(desc), _p(ctx_len), _p(q), _p(basis), _p(qs),
+                                       _p(qs_scale), _p(index_query), _p(index_keys), _p(index_scale),
+                                       ctypes.byref(kv), _p(idx), _p(n_sel), float(sm_scale), _p(out),
+                                       _p(flags), _stream(stream)))
+
+
 def workspace_size_multi(desc: LayerDesc, n_query: int) -> int:
     n = _lib.c_sz()
     _check(lib().sparsekv_workspace_size_multi(ctypes.byref(desc), int(n_query), ctypes.byref(n)))

@@ -71,6 +71,9 @@ SIGNATURES = [
                                 c_vp, c_sz, c_vp]),
     ("sparsekv_step", c_i32, [P(LayerDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                               P(KVView), c_vp, c_vp, ctypes.c_float, c_vp, c_vp, c_sz, c_vp]),
+    ("sparsekv_step_noalloc", c_i32, [P(LayerDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                      c_vp, P(KVView), c_vp, c_vp, ctypes.c_float, c_vp, c_vp,
+                                      c_vp]),
     ("sparsekv_workspace_size_multi", c_i32, [P(LayerDesc), c_i32, P(c_sz)]),
     ("sparsekv_step_multi", c_i32, [P(LayerDesc), c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                     P(KVView), c_vp, c_vp, ctypes.c_float, c_vp, c_vp, c_sz, c_vp]),

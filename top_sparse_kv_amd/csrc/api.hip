@@ -8,6 +8,7 @@
 #include <string.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <vector>
 
 namespace skv {
@@ -127,6 +128,46 @@ static skv_status check_kv(const skv_layer_desc* d, const skv_kv_view* kv) {
   if ((((uintptr_t)kv->k) | ((uintptr_t)kv->v)) % 16)
     return set_error(SKV_ERR_INVALID, "k / v must be 16-byte aligned");
   return SKV_OK;
+}
+
+// ---- scratch of the allocation-free step ---------------------------------
+// A file-scope device array stands in for the caller's workspace; every device
+// the library runs on holds its own copy (zero at load) until the process
+// ends.  Host code never passes `scratch` itself to a kernel (its host-side
+// name is a stand-in, not a device address): the address is looked up once per
+// device with hipGetSymbolAddress and kept below.
+constexpr size_t kScratchBytes = (size_t)SKV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static void* g_scratch_addr[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+// device address of `scratch` on the current device
+static skv_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return set_error(SKV_ERR_HIP, "step_noalloc: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return set_error(SKV_ERR_UNSUPPORTED, "step_noalloc: device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> guard(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return set_error(SKV_ERR_HIP, "step_noalloc: scratch address: %s", hipGetErrorString(e));
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return SKV_OK;
+}
+
+// hands the call's flag word to the caller (if asked) and clears it, so the
+// next call on this device starts from zero
+__global__ void flags_handoff_kernel(uint32_t* __restrict__ f, uint32_t* __restrict__ out) {
+  const uint32_t v = *f;
+  if (out) *out = v;
+  *f = 0u;
 }
 
 }  // namespace skv
@@ -355,6 +396,39 @@ skv_status sparsekv_attend(const skv_layer_desc* d, const void* q, const skv_kv_
                   "attend");
 }
 
+static skv_status check_step_args(const skv_layer_desc* d, const int32_t* ctx_len, const void* q,
+                                  const float* basis, const int8_t* qs, const float* qs_scale,
+                                  const void* index_query, const void* index_keys,
+                                  const uint16_t* index_scale, const skv_kv_view* kv,
+                                  const int32_t* idx, const int32_t* n_sel, const float* out) {
+  skv_status s = check_kv(d, kv);
+  if (s != SKV_OK) return s;
+  if (!ctx_len || !q || !index_keys || !idx || !n_sel || !out)
+    return set_error(SKV_ERR_INVALID, "step: NULL pointer");
+  if (((uintptr_t)index_keys) % 16) return set_error(SKV_ERR_INVALID, "step: index_keys not 16-byte aligned");
+  const bool tok = d->index_mode == SKV_INDEX_SKETCH_INT4;
+  if (tok && (!basis || !qs || !qs_scale || !index_scale))
+    return set_error(SKV_ERR_INVALID, "step: token mode needs basis, qs, qs_scale and index_scale");
+  if (!tok && !index_query) return set_error(SKV_ERR_INVALID, "step: block mode needs index_query");
+  return SKV_OK;
+}
+
+static hipError_t launch_step(const skv_layer_desc* d, const int32_t* ctx_len, const void* q,
+                              const float* basis, int8_t* qs, float* qs_scale,
+                              const void* index_query, const void* index_keys,
+                              const uint16_t* index_scale, const skv_kv_view* kv, int32_t* idx,
+                              int32_t* n_sel, float sm_scale, float* out, void* ws,
+                              const WsLayout& L, hipStream_t st) {
+  const bool tok = d->index_mode == SKV_INDEX_SKETCH_INT4;
+  // token mode: the projection here, its quantization in the front kernel
+  hipError_t e = tok ? launch_qsketch_proj(*d, q, basis, ws, L, st) : hipSuccess;
+  if (e == hipSuccess)
+    e = launch_score_select(*d, ctx_len, tok ? nullptr : index_query, q, basis, tok ? qs : nullptr,
+                            tok ? qs_scale : nullptr, index_keys, index_scale, idx, n_sel, ws, L, st);
+  if (e == hipSuccess) e = launch_attend(*d, q, *kv, idx, n_sel, sm_scale, out, ws, L, st);
+  return e;
+}
+
 skv_status sparsekv_step(const skv_layer_desc* d, const int32_t* ctx_len, const void* q,
                          const float* basis, int8_t* qs, float* qs_scale, const void* index_query,
                          const void* index_keys, const uint16_t* index_scale,
@@ -364,22 +438,37 @@ skv_status sparsekv_step(const skv_layer_desc* d, const int32_t* ctx_len, const 
   if (s != SKV_OK) return s;
   WsLayout L;
   if ((s = check_ws(d, ws, ws_bytes, &L)) != SKV_OK) return s;
-  if ((s = check_kv(d, kv)) != SKV_OK) return s;
-  if (!ctx_len || !q || !index_keys || !idx || !n_sel || !out)
-    return set_error(SKV_ERR_INVALID, "step: NULL pointer");
-  if (((uintptr_t)index_keys) % 16) return set_error(SKV_ERR_INVALID, "step: index_keys not 16-byte aligned");
-  const bool tok = d->index_mode == SKV_INDEX_SKETCH_INT4;
-  if (tok && (!basis || !qs || !qs_scale || !index_scale))
-    return set_error(SKV_ERR_INVALID, "step: token mode needs basis, qs, qs_scale and index_scale");
-  if (!tok && !index_query) return set_error(SKV_ERR_INVALID, "step: block mode needs index_query");
-  hipStream_t st = (hipStream_t)stream;
-  // token mode: the projection here, its quantization in the front kernel
-  hipError_t e = tok ? launch_qsketch_proj(*d, q, basis, ws, L, st) : hipSuccess;
-  if (e == hipSuccess)
-    e = launch_score_select(*d, ctx_len, tok ? nullptr : index_query, q, basis, tok ? qs : nullptr,
-                            tok ? qs_scale : nullptr, index_keys, index_scale, idx, n_sel, ws, L, st);
-  if (e == hipSuccess) e = launch_attend(*d, q, *kv, idx, n_sel, sm_scale, out, ws, L, st);
-  return launched(e, "step");
+  if ((s = check_step_args(d, ctx_len, q, basis, qs, qs_scale, index_query, index_keys, index_scale,
+                           kv, idx, n_sel, out)) != SKV_OK)
+    return s;
+  return launched(launch_step(d, ctx_len, q, basis, qs, qs_scale, index_query, index_keys,
+                              index_scale, kv, idx, n_sel, sm_scale, out, ws, L, (hipStream_t)stream),
+                  "step");
+}
+
+skv_status sparsekv_step_noalloc(const skv_layer_desc* d, const int32_t* ctx_len, const void* q,
+                                 const float* basis, int8_t* qs, float* qs_scale,
+                                 const void* index_query, const void* index_keys,
+                                 const uint16_t* index_scale, const skv_kv_view* kv, int32_t* idx,
+                                 int32_t* n_sel, float sm_scale, float* out, uint32_t* flags,
+                                 void* stream) {
+  skv_status s = validate_desc(d);
+  if (s != SKV_OK) return s;
+  const WsLayout L = ws_layout(*d);
+  if (L.total > kScratchBytes)
+    return set_error(SKV_ERR_WORKSPACE, "step_noalloc: the layer needs %zu bytes of scratch, more than %zu",
+                     L.total, kScratchBytes);
+  if ((s = check_step_args(d, ctx_len, q, basis, qs, qs_scale, index_query, index_keys, index_scale,
+                           kv, idx, n_sel, out)) != SKV_OK)
+    return s;
+  void* ws = nullptr;   // the device address of `scratch`, never the array's host-side name
+  if ((s = scratch_address(&ws)) != SKV_OK) return s;
+  const hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_step(d, ctx_len, q, basis, qs, qs_scale, index_query, index_keys,
+                             index_scale, kv, idx, n_sel, sm_scale, out, ws, L, st);
+  if (e != hipSuccess) return launched(e, "step_noalloc");
+  hipLaunchKernelGGL(flags_handoff_kernel, dim3(1), dim3(1), 0, st, ws_ptr<uint32_t>(ws, L.flags), flags);
+  return launched(hipGetLastError(), "step_noalloc");
 }
 
 skv_status sparsekv_append(const skv_layer_desc* d, int32_t* ctx_len, const void* k_new,
