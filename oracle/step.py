@@ -410,6 +410,36 @@ def tier_attention(q_b, records_b, res_k, res_v, res_ks, res_vs, idx, T, S, L,
     return attention_rows(f16_to_f64(q_b), kd, vd, sm_scale, group)
 
 
+def paged_tier_attention(q_b, records_b, k8_b, v8_b, ks_b, vs_b, idx, T, S, L, page_block, P,
+                         sm_scale, group, D):
+    """Attention of one sequence under page residency (page "vLLM's Hybrid
+    HiSparse Triples Concurrent Requests on Million-Token Contexts", section
+    "Three residency states, one block pool": rows of resident pages are read
+    in place, the rest through the hot buffer from host memory).  Sinks
+    [0,S), tail [T-L,T) and middle positions whose page p // P is mapped
+    (page_block[p // P] >= 0) use the sequence's own int8 rows k8_b/v8_b
+    [T][H_kv][D] with fp16 row scales ks_b/vs_b [T][H_kv]; the other middle
+    positions use their host records turned into int8 rows."""
+    idx = np.asarray(idx, dtype=np.int64)
+    n_kv = records_b.shape[1]
+    rb = D // 2 + 2 * (D // HOST_GROUP)
+    page_block = np.asarray(page_block, dtype=np.int64)
+    n = idx.size
+    kd = np.empty((n, n_kv, D))
+    vd = np.empty((n, n_kv, D))
+    for r, p in enumerate(idx.tolist()):
+        if p < S or p >= T - L or page_block[p // P] >= 0:
+            kd[r] = dequant_rows(k8_b[p], ks_b[p], "i8")
+            vd[r] = dequant_rows(v8_b[p], vs_b[p], "i8")
+        else:
+            for h in range(n_kv):
+                k8, ksc = host_row_dequant(records_b[p, h, :rb], D)
+                v8, vsc = host_row_dequant(records_b[p, h, rb:], D)
+                kd[r, h] = k8.astype(np.float64) * np.float64(ksc)
+                vd[r, h] = v8.astype(np.float64) * np.float64(vsc)
+    return attention_rows(f16_to_f64(q_b), kd, vd, sm_scale, group)
+
+
 # ----------------------------------------------------------------------------
 # byte counts   [P3] closed forms; [P4] "Why", "What Needs to Stay in VRAM"
 # ----------------------------------------------------------------------------
@@ -485,6 +515,9 @@ PINS = {
     "attention_rows": "torch fp64 scaled_dot_product_attention on the dense case, one row -> v, q=0 -> mean of v, dense == sparse bitwise",
     "host_row_dequant": "hand-worked fixture, |r8| <= 127, monotone in the code within a group",
     "ClockTier": "hand-traced fixtures with W = 1 and W = 2 (the W = 2 trace separates the window from W = 1 and from a '>=' window test), hits+misses=picks, window-pinned slots never evicted, occupancy",
+    "paged_tier_attention": "one-row selections read exactly the source the page rule names (sink, tail "
+                            "boundary, mapped page edges, unmapped neighbours); no mapped page equals "
+                            "tier_attention and every page mapped equals sparse_attention, bit for bit",
     "tier_attention": "equal bit for bit to sparse_attention over a plain int8 cache holding the rows the host records decode to (codes derived in exact rationals); hand-worked position -> row table for sinks, the first middle row, the tail boundary T-L and the last position",
     "byte counts": "4 MiB / 48 MiB, 64 MiB, 130 B, 272 B, 27.75 / 27.00 / 0.75 KiB closed forms",
     "attention output values": "parity unpinned by the pages (they print no worked values); pinned by the library routine and special cases above",

@@ -540,6 +540,129 @@ def test_tier_attention_position_rows():
         assert np.all(o == val), (p, o[0, :4])
 
 
+def test_residency_fixture():
+    """Hand trace of page residency over an LRU hot buffer
+    (tests/golden/residency_trace.txt): picks of mapped pages are read in
+    place at block*P + p%P, the others go through the hot buffer; mapping
+    changes between steps move picks between the two; full, mixed and no
+    residency all appear."""
+    lines = list(_lines("residency_trace.txt"))
+    n_slots, P, n_pages = (int(lines[i].split()[1]) for i in range(3))
+    tier = oracle.residency.PagedTier(oracle.residency.LruTier(n_slots, 100), P, n_pages)
+    code = {oracle.residency.IN_PLACE: "R", oracle.residency.HIT: "H", oracle.residency.MISS: "M"}
+    for ln in lines[3:]:
+        w = ln.split()
+        if w[0] == "map":
+            tier.map_page(int(w[1]), int(w[2]))
+        elif w[0] == "unmap":
+            tier.unmap_page(int(w[1]))
+        elif w[0] == "mapall":
+            for g in range(n_pages):
+                tier.map_page(g, g)
+        elif w[0] == "unmapall":
+            for g in range(n_pages):
+                tier.unmap_page(g)
+        elif w[0] == "final":
+            assert tier.hot.pos.tolist() == [int(x) for x in w[1:]]
+        else:
+            s, picks, per, counts = (x.strip() for x in ln.split("|"))
+            kind, where, cnt = tier.step(np.array([int(x) for x in picks.split()]), int(s))
+            got = ["%s%d" % (code[int(k)], int(x)) for k, x in zip(kind, where)]
+            assert got == per.split(), ln
+            assert cnt == tuple(int(x) for x in counts.split()), ln
+
+
+def test_residency_invariants_drifting_workload():
+    """With pages mapped and unmapped at random between steps: in place + hits
+    + misses = picks; in-place picks are exactly those of mapped pages, at
+    their pool row; every other pick sits in the hot slot reported; and with
+    no page ever mapped the slots equal those of the bare hot buffer."""
+    T, S, L, k, P = 30_000, 64, 1024, 256, 64
+    n_pages = (T + P - 1) // P
+    picks = synth.drift_picks(1, T, S, L, k, 40, seed=45, window=4096, sigma_c=256.0)
+    rng = np.random.default_rng(7)
+    paged = oracle.residency.PagedTier(oracle.residency.LruTier(2 * k, T), P, n_pages)
+    plain = oracle.residency.PagedTier(oracle.residency.LruTier(2 * k, T), P, n_pages)
+    bare = oracle.residency.LruTier(2 * k, T)
+    for s in range(40):
+        for g in rng.choice(n_pages, size=20, replace=False).tolist():
+            if paged.block[g] >= 0:
+                paged.unmap_page(g)
+            else:
+                paged.map_page(g, int(rng.integers(0, 1000)))
+        p = np.asarray(picks[s][0], dtype=np.int64)
+        kind, where, (n_in, h, m) = paged.step(p, s)
+        assert n_in + h + m == p.size
+        mapped = paged.block[p // P] >= 0
+        assert np.array_equal(kind == oracle.residency.IN_PLACE, mapped)
+        assert np.array_equal(where[mapped], paged.block[p[mapped] // P] * P + p[mapped] % P)
+        assert np.array_equal(paged.hot.pos[where[~mapped]], p[~mapped])
+        k2, w2, c2 = plain.step(p, s)
+        slots, h2, m2 = bare.step(p, s)
+        assert np.array_equal(w2, slots) and c2 == (0, h2, m2)
+        assert not (k2 == oracle.residency.IN_PLACE).any()
+
+
+def test_paged_attention_one_row_sources():
+    """Hand-worked sources (T = 16, S = 2, L = 3, pages of 4, pages 1 and 2
+    mapped, D = 64, one head): attending one position returns the V row of the
+    source the rule names.  The GPU-side int8 V row of position p is the
+    constant 10 + p (scale 1); the host record of p has V codes c = p % 7 - 3
+    with group scale 127, which decodes with s' = 7 to rint(127 c / 7) = 18c
+    for |c| <= 3, i.e. the value 126 c.  Sinks 0, 1, tail 13..15 and the mapped
+    positions 4..11 read 10 + p; the unmapped middle positions 2, 3, 12 read
+    126 (p % 7 - 3).  K rows are zero (equal logits)."""
+    T, S, L, P, D = 16, 2, 3, 4, 64
+    rb = D // 2 + 2
+    records = np.zeros((T, 1, 2 * rb), dtype=np.uint8)
+    for p in range(T):
+        records[p, 0, :rb] = _host_row(np.zeros(D, np.int8), [127.0])
+        records[p, 0, rb:] = _host_row(np.full(D, p % 7 - 3, np.int8), [127.0])
+    k8 = np.zeros((T, 1, D), np.int8)
+    v8 = np.array([np.full((1, D), 10 + p, np.int8) for p in range(T)])
+    ones = np.ones((T, 1), np.float16)
+    page_block = np.array([-1, 0, 1, -1])
+    q = np.ones((1, D), np.float16)
+    expect = {0: 10, 1: 11, 2: -126, 3: 0, 4: 14, 5: 15, 6: 16, 7: 17, 8: 18, 9: 19, 10: 20, 11: 21,
+              12: 252, 13: 23, 14: 24, 15: 25}
+    for p, val in expect.items():
+        o = oracle.paged_tier_attention(q, records, k8, v8, ones, ones, np.array([p]), T, S, L,
+                                        page_block, P, 0.125, 1, D)
+        assert np.all(o == val), (p, o[0, :4])
+
+
+def test_paged_attention_reduces_to_tier_and_plain_attention():
+    """No page mapped: equal bit for bit to tier_attention with the sinks and
+    tail of the same int8 cache as its resident rows; every page mapped: equal
+    bit for bit to sparse_attention over the int8 cache."""
+    rng = np.random.default_rng(32)
+    n_kv, G, D, T, S, L, P = 2, 2, 128, 40, 4, 6, 4
+    rb = D // 2 + 2 * (D // 64)
+    records = rng.integers(0, 256, size=(T, n_kv, 2 * rb), dtype=np.uint8)
+    for part in (0, 1):   # finite, positive group scales
+        off = part * rb + D // 2
+        records[:, :, off:off + 2 * (D // 64)] = (
+            rng.uniform(0.01, 2.0, size=(T, n_kv, D // 64)).astype(np.float16).view(np.uint8))
+    k8 = rng.integers(-127, 128, size=(T, n_kv, D), dtype=np.int8)
+    v8 = rng.integers(-127, 128, size=(T, n_kv, D), dtype=np.int8)
+    ks = rng.uniform(0.001, 0.05, size=(T, n_kv)).astype(np.float16)
+    vs = rng.uniform(0.001, 0.05, size=(T, n_kv)).astype(np.float16)
+    q = rng.standard_normal((n_kv * G, D)).astype(np.float16)
+    idx = np.sort(np.concatenate([np.arange(S), rng.choice(np.arange(S, T - L), 12, replace=False),
+                                  np.arange(T - L, T)]))
+    res = np.concatenate([np.arange(S), np.arange(T - L, T)])
+    n_pages = T // P
+    none = oracle.paged_tier_attention(q, records, k8, v8, ks, vs, idx, T, S, L, np.full(n_pages, -1), P,
+                                       D ** -0.5, G, D)
+    tier = oracle.tier_attention(q, records, k8[res], v8[res], ks[res], vs[res], idx, T, S, L, D ** -0.5, G, D)
+    assert np.array_equal(none, tier)
+    full = oracle.paged_tier_attention(q, records, k8, v8, ks, vs, idx, T, S, L, np.arange(n_pages), P,
+                                       D ** -0.5, G, D)
+    plain = oracle.sparse_attention(q, k8, v8, ks, vs, idx, D ** -0.5, G, "i8")
+    assert np.array_equal(full, plain)
+    assert not np.array_equal(none, plain)
+
+
 def test_clock_fixture():
     lines = list(_lines("clock_trace.txt"))
     n = int(lines[0].split()[1])
