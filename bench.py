@@ -92,6 +92,14 @@ CONFIGS = {
                  kv="i8", layers=1, seed=1005, warm_steps=64, steps=256,
                  workload="4 seq x 250,000 tokens; cfg2 layer shape; int4 host-RAM K/V records read "
                           "zero-copy, 2.5% hot slots (windowed CLOCK), drifting-locality picks"),
+    "cfg5r": dict(kind="tier", B=4, T=250_000, n_kv=4, n_q=24, D=256, S=64, k=2048, L=1024,
+                  kv="i8", layers=1, seed=1005, warm_steps=64, steps=256, policy="lru", slots=4096,
+                  page_tokens=64, pool_pages=1024,
+                  workload="4 seq x 250,000 tokens; cfg2 layer shape; mixed residency: pages of 64 "
+                           "tokens, the 1,024 most recent middle pages of each sequence's 3,907 "
+                           "resident on the GPU and read in place, "
+                           "the rest int4 host-RAM records read zero-copy through an LRU hot buffer "
+                           "of 4,096 slots; drifting-locality picks"),
     "cfg3": dict(kind="block", B=1, T=1_048_576, n_kv=2, n_q=16, D=256, k=512, layers=12,
                  seed=1003,
                  workload="1 seq x 1,048,576 tokens; 12 QSA layers; 2 KV x 16 q heads, head_dim "
@@ -291,6 +299,162 @@ def rocprof_summary(path, out):
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_cores() -> int:
+    """CPUs this process may run on (the box's share), capped at 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def read_ceiling(buf: torch.Tensor, nbytes: int, reps: int = 20):
+    """The library's plain streaming read (sparsekv_read_bytes) over nbytes of
+    a device buffer, best of a few grid sizes: the rate a kernel that only
+    reads those bytes reaches on this GPU, each launch timed by its own
+    events."""
+    nb = min(nbytes, buf.numel() * buf.element_size()) // 16 * 16
+    best = None
+    sink = torch.zeros(8192, dtype=torch.int32, device="cuda")
+    for n_wg in (2048, 4096, 8192):
+        for _ in range(3):
+            skv.read_bytes(buf.data_ptr(), nb, sink, n_wg)
+        skv.timer_enable(True)
+        for _ in range(reps):
+            skv.read_bytes(buf.data_ptr(), nb, sink, n_wg)
+        ms, n = skv.timer_read()
+        skv.timer_enable(False)
+        us = ms * 1e3 / max(1, n)
+        if best is None or us < best["avg_launch_us"]:
+            best = {"bytes": nb, "n_wg": n_wg, "avg_launch_us": round(us, 2),
+                    "GBps": round(nb / us / 1e3, 1), "frac": round(nb / us / 1e3 / PEAK_HBM_GBS, 4),
+                    "launches_timed": n}
+    return best
+
+
+def _hip_runtime():
+    """The HIP runtime library this process already uses (torch loaded it)."""
+    import ctypes
+    with open("/proc/self/maps") as f:
+        for ln in f:
+            path = ln.split()[-1]
+            if "libamdhip64.so" in path and os.path.exists(path):
+                return ctypes.CDLL(path)
+    return None
+
+
+def zero_copy_read(mib: int, reps: int = 20):
+    """The library's plain streaming read over `mib` MiB of pinned, device-mapped
+    host memory (hipHostMalloc, its device address from
+    hipHostGetDevicePointer): the rate a kernel that only reads host memory
+    reaches over this GPU's link; also the known-size read the IO counters are
+    calibrated on."""
+    import ctypes
+    hip = _hip_runtime()
+    if hip is None:
+        return None
+    nb = mib << 20
+    hptr, dptr = ctypes.c_void_p(), ctypes.c_void_p()
+    if hip.hipHostMalloc(ctypes.byref(hptr), ctypes.c_size_t(nb), ctypes.c_uint(0x1 | 0x2)) != 0:
+        return None
+    try:
+        ctypes.memset(hptr, 1, nb)
+        if hip.hipHostGetDevicePointer(ctypes.byref(dptr), hptr, ctypes.c_uint(0)) != 0 or not dptr.value:
+            return None
+        sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+        for _ in range(3):
+            skv.read_bytes(dptr.value, nb, sink, 1024)
+        skv.timer_enable(True)
+        for _ in range(reps):
+            skv.read_bytes(dptr.value, nb, sink, 1024)
+        ms, n = skv.timer_read()
+        skv.timer_enable(False)
+        torch.cuda.synchronize()
+        us = ms * 1e3 / max(1, n)
+        return {"bytes": nb, "n_wg": 1024, "avg_launch_us": round(us, 2), "GBps": round(nb / us / 1e3, 2),
+                "launches_timed": n}
+    finally:
+        torch.cuda.synchronize()
+        hip.hipHostFree(hptr)
+
+
+def _oracle_seq_worker(a):
+    """One process of the all-core oracle run: `reps` layer-steps of one
+    sequence (query sketch, exact keys, selection, attention over its gathered
+    rows), inputs memory-mapped from files the parent wrote."""
+    d, b, T, S, k, L, group, sm, reps = a
+    import oracle
+    from threadpoolctl import threadpool_limits
+    ld = lambda name: np.load(os.path.join(d, "%s_%d.npy" % (name, b)), mmap_mode="r")
+    q, codes, sks = ld("q"), ld("codes"), ld("sks")
+    basis = np.load(os.path.join(d, "basis.npy"))
+    kr, vr, ks, vs = ld("kr"), ld("vr"), ld("ks"), ld("vs")
+    with threadpool_limits(limits=1):
+        t = time.perf_counter()
+        for _ in range(reps):
+            qs, _ = oracle.query_sketch(q, basis, group)
+            keys = oracle.sketch_keys(qs, codes, sks, [T], S, k, L)
+            sel = oracle.select_tokens(keys[0], T, S, k, L)
+            oracle.sparse_attention(q[0], kr, vr, ks, vs, np.arange(sel.size), sm, group, "i8")
+        return time.perf_counter() - t
+
+
+def cpu_baseline_all_cores(layer: Layer, cfg, seq_step_s: float, min_seconds=10.0):
+    """The same oracle layer-step with its sequences spread over the host's
+    cores (one process per sequence, each limited to one BLAS thread); inputs
+    are written once to memory-mapped files, outside the timed region."""
+    import multiprocessing as mp
+    import shutil
+    import tempfile
+    import oracle
+    c = layer.case
+    n = min(c.B, host_cores())
+    if n < 2 or cfg.get("M") or cfg["kind"] != "token":
+        return None
+    d = tempfile.mkdtemp(prefix="skv_oracle_", dir="/dev/shm" if os.path.isdir("/dev/shm") else None)
+    try:
+        q = c.q.cpu().numpy()
+        basis = c.basis.cpu().numpy()
+        np.save(os.path.join(d, "basis.npy"), basis)
+        qs, _ = oracle.query_sketch(q, basis, c.group)
+        keys = oracle.sketch_keys(qs, c.codes.cpu().numpy(), c.sk_scale.cpu().numpy(), c.lens, c.S, c.k, c.L)
+        for b in range(c.B):
+            sel = oracle.select_tokens(keys[b], c.lens[b], c.S, c.k, c.L)
+            ii = torch.from_numpy(sel).cuda()
+            for name, t in (("kr", c.k_cache), ("vr", c.v_cache), ("ks", c.k_scale), ("vs", c.v_scale)):
+                np.save(os.path.join(d, "%s_%d.npy" % (name, b)), t[b].index_select(0, ii).cpu().numpy())
+            np.save(os.path.join(d, "q_%d.npy" % b), q[b:b + 1])
+            np.save(os.path.join(d, "codes_%d.npy" % b), c.codes[b:b + 1].cpu().numpy())
+            np.save(os.path.join(d, "sks_%d.npy" % b), c.sk_scale[b:b + 1].cpu().numpy())
+        # repetitions so that the parallel run takes about min_seconds
+        reps = max(1, int(min_seconds / max(1e-3, seq_step_s * c.B / n)))
+        reps = min(reps, 20)
+        args = [(d, b, c.lens[b], c.S, c.k, c.L, c.group, layer.sm, reps) for b in range(c.B)]
+        with mp.get_context("spawn").Pool(n) as pool:
+            pool.map(_oracle_seq_worker, [(d, b, c.lens[b], c.S, c.k, c.L, c.group, layer.sm, 1)
+                                          for b in range(n)])   # start-up outside the timing
+            t = time.perf_counter()
+            pool.map(_oracle_seq_worker, args, chunksize=1)
+            wall = time.perf_counter() - t
+        return dict(value=reps / wall, unit="layer-steps/s", cores=n, kind="oracle",
+                    sample="%d repetitions of one full layer-step of layer 0 (%d sequences x %d tokens), "
+                           "one process per sequence on %d cores" % (reps, c.B, c.T_max, n),
+                    seconds=wall)
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
 
 
 def cpu_baseline(layer: Layer, cfg):
@@ -657,11 +821,30 @@ def bench_tier(cfg, args):
     desc = skv.token_desc(B, T, cfg["n_kv"], cfg["n_q"], cfg["D"], topk=k, n_sink=S, n_tail=L)
     n_slots = cfg.get("slots", c.n_slots)
     lru = cfg.get("policy") == "lru"
-    tier = skv.Tier(desc, T, n_slots, 1, policy=skv.SKV_TIER_LRU if lru else skv.SKV_TIER_CLOCK)
+    P, pool = cfg.get("page_tokens", 0), cfg.get("pool_pages", 0)
+    tier = skv.Tier(desc, T, n_slots, 1, policy=skv.SKV_TIER_LRU if lru else skv.SKV_TIER_CLOCK,
+                    page_tokens=P, pool_pages=pool)
+    mapped = []
     try:
         tier.host_records()[:] = c.records.cpu().numpy()
         tier.load_resident(c.res_k, c.res_v, c.res_ks, c.res_vs)
         res = tier.resident()
+        if pool:
+            # mixed residency: the most recent middle pages of every sequence
+            # stay on the GPU (their int8 rows copied into the pool), the rest
+            # are placeholders read through the hot buffer
+            last = (T - L) // P - 1
+            mapped = list(range(last - pool + 1, last + 1))
+            log("mapping %d pages per sequence" % len(mapped))
+            for b in range(B):
+                for j0 in range(0, len(mapped), 128):
+                    part = mapped[j0:j0 + 128]
+                    rk, rks, rv, rvs = synth.tier_page_rows(B, T, n_kv=cfg["n_kv"], D=cfg["D"], seed=cfg["seed"],
+                                                            page_tokens=P, pages=[(b, g) for g in part],
+                                                            device="cuda")
+                    for j, g in enumerate(part):
+                        tier.map_page(b, g, j0 + j, rk[j], rv[j], rks[j], rvs[j])
+                    torch.cuda.synchronize()
         cap = skv.select_capacity(desc)
         nst = warm + steps
         if M == 1:
@@ -693,7 +876,7 @@ def bench_tier(cfg, args):
 
         def attend():
             if M == 1:
-                skv.attend(desc, q, res, rows, nsel, sm, out, ws)
+                tier.attend(q, rows, nsel, sm, out, ws)
             else:
                 skv.attend_multi(desc, M, q, res, rows, nsel, sm, out, ws)
         log("warmup", warm)
@@ -723,8 +906,8 @@ def bench_tier(cfg, args):
         e1.record()
         e1.synchronize()
         rsecs = e0.elapsed_time(e1) / 1e3
-        # the host-record fetch kernel alone, timed by its own dispatches (a
-        # third replay of the same picks: the same misses)
+        # the fused resolver (resolve + zero-copy fetch), timed by its own
+        # dispatches (a third replay of the same picks: the same misses)
         tier.reset()
         for s_ in range(warm):
             resolve(s_)
@@ -734,14 +917,17 @@ def bench_tier(cfg, args):
         f_ms, f_n = skv.timer_read()
         skv.timer_enable(False)
         assert skv.check(ws) == 0
+        zc = zero_copy_read(64)
         cpu = None
         if not args.no_cpu_baseline:
             log("cpu baseline (oracle)")
             cpu = _tier_cpu_baseline(cfg, c, mpicks, warm, tier.host_records()[0], lru, n_slots,
-                                     q[0].cpu().numpy() if M > 1 else None)
+                                     q[0].cpu().numpy() if M > 1 else None, pages=mapped)
+            cpu["cpu_model"] = cpu_model()
     finally:
         tier.close()
     hits, misses = st1.hits - st0.hits, st1.misses - st0.misses
+    in_place = st1.in_place - st0.in_place
     hbytes = st1.host_bytes - st0.host_bytes
     res_line = {
         "metric": METRIC,
@@ -758,13 +944,16 @@ def bench_tier(cfg, args):
         "data": "synthetic",
         "config": dict({"workload": cfg["workload"], "name": args.config, "batch": B, "ctx": T,
                         "hot_slots_per_seq": n_slots, "policy": "lru" if lru else "windowed-clock"},
+                       **({"page_tokens": P, "resident_pages_per_seq": pool} if pool else {}),
                        **({"query_tokens_per_seq": M} if M > 1 else {})),
         "tier": {"miss_rate": round(misses / max(1, hits + misses), 4), "hits": hits, "misses": misses,
+                 "in_place": in_place,
                  "host_bytes_per_step": round(hbytes / steps),
                  "pcie_GBps_over_step": round(hbytes / secs / 1e9, 2),
                  "resolve_us": round(rsecs / steps * 1e6, 2),
                  "pcie_GBps_during_resolve": round(hbytes / rsecs / 1e9, 2),
-                 "pcie_peak_GBps": 64.0},
+                 "pcie_peak_GBps": 64.0,
+                 "zero_copy_read": zc},
         "roofline": None,
         "cpu_baseline": cpu,
     }
@@ -773,7 +962,7 @@ def bench_tier(cfg, args):
     if f_n:
         f_s = f_ms / 1e3 / f_n
         per = hbytes / steps
-        res_line["roofline"] = {"kernel": "tier_fetch", "bound": "pcie",
+        res_line["roofline"] = {"kernel": "tier_resolve (resolve + zero-copy fetch, one kernel)", "bound": "pcie",
                                 "achieved": round(per / f_s / 1e9, 2), "peak": PCIE5_X16_GBS,
                                 "unit": "GB/s", "frac": round(per / f_s / 1e9 / PCIE5_X16_GBS, 4),
                                 "traffic": None, "bytes_per_launch": round(per),
@@ -781,7 +970,8 @@ def bench_tier(cfg, args):
     print(json.dumps(res_line), flush=True)
 
 
-def _tier_cpu_baseline(cfg, c, lists, warm, records_b, lru, n_slots, qm=None, min_seconds=10.0):
+def _tier_cpu_baseline(cfg, c, lists, warm, records_b, lru, n_slots, qm=None, min_seconds=10.0,
+                       pages=()):
     """The oracle's host-tier layer-step on sequence 0 (hot-buffer resolve with
     its policy, then attention over the resident rows and the fetched host
     records; with several query tokens each query's list and attention),
@@ -793,11 +983,34 @@ def _tier_cpu_baseline(cfg, c, lists, warm, records_b, lru, n_slots, qm=None, mi
     M = lists.shape[2]
     T1 = T - M + 1
     tier = oracle.residency.LruTier(n_slots, T) if lru else oracle.ClockTier(n_slots, T, window=1)
+    paged = None
+    if pages:
+        # sequence 0's mapped pages: the page table and the int8 rows they hold
+        P = cfg["page_tokens"]
+        paged = oracle.residency.PagedTier(tier, P, (T + P - 1) // P)
+        k8 = np.zeros((T, cfg["n_kv"], cfg["D"]), np.int8)
+        v8 = np.zeros_like(k8)
+        ks8 = np.zeros((T, cfg["n_kv"]), np.float16)
+        vs8 = np.zeros_like(ks8)
+        rk, rks, rv, rvs = synth.tier_page_rows(cfg["B"], T, n_kv=cfg["n_kv"], D=cfg["D"], seed=cfg["seed"],
+                                                page_tokens=P, pages=[(0, g) for g in pages], device="cuda")
+        for j, g in enumerate(pages):
+            paged.map_page(g, j)
+            m = min(P, T - g * P)
+            k8[g * P:g * P + m], v8[g * P:g * P + m] = rk[j, :m].cpu().numpy(), rv[j, :m].cpu().numpy()
+            ks8[g * P:g * P + m], vs8[g * P:g * P + m] = rks[j, :m].cpu().numpy(), rvs[j, :m].cpu().numpy()
+        for arr, x in zip((k8, v8, ks8, vs8), (c.res_k[0], c.res_v[0], c.res_ks[0], c.res_vs[0])):
+            x = x.cpu().numpy()
+            arr[:S] = x[:S]
+            arr[T - L:] = x[S:]
 
     def full(s_, j):
         return np.concatenate([np.arange(S), lists[s_, 0, j], np.arange(T1 + j - L, T1 + j)])
     for s_ in range(warm):
-        oracle.multiquery.tier_resolve_lists(tier, [full(s_, j) for j in range(M)], T, S, L, s_)
+        if paged is not None:
+            paged.step(lists[s_, 0, 0], s_)
+        else:
+            oracle.multiquery.tier_resolve_lists(tier, [full(s_, j) for j in range(M)], T, S, L, s_)
     qs = [c.q[0].cpu().numpy()] if M == 1 else [qm[j] for j in range(M)]
     rk, rv = c.res_k[0].cpu().numpy(), c.res_v[0].cpu().numpy()
     rks, rvs = c.res_ks[0].cpu().numpy(), c.res_vs[0].cpu().numpy()
@@ -808,10 +1021,15 @@ def _tier_cpu_baseline(cfg, c, lists, warm, records_b, lru, n_slots, qm=None, mi
             s_ = warm + reps
             idx = [full(s_, j) for j in range(M)]
             t0 = time.perf_counter()
-            oracle.multiquery.tier_resolve_lists(tier, idx, T, S, L, s_)
-            for j in range(M):
-                oracle.tier_attention(qs[j], records_b, rk, rv, rks, rvs, idx[j], T, S, L, sm,
-                                      cfg["n_q"] // cfg["n_kv"], cfg["D"])
+            if paged is not None:
+                paged.step(lists[s_, 0, 0], s_)
+                oracle.paged_tier_attention(qs[0], records_b, k8, v8, ks8, vs8, idx[0], T, S, L, paged.block,
+                                            paged.P, sm, cfg["n_q"] // cfg["n_kv"], cfg["D"])
+            else:
+                oracle.multiquery.tier_resolve_lists(tier, idx, T, S, L, s_)
+                for j in range(M):
+                    oracle.tier_attention(qs[j], records_b, rk, rv, rks, rvs, idx[j], T, S, L, sm,
+                                          cfg["n_q"] // cfg["n_kv"], cfg["D"])
             t_total += time.perf_counter() - t0
             reps += 1
     return {"value": round(reps / t_total / B, 4), "unit": "layer-steps/s", "cores": 1,
@@ -973,10 +1191,24 @@ def main():
             torch.bitwise_not(src, out=dst)
         torch.cuda.synchronize()
         res["calib_copy_bytes"] = CALIB_BYTES
+    if not multi:
+        # the plain-read ceiling of the scan's bytes (a device buffer of layer 0)
+        rc = read_ceiling(layers[0].case.k_cache, ab["scan"])
+        rc["scan_kernel_over_ceiling"] = round(rc["avg_launch_us"] / (score_s * 1e6), 4)
+        res["read_ceiling"] = rc
     if not args.no_cpu_baseline:
-        log("cpu baseline (oracle)")
+        log("cpu baseline (oracle, one core)")
         cb = cpu_baseline(layers[0], cfg)
-        res["cpu_baseline"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in cb.items()}
+        cb = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in cb.items()}
+        cb["cpu_model"] = cpu_model()
+        log("cpu baseline (oracle, all cores)")
+        allc = cpu_baseline_all_cores(layers[0], cfg, 1.0 / cb["value"] / cfg["B"]) if not multi else None
+        if allc:
+            one = cb
+            cb = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in allc.items()}
+            cb["cpu_model"] = one["cpu_model"]
+            cb["one_core"] = {k: one[k] for k in ("value", "cores", "sample", "seconds")}
+        res["cpu_baseline"] = cb
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

@@ -47,10 +47,12 @@
 extern "C" {
 #endif
 
-#define SPARSEKV_ABI_VERSION 5   /* 3: multi-query step, prefill over host K/V, tier policy field;
+#define SPARSEKV_ABI_VERSION 6   /* 3: multi-query step, prefill over host K/V, tier policy field;
                                     4: tier append (host records sized by max_ctx, tail ring),
                                        multi-query tier resolve and attention;
-                                    5: the step without a workspace argument */
+                                    5: the step without a workspace argument;
+                                    6: tier page residency (desc fields, map / unmap, in_place
+                                       counter), tier_attend, tier_host_ptr */
 
 typedef int32_t skv_status;
 enum {
@@ -77,6 +79,7 @@ enum {
   SKV_FLAG_INDEX_RANGE = 1u << 1,  /* attend: an index outside [0, rows) or n_sel > cap (skipped/clamped) */
   SKV_FLAG_TOPK_SLOW = 1u << 2,    /* informational: a sequence needed the exact slow select path */
   SKV_FLAG_TIER_INPUT = 1u << 3,   /* tier: a pick outside [0, ctx) or unsorted input (skipped) */
+  SKV_FLAG_TIER_WAIT = 1u << 4,    /* tier: a fetch workgroup stopped waiting for its resolver (rows not fetched) */
 };
 
 /*
@@ -397,13 +400,29 @@ skv_status sparsekv_check(void* ws, size_t ws_bytes, void* stream, uint32_t* fla
  * the merge of its partials); any other nonzero value (SKV_TIMER_STREAM) times
  * the dominant kernel of a call: the streaming score-and-collect kernel (the
  * one that reads the whole index in sparsekv_score_topk, sparsekv_step,
- * sparsekv_step_multi), the host-record fetch of sparsekv_tier_resolve and the
+ * sparsekv_step_multi), the resolver of sparsekv_tier_resolve (it fetches the misses) and the
  * kernel of sparsekv_append and sparsekv_tier_append.  Up to 4096 launches are recorded.  Enabling again
  * discards earlier records.  sparsekv_timer_read synchronizes on the recorded
  * events and returns the summed kernel time (ms) and the number of launches. */
 #define SKV_TIMER_STREAM 1
 #define SKV_TIMER_ATTEND 2
 skv_status sparsekv_timer_enable(int enable);
+/* ---- measurement aid: a plain streaming read ---------------------------------
+ * Not a step of the method: the reference rate for its dominant read.  Page
+ * "3.14M Context on 3x 3090 ...", section "What Needs to Stay in VRAM" (the
+ * index scan is the per-step read that grows with context) and page "8 agents
+ * x 250K ...", section "The mechanism" (misses read host memory over PCIe):
+ * reading the same bytes with no arithmetic bounds what the scan (device
+ * memory) or the zero-copy fetch (mapped host memory) can reach.
+ *   src    device address of device memory or of mapped pinned host memory,
+ *          16-byte aligned; every 16-byte word of [src, src + bytes) is loaded
+ *          once (bytes a multiple of 16)
+ *   sink   device uint32 [n_wg]: each workgroup stores the xor of its words
+ *   n_wg   workgroups of 256 threads, 1 .. SKV_READ_MAX_WG
+ * Timed by sparsekv_timer_enable(SKV_TIMER_STREAM) like the dominant kernels. */
+#define SKV_READ_MAX_WG 65536
+skv_status sparsekv_read_bytes(const void* src, size_t bytes, uint32_t* sink, int32_t n_wg,
+                               void* stream);
 skv_status sparsekv_timer_read(double* total_ms, int64_t* launches);
 
 /* ---- host-RAM tier (optional) ----------------------------------------------
@@ -425,7 +444,8 @@ skv_status sparsekv_timer_read(double* total_ms, int64_t* launches);
  * operation one fp32 IEEE operation (c*g and gmax*7 are exact).
  *
  * Resident rows per sequence (an skv_kv_view, int8 + fp16 row scales):
- *   [0, S) sinks, [S, S+L) tail, [S+L, S+L+n_slots) hot slots.  The tail is a
+ *   [0, S) sinks, [S, S+L) tail, [S+L, S+L+n_slots) hot slots,
+ *   [S+L+n_slots, S+L+n_slots + pool_pages*page_tokens) the page pool.  The tail is a
  *   ring anchored at the creation context ctx0 = desc.ctx: tail position p
  *   sits in row S + ((p - ctx0) mod L), so at creation row S+i holds position
  *   ctx0-L+i.  The caller loads sinks and tail once, before any append, with
@@ -436,7 +456,20 @@ skv_status sparsekv_timer_read(double* total_ms, int64_t* launches);
  * buffer are hits (ref=1, last=s); the misses, in ascending position order,
  * each take the first slot the hand reaches that is empty, or unused for the
  * last W steps (last <= s-W) and unreferenced -- a referenced slot outside
- * the window has its reference cleared as the hand passes it. */
+ * the window has its reference cleared as the hand passes it.
+ *
+ * Page residency (page "vLLM's Hybrid HiSparse Triples Concurrent Requests on
+ * Million-Token Contexts", section "Three residency states, one block pool"):
+ * with page_tokens P > 0 the positions of a sequence form pages of P
+ * (page = p / P) and each page is either mapped to a block of the sequence's
+ * device pool -- its int8 rows resident, read in place -- or a placeholder
+ * whose picks go through the hot buffer from host memory.  Every page mapped
+ * is full residency, some mapped is mixed residency, none is no residency
+ * (the default); sinks and tail are resident in every state.  The caller
+ * decides, between steps, which pages to map (sparsekv_tier_map_page copies
+ * a page's rows into a block) and which to give up (sparsekv_tier_unmap_page),
+ * e.g. under memory pressure; a middle pick of a mapped page p sits in
+ * resident row S+L+n_slots + block*P + p%P and counts as in_place. */
 typedef struct skv_tier skv_tier;
 
 /* Hot-buffer policies.  SKV_TIER_CLOCK: the windowed CLOCK above.
@@ -461,6 +494,9 @@ typedef struct {
                              already pinned and mapped (e.g. hipHostMalloc) */
   int32_t policy;         /* SKV_TIER_*; a struct_size that ends before this
                              field means SKV_TIER_CLOCK */
+  int32_t page_tokens;    /* P: 0 (no page table) or a power of two in [16, 4096];
+                             a struct_size that ends before pool_pages means 0 */
+  int32_t pool_pages;     /* pool blocks of P rows per sequence (0 with P = 0) */
 } skv_tier_desc;
 
 typedef struct {
@@ -469,13 +505,16 @@ typedef struct {
   int64_t hits;
   int64_t misses;
   int64_t host_bytes;     /* bytes read from host memory = misses * H_kv * record */
+  int64_t in_place;       /* picks read in place from mapped pages; picks = in_place + hits + misses */
 } skv_tier_stats;
 
 /* Allocates the tier (device slot state + resident rows; host records unless
  * given).  Host call, synchronous.  SKV_ERR_OOM / SKV_ERR_HOST_MEMORY on failure. */
 skv_status sparsekv_tier_create(const skv_tier_desc* d, skv_tier** out);
-/* Host pointer of the host records (the caller fills them before resolving). */
+/* Host pointer of the host records (the caller fills them before resolving);
+ * sparsekv_tier_host_ptr is the same call under its other name. */
 void* sparsekv_tier_host_records(skv_tier* t);
+void* sparsekv_tier_host_ptr(skv_tier* t);
 /* Device view of the resident rows. */
 skv_status sparsekv_tier_resident(skv_tier* t, skv_kv_view* view);
 /* Copies the caller's sink+tail rows ([B][S+L][H_kv][D] int8 and
@@ -483,10 +522,15 @@ skv_status sparsekv_tier_resident(skv_tier* t, skv_kv_view* view);
 skv_status sparsekv_tier_load_resident(skv_tier* t, const int8_t* k, const int8_t* v,
                                        const uint16_t* k_scale, const uint16_t* v_scale,
                                        void* stream);
-/* One step: for each sequence, resolves the selected positions idx[b][0..n_sel)
- * (ascending) against the hot buffer, fetches the misses from host memory into
- * their slots, and writes rows[b][i] = the resident row of idx[b][i].  The
- * caller then runs sparsekv_attend on the resident view with rows, n_sel. */
+/* One step, one kernel (the fused resolver of page "vLLM's Hybrid HiSparse
+ * ...", section "Three residency states, one block pool"): for each sequence,
+ * resolves the selected positions idx[b][0..n_sel) (ascending) -- sinks and
+ * tail resident, middle picks of mapped pages in place, the others against
+ * the hot buffer (hits refresh their entry, misses take slots) -- reads each
+ * missed record from host memory into its slot as int8 rows, and writes
+ * rows[b][i] = the resident row of idx[b][i].  The caller then runs
+ * sparsekv_tier_attend (or sparsekv_attend on the resident view) with rows,
+ * n_sel. */
 skv_status sparsekv_tier_resolve(skv_tier* t, const int32_t* idx, const int32_t* n_sel,
                                  int32_t step, int32_t* rows, void* stream);
 /* Several query tokens per sequence (a step verifying drafted tokens; page "8
@@ -507,6 +551,27 @@ skv_status sparsekv_tier_resolve(skv_tier* t, const int32_t* idx, const int32_t*
 skv_status sparsekv_tier_resolve_multi(skv_tier* t, int32_t n_query, const int32_t* idx,
                                        const int32_t* n_sel, int32_t step, int32_t* rows,
                                        void* stream);
+/* Attention over the tier's resident rows: sparsekv_attend on the view
+ * sparsekv_tier_resident returns, with rows [B][cap] and n_sel from
+ * sparsekv_tier_resolve (page "8 agents x 250K ...", section "The mechanism":
+ * exact attention on the kept rows, wherever they are resident).  ws as for
+ * sparsekv_attend with the tier's layer descriptor. */
+skv_status sparsekv_tier_attend(skv_tier* t, const void* q, const int32_t* rows,
+                                const int32_t* n_sel, float sm_scale, float* out, void* ws,
+                                size_t ws_bytes, void* stream);
+/* Page residency.  map_page makes page `page` of sequence `seq` resident in
+ * pool block `block` (0 <= block < pool_pages): when k is given, its rows are
+ * first copied from device arrays k, v [P][H_kv][D] int8 and k_scale,
+ * v_scale [P][H_kv] fp16 (positions page*P .. page*P+P-1, the rows a plain
+ * int8 cache holds for them); with k, v, k_scale, v_scale all NULL the block
+ * must already hold them.  unmap_page returns the page to host-only (its
+ * block becomes free).  Both are enqueued on stream (the next resolve on that
+ * stream sees them); SKV_ERR_STATE if the page is already mapped / not
+ * mapped or the block is taken; SKV_ERR_INVALID for out-of-range arguments. */
+skv_status sparsekv_tier_map_page(skv_tier* t, int32_t seq, int32_t page, int32_t block,
+                                  const int8_t* k, const int8_t* v, const uint16_t* k_scale,
+                                  const uint16_t* v_scale, void* stream);
+skv_status sparsekv_tier_unmap_page(skv_tier* t, int32_t seq, int32_t page, void* stream);
 /* Decode-step append for a tier (page "8 agents x 250K ...", section "The
  * mechanism": every token's K/V also goes to host RAM as int4 in 64-dim groups;
  * the GPU keeps the sinks and the recent tail).  For every sequence b the new

@@ -17,6 +17,7 @@ from .gen import (  # noqa: F401
     make_token_case,
     make_block_case,
     make_tier_case,
+    tier_page_rows,
     drift_picks,
     draft_picks,
     multi_queries,

@@ -421,6 +421,39 @@ def make_tier_case(B: int, T: int, *, n_kv: int, n_q: int, D: int, S: int, k: in
                     q=q.to(device), records=rec, res_k=rk, res_v=rv, res_ks=rks, res_vs=rvs)
 
 
+def tier_page_rows(B: int, T: int, *, n_kv: int, D: int, seed: int, page_tokens: int, pages,
+                   device="cpu"):
+    """int8 rows + fp16 row scales of whole pages of a tier case: the same
+    tokens as make_tier_case's host records (same random streams), stored the
+    way a plain int8 cache holds them.  pages: list of (sequence, page);
+    returns k8, ks, v8, vs shaped [len(pages)][page_tokens][n_kv][D] / [..][n_kv]
+    (positions past T are zero rows)."""
+    P = int(page_tokens)
+    assert CHUNK % P == 0
+    n = len(pages)
+    k8 = torch.zeros((n, P, n_kv, D), dtype=torch.int8, device=device)
+    v8 = torch.zeros((n, P, n_kv, D), dtype=torch.int8, device=device)
+    ks = torch.zeros((n, P, n_kv), dtype=torch.float16, device=device)
+    vs = torch.zeros((n, P, n_kv), dtype=torch.float16, device=device)
+    cache = {}
+    for j, (b, g) in enumerate(pages):
+        p0 = g * P
+        if p0 >= T:
+            continue
+        c = p0 // CHUNK
+        if (b, c) not in cache:
+            cache.clear()
+            xk = _randn(device, seed, (_T_HK, b, c), (CHUNK, n_kv, D))
+            xv = _randn(device, seed, (_T_HV, b, c), (CHUNK, n_kv, D))
+            cache[(b, c)] = (_rows_to_i8(xk), _rows_to_i8(xv))
+        (rk, rks), (rv, rvs) = cache[(b, c)]
+        o = p0 - c * CHUNK
+        m = min(P, T - p0)
+        k8[j, :m], ks[j, :m] = rk[o:o + m], rks[o:o + m]
+        v8[j, :m], vs[j, :m] = rv[o:o + m], rvs[o:o + m]
+    return k8, ks, v8, vs
+
+
 def drift_picks(B: int, T: int, S: int, L: int, k: int, n_steps: int, seed: int, *,
                 sigma_c: float = 256.0, window: int = 65536, rho: float = 0.165) -> np.ndarray:
     """Drifting-locality pick schedule, int32 [n_steps][B][k], each row sorted.

@@ -62,7 +62,11 @@ def test_struct_sizes_match_header(skv):
     # the C structs are plain int32 / pointer layouts; sizes pinned here
     assert ctypes.sizeof(skv.LayerDesc) == 15 * 4
     assert ctypes.sizeof(skv.KVView) == 5 * 8
-    assert skv.abi_version() == 5
+    # skv_tier_desc: size, layer, ctx, n_slots, window, (pad) host pointer, policy,
+    # page_tokens, pool_pages, (pad); skv_tier_stats: six int64
+    assert ctypes.sizeof(skv.TierDesc) == 104
+    assert ctypes.sizeof(skv.TierStats) == 6 * 8
+    assert skv.abi_version() == 6
 
 
 def test_capacity_and_workspace(skv):
@@ -206,9 +210,25 @@ def test_tier_policy_checks(skv):
     assert lib.sparsekv_tier_create(ctypes.byref(td), ctypes.byref(h)) == 1
     td = skv.TierDesc(ctypes.sizeof(skv.TierDesc), layer, 10_000, 200, 1, None, 7)
     assert lib.sparsekv_tier_create(ctypes.byref(td), ctypes.byref(h)) == 1
-    td = skv.TierDesc(ctypes.sizeof(skv.TierDesc) - 8, layer, 10_000, 60, 1, None, skv.SKV_TIER_LRU)
+    td = skv.TierDesc(skv.TierDesc.policy.offset, layer, 10_000, 60, 1, None, skv.SKV_TIER_LRU)
     # read as CLOCK: 60 slots do not exceed window * topk = 64
     assert lib.sparsekv_tier_create(ctypes.byref(td), ctypes.byref(h)) == 1
+
+
+def test_tier_page_checks(skv):
+    """Page sizes must be 0 or a power of two in [16, 4096], a pool needs a
+    page size; map / unmap / attend reject a NULL tier on the host."""
+    lib = skv.lib()
+    layer = skv.token_desc(2, 10_000, 4, 24, 256, topk=64, n_sink=4, n_tail=8)
+    h = ctypes.c_void_p()
+    for P, pool in ((48, 4), (8, 4), (8192, 1), (0, 4), (64, -1)):
+        td = skv.TierDesc(ctypes.sizeof(skv.TierDesc), layer, 10_000, 200, 1, None, 0, P, pool)
+        assert lib.sparsekv_tier_create(ctypes.byref(td), ctypes.byref(h)) == 1, (P, pool)
+        assert b"page" in lib.sparsekv_last_error() or b"pool" in lib.sparsekv_last_error()
+    assert lib.sparsekv_tier_map_page(None, 0, 0, 0, None, None, None, None, None) == 1
+    assert lib.sparsekv_tier_unmap_page(None, 0, 0, None) == 1
+    assert lib.sparsekv_tier_attend(None, None, None, None, 1.0, None, None, 0, None) == 1
+    assert lib.sparsekv_tier_host_ptr(None) is None
 
 
 def test_tier_append_null_checks(skv):

@@ -47,7 +47,7 @@ def _run(B, T, S, L, k, n_slots, n_steps, check_out_steps, seed, window=1, devic
                                      np.broadcast_to(np.arange(T - L, T), (B, L))], axis=1).astype(np.int32)
             idx = torch.from_numpy(idx_np).cuda()
             tier.resolve(idx, nsel, s, rows)
-            skv.attend(desc, q, res, rows, nsel, sm, out, ws)
+            tier.attend(q, rows, nsel, sm, out, ws)
             st = tier.stats()
             slots = tier.slots()
             h_s = m_s = 0

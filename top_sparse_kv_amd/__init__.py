@@ -165,6 +165,15 @@ def step_noalloc(desc, ctx_len, q, basis, qs, qs_scale, index_query, index_keys,
                                        _p(flags), _stream(stream)))
 
 
+def read_bytes(src_ptr: int, nbytes: int, sink, n_wg: int, stream=None):
+    """sparsekv_read_bytes: a plain streaming read of nbytes at device address
+    src_ptr (device memory or mapped pinned host memory); sink int32 device
+    tensor of >= n_wg elements."""
+    _dev(sink)
+    _check(lib().sparsekv_read_bytes(ctypes.c_void_p(src_ptr), int(nbytes), _p(sink), int(n_wg),
+                                     _stream(stream)))
+
+
 def workspace_size_multi(desc: LayerDesc, n_query: int) -> int:
     n = _lib.c_sz()
     _check(lib().sparsekv_workspace_size_multi(ctypes.byref(desc), int(n_query), ctypes.byref(n)))
@@ -269,10 +278,13 @@ class Tier:
     SKV_TIER_CLOCK (windowed CLOCK) or SKV_TIER_LRU."""
 
     def __init__(self, layer: LayerDesc, ctx: int, n_slots: int, window: int = 1,
-                 host_records: Optional[int] = None, policy: int = SKV_TIER_CLOCK):
+                 host_records: Optional[int] = None, policy: int = SKV_TIER_CLOCK,
+                 page_tokens: int = 0, pool_pages: int = 0):
         self.layer = layer
         d = TierDesc(ctypes.sizeof(TierDesc), layer, ctx, n_slots, window,
-                     ctypes.c_void_p(host_records) if host_records else None, policy)
+                     ctypes.c_void_p(host_records) if host_records else None, policy,
+                     page_tokens, pool_pages)
+        self.page_tokens, self.pool_pages = page_tokens, pool_pages
         h = ctypes.c_void_p()
         _check(lib().sparsekv_tier_create(ctypes.byref(d), ctypes.byref(h)))
         self._h = h
@@ -320,6 +332,24 @@ class Tier:
         _dev(idx, n_sel, rows)
         _check(lib().sparsekv_tier_resolve_multi(self._h, int(n_query), _p(idx), _p(n_sel),
                                                  int(step), _p(rows), _stream(stream)))
+
+    def attend(self, q, rows, n_sel, sm_scale, out, ws, stream=None):
+        """sparsekv_tier_attend: attention over the resident rows listed in rows."""
+        _dev(q, rows, n_sel, out, ws)
+        _check(lib().sparsekv_tier_attend(self._h, _p(q), _p(rows), _p(n_sel), float(sm_scale), _p(out),
+                                          _p(ws), ws.numel(), _stream(stream)))
+
+    def map_page(self, seq: int, page: int, block: int, k=None, v=None, k_scale=None, v_scale=None,
+                 stream=None):
+        """sparsekv_tier_map_page: page `page` of sequence `seq` resident in pool
+        block `block`; k, v [P][H_kv][D] int8 and scales [P][H_kv] (device), or
+        all None when the block already holds the rows."""
+        _dev(k, v, k_scale, v_scale)
+        _check(lib().sparsekv_tier_map_page(self._h, int(seq), int(page), int(block), _p(k), _p(v),
+                                            _p(k_scale), _p(v_scale), _stream(stream)))
+
+    def unmap_page(self, seq: int, page: int, stream=None):
+        _check(lib().sparsekv_tier_unmap_page(self._h, int(seq), int(page), _stream(stream)))
 
     def stats(self, stream=None) -> TierStats:
         s = TierStats()

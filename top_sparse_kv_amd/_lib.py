@@ -25,6 +25,7 @@ SKV_INDEX_SKETCH_INT4, SKV_INDEX_POOLED_BF16 = 0, 1
 SKV_KV_I8_ROWSCALE, SKV_KV_F16, SKV_KV_BF16 = 0, 1, 2
 SKV_Q_F16, SKV_Q_BF16 = 0, 1
 SKV_FLAG_CTX_RANGE, SKV_FLAG_INDEX_RANGE, SKV_FLAG_TOPK_SLOW, SKV_FLAG_TIER_INPUT = 1, 2, 4, 8
+SKV_FLAG_TIER_WAIT = 16
 SKV_TIER_CLOCK, SKV_TIER_LRU = 0, 1
 SKV_TIMER_STREAM, SKV_TIMER_ATTEND = 1, 2
 STATUS = {0: "SKV_OK", 1: "SKV_ERR_INVALID", 2: "SKV_ERR_UNSUPPORTED", 3: "SKV_ERR_WORKSPACE",
@@ -45,12 +46,13 @@ class KVView(ctypes.Structure):
 
 class TierDesc(ctypes.Structure):
     _fields_ = [("struct_size", c_u32), ("layer", LayerDesc), ("ctx", c_i32), ("n_slots", c_i32),
-                ("window", c_i32), ("host_records", c_vp), ("policy", c_i32)]
+                ("window", c_i32), ("host_records", c_vp), ("policy", c_i32),
+                ("page_tokens", c_i32), ("pool_pages", c_i32)]
 
 
 class TierStats(ctypes.Structure):
     _fields_ = [("steps", c_i64), ("picks", c_i64), ("hits", c_i64), ("misses", c_i64),
-                ("host_bytes", c_i64)]
+                ("host_bytes", c_i64), ("in_place", c_i64)]
 
 
 # (name, restype, argtypes) of every symbol include/sparsekv.h declares
@@ -74,6 +76,7 @@ SIGNATURES = [
     ("sparsekv_step_noalloc", c_i32, [P(LayerDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                       c_vp, P(KVView), c_vp, c_vp, ctypes.c_float, c_vp, c_vp,
                                       c_vp]),
+    ("sparsekv_read_bytes", c_i32, [c_vp, c_sz, c_vp, c_i32, c_vp]),
     ("sparsekv_workspace_size_multi", c_i32, [P(LayerDesc), c_i32, P(c_sz)]),
     ("sparsekv_step_multi", c_i32, [P(LayerDesc), c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                     P(KVView), c_vp, c_vp, ctypes.c_float, c_vp, c_vp, c_sz, c_vp]),
@@ -91,10 +94,14 @@ SIGNATURES = [
     ("sparsekv_timer_read", c_i32, [P(ctypes.c_double), P(c_i64)]),
     ("sparsekv_tier_create", c_i32, [P(TierDesc), P(c_vp)]),
     ("sparsekv_tier_host_records", c_vp, [c_vp]),
+    ("sparsekv_tier_host_ptr", c_vp, [c_vp]),
     ("sparsekv_tier_resident", c_i32, [c_vp, P(KVView)]),
     ("sparsekv_tier_load_resident", c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     ("sparsekv_tier_resolve", c_i32, [c_vp, c_vp, c_vp, c_i32, c_vp, c_vp]),
     ("sparsekv_tier_resolve_multi", c_i32, [c_vp, c_i32, c_vp, c_vp, c_i32, c_vp, c_vp]),
+    ("sparsekv_tier_attend", c_i32, [c_vp, c_vp, c_vp, c_vp, ctypes.c_float, c_vp, c_vp, c_sz, c_vp]),
+    ("sparsekv_tier_map_page", c_i32, [c_vp, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    ("sparsekv_tier_unmap_page", c_i32, [c_vp, c_i32, c_i32, c_vp]),
     ("sparsekv_tier_append", c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     ("sparsekv_tier_stats", c_i32, [c_vp, P(TierStats), c_vp]),
     ("sparsekv_tier_slots", c_i32, [c_vp, c_vp, c_vp]),

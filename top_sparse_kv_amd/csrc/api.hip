@@ -3,6 +3,8 @@
 // enqueued; device-side conditions are recorded in the workspace flag word.
 #include "skv_internal.h"
 
+#include <hip/hip_ext.h>
+
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -168,6 +170,34 @@ __global__ void flags_handoff_kernel(uint32_t* __restrict__ f, uint32_t* __restr
   const uint32_t v = *f;
   if (out) *out = v;
   *f = 0u;
+}
+
+// ---- plain streaming read (measurement aid) -------------------------------
+// Every 16-byte word of the buffer is loaded once (8 per thread in flight);
+// each workgroup stores the xor of what it read, so no load is dropped.
+constexpr int kReadThreads = 256;
+constexpr int kReadUnroll = 8;
+__global__ __launch_bounds__(kReadThreads) void read_bytes_kernel(const uint4* __restrict__ src,
+                                                                  size_t n16, uint32_t* __restrict__ sink) {
+  uint32_t acc = 0;
+  const size_t stride = (size_t)gridDim.x * kReadThreads;
+  size_t i = (size_t)blockIdx.x * kReadThreads + threadIdx.x;
+  for (; i + (kReadUnroll - 1) * stride < n16; i += kReadUnroll * stride) {
+    uint4 w[kReadUnroll];
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) w[u] = src[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) acc ^= w[u].x ^ w[u].y ^ w[u].z ^ w[u].w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 w = src[i];
+    acc ^= w.x ^ w.y ^ w.z ^ w.w;
+  }
+  for (int o = 32; o > 0; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o);
+  __shared__ uint32_t s_acc[kReadThreads / 64];
+  if ((threadIdx.x & 63) == 0) s_acc[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = s_acc[0] ^ s_acc[1] ^ s_acc[2] ^ s_acc[3];
 }
 
 }  // namespace skv
@@ -510,6 +540,22 @@ skv_status sparsekv_append_block(const skv_layer_desc* d, int32_t* ctx_len, cons
   return launched(launch_append_block(*d, ctx_len, k_new, v_new, index_raw, index_stage, *kv,
                                       index_keys, ws, L, (hipStream_t)stream),
                   "append_block");
+}
+
+skv_status sparsekv_read_bytes(const void* src, size_t bytes, uint32_t* sink, int32_t n_wg,
+                               void* stream) {
+  if (!src || !sink) return set_error(SKV_ERR_INVALID, "read_bytes: NULL pointer");
+  if (((uintptr_t)src) % 16 || bytes % 16) return set_error(SKV_ERR_INVALID, "read_bytes: needs 16-byte alignment and size");
+  if (n_wg < 1 || n_wg > SKV_READ_MAX_WG) return set_error(SKV_ERR_INVALID, "read_bytes: n_wg %d outside [1, %d]", n_wg, SKV_READ_MAX_WG);
+  if (bytes == 0) return SKV_OK;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  const hipStream_t st = (hipStream_t)stream;
+  if (timer_next(kTimerStream, &ev0, &ev1))
+    hipExtLaunchKernelGGL(read_bytes_kernel, dim3(n_wg), dim3(kReadThreads), 0, st, ev0, ev1, 0,
+                          (const uint4*)src, bytes / 16, sink);
+  else
+    hipLaunchKernelGGL(read_bytes_kernel, dim3(n_wg), dim3(kReadThreads), 0, st, (const uint4*)src, bytes / 16, sink);
+  return launched(hipGetLastError(), "read_bytes");
 }
 
 skv_status sparsekv_timer_enable(int enable) {

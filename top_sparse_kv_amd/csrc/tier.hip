@@ -15,9 +15,25 @@
 // rather than registering an existing anonymous mapping, and the kernel reads
 // it through the device address hipHostGetDevicePointer returns.
 //
-// Per step: tier_resolve (one workgroup per sequence) marks hits, then places
-// the misses; tier_fetch (many workgroups) reads the missed records over PCIe
-// and writes int8 rows + fp16 scales into their slots.
+// Residency states (page "vLLM's Hybrid HiSparse Triples Concurrent Requests
+// on Million-Token Contexts", section "Three residency states, one block
+// pool"): a page table per sequence maps pages of P positions to blocks of a
+// device pool (full residency: every page mapped; mixed: some; none: no page).
+// A middle pick of a mapped page is read where it sits in the pool; the other
+// middle picks go through the hot buffer.
+//
+// Per step one kernel -- the single fused resolver the residency section
+// describes -- with 1 + F workgroups per sequence.  The first resolves the
+// picks (in place, hit, miss) and places the misses; the other F read the
+// missed records over PCIe and write them into their slots as int8 rows +
+// fp16 scales.  Host reads need many compute units in flight (one workgroup
+// alone pulls a few GB/s), so the fetch is spread; the resolver publishes the
+// misses' positions as soon as they are classified, so the PCIe reads overlap
+// the placement, then their slots.  A fetch workgroup only ever waits for the
+// resolver of its own sequence, which has a lower workgroup id and is
+// dispatched before it; the wait is bounded (a flag is raised if it ends
+// without the resolver's word), and the last workgroup of a sequence to
+// finish clears the sequence's hand-off words for the next call.
 //
 // Placement in parallel.  Walking the slots in hand order from where the hand
 // stopped, a slot is "free" if it is empty or unpinned (last <= step - W) with
@@ -70,11 +86,20 @@ struct skv_tier {
   int32_t* slot_of_pos;  // [B][cap_ctx]
   int32_t* ctx_dev;      // [B] context of each sequence (advanced by sparsekv_tier_append)
   int64_t appends;       // sparsekv_tier_append calls
+  int P, page_shift;     // page size (positions, a power of two) and its log2; 0 / 0: no page table
+  int pool_pages;        // pool blocks per sequence
+  int n_pages;           // pages per sequence: ceil(cap_ctx / P)
+  int64_t pool_row0;     // first pool row of a sequence in the resident rows
+  int32_t* page_block;   // [B][n_pages] pool block of each page, -1: host only (device)
+  int32_t* page_host;    // host mirror of page_block
+  int32_t* block_page;   // [B][pool_pages] page held by each block, -1: free (host)
+  int n_fetch;           // fetch workgroups per sequence
   int mstride;           // misses per sequence the arrays below hold
-  int32_t* miss_pos;     // [B][mstride]
+  int32_t* miss_pos;     // [B][mstride] resolver -> fetch workgroups
   int32_t* miss_slot;    // [B][mstride]
-  int32_t* miss_count;   // [B]
-  unsigned long long* counters;  // picks, hits, misses
+  int32_t* miss_n;       // [B]
+  int32_t* sync;         // [B][4]: positions listed, slots placed, arrivals
+  unsigned long long* counters;  // picks, hits, misses, in place
   uint32_t* flags;
   int64_t steps;
 };
@@ -101,7 +126,143 @@ __global__ void tier_reset_kernel(int32_t* slot_pos, int32_t* slot_last, int32_t
   }
   for (size_t i = tid; i < (size_t)B * cap_ctx; i += nth) slot_of_pos[i] = -1;
   for (size_t i = tid; i < (size_t)B; i += nth) hand[i] = 0;
-  if (tid < 3) counters[tid] = 0ull;
+  if (tid < 4) counters[tid] = 0ull;
+}
+
+// ---- hand-off between the resolver and the fetch workgroups of a sequence ----
+// Words w[0] (miss positions listed), w[1] (slots placed), w[2] (arrivals).
+// Everything handed over (positions, slots, counts, the words) is written and
+// read with device-scope atomic accesses, which are coherent across the XCDs'
+// L2 caches by themselves; so no release or acquire fence is needed.  (A
+// device-scope release fence writes the XCD's whole L2 back and here queues
+// behind the fetch workgroups' host reads; an acquire fence invalidates it.)
+constexpr uint64_t kWaitTicks = 5000000;   // 50 ms of the 100 MHz constant clock
+
+__device__ __forceinline__ void put(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t get(const int32_t* p) {
+  return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// every thread's earlier put()s complete, then word = 1
+__device__ __forceinline__ void publish(int32_t* word) {
+  __builtin_amdgcn_s_waitcnt(0);   // this thread's stores are acknowledged
+  __syncthreads();
+  if (threadIdx.x == 0) put(word, 1);
+}
+
+// thread 0 polls the word (bounded); false if it never became 1
+__device__ __forceinline__ bool wait_word(int32_t* word, uint32_t* flags, int* s_ok) {
+  if (threadIdx.x == 0) {
+    const uint64_t t0 = wall_clock64();
+    int ok = 1;
+    while (get(word) == 0) {
+      if (wall_clock64() - t0 > kWaitTicks) {
+        ok = 0;
+        raise_flag(flags, SKV_FLAG_TIER_WAIT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
+    }
+    *s_ok = ok;
+  }
+  __syncthreads();
+  return *s_ok != 0;
+}
+
+// one more workgroup of the sequence done (thread 0); the last of the 1 + F
+// clears the words for the next call
+__device__ __forceinline__ void arrive(int32_t* w, int n_fetch) {
+  const int old = atomicAdd(w + 2, 1);
+  if (old == n_fetch) {
+    w[0] = 0;
+    w[1] = 0;
+    w[2] = 0;
+  }
+}
+
+// Fetch workgroup `part` of F.  Task t = (miss, KV head) = (t / H_kv, t % H_kv);
+// round r, batch slot u, workgroup part p, wave w take task
+// ((r * BATCH + u) * F + p) * W + w (W waves per workgroup), so every round
+// covers BATCH * F * W consecutive tasks; lanes 0-31 handle the K row and
+// 32-63 the V row, 8 dims each.  A round reads and converts its records, then
+// (first round only) waits for the slots, then stores.  The round count is the
+// same for every wave of the workgroup, so the waits' barriers line up.
+constexpr int kFetchBatch = 4;
+template <int BATCH>
+__device__ void fetch_part(const uint8_t* __restrict__ host, const int32_t* mpos, const int32_t* mslot,
+                           const int32_t* mcount, int32_t* w, uint32_t* flags, int part, int n_fetch, int b,
+                           int64_t host_ctx, int Hkv, int8_t* __restrict__ res_k, int8_t* __restrict__ res_v,
+                           uint16_t* __restrict__ res_ks, uint16_t* __restrict__ res_vs, int64_t res_rows,
+                           int res_off) {
+  constexpr int D = 256;
+  constexpr int ROWB = D / 2 + 2 * (D / 64);   // 136
+  __shared__ int s_ok[2];   // one word per wait: no wave reads one while thread 0 writes the other
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = (int)(blockDim.x >> 6);
+  const int half = lane >> 5, ln = lane & 31;
+  const bool listed = wait_word(w + 0, flags, &s_ok[0]);
+  const int ntask = listed ? get(mcount) * Hkv : 0;
+  const int per_round = BATCH * n_fetch * nw;
+  const int rounds = (ntask + per_round - 1) / per_round;   // the same in every wave
+  for (int r = 0; r < rounds; ++r) {
+    uint2 rowv[BATCH];
+    uint16_t sbits[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int task = ((r * BATCH + u) * n_fetch + part) * nw + wave;
+      rowv[u] = make_uint2(0u, 0u);
+      sbits[u] = 0;
+      if (task < ntask) {
+        const int mi = task / Hkv, h = task - mi * Hkv;
+        const uint8_t* row = host + (((size_t)b * host_ctx + get(mpos + mi)) * Hkv + h) * (2 * ROWB) + half * ROWB;
+        const uint32_t codes = *reinterpret_cast<const uint32_t*>(row + 4 * ln);
+        const uint2 sc = *reinterpret_cast<const uint2*>(row + D / 2);
+        const float g0 = half_bits_to_float((uint16_t)(sc.x & 0xFFFF));
+        const float g1 = half_bits_to_float((uint16_t)(sc.x >> 16));
+        const float g2 = half_bits_to_float((uint16_t)(sc.y & 0xFFFF));
+        const float g3 = half_bits_to_float((uint16_t)(sc.y >> 16));
+        const float gmax = fmaxf(fmaxf(g0, g1), fmaxf(g2, g3));
+        // fp32 quotients via one fp64 divide + one rounding (= correctly rounded fp32)
+        const __half sp_h = __float2half_rn((float)((double)(gmax * 7.0f) / 127.0));
+        const float spf = __half2float(sp_h);
+        const int grp = ln >> 3;    // 8 dims per lane, 64 dims per group
+        const float gs = grp == 0 ? g0 : (grp == 1 ? g1 : (grp == 2 ? g2 : g3));
+        uint32_t o2[2] = {0u, 0u};
+        if (spf != 0.0f) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            int c = (int)((codes >> (4 * e)) & 0xFu);
+            c = (c ^ 8) - 8;
+            float q = rintf((float)((double)((float)c * gs) / (double)spf));
+            q = fminf(fmaxf(q, -127.0f), 127.0f);
+            o2[e >> 2] |= ((uint32_t)(uint8_t)(int8_t)(int)q) << (8 * (e & 3));
+          }
+        }
+        rowv[u] = make_uint2(o2[0], o2[1]);
+        sbits[u] = __half_as_ushort(sp_h);
+      }
+    }
+    if (r == 0 && !wait_word(w + 1, flags, &s_ok[1])) break;   // workgroup-uniform
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int task = ((r * BATCH + u) * n_fetch + part) * nw + wave;
+      if (task >= ntask) continue;
+      const int mi = task / Hkv, h = task - mi * Hkv;
+      const int slot = get(mslot + mi);
+      if (slot < 0) continue;   // not placed (flagged by the resolver)
+      const size_t rr = ((size_t)b * res_rows + res_off + slot) * Hkv + h;
+      int8_t* dst = (half ? res_v : res_k) + rr * D + 8 * ln;
+      *reinterpret_cast<uint2*>(dst) = rowv[u];
+      if (ln == 0) (half ? res_vs : res_ks)[rr] = sbits[u];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) arrive(w, n_fetch);
+}
+
+__global__ void tier_set_page_kernel(int32_t* page_block, int64_t at, int32_t block) {
+  page_block[at] = block;
 }
 
 // MULTI: several pick lists per sequence (mq of them); one list compiles to
@@ -111,28 +272,41 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ n_sel, int32_t* __restrict__ rows,
     int32_t* __restrict__ slot_pos, int32_t* __restrict__ slot_last, int32_t* __restrict__ slot_ref,
     int32_t* __restrict__ hand_arr, int32_t* __restrict__ slot_of_pos,
-    int32_t* __restrict__ miss_pos, int32_t* __restrict__ miss_slot, int32_t* __restrict__ miss_count,
     unsigned long long* __restrict__ counters, uint32_t* __restrict__ flags,
     const int32_t* __restrict__ tier_ctx, int T0, int cap_ctx, int S, int L,
-    int k, int n_slots, int W, int cap, int step, int mq, int mstride) {
+    int k, int n_slots, int W, int cap, int step, int mq,
+    const int32_t* __restrict__ page_block, int n_pages, int page_shift, int64_t pool_row0,
+    const uint8_t* __restrict__ host, int8_t* __restrict__ res_k, int8_t* __restrict__ res_v,
+    uint16_t* __restrict__ res_ks, uint16_t* __restrict__ res_vs, int64_t res_rows, int Hkv,
+    int32_t* __restrict__ miss_pos, int32_t* __restrict__ miss_slot, int32_t* __restrict__ miss_n,
+    int32_t* __restrict__ sync, int mstride, int n_fetch) {
   __shared__ int32_t s_pos[kMaxSlots];
   __shared__ int32_t s_last[kMaxSlots];
   __shared__ uint8_t s_ref[kMaxSlots];
-  __shared__ int32_t s_miss[kMaxListMisses];   // input index of each miss
+  __shared__ int32_t s_miss[kMaxListMisses];   // input index of each miss; its slot once placed
   __shared__ int32_t s_mpos[kMaxListMisses];   // its position (read by the serial placement)
   __shared__ uint32_t s_wsum[kResolveThreads / 64];
-  __shared__ int s_nm, s_nmid, s_bad, s_tlast, s_hand, s_moff;
-  const int b = blockIdx.x;
+  __shared__ int s_nm, s_nmid, s_ninp, s_bad, s_tlast, s_hand, s_placed;
+  const int b = blockIdx.x / (1 + n_fetch), role = blockIdx.x % (1 + n_fetch);
+  if (role != 0) {   // a fetch workgroup (workgroup-uniform, before any barrier of the resolver)
+    fetch_part<MULTI ? kFetchBatch / 2 : kFetchBatch>(host, miss_pos + (size_t)b * mstride,
+                                                      miss_slot + (size_t)b * mstride, miss_n + b,
+                                                      sync + 4 * b, flags, role - 1, n_fetch, b, cap_ctx,
+                                                      Hkv, res_k, res_v, res_ks, res_vs, res_rows, S + L);
+    return;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int32_t* sp = slot_pos + (size_t)b * n_slots;
   int32_t* sl = slot_last + (size_t)b * n_slots;
   int32_t* sr = slot_ref + (size_t)b * n_slots;
   int32_t* sop = slot_of_pos + (size_t)b * cap_ctx;
+  const int32_t* pgb = page_block ? page_block + (size_t)b * n_pages : nullptr;
+  const int pmask = (1 << page_shift) - 1;
   // scalars first: their loads overlap the slot-table copy
   const int T = tier_ctx[b];   // this sequence's context (sinks, middle, tail ring)
   int hand = hand_arr[b];
   int n_next = n_sel[(size_t)b * mq];
-  int moff = 0;   // misses placed by the earlier lists
+  int moff = 0;   // misses handed to the fetch workgroups by the earlier lists
   for (int i = threadIdx.x; i < n_slots; i += blockDim.x) {
     s_pos[i] = sp[i];
     s_last[i] = sl[i];
@@ -150,6 +324,7 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
   if (threadIdx.x == 0) {   // nobody reads these between the previous list's last barrier and the next
     s_nm = 0;
     s_nmid = 0;
+    s_ninp = 0;
     s_tlast = -1;
   }
   if (n < 0 || n > cap) {
@@ -160,15 +335,47 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
   int32_t* rb = rows + ((size_t)b * mq + qj) * cap;
   __syncthreads();
 
-  // phase A: classify; hits refresh their slot; misses listed in input order
+  // phase A: classify; hits refresh their slot; misses listed in input order.
+  // The picks of the first kPre rounds and their slot / page lookups are
+  // loaded together first (the lookups do not change before the placement),
+  // so the rounds cost one pair of dependent round trips, not one each.
+  constexpr int kPre = 4;
+  int pp[kPre], pq[kPre], ps[kPre], pg[kPre];
+#pragma unroll
+  for (int r = 0; r < kPre; ++r) {
+    const int i = r * (int)blockDim.x + (int)threadIdx.x;
+    pp[r] = i < n ? ib[i] : -1;
+    pq[r] = (i < n && i > 0) ? ib[i - 1] : INT32_MIN;
+  }
+#pragma unroll
+  for (int r = 0; r < kPre; ++r) {
+    const int p = pp[r];
+    const bool midr = p >= S && p < T - L;   // then 0 <= p < T <= cap_ctx
+    ps[r] = midr ? sop[p] : -1;
+    pg[r] = (midr && pgb) ? pgb[p >> page_shift] : -1;
+  }
   const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  for (int base = 0; base < n; base += blockDim.x) {
+  int round = 0;
+  for (int base = 0; base < n; base += blockDim.x, ++round) {
     const int i = base + threadIdx.x;
-    bool miss = false, mid = false;
-    int p = 0;
-    if (i < n) {
+    bool miss = false, mid = false, inpl = false;
+    int p = pp[0], prev = pq[0], s_pre = ps[0], blk_pre = pg[0];
+#pragma unroll
+    for (int u = 0; u + 1 < kPre; ++u) {   // static indices: the next round moves to slot 0
+      pp[u] = pp[u + 1];
+      pq[u] = pq[u + 1];
+      ps[u] = ps[u + 1];
+      pg[u] = pg[u + 1];
+    }
+    if (round >= kPre && i < n) {   // rounds past the prefetched ones load here
       p = ib[i];
-      const bool sorted = i == 0 || ib[i - 1] < p;
+      prev = i > 0 ? ib[i - 1] : INT32_MIN;
+      const bool midr = p >= S && p < T - L;
+      s_pre = midr ? sop[p] : -1;
+      blk_pre = (midr && pgb) ? pgb[p >> page_shift] : -1;
+    }
+    if (i < n) {
+      const bool sorted = i == 0 || prev < p;
       if (p < 0 || p >= T || !sorted) {
         s_bad = 1;
         rb[i] = 0;
@@ -178,22 +385,30 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
         const int r = (p - T0) % L;   // tail ring anchored at the creation context
         rb[i] = S + (r < 0 ? r + L : r);
       } else {
-        mid = true;
-        const int s = sop[p];
-        if (s >= 0) {
+        // a mapped page wins over the hot buffer
+        const int blk = blk_pre;
+        const int s = s_pre;
+        if (blk >= 0) {
+          inpl = true;
+          rb[i] = (int)(pool_row0 + ((int64_t)blk << page_shift) + (p & pmask));
+        } else if (s >= 0) {
+          mid = true;
           s_ref[s] = 1;
           s_last[s] = step;
           rb[i] = S + L + s;
         } else {
+          mid = true;
           miss = true;
         }
       }
     }
     const uint64_t m = __ballot(miss);
     const uint64_t mm = __ballot(mid);
+    const uint64_t mi_ = __ballot(inpl);
     if (lane == 0) {
       s_wsum[wave] = (uint32_t)__popcll(m);
       atomicAdd(&s_nmid, (int)__popcll(mm));
+      if (mi_) atomicAdd(&s_ninp, (int)__popcll(mi_));
     }
     __syncthreads();
     int off = s_nm;
@@ -225,6 +440,13 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
   if (!fits) {
     for (int mi = threadIdx.x; mi < min(s_nm, km); mi += blockDim.x) rb[s_miss[mi]] = 0;
     if (threadIdx.x == 0) s_bad = 1;
+  }
+  if constexpr (!MULTI) {
+    // one pick list: the misses' positions go to the fetch workgroups now, so
+    // their host reads overlap the placement below
+    for (int mi = threadIdx.x; mi < nm; mi += blockDim.x) put(miss_pos + (size_t)b * mstride + mi, s_mpos[mi]);
+    if (threadIdx.x == 0) put(miss_n + b, nm);
+    publish(sync + 4 * b + 0);
   }
   __syncthreads();
 
@@ -341,8 +563,7 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
           s_last[j] = step;
           sop[p] = j;
           rb[i] = S + L + j;
-          miss_pos[(size_t)b * mstride + moff + mi] = p;
-          miss_slot[(size_t)b * mstride + moff + mi] = j;
+          s_miss[mi] = j;   // its slot, for the fetch
         }
       }
     }
@@ -352,11 +573,12 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
     for (int mi = placed + (int)threadIdx.x; mi < nm; mi += blockDim.x) rb[s_miss[mi]] = 0;
     __syncthreads();
     if (threadIdx.x == 0) {
-      s_moff = moff + placed;
+      s_placed = placed;
       s_hand = h0;
-      atomicAdd(&counters[0], (unsigned long long)s_nmid);
+      atomicAdd(&counters[0], (unsigned long long)(s_nmid + s_ninp));
       atomicAdd(&counters[1], (unsigned long long)(s_nmid - nm));
       atomicAdd(&counters[2], (unsigned long long)nm);
+      atomicAdd(&counters[3], (unsigned long long)s_ninp);
       if (placed < nm) s_bad = 1;
     }
     __syncthreads();
@@ -394,8 +616,7 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
     s_last[j] = step;
     sop[p] = j;
     rb[i] = S + L + j;
-    miss_pos[(size_t)b * mstride + moff + mi] = p;
-    miss_slot[(size_t)b * mstride + moff + mi] = j;
+    s_miss[mi] = j;   // its slot, for the fetch
     if (mi == placed - 1) s_tlast = t;
   };
   uint32_t rleft = 0;   // referenced slots not taken
@@ -430,75 +651,39 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
   if (threadIdx.x == 0) {
     if (placed < nm) s_bad = 1;
     s_hand = placed > 0 ? (h0 + tlast + 1 < n_slots ? h0 + tlast + 1 : h0 + tlast + 1 - n_slots) : h0;
-    s_moff = moff + placed;
-    atomicAdd(&counters[0], (unsigned long long)s_nmid);
+    s_placed = placed;
+    atomicAdd(&counters[0], (unsigned long long)(s_nmid + s_ninp));
     atomicAdd(&counters[1], (unsigned long long)(s_nmid - nm));
     atomicAdd(&counters[2], (unsigned long long)nm);
+    atomicAdd(&counters[3], (unsigned long long)s_ninp);
   }
   __syncthreads();
   }   // policy
   hand = s_hand;
-  moff = s_moff;
+  // the slots of this list's misses (-1: not placed, nothing written); with
+  // several lists also their positions, after those of the earlier lists
+  for (int mi = threadIdx.x; mi < nm; mi += blockDim.x) {
+    if (MULTI) put(miss_pos + (size_t)b * mstride + moff + mi, s_mpos[mi]);
+    put(miss_slot + (size_t)b * mstride + moff + mi, mi < s_placed ? s_miss[mi] : -1);
+  }
+  if (MULTI) moff += nm;
+  __syncthreads();   // s_mpos / s_miss are reused by the next list
   if (qj + 1 < mq) n_next = n_sel[(size_t)b * mq + qj + 1];
   }   // pick lists
+  if constexpr (MULTI) {
+    if (threadIdx.x == 0) put(miss_n + b, moff);
+    publish(sync + 4 * b + 0);
+  }
+  publish(sync + 4 * b + 1);
   if (threadIdx.x == 0) {
-    miss_count[b] = moff;
     hand_arr[b] = hand;
     if (s_bad) raise_flag(flags, SKV_FLAG_TIER_INPUT);
+    arrive(sync + 4 * b, n_fetch);
   }
   for (int i = threadIdx.x; i < n_slots; i += blockDim.x) {
     sp[i] = s_pos[i];
     sl[i] = s_last[i];
     sr[i] = (int32_t)s_ref[i];
-  }
-}
-
-// Reads missed host records over PCIe and writes int8 rows into their slots.
-// One wave per (miss, KV head): lanes 0-31 the K row, 32-63 the V row, 8 dims each.
-__global__ __launch_bounds__(256) void tier_fetch_kernel(
-    const uint8_t* __restrict__ host, const int32_t* __restrict__ miss_pos,
-    const int32_t* __restrict__ miss_slot, const int32_t* __restrict__ miss_count,
-    int8_t* __restrict__ res_k, int8_t* __restrict__ res_v, uint16_t* __restrict__ res_ks,
-    uint16_t* __restrict__ res_vs, int64_t host_ctx, int Hkv, int mstride, int64_t res_rows, int res_off) {
-  constexpr int D = 256;
-  constexpr int ROWB = D / 2 + 2 * (D / 64);   // 136
-  const int b = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  const int half = lane >> 5, ln = lane & 31;
-  const int nm = miss_count[b];
-  const int nwaves = gridDim.x * (blockDim.x >> 6);
-  for (int task = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); task < nm * Hkv; task += nwaves) {
-    const int mi = task / Hkv, h = task % Hkv;
-    const int p = miss_pos[(size_t)b * mstride + mi];
-    const int slot = miss_slot[(size_t)b * mstride + mi];
-    const uint8_t* row = host + (((size_t)b * host_ctx + p) * Hkv + h) * (2 * ROWB) + half * ROWB;
-    const uint32_t codes = *reinterpret_cast<const uint32_t*>(row + 4 * ln);
-    const uint2 sc = *reinterpret_cast<const uint2*>(row + D / 2);
-    const float g0 = half_bits_to_float((uint16_t)(sc.x & 0xFFFF));
-    const float g1 = half_bits_to_float((uint16_t)(sc.x >> 16));
-    const float g2 = half_bits_to_float((uint16_t)(sc.y & 0xFFFF));
-    const float g3 = half_bits_to_float((uint16_t)(sc.y >> 16));
-    const float gmax = fmaxf(fmaxf(g0, g1), fmaxf(g2, g3));
-    // fp32 quotients via one fp64 divide + one rounding (= correctly rounded fp32)
-    const __half sp_h = __float2half_rn((float)((double)(gmax * 7.0f) / 127.0));
-    const float spf = __half2float(sp_h);
-    const int grp = ln >> 3;    // 8 dims per lane, 64 dims per group
-    const float gs = grp == 0 ? g0 : (grp == 1 ? g1 : (grp == 2 ? g2 : g3));
-    uint32_t out[2] = {0u, 0u};
-    if (spf != 0.0f) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        int c = (int)((codes >> (4 * e)) & 0xFu);
-        c = (c ^ 8) - 8;
-        float r = rintf((float)((double)((float)c * gs) / (double)spf));
-        r = fminf(fmaxf(r, -127.0f), 127.0f);
-        out[e >> 2] |= ((uint32_t)(uint8_t)(int8_t)(int)r) << (8 * (e & 3));
-      }
-    }
-    const size_t rr = ((size_t)b * res_rows + res_off + slot) * Hkv + h;
-    int8_t* dst = (half ? res_v : res_k) + rr * D + 8 * ln;
-    *reinterpret_cast<uint2*>(dst) = make_uint2(out[0], out[1]);
-    if (ln == 0) (half ? res_vs : res_ks)[rr] = __half_as_ushort(sp_h);
   }
 }
 
@@ -518,11 +703,13 @@ using skv::set_error;
 static void tier_free(skv_tier* t) {
   if (!t) return;
   void* dev[] = {t->res_k, t->res_v, t->res_ks, t->res_vs, t->slot_pos, t->slot_last, t->slot_ref,
-                 t->hand, t->slot_of_pos, t->ctx_dev, t->miss_pos, t->miss_slot, t->miss_count,
-                 t->counters, t->flags};
+                 t->hand, t->slot_of_pos, t->ctx_dev, t->page_block, t->counters, t->flags,
+                 t->miss_pos, t->miss_slot, t->miss_n, t->sync};
   for (void* p : dev)
     if (p) (void)hipFree(p);
   if (t->own_host && t->host) (void)hipHostFree(t->host);
+  delete[] t->page_host;
+  delete[] t->block_page;
   delete t;
 }
 
@@ -530,9 +717,17 @@ extern "C" skv_status sparsekv_tier_create(const skv_tier_desc* d, skv_tier** ou
   if (!d || !out) return set_error(SKV_ERR_INVALID, "tier_create: NULL argument");
   *out = nullptr;
   constexpr size_t kMinDesc = offsetof(skv_tier_desc, policy);
+  constexpr size_t kPagedDesc = offsetof(skv_tier_desc, pool_pages) + sizeof(int32_t);
   if (d->struct_size < kMinDesc)
     return set_error(SKV_ERR_INVALID, "tier_create: struct_size %u < %zu", d->struct_size, kMinDesc);
-  const int policy = d->struct_size >= sizeof(skv_tier_desc) ? d->policy : SKV_TIER_CLOCK;
+  const int policy = d->struct_size >= offsetof(skv_tier_desc, policy) + sizeof(int32_t) ? d->policy
+                                                                                         : SKV_TIER_CLOCK;
+  const int P = d->struct_size >= kPagedDesc ? d->page_tokens : 0;
+  const int pool_pages = d->struct_size >= kPagedDesc ? d->pool_pages : 0;
+  if (P != 0 && (P < 16 || P > 4096 || (P & (P - 1))))
+    return set_error(SKV_ERR_INVALID, "tier_create: page_tokens %d is not 0 or a power of two in [16, 4096]", P);
+  if (pool_pages < 0 || (pool_pages > 0 && P == 0))
+    return set_error(SKV_ERR_INVALID, "tier_create: pool_pages %d needs page_tokens", pool_pages);
   if (policy != SKV_TIER_CLOCK && policy != SKV_TIER_LRU)
     return set_error(SKV_ERR_INVALID, "tier_create: policy %d unknown", policy);
   skv_status s = skv::validate_desc(&d->layer);
@@ -560,10 +755,32 @@ extern "C" skv_status sparsekv_tier_create(const skv_tier_desc* d, skv_tier** ou
   t->B = L.batch; t->T0 = d->ctx; t->cap_ctx = L.max_ctx; t->S = L.n_sink; t->L = L.n_tail; t->k = L.topk;
   t->Hkv = L.n_kv_heads; t->D = L.head_dim; t->n_slots = d->n_slots; t->W = d->window;
   t->cap = skv::select_capacity(L);
-  t->mstride = skv::kMaxQueries * (t->k + skv::kMaxQueries);
   t->row_bytes = t->D / 2 + 2 * (t->D / 64);
   t->rec_bytes = 2 * t->row_bytes;
-  t->res_rows = (int64_t)t->S + t->L + t->n_slots;
+  t->P = P;
+  t->page_shift = P ? __builtin_ctz((unsigned)P) : 0;
+  t->pool_pages = pool_pages;
+  t->n_pages = P ? (t->cap_ctx + P - 1) / P : 0;
+  t->pool_row0 = (int64_t)t->S + t->L + t->n_slots;
+  // about one workgroup per compute unit: F fetch workgroups per sequence
+  t->n_fetch = std::max(1, std::min(63, 256 / t->B - 1));
+  t->mstride = skv::kMaxQueries * skv::kMaxListMisses;
+  t->res_rows = t->pool_row0 + (int64_t)pool_pages * P;
+  if (t->res_rows > INT32_MAX) {
+    tier_free(t);
+    return set_error(SKV_ERR_INVALID, "tier_create: %lld resident rows per sequence exceed int32 row ids",
+                     (long long)t->res_rows);
+  }
+  if (P) {
+    t->page_host = new (std::nothrow) int32_t[(size_t)t->B * t->n_pages];
+    t->block_page = new (std::nothrow) int32_t[(size_t)t->B * (pool_pages > 0 ? pool_pages : 1)];
+    if (!t->page_host || !t->block_page) {
+      tier_free(t);
+      return set_error(SKV_ERR_OOM, "tier: host allocation failed");
+    }
+    std::fill(t->page_host, t->page_host + (size_t)t->B * t->n_pages, -1);
+    std::fill(t->block_page, t->block_page + (size_t)t->B * (pool_pages > 0 ? pool_pages : 1), -1);
+  }
   const size_t host_bytes = (size_t)t->B * t->cap_ctx * t->Hkv * t->rec_bytes;
   if (d->host_records) {
     t->host = d->host_records;
@@ -596,10 +813,12 @@ extern "C" skv_status sparsekv_tier_create(const skv_tier_desc* d, skv_tier** ou
             hipMalloc(&t->hand, (size_t)t->B * 4) == hipSuccess &&
             hipMalloc(&t->slot_of_pos, (size_t)t->B * t->cap_ctx * 4) == hipSuccess &&
             hipMalloc(&t->ctx_dev, (size_t)t->B * 4) == hipSuccess &&
+            (!P || hipMalloc(&t->page_block, (size_t)t->B * t->n_pages * 4) == hipSuccess) &&
+            hipMalloc(&t->counters, 4 * sizeof(unsigned long long)) == hipSuccess &&
             hipMalloc(&t->miss_pos, (size_t)t->B * t->mstride * 4) == hipSuccess &&
             hipMalloc(&t->miss_slot, (size_t)t->B * t->mstride * 4) == hipSuccess &&
-            hipMalloc(&t->miss_count, (size_t)t->B * 4) == hipSuccess &&
-            hipMalloc(&t->counters, 3 * sizeof(unsigned long long)) == hipSuccess &&
+            hipMalloc(&t->miss_n, (size_t)t->B * 4) == hipSuccess &&
+            hipMalloc(&t->sync, (size_t)t->B * 16) == hipSuccess &&
             hipMalloc(&t->flags, 256) == hipSuccess;
   if (!ok) {
     (void)hipGetLastError();
@@ -608,7 +827,8 @@ extern "C" skv_status sparsekv_tier_create(const skv_tier_desc* d, skv_tier** ou
   }
   if (hipMemset(t->res_k, 0, rr * t->D) != hipSuccess || hipMemset(t->res_v, 0, rr * t->D) != hipSuccess ||
       hipMemset(t->res_ks, 0, rr * 2) != hipSuccess || hipMemset(t->res_vs, 0, rr * 2) != hipSuccess ||
-      hipMemset(t->flags, 0, 256) != hipSuccess) {
+      hipMemset(t->flags, 0, 256) != hipSuccess || hipMemset(t->sync, 0, (size_t)t->B * 16) != hipSuccess ||
+      (P && hipMemset(t->page_block, 0xFF, (size_t)t->B * t->n_pages * 4) != hipSuccess)) {
     tier_free(t);
     return set_error(SKV_ERR_HIP, "tier: initial clear failed");
   }
@@ -630,6 +850,7 @@ extern "C" skv_status sparsekv_tier_create(const skv_tier_desc* d, skv_tier** ou
 }
 
 extern "C" void* sparsekv_tier_host_records(skv_tier* t) { return t ? t->host : nullptr; }
+extern "C" void* sparsekv_tier_host_ptr(skv_tier* t) { return t ? t->host : nullptr; }
 
 extern "C" skv_status sparsekv_tier_resident(skv_tier* t, skv_kv_view* v) {
   if (!t || !v) return set_error(SKV_ERR_INVALID, "tier_resident: NULL argument");
@@ -672,12 +893,24 @@ static skv_status tier_resolve_lists(skv_tier* t, int32_t n_query, const int32_t
     return set_error(SKV_ERR_UNSUPPORTED, "tier_resolve: n_query %d outside [1, %d]", n_query,
                      skv::kMaxQueries);
   hipStream_t st = (hipStream_t)stream;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  const bool timed = skv::timer_next(skv::kTimerStream, &ev0, &ev1);   // diagnostic timer
+#define SKV_RESOLVE_ARGS                                                                           \
+  idx, n_sel, rows, t->slot_pos, t->slot_last, t->slot_ref, t->hand, t->slot_of_pos, t->counters,  \
+      t->flags, t->ctx_dev, t->T0, t->cap_ctx, t->S, t->L, t->k, t->n_slots, t->W, t->cap, step,    \
+      n_query, t->page_block, t->n_pages, t->page_shift, t->pool_row0, t->host_dev, t->res_k,       \
+      t->res_v, t->res_ks, t->res_vs, t->res_rows, t->Hkv, t->miss_pos, t->miss_slot, t->miss_n, t->sync, \
+      t->mstride, t->n_fetch
+  const dim3 grid((unsigned)(t->B * (1 + t->n_fetch)));
 #define SKV_RESOLVE(POL)                                                                           \
-  hipLaunchKernelGGL((skv::tier_resolve_kernel<POL, MUL>), dim3(t->B), dim3(skv::kResolveThreads), 0, st, \
-                     idx, n_sel, rows, t->slot_pos, t->slot_last, t->slot_ref, t->hand,            \
-                     t->slot_of_pos, t->miss_pos, t->miss_slot, t->miss_count, t->counters,        \
-                     t->flags, t->ctx_dev, t->T0, t->cap_ctx, t->S, t->L, t->k, t->n_slots, t->W,  \
-                     t->cap, step, n_query, t->mstride)
+  do {                                                                                             \
+    if (timed)                                                                                     \
+      hipExtLaunchKernelGGL((skv::tier_resolve_kernel<POL, MUL>), grid, dim3(skv::kResolveThreads),         \
+                            0, st, ev0, ev1, 0, SKV_RESOLVE_ARGS);                                 \
+    else                                                                                           \
+      hipLaunchKernelGGL((skv::tier_resolve_kernel<POL, MUL>), grid, dim3(skv::kResolveThreads), 0,         \
+                         st, SKV_RESOLVE_ARGS);                                                    \
+  } while (0)
   if (n_query == 1) {
     constexpr bool MUL = false;
     if (t->policy == SKV_TIER_LRU) SKV_RESOLVE(SKV_TIER_LRU);
@@ -688,18 +921,8 @@ static skv_status tier_resolve_lists(skv_tier* t, int32_t n_query, const int32_t
     else SKV_RESOLVE(SKV_TIER_CLOCK);
   }
 #undef SKV_RESOLVE
+#undef SKV_RESOLVE_ARGS
   if (hipGetLastError() != hipSuccess) return set_error(SKV_ERR_HIP, "tier_resolve: launch failed");
-  hipEvent_t ev0 = nullptr, ev1 = nullptr;
-  if (skv::timer_next(skv::kTimerStream, &ev0, &ev1))   // diagnostic timer (sparsekv_timer_enable)
-    hipExtLaunchKernelGGL(skv::tier_fetch_kernel, dim3(128, t->B), dim3(256), 0, st, ev0, ev1, 0,
-                          t->host_dev, t->miss_pos, t->miss_slot, t->miss_count, t->res_k, t->res_v,
-                          t->res_ks, t->res_vs, (int64_t)t->cap_ctx, t->Hkv, t->mstride, t->res_rows,
-                          t->S + t->L);
-  else
-    hipLaunchKernelGGL(skv::tier_fetch_kernel, dim3(128, t->B), dim3(256), 0, st, t->host_dev,
-                       t->miss_pos, t->miss_slot, t->miss_count, t->res_k, t->res_v, t->res_ks,
-                       t->res_vs, (int64_t)t->cap_ctx, t->Hkv, t->mstride, t->res_rows, t->S + t->L);
-  if (hipGetLastError() != hipSuccess) return set_error(SKV_ERR_HIP, "tier_fetch: launch failed");
   t->steps += 1;
   return SKV_OK;
 }
@@ -737,7 +960,7 @@ extern "C" skv_status sparsekv_tier_append(skv_tier* t, int32_t* ctx_len, const 
 
 extern "C" skv_status sparsekv_tier_stats(skv_tier* t, skv_tier_stats* out, void* stream) {
   if (!t || !out) return set_error(SKV_ERR_INVALID, "tier_stats: NULL argument");
-  unsigned long long c[3] = {0, 0, 0};
+  unsigned long long c[4] = {0, 0, 0, 0};
   uint32_t fl = 0;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess ||
       hipMemcpy(c, t->counters, sizeof(c), hipMemcpyDeviceToHost) != hipSuccess ||
@@ -748,6 +971,7 @@ extern "C" skv_status sparsekv_tier_stats(skv_tier* t, skv_tier_stats* out, void
   out->hits = (int64_t)c[1];
   out->misses = (int64_t)c[2];
   out->host_bytes = (int64_t)c[2] * t->Hkv * t->rec_bytes;
+  out->in_place = (int64_t)c[3];
   if (fl) return set_error(SKV_ERR_STATE, "tier: device flags 0x%x (invalid selection or append input)", fl);
   return SKV_OK;
 }
@@ -758,6 +982,67 @@ extern "C" skv_status sparsekv_tier_slots(skv_tier* t, int32_t* slot_pos_host, v
       hipMemcpy(slot_pos_host, t->slot_pos, (size_t)t->B * t->n_slots * 4, hipMemcpyDeviceToHost) != hipSuccess)
     return set_error(SKV_ERR_HIP, "tier_slots: readback failed");
   return SKV_OK;
+}
+
+extern "C" skv_status sparsekv_tier_map_page(skv_tier* t, int32_t seq, int32_t page, int32_t block,
+                                             const int8_t* k, const int8_t* v, const uint16_t* ks,
+                                             const uint16_t* vs, void* stream) {
+  if (!t) return set_error(SKV_ERR_INVALID, "tier_map_page: NULL tier");
+  if (!t->P || t->pool_pages < 1) return set_error(SKV_ERR_STATE, "tier_map_page: the tier has no page pool");
+  if (seq < 0 || seq >= t->B || page < 0 || page >= t->n_pages || block < 0 || block >= t->pool_pages)
+    return set_error(SKV_ERR_INVALID, "tier_map_page: seq %d / page %d / block %d out of range", seq, page, block);
+  const size_t pi = (size_t)seq * t->n_pages + page, bi = (size_t)seq * t->pool_pages + block;
+  if (t->page_host[pi] >= 0)
+    return set_error(SKV_ERR_STATE, "tier_map_page: page %d of sequence %d is already mapped", page, seq);
+  if (t->block_page[bi] >= 0)
+    return set_error(SKV_ERR_STATE, "tier_map_page: block %d of sequence %d holds page %d", block, seq,
+                     t->block_page[bi]);
+  if ((k != nullptr) != (v != nullptr) || (k != nullptr) != (ks != nullptr) || (k != nullptr) != (vs != nullptr))
+    return set_error(SKV_ERR_INVALID, "tier_map_page: give all of k, v, k_scale, v_scale or none");
+  hipStream_t st = (hipStream_t)stream;
+  if (k) {
+    const size_t row0 = (size_t)seq * t->res_rows + (size_t)t->pool_row0 + (size_t)block * t->P;
+    const size_t rows = (size_t)t->P * t->Hkv;   // (row, head) pairs of the page
+    if (hipMemcpyAsync(t->res_k + row0 * t->Hkv * t->D, k, rows * t->D, hipMemcpyDeviceToDevice, st) != hipSuccess ||
+        hipMemcpyAsync(t->res_v + row0 * t->Hkv * t->D, v, rows * t->D, hipMemcpyDeviceToDevice, st) != hipSuccess ||
+        hipMemcpyAsync(t->res_ks + row0 * t->Hkv, ks, rows * 2, hipMemcpyDeviceToDevice, st) != hipSuccess ||
+        hipMemcpyAsync(t->res_vs + row0 * t->Hkv, vs, rows * 2, hipMemcpyDeviceToDevice, st) != hipSuccess)
+      return set_error(SKV_ERR_HIP, "tier_map_page: copy failed");
+  }
+  hipLaunchKernelGGL(skv::tier_set_page_kernel, dim3(1), dim3(1), 0, st, t->page_block, (int64_t)pi, block);
+  if (hipGetLastError() != hipSuccess) return set_error(SKV_ERR_HIP, "tier_map_page: launch failed");
+  t->page_host[pi] = block;
+  t->block_page[bi] = page;
+  return SKV_OK;
+}
+
+extern "C" skv_status sparsekv_tier_unmap_page(skv_tier* t, int32_t seq, int32_t page, void* stream) {
+  if (!t) return set_error(SKV_ERR_INVALID, "tier_unmap_page: NULL tier");
+  if (!t->P || t->pool_pages < 1) return set_error(SKV_ERR_STATE, "tier_unmap_page: the tier has no page pool");
+  if (seq < 0 || seq >= t->B || page < 0 || page >= t->n_pages)
+    return set_error(SKV_ERR_INVALID, "tier_unmap_page: seq %d / page %d out of range", seq, page);
+  const size_t pi = (size_t)seq * t->n_pages + page;
+  const int32_t block = t->page_host[pi];
+  if (block < 0) return set_error(SKV_ERR_STATE, "tier_unmap_page: page %d of sequence %d is not mapped", page, seq);
+  hipLaunchKernelGGL(skv::tier_set_page_kernel, dim3(1), dim3(1), 0, (hipStream_t)stream, t->page_block,
+                     (int64_t)pi, -1);
+  if (hipGetLastError() != hipSuccess) return set_error(SKV_ERR_HIP, "tier_unmap_page: launch failed");
+  t->page_host[pi] = -1;
+  t->block_page[(size_t)seq * t->pool_pages + block] = -1;
+  return SKV_OK;
+}
+
+extern "C" skv_status sparsekv_tier_attend(skv_tier* t, const void* q, const int32_t* rows,
+                                           const int32_t* n_sel, float sm_scale, float* out, void* ws,
+                                           size_t ws_bytes, void* stream) {
+  if (!t) return set_error(SKV_ERR_INVALID, "tier_attend: NULL tier");
+  skv_kv_view v;
+  v.k = t->res_k;
+  v.v = t->res_v;
+  v.k_scale = t->res_ks;
+  v.v_scale = t->res_vs;
+  v.rows = t->res_rows;
+  return sparsekv_attend(&t->desc.layer, q, &v, rows, n_sel, sm_scale, out, ws, ws_bytes, stream);
 }
 
 extern "C" skv_status sparsekv_tier_reset(skv_tier* t, void* stream) {
