@@ -263,6 +263,28 @@ def committed_traffic():
         return None
 
 
+TIER_IO_FILE = os.path.join(ROOT, "profiles", "tier_resolve_cfg5_pcie_traffic.md")
+TIER_SRC = [os.path.join(ROOT, "top_sparse_kv_amd", "csrc", "tier.hip")]
+
+
+def committed_io_ratio(config: str):
+    """Host (PCIe) bytes the fused tier resolver reads per algorithmic host
+    byte, from the committed counter summary of this line, or None when there
+    is none or the kernel source changed since it was taken."""
+    try:
+        with open(TIER_IO_FILE) as f:
+            fields = dict(ln.split(":", 1) for ln in f.read().splitlines()
+                          if ln.startswith(("io_ratio_", "tier_src_sha256_16:")))
+    except OSError:
+        return None
+    if fields.get("tier_src_sha256_16", "").strip() != source_hash(TIER_SRC):
+        return None
+    try:
+        return float(fields["io_ratio_" + config])
+    except (KeyError, ValueError):
+        return None
+
+
 def rocprof_summary(path, out):
     """Writes a short text summary of a rocprofv3 csv: kernel stats (average
     duration per library kernel) or counter collection (average value per
@@ -895,6 +917,9 @@ def bench_tier(cfg, args):
         e1.synchronize()
         secs = e0.elapsed_time(e1) / 1e3
         st1 = tier.stats()
+        # host bytes of every resolver dispatch in this process (the counter
+        # pass over this command sees all of them)
+        all_bytes, all_calls = st1.host_bytes, st1.steps
         # the resolve alone, on a replay of the same picks from a reset buffer
         tier.reset()
         for s_ in range(warm):
@@ -906,6 +931,9 @@ def bench_tier(cfg, args):
         e1.record()
         e1.synchronize()
         rsecs = e0.elapsed_time(e1) / 1e3
+        st2 = tier.stats()
+        all_bytes += st2.host_bytes
+        all_calls += st2.steps
         # the fused resolver (resolve + zero-copy fetch), timed by its own
         # dispatches (a third replay of the same picks: the same misses)
         tier.reset()
@@ -916,6 +944,9 @@ def bench_tier(cfg, args):
             resolve(s_)
         f_ms, f_n = skv.timer_read()
         skv.timer_enable(False)
+        st3 = tier.stats()
+        all_bytes += st3.host_bytes
+        all_calls += st3.steps
         assert skv.check(ws) == 0
         zc = zero_copy_read(64)
         cpu = None
@@ -953,7 +984,8 @@ def bench_tier(cfg, args):
                  "resolve_us": round(rsecs / steps * 1e6, 2),
                  "pcie_GBps_during_resolve": round(hbytes / rsecs / 1e9, 2),
                  "pcie_peak_GBps": 64.0,
-                 "zero_copy_read": zc},
+                 "zero_copy_read": zc,
+                 "host_bytes_all_resolves": int(all_bytes), "resolve_calls": int(all_calls)},
         "roofline": None,
         "cpu_baseline": cpu,
     }
@@ -962,10 +994,11 @@ def bench_tier(cfg, args):
     if f_n:
         f_s = f_ms / 1e3 / f_n
         per = hbytes / steps
+        io = committed_io_ratio(args.config)
         res_line["roofline"] = {"kernel": "tier_resolve (resolve + zero-copy fetch, one kernel)", "bound": "pcie",
                                 "achieved": round(per / f_s / 1e9, 2), "peak": PCIE5_X16_GBS,
                                 "unit": "GB/s", "frac": round(per / f_s / 1e9 / PCIE5_X16_GBS, 4),
-                                "traffic": None, "bytes_per_launch": round(per),
+                                "traffic": round(io * per) if io else None, "bytes_per_launch": round(per),
                                 "avg_launch_us": round(f_s * 1e6, 2), "launches_timed": f_n}
     print(json.dumps(res_line), flush=True)
 
