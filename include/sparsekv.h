@@ -79,7 +79,7 @@ enum {
   SKV_FLAG_INDEX_RANGE = 1u << 1,  /* attend: an index outside [0, rows) or n_sel > cap (skipped/clamped) */
   SKV_FLAG_TOPK_SLOW = 1u << 2,    /* informational: a sequence needed the exact slow select path */
   SKV_FLAG_TIER_INPUT = 1u << 3,   /* tier: a pick outside [0, ctx) or unsorted input (skipped) */
-  SKV_FLAG_TIER_WAIT = 1u << 4,    /* tier: a fetch workgroup stopped waiting for its resolver (rows not fetched) */
+  SKV_FLAG_WAIT = 1u << 4,         /* a workgroup stopped waiting for another of its sequence (results incomplete) */
 };
 
 /*

@@ -25,7 +25,7 @@ SKV_INDEX_SKETCH_INT4, SKV_INDEX_POOLED_BF16 = 0, 1
 SKV_KV_I8_ROWSCALE, SKV_KV_F16, SKV_KV_BF16 = 0, 1, 2
 SKV_Q_F16, SKV_Q_BF16 = 0, 1
 SKV_FLAG_CTX_RANGE, SKV_FLAG_INDEX_RANGE, SKV_FLAG_TOPK_SLOW, SKV_FLAG_TIER_INPUT = 1, 2, 4, 8
-SKV_FLAG_TIER_WAIT = 16
+SKV_FLAG_WAIT = 16
 SKV_TIER_CLOCK, SKV_TIER_LRU = 0, 1
 SKV_TIMER_STREAM, SKV_TIMER_ATTEND = 1, 2
 STATUS = {0: "SKV_OK", 1: "SKV_ERR_INVALID", 2: "SKV_ERR_UNSUPPORTED", 3: "SKV_ERR_WORKSPACE",

@@ -160,7 +160,7 @@ __device__ __forceinline__ bool wait_word(int32_t* word, uint32_t* flags, int* s
     while (get(word) == 0) {
       if (wall_clock64() - t0 > kWaitTicks) {
         ok = 0;
-        raise_flag(flags, SKV_FLAG_TIER_WAIT);
+        raise_flag(flags, SKV_FLAG_WAIT);
         break;
       }
       __builtin_amdgcn_s_sleep(8);
