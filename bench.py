@@ -48,6 +48,14 @@ CONFIGS = {
                  kv="i8", layers=8, seed=1002,
                  workload="8 seq x 250,000 tokens; 4 KV x 24 q heads, head_dim 256; int4 rank-64 "
                           "sketch; int8 K/V + fp16 row scales; top-2048 + 64 sinks + 1024 tail"),
+    "cfg2k": dict(kind="token", B=8, T=250_000, n_kv=4, n_q=24, D=256, S=64, k=4096, L=1024, kv="i8",
+                  layers=8, seed=1002,
+                  workload="8 seq x 250,000 tokens; cfg2 layer shape with the largest budget, top-4096 "
+                           "+ 64 sinks + 1024 tail (5,184 rows per sequence)"),
+    "cfg2kl": dict(kind="token", B=1, T=2_097_152, n_kv=4, n_q=24, D=256, S=64, k=4096, L=1024, kv="i8",
+                   layers=2, seed=73,
+                   workload="1 seq x 2,097,152 tokens (the largest context) with the largest budget, "
+                            "top-4096 + 64 sinks + 1024 tail; cfg2 layer shape"),
     "cfg4a": dict(kind="token", B=32, T=131_072, n_kv=4, n_q=24, D=256, S=64, k=2048, L=1024,
                   kv="i8", layers=4, seed=1004,
                   workload="32 seq x 131,072 tokens; cfg2 layer shape"),
@@ -1124,7 +1132,7 @@ def main():
     skv.check(ws)
     log("timing %d layer-steps" % args.steps)
     secs = time_loop(Layer.step, layers, ws, args.steps)
-    skv.check(ws)
+    step_flags = skv.check(ws)   # SKV_FLAG_TOPK_SLOW: some select ran the exact slow path
     # the dominant kernel, in the same step loop: its dispatches record events
     skv.timer_enable(True)
     time_loop(Layer.step, layers, ws, max(50, args.steps // 2))
@@ -1209,6 +1217,7 @@ def main():
         "step_hbm": {"algorithmic_bytes": ab["total"], "achieved_GBps": round(ab["total"] * value / 1e9, 1),
                      "frac_of_peak": round(ab["total"] * value / 1e9 / PEAK_HBM_GBS, 4)},
         "kernels_us": {k: round(v * 1e6, 2) for k, v in kt.items()},
+        "select_slow_path": bool(step_flags & skv.SKV_FLAG_TOPK_SLOW),
         "roofline": roof,
         "other_kernel": att,
     }
