@@ -1095,6 +1095,9 @@ def main():
     ap.add_argument("--rocprof-summary", metavar="CSV",
                     help="summarise a rocprofv3 csv into --out and exit")
     ap.add_argument("--out", default=None)
+    ap.add_argument("--contraction-path", choices=["mfma", "valu"], default="mfma",
+                    help="kernel of single-query int8 attention: matrix cores (default) or the "
+                         "fp32 vector-ALU kernel kept to measure what the matrix cores bring")
     args = ap.parse_args()
     if args.rocprof_summary:
         rocprof_summary(args.rocprof_summary, args.out or "/dev/stdout")
@@ -1106,6 +1109,8 @@ def main():
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     cfg = CONFIGS[args.config]
+    if args.contraction_path == "valu":
+        skv.set_contraction_path(skv.SKV_PATH_VALU)
     if cfg["kind"] == "prefill":
         bench_prefill(cfg, args)
         return
@@ -1144,6 +1149,20 @@ def main():
     time_loop(Layer.step, layers, ws, att_steps)
     att_ms, att_n = skv.timer_read()
     skv.timer_enable(False)
+    # the same launches on the other units (matrix cores vs vector ALUs): what
+    # the matrix cores bring to the contraction each path puts on them (one
+    # query: the attention kernel; several: the sketch score)
+    alt = None
+    if cfg["kind"] == "token" and (multi or cfg["kv"] == "i8"):
+        other = skv.SKV_PATH_MFMA if args.contraction_path == "valu" else skv.SKV_PATH_VALU
+        skv.set_contraction_path(other)
+        time_loop(Layer.step, layers, ws, 5)
+        skv.timer_enable(skv.SKV_TIMER_STREAM if multi else skv.SKV_TIMER_ATTEND)
+        time_loop(Layer.step, layers, ws, att_steps)
+        alt_ms, alt_n = skv.timer_read()
+        skv.timer_enable(False)
+        skv.set_contraction_path(skv.SKV_PATH_VALU if args.contraction_path == "valu" else skv.SKV_PATH_MFMA)
+        alt = ("mfma" if other == skv.SKV_PATH_MFMA else "valu", alt_ms / 1e3 / max(1, alt_n))
     nk = max(50, args.steps // 2)
     kt = {}
     for name in [] if multi else (["qsketch"] if cfg["kind"] == "token" else []) + [
@@ -1180,7 +1199,8 @@ def main():
     # the dominant kernel of the step: the fused score-and-collect stream
     score_s = score_ms / 1e3 / max(1, score_n)
     traffic = committed_traffic() if args.config == "cfg2" else None
-    roof = dict(kernel="score_collect_multi" if multi else "score_collect", bound="hbm",
+    roof = dict(kernel=("score_collect_multi" + (" (vector ALU)" if args.contraction_path == "valu" else ""))
+                if multi else "score_collect", bound="hbm",
                 achieved=round(ab["scan"] / score_s / 1e9, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                 frac=round(ab["scan"] / score_s / 1e9 / PEAK_HBM_GBS, 4), traffic=traffic,
                 bytes_per_launch=ab["scan"], avg_launch_us=round(score_s * 1e6, 2),
@@ -1190,11 +1210,16 @@ def main():
     # the query rows it reads
     att_s = att_ms / 1e3 / att_steps   # one attention launch per step
     att_bytes = ab["gather"] + cfg["B"] * max(1, multi) * cfg["n_q"] * cfg["D"] * 2
-    att = dict(kernel="attend", bound="hbm", achieved=round(att_bytes / att_s / 1e9, 1),
+    att = dict(kernel="attend" if args.contraction_path == "mfma" or multi else "attend (vector ALU)", bound="hbm",
+               achieved=round(att_bytes / att_s / 1e9, 1),
                peak=PEAK_HBM_GBS, unit="GB/s",
                frac=round(att_bytes / att_s / 1e9 / PEAK_HBM_GBS, 4), traffic=None,
                bytes_per_launch=att_bytes, avg_launch_us=round(att_s * 1e6, 2),
                launches_timed=att_n, launches_per_step=round(att_n / att_steps, 2))
+    if alt:
+        d, nb = (roof, ab["scan"]) if multi else (att, att_bytes)
+        d["other_path"] = {"path": alt[0], "avg_launch_us": round(alt[1] * 1e6, 2),
+                           "achieved": round(nb / alt[1] / 1e9, 1)}
     if multi and att_s > score_s:
         # several queries: the per-query gathers outweigh the one shared scan
         roof, att = att, roof
@@ -1213,6 +1238,7 @@ def main():
         "data": "synthetic",
         "config": dict({"workload": cfg["workload"], "name": args.config, "batch": cfg["B"],
                         "ctx": cfg["T"], "rotating_layers": n_layers},
+                       **({"contraction_path": "valu"} if args.contraction_path == "valu" else {}),
                        **({"query_tokens_per_seq": multi} if multi else {})),
         "step_hbm": {"algorithmic_bytes": ab["total"], "achieved_GBps": round(ab["total"] * value / 1e9, 1),
                      "frac_of_peak": round(ab["total"] * value / 1e9 / PEAK_HBM_GBS, 4)},

@@ -47,12 +47,13 @@
 extern "C" {
 #endif
 
-#define SPARSEKV_ABI_VERSION 6   /* 3: multi-query step, prefill over host K/V, tier policy field;
+#define SPARSEKV_ABI_VERSION 7   /* 3: multi-query step, prefill over host K/V, tier policy field;
                                     4: tier append (host records sized by max_ctx, tail ring),
                                        multi-query tier resolve and attention;
                                     5: the step without a workspace argument;
                                     6: tier page residency (desc fields, map / unmap, in_place
-                                       counter), tier_attend, tier_host_ptr */
+                                       counter), tier_attend, tier_host_ptr;
+                                    7: contraction path switch (measurement aid) */
 
 typedef int32_t skv_status;
 enum {
@@ -407,6 +408,7 @@ skv_status sparsekv_check(void* ws, size_t ws_bytes, void* stream, uint32_t* fla
 #define SKV_TIMER_STREAM 1
 #define SKV_TIMER_ATTEND 2
 skv_status sparsekv_timer_enable(int enable);
+skv_status sparsekv_timer_read(double* total_ms, int64_t* launches);
 /* ---- measurement aid: a plain streaming read ---------------------------------
  * Not a step of the method: the reference rate for its dominant read.  Page
  * "3.14M Context on 3x 3090 ...", section "What Needs to Stay in VRAM" (the
@@ -423,7 +425,32 @@ skv_status sparsekv_timer_enable(int enable);
 #define SKV_READ_MAX_WG 65536
 skv_status sparsekv_read_bytes(const void* src, size_t bytes, uint32_t* sink, int32_t n_wg,
                                void* stream);
-skv_status sparsekv_timer_read(double* total_ms, int64_t* launches);
+
+/* ---- measurement aid: the dense contractions on the vector ALUs -------------
+ * Not a step of the method: selects the units that compute the path's two
+ * dense contractions, to measure what the matrix cores bring.
+ *   SKV_PATH_MFMA (the default): matrix-core tiles.
+ *   SKV_PATH_VALU: kernels with the same grid, data layout and outputs that
+ *     compute on the vector ALUs.
+ * The contractions:
+ *   - single-query attention over int8 K/V with row scales (one query per
+ *     sequence, head_dim 128 or 256, at most 7 query heads per KV head at
+ *     head_dim 256 or 12 at 128, the 8-wave workgroup shape) in
+ *     sparsekv_attend, sparsekv_step, sparsekv_step_noalloc and
+ *     sparsekv_tier_attend; page "8 agents x 250K ...", section "The
+ *     mechanism" (exact attention over the gathered rows).  Matrix cores: fp16
+ *     tiles, the probabilities entering P.V as two fp16 parts; vector ALUs:
+ *     fp32 dot products.  Outputs agree to fp32 rounding.
+ *   - the multi-query sketch score (sparsekv_step_multi, sketch rows of at
+ *     most 128 bytes); same page, section "What shipped" (the drafted tokens
+ *     verified in one step).  Matrix cores: int8 tiles; vector ALUs: 4-way
+ *     int8 dot instructions.  Integer arithmetic: index sets and keys are
+ *     bit-identical.
+ * Every other shape takes the matrix-core kernel.  Process-wide and not
+ * thread-safe: set it between calls.  SKV_ERR_INVALID for any other value. */
+#define SKV_PATH_MFMA 0
+#define SKV_PATH_VALU 1
+skv_status sparsekv_set_contraction_path(int32_t path);
 
 /* ---- host-RAM tier (optional) ----------------------------------------------
  * Page "8 agents x 250K ...", section "The mechanism": K/V of every token sit

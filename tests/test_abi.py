@@ -66,7 +66,7 @@ def test_struct_sizes_match_header(skv):
     # page_tokens, pool_pages, (pad); skv_tier_stats: six int64
     assert ctypes.sizeof(skv.TierDesc) == 104
     assert ctypes.sizeof(skv.TierStats) == 6 * 8
-    assert skv.abi_version() == 6
+    assert skv.abi_version() == 7
 
 
 def test_capacity_and_workspace(skv):
@@ -165,6 +165,15 @@ def test_status_strings(skv):
     for s in range(8):
         assert lib.sparsekv_status_str(s)
     assert lib.sparsekv_status_str(99) == b"unknown status"
+
+
+def test_contraction_path_switch(skv):
+    """The measurement switch takes exactly its two values (no device work)."""
+    lib = skv.lib()
+    assert lib.sparsekv_set_contraction_path(2) == 1
+    assert lib.sparsekv_set_contraction_path(-1) == 1
+    assert lib.sparsekv_set_contraction_path(skv.SKV_PATH_VALU) == 0
+    assert lib.sparsekv_set_contraction_path(skv.SKV_PATH_MFMA) == 0
 
 
 def test_multi_query_host_checks(skv):

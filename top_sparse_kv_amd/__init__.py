@@ -21,7 +21,7 @@ from ._lib import (KVView, LayerDesc, TierDesc, TierStats, SKV_INDEX_SKETCH_INT4
                    SKV_INDEX_POOLED_BF16, SKV_KV_I8_ROWSCALE, SKV_KV_F16, SKV_KV_BF16, SKV_Q_F16,
                    SKV_Q_BF16, SKV_FLAG_CTX_RANGE, SKV_FLAG_INDEX_RANGE, SKV_FLAG_TOPK_SLOW,
                    SKV_FLAG_TIER_INPUT, SKV_TIER_CLOCK, SKV_TIER_LRU,
-                   SKV_TIMER_STREAM, SKV_TIMER_ATTEND)
+                   SKV_TIMER_STREAM, SKV_TIMER_ATTEND, SKV_PATH_MFMA, SKV_PATH_VALU)
 
 
 class SkvError(RuntimeError):
@@ -247,6 +247,13 @@ def timer_enable(on=True):
     SKV_TIMER_STREAM: the streaming kernel of each call."""
     kind = 0 if not on else (SKV_TIMER_ATTEND if on == SKV_TIMER_ATTEND else SKV_TIMER_STREAM)
     _check(lib().sparsekv_timer_enable(kind))
+
+
+def set_contraction_path(path: int):
+    """sparsekv_set_contraction_path: SKV_PATH_MFMA (default, matrix cores) or
+    SKV_PATH_VALU (vector ALUs) for single-query int8 attention and the
+    multi-query sketch score; a measurement aid, process-wide."""
+    _check(lib().sparsekv_set_contraction_path(int(path)))
 
 
 def timer_read():

@@ -28,6 +28,7 @@ SKV_FLAG_CTX_RANGE, SKV_FLAG_INDEX_RANGE, SKV_FLAG_TOPK_SLOW, SKV_FLAG_TIER_INPU
 SKV_FLAG_WAIT = 16
 SKV_TIER_CLOCK, SKV_TIER_LRU = 0, 1
 SKV_TIMER_STREAM, SKV_TIMER_ATTEND = 1, 2
+SKV_PATH_MFMA, SKV_PATH_VALU = 0, 1
 STATUS = {0: "SKV_OK", 1: "SKV_ERR_INVALID", 2: "SKV_ERR_UNSUPPORTED", 3: "SKV_ERR_WORKSPACE",
           4: "SKV_ERR_OOM", 5: "SKV_ERR_HIP", 6: "SKV_ERR_HOST_MEMORY", 7: "SKV_ERR_STATE"}
 
@@ -92,6 +93,7 @@ SIGNATURES = [
     ("sparsekv_check", c_i32, [c_vp, c_sz, c_vp, P(c_u32)]),
     ("sparsekv_timer_enable", c_i32, [c_i32]),
     ("sparsekv_timer_read", c_i32, [P(ctypes.c_double), P(c_i64)]),
+    ("sparsekv_set_contraction_path", c_i32, [c_i32]),
     ("sparsekv_tier_create", c_i32, [P(TierDesc), P(c_vp)]),
     ("sparsekv_tier_host_records", c_vp, [c_vp]),
     ("sparsekv_tier_host_ptr", c_vp, [c_vp]),

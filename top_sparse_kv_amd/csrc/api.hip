@@ -573,6 +573,13 @@ skv_status sparsekv_timer_enable(int enable) {
   return ok();
 }
 
+skv_status sparsekv_set_contraction_path(int32_t path) {
+  if (path != SKV_PATH_MFMA && path != SKV_PATH_VALU)
+    return set_error(SKV_ERR_INVALID, "contraction path: %d is neither SKV_PATH_MFMA nor SKV_PATH_VALU", (int)path);
+  g_contract_path = path;
+  return ok();
+}
+
 skv_status sparsekv_timer_read(double* total_ms, int64_t* launches) {
   if (!total_ms || !launches) return set_error(SKV_ERR_INVALID, "timer: NULL pointer");
   double t = 0.0;

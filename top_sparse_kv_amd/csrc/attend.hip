@@ -510,6 +510,162 @@ __global__ __launch_bounds__(64 * WAVES) void attend_kernel(
   }
 }
 
+// ---- the same attention on the vector ALUs (a measurement aid) ------------
+// Same workgroups, rows and partials as attend_kernel<KV_I8, D, 8, ·> with one
+// query per sequence, but both contractions are fp32 dot products on the
+// vector ALUs: for the logits lane l holds row l%32 of its wave's 32 and the
+// query heads [h0, h0 + ceil(G/2)) of half l/32, reading its K row 16 bytes at
+// a time against Q in LDS; for P.V lane l owns D/64 columns and reads them
+// from the 32 V rows (one row = 64 lanes x D/64 bytes, contiguous), with the
+// row-scaled probabilities from LDS.  The waves merge in LDS as in the
+// one-stage path.  Exists to measure what the matrix cores bring.
+constexpr int kValuWaves = 8;
+template <int D>
+__global__ __launch_bounds__(64 * kValuWaves) void attend_valu_kernel(
+    const __half* __restrict__ qv, const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
+    const uint16_t* __restrict__ ksc, const uint16_t* __restrict__ vsc, int64_t rows,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ n_sel, int cap, float scale_log2,
+    int Hq, int Hkv, float* __restrict__ part_ml, float* __restrict__ part_o, int n_chunks,
+    uint32_t* __restrict__ flags, int n_keys) {
+  constexpr int W = kValuWaves;
+  constexpr int GM = 16;          // query heads per KV head, at most
+  constexpr int GH = GM / 2;      // heads per half-wave in the logits
+  constexpr int CPL = D / 64;     // P.V columns per lane
+  // LDS (dynamic, sized by the launch): the waves' output slots [W][G][D] (Q
+  // [G][D] in their first part until the logits are done), the row-scaled
+  // probabilities [W][G][32], and each wave's max, sum and merge factor [W][G]
+  extern __shared__ float s_o[];
+  // workgroup -> (KV head h, chunk c, sequence b), as attend_kernel with one query
+  const int xcd = blockIdx.x & 7, sg = blockIdx.x >> 3;
+  const int key = (sg / Hkv) * 8 + xcd;
+  if (key >= n_keys) return;   // before any barrier
+  const int h = sg % Hkv, c = key % n_chunks, b = key / n_chunks;
+  const int G = Hq / Hkv;
+  float* s_p = s_o + W * G * D;
+  float* s_m = s_p + W * G * 32;
+  float* s_l = s_m + W * G;
+  float* s_f = s_l + W * G;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int n = n_sel[b];
+  if (n < 0 || n > cap) {
+    if (threadIdx.x == 0 && c == 0 && h == 0) raise_flag(flags, SKV_FLAG_INDEX_RANGE);
+    n = n < 0 ? 0 : cap;
+  }
+  const int r0 = c * 32 * W;
+  if (r0 >= n) return;
+  float* s_q = s_o;
+  for (int x = threadIdx.x; x < G * D; x += blockDim.x)
+    s_q[x] = __half2float(qv[((size_t)b * Hq + (size_t)h * G) * D + x]);
+  __syncthreads();
+  // ---- logits of this lane's row for its half of the heads ----
+  const int r = lane & 31, hh = lane >> 5;
+  const int ri = r0 + wave * 32 + r;
+  const int tok = ri < n ? idx[(size_t)b * cap + ri] : -1;
+  const bool ok = ri < n && tok >= 0 && (int64_t)tok < rows;
+  if (ri < n && !ok) raise_flag(flags, SKV_FLAG_INDEX_RANGE);
+  const int t = ok ? tok : 0;
+  const size_t kb = ((size_t)b * rows + t) * Hkv + h;
+  const int j0 = hh * ((G + 1) / 2), j1 = min(G, j0 + (G + 1) / 2);
+  float acc[GH];
+#pragma unroll
+  for (int jj = 0; jj < GH; ++jj) acc[jj] = 0.0f;
+  const int8_t* krow = kc + kb * D;
+  for (int d0 = 0; d0 < D; d0 += 16) {
+    const int4 w = *reinterpret_cast<const int4*>(krow + d0);
+    const int wd[4] = {w.x, w.y, w.z, w.w};
+    float kf[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) kf[e] = (float)(int8_t)((wd[e >> 2] >> (8 * (e & 3))) & 0xFF);
+#pragma unroll
+    for (int jj = 0; jj < GH; ++jj) {
+      const int j = j0 + jj;
+      if (j < j1) {
+        const float* qp = s_q + j * D + d0;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[jj] += qp[e] * kf[e];
+      }
+    }
+  }
+  const float ks = half_bits_to_float(ksc[kb]);
+  const float vs = half_bits_to_float(vsc[kb]);
+#pragma unroll
+  for (int jj = 0; jj < GH; ++jj) {
+    const int j = j0 + jj;
+    const float lg = ok ? acc[jj] * ks * scale_log2 : -INFINITY;
+    float m = lg;
+    for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));   // over the 32 rows
+    const float p = lg == -INFINITY ? 0.0f : exp2f(lg - m);
+    float sum = p;
+    for (int o = 16; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+    if (j < j1) {
+      s_p[(wave * G + j) * 32 + r] = p * vs;
+      if (r == 0) {
+        s_m[wave * G + j] = m;
+        s_l[wave * G + j] = sum;
+      }
+    }
+  }
+  __syncthreads();   // s_p complete; Q no longer read (s_o reused below)
+  // ---- P.V: lane owns columns lane*CPL .. +CPL ----
+  float o[GM][CPL];
+#pragma unroll
+  for (int j = 0; j < GM; ++j)
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) o[j][e] = 0.0f;
+  uint32_t vw[32];
+#pragma unroll
+  for (int rr = 0; rr < 32; ++rr) {
+    const int tr = __shfl(t, rr);   // lanes 0..31 hold the rows' tokens
+    const int8_t* vp = vc + (((size_t)b * rows + tr) * Hkv + h) * D + lane * CPL;
+    vw[rr] = CPL == 4 ? *reinterpret_cast<const uint32_t*>(vp) : (uint32_t)*reinterpret_cast<const uint16_t*>(vp);
+  }
+#pragma unroll
+  for (int rr = 0; rr < 32; ++rr) {
+    float vf[CPL];
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) vf[e] = (float)(int8_t)((vw[rr] >> (8 * e)) & 0xFF);
+#pragma unroll
+    for (int j = 0; j < GM; ++j) {
+      if (j < G) {
+        const float pj = s_p[(wave * G + j) * 32 + rr];
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) o[j][e] += pj * vf[e];
+      }
+    }
+  }
+  // ---- merge the waves: each wave's slot, then the sum in wave order ----
+#pragma unroll
+  for (int j = 0; j < GM; ++j)
+    if (j < G)
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) s_o[((size_t)wave * G + j) * D + lane * CPL + e] = o[j][e];
+  __syncthreads();
+  const size_t pbase = ((size_t)b * Hkv + h) * n_chunks + c;
+  if ((int)threadIdx.x < G) {
+    const int j = threadIdx.x;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < W; ++w) M = fmaxf(M, s_m[w * G + j]);
+    float Ls = 0.0f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const float f = s_m[w * G + j] == -INFINITY ? 0.0f : exp2f(s_m[w * G + j] - M);
+      s_f[w * G + j] = f;
+      Ls += s_l[w * G + j] * f;
+    }
+    part_ml[(pbase * 16 + j) * 2 + 0] = M;
+    part_ml[(pbase * 16 + j) * 2 + 1] = Ls;
+  }
+  __syncthreads();
+  for (int x = threadIdx.x; x < G * D; x += blockDim.x) {
+    const int j = x / D, d = x % D;
+    float a = 0.0f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) a += s_o[((size_t)w * G + j) * D + d] * s_f[w * G + j];
+    part_o[(pbase * G + j) * D + d] = a;
+  }
+}
+
 // merge the chunks of each (sequence, query head) in ascending chunk order
 constexpr int kMaxChunks = kMaxAttChunks;   // one thread per chunk
 
@@ -570,6 +726,8 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(
 
 }  // namespace
 
+int g_contract_path = SKV_PATH_MFMA;
+
 hipError_t launch_attend(const skv_layer_desc& d, const void* q, const skv_kv_view& kv,
                          const int32_t* idx, const int32_t* n_sel, float sm_scale, float* out,
                          void* ws, const WsLayout& Lw, hipStream_t st, int mq) {
@@ -621,7 +779,28 @@ hipError_t launch_attend(const skv_layer_desc& d, const void* q, const skv_kv_vi
     else SKV_AT(KVT, DD, 2);                                                                       \
   } while (0)
   const int kvt = d.kv_dtype == SKV_KV_I8_ROWSCALE ? KV_I8 : (d.kv_dtype == SKV_KV_F16 ? KV_F16 : KV_BF16);
-  if (kvt == KV_I8 && d.head_dim == 256) SKV_AT_W(KV_I8, 256);
+  // LDS of the vector-ALU kernel: output slots, probabilities, max / sum / factor
+  const size_t lv = (size_t)kValuWaves * G * (d.head_dim + 32 + 3) * sizeof(float);
+  if (g_contract_path == SKV_PATH_VALU && kvt == KV_I8 && mq == 1 && waves == kValuWaves &&
+      (d.head_dim == 256 || d.head_dim == 128) && lv <= 64 * 1024) {
+    // the vector-ALU kernel (measurement aid): same grid, partials and merge
+#define SKV_AV(DD)                                                                                 \
+  do {                                                                                             \
+    if (timed)                                                                                     \
+      hipExtLaunchKernelGGL((attend_valu_kernel<DD>), grid, dim3(64 * kValuWaves), lv, st, ev0, ev1, 0, \
+                            (const __half*)q, (const int8_t*)kv.k, (const int8_t*)kv.v, kv.k_scale,  \
+                            kv.v_scale, kv.rows, idx, n_sel, cap, sl, d.n_q_heads, d.n_kv_heads,     \
+                            part_ml, part_o, Lw.n_att_chunks, flags, n_keys);                        \
+    else                                                                                           \
+      hipLaunchKernelGGL((attend_valu_kernel<DD>), grid, dim3(64 * kValuWaves), lv, st,            \
+                         (const __half*)q, (const int8_t*)kv.k, (const int8_t*)kv.v, kv.k_scale,     \
+                         kv.v_scale, kv.rows, idx, n_sel, cap, sl, d.n_q_heads, d.n_kv_heads,        \
+                         part_ml, part_o, Lw.n_att_chunks, flags, n_keys);                           \
+  } while (0)
+    if (d.head_dim == 256) SKV_AV(256);
+    else SKV_AV(128);
+#undef SKV_AV
+  } else if (kvt == KV_I8 && d.head_dim == 256) SKV_AT_W(KV_I8, 256);
   else if (kvt == KV_I8 && d.head_dim == 128) SKV_AT_W(KV_I8, 128);
   else if (kvt == KV_F16 && d.head_dim == 256) SKV_AT_W(KV_F16, 256);
   else if (kvt == KV_F16 && d.head_dim == 128) SKV_AT_W(KV_F16, 128);

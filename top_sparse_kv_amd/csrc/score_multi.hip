@@ -87,6 +87,50 @@ struct MqTile {
   }
 };
 
+// The same 16x dots on the vector ALUs (a measurement aid): lane (query j =
+// l%16, group g = l/16) computes tokens 4g..4g+3 of a tile against query j
+// itself, reading the tile's code rows from LDS (staged there by the wave) and
+// holding query j's codes as even-dim and odd-dim dwords, with 4-way int8 dot
+// instructions against the nibbles masked (odd dims) or shifted (even dims)
+// into the high half of each byte, as in the matrix-core operands.
+template <int TB>
+struct MqTileValu {
+  static constexpr int NU = TB / 4;       // code dwords per token
+  static constexpr int RS = TB + 16;      // LDS row stride (bytes): 4 rows, 4 bank groups
+  int qe[NU], qo[NU];
+
+  __device__ __forceinline__ void init(const int8_t* q8, int lane) {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(q8 + (lane & 15) * 2 * TB);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const uint32_t x0 = p[2 * u], x1 = p[2 * u + 1];   // query dims 8u .. 8u+7
+      qe[u] = (int)((x0 & 0xFFu) | ((x0 >> 8) & 0xFF00u) | ((x1 & 0xFFu) << 16) | ((x1 << 8) & 0xFF000000u));
+      qo[u] = (int)(((x0 >> 8) & 0xFFu) | ((x0 >> 16) & 0xFF00u) | ((x1 << 8) & 0xFF0000u) | (x1 & 0xFF000000u));
+    }
+  }
+  // rows: the tile's 16 code rows in LDS; element e = token 4g + e
+  __device__ __forceinline__ v4i dots(const uint8_t* rows, int lane) const {
+    const int g = lane >> 4;
+    v4i c;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const u32x4* rp = reinterpret_cast<const u32x4*>(rows + (4 * g + e) * RS);
+      int acc = 0;
+#pragma unroll
+      for (int x = 0; x < NU / 4; ++x) {
+        const u32x4 w = rp[x];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          acc = __builtin_amdgcn_sdot4((int)((w[t] << 4) & 0xF0F0F0F0u), qe[4 * x + t], acc, false);
+          acc = __builtin_amdgcn_sdot4((int)(w[t] & 0xF0F0F0F0u), qo[4 * x + t], acc, false);
+        }
+      }
+      c[e] = acc;
+    }
+    return c;
+  }
+};
+
 // the digit and the exact key of a token from its dot and fp16 scale (the same
 // formulas as the single-query stream)
 __device__ __forceinline__ uint32_t mq_digit(int d, uint32_t sc) {
@@ -201,7 +245,8 @@ __global__ __launch_bounds__(kThreads) void sample_multi_kernel(
   }
 }
 
-template <int TB>
+// VALU: the dots on the vector ALUs (MqTileValu), else on the matrix cores
+template <int TB, bool VALU>
 __global__ __launch_bounds__(kThreads) void score_multi_kernel(
     const int8_t* __restrict__ qs, const uint8_t* __restrict__ ik, const uint16_t* __restrict__ isc,
     const int32_t* __restrict__ ctx_len, const TopkState* __restrict__ state,
@@ -210,6 +255,8 @@ __global__ __launch_bounds__(kThreads) void score_multi_kernel(
   constexpr int NQ = 2 * TB, NL = TB / 64;
   __shared__ __align__(16) int8_t s_q[kMaxQueries * NQ];
   __shared__ uint32_t s_cnt[kThreads / 64][16];
+  // VALU: each wave's 64 code rows (row stride TB + 16 bytes)
+  __shared__ __align__(16) uint8_t s_w[VALU ? (kThreads / 64) * 64 * (TB + 16) : 16];
   const int b = blockIdx.y, seg = blockIdx.x;
   const int T = clamp_ctx(ctx_len, b, max_ctx, seg == 0 ? flags : nullptr);
   const Range r = cand_range(SKV_INDEX_SKETCH_INT4, T, S, k, L);   // the last query's range
@@ -246,9 +293,19 @@ __global__ __launch_bounds__(kThreads) void score_multi_kernel(
       w[t][m] = __builtin_nontemporal_load(
           reinterpret_cast<const u32x4*>(cb + (size_t)(r.lo + i) * TB + 64 * m));
   }
+  if constexpr (VALU) {
+    // lane (j, g) holds bytes [16g + 64m, +16) of token 16t + j of the batch
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+      for (int m = 0; m < NL; ++m)
+        *reinterpret_cast<u32x4*>(s_w + (wave * 64 + 16 * t + j) * (TB + 16) + 16 * g + 64 * m) = w[t][m];
+  }
   __syncthreads();
   MqTile<TB> tile;
-  tile.init(s_q, lane);
+  MqTileValu<TB> vtile;
+  if constexpr (VALU) vtile.init(s_q, lane);
+  else tile.init(s_q, lane);
 
   // pass 1: digits and selection; bit 4t+e of mask = token 16t + 4g + e of the batch
   v4i c[kTiles];
@@ -256,7 +313,8 @@ __global__ __launch_bounds__(kThreads) void score_multi_kernel(
   uint32_t mask = 0;
 #pragma unroll
   for (int t = 0; t < kTiles; ++t) {
-    c[t] = tile.mma(w[t]);
+    if constexpr (VALU) c[t] = vtile.dots(s_w + (wave * 64 + 16 * t) * (TB + 16), lane);
+    else c[t] = tile.mma(w[t]);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       scs[t][e] = __shfl(sc_l, 16 * t + 4 * g + e);
@@ -324,18 +382,30 @@ hipError_t launch_multi_tb(const skv_layer_desc& dv, int mq, const int32_t* ctx_
   if (e != hipSuccess) return e;
   const dim3 grid(L.n_seg, B);
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
-  if (timer_next(kTimerStream, &ev0, &ev1))
-    hipExtLaunchKernelGGL((score_multi_kernel<TB>), grid, dim3(kThreads), 0, st, ev0, ev1, 0,
-                          (const int8_t*)qs_out, ik, isc, ctx_len, ws_ptr<const TopkState>(ws, L.state),
-                          ws_ptr<Cand>(ws, L.cand), ws_ptr<uint32_t>(ws, L.segcnt),
-                          ws_ptr<uint32_t>(ws, L.flags), dv.max_ctx, dv.n_sink, dv.topk, dv.n_tail,
-                          L.n_seg, mq);
-  else
-    hipLaunchKernelGGL((score_multi_kernel<TB>), grid, dim3(kThreads), 0, st, (const int8_t*)qs_out,
-                       ik, isc, ctx_len, ws_ptr<const TopkState>(ws, L.state),
-                       ws_ptr<Cand>(ws, L.cand), ws_ptr<uint32_t>(ws, L.segcnt),
-                       ws_ptr<uint32_t>(ws, L.flags), dv.max_ctx, dv.n_sink, dv.topk, dv.n_tail,
-                       L.n_seg, mq);
+  const bool timed = timer_next(kTimerStream, &ev0, &ev1);
+#define SKV_SM(VV)                                                                                 \
+  do {                                                                                             \
+    if (timed)                                                                                     \
+      hipExtLaunchKernelGGL((score_multi_kernel<TB, VV>), grid, dim3(kThreads), 0, st, ev0, ev1, 0, \
+                            (const int8_t*)qs_out, ik, isc, ctx_len,                               \
+                            ws_ptr<const TopkState>(ws, L.state), ws_ptr<Cand>(ws, L.cand),        \
+                            ws_ptr<uint32_t>(ws, L.segcnt), ws_ptr<uint32_t>(ws, L.flags),         \
+                            dv.max_ctx, dv.n_sink, dv.topk, dv.n_tail, L.n_seg, mq);               \
+    else                                                                                           \
+      hipLaunchKernelGGL((score_multi_kernel<TB, VV>), grid, dim3(kThreads), 0, st,                \
+                         (const int8_t*)qs_out, ik, isc, ctx_len,                                  \
+                         ws_ptr<const TopkState>(ws, L.state), ws_ptr<Cand>(ws, L.cand),           \
+                         ws_ptr<uint32_t>(ws, L.segcnt), ws_ptr<uint32_t>(ws, L.flags),            \
+                         dv.max_ctx, dv.n_sink, dv.topk, dv.n_tail, L.n_seg, mq);                  \
+  } while (0)
+  // the vector-ALU variant (a measurement aid) for sketch rows up to 128 bytes
+  if constexpr (TB <= 128) {
+    if (g_contract_path == SKV_PATH_VALU) SKV_SM(true);
+    else SKV_SM(false);
+  } else {
+    SKV_SM(false);
+  }
+#undef SKV_SM
   return hipGetLastError();
 }
 

@@ -161,6 +161,9 @@ __device__ __forceinline__ float bf16_bits_to_float(uint16_t h) {
 constexpr int kTimerStream = SKV_TIMER_STREAM;   // the call's streaming kernel
 constexpr int kTimerAttend = SKV_TIMER_ATTEND;   // the attention kernel
 bool timer_next(int kind, hipEvent_t* start, hipEvent_t* stop);
+// units of the dense contractions (attention, multi-query score): SKV_PATH_MFMA
+// or SKV_PATH_VALU (a measurement aid)
+extern int g_contract_path;
 
 // ---------------------------------------------------------------------------
 // launchers (each returns hipSuccess or the launch error)
