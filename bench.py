@@ -471,7 +471,7 @@ def cpu_baseline_all_cores(layer: Layer, cfg, seq_step_s: float, min_seconds=10.
             np.save(os.path.join(d, "sks_%d.npy" % b), c.sk_scale[b:b + 1].cpu().numpy())
         # repetitions so that the parallel run takes about min_seconds
         reps = max(1, int(min_seconds / max(1e-3, seq_step_s * c.B / n)))
-        reps = min(reps, 20)
+        reps = min(reps, 200)
         args = [(d, b, c.lens[b], c.S, c.k, c.L, c.group, layer.sm, reps) for b in range(c.B)]
         with mp.get_context("spawn").Pool(n) as pool:
             pool.map(_oracle_seq_worker, [(d, b, c.lens[b], c.S, c.k, c.L, c.group, layer.sm, 1)
@@ -497,7 +497,7 @@ def cpu_baseline(layer: Layer, cfg):
         return _cpu_baseline(layer, cfg)
 
 
-def _cpu_baseline(layer: Layer, cfg, min_seconds=10.0, max_reps=20):
+def _cpu_baseline(layer: Layer, cfg, min_seconds=10.0, max_reps=500):
     """Repeats the oracle's layer-step until about min_seconds of timed CPU
     work have accumulated; the gathered K/V rows are moved to the host once,
     outside the timed sections."""

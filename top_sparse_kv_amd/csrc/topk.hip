@@ -334,7 +334,7 @@ constexpr int kOneTripSegs = 2 * kFT;       // segments the one-round-trip path 
 // LDS of the final select, shared by its paths (bytes): the one-trip path's
 // candidate arrays (key, position, digit) plus a member list, or the other
 // paths' register-gather lists and segment offsets
-constexpr size_t kFastBytes = (size_t)kListCap * 14 + 320 * 12 + (size_t)(2 * kOneTripSegs + 2) * 4;
+constexpr size_t kFastBytes = (size_t)kListCap * 14 + 320 * 12;
 constexpr size_t kOldBytes = (size_t)(kListCap + 64) * 12 + (size_t)(kMaxSeg + 1) * 4;
 constexpr size_t kSelLds = kFastBytes > kOldBytes ? kFastBytes : kOldBytes;
 
@@ -377,99 +377,54 @@ __global__ __launch_bounds__(kFT) void topk_final_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
   if (n_parts <= kOneTripSegs) {
-    // ---- two round trips: each thread reads the count of one segment (at
-    // most 1024 segments) together with its first kFetch records (a segment
-    // averages a few candidates, one cache line), or the counts of two
-    // adjacent segments (up to 2048: most hold none, so no record is read
-    // yet); a block prefix sum places the records in LDS in position order;
-    // then the whole block gathers every record not read yet (the long
-    // segments' rest), one contiguous run of them per thread ----
+    // ---- per 1024 segments: each thread reads one segment's count together
+    // with its first kFetch records (a segment averages a few candidates), a
+    // block prefix sum places them in LDS in position order, and the longer
+    // segments read the rest in one more batch ----
     uint64_t* c_key = s_mem;                                                  // [kListCap]
     uint32_t* c_pos = reinterpret_cast<uint32_t*>(c_key + kListCap);          // [kListCap]
     uint16_t* c_dig = reinterpret_cast<uint16_t*>(c_pos + kListCap);          // [kListCap]
     uint64_t* m_hi = reinterpret_cast<uint64_t*>(c_dig + kListCap);           // [320]
     uint32_t* m_lo = reinterpret_cast<uint32_t*>(m_hi + 320);                 // [320]
-    uint32_t* s_soff = m_lo + 320;                                            // [kOneTripSegs + 1]
-    uint32_t* s_eoff = s_soff + kOneTripSegs + 1;                             // [kOneTripSegs + 1]
     uint32_t total = 0;
     bool fits = true;
-    {
-      const bool two = n_parts > kFT;   // workgroup-uniform
-      const uint32_t F0 = two ? 0u : (uint32_t)kFetch;   // records read with the count
-      const int s0 = two ? 2 * (int)threadIdx.x : (int)threadIdx.x;
-      uint32_t cnt[2];
+    for (int r0 = 0; r0 < n_parts; r0 += kFT) {   // workgroup-uniform
+      const int seg = r0 + (int)threadIdx.x;
+      const int segc = min(seg, n_parts - 1);
+      const u32x4* src = reinterpret_cast<const u32x4*>(cb + (size_t)segc * seg_items);
+      uint32_t cnt = sc[segc];
       u32x4 rr[kFetch];
-      {
-        const int segc = min(s0, n_parts - 1);
-        cnt[0] = sc[segc];
-        cnt[1] = two ? sc[min(s0 + 1, n_parts - 1)] : 0u;
-        if (!two) {
-          const u32x4* src = reinterpret_cast<const u32x4*>(cb + (size_t)segc * seg_items);
 #pragma unroll
-          for (int m = 0; m < kFetch; ++m) rr[m] = src[m];   // unconditional, inside the segment
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-        cnt[q] = (q == 0 || two) && s0 + q < n_parts ? min(cnt[q], (uint32_t)seg_items) : 0u;
-      uint32_t tot = 0, etot = 0;
-      const uint32_t off = block_excl_scan(cnt[0] + cnt[1], sh.wsum, &tot);
-      const uint32_t ex[2] = {cnt[0] > F0 ? cnt[0] - F0 : 0u, cnt[1] > F0 ? cnt[1] - F0 : 0u};
-      const uint32_t eoff = block_excl_scan(ex[0] + ex[1], sh.wsum, &etot);
-      if (tot > (uint32_t)kListCap) {   // uniform: more candidates than LDS holds
+      for (int m = 0; m < kFetch; ++m) rr[m] = src[m];   // unconditional, inside the segment
+      cnt = seg < n_parts ? min(cnt, (uint32_t)seg_items) : 0u;
+      uint32_t tot = 0;
+      const uint32_t off = total + block_excl_scan(cnt, sh.wsum, &tot);
+      if (total + tot > (uint32_t)kListCap) {   // uniform: more candidates than LDS holds
         fits = false;
-      } else {
-        if (!two) {
-#pragma unroll
-          for (int m = 0; m < kFetch; ++m)
-            if ((uint32_t)m < cnt[0]) {
-              c_key[off + m] = ((uint64_t)rr[m].y << 32) | rr[m].x;
-              c_pos[off + m] = rr[m].z;
-              c_dig[off + m] = (uint16_t)rr[m].w;
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-          if (s0 + q < n_parts && (q == 0 || two)) {
-            s_soff[s0 + q] = off + (q ? cnt[0] : 0u);
-            s_eoff[s0 + q] = eoff + (q ? ex[0] : 0u);
-          }
-        if (threadIdx.x == 0) {
-          s_soff[n_parts] = tot;
-          s_eoff[n_parts] = etot;
-        }
-        total = tot;
-        if (etot > 0u) {   // uniform
-          __syncthreads();
-          // extra record e (< etot <= kListCap = 8 * kFT) is record
-          // F0 + e - s_eoff[c] of the segment c holding it
-          constexpr int EMAX = kListCap / kFT;
-          const uint32_t ept = (etot + kFT - 1) / kFT;   // <= EMAX
-          const uint32_t e0 = ept * threadIdx.x;
-          if (e0 < etot) {
-            int c = seg_of(s_eoff, n_parts, e0);
-            u32x4 xr[EMAX];
-            uint32_t xat[EMAX];
-#pragma unroll
-            for (int m = 0; m < EMAX; ++m) {
-              if ((uint32_t)m < ept) {
-                const uint32_t e = min(e0 + (uint32_t)m, etot - 1u);
-                while (c + 1 < n_parts && s_eoff[c + 1] <= e) ++c;
-                const uint32_t j = F0 + (e - s_eoff[c]);   // < the segment's count
-                xr[m] = reinterpret_cast<const u32x4*>(cb + (size_t)c * seg_items)[j];
-                xat[m] = s_soff[c] + j;
-              }
-            }
-#pragma unroll
-            for (int m = 0; m < EMAX; ++m)
-              if ((uint32_t)m < ept && e0 + (uint32_t)m < etot) {
-                c_key[xat[m]] = ((uint64_t)xr[m].y << 32) | xr[m].x;
-                c_pos[xat[m]] = xr[m].z;
-                c_dig[xat[m]] = (uint16_t)xr[m].w;
-              }
-          }
-        }
+        break;
       }
+#pragma unroll
+      for (int m = 0; m < kFetch; ++m)
+        if ((uint32_t)m < cnt) {
+          c_key[off + m] = ((uint64_t)rr[m].y << 32) | rr[m].x;
+          c_pos[off + m] = rr[m].z;
+          c_dig[off + m] = (uint16_t)rr[m].w;
+        }
+      // longer segments: the next kFetch2 records in one batch, then (rare)
+      // further batches
+      for (uint32_t m0 = kFetch; m0 < cnt; m0 += kFetch2) {
+        u32x4 r2[kFetch2];
+#pragma unroll
+        for (int m = 0; m < kFetch2; ++m) r2[m] = src[min(m0 + (uint32_t)m, cnt - 1)];
+#pragma unroll
+        for (int m = 0; m < kFetch2; ++m)
+          if (m0 + (uint32_t)m < cnt) {
+            c_key[off + m0 + m] = ((uint64_t)r2[m].y << 32) | r2[m].x;
+            c_pos[off + m0 + m] = r2[m].z;
+            c_dig[off + m0 + m] = (uint16_t)r2[m].w;
+          }
+      }
+      total += tot;
     }
     __syncthreads();
     if (fits && total >= (uint32_t)k) {
