@@ -669,87 +669,61 @@ __global__ __launch_bounds__(64 * kValuWaves) void attend_valu_kernel(
 // merge the chunks of each (sequence, query head) in ascending chunk order
 constexpr int kMaxChunks = kMaxAttChunks;   // one thread per chunk
 
-// NG groups of 256 threads; thread d of a group owns output column d
-// (D <= 256), group q the partials [q*per, (q+1)*per) (per = ceil(n_chunks /
-// NG)), summed in ascending order and the groups' sums added in group order:
-// a fixed order, so the result does not depend on scheduling.  The first
-// kMergeBatch partials of every group are loaded together with the (max, sum)
-// pairs, before the factors are known, so a merge of up to NG*kMergeBatch
-// partials costs one round trip plus the reductions.  Partials at or past the
-// selection's end are never written in this call: they are skipped by a
-// select, not multiplied by zero.
+// Thread d owns output column d (D <= 256); the partials of the first
+// kMergeBatch chunks are loaded together with the (max, sum) pairs, before the
+// factors are known, so a small merge costs one round trip plus the reductions.
+// Chunks at or past the selection's end are not written in this call: they
+// are skipped by a select, not multiplied by a zero factor.
 constexpr int kMergeBatch = 16;
 
-template <int NG>
-__global__ __launch_bounds__(256 * NG) void attend_merge_kernel(
+__global__ __launch_bounds__(256) void attend_merge_kernel(
     const float* __restrict__ part_ml, const float* __restrict__ part_o,
     const int32_t* __restrict__ n_sel, int cap, int Hq, int Hkv, int D, int n_chunks,
     int rows_per_chunk, float* __restrict__ out) {
-  constexpr int NW = 4 * NG;   // waves
-  __shared__ float s_f[kMaxChunks + kMergeBatch];   // read past nc only under a select
-  __shared__ float s_red[2][NW];
-  __shared__ float s_acc[NG][256];
+  __shared__ float s_f[kMaxChunks + kMergeBatch];
+  __shared__ float s_red[2][4];
   const int jq = blockIdx.x, b = blockIdx.y;
   const int G = Hq / Hkv;
   const int h = jq / G, j = jq % G;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int grp = threadIdx.x >> 8, t = threadIdx.x & 255;
-  const size_t pb = ((size_t)b * Hkv + h) * n_chunks;
-  const int d = min(t, D - 1);
-  const float* po = part_o + (pb * G + j) * D + d;   // partial cc at po[cc * G * D]
-  const size_t cstride = (size_t)G * D;
-  const int per = (n_chunks + NG - 1) / NG;
-  const int c0 = grp * per;
-  float v[kMergeBatch];
-#pragma unroll
-  for (int u = 0; u < kMergeBatch; ++u) v[u] = po[(size_t)min(c0 + u, n_chunks - 1) * cstride];   // unconditional
-  const int c = threadIdx.x;   // one partial per thread (n_chunks <= kMaxChunks)
-  const float m = part_ml[((pb + min(c, n_chunks - 1)) * 16 + j) * 2];
-  const float l = part_ml[((pb + min(c, n_chunks - 1)) * 16 + j) * 2 + 1];
   int n = n_sel[b];
   n = n < 0 ? 0 : (n > cap ? cap : n);
   const int nc = min((n + rows_per_chunk - 1) / rows_per_chunk, n_chunks);
+  const size_t pb = ((size_t)b * Hkv + h) * n_chunks;
+  const int d = min((int)threadIdx.x, D - 1);
+  const float* po = part_o + (pb * G + j) * D + d;   // chunk cc at po[cc * G * D]
+  const size_t cstride = (size_t)G * D;
+  float v[kMergeBatch];
+#pragma unroll
+  for (int u = 0; u < kMergeBatch; ++u) v[u] = po[(size_t)min(u, n_chunks - 1) * cstride];   // unconditional
+  const int c = threadIdx.x;   // one chunk per thread (n_chunks <= kMaxChunks)
+  const float m = part_ml[((pb + min(c, n_chunks - 1)) * 16 + j) * 2];
+  const float l = part_ml[((pb + min(c, n_chunks - 1)) * 16 + j) * 2 + 1];
   const bool live = c < nc && m != -INFINITY;
   float M = live ? m : -INFINITY;
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   if (lane == 0) s_red[0][wave] = M;
   __syncthreads();
-  M = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) M = fmaxf(M, s_red[0][w]);
+  M = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
   const float f = live ? exp2f(m - M) : 0.0f;
   float Ls = live ? l * f : 0.0f;
   for (int off = 32; off > 0; off >>= 1) Ls += __shfl_xor(Ls, off);
   if (lane == 0) s_red[1][wave] = Ls;
-  if (c < kMaxChunks) s_f[c] = f;
+  s_f[c] = f;
   __syncthreads();
-  Ls = 0.0f;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) Ls += s_red[1][w];
+  Ls = (s_red[1][0] + s_red[1][1]) + (s_red[1][2] + s_red[1][3]);
   const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
-  // this group's partials in ascending order
-  const int c1 = min(c0 + per, nc);
+  // chunks in ascending order
   float acc = 0.0f;
 #pragma unroll
-  for (int u = 0; u < kMergeBatch; ++u) acc += c0 + u < c1 ? v[u] * s_f[c0 + u] : 0.0f;
-  for (int cc = c0 + kMergeBatch; cc < c1; cc += kMergeBatch) {
+  for (int u = 0; u < kMergeBatch; ++u) acc += u < nc ? v[u] * s_f[u] : 0.0f;
+  for (int cc = kMergeBatch; cc < nc; cc += kMergeBatch) {
 #pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) v[u] = po[(size_t)min(cc + u, c1 - 1) * cstride];
+    for (int u = 0; u < kMergeBatch; ++u) v[u] = po[(size_t)min(cc + u, nc - 1) * cstride];
 #pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) acc += cc + u < c1 ? v[u] * s_f[cc + u] : 0.0f;
+    for (int u = 0; u < kMergeBatch; ++u) acc += cc + u < nc ? v[u] * s_f[cc + u] : 0.0f;
   }
-  if constexpr (NG == 1) {
-    if (t < D) out[((size_t)b * Hq + jq) * D + t] = acc * inv;
-  } else {
-    s_acc[grp][t] = acc;
-    __syncthreads();
-    if (grp == 0 && t < D) {
-      float a = s_acc[0][t];
-#pragma unroll
-      for (int q = 1; q < NG; ++q) a += s_acc[q][t];
-      out[((size_t)b * Hq + jq) * D + t] = a * inv;
-    }
-  }
+  if ((int)threadIdx.x < D) out[((size_t)b * Hq + jq) * D + threadIdx.x] = acc * inv;
 }
 
 }  // namespace
@@ -842,19 +816,9 @@ hipError_t launch_attend(const skv_layer_desc& d, const void* q, const skv_kv_vi
 #undef SKV_AT_ARGS
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // one partial per workgroup (32 * waves rows)
-  const int parts = Lw.n_att_chunks;
-  const int rows_per_part = att_rows_per_wg(d);
-  const dim3 mgrid(d.n_q_heads, d.batch);
-  if (parts <= kMergeBatch)
-    hipLaunchKernelGGL(attend_merge_kernel<1>, mgrid, dim3(256), 0, st, part_ml, part_o, n_sel, cap,
-                       d.n_q_heads, d.n_kv_heads, d.head_dim, parts, rows_per_part, out);
-  else if (parts <= 2 * kMergeBatch)
-    hipLaunchKernelGGL(attend_merge_kernel<2>, mgrid, dim3(512), 0, st, part_ml, part_o, n_sel, cap,
-                       d.n_q_heads, d.n_kv_heads, d.head_dim, parts, rows_per_part, out);
-  else
-    hipLaunchKernelGGL(attend_merge_kernel<4>, mgrid, dim3(1024), 0, st, part_ml, part_o, n_sel, cap,
-                       d.n_q_heads, d.n_kv_heads, d.head_dim, parts, rows_per_part, out);
+  hipLaunchKernelGGL(attend_merge_kernel, dim3(d.n_q_heads, d.batch), dim3(256), 0, st, part_ml,
+                     part_o, n_sel, cap, d.n_q_heads, d.n_kv_heads, d.head_dim, Lw.n_att_chunks,
+                     att_rows_per_wg(d), out);
   return hipGetLastError();
 }
 
