@@ -1058,7 +1058,7 @@ def _tier_cpu_baseline(cfg, c, lists, warm, records_b, lru, n_slots, qm=None, mi
     sm = cfg["D"] ** -0.5
     t_total, reps = 0.0, 0
     with threadpool_limits(limits=1):
-        while reps < 40 and (reps == 0 or t_total < min_seconds) and warm + reps < lists.shape[0]:
+        while reps < 400 and (reps == 0 or t_total < min_seconds) and warm + reps < lists.shape[0]:
             s_ = warm + reps
             idx = [full(s_, j) for j in range(M)]
             t0 = time.perf_counter()
