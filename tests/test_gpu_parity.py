@@ -360,26 +360,32 @@ def _fused_select_vs_oracle(skv, c, qs_np):
     return flags
 
 
-def test_fused_select_all_keys_equal():
+@pytest.mark.parametrize("B", [1, 2])
+def test_fused_select_all_keys_equal(B):
     """A zero query sketch makes every key 0: every candidate ties, there are
     more candidates than the select holds in LDS, and the budget goes to the
-    lowest positions (the select over the candidate records in memory)."""
+    lowest positions (the select over the candidate records in memory).  One
+    sequence takes the threshold over every sampled digit, two over the front
+    workgroups' summary rows."""
     skv = need_gpu()
-    c = _cfg2(2, 40_000, [40_000, 25_000], device="cuda")
+    c = _cfg2(B, 40_000, [40_000, 25_000][:B], device="cuda")
     qs = np.zeros((c.B, 256), dtype=np.int8)
     flags = _fused_select_vs_oracle(skv, c, qs)
     assert flags & skv.SKV_FLAG_TOPK_SLOW
 
 
-def test_fused_select_sample_overshoot():
+@pytest.mark.parametrize("B", [1, 2])
+def test_fused_select_sample_overshoot(B):
     """Large keys planted on three of the sixteen keys of every sampled line
     make the threshold too high: every sampled workgroup's largest digits are
     planted ones, yet the planted keys are fewer than the budget, so the
-    select recomputes every key of the sequence (the exact fallback)."""
+    select recomputes every key of the sequence (the exact fallback).  One
+    sequence takes the threshold over every sampled digit, two over the front
+    workgroups' summary rows."""
     skv = need_gpu()
-    c = _cfg2(1, 120_000, [120_000], n_needles=0, device="cuda")
-    qs = np.zeros((1, 256), dtype=np.int8)
-    qs[0, :] = 1
+    c = _cfg2(B, 120_000, [120_000] * B, n_needles=0, device="cuda")
+    qs = np.zeros((B, 256), dtype=np.int8)
+    qs[:, :] = 1
     n = c.lens[0] - c.S - c.L
     s = max(n // (4 * c.k), 1)                    # the sample takes every s-th line of 16
     lines = (n + 15) // 16
@@ -389,8 +395,8 @@ def test_fused_select_sample_overshoot():
     sampled = np.array([c.S + 16 * s * j + e for j in range(nsl) for e in range(3)])
     assert s == 14 and 1000 < sampled.size < c.k
     # all codes +7 (nibbles 0x7 in both halves): dot = 7 * 256 with qs = 1
-    codes[0, sampled] = 0x77
-    scale[0, sampled] = np.float16(8.0).view(np.uint16)
+    codes[:, sampled] = 0x77
+    scale[:, sampled] = np.float16(8.0).view(np.uint16)
     c.codes.copy_(torch.from_numpy(codes))
     c.sk_scale.copy_(torch.from_numpy(scale.view(np.float16)))
     flags = _fused_select_vs_oracle(skv, c, qs)

@@ -263,7 +263,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
 // kernel takes the need-th largest digit over the rows of a sequence; a row
 // holding more of the sequence's top samples than q can only lower that
 // threshold (more candidates).
-template <class Src, bool FROM_PROJ>
+template <class Src, bool FROM_PROJ, bool ROWS>
 __global__ __launch_bounds__(kFrontThreads) void front_kernel(
     const void* __restrict__ iq, const float* __restrict__ sproj, int8_t* __restrict__ qs_out,
     float* __restrict__ qscale_out, const void* __restrict__ ik, const uint16_t* __restrict__ isc,
@@ -319,6 +319,18 @@ __global__ __launch_bounds__(kFrontThreads) void front_kernel(
     qrow = reinterpret_cast<const uint8_t*>(iq) + (size_t)b * Src::QROW;
   }
   src.init_query(qrow, sub);
+  if constexpr (!ROWS) {
+    // every sampled digit, in line order (workgroup w's lines at w * MW)
+    uint16_t* all = summ + (size_t)b * summ_stride + (size_t)w * MW;
+#pragma unroll
+    for (int u = 0; u < FU; ++u) {
+      uint32_t dig;
+      if constexpr (Src::HAS_AUX) dig = src.digit_of(src.dot(wv[u]), ax[u]);
+      else dig = key_digit16(src.key(wv[u], ax[u]));
+      if (sub == 0) all[wave * PER_IT + u * IPW + tw] = ok[u] ? (uint16_t)dig : (uint16_t)0u;
+    }
+    return;
+  }
 #pragma unroll
   for (int u = 0; u < FU; ++u) {
     uint32_t dig;
@@ -391,6 +403,15 @@ __global__ __launch_bounds__(1024) void beta_kernel(const uint16_t* __restrict__
   if (threadIdx.x == 0) state[b].beta = beta;
 }
 
+// The front leaves per-workgroup summary rows of the sample (the threshold
+// kernel then reads at most 2048 digits with one wave per sequence) or every
+// sampled digit (a 1024-thread workgroup per sequence takes the threshold over
+// all of them).  The rows cost each front workgroup a selection (~3 us) and
+// save the threshold kernel most of its reads; measured per layer-step: rows
+// 1-1.5 us faster at 8 sequences, every digit 1.2 us faster at one sequence
+// and 1.5-2 us faster at 32.
+inline bool front_rows(const skv_layer_desc& d) { return d.batch >= 2 && d.batch <= 16; }
+
 template <class Src>
 hipError_t launch_token_or_block(const skv_layer_desc& d, const int32_t* ctx_len, const void* iq,
                                  const void* q, const float* basis, int8_t* qs_out,
@@ -414,17 +435,23 @@ hipError_t launch_token_or_block(const skv_layer_desc& d, const int32_t* ctx_len
   const dim3 fgrid(front_wgs(Lw->n_samp, Src::LANES), d.batch);
   uint16_t* summ = ws_ptr<uint16_t>(ws, Lw->sdig);
   const int summ_stride = Lw->summ_stride;
-  if (qs_out)
-    hipLaunchKernelGGL((front_kernel<Src, true>), fgrid, dim3(kFrontThreads), 0, st, nullptr,
-                       ws_ptr<const float>(ws, Lw->sproj), qs_out, qscale_out, ik, isc, ctx_len, summ,
-                       summ_stride, mode, d.max_ctx, S, d.topk, L);
-  else
-    hipLaunchKernelGGL((front_kernel<Src, false>), fgrid, dim3(kFrontThreads), 0, st, iq, nullptr,
-                       nullptr, nullptr, ik, isc, ctx_len, summ, summ_stride, mode, d.max_ctx, S,
-                       d.topk, L);
   TopkState* state = ws_ptr<TopkState>(ws, Lw->state);
-  hipLaunchKernelGGL(summary_beta_kernel<Src::LANES>, dim3(d.batch), dim3(64), 0, st,
-                     (const uint16_t*)summ, summ_stride, ctx_len, state, mode, d.max_ctx, S, d.topk, L);
+  const bool rows = front_rows(d);
+#define SKV_FRONT(FP, RW)                                                                          \
+  hipLaunchKernelGGL((front_kernel<Src, FP, RW>), fgrid, dim3(kFrontThreads), 0, st,             \
+                     FP ? nullptr : iq, FP ? ws_ptr<const float>(ws, Lw->sproj) : nullptr, qs_out, \
+                     qscale_out, ik, isc, ctx_len, summ, summ_stride, mode, d.max_ctx, S, d.topk, L)
+  if (qs_out && rows) SKV_FRONT(true, true);
+  else if (qs_out) SKV_FRONT(true, false);
+  else if (rows) SKV_FRONT(false, true);
+  else SKV_FRONT(false, false);
+#undef SKV_FRONT
+  if (rows)
+    hipLaunchKernelGGL(summary_beta_kernel<Src::LANES>, dim3(d.batch), dim3(64), 0, st,
+                       (const uint16_t*)summ, summ_stride, ctx_len, state, mode, d.max_ctx, S, d.topk, L);
+  else   // every sampled digit of a sequence, one workgroup per sequence
+    hipLaunchKernelGGL(beta_kernel, dim3(d.batch), dim3(1024), 0, st, (const uint16_t*)summ,
+                       summ_stride / kLineKeys, ctx_len, state, mode, d.max_ctx, S, d.topk, L, 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const void* iq_score = qs_out ? (const void*)qs_out : iq;
