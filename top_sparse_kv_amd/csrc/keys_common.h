@@ -111,6 +111,16 @@ __host__ __device__ constexpr int front_lines(int lanes) {   // sample lines per
 __host__ __device__ __forceinline__ int front_wgs(int nsl, int lanes) {
   return (nsl + front_lines(lanes) - 1) / front_lines(lanes);
 }
+// without summary rows (every sampled digit written out) the front uses
+// smaller workgroups, 8 loads per lane: the sample is spread over more compute
+// units, each of which gathers only a few lines (4 to 32 per workgroup)
+constexpr int kFrontThreadsAll = 256;
+__host__ __device__ constexpr int front_lines_all(int lanes) {
+  return (kFrontThreadsAll / 64) * 8 * (64 / lanes) / kLineKeys;
+}
+__host__ __device__ __forceinline__ int front_wgs_all(int nsl, int lanes) {
+  return (nsl + front_lines_all(lanes) - 1) / front_lines_all(lanes);
+}
 // digits kept per front workgroup: 1.5 times its share of the needed samples
 // plus 8, rounded up to a multiple of 8, at most its sample (a workgroup
 // holding more of the sequence's top samples than that only lowers the

@@ -264,18 +264,20 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
 // holding more of the sequence's top samples than q can only lower that
 // threshold (more candidates).
 template <class Src, bool FROM_PROJ, bool ROWS>
-__global__ __launch_bounds__(kFrontThreads) void front_kernel(
+__global__ __launch_bounds__(ROWS ? kFrontThreads : kFrontThreadsAll) void front_kernel(
     const void* __restrict__ iq, const float* __restrict__ sproj, int8_t* __restrict__ qs_out,
     float* __restrict__ qscale_out, const void* __restrict__ ik, const uint16_t* __restrict__ isc,
     const int32_t* __restrict__ ctx_len, uint16_t* __restrict__ summ, int summ_stride, int mode,
     int max_ctx, int S, int k, int L) {
-  constexpr int N = Src::LANES, IPW = 64 / N, FU = front_unroll(N), PER_IT = FU * IPW;
+  constexpr int N = Src::LANES, IPW = 64 / N, FU = ROWS ? front_unroll(N) : 8, PER_IT = FU * IPW;
   constexpr int LPW = PER_IT / kLineKeys;                   // sample lines per wave
-  constexpr int NWV = kFrontThreads / 64;
+  constexpr int NTH = ROWS ? kFrontThreads : kFrontThreadsAll;
+  constexpr int NWV = NTH / 64;
   constexpr int LPG = LPW * NWV;                            // sample lines per workgroup
   constexpr int MW = LPG * kLineKeys;                       // sample slots per workgroup
   constexpr int NQ = 32 * N;                                // int8 query sketch values (token mode)
-  static_assert(LPG == front_lines(N), "front geometry");
+  static_assert(LPG == (ROWS ? front_lines(N) : front_lines_all(N)), "front geometry");
+  // token mode (the only FROM_PROJ caller) has N <= 16: NQ <= 512 = 2 * 256 values
   __shared__ int8_t q8[512];
   __shared__ __attribute__((aligned(16))) uint16_t s_dig[MW];
   __shared__ uint32_t s_red[32];
@@ -285,7 +287,7 @@ __global__ __launch_bounds__(kFrontThreads) void front_kernel(
   const Range r = cand_range(mode, ctx_of(ctx_len, b, max_ctx), S, k, L);
   const int s = r.dense ? 1 : sample_stride(r.n, k);
   const int nsl = r.dense ? 0 : sample_lines(r.n, k);
-  const int nwg = front_wgs(nsl, N);
+  const int nwg = ROWS ? front_wgs(nsl, N) : front_wgs_all(nsl, N);
   if (w >= nwg && !(FROM_PROJ && w == 0)) return;   // workgroup-uniform
   const int sub = lane % N, tw = lane / N;
   Src src;
@@ -310,7 +312,7 @@ __global__ __launch_bounds__(kFrontThreads) void front_kernel(
   if constexpr (FROM_PROJ) {
     const float scale = quantize_sketch(sproj + (size_t)b * NQ, NQ, q8, s_red);
     if (w == 0) {
-      for (int i = threadIdx.x; i < NQ; i += kFrontThreads) qs_out[(size_t)b * NQ + i] = q8[i];
+      for (int i = threadIdx.x; i < NQ; i += NTH) qs_out[(size_t)b * NQ + i] = q8[i];
       if (threadIdx.x == 0) qscale_out[b] = scale;
     }
     if (w >= nwg) return;   // workgroup-uniform: dense sequence, sketch written
@@ -432,13 +434,13 @@ hipError_t launch_token_or_block(const skv_layer_desc& d, const int32_t* ctx_len
     return hipGetLastError();
   }
   // the front kernel: grid wide enough for the largest sample of a sequence
-  const dim3 fgrid(front_wgs(Lw->n_samp, Src::LANES), d.batch);
+  const bool rows = front_rows(d);
+  const dim3 fgrid(rows ? front_wgs(Lw->n_samp, Src::LANES) : front_wgs_all(Lw->n_samp, Src::LANES), d.batch);
   uint16_t* summ = ws_ptr<uint16_t>(ws, Lw->sdig);
   const int summ_stride = Lw->summ_stride;
   TopkState* state = ws_ptr<TopkState>(ws, Lw->state);
-  const bool rows = front_rows(d);
 #define SKV_FRONT(FP, RW)                                                                          \
-  hipLaunchKernelGGL((front_kernel<Src, FP, RW>), fgrid, dim3(kFrontThreads), 0, st,             \
+  hipLaunchKernelGGL((front_kernel<Src, FP, RW>), fgrid, dim3(RW ? kFrontThreads : kFrontThreadsAll), 0, st, \
                      FP ? nullptr : iq, FP ? ws_ptr<const float>(ws, Lw->sproj) : nullptr, qs_out, \
                      qscale_out, ik, isc, ctx_len, summ, summ_stride, mode, d.max_ctx, S, d.topk, L)
   if (qs_out && rows) SKV_FRONT(true, true);
