@@ -97,40 +97,18 @@ __host__ __device__ __forceinline__ uint32_t sample_need(int n, int k) {
 
 // ---------------------------------------------------------------------------
 // front of the fused step: the sample is read by workgroups of kFrontThreads,
-// each covering kFrontLines<LANES> consecutive sample lines, and each leaves
-// a summary row of its largest sampled digits (summary_q of them); the
-// threshold is the need-th largest digit over all rows of a sequence
+// 8 loads per lane, each covering front_lines(LANES) consecutive sample lines
+// (4 to 32): the sample is spread over many compute units, each of which
+// gathers only a few lines; every sampled digit is written out and the
+// threshold is the need-th largest of them
 // ---------------------------------------------------------------------------
-constexpr int kFrontThreads = 512;
-// loads per lane of a front workgroup: 8 (a workgroup covers 32 lines or more
-// for lanes <= 8), 16 for wider keys (16 lines at 32 lanes)
-__host__ __device__ constexpr int front_unroll(int lanes) { return lanes >= 16 ? 16 : 8; }
+constexpr int kFrontThreads = 256;
+constexpr int kFrontUnroll = 8;
 __host__ __device__ constexpr int front_lines(int lanes) {   // sample lines per front workgroup
-  return (kFrontThreads / 64) * front_unroll(lanes) * (64 / lanes) / kLineKeys;
+  return (kFrontThreads / 64) * kFrontUnroll * (64 / lanes) / kLineKeys;
 }
 __host__ __device__ __forceinline__ int front_wgs(int nsl, int lanes) {
   return (nsl + front_lines(lanes) - 1) / front_lines(lanes);
-}
-// without summary rows (every sampled digit written out) the front uses
-// smaller workgroups, 8 loads per lane: the sample is spread over more compute
-// units, each of which gathers only a few lines (4 to 32 per workgroup)
-constexpr int kFrontThreadsAll = 256;
-__host__ __device__ constexpr int front_lines_all(int lanes) {
-  return (kFrontThreadsAll / 64) * 8 * (64 / lanes) / kLineKeys;
-}
-__host__ __device__ __forceinline__ int front_wgs_all(int nsl, int lanes) {
-  return (nsl + front_lines_all(lanes) - 1) / front_lines_all(lanes);
-}
-// digits kept per front workgroup: 1.5 times its share of the needed samples
-// plus 8, rounded up to a multiple of 8, at most its sample (a workgroup
-// holding more of the sequence's top samples than that only lowers the
-// threshold, i.e. adds candidates).  With the stride rule above, all rows of a
-// sequence hold at most 1024 digits (2048 with 32-lane keys).
-__host__ __device__ __forceinline__ int summary_q(uint32_t need, int nwg, int lanes) {
-  int q = (int)((3u * need + 2u * (uint32_t)nwg - 1u) / (2u * (uint32_t)nwg)) + 8;
-  q = (q + 7) & ~7;
-  const int m = front_lines(lanes) * kLineKeys;
-  return q < m ? q : m;
 }
 
 // ---------------------------------------------------------------------------
@@ -425,84 +403,6 @@ __device__ __forceinline__ float quantize_sketch(const float* sp, int n, int8_t*
   if (ok1) q8[t + nb] = code(v1);
   __syncthreads();
   return scale;
-}
-
-// ---------------------------------------------------------------------------
-// the need-th largest of m 16-bit digits, by one wave
-// ---------------------------------------------------------------------------
-// LDS operations of one wave complete in issue order; this keeps the compiler
-// from reordering them across the point (no barrier: other waves may be gone)
-__device__ __forceinline__ void wave_lds_order() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-}
-
-// dg: m digits (global or LDS), 16-byte aligned; 0 marks an empty slot.  Lane
-// l holds chunks l, l+64, ... of 8 digits (V chunks per lane, m <= 512*V).
-// hist: 256 words of LDS owned by this wave.  Two passes of a 256-bin
-// histogram (high byte, then the low byte inside the chosen high-byte bin),
-// each scanned from the top by a wave prefix sum.  Returns the largest t with
-// at least `need` digits >= t, or 0 when fewer than need digits are nonzero
-// (keep everything).  Every lane of the wave must call it.
-template <int V>
-__device__ __forceinline__ uint32_t wave_kth_largest(const uint16_t* dg, int m, uint32_t need,
-                                                     uint32_t* hist) {
-  const int lane = threadIdx.x & 63;
-  uint32_t d[8 * V];
-#pragma unroll
-  for (int c = 0; c < V; ++c) {
-    const int ch = c * 64 + lane, nch = (m + 7) / 8;
-    u32x4 v = reinterpret_cast<const u32x4*>(dg)[min(ch, nch - 1)];   // unconditional
-    if (ch >= nch) v = (u32x4){0u, 0u, 0u, 0u};
-    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) d[8 * c + e] = (w4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-  }
-  uint32_t tau = 0, rem = need;
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) hist[4 * lane + j] = 0u;
-    wave_lds_order();
-#pragma unroll
-    for (int e = 0; e < 8 * V; ++e) {
-      const uint32_t x = d[e];
-      if (pass == 0) {
-        if (x) atomicAdd(&hist[x >> 8], 1u);
-      } else if (x && (x >> 8) == (tau >> 8)) {
-        atomicAdd(&hist[x & 255u], 1u);
-      }
-    }
-    wave_lds_order();
-    // lane l owns bins 255-4l .. 252-4l, counted from the top
-    uint32_t c[4], t = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      c[j] = hist[255 - 4 * lane - j];
-      t += c[j];
-    }
-    const uint32_t incl = wave_incl_scan(t);
-    const uint64_t hit = __ballot(incl >= rem);
-    if (!hit) return 0u;                       // fewer than need nonzero digits
-    const int l = (int)__ffsll((unsigned long long)hit) - 1;
-    uint32_t cum = incl - t, bin = 0, before = 0;
-    bool found = false;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (!found && cum + c[j] >= rem) {
-        found = true;
-        bin = (uint32_t)(255 - 4 * lane - j);
-        before = cum;
-      }
-      cum += c[j];
-    }
-    bin = (uint32_t)__builtin_amdgcn_readlane((int)bin, l);
-    before = (uint32_t)__builtin_amdgcn_readlane((int)before, l);
-    tau = pass == 0 ? bin << 8 : (tau & 0xFF00u) | bin;
-    rem -= before;
-    wave_lds_order();
-  }
-  return tau;
 }
 
 // ---------------------------------------------------------------------------

@@ -19,9 +19,10 @@
 // consecutive memory; each wave keeps two batches of eight such loads in
 // flight.  The kernels:
 //   score_kernel<keys>     writes every key (sparsekv_score);
-//   sample_kernel          the 16-bit digits (key rounded to fp32, 1/128
+//   front_kernel           the 16-bit digits (key rounded to fp32, 1/128
 //                          octave per bucket) of a sample of whole 16-candidate
-//                          lines, written to the workspace;
+//                          lines, written to the workspace (token mode: after
+//                          quantizing the projected query sketch);
 //   beta_kernel            one workgroup per sequence finds, from the sampled
 //                          digits, the threshold digit beta (a 256-bin LDS
 //                          histogram window slid down from the largest digit);
@@ -258,36 +259,31 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
 // [16*s*j, 16*s*j + 16)), issuing those loads first.  Token mode with
 // FROM_PROJ: the fp32 query sketch in the workspace is quantized here (one
 // int8 scale per sequence) and workgroup 0 writes it out.  Then the 16-bit
-// digits of its sampled keys, and a summary row: the q largest of them (as a
-// multiset, unordered; empty sample slots count as digit 0).  The threshold
-// kernel takes the need-th largest digit over the rows of a sequence; a row
-// holding more of the sequence's top samples than q can only lower that
-// threshold (more candidates).
-template <class Src, bool FROM_PROJ, bool ROWS>
-__global__ __launch_bounds__(ROWS ? kFrontThreads : kFrontThreadsAll) void front_kernel(
+// digits of its sampled keys, written in line order (empty sample slots as
+// digit 0); the threshold kernel takes the need-th largest digit of the
+// sequence's sample.
+template <class Src, bool FROM_PROJ>
+__global__ __launch_bounds__(kFrontThreads) void front_kernel(
     const void* __restrict__ iq, const float* __restrict__ sproj, int8_t* __restrict__ qs_out,
     float* __restrict__ qscale_out, const void* __restrict__ ik, const uint16_t* __restrict__ isc,
-    const int32_t* __restrict__ ctx_len, uint16_t* __restrict__ summ, int summ_stride, int mode,
+    const int32_t* __restrict__ ctx_len, uint16_t* __restrict__ sdig, int sdig_stride, int mode,
     int max_ctx, int S, int k, int L) {
-  constexpr int N = Src::LANES, IPW = 64 / N, FU = ROWS ? front_unroll(N) : 8, PER_IT = FU * IPW;
+  constexpr int N = Src::LANES, IPW = 64 / N, FU = kFrontUnroll, PER_IT = FU * IPW;
   constexpr int LPW = PER_IT / kLineKeys;                   // sample lines per wave
-  constexpr int NTH = ROWS ? kFrontThreads : kFrontThreadsAll;
-  constexpr int NWV = NTH / 64;
+  constexpr int NWV = kFrontThreads / 64;
   constexpr int LPG = LPW * NWV;                            // sample lines per workgroup
   constexpr int MW = LPG * kLineKeys;                       // sample slots per workgroup
   constexpr int NQ = 32 * N;                                // int8 query sketch values (token mode)
-  static_assert(LPG == (ROWS ? front_lines(N) : front_lines_all(N)), "front geometry");
-  // token mode (the only FROM_PROJ caller) has N <= 16: NQ <= 512 = 2 * 256 values
+  static_assert(LPG == front_lines(N), "front geometry");
+  // token mode (the only FROM_PROJ caller) has N <= 16: NQ <= 512 = 2 * kFrontThreads
   __shared__ int8_t q8[512];
-  __shared__ __attribute__((aligned(16))) uint16_t s_dig[MW];
   __shared__ uint32_t s_red[32];
-  __shared__ uint32_t s_hist[256];
   const int b = blockIdx.y, w = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const Range r = cand_range(mode, ctx_of(ctx_len, b, max_ctx), S, k, L);
   const int s = r.dense ? 1 : sample_stride(r.n, k);
   const int nsl = r.dense ? 0 : sample_lines(r.n, k);
-  const int nwg = ROWS ? front_wgs(nsl, N) : front_wgs_all(nsl, N);
+  const int nwg = front_wgs(nsl, N);
   if (w >= nwg && !(FROM_PROJ && w == 0)) return;   // workgroup-uniform
   const int sub = lane % N, tw = lane / N;
   Src src;
@@ -312,7 +308,7 @@ __global__ __launch_bounds__(ROWS ? kFrontThreads : kFrontThreadsAll) void front
   if constexpr (FROM_PROJ) {
     const float scale = quantize_sketch(sproj + (size_t)b * NQ, NQ, q8, s_red);
     if (w == 0) {
-      for (int i = threadIdx.x; i < NQ; i += NTH) qs_out[(size_t)b * NQ + i] = q8[i];
+      for (int i = threadIdx.x; i < NQ; i += kFrontThreads) qs_out[(size_t)b * NQ + i] = q8[i];
       if (threadIdx.x == 0) qscale_out[b] = scale;
     }
     if (w >= nwg) return;   // workgroup-uniform: dense sequence, sketch written
@@ -321,72 +317,14 @@ __global__ __launch_bounds__(ROWS ? kFrontThreads : kFrontThreadsAll) void front
     qrow = reinterpret_cast<const uint8_t*>(iq) + (size_t)b * Src::QROW;
   }
   src.init_query(qrow, sub);
-  if constexpr (!ROWS) {
-    // every sampled digit, in line order (workgroup w's lines at w * MW)
-    uint16_t* all = summ + (size_t)b * summ_stride + (size_t)w * MW;
-#pragma unroll
-    for (int u = 0; u < FU; ++u) {
-      uint32_t dig;
-      if constexpr (Src::HAS_AUX) dig = src.digit_of(src.dot(wv[u]), ax[u]);
-      else dig = key_digit16(src.key(wv[u], ax[u]));
-      if (sub == 0) all[wave * PER_IT + u * IPW + tw] = ok[u] ? (uint16_t)dig : (uint16_t)0u;
-    }
-    return;
-  }
+  uint16_t* dg = sdig + (size_t)b * sdig_stride + (size_t)w * MW;   // this workgroup's lines
 #pragma unroll
   for (int u = 0; u < FU; ++u) {
     uint32_t dig;
     if constexpr (Src::HAS_AUX) dig = src.digit_of(src.dot(wv[u]), ax[u]);
     else dig = key_digit16(src.key(wv[u], ax[u]));
-    if (sub == 0) s_dig[wave * PER_IT + u * IPW + tw] = ok[u] ? (uint16_t)dig : (uint16_t)0u;
+    if (sub == 0) dg[wave * PER_IT + u * IPW + tw] = ok[u] ? (uint16_t)dig : (uint16_t)0u;
   }
-  // the q largest digits of the workgroup, by wave 0: tau = the q-th largest,
-  // the digits above it compacted by a wave prefix sum, then tau repeated
-  const int qw = summary_q(sample_need(r.n, k), nwg, N);
-  __syncthreads();
-  if (wave != 0) return;
-  constexpr int V = (MW + 511) / 512;   // 8-digit chunks per lane
-  const uint32_t tau = wave_kth_largest<V>(s_dig, MW, (uint32_t)qw, s_hist);
-  uint16_t* row = summ + (size_t)b * summ_stride + (size_t)w * qw;
-  uint32_t at = 0;
-#pragma unroll
-  for (int c = 0; c < V; ++c) {
-    const int ch = c * 64 + lane;
-    const u32x4 v = ch < MW / 8 ? reinterpret_cast<const u32x4*>(s_dig)[ch] : (u32x4){0u, 0u, 0u, 0u};
-    const uint32_t dw[4] = {v.x, v.y, v.z, v.w};
-    uint32_t gt = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) gt += (uint32_t)(((dw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) > tau);
-    const uint32_t incl = wave_incl_scan(gt);
-    uint32_t o = at + incl - gt;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t x = (dw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-      if (x > tau) row[o++] = (uint16_t)x;
-    }
-    at += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-  }
-  for (int i = (int)at + lane; i < qw; i += 64) row[i] = (uint16_t)tau;
-}
-
-// Threshold digit of each sequence: the need-th largest digit over the
-// summary rows the front kernel left (at most 2048 digits, summary_q), by one
-// wave per sequence.
-template <int LANES>
-__global__ __launch_bounds__(64) void summary_beta_kernel(const uint16_t* __restrict__ summ,
-                                                          int summ_stride,
-                                                          const int32_t* __restrict__ ctx_len,
-                                                          TopkState* __restrict__ state, int mode,
-                                                          int max_ctx, int S, int k, int L) {
-  const int b = blockIdx.x;
-  const Range r = cand_range(mode, ctx_of(ctx_len, b, max_ctx), S, k, L);
-  if (r.dense) return;
-  const int nwg = front_wgs(sample_lines(r.n, k), LANES);
-  const uint32_t need = sample_need(r.n, k);
-  const int m = nwg * summary_q(need, nwg, LANES);
-  __shared__ uint32_t hist[256];
-  const uint32_t beta = wave_kth_largest<4>(summ + (size_t)b * summ_stride, min(m, 2048), need, hist);
-  if (threadIdx.x == 0) state[b].beta = beta;
 }
 
 // Threshold digit of each (virtual) sequence from its sampled digits.  With
@@ -404,15 +342,6 @@ __global__ __launch_bounds__(1024) void beta_kernel(const uint16_t* __restrict__
                                 sample_lines(r.n, k) * kLineKeys, sample_need(r.n, k), red);
   if (threadIdx.x == 0) state[b].beta = beta;
 }
-
-// The front leaves per-workgroup summary rows of the sample (the threshold
-// kernel then reads at most 2048 digits with one wave per sequence) or every
-// sampled digit (a 1024-thread workgroup per sequence takes the threshold over
-// all of them).  The rows cost each front workgroup a selection (~3 us) and
-// save the threshold kernel most of its reads; measured per layer-step: rows
-// 1-1.5 us faster at 8 sequences, every digit 1.2 us faster at one sequence
-// and 1.5-2 us faster at 32.
-inline bool front_rows(const skv_layer_desc& d) { return d.batch >= 2 && d.batch <= 16; }
 
 template <class Src>
 hipError_t launch_token_or_block(const skv_layer_desc& d, const int32_t* ctx_len, const void* iq,
@@ -434,26 +363,21 @@ hipError_t launch_token_or_block(const skv_layer_desc& d, const int32_t* ctx_len
     return hipGetLastError();
   }
   // the front kernel: grid wide enough for the largest sample of a sequence
-  const bool rows = front_rows(d);
-  const dim3 fgrid(rows ? front_wgs(Lw->n_samp, Src::LANES) : front_wgs_all(Lw->n_samp, Src::LANES), d.batch);
-  uint16_t* summ = ws_ptr<uint16_t>(ws, Lw->sdig);
-  const int summ_stride = Lw->summ_stride;
+  const dim3 fgrid(front_wgs(Lw->n_samp, Src::LANES), d.batch);
+  uint16_t* sdig = ws_ptr<uint16_t>(ws, Lw->sdig);
+  const int sdig_stride = Lw->sdig_stride;
   TopkState* state = ws_ptr<TopkState>(ws, Lw->state);
-#define SKV_FRONT(FP, RW)                                                                          \
-  hipLaunchKernelGGL((front_kernel<Src, FP, RW>), fgrid, dim3(RW ? kFrontThreads : kFrontThreadsAll), 0, st, \
-                     FP ? nullptr : iq, FP ? ws_ptr<const float>(ws, Lw->sproj) : nullptr, qs_out, \
-                     qscale_out, ik, isc, ctx_len, summ, summ_stride, mode, d.max_ctx, S, d.topk, L)
-  if (qs_out && rows) SKV_FRONT(true, true);
-  else if (qs_out) SKV_FRONT(true, false);
-  else if (rows) SKV_FRONT(false, true);
-  else SKV_FRONT(false, false);
-#undef SKV_FRONT
-  if (rows)
-    hipLaunchKernelGGL(summary_beta_kernel<Src::LANES>, dim3(d.batch), dim3(64), 0, st,
-                       (const uint16_t*)summ, summ_stride, ctx_len, state, mode, d.max_ctx, S, d.topk, L);
-  else   // every sampled digit of a sequence, one workgroup per sequence
-    hipLaunchKernelGGL(beta_kernel, dim3(d.batch), dim3(1024), 0, st, (const uint16_t*)summ,
-                       summ_stride / kLineKeys, ctx_len, state, mode, d.max_ctx, S, d.topk, L, 1);
+  if (qs_out)
+    hipLaunchKernelGGL((front_kernel<Src, true>), fgrid, dim3(kFrontThreads), 0, st, nullptr,
+                       ws_ptr<const float>(ws, Lw->sproj), qs_out, qscale_out, ik, isc, ctx_len, sdig,
+                       sdig_stride, mode, d.max_ctx, S, d.topk, L);
+  else
+    hipLaunchKernelGGL((front_kernel<Src, false>), fgrid, dim3(kFrontThreads), 0, st, iq, nullptr,
+                       nullptr, nullptr, ik, isc, ctx_len, sdig, sdig_stride, mode, d.max_ctx, S,
+                       d.topk, L);
+  // the threshold: one 1024-thread workgroup per sequence over its sample
+  hipLaunchKernelGGL(beta_kernel, dim3(d.batch), dim3(1024), 0, st, (const uint16_t*)sdig,
+                     sdig_stride / kLineKeys, ctx_len, state, mode, d.max_ctx, S, d.topk, L, 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const void* iq_score = qs_out ? (const void*)qs_out : iq;

@@ -38,13 +38,13 @@ struct WsLayout {
   size_t flags;        // uint32 flag word (+ padding)
   size_t state;        // [B] TopkState (sparsekv_topk path)
   size_t sproj;        // [B][H_kv*R] f32 unquantized query sketch
-  size_t sdig;         // [B][summ_stride] u16 sampled key digits / front summary rows
+  size_t sdig;         // [B][sdig_stride] u16 sampled key digits
   size_t segcnt;       // [B][n_seg] u32 candidates found in each segment
   size_t cand;         // [B][n_seg*seg_items] Cand; also the fallback key buffer
   int n_seg;           // segments per sequence
   int seg_items;       // candidates per segment
   int n_samp;          // largest number of sampled lines per sequence
-  int summ_stride;     // u16 per sequence in sdig: room for every front workgroup's whole sample
+  int sdig_stride;     // u16 per sequence in sdig: room for every front workgroup's whole sample
   size_t att_ml;       // [B][H_kv][n_chunks][16][2] f32  (m, l) per head row
   size_t att_o;        // [B][H_kv][n_chunks][G][D] f32
   size_t total;
@@ -97,8 +97,8 @@ inline WsLayout ws_layout(const skv_layer_desc& d) {
   w.n_samp = max_sample_lines(max_cand);
   w.state = off;   off = align_up(off + B * sizeof(TopkState), 256);
   w.sproj = off;   off = align_up(off + B * (size_t)(d.n_kv_heads * (d.rank > 0 ? d.rank : 1)) * 4, 256);
-  w.summ_stride = (w.n_samp + 256) * 16;   // >= front workgroups x sample slots of each (<= 256 lines)
-  w.sdig = off;    off = align_up(off + B * (size_t)w.summ_stride * 2, 256);
+  w.sdig_stride = (w.n_samp + 256) * 16;   // >= front workgroups x sample slots of each (<= 32 lines)
+  w.sdig = off;    off = align_up(off + B * (size_t)w.sdig_stride * 2, 256);
   w.segcnt = off;  off = align_up(off + B * w.n_seg * 4, 256);
   w.cand = off;    off = align_up(off + B * (size_t)w.n_seg * w.seg_items * 16, 256);
   const int cap = select_capacity(d);
