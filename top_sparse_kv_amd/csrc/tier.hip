@@ -84,6 +84,8 @@ struct skv_tier {
   int32_t* slot_ref;     // [B][n_slots]
   int32_t* hand;         // [B]
   int32_t* slot_of_pos;  // [B][cap_ctx]
+  uint32_t* hot_bits;    // [B][hot_words]: bit p set while position p is in the hot buffer
+  int hot_words;         // ceil(cap_ctx / 32)
   int32_t* ctx_dev;      // [B] context of each sequence (advanced by sparsekv_tier_append)
   int64_t appends;       // sparsekv_tier_append calls
   int P, page_shift;     // page size (positions, a power of two) and its log2; 0 / 0: no page table
@@ -115,8 +117,9 @@ constexpr int kMaxListMisses = kMaxTopk + kMaxQueries;
 constexpr int kNoStep = -(1 << 30);
 
 __global__ void tier_reset_kernel(int32_t* slot_pos, int32_t* slot_last, int32_t* slot_ref,
-                                  int32_t* hand, int32_t* slot_of_pos, unsigned long long* counters,
-                                  int B, int n_slots, int cap_ctx) {
+                                  int32_t* hand, int32_t* slot_of_pos, uint32_t* hot_bits,
+                                  unsigned long long* counters, int B, int n_slots, int cap_ctx,
+                                  int hot_words) {
   const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t nth = (size_t)gridDim.x * blockDim.x;
   for (size_t i = tid; i < (size_t)B * n_slots; i += nth) {
@@ -125,6 +128,7 @@ __global__ void tier_reset_kernel(int32_t* slot_pos, int32_t* slot_last, int32_t
     slot_ref[i] = 0;
   }
   for (size_t i = tid; i < (size_t)B * cap_ctx; i += nth) slot_of_pos[i] = -1;
+  for (size_t i = tid; i < (size_t)B * hot_words; i += nth) hot_bits[i] = 0u;
   for (size_t i = tid; i < (size_t)B; i += nth) hand[i] = 0;
   if (tid < 4) counters[tid] = 0ull;
 }
@@ -272,6 +276,7 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ n_sel, int32_t* __restrict__ rows,
     int32_t* __restrict__ slot_pos, int32_t* __restrict__ slot_last, int32_t* __restrict__ slot_ref,
     int32_t* __restrict__ hand_arr, int32_t* __restrict__ slot_of_pos,
+    uint32_t* __restrict__ hot_bits, int hot_words,
     unsigned long long* __restrict__ counters, uint32_t* __restrict__ flags,
     const int32_t* __restrict__ tier_ctx, int T0, int cap_ctx, int S, int L,
     int k, int n_slots, int W, int cap, int step, int mq,
@@ -285,8 +290,12 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
   __shared__ uint8_t s_ref[kMaxSlots];
   __shared__ int32_t s_miss[kMaxListMisses];   // input index of each miss; its slot once placed
   __shared__ int32_t s_mpos[kMaxListMisses];   // its position (read by the serial placement)
+  __shared__ uint16_t s_hit[kMaxListMisses];   // one pick list: input index of each hit
   __shared__ uint32_t s_wsum[kResolveThreads / 64];
-  __shared__ int s_nm, s_nmid, s_ninp, s_bad, s_tlast, s_hand, s_placed;
+  // per-wave counts of a classification round (misses, hits, middle, in
+  // place), two buffers used by alternate rounds: one barrier per round
+  __shared__ __align__(16) uint32_t s_cnt[2][kResolveThreads / 64][4];
+  __shared__ int s_nm, s_nh, s_nmid, s_ninp, s_bad, s_tlast, s_hand, s_placed;
   const int b = blockIdx.x / (1 + n_fetch), role = blockIdx.x % (1 + n_fetch);
   if (role != 0) {   // a fetch workgroup (workgroup-uniform, before any barrier of the resolver)
     fetch_part<MULTI ? kFetchBatch / 2 : kFetchBatch>(host, miss_pos + (size_t)b * mstride,
@@ -300,6 +309,7 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
   int32_t* sl = slot_last + (size_t)b * n_slots;
   int32_t* sr = slot_ref + (size_t)b * n_slots;
   int32_t* sop = slot_of_pos + (size_t)b * cap_ctx;
+  uint32_t* hb = hot_bits + (size_t)b * hot_words;
   const int32_t* pgb = page_block ? page_block + (size_t)b * n_pages : nullptr;
   const int pmask = (1 << page_shift) - 1;
   // scalars first: their loads overlap the slot-table copy
@@ -307,10 +317,14 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
   int hand = hand_arr[b];
   int n_next = n_sel[(size_t)b * mq];
   int moff = 0;   // misses handed to the fetch workgroups by the earlier lists
-  for (int i = threadIdx.x; i < n_slots; i += blockDim.x) {
-    s_pos[i] = sp[i];
-    s_last[i] = sl[i];
-    s_ref[i] = (uint8_t)sr[i];
+  if constexpr (MULTI) {
+    // several lists: the slot table first (one list loads it once the misses
+    // are handed over, off the fetch's critical path)
+    for (int i = threadIdx.x; i < n_slots; i += blockDim.x) {
+      s_pos[i] = sp[i];
+      s_last[i] = sl[i];
+      s_ref[i] = (uint8_t)sr[i];
+    }
   }
   if (threadIdx.x == 0) s_bad = 0;
   // The mq pick lists of the sequence (several query tokens) are resolved one
@@ -323,6 +337,7 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
   int n = n_next;
   if (threadIdx.x == 0) {   // nobody reads these between the previous list's last barrier and the next
     s_nm = 0;
+    s_nh = 0;
     s_nmid = 0;
     s_ninp = 0;
     s_tlast = -1;
@@ -339,6 +354,11 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
   // The picks of the first kPre rounds and their slot / page lookups are
   // loaded together first (the lookups do not change before the placement),
   // so the rounds cost one pair of dependent round trips, not one each.
+  // One list: the hot test reads the bitmap of hot positions instead of the
+  // slot of each pick (the picks ascend, so a 64-byte line of bits serves
+  // several of them: about a quarter of the scattered lines), and the hits
+  // are only listed; their slots are looked up once the misses are handed
+  // over.
   constexpr int kPre = 4;
   int pp[kPre], pq[kPre], ps[kPre], pg[kPre];
 #pragma unroll
@@ -351,11 +371,13 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
   for (int r = 0; r < kPre; ++r) {
     const int p = pp[r];
     const bool midr = p >= S && p < T - L;   // then 0 <= p < T <= cap_ctx
-    ps[r] = midr ? sop[p] : -1;
+    if constexpr (MULTI) ps[r] = midr ? sop[p] : -1;
+    else ps[r] = midr ? (int)hb[p >> 5] : 0;   // the bitmap word of p
     pg[r] = (midr && pgb) ? pgb[p >> page_shift] : -1;
   }
   const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   int round = 0;
+  int nm_run = 0, nh_run = 0, nmid_run = 0, ninp_run = 0;   // the same in every thread
   for (int base = 0; base < n; base += blockDim.x, ++round) {
     const int i = base + threadIdx.x;
     bool miss = false, mid = false, inpl = false;
@@ -371,9 +393,11 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
       p = ib[i];
       prev = i > 0 ? ib[i - 1] : INT32_MIN;
       const bool midr = p >= S && p < T - L;
-      s_pre = midr ? sop[p] : -1;
+      if constexpr (MULTI) s_pre = midr ? sop[p] : -1;
+      else s_pre = midr ? (int)hb[p >> 5] : 0;
       blk_pre = (midr && pgb) ? pgb[p >> page_shift] : -1;
     }
+    bool hit = false;
     if (i < n) {
       const bool sorted = i == 0 || prev < p;
       if (p < 0 || p >= T || !sorted) {
@@ -391,11 +415,15 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
         if (blk >= 0) {
           inpl = true;
           rb[i] = (int)(pool_row0 + ((int64_t)blk << page_shift) + (p & pmask));
-        } else if (s >= 0) {
+        } else if (MULTI ? s >= 0 : (((uint32_t)s >> (p & 31)) & 1u) != 0u) {
           mid = true;
-          s_ref[s] = 1;
-          s_last[s] = step;
-          rb[i] = S + L + s;
+          if constexpr (MULTI) {
+            s_ref[s] = 1;
+            s_last[s] = step;
+            rb[i] = S + L + s;
+          } else {
+            hit = true;
+          }
         } else {
           mid = true;
           miss = true;
@@ -405,14 +433,28 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
     const uint64_t m = __ballot(miss);
     const uint64_t mm = __ballot(mid);
     const uint64_t mi_ = __ballot(inpl);
-    if (lane == 0) {
-      s_wsum[wave] = (uint32_t)__popcll(m);
-      atomicAdd(&s_nmid, (int)__popcll(mm));
-      if (mi_) atomicAdd(&s_ninp, (int)__popcll(mi_));
-    }
+    const uint64_t mh = MULTI ? 0ull : __ballot(hit);
+    uint32_t (*cnt)[4] = s_cnt[round & 1];
+    if (lane == 0)
+      *reinterpret_cast<u32x4*>(cnt[wave]) = (u32x4){(uint32_t)__popcll(m), (uint32_t)__popcll(mh),
+                                                     (uint32_t)__popcll(mm), (uint32_t)__popcll(mi_)};
     __syncthreads();
-    int off = s_nm;
-    for (int w = 0; w < wave; ++w) off += (int)s_wsum[w];
+    // every wave's counts: lane l < 16 reads wave l's, four wave scans give
+    // this wave's offsets (the prefix before it) and the round's totals
+    int off, hoff;
+    {
+      constexpr int NW = kResolveThreads / 64;   // the workgroup is always this size
+      const u32x4 c = lane < NW ? *reinterpret_cast<const u32x4*>(cnt[lane]) : (u32x4){0u, 0u, 0u, 0u};
+      const uint32_t ix = wave_incl_scan(c.x), iy = wave_incl_scan(c.y);
+      const uint32_t iz = wave_incl_scan(c.z), iw = wave_incl_scan(c.w);
+      const int wv = __builtin_amdgcn_readfirstlane(wave);
+      off = nm_run + (wv > 0 ? __builtin_amdgcn_readlane((int)ix, wv - 1) : 0);
+      hoff = nh_run + (wv > 0 ? __builtin_amdgcn_readlane((int)iy, wv - 1) : 0);
+      nm_run += __builtin_amdgcn_readlane((int)ix, 63);
+      nh_run += __builtin_amdgcn_readlane((int)iy, 63);
+      nmid_run += __builtin_amdgcn_readlane((int)iz, 63);
+      ninp_run += __builtin_amdgcn_readlane((int)iw, 63);
+    }
     if (miss) {
       const int at = off + (int)__popcll(m & lt_mask);
       if (at < km) {
@@ -423,14 +465,25 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
         s_bad = 1;
       }
     }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      int tot = 0;
-      for (int w = 0; w < (int)(blockDim.x >> 6); ++w) tot += (int)s_wsum[w];
-      s_nm += tot;
+    if constexpr (!MULTI) {
+      if (hit) {
+        const int at = hoff + (int)__popcll(mh & lt_mask);
+        if (at < kMaxListMisses) {
+          s_hit[at] = (uint16_t)i;
+        } else {
+          rb[i] = 0;      // more middle picks than a list holds: flagged
+          s_bad = 1;
+        }
+      }
     }
-    __syncthreads();
   }
+  if (threadIdx.x == 0) {
+    s_nm = nm_run;
+    s_nh = nh_run;
+    s_nmid = nmid_run;
+    s_ninp = ninp_run;
+  }
+  __syncthreads();
   // a victim always exists when fewer slots are pinned than exist: at most the
   // middle picks of this step plus those of the previous W-1 steps (LRU: the
   // slots not used in this step are the candidates)
@@ -447,6 +500,41 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
     for (int mi = threadIdx.x; mi < nm; mi += blockDim.x) put(miss_pos + (size_t)b * mstride + mi, s_mpos[mi]);
     if (threadIdx.x == 0) put(miss_n + b, nm);
     publish(sync + 4 * b + 0);
+    // now the slot table, then the hits: each refreshes its slot and takes
+    // its row (the slot lookups of up to four hits per thread in flight)
+    for (int j = threadIdx.x; j < n_slots; j += blockDim.x) {
+      s_pos[j] = sp[j];
+      s_last[j] = sl[j];
+      s_ref[j] = (uint8_t)sr[j];
+    }
+    __syncthreads();
+    const int nh = min(s_nh, kMaxListMisses);
+    for (int h0 = 0; h0 < nh; h0 += 4 * (int)blockDim.x) {
+      int hi[4], hs[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int h = h0 + u * (int)blockDim.x + (int)threadIdx.x;
+        hi[u] = h < nh ? (int)s_hit[h] : -1;
+      }
+      int hp[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) hp[u] = hi[u] >= 0 ? ib[hi[u]] : 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) hs[u] = hi[u] >= 0 ? sop[hp[u]] : -1;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (hi[u] < 0) continue;
+        const int sl_ = hs[u];
+        if (sl_ >= 0 && sl_ < n_slots) {
+          s_ref[sl_] = 1;
+          s_last[sl_] = step;
+          rb[hi[u]] = S + L + sl_;
+        } else {   // the bitmap and the slot map disagree: cannot happen; flagged
+          rb[hi[u]] = 0;
+          s_bad = 1;
+        }
+      }
+    }
   }
   __syncthreads();
 
@@ -558,10 +646,14 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
         if (mi < nm) {   // the victims are exactly nm; kept as a guard
           const int p = s_mpos[mi], i = s_miss[mi];
           const int old = s_pos[j];
-          if (old >= 0) sop[old] = -1;
+          if (old >= 0) {
+            sop[old] = -1;
+            atomicAnd(hb + (old >> 5), ~(1u << (old & 31)));
+          }
           s_pos[j] = p;
           s_last[j] = step;
           sop[p] = j;
+          atomicOr(hb + (p >> 5), 1u << (p & 31));
           rb[i] = S + L + j;
           s_miss[mi] = j;   // its slot, for the fetch
         }
@@ -610,11 +702,15 @@ __global__ __launch_bounds__(kResolveThreads) void tier_resolve_kernel(
   auto take = [&](int mi, int j, int t) {
     const int p = s_mpos[mi], i = s_miss[mi];
     const int old = s_pos[j];
-    if (old >= 0) sop[old] = -1;
+    if (old >= 0) {
+      sop[old] = -1;
+      atomicAnd(hb + (old >> 5), ~(1u << (old & 31)));
+    }
     s_pos[j] = p;
     s_ref[j] = 1;
     s_last[j] = step;
     sop[p] = j;
+    atomicOr(hb + (p >> 5), 1u << (p & 31));
     rb[i] = S + L + j;
     s_miss[mi] = j;   // its slot, for the fetch
     if (mi == placed - 1) s_tlast = t;
@@ -703,7 +799,7 @@ using skv::set_error;
 static void tier_free(skv_tier* t) {
   if (!t) return;
   void* dev[] = {t->res_k, t->res_v, t->res_ks, t->res_vs, t->slot_pos, t->slot_last, t->slot_ref,
-                 t->hand, t->slot_of_pos, t->ctx_dev, t->page_block, t->counters, t->flags,
+                 t->hand, t->slot_of_pos, t->hot_bits, t->ctx_dev, t->page_block, t->counters, t->flags,
                  t->miss_pos, t->miss_slot, t->miss_n, t->sync};
   for (void* p : dev)
     if (p) (void)hipFree(p);
@@ -752,7 +848,7 @@ extern "C" skv_status sparsekv_tier_create(const skv_tier_desc* d, skv_tier** ou
   memset(t, 0, sizeof(*t));
   memcpy(&t->desc, d, std::min<size_t>(d->struct_size, sizeof(skv_tier_desc)));
   t->policy = policy;
-  t->B = L.batch; t->T0 = d->ctx; t->cap_ctx = L.max_ctx; t->S = L.n_sink; t->L = L.n_tail; t->k = L.topk;
+  t->B = L.batch; t->T0 = d->ctx; t->cap_ctx = L.max_ctx; t->hot_words = (L.max_ctx + 31) / 32; t->S = L.n_sink; t->L = L.n_tail; t->k = L.topk;
   t->Hkv = L.n_kv_heads; t->D = L.head_dim; t->n_slots = d->n_slots; t->W = d->window;
   t->cap = skv::select_capacity(L);
   t->row_bytes = t->D / 2 + 2 * (t->D / 64);
@@ -812,6 +908,7 @@ extern "C" skv_status sparsekv_tier_create(const skv_tier_desc* d, skv_tier** ou
             hipMalloc(&t->slot_ref, ns * 4) == hipSuccess &&
             hipMalloc(&t->hand, (size_t)t->B * 4) == hipSuccess &&
             hipMalloc(&t->slot_of_pos, (size_t)t->B * t->cap_ctx * 4) == hipSuccess &&
+            hipMalloc(&t->hot_bits, (size_t)t->B * t->hot_words * 4) == hipSuccess &&
             hipMalloc(&t->ctx_dev, (size_t)t->B * 4) == hipSuccess &&
             (!P || hipMalloc(&t->page_block, (size_t)t->B * t->n_pages * 4) == hipSuccess) &&
             hipMalloc(&t->counters, 4 * sizeof(unsigned long long)) == hipSuccess &&
@@ -840,7 +937,8 @@ extern "C" skv_status sparsekv_tier_create(const skv_tier_desc* d, skv_tier** ou
     }
   }
   hipLaunchKernelGGL(skv::tier_reset_kernel, dim3(256), dim3(256), 0, 0, t->slot_pos, t->slot_last,
-                     t->slot_ref, t->hand, t->slot_of_pos, t->counters, t->B, t->n_slots, t->cap_ctx);
+                     t->slot_ref, t->hand, t->slot_of_pos, t->hot_bits, t->counters, t->B, t->n_slots,
+                     t->cap_ctx, t->hot_words);
   if (hipGetLastError() != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
     tier_free(t);
     return set_error(SKV_ERR_HIP, "tier: reset kernel failed");
@@ -896,7 +994,8 @@ static skv_status tier_resolve_lists(skv_tier* t, int32_t n_query, const int32_t
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   const bool timed = skv::timer_next(skv::kTimerStream, &ev0, &ev1);   // diagnostic timer
 #define SKV_RESOLVE_ARGS                                                                           \
-  idx, n_sel, rows, t->slot_pos, t->slot_last, t->slot_ref, t->hand, t->slot_of_pos, t->counters,  \
+  idx, n_sel, rows, t->slot_pos, t->slot_last, t->slot_ref, t->hand, t->slot_of_pos, t->hot_bits, \
+      t->hot_words, t->counters,                                                                   \
       t->flags, t->ctx_dev, t->T0, t->cap_ctx, t->S, t->L, t->k, t->n_slots, t->W, t->cap, step,    \
       n_query, t->page_block, t->n_pages, t->page_shift, t->pool_row0, t->host_dev, t->res_k,       \
       t->res_v, t->res_ks, t->res_vs, t->res_rows, t->Hkv, t->miss_pos, t->miss_slot, t->miss_n, t->sync, \
@@ -1048,8 +1147,8 @@ extern "C" skv_status sparsekv_tier_attend(skv_tier* t, const void* q, const int
 extern "C" skv_status sparsekv_tier_reset(skv_tier* t, void* stream) {
   if (!t) return set_error(SKV_ERR_INVALID, "tier_reset: NULL argument");
   hipLaunchKernelGGL(skv::tier_reset_kernel, dim3(256), dim3(256), 0, (hipStream_t)stream,
-                     t->slot_pos, t->slot_last, t->slot_ref, t->hand, t->slot_of_pos, t->counters,
-                     t->B, t->n_slots, t->cap_ctx);
+                     t->slot_pos, t->slot_last, t->slot_ref, t->hand, t->slot_of_pos, t->hot_bits,
+                     t->counters, t->B, t->n_slots, t->cap_ctx, t->hot_words);
   if (hipGetLastError() != hipSuccess) return set_error(SKV_ERR_HIP, "tier_reset: launch failed");
   t->steps = 0;
   return SKV_OK;
