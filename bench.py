@@ -45,7 +45,7 @@ T0 = time.monotonic()
 
 CONFIGS = {
     "cfg2": dict(kind="token", B=8, T=250_000, n_kv=4, n_q=24, D=256, S=64, k=2048, L=1024,
-                 kv="i8", layers=8, seed=1002,
+                 kv="i8", layers=8, seed=1002, mb=2,
                  workload="8 seq x 250,000 tokens; 4 KV x 24 q heads, head_dim 256; int4 rank-64 "
                           "sketch; int8 K/V + fp16 row scales; top-2048 + 64 sinks + 1024 tail"),
     "cfg2k": dict(kind="token", B=8, T=250_000, n_kv=4, n_q=24, D=256, S=64, k=4096, L=1024, kv="i8",
@@ -164,6 +164,37 @@ class Layer:
         self.out = torch.zeros((c.B, c.n_q, c.D), dtype=torch.float32, device="cuda")
         self.sm = c.D ** -0.5
 
+    def split(self, m):
+        """The batch as m micro-batches of B/m sequences: per micro-batch, the
+        same call on views of this layer's buffers (sequences are independent,
+        so a micro-batch's results are those of its sequences in the whole
+        batch).  Each micro-batch runs on its own stream with its own
+        workspace."""
+        c, per = self.case, self.case.B // m
+        self.groups = []
+        for g in range(m):
+            sl = slice(g * per, (g + 1) * per)
+            kv = skv.kv_view(c.k_cache[sl], c.v_cache[sl], c.k_scale[sl], c.v_scale[sl])
+            if self.M:
+                desc = skv.token_desc(per, c.T_max, c.n_kv, c.n_q, c.D, topk=c.k, n_sink=c.S,
+                                      n_tail=c.L, kv_dtype=self.desc.kv_dtype)
+                a = (desc, self.M, self.ctx[sl], self.mq[sl], self.basis, self.mqs[sl],
+                     self.mqsc[sl], self.ikeys[sl], self.iscale[sl], kv, self.midx[sl],
+                     self.mnsel[sl], self.sm, self.mout[sl])
+                self.groups.append((skv.step_multi, a))
+            else:
+                desc = skv.token_desc(per, c.T_max, c.n_kv, c.n_q, c.D, topk=c.k, n_sink=c.S,
+                                      n_tail=c.L, kv_dtype=self.desc.kv_dtype)
+                a = (desc, self.ctx[sl], self.q[sl], self.basis, self.qs[sl], self.qsc[sl], None,
+                     self.ikeys[sl], self.iscale[sl], kv, self.idx[sl], self.nsel[sl], self.sm,
+                     self.out[sl])
+                self.groups.append((skv.step, a))
+        return self.groups
+
+    def step_groups(self, wss, streams):
+        for (fn, a), w, st in zip(self.groups, wss, streams):
+            fn(*a, w, stream=st)
+
     def step(self, ws):
         if self.M:
             skv.step_multi(self.desc, self.M, self.ctx, self.mq, self.basis, self.mqs, self.mqsc,
@@ -231,6 +262,25 @@ def algorithmic_bytes_multi(cfg, union_rows):
     gather = union_rows * n_kv * (D + 2) * 2
     other = B * M * n_q * D * (2 + 4) + n_kv * D * 64 * 4
     return dict(scan=scan, gather=gather, other=other, total=scan + gather + other)
+
+
+def time_loop_groups(layers, wss, streams, n):
+    """n layer-steps, each as the layer's micro-batches on their streams (each
+    stream runs its micro-batch's layer-steps in order); the streams fork from
+    and join back to the current stream inside the timed region."""
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for s in streams:
+        s.wait_event(e0)
+    for i in range(n):
+        layers[i % len(layers)].step_groups(wss, streams)
+    for s in streams:
+        st.wait_stream(s)
+    e1.record(st)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / 1e3   # seconds
 
 
 def time_loop(fn, layers, ws, n):
@@ -1087,6 +1137,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--config", default="cfg2", choices=sorted(CONFIGS))
     ap.add_argument("--layers", type=int, default=0, help="rotating layer buffers (0 = config default)")
+    ap.add_argument("--micro-batches", type=int, default=0,
+                    help="token configs: run the batch as this many micro-batches on as many streams "
+                         "(0 = config default, 1 = one call per layer-step on one stream)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--chunk-mib", type=int, default=0,
                     help="prefill: device working buffer in MiB (0 = config default)")
@@ -1135,9 +1188,34 @@ def main():
     for i in range(args.warmup):
         layers[i % n_layers].step(ws)
     skv.check(ws)
-    log("timing %d layer-steps" % args.steps)
-    secs = time_loop(Layer.step, layers, ws, args.steps)
-    step_flags = skv.check(ws)   # SKV_FLAG_TOPK_SLOW: some select ran the exact slow path
+    mb = args.micro_batches or cfg.get("mb", 1)
+    if mb > 1 and (cfg["kind"] != "token" or cfg["B"] % mb):
+        sys.exit("--micro-batches %d: needs a token-mode batch divisible by it" % mb)
+    single = None
+    if mb > 1:
+        # the batch as mb micro-batches on mb streams: while one micro-batch
+        # runs its latency-bound select and attention, another streams its
+        # sketch; each stream keeps its own micro-batch's layer-steps in order
+        streams = [torch.cuda.Stream() for _ in range(mb)]
+        for L in layers:
+            L.split(mb)
+        wss = [skv.workspace_multi(a[0], multi) if multi else skv.workspace(a[0])
+               for _, a in layers[0].groups]
+        time_loop_groups(layers, wss, streams, args.warmup)
+        log("timing %d layer-steps as %d micro-batches of %d sequences"
+            % (args.steps, mb, cfg["B"] // mb))
+        secs = time_loop_groups(layers, wss, streams, args.steps)
+        step_flags = 0
+        for w in wss:
+            step_flags |= skv.check(w)
+        log("timing %d layer-steps as one call each on one stream" % args.steps)
+        s1 = time_loop(Layer.step, layers, ws, args.steps)
+        step_flags |= skv.check(ws)
+        single = {"value": round(args.steps / s1, 2), "ms_per_step": round(1e3 * s1 / args.steps, 5)}
+    else:
+        log("timing %d layer-steps" % args.steps)
+        secs = time_loop(Layer.step, layers, ws, args.steps)
+        step_flags = skv.check(ws)   # SKV_FLAG_TOPK_SLOW: some select ran the exact slow path
     # the dominant kernel, in the same step loop: its dispatches record events
     skv.timer_enable(True)
     time_loop(Layer.step, layers, ws, max(50, args.steps // 2))
@@ -1239,6 +1317,8 @@ def main():
         "config": dict({"workload": cfg["workload"], "name": args.config, "batch": cfg["B"],
                         "ctx": cfg["T"], "rotating_layers": n_layers},
                        **({"contraction_path": "valu"} if args.contraction_path == "valu" else {}),
+                       **({"micro_batches": mb, "schedule": "%d micro-batches of %d sequences on %d "
+                           "streams" % (mb, cfg["B"] // mb, mb)} if mb > 1 else {}),
                        **({"query_tokens_per_seq": multi} if multi else {})),
         "step_hbm": {"algorithmic_bytes": ab["total"], "achieved_GBps": round(ab["total"] * value / 1e9, 1),
                      "frac_of_peak": round(ab["total"] * value / 1e9 / PEAK_HBM_GBS, 4)},
@@ -1247,6 +1327,9 @@ def main():
         "roofline": roof,
         "other_kernel": att,
     }
+    if single:
+        # the same layer-steps issued as one call per step on one stream
+        res["single_stream"] = single
     if multi:
         res["query_tokens_per_s"] = round(value * cfg["B"] * multi, 1)
         res["step_hbm"]["union_rows"] = int(ab["gather"] // (cfg["n_kv"] * (cfg["D"] + 2) * 2))

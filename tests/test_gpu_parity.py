@@ -220,6 +220,60 @@ def test_determinism_and_graph_replay():
             assert np.array_equal(idx.cpu().numpy()[bb, :n], a["idx"][bb, :n])
 
 
+def test_micro_batches_on_streams():
+    """The batch split into micro-batches of consecutive sequences, each on its
+    own stream with its own workspace, several layer-steps in a row: every
+    sequence gets the same picks and outputs as in the one-call step, and the
+    outputs match the oracle."""
+    skv = need_gpu()
+    lens = [20_000, 9_000, 3_000, 15_500, 20_000, 3_136]
+    c = _cfg2(6, 20_000, lens, device="cuda")
+    sm = 256 ** -0.5
+    say("micro-batches", lens)
+    a = run_token_gpu(skv, c, sm, fused=True)
+    o = oracle_token(c, sm)
+    cap = skv.select_capacity(token_desc_of(skv, c))
+    for m in (2, 3):
+        per = c.B // m
+        qs = torch.zeros((c.B, 256), dtype=torch.int8, device="cuda")
+        qsc = torch.zeros((c.B,), dtype=torch.float32, device="cuda")
+        idx = torch.full((c.B, cap), -1, dtype=torch.int32, device="cuda")
+        nsel = torch.zeros((c.B,), dtype=torch.int32, device="cuda")
+        out = torch.zeros((c.B, c.n_q, c.D), dtype=torch.float32, device="cuda")
+        streams = [torch.cuda.Stream() for _ in range(m)]
+        calls = []
+        for g in range(m):
+            sl = slice(g * per, (g + 1) * per)
+            desc = skv.token_desc(per, c.T_max, c.n_kv, c.n_q, c.D, topk=c.k, n_sink=c.S,
+                                  n_tail=c.L, kv_dtype=skv.SKV_KV_I8_ROWSCALE)
+            kv = skv.kv_view(c.k_cache[sl], c.v_cache[sl], c.k_scale[sl], c.v_scale[sl])
+            calls.append((desc, c.ctx_len[sl], c.q[sl], c.basis, qs[sl], qsc[sl], None,
+                          c.codes[sl], c.sk_scale[sl], kv, idx[sl], nsel[sl], sm, out[sl],
+                          skv.workspace(desc)))
+        ev = torch.cuda.Event()
+        ev.record()
+        for st in streams:
+            st.wait_event(ev)
+        for rep in range(3):
+            for st, args in zip(streams, calls):
+                skv.step(*args, stream=st)
+        for st in streams:
+            torch.cuda.current_stream().wait_stream(st)
+        torch.cuda.synchronize()
+        for args in calls:
+            assert skv.check(args[-1]) == a["flags"]
+        assert np.array_equal(qs.cpu().numpy(), a["qs"])
+        assert np.array_equal(nsel.cpu().numpy(), a["n_sel"])
+        g = dict(a, idx=idx.cpu().numpy(), out=out.cpu().numpy().astype(np.float64))
+        for b in range(c.B):
+            n = int(a["n_sel"][b])
+            assert np.array_equal(g["idx"][b, :n], a["idx"][b, :n]), (m, b)
+            compare_sel(g, o, b)
+            compare_out(g, o, b)
+        say("micro-batches m=%d: max diff to the one-call step %.3g"
+            % (m, float(np.abs(g["out"] - a["out"]).max())))
+
+
 def test_device_flags():
     """Out-of-range ctx_len and attention indices are clamped/skipped and flagged."""
     skv = need_gpu()
