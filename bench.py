@@ -49,7 +49,7 @@ CONFIGS = {
                  workload="8 seq x 250,000 tokens; 4 KV x 24 q heads, head_dim 256; int4 rank-64 "
                           "sketch; int8 K/V + fp16 row scales; top-2048 + 64 sinks + 1024 tail"),
     "cfg2k": dict(kind="token", B=8, T=250_000, n_kv=4, n_q=24, D=256, S=64, k=4096, L=1024, kv="i8",
-                  layers=8, seed=1002,
+                  layers=8, seed=1002, mb=2,
                   workload="8 seq x 250,000 tokens; cfg2 layer shape with the largest budget, top-4096 "
                            "+ 64 sinks + 1024 tail (5,184 rows per sequence)"),
     "cfg2kl": dict(kind="token", B=1, T=2_097_152, n_kv=4, n_q=24, D=256, S=64, k=4096, L=1024, kv="i8",
@@ -57,13 +57,13 @@ CONFIGS = {
                    workload="1 seq x 2,097,152 tokens (the largest context) with the largest budget, "
                             "top-4096 + 64 sinks + 1024 tail; cfg2 layer shape"),
     "cfg4a": dict(kind="token", B=32, T=131_072, n_kv=4, n_q=24, D=256, S=64, k=2048, L=1024,
-                  kv="i8", layers=4, seed=1004,
+                  kv="i8", layers=4, seed=1004, mb=2,
                   workload="32 seq x 131,072 tokens; cfg2 layer shape"),
     "cfg4b": dict(kind="token", B=32, T=250_000, n_kv=4, n_q=24, D=256, S=64, k=2048, L=1024,
-                  kv="i8", layers=2, seed=1014, mixed=(2048, 250_000),
+                  kv="i8", layers=2, seed=1014, mixed=(2048, 250_000), mb=2,
                   workload="32 seq, lengths uniform in 2,048..250,000 (seeded); cfg2 layer shape"),
     "cfg2m": dict(kind="token", B=8, T=250_000, n_kv=4, n_q=24, D=256, S=64, k=2048, L=1024,
-                  kv="i8", layers=8, seed=1002, M=8,
+                  kv="i8", layers=8, seed=1002, M=8, mb=2,
                   workload="8 seq x 250,000 tokens, 8 query tokens each (current + 7 drafted, "
                            "one pick per query at its causal context); cfg2 layer shape"),
     "cfg3p": dict(kind="prefill", T=1_048_576, P=4096, n_kv=2, n_q=16, D=256, k=512,
