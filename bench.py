@@ -63,7 +63,7 @@ CONFIGS = {
                   kv="i8", layers=2, seed=1014, mixed=(2048, 250_000), mb=2,
                   workload="32 seq, lengths uniform in 2,048..250,000 (seeded); cfg2 layer shape"),
     "cfg2m": dict(kind="token", B=8, T=250_000, n_kv=4, n_q=24, D=256, S=64, k=2048, L=1024,
-                  kv="i8", layers=8, seed=1002, M=8, mb=2,
+                  kv="i8", layers=8, seed=1002, M=8,
                   workload="8 seq x 250,000 tokens, 8 query tokens each (current + 7 drafted, "
                            "one pick per query at its causal context); cfg2 layer shape"),
     "cfg3p": dict(kind="prefill", T=1_048_576, P=4096, n_kv=2, n_q=16, D=256, k=512,
@@ -351,7 +351,25 @@ def rocprof_summary(path, out):
     import collections
     import csv
     lines = []
-    if path.endswith("kernel_stats.csv"):
+    if path.endswith("kernel_trace.csv"):
+        # per kernel and grid shape (a micro-batch's launches have their own
+        # grid), from the individual dispatches
+        groups = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            nm = r["Kernel_Name"]
+            if "skv" not in nm:
+                continue
+            nm = nm.replace("(anonymous namespace)::", "").split("(")[0]
+            gx = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+            gy = int(r["Grid_Size_Y"]) // max(1, int(r["Workgroup_Size_Y"]))
+            groups[(nm, "%d x %d" % (gx, gy))].append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        lines.append("| kernel | workgroups | calls | avg us | min us | max us |")
+        lines.append("|---|---|---|---|---|---|")
+        for (nm, grid), ts in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+            lines.append("| %s | %s | %d | %.2f | %.2f | %.2f |" % (
+                nm, grid, len(ts), sum(ts) / len(ts), min(ts), max(ts)))
+    elif path.endswith("kernel_stats.csv"):
         lines.append("| kernel | calls | avg us | min us | max us |")
         lines.append("|---|---|---|---|---|")
         for r in csv.DictReader(open(path)):
