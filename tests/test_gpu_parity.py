@@ -140,10 +140,45 @@ def test_largest_context_and_budget():
     o = oracle_token(c, sm)
     err = _check_token(c, g, o)
     assert g["n_sel"].tolist() == [64 + 4096 + 1024]
-    # at this budget the candidates can outnumber the 8192 the fast select
-    # holds; the exact slower path then runs and raises the informational flag
-    assert g["flags"] & ~skv.SKV_FLAG_TOPK_SLOW == 0
+    # the capped sample lets about 9,000 candidates through at this budget:
+    # more than the LDS lists hold (8,192), within the register path (12,288)
+    assert g["flags"] == 0, g["flags"]
     say("largest context max err", err, "flags", g["flags"])
+
+
+@pytest.mark.parametrize("case", ["two_clusters", "all_equal"])
+def test_topk_register_path_capacity(case):
+    """Between 8,192 and 12,288 candidates: the select keeps them in
+    registers.  two_clusters: 2,000 keys above 8,000 distinct keys of one
+    threshold bucket, all kept as candidates, the bucket ranked in full;
+    all_equal: 10,000 equal keys, one bucket larger than its LDS member list,
+    so the exact path over the records runs (informational flag)."""
+    skv = need_gpu()
+    S, k, L = 64, 2048, 1024
+    T = 12_000 if case == "two_clusters" else 11_088
+    desc = skv.token_desc(1, T, 4, 24, 256, topk=k, n_sink=S, n_tail=L)
+    keys = np.ones((1, T))
+    if case == "two_clusters":
+        mid = np.arange(S, T - L)
+        keys[0, mid[:2000]] = 10.0 + 1e-6 * np.arange(2000)
+        keys[0, mid[2000:10000]] = 5.0 + 1e-9 * np.arange(8000)
+    else:
+        keys[0] = 3.0
+    kt = torch.from_numpy(keys).cuda()
+    ctx = torch.full((1,), T, dtype=torch.int32, device="cuda")
+    cap = skv.select_capacity(desc)
+    idx = torch.zeros((1, cap), dtype=torch.int32, device="cuda")
+    nsel = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    ws = skv.workspace(desc)
+    skv.topk(desc, ctx, kt, idx, nsel, ws)
+    flags = skv.check(ws)
+    want = oracle.select_tokens(keys[0], T, S, k, L)
+    assert nsel[0].item() == want.size
+    assert np.array_equal(idx.cpu().numpy()[0, :want.size], want)
+    if case == "two_clusters":
+        assert flags == 0, flags
+    else:
+        assert flags == skv.SKV_FLAG_TOPK_SLOW, flags
 
 
 def test_topk_ties_and_degenerate_keys():

@@ -41,7 +41,12 @@ constexpr int kSelThreads = 256;
 constexpr int kFinalThreads = 1024;   // sample kernel of the keys path
 constexpr int kFT = 1024;             // final select kernel
 constexpr int kSegPT = kMaxSeg / kFT; // segment counts per thread
-constexpr int kGPT = kListCap / kFT;  // candidates per thread in the fast path
+// candidates the register path holds (per thread kGPT, in registers): more
+// than the LDS lists, since the capped sample of a multi-million-token
+// context lets about 9,000 through at k = 4096; the threshold bin's members
+// still go through an LDS list of kListCap
+constexpr int kRegCap = 12288;
+constexpr int kGPT = kRegCap / kFT;
 
 // ---------------------------------------------------------------------------
 // sample and collect from materialized keys
@@ -572,7 +577,7 @@ __global__ __launch_bounds__(kFT) void topk_final_kernel(
     __syncthreads();
   }
 
-  if (total >= (uint32_t)k && total <= (uint32_t)kListCap) {
+  if (total >= (uint32_t)k && total <= (uint32_t)kRegCap) {
     // ---- fast path: the candidates stay in registers, in position order ----
     // Thread t holds the contiguous run [kGPT*t, kGPT*(t+1)): one search for
     // its first segment, then a walk; all its loads are issued together.
@@ -650,6 +655,7 @@ __global__ __launch_bounds__(kFT) void topk_final_kernel(
       if (j0 + m < n && bin_of(rec[m].w) == fbin) ++mine;
     uint32_t mb = 0;
     uint32_t at = block_excl_scan(mine, sh.wsum, &mb);
+    if (mb <= (uint32_t)kListCap) {   // workgroup-uniform; else the path over the records below
 #pragma unroll
     for (int m = 0; m < kGPT; ++m)
       if (j0 + m < n && bin_of(rec[m].w) == fbin) {
@@ -723,6 +729,8 @@ __global__ __launch_bounds__(kFT) void topk_final_kernel(
         ++rank;
       }
     return;
+    }
+    __syncthreads();   // the LDS is reused below
   }
 
   if (threadIdx.x == 0) raise_flag(flags, SKV_FLAG_TOPK_SLOW);
