@@ -146,24 +146,40 @@ def test_largest_context_and_budget():
     say("largest context max err", err, "flags", g["flags"])
 
 
-@pytest.mark.parametrize("case", ["two_clusters", "all_equal"])
+@pytest.mark.parametrize("case", ["two_clusters", "all_equal", "mid_bucket", "mid_bucket_regs"])
 def test_topk_register_path_capacity(case):
-    """Between 8,192 and 12,288 candidates: the select keeps them in
-    registers.  two_clusters: 2,000 keys above 8,000 distinct keys of one
+    """Between 8,192 and 12,288 candidates the select keeps them in
+    registers, and threshold buckets of up to 1,024 members are ranked
+    pairwise.  two_clusters: 2,000 keys above 8,000 distinct keys of one
     threshold bucket, all kept as candidates, the bucket ranked in full;
     all_equal: 10,000 equal keys, one bucket larger than its LDS member list,
-    so the exact path over the records runs (informational flag)."""
+    so the exact path over the records runs (informational flag); mid_bucket:
+    1,500 keys above a bucket of 700 distinct keys that holds the k-th
+    largest (one thread per member) and 1,500 lower candidates, all in the
+    LDS list; mid_bucket_regs: the same with 9,000 lower candidates, so the
+    candidates sit in registers."""
     skv = need_gpu()
     S, k, L = 64, 2048, 1024
-    T = 12_000 if case == "two_clusters" else 11_088
+    T = {"two_clusters": 12_000, "all_equal": 11_088, "mid_bucket": 20_000, "mid_bucket_regs": 20_000}[case]
     desc = skv.token_desc(1, T, 4, 24, 256, topk=k, n_sink=S, n_tail=L)
     keys = np.ones((1, T))
+    mid = np.arange(S, T - L)
     if case == "two_clusters":
-        mid = np.arange(S, T - L)
         keys[0, mid[:2000]] = 10.0 + 1e-6 * np.arange(2000)
         keys[0, mid[2000:10000]] = 5.0 + 1e-9 * np.arange(8000)
-    else:
+    elif case == "all_equal":
         keys[0] = 3.0
+    else:
+        # interleaved so that every sampled line sees all three groups
+        rng = np.random.default_rng(11)
+        sel = rng.permutation(mid.size)
+        top, bucket = mid[sel[:1500]], mid[sel[1500:2200]]
+        keys[0, top] = 10.0 + 1e-6 * np.arange(1500)
+        keys[0, bucket] = 5.0 + 1e-9 * rng.permutation(700)
+        # below the bucket, the keys the threshold lands among (all kept as
+        # candidates): 1,500 (candidates in the LDS list) or 9,000 (in registers)
+        n3 = 9000 if case == "mid_bucket_regs" else 1500
+        keys[0, mid[sel[2200:2200 + n3]]] = (4.9 if n3 == 9000 else 3.0) + 1e-9 * np.arange(n3)
     kt = torch.from_numpy(keys).cuda()
     ctx = torch.full((1,), T, dtype=torch.int32, device="cuda")
     cap = skv.select_capacity(desc)
@@ -175,10 +191,10 @@ def test_topk_register_path_capacity(case):
     want = oracle.select_tokens(keys[0], T, S, k, L)
     assert nsel[0].item() == want.size
     assert np.array_equal(idx.cpu().numpy()[0, :want.size], want)
-    if case == "two_clusters":
-        assert flags == 0, flags
-    else:
+    if case == "all_equal":
         assert flags == skv.SKV_FLAG_TOPK_SLOW, flags
+    else:
+        assert flags == 0, flags
 
 
 def test_topk_ties_and_degenerate_keys():

@@ -329,7 +329,9 @@ struct NoSrc {
   static constexpr int LANES = 64;
 };
 
-constexpr uint32_t kRankMax = 256;   // bucket sizes resolved by pairwise ranks
+// bucket sizes resolved by pairwise ranks: 16, 8, 4, 2 or 1 threads per
+// member (a wider bucket takes the multi-pass radix select)
+constexpr uint32_t kRankMax = 1024;
 
 // RECOMPUTE (the fused path): keys are recomputed from the index when the
 // candidates are too few.
@@ -339,7 +341,7 @@ constexpr int kOneTripSegs = 2 * kFT;       // segments the one-round-trip path 
 // LDS of the final select, shared by its paths (bytes): the one-trip path's
 // candidate arrays (key, position, digit) plus a member list, or the other
 // paths' register-gather lists and segment offsets
-constexpr size_t kFastBytes = (size_t)kListCap * 14 + 320 * 12;
+constexpr size_t kFastBytes = (size_t)kListCap * 14 + (kRankMax + 64) * 12;
 constexpr size_t kOldBytes = (size_t)(kListCap + 64) * 12 + (size_t)(kMaxSeg + 1) * 4;
 constexpr size_t kSelLds = kFastBytes > kOldBytes ? kFastBytes : kOldBytes;
 
@@ -389,8 +391,8 @@ __global__ __launch_bounds__(kFT) void topk_final_kernel(
     uint64_t* c_key = s_mem;                                                  // [kListCap]
     uint32_t* c_pos = reinterpret_cast<uint32_t*>(c_key + kListCap);          // [kListCap]
     uint16_t* c_dig = reinterpret_cast<uint16_t*>(c_pos + kListCap);          // [kListCap]
-    uint64_t* m_hi = reinterpret_cast<uint64_t*>(c_dig + kListCap);           // [320]
-    uint32_t* m_lo = reinterpret_cast<uint32_t*>(m_hi + 320);                 // [320]
+    uint64_t* m_hi = reinterpret_cast<uint64_t*>(c_dig + kListCap);           // [kRankMax + 64]
+    uint32_t* m_lo = reinterpret_cast<uint32_t*>(m_hi + kRankMax + 64);       // [kRankMax + 64]
     uint32_t total = 0;
     bool fits = true;
     for (int r0 = 0; r0 < n_parts; r0 += kFT) {   // workgroup-uniform
@@ -491,7 +493,7 @@ __global__ __launch_bounds__(kFT) void topk_final_kernel(
           m_lo[mb + threadIdx.x] = 0u;
         }
         __syncthreads();
-        const int P = mb <= 64 ? 16 : (mb <= 128 ? 8 : 4);
+        const int P = mb <= 64 ? 16 : (mb <= 128 ? 8 : (mb <= 256 ? 4 : (mb <= 512 ? 2 : 1)));
         const int mm = (int)threadIdx.x / P, part = (int)threadIdx.x % P;
         uint32_t rank = 0;
         uint64_t hi = 0;
@@ -671,7 +673,7 @@ __global__ __launch_bounds__(kFT) void topk_final_kernel(
     if (mb <= kRankMax) {
       // each member counts the members above it (P threads per member, each
       // over every P-th member); rank r-1 is the threshold
-      const int P = mb <= 64 ? 16 : (mb <= 128 ? 8 : 4);
+      const int P = mb <= 64 ? 16 : (mb <= 128 ? 8 : (mb <= 256 ? 4 : (mb <= 512 ? 2 : 1)));
       const int m = (int)threadIdx.x / P, part = (int)threadIdx.x % P;
       uint32_t rank = 0;
       uint64_t hi = 0;
