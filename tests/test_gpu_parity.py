@@ -95,6 +95,47 @@ def test_config3_shape_boundaries():
         assert 4 * blk in set(g["idx"][0, :2048].tolist())
 
 
+def test_pooled_keys_out_of_domain():
+    """Block mode outside the bf16 range where an fp64 sum of products is
+    exact in any order (the generator's inputs are flushed into it): inputs
+    spanning 2^-20 .. 2^10, so products span about 60 bits.  Each product of
+    two bf16 values is exact in fp32; the kernel sums them in fp64 in its own
+    order, so a key is the exact dot product within the fp64 summation bound
+    (127 units of 2^-53 times the sum of the products' magnitudes), and the
+    picks are a top-k of the exact keys up to that bound.  Bit-exact parity is
+    claimed inside the domain only."""
+    import math
+    skv = need_gpu()
+    c = _cfg3(1, 40_000, device="cuda")
+    g = torch.Generator().manual_seed(21)
+    def wide(shape):
+        e = torch.randint(-20, 10, shape, generator=g).to(torch.float32)
+        return (torch.randn(shape, generator=g) * torch.exp2(e)).to(torch.bfloat16)
+    c.qi = wide(tuple(c.qi.shape)).cuda()
+    c.kp = wide(tuple(c.kp.shape)).cuda()
+    say("pooled keys out of domain")
+    gres = run_block_gpu(skv, c, 256 ** -0.5)
+    nb = c.lens[0] // 4
+    qi = c.qi[0].float().cpu().numpy().astype(np.float64)
+    kp = c.kp[0, :nb].float().cpu().numpy().astype(np.float64)
+    prods = kp * qi[None, :]                      # exact: two bf16 values
+    exact = np.array([math.fsum(r) for r in prods])
+    bound = 127 * 2.0 ** -53 * np.abs(prods).sum(axis=1)
+    gk = gres["keys"][0, :nb]
+    assert np.all(np.abs(gk - exact) <= bound), "a key outside the fp64 summation bound"
+    # the picked blocks are a top-k of the exact keys, up to the bound
+    n = int(gres["n_sel"][0])
+    picked = np.unique(gres["idx"][0, :n] // 4)
+    picked = picked[picked < nb]
+    assert picked.size == c.k
+    kth = np.sort(exact)[-c.k]
+    slack = 2 * bound.max()
+    assert exact[picked].min() >= kth - slack
+    others = np.setdiff1d(np.arange(nb), picked)
+    assert exact[others].max() <= kth + slack
+    say("out of domain: max key error %.3g (bound %.3g)" % (np.abs(gk - exact).max(), bound.max()))
+
+
 def test_empty_and_tiny_sequences():
     skv = need_gpu()
     lens = [0, 1, 2, 399, 400, 401, 1000]
