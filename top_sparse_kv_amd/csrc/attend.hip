@@ -669,18 +669,19 @@ __global__ __launch_bounds__(64 * kValuWaves) void attend_valu_kernel(
 // merge the chunks of each (sequence, query head) in ascending chunk order
 constexpr int kMaxChunks = kMaxAttChunks;   // one thread per chunk
 
-// Thread d owns output column d (D <= 256); the partials of the first
-// kMergeBatch chunks are loaded together with the (max, sum) pairs, before the
-// factors are known, so a small merge costs one round trip plus the reductions.
-// Chunks at or past the selection's end are not written in this call: they
-// are skipped by a select, not multiplied by a zero factor.
-constexpr int kMergeBatch = 16;
-
+// Thread d owns output column d (D <= 256); the partials of the first MB
+// chunks are loaded together with the (max, sum) pairs, before the factors
+// are known, so a merge of up to MB chunks costs one round trip plus the
+// reductions (MB = 16, or 32 past 16 chunks: one sequence's 2,051 rows in
+// 2-wave chunks make 33).  Chunks at or past the selection's end are not
+// written in this call: they are skipped by a select, not multiplied by a
+// zero factor.
+template <int MB>
 __global__ __launch_bounds__(256) void attend_merge_kernel(
     const float* __restrict__ part_ml, const float* __restrict__ part_o,
     const int32_t* __restrict__ n_sel, int cap, int Hq, int Hkv, int D, int n_chunks,
     int rows_per_chunk, float* __restrict__ out) {
-  __shared__ float s_f[kMaxChunks + kMergeBatch];
+  __shared__ float s_f[kMaxChunks + MB];
   __shared__ float s_red[2][4];
   const int jq = blockIdx.x, b = blockIdx.y;
   const int G = Hq / Hkv;
@@ -693,9 +694,9 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(
   const int d = min((int)threadIdx.x, D - 1);
   const float* po = part_o + (pb * G + j) * D + d;   // chunk cc at po[cc * G * D]
   const size_t cstride = (size_t)G * D;
-  float v[kMergeBatch];
+  float v[MB];
 #pragma unroll
-  for (int u = 0; u < kMergeBatch; ++u) v[u] = po[(size_t)min(u, n_chunks - 1) * cstride];   // unconditional
+  for (int u = 0; u < MB; ++u) v[u] = po[(size_t)min(u, n_chunks - 1) * cstride];   // unconditional
   const int c = threadIdx.x;   // one chunk per thread (n_chunks <= kMaxChunks)
   const float m = part_ml[((pb + min(c, n_chunks - 1)) * 16 + j) * 2];
   const float l = part_ml[((pb + min(c, n_chunks - 1)) * 16 + j) * 2 + 1];
@@ -716,12 +717,12 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(
   // chunks in ascending order
   float acc = 0.0f;
 #pragma unroll
-  for (int u = 0; u < kMergeBatch; ++u) acc += u < nc ? v[u] * s_f[u] : 0.0f;
-  for (int cc = kMergeBatch; cc < nc; cc += kMergeBatch) {
+  for (int u = 0; u < MB; ++u) acc += u < nc ? v[u] * s_f[u] : 0.0f;
+  for (int cc = MB; cc < nc; cc += MB) {
 #pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) v[u] = po[(size_t)min(cc + u, nc - 1) * cstride];
+    for (int u = 0; u < MB; ++u) v[u] = po[(size_t)min(cc + u, nc - 1) * cstride];
 #pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) acc += cc + u < nc ? v[u] * s_f[cc + u] : 0.0f;
+    for (int u = 0; u < MB; ++u) acc += cc + u < nc ? v[u] * s_f[cc + u] : 0.0f;
   }
   if ((int)threadIdx.x < D) out[((size_t)b * Hq + jq) * D + threadIdx.x] = acc * inv;
 }
@@ -816,9 +817,14 @@ hipError_t launch_attend(const skv_layer_desc& d, const void* q, const skv_kv_vi
 #undef SKV_AT_ARGS
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attend_merge_kernel, dim3(d.n_q_heads, d.batch), dim3(256), 0, st, part_ml,
-                     part_o, n_sel, cap, d.n_q_heads, d.n_kv_heads, d.head_dim, Lw.n_att_chunks,
-                     att_rows_per_wg(d), out);
+  if (Lw.n_att_chunks <= 16)
+    hipLaunchKernelGGL(attend_merge_kernel<16>, dim3(d.n_q_heads, d.batch), dim3(256), 0, st, part_ml,
+                       part_o, n_sel, cap, d.n_q_heads, d.n_kv_heads, d.head_dim, Lw.n_att_chunks,
+                       att_rows_per_wg(d), out);
+  else
+    hipLaunchKernelGGL(attend_merge_kernel<32>, dim3(d.n_q_heads, d.batch), dim3(256), 0, st, part_ml,
+                       part_o, n_sel, cap, d.n_q_heads, d.n_kv_heads, d.head_dim, Lw.n_att_chunks,
+                       att_rows_per_wg(d), out);
   return hipGetLastError();
 }
 
