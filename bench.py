@@ -35,6 +35,7 @@ PEAK_HBM_GBS = 8000.0
 CALIB_BYTES = 1 << 30          # plain streaming kernel used to scale FETCH_SIZE / WRITE_SIZE
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_collect_cfg2_traffic.md")
 SCORE_SRC = [os.path.join(ROOT, "top_sparse_kv_amd", "csrc", f) for f in ("score.hip", "keys_common.h")]
+ATTEND_SRC = [os.path.join(ROOT, "top_sparse_kv_amd", "csrc", f) for f in ("attend.hip", "skv_internal.h")]
 
 
 def log(*a):
@@ -304,19 +305,22 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
-def committed_traffic():
-    """HBM bytes per score launch from the committed counter summary, or None
-    when there is none or the kernel source changed since it was taken."""
+def committed_traffic(prefix="", src=None):
+    """HBM bytes per launch of a kernel from the committed counter summary
+    (the score stream's fields, or those named with prefix), or None when
+    there is none or the kernel's sources changed since it was taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             fields = dict(ln.split(":", 1) for ln in f.read().splitlines()
-                          if ln.startswith(("traffic_bytes_per_launch:", "score_src_sha256_16:")))
+                          if ln.startswith((prefix + "traffic_bytes_per_launch:",
+                                            prefix + ("src_sha256_16:" if prefix else "score_src_sha256_16:"))))
     except OSError:
         return None
-    if fields.get("score_src_sha256_16", "").strip() != source_hash(SCORE_SRC):
+    key = prefix + ("src_sha256_16" if prefix else "score_src_sha256_16")
+    if fields.get(key, "").strip() != source_hash(src or SCORE_SRC):
         return None
     try:
-        return int(float(fields["traffic_bytes_per_launch"]))
+        return int(float(fields[prefix + "traffic_bytes_per_launch"]))
     except (KeyError, ValueError):
         return None
 
@@ -1309,7 +1313,9 @@ def main():
     att = dict(kernel="attend" if args.contraction_path == "mfma" or multi else "attend (vector ALU)", bound="hbm",
                achieved=round(att_bytes / att_s / 1e9, 1),
                peak=PEAK_HBM_GBS, unit="GB/s",
-               frac=round(att_bytes / att_s / 1e9 / PEAK_HBM_GBS, 4), traffic=None,
+               frac=round(att_bytes / att_s / 1e9 / PEAK_HBM_GBS, 4),
+               traffic=committed_traffic("attend_", ATTEND_SRC)
+               if args.config == "cfg2" and args.contraction_path == "mfma" else None,
                bytes_per_launch=att_bytes, avg_launch_us=round(att_s * 1e6, 2),
                launches_timed=att_n, launches_per_step=round(att_n / att_steps, 2))
     if alt:
