@@ -326,37 +326,9 @@ def test_micro_batches_on_streams():
     o = oracle_token(c, sm)
     cap = skv.select_capacity(token_desc_of(skv, c))
     for m in (2, 3):
-        per = c.B // m
-        qs = torch.zeros((c.B, 256), dtype=torch.int8, device="cuda")
-        qsc = torch.zeros((c.B,), dtype=torch.float32, device="cuda")
-        idx = torch.full((c.B, cap), -1, dtype=torch.int32, device="cuda")
-        nsel = torch.zeros((c.B,), dtype=torch.int32, device="cuda")
-        out = torch.zeros((c.B, c.n_q, c.D), dtype=torch.float32, device="cuda")
-        streams = [torch.cuda.Stream() for _ in range(m)]
-        calls = []
-        for g in range(m):
-            sl = slice(g * per, (g + 1) * per)
-            desc = skv.token_desc(per, c.T_max, c.n_kv, c.n_q, c.D, topk=c.k, n_sink=c.S,
-                                  n_tail=c.L, kv_dtype=skv.SKV_KV_I8_ROWSCALE)
-            kv = skv.kv_view(c.k_cache[sl], c.v_cache[sl], c.k_scale[sl], c.v_scale[sl])
-            calls.append((desc, c.ctx_len[sl], c.q[sl], c.basis, qs[sl], qsc[sl], None,
-                          c.codes[sl], c.sk_scale[sl], kv, idx[sl], nsel[sl], sm, out[sl],
-                          skv.workspace(desc)))
-        ev = torch.cuda.Event()
-        ev.record()
-        for st in streams:
-            st.wait_event(ev)
-        for rep in range(3):
-            for st, args in zip(streams, calls):
-                skv.step(*args, stream=st)
-        for st in streams:
-            torch.cuda.current_stream().wait_stream(st)
-        torch.cuda.synchronize()
-        for args in calls:
-            assert skv.check(args[-1]) == a["flags"]
-        assert np.array_equal(qs.cpu().numpy(), a["qs"])
-        assert np.array_equal(nsel.cpu().numpy(), a["n_sel"])
-        g = dict(a, idx=idx.cpu().numpy(), out=out.cpu().numpy().astype(np.float64))
+        g = _run_micro_batches(skv, c, sm, m, reps=3, flags=a["flags"])
+        assert np.array_equal(g["qs"], a["qs"])
+        assert np.array_equal(g["n_sel"], a["n_sel"])
         for b in range(c.B):
             n = int(a["n_sel"][b])
             assert np.array_equal(g["idx"][b, :n], a["idx"][b, :n]), (m, b)
@@ -364,6 +336,45 @@ def test_micro_batches_on_streams():
             compare_out(g, o, b)
         say("micro-batches m=%d: max diff to the one-call step %.3g"
             % (m, float(np.abs(g["out"] - a["out"]).max())))
+
+
+def _run_micro_batches(skv, c, sm, m, reps, flags):
+    """The batch as m micro-batches of consecutive sequences, each a step call
+    on views of the same buffers with its own workspace and stream, reps
+    layer-steps in a row with nothing ordering the streams against each other
+    (the schedule the benchmark times); every workspace must end with the
+    given flags.  Returns the results as numpy arrays."""
+    per = c.B // m
+    cap = skv.select_capacity(token_desc_of(skv, c))
+    qs = torch.zeros((c.B, c.n_kv * c.R), dtype=torch.int8, device="cuda")
+    qsc = torch.zeros((c.B,), dtype=torch.float32, device="cuda")
+    idx = torch.full((c.B, cap), -1, dtype=torch.int32, device="cuda")
+    nsel = torch.zeros((c.B,), dtype=torch.int32, device="cuda")
+    out = torch.zeros((c.B, c.n_q, c.D), dtype=torch.float32, device="cuda")
+    streams = [torch.cuda.Stream() for _ in range(m)]
+    calls = []
+    for g in range(m):
+        sl = slice(g * per, (g + 1) * per)
+        desc = skv.token_desc(per, c.T_max, c.n_kv, c.n_q, c.D, topk=c.k, n_sink=c.S,
+                              n_tail=c.L, kv_dtype=skv.SKV_KV_I8_ROWSCALE)
+        kv = skv.kv_view(c.k_cache[sl], c.v_cache[sl], c.k_scale[sl], c.v_scale[sl])
+        calls.append((desc, c.ctx_len[sl], c.q[sl], c.basis, qs[sl], qsc[sl], None,
+                      c.codes[sl], c.sk_scale[sl], kv, idx[sl], nsel[sl], sm, out[sl],
+                      skv.workspace(desc)))
+    ev = torch.cuda.Event()
+    ev.record()
+    for st in streams:
+        st.wait_event(ev)
+    for rep in range(reps):
+        for st, args in zip(streams, calls):
+            skv.step(*args, stream=st)
+    for st in streams:
+        torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    for args in calls:
+        assert skv.check(args[-1]) == flags
+    return dict(qs=qs.cpu().numpy(), qscale=qsc.cpu().numpy(), n_sel=nsel.cpu().numpy(),
+                idx=idx.cpu().numpy(), out=out.cpu().numpy().astype(np.float64), flags=flags)
 
 
 def test_device_flags():
@@ -406,6 +417,17 @@ def test_full_config2_8x250k():
     assert g["n_sel"].tolist() == [3136] * 8
     assert g["flags"] == 0
     say("cfg2 full max err", err)
+    # the launch configuration the benchmark times: two micro-batches of 4
+    # sequences on two streams, several layer-steps in a row
+    say("cfg2 full: two micro-batches on two streams")
+    mb = _run_micro_batches(skv, c, sm, 2, reps=4, flags=0)
+    assert np.array_equal(mb["qs"], g["qs"])
+    assert np.array_equal(mb["n_sel"], g["n_sel"])
+    assert np.array_equal(mb["idx"], g["idx"])
+    for b in range(c.B):
+        compare_out(mb, o, b)
+    say("cfg2 full, micro-batches: max diff to the one-call step %.3g"
+        % float(np.abs(mb["out"] - g["out"]).max()))
 
 
 def test_full_config3_1m():
