@@ -417,17 +417,23 @@ def test_full_config2_8x250k():
     assert g["n_sel"].tolist() == [3136] * 8
     assert g["flags"] == 0
     say("cfg2 full max err", err)
-    # the launch configuration the benchmark times: two micro-batches of 4
-    # sequences on two streams, several layer-steps in a row
-    say("cfg2 full: two micro-batches on two streams")
-    mb = _run_micro_batches(skv, c, sm, 2, reps=4, flags=0)
+    _check_micro_batches(skv, c, sm, g, o, "cfg2")
+
+
+def _check_micro_batches(skv, c, sm, g, o, name):
+    """The launch configuration the benchmark times for a large batch: two
+    micro-batches of B/2 sequences on two streams, several layer-steps in a
+    row.  Every sequence gets the one-call step's sketch, picks and outputs,
+    within tolerance of the oracle."""
+    say("%s full: two micro-batches on two streams" % name)
+    mb = _run_micro_batches(skv, c, sm, 2, reps=4, flags=g["flags"])
     assert np.array_equal(mb["qs"], g["qs"])
     assert np.array_equal(mb["n_sel"], g["n_sel"])
     assert np.array_equal(mb["idx"], g["idx"])
     for b in range(c.B):
         compare_out(mb, o, b)
-    say("cfg2 full, micro-batches: max diff to the one-call step %.3g"
-        % float(np.abs(mb["out"] - g["out"]).max()))
+    say("%s full, micro-batches: max diff to the one-call step %.3g"
+        % (name, float(np.abs(mb["out"] - g["out"]).max())))
 
 
 def test_full_config3_1m():
@@ -454,6 +460,7 @@ def test_full_config4a_32x128k():
     o = oracle_token(c, sm)
     _check_token(c, g, o)
     assert g["flags"] == 0
+    _check_micro_batches(skv, c, sm, g, o, "cfg4a")
 
 
 def test_full_config4b_mixed():
@@ -469,6 +476,7 @@ def test_full_config4b_mixed():
     _check_token(c, g, o)
     for b in range(32):
         assert g["n_sel"][b] == min(lens[b], 3136)
+    _check_micro_batches(skv, c, sm, g, o, "cfg4b")
 
 
 @pytest.mark.parametrize("mode", ["token", "block"])
