@@ -300,3 +300,37 @@ def test_header_is_plain_c(tmp_path):
                             *lang, "-I", os.path.join(root, "include"), str(src)],
                            capture_output=True, text=True)
         assert r.returncode == 0, r.stderr
+
+
+def test_committed_traffic_summary(tmp_path):
+    """The counter summary bench.py reads its `traffic` fields from is
+    self-consistent: each kernel's bytes per launch are its FETCH_SIZE and
+    WRITE_SIZE averages (KiB per dispatch) scaled by the calibration copy's
+    factors, as the tables of the same file give them; a source hash that
+    does not match the tree yields None (no GPU needed)."""
+    import importlib.util
+    import re
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(root, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    text = open(bench.TRAFFIC_FILE).read()
+
+    def avg(kernel, counter):
+        vals = [float(m.group(1)) for m in re.finditer(
+            r"^\| [^|]*%s[^|]* \| \d+ \| %s \| ([0-9.e+]+) \|$" % (re.escape(kernel), counter), text, re.M)]
+        assert len(vals) == 1, (kernel, counter, vals)
+        return vals[0]
+
+    copy = "bitwise_not_kernel"
+    f_scale = 1048576.0 / avg(copy, "FETCH_SIZE")
+    w_scale = 1048576.0 / avg(copy, "WRITE_SIZE")
+    for prefix, kernel in (("", "score_kernel<skv::SketchSrc<8>, true>"),
+                           ("attend_", "attend_kernel<0, 256, 8, true>")):
+        want = 1024 * (avg(kernel, "FETCH_SIZE") * f_scale + avg(kernel, "WRITE_SIZE") * w_scale)
+        got = int(re.search(r"^%straffic_bytes_per_launch: (\d+)$" % prefix, text, re.M).group(1))
+        assert abs(got - want) <= 2, (kernel, got, want)
+    stale = tmp_path / "other.hip"
+    stale.write_text("// not the kernel's source\n")
+    assert bench.committed_traffic("attend_", [str(stale)]) is None
+    assert bench.committed_traffic("", [str(stale)]) is None
