@@ -479,6 +479,25 @@ def test_full_config4b_mixed():
     _check_micro_batches(skv, c, sm, g, o, "cfg4b")
 
 
+def test_full_top4096_8x250k():
+    """The largest budget at the headline shape: 8 x 250,000 with top-4096 +
+    64 sinks + 1,024 tail (5,184 rows per sequence), every sequence against
+    the oracle, then as the two micro-batches the benchmark times."""
+    skv = need_gpu()
+    say("top-4096 full: generating 8 x 250,000")
+    c = synth.make_token_case(8, 250_000, None, n_kv=4, n_q=24, D=256, S=64, k=4096, L=1024,
+                              kv_format="i8", seed=1002, device="cuda")
+    sm = 256 ** -0.5
+    g = run_token_gpu(skv, c, sm, fused=True)
+    say("top-4096 full: oracle on all 8 sequences")
+    o = oracle_token(c, sm)
+    err = _check_token(c, g, o)
+    assert g["n_sel"].tolist() == [64 + 4096 + 1024] * 8
+    assert g["flags"] == 0, g["flags"]
+    say("top-4096 full max err", err)
+    _check_micro_batches(skv, c, sm, g, o, "top-4096")
+
+
 @pytest.mark.parametrize("mode", ["token", "block"])
 def test_score_topk_matches_separate_calls(mode):
     """The fused score+select entry point (no keys materialized) gives the
