@@ -1350,6 +1350,8 @@ def main():
         "select_slow_path": bool(step_flags & skv.SKV_FLAG_TOPK_SLOW),
         "roofline": roof,
         "other_kernel": att,
+        # each layer-step covers every sequence of the batch once
+        "sequence_layer_steps_per_s": round(value * cfg["B"], 1),
     }
     if single:
         # the same layer-steps issued as one call per step on one stream
