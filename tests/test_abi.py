@@ -334,3 +334,28 @@ def test_committed_traffic_summary(tmp_path):
     stale.write_text("// not the kernel's source\n")
     assert bench.committed_traffic("attend_", [str(stale)]) is None
     assert bench.committed_traffic("", [str(stale)]) is None
+
+
+def test_committed_tier_io_summary():
+    """The host-tier counter summary is self-consistent: per line, the IO read
+    counter per dispatch x dispatches x the calibrated bytes per count gives
+    the host bytes counted, their ratio to the algorithmic host bytes is the
+    ratio in the table, and that ratio is the io_ratio bench.py reads (no GPU
+    needed)."""
+    import importlib.util
+    import re
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(root, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    text = open(bench.TIER_IO_FILE).read()
+    per_count = float(re.search(r"so one\s+count = ([0-9.]+) B", text).group(1))
+    num = lambda x: float(x.replace(",", ""))
+    rows = re.findall(r"^\| (cfg5\w*) \| [^|]+ \| (\d+) \| ([0-9,.]+) \| ([0-9,]+) \| ([0-9,]+) \| ([0-9.]+) \|$",
+                      text, re.M)
+    assert {r[0] for r in rows} == {"cfg5", "cfg5r"}
+    for name, disp, per, counted, alg, ratio in rows:
+        assert abs(num(per) * int(disp) * per_count - num(counted)) <= 1e-5 * num(counted), name
+        assert abs(num(counted) / num(alg) - float(ratio)) < 1e-4, name
+        got = float(re.search(r"^io_ratio_%s: ([0-9.]+)$" % name, text, re.M).group(1))
+        assert got == float(ratio), name
